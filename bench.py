@@ -1,0 +1,347 @@
+#!/usr/bin/env python3
+"""Benchmark of the CSA2 FP4 sparse-attention decode hot path on one MI355X.
+
+Default workload: the 1M-context decoder stack, batch 8, four layers in roles
+[Full, Reindex, Reuse, Reuse] with a 16,384-candidate pool, Top-K 2,048, 64
+heads and a 128-token window (the scale the DeepSeek-V4.1-Flash write-ups
+describe).  One step = pack the current token's latent row into the FP4 cache,
+then every layer's indexer / selection / sparse attention / window merge.
+
+Prints ONE JSON line: query-tokens/s over the timed steps, the step's
+algorithmic HBM GB/s, the roofline of the dominant kernel (the Full-layer
+index scan) timed with HIP events on the launch stream, and the CPU oracle
+timed on a bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload stack_1m_b8|full_decode_b64|tiny_decode|pack_1m]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+METRIC = "decode query-tokens/s + achieved HBM GB/s, CSA2 FP4 sparse attn @1M ctx"
+HBM_PEAK_GBPS = 8000.0
+SIGMA = 1.0 / math.sqrt(128)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="stack_1m_b8")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="sequences in the CPU-baseline sample (0 = auto)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
+    return ap.parse_args()
+
+
+def kernel_source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(HERE, "fp4_sparse_attention_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(name, digest):
+    """HBM bytes per launch from committed counter runs, if taken on this kernel source."""
+    path = os.path.join(HERE, "profiles", f"{name}_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def decode_step_bytes(B, T, H, K, P, modes, W=128):
+    """Compulsory bytes of one decode step (each call's inputs read once, outputs written once)."""
+    C = 512
+    total = B * (2 * C + 288)                          # pack the current token's row
+    for mode in modes:
+        if mode == "full":
+            total += B * T * (64 + 4) + B * 64          # keys + score write + query
+            if P:
+                total += B * T * 4 + B * P * 8          # pool selection: read scores, write pool + scores
+                total += B * P * 8 + B * K * 4          # top-K of the pool
+            else:
+                total += B * T * 4 + B * K * 4
+        elif mode == "reindex":
+            total += B * P * (4 + 64 + 4) + B * 64      # pool ids, gathered keys, scores
+            total += B * P * 8 + B * K * 4
+        # sparse attention: idx, gathered FP4 rows, queries, o + lse
+        total += B * K * (4 + 288) + B * H * C * 2 + B * H * (C + 1) * 4
+        # window merge: window rows, queries, sparse o/lse in, o/lse out
+        total += B * W * C * 2 + B * H * C * 2 + 2 * B * H * (C + 1) * 4
+    return total
+
+
+def cpu_baseline_decode(wl, cfg, n_seq):
+    """Time the CPU oracle on n_seq sequences of the same decode step."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+    from oracle import formats as OF, indexer as OI, topk as OT, attention as OA
+
+    cores = len(os.sched_getaffinity(0))
+    blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max(blas) if blas else 1
+    modes = cfg.modes
+    P = cfg.pool if "reindex" in modes else 0
+    elapsed = 0.0
+    for b in range(n_seq):
+        # inputs (generator data), copied to the host outside the timed region
+        k_host = wl.k_idx[b].cpu().numpy()
+        layers = [(io.q_idx[b].cpu().numpy(), io.q_lat[b].to(torch.float64).cpu().numpy(),
+                   io.swa[b].to(torch.float64).cpu().numpy()) for io in wl.layers]
+        new_row = wl.new_rows[b:b + 1].to(torch.float64).cpu().numpy()
+        t0 = time.perf_counter()
+        OF.fp4_pack(new_row)
+        pool = None
+        prev = None
+        needed = []
+        for mode, (q_idx, q_lat, swa) in zip(modes, layers):
+            if mode == "full":
+                s = OI.full_scores(q_idx, k_host)
+                if P:
+                    pool = OT.candidate_pool(s, P)
+                    idx = OT.topk(np.where(pool >= 0, s[np.clip(pool, 0, None)], -np.inf), cfg.topk, index_map=pool)
+                else:
+                    idx = OT.topk(s, cfg.topk)
+            elif mode == "reindex":
+                idx = OT.topk(OI.reindex_scores(q_idx, k_host, pool), cfg.topk, index_map=pool)
+            else:
+                idx = prev
+            prev = idx
+            needed.append(idx)
+        elapsed += time.perf_counter() - t0
+        # the oracle packs the latent rows it attends over; drawing them is input generation
+        rows_by_layer = []
+        for idx in needed:
+            pos = idx[idx >= 0]
+            rows_by_layer.append(wl.latent_host(b, pos))
+        t0 = time.perf_counter()
+        for (q_idx, q_lat, swa), lat in zip(layers, rows_by_layer):
+            c, s_ = OF.fp4_pack(lat)
+            rows = OF.fp4_unpack(c, s_)
+            o_s, l_s = OA.attend(q_lat, rows, SIGMA)
+            o_w, l_w = OA.attend(q_lat, OA.window_rows(swa, 0, cfg.window), SIGMA)
+            OA.merge(o_s, l_s, o_w, l_w)
+        elapsed += time.perf_counter() - t0
+    return {"value": n_seq / elapsed, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_seq} of {cfg.batch} sequences of one {len(modes)}-layer step "
+                      f"(numpy; BLAS pool {threads} threads of {cores} allowed cores; index scan single-threaded int64)",
+            "seconds": elapsed}
+
+
+class Workload:
+    """Seeded decode inputs on the GPU; the FP4 cache is packed by the library."""
+
+    def __init__(self, cfg, dev, chunk_rows=65536):
+        import torch
+        import workloads as W
+        from fp4_sparse_attention_amd.decode import LayerIO, pack_cache
+        B, T = cfg.batch, cfg.context
+        self.T = T
+        self.cfg = cfg
+        self.dev = dev
+        self.chunk_rows = min(chunk_rows, T)
+        self.n_chunks = (T + self.chunk_rows - 1) // self.chunk_rows
+        self.outliers = W.outlier_channels(cfg.seed)
+        self.codes = torch.empty((B, T, 256), dtype=torch.uint8, device=dev)
+        self.scales = torch.empty((B, T, 32), dtype=torch.uint8, device=dev)
+        pack_cache(self.codes, self.scales, self.latent_chunk, self.chunk_rows)
+        self.k_idx = torch.stack([W.fp8_normal(cfg.seed, (T, 64), device=dev, chunk_index=b) for b in range(B)])
+        self.layers = []
+        for li in range(len(cfg.modes)):
+            d = W.decode_layer_inputs(cfg.seed, li, B, cfg.heads, cfg.window, B, device=dev, outliers=self.outliers)
+            self.layers.append(LayerIO(d["q_lat"], d["q_idx"], d["swa"],
+                                       torch.zeros(B, dtype=torch.int32, device=dev),
+                                       torch.full((B,), min(cfg.window, T), dtype=torch.int32, device=dev)))
+        # the current token's latent row, packed into position T-1 by every step
+        self.new_rows = self.latent_chunk_rows_at(T - 1)
+        torch.cuda.synchronize()
+
+    def latent_chunk(self, b, c):
+        import workloads as W
+        n = min(self.chunk_rows, self.T - c * self.chunk_rows)
+        return W.latent_rows(self.cfg.seed, n, device=self.dev, outliers=self.outliers,
+                             chunk_index=b * self.n_chunks + c)
+
+    def latent_chunk_rows_at(self, pos):
+        import torch
+        c = pos // self.chunk_rows
+        return torch.stack([self.latent_chunk(b, c)[pos - c * self.chunk_rows] for b in range(self.cfg.batch)])
+
+    def latent_host(self, b, positions):
+        import numpy as np
+        import torch
+        positions = np.asarray(positions, dtype=np.int64)
+        out = np.empty((positions.shape[0], 512))
+        chunk = positions // self.chunk_rows
+        for c in np.unique(chunk):
+            rows = self.latent_chunk(b, int(c)).to(torch.float64).cpu().numpy()
+            sel = chunk == c
+            out[sel] = rows[positions[sel] - c * self.chunk_rows]
+        return out
+
+
+def bench_decode(args, cfg):
+    import torch
+    from fp4_sparse_attention_amd.decode import Csa2DecodeStack
+    dev = torch.device("cuda:0")
+    wl = Workload(cfg, dev)
+    stack = Csa2DecodeStack(cfg.batch, cfg.context, cfg.heads, cfg.topk, cfg.modes,
+                            pool_size=cfg.pool if cfg.pool else 16384)
+    for _ in range(args.warmup):
+        stack.step(wl.codes, wl.scales, wl.k_idx, wl.layers, SIGMA, new_rows=wl.new_rows)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    index_ev = []
+    t_start.record()
+    for _ in range(args.steps):
+        stack.step(wl.codes, wl.scales, wl.k_idx, wl.layers, SIGMA, new_rows=wl.new_rows, time_index=True)
+        index_ev.append(stack.index_events)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / args.steps
+    idx_ms = sum(a.elapsed_time(b) for a, b in index_ev) / len(index_ev)
+    B, T, H, K = cfg.batch, cfg.context, cfg.heads, cfg.topk
+    P = min(cfg.pool, T) if "reindex" in cfg.modes else 0
+    step_bytes = decode_step_bytes(B, T, H, K, P, cfg.modes, cfg.window)
+    idx_bytes = B * T * (64 + 4) + B * 64
+    achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
+    digest = kernel_source_digest(["index.hip", "common.hpp"])
+    rec = {
+        "metric": METRIC,
+        "value": B / (ms * 1e-3),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e2m1/e4m3 storage; e4m3xe4m3->f32 index; f16xf16->f32 attention",
+        "data": "synthetic (seeded torch normal draws; FP4 cache packed by the library)",
+        "config": {"workload": cfg.name, "batch": B, "context": T, "heads": H, "topk": K,
+                   "layers": list(cfg.modes), "pool": P, "window": cfg.window, "latent_channels": 512},
+        "achieved_hbm_gbps": step_bytes / (ms * 1e-3) / 1e9,
+        "step_algorithmic_bytes": step_bytes,
+        "roofline": {"kernel": "csa2_index_full (index_rows_kernel)", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic("index_full", digest),
+                     "launch_ms": idx_ms, "bytes_per_launch": idx_bytes},
+    }
+    if not args.no_cpu_baseline:
+        n_seq = args.cpu_sample or (1 if T >= (1 << 20) else 2)
+        rec["cpu_baseline"] = cpu_baseline_decode(wl, cfg, min(n_seq, B))
+    else:
+        rec["cpu_baseline"] = None
+    return rec
+
+
+def bench_pack(args, cfg):
+    import torch
+    import workloads as W
+    import fp4_sparse_attention_amd as F
+    dev = torch.device("cuda:0")
+    n, C = cfg.rows, cfg.channels
+    x = W.latent_rows(cfg.seed, n, device=dev, outliers=W.outlier_channels(cfg.seed))
+    codes = torch.empty((n, C // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((n, C // 16), dtype=torch.uint8, device=dev)
+    xb = torch.empty_like(x)
+    for _ in range(args.warmup):
+        F.csa2_fp4_pack(x, codes, scales)
+        F.csa2_fp4_unpack(codes, scales, xb)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
+    for i in range(args.steps):
+        ev[3 * i].record()
+        F.csa2_fp4_pack(x, codes, scales)
+        ev[3 * i + 1].record()
+        F.csa2_fp4_unpack(codes, scales, xb)
+        ev[3 * i + 2].record()
+    torch.cuda.synchronize()
+    pack_ms = sum(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(args.steps)) / args.steps
+    unpack_ms = sum(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(args.steps)) / args.steps
+    bytes_dir = n * (2 * C + C // 2 + C // 16)
+    achieved = bytes_dir / (pack_ms * 1e-3) / 1e9
+    digest = kernel_source_digest(["pack.hip", "common.hpp"])
+    ms = pack_ms + unpack_ms
+    rec = {
+        "metric": "FP4 pack+unpack rows/s (memory-bound stream)", "value": n / (ms * 1e-3), "unit": "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 <-> e2m1 + e4m3", "data": "synthetic",
+        "config": {"workload": cfg.name, "rows": n, "channels": C},
+        "achieved_hbm_gbps": 2 * bytes_dir / (ms * 1e-3) / 1e9,
+        "unpack_gbps": bytes_dir / (unpack_ms * 1e-3) / 1e9,
+        "roofline": {"kernel": "csa2_fp4_pack", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic("fp4_pack", digest), "launch_ms": pack_ms,
+                     "bytes_per_launch": bytes_dir},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import formats as OF
+        sample = 65536
+        xs = x[:sample].to(torch.float64).cpu().numpy()
+        t0 = time.perf_counter()
+        c, s = OF.fp4_pack(xs)
+        OF.fp4_unpack(c, s)
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": sample / dt, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                               "sample": f"first {sample} rows, pack then unpack (numpy, single thread)",
+                               "seconds": dt}
+    return rec
+
+
+def copy_calibration():
+    import torch
+    dev = torch.device("cuda:0")
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_each_way": 1 << 30, "copies": 3}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import fp4_sparse_attention_amd as F
+    F.lib()                       # fail loudly if the HIP library is missing
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    import workloads as W
+    cfg = W.by_name(args.workload)
+    print(f"# workload {cfg.name}: building inputs", file=sys.stderr, flush=True)
+    if isinstance(cfg, W.PackStream):
+        rec = bench_pack(args, cfg)
+    else:
+        rec = bench_decode(args, cfg)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

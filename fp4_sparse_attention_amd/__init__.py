@@ -1,0 +1,267 @@
+"""Python binding of libcsa2 (CSA2 FP4 sparse-attention decode on MI355X / gfx950).
+
+Argument marshalling only: every function below takes torch tensors that
+already live on the GPU, checks their dtype/shape/contiguity, passes raw device
+pointers, sizes and torch's current HIP stream to the C ABI declared in
+include/csa2.h, and raises Csa2Error on a non-zero status.  All arithmetic runs
+in the library's HIP kernels; there is no fallback.  The library is loaded from
+this package directory; build it first with
+``python -m fp4_sparse_attention_amd.build``.
+"""
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcsa2.so")
+
+_c_void_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_size_t = ctypes.c_size_t
+
+_SIGS = {
+    "csa2_abi_version": (_i32, []),
+    "csa2_status_str": (ctypes.c_char_p, [_i32]),
+    "csa2_fp4_pack": (_i32, [_c_void_p, _i64, _i32, _i64, _c_void_p, _i64, _c_void_p, _i64, _c_void_p]),
+    "csa2_fp4_unpack": (_i32, [_c_void_p, _c_void_p, _i64, _i32, _c_void_p, _c_void_p]),
+    "csa2_index_full": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "csa2_index_reindex": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i64, _c_void_p, _c_void_p, _i32, _c_void_p,
+                                  _c_void_p]),
+    "csa2_topk_workspace_size": (_size_t, [_i32, _i64, _i32]),
+    "csa2_topk": (_i32, [_c_void_p, _i32, _i64, _i64, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t,
+                         _c_void_p]),
+    "csa2_sparse_decode_workspace_size": (_size_t, [_i32, _i32, _i32]),
+    "csa2_sparse_decode": (_i32, [_c_void_p, _i32, _i32, _c_void_p, _c_void_p, _i32, _i64, _c_void_p, _c_void_p,
+                                  _i32, _f32, _c_void_p, _c_void_p, _c_void_p, _size_t, _c_void_p]),
+    "csa2_swa_merge_workspace_size": (_size_t, [_i32, _i32]),
+    "csa2_swa_merge": (_i32, [_c_void_p, _i32, _i32, _c_void_p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _f32,
+                              _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t, _c_void_p]),
+}
+
+_lib = None
+
+
+class Csa2Error(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        msg = lib().csa2_status_str(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{fn} failed with status {status}: {msg}")
+
+
+def lib():
+    """The loaded libcsa2 (ctypes.CDLL).  Raises if the library has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libcsa2.so not found at {LIB_PATH}; run `python -m fp4_sparse_attention_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def exported_symbols():
+    return sorted(_SIGS)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(fn, status):
+    if status != 0:
+        raise Csa2Error(fn, status)
+
+
+def _need(t, dtype, name, ndim=None):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a GPU tensor")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
+
+
+def _dense(t, name):
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def csa2_abi_version():
+    return lib().csa2_abi_version()
+
+
+def csa2_fp4_pack(x, codes, scales, stream=None):
+    """x bf16 [n, C] (rows may be strided) -> codes uint8 [n, C/2], scales uint8 [n, C/16].
+    codes / scales may be row-strided views (e.g. one row per sequence of a cache)."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(codes, torch.uint8, "codes", 2)
+    _need(scales, torch.uint8, "scales", 2)
+    n, C = x.shape
+    if codes.shape != (n, C // 2) or scales.shape != (n, C // 16):
+        raise ValueError("codes/scales shape mismatch")
+    for t, nm in ((x, "x"), (codes, "codes"), (scales, "scales")):
+        if t.stride(1) != 1:
+            raise ValueError(f"{nm}: channels must be contiguous")
+    st = lib().csa2_fp4_pack(_p(x), n, C, x.stride(0), _p(codes), codes.stride(0), _p(scales), scales.stride(0),
+                             _stream(stream))
+    _check("csa2_fp4_pack", st)
+
+
+def csa2_fp4_unpack(codes, scales, x, stream=None):
+    _need(codes, torch.uint8, "codes", 2)
+    _need(scales, torch.uint8, "scales", 2)
+    _need(x, torch.bfloat16, "x", 2)
+    for t, nm in ((codes, "codes"), (scales, "scales"), (x, "x")):
+        _dense(t, nm)
+    n, C = x.shape
+    if codes.shape != (n, C // 2) or scales.shape != (n, C // 16):
+        raise ValueError("codes/scales shape mismatch")
+    _check("csa2_fp4_unpack", lib().csa2_fp4_unpack(_p(codes), _p(scales), n, C, _p(x), _stream(stream)))
+
+
+def csa2_index_full(q_idx, k_idx, scores, row_seq=None, row_limit=None, stream=None):
+    """q_idx uint8 [R, 64]; k_idx uint8 [B, T, 64]; scores fp32 [R, T] (written)."""
+    _need(q_idx, torch.uint8, "q_idx", 2)
+    _need(k_idx, torch.uint8, "k_idx", 3)
+    _need(scores, torch.float32, "scores", 2)
+    for t, nm in ((q_idx, "q_idx"), (k_idx, "k_idx"), (scores, "scores")):
+        _dense(t, nm)
+    R = q_idx.shape[0]
+    B, T, D = k_idx.shape
+    if D != 64 or q_idx.shape[1] != 64 or scores.shape != (R, T):
+        raise ValueError("index shapes")
+    if row_seq is not None:
+        _need(row_seq, torch.int32, "row_seq", 1)
+    if row_limit is not None:
+        _need(row_limit, torch.int64, "row_limit", 1)
+    st = lib().csa2_index_full(_p(q_idx), _p(k_idx), R, B, T, _p(row_seq), _p(row_limit), _p(scores), _stream(stream))
+    _check("csa2_index_full", st)
+
+
+def csa2_index_reindex(q_idx, k_idx, pool, scores, row_seq=None, stream=None):
+    """q_idx uint8 [R, 64]; k_idx uint8 [B, T, 64]; pool int32 [R, P]; scores fp32 [R, P]."""
+    _need(q_idx, torch.uint8, "q_idx", 2)
+    _need(k_idx, torch.uint8, "k_idx", 3)
+    _need(pool, torch.int32, "pool", 2)
+    _need(scores, torch.float32, "scores", 2)
+    for t, nm in ((q_idx, "q_idx"), (k_idx, "k_idx"), (pool, "pool"), (scores, "scores")):
+        _dense(t, nm)
+    R, P = pool.shape
+    B, T, _ = k_idx.shape
+    if scores.shape != (R, P) or q_idx.shape != (R, 64):
+        raise ValueError("reindex shapes")
+    if row_seq is not None:
+        _need(row_seq, torch.int32, "row_seq", 1)
+    st = lib().csa2_index_reindex(_p(q_idx), _p(k_idx), R, B, T, _p(row_seq), _p(pool), P, _p(scores),
+                                  _stream(stream))
+    _check("csa2_index_reindex", st)
+
+
+def csa2_topk_workspace_size(R, N, k):
+    return int(lib().csa2_topk_workspace_size(R, N, k))
+
+
+def csa2_topk(scores, k, idx_out, score_out=None, index_map=None, workspace=None, stream=None):
+    """scores fp32 [R, N] (row stride may exceed N); idx_out int32 [R, k]; score_out fp32 [R, k] or None;
+    index_map int32 [R, N] or None; workspace uint8 tensor (allocated here if None)."""
+    _need(scores, torch.float32, "scores", 2)
+    _need(idx_out, torch.int32, "idx_out", 2)
+    if scores.stride(1) != 1:
+        raise ValueError("scores: columns must be contiguous")
+    R, N = scores.shape
+    if idx_out.shape != (R, k):
+        raise ValueError("idx_out shape")
+    _dense(idx_out, "idx_out")
+    if score_out is not None:
+        _need(score_out, torch.float32, "score_out", 2)
+        _dense(score_out, "score_out")
+    if index_map is not None:
+        _need(index_map, torch.int32, "index_map", 2)
+        _dense(index_map, "index_map")
+    need = csa2_topk_workspace_size(R, N, k)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    st = lib().csa2_topk(_p(scores), R, N, scores.stride(0), k, _p(index_map), _p(idx_out), _p(score_out),
+                         _p(workspace), workspace.numel(), _stream(stream))
+    _check("csa2_topk", st)
+
+
+def csa2_sparse_decode_workspace_size(R, H, K):
+    return int(lib().csa2_sparse_decode_workspace_size(R, H, K))
+
+
+def csa2_sparse_decode(q_lat, codes, scales, idx, softmax_scale, o, lse, row_seq=None, workspace=None,
+                       stream=None):
+    """q_lat bf16 [R, H, 512]; codes uint8 [B, T, 256]; scales uint8 [B, T, 32]; idx int32 [R, K];
+    o fp32 [R, H, 512]; lse fp32 [R, H]."""
+    _need(q_lat, torch.bfloat16, "q_lat", 3)
+    _need(codes, torch.uint8, "codes", 3)
+    _need(scales, torch.uint8, "scales", 3)
+    _need(idx, torch.int32, "idx", 2)
+    _need(o, torch.float32, "o", 3)
+    _need(lse, torch.float32, "lse", 2)
+    for t, nm in ((q_lat, "q_lat"), (codes, "codes"), (scales, "scales"), (idx, "idx"), (o, "o"), (lse, "lse")):
+        _dense(t, nm)
+    R, H, C = q_lat.shape
+    B, T, cb = codes.shape
+    K = idx.shape[1]
+    if C != 512 or cb != 256 or scales.shape != (B, T, 32) or o.shape != (R, H, 512) or lse.shape != (R, H):
+        raise ValueError("sparse_decode shapes")
+    if row_seq is not None:
+        _need(row_seq, torch.int32, "row_seq", 1)
+    need = csa2_sparse_decode_workspace_size(R, H, K)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_lat.device)
+    st = lib().csa2_sparse_decode(_p(q_lat), R, H, _p(codes), _p(scales), B, T, _p(row_seq), _p(idx), K,
+                                  float(softmax_scale), _p(o), _p(lse), _p(workspace), workspace.numel(),
+                                  _stream(stream))
+    _check("csa2_sparse_decode", st)
+
+
+def csa2_swa_merge_workspace_size(R, H):
+    return int(lib().csa2_swa_merge_workspace_size(R, H))
+
+
+def csa2_swa_merge(q_lat, swa, swa_start, swa_len, softmax_scale, o_out, lse_out=None, o_sparse=None,
+                   lse_sparse=None, row_seq=None, workspace=None, stream=None):
+    """q_lat bf16 [R, H, 512]; swa bf16 [B, S, 512]; swa_start / swa_len int32 [R];
+    o_sparse / lse_sparse: the sparse result or None; o_out fp32 [R, H, 512]; lse_out fp32 [R, H] or None."""
+    _need(q_lat, torch.bfloat16, "q_lat", 3)
+    _need(swa, torch.bfloat16, "swa", 3)
+    _need(swa_start, torch.int32, "swa_start", 1)
+    _need(swa_len, torch.int32, "swa_len", 1)
+    _need(o_out, torch.float32, "o_out", 3)
+    for t, nm in ((q_lat, "q_lat"), (swa, "swa"), (swa_start, "swa_start"), (swa_len, "swa_len"),
+                  (o_out, "o_out")):
+        _dense(t, nm)
+    R, H, _ = q_lat.shape
+    B, S, C = swa.shape
+    if C != 512 or o_out.shape != (R, H, 512) or swa_start.shape != (R,) or swa_len.shape != (R,):
+        raise ValueError("swa_merge shapes")
+    for t, nm, dt in ((o_sparse, "o_sparse", torch.float32), (lse_sparse, "lse_sparse", torch.float32),
+                      (lse_out, "lse_out", torch.float32)):
+        if t is not None:
+            _need(t, dt, nm)
+            _dense(t, nm)
+    if row_seq is not None:
+        _need(row_seq, torch.int32, "row_seq", 1)
+    need = csa2_swa_merge_workspace_size(R, H)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_lat.device)
+    st = lib().csa2_swa_merge(_p(q_lat), R, H, _p(swa), B, S, _p(row_seq), _p(swa_start), _p(swa_len),
+                              float(softmax_scale), _p(o_sparse), _p(lse_sparse), _p(o_out), _p(lse_out),
+                              _p(workspace), workspace.numel(), _stream(stream))
+    _check("csa2_swa_merge", st)

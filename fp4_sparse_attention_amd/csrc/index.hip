@@ -1,0 +1,229 @@
+// Indexer scoring kernels: Full mode (every visible position) and Reindex mode
+// (only the candidate-pool positions), per the CSA2 roles paragraph of the
+// MarkTechPost retelling of DeepSeek-V4.1-Flash.
+//
+// score(r, j) = sum_{d<64} q_idx[r][d] * k_idx[seq(r)][j][d], E4M3 x E4M3 with
+// fp32 accumulation, computed on the fp8 matrix cores:
+//   v_mfma_f32_32x32x64_f8f6f4:  C[32 x 32] += A[32 x 64] * B[64 x 32]
+// with A = up to 32 query rows of one sequence and B = 32 keys (one 64-byte key
+// per column).  Lane l owns row/column (l % 32) and one 32-byte half of the
+// 64-d contraction, so a wave loads a 2 KB tile of 32 consecutive keys with two
+// 16-byte loads per lane (fully coalesced); A and B use the same lane->k map.
+// Output C: lane l, register v holds column l % 32 and row
+// 8*(v/4) + 4*(l/32) + (v%4); row 0 therefore sits in register 0 of lanes 0-31,
+// which store 32 consecutive scores as one 128-byte line.
+//
+// Decode (one query per sequence) is HBM-bound: 64 bytes of key per score, and
+// the matrix cores are ~10% busy.  Chunked prefill fills all 32 rows of A and
+// is bound by the fp32 score writes.
+#include "common.hpp"
+
+namespace csa2 {
+
+constexpr int kTile = 32;          // keys per MFMA tile
+constexpr int kUnroll = 4;         // tiles in flight per wave
+
+__device__ __forceinline__ f32x16 mfma_fp8_32x32x64(const i32x8& a, const i32x8& b, f32x16 c) {
+  // scale operands 0 select the unscaled instruction (plain fp8 x fp8)
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ i32x8 load_half_key(const uint8_t* p) {
+  uint4 x = ld_nt16(p);
+  uint4 y = ld_nt16(p + 16);
+  i32x8 r;
+  r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
+  r[4] = y.x; r[5] = y.y; r[6] = y.z; r[7] = y.w;
+  return r;
+}
+
+// One query row per workgroup row (grid.y = R).  Used for decode (Full and
+// Reindex).  kGather: column c of row r scores position pool[r][c].
+template <bool kGather>
+__global__ void __launch_bounds__(256)
+index_rows_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx, int64_t T,
+                  const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit,
+                  const int32_t* __restrict__ pool, int64_t n_cols, float* __restrict__ scores,
+                  int tiles_per_block) {
+  const int r = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int half = lane >> 5;
+  const int col_in_tile = lane & 31;
+  const int seq = row_seq ? row_seq[r] : r;
+  const uint8_t* kseq = k_idx + (int64_t)seq * T * kIndexDim;
+  const int64_t limit = row_limit ? row_limit[r] : T - 1;
+  float* out = scores + (int64_t)r * n_cols;
+  const int32_t* prow = kGather ? pool + (int64_t)r * n_cols : nullptr;
+
+  i32x8 a = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (col_in_tile == 0) {
+    const uint4* q = reinterpret_cast<const uint4*>(q_idx + (int64_t)r * kIndexDim + 32 * half);
+    uint4 x = q[0], y = q[1];
+    a[0] = x.x; a[1] = x.y; a[2] = x.z; a[3] = x.w;
+    a[4] = y.x; a[5] = y.y; a[6] = y.z; a[7] = y.w;
+  }
+
+  const int64_t n_tiles = (n_cols + kTile - 1) / kTile;
+  const int64_t t_begin = (int64_t)blockIdx.x * tiles_per_block;
+  const int64_t t_end = min(n_tiles, t_begin + tiles_per_block);
+  const float neg_inf = -__builtin_inff();
+
+  for (int64_t t0 = t_begin + wave; t0 < t_end; t0 += 4 * kUnroll) {
+    i32x8 b[kUnroll];
+    int64_t pos[kUnroll];
+    bool ok[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      int64_t t = t0 + 4 * u;
+      int64_t c = t * kTile + col_in_tile;
+      int64_t p = -1;
+      if (t < t_end && c < n_cols) p = kGather ? (int64_t)prow[c] : c;
+      ok[u] = p >= 0 && p < T && p <= limit;
+      pos[u] = c;
+      b[u] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      if (ok[u]) b[u] = load_half_key(kseq + p * kIndexDim + 32 * half);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      int64_t t = t0 + 4 * u;
+      f32x16 acc = {};
+      acc = mfma_fp8_32x32x64(a, b[u], acc);
+      if (t < t_end && half == 0 && pos[u] < n_cols) out[pos[u]] = ok[u] ? acc[0] : neg_inf;
+    }
+  }
+}
+
+// Up to 32 query rows per workgroup (grid.y = ceil(R/32)): chunked prefill.
+// Rows of one workgroup that share a sequence are scored together; a
+// workgroup whose rows span several sequences handles one sequence at a time.
+__global__ void __launch_bounds__(256)
+index_block_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx, int R, int64_t T,
+                   const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit,
+                   float* __restrict__ scores, int tiles_per_block) {
+  __shared__ int s_seq[32];
+  __shared__ int64_t s_lim[32];
+  const int r0 = blockIdx.y * 32;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  if (threadIdx.x < 32) {
+    int r = r0 + threadIdx.x;
+    s_seq[threadIdx.x] = r < R ? (row_seq ? row_seq[r] : r) : -1;
+    s_lim[threadIdx.x] = r < R ? (row_limit ? row_limit[r] : T - 1) : -1;
+  }
+  __syncthreads();
+
+  const int64_t n_tiles = (T + kTile - 1) / kTile;
+  const int64_t t_begin = (int64_t)blockIdx.x * tiles_per_block;
+  const int64_t t_end = min(n_tiles, t_begin + tiles_per_block);
+  const float neg_inf = -__builtin_inff();
+
+  // rows m held by this lane's output registers
+  uint32_t done = 0;
+  for (int m = 0; m < 32; ++m)
+    if (s_seq[m] < 0) done |= 1u << m;
+
+  while (done != 0xFFFFFFFFu) {
+    int first = __builtin_ctz(~done);
+    const int seq = s_seq[first];
+    uint32_t active = 0;
+    for (int m = 0; m < 32; ++m)
+      if (!(done >> m & 1u) && s_seq[m] == seq) active |= 1u << m;
+    done |= active;
+    // the largest visible position among the active rows bounds the useful tiles
+    int64_t max_lim = -1;
+    for (int m = 0; m < 32; ++m)
+      if (active >> m & 1u) max_lim = max(max_lim, s_lim[m]);
+
+    i32x8 a = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (active >> l32 & 1u) {
+      const uint4* q = reinterpret_cast<const uint4*>(q_idx + (int64_t)(r0 + l32) * kIndexDim + 32 * half);
+      uint4 x = q[0], y = q[1];
+      a[0] = x.x; a[1] = x.y; a[2] = x.z; a[3] = x.w;
+      a[4] = y.x; a[5] = y.y; a[6] = y.z; a[7] = y.w;
+    }
+    const uint8_t* kseq = k_idx + (int64_t)seq * T * kIndexDim;
+
+    for (int64_t t0 = t_begin + wave; t0 < t_end; t0 += 4 * kUnroll) {
+      i32x8 b[kUnroll];
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        int64_t t = t0 + 4 * u;
+        int64_t c = t * kTile + l32;
+        b[u] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (t < t_end && c < T && t * kTile <= max_lim) b[u] = load_half_key(kseq + c * kIndexDim + 32 * half);
+      }
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        int64_t t = t0 + 4 * u;
+        if (t >= t_end) break;
+        int64_t c = t * kTile + l32;
+        f32x16 acc = {};
+        if (t * kTile <= max_lim) acc = mfma_fp8_32x32x64(a, b[u], acc);
+        if (c < T) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            int m = 8 * (v >> 2) + 4 * half + (v & 3);
+            if ((active >> m & 1u) && r0 + m < R) {
+              float s = c <= s_lim[m] ? acc[v] : neg_inf;
+              scores[(int64_t)(r0 + m) * T + c] = s;
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+static int tiles_per_block_for(int64_t n_tiles, int64_t rows) {
+  // aim for >= ~2048 workgroups in total, at least 16 tiles (2 KB/wave-tile) each
+  int64_t want_blocks_per_row = (2048 + rows - 1) / rows;
+  int64_t tpb = (n_tiles + want_blocks_per_row - 1) / want_blocks_per_row;
+  if (tpb < 16) tpb = 16;
+  tpb = (tpb + 15) / 16 * 16;
+  return (int)tpb;
+}
+
+}  // namespace csa2
+
+using namespace csa2;
+
+extern "C" csa2_status csa2_index_full(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int32_t B,
+                                       int64_t T, const int32_t* row_seq, const int64_t* row_limit,
+                                       float* scores, void* stream) {
+  if (!q_idx || !k_idx || !scores) return CSA2_EINVAL;
+  if (R <= 0 || B <= 0 || T <= 0) return CSA2_EINVAL;
+  if (!row_seq && R != B) return CSA2_EINVAL;
+  if (T % 4 != 0 || T >= (int64_t(1) << 31)) return CSA2_ESHAPE;
+  if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(scores, 16)) return CSA2_EALIGN;
+  const int64_t n_tiles = (T + kTile - 1) / kTile;
+  hipStream_t s = (hipStream_t)stream;
+  if (row_seq && R >= 32) {
+    int tpb = tiles_per_block_for(n_tiles, (R + 31) / 32);
+    dim3 grid(ceil_div(n_tiles, tpb), ceil_div(R, 32));
+    index_block_kernel<<<grid, 256, 0, s>>>(q_idx, k_idx, R, T, row_seq, row_limit, scores, tpb);
+  } else {
+    int tpb = tiles_per_block_for(n_tiles, R);
+    dim3 grid(ceil_div(n_tiles, tpb), R);
+    index_rows_kernel<false><<<grid, 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, nullptr, T, scores, tpb);
+  }
+  return launch_status();
+}
+
+extern "C" csa2_status csa2_index_reindex(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int32_t B,
+                                          int64_t T, const int32_t* row_seq, const int32_t* pool, int32_t P,
+                                          float* scores, void* stream) {
+  if (!q_idx || !k_idx || !scores || !pool) return CSA2_EINVAL;
+  if (R <= 0 || B <= 0 || T <= 0 || P <= 0) return CSA2_EINVAL;
+  if (!row_seq && R != B) return CSA2_EINVAL;
+  if (P % 4 != 0 || T >= (int64_t(1) << 31)) return CSA2_ESHAPE;
+  if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(scores, 16) || !aligned(pool, 16)) return CSA2_EALIGN;
+  const int64_t n_tiles = (P + kTile - 1) / kTile;
+  int tpb = tiles_per_block_for(n_tiles, R);
+  dim3 grid(ceil_div(n_tiles, tpb), R);
+  index_rows_kernel<true><<<grid, 256, 0, (hipStream_t)stream>>>(q_idx, k_idx, T, row_seq, nullptr, pool, P,
+                                                                 scores, tpb);
+  return launch_status();
+}

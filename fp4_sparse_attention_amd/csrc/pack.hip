@@ -1,0 +1,192 @@
+// FP4 KV-cache pack / unpack kernels (E2M1 elements, one E4M3 scale per 16
+// channels, no global scale -- the NVFP4-style layout of the KV-cache paragraph
+// of the MarkTechPost retelling of DeepSeek-V4.1-Flash).
+//
+// Work split: one thread owns 32 consecutive channels of one row (two scale
+// blocks): 64 bytes of bf16 in, 16 bytes of codes + 2 scale bytes out, all as
+// vector loads/stores.  Sixteen threads cover a 512-channel row, so a wave
+// streams four whole rows per step.  The kernels are HBM-bound; the arithmetic
+// is kept to integer/compare work (about a dozen lane-ops per element).
+#include "common.hpp"
+
+namespace csa2 {
+
+// Nearest E4M3FN code to a non-negative fp32 value, ties to the even code,
+// finite values >= 448 saturate to 0x7E.  The input is the correctly rounded
+// fp32 quotient amax/6 with amax a bf16 value: a tie of the E4M3 grid has at
+// most 5 significant bits, so the quotient is either exactly a tie (and exact
+// in fp32) or far (>= 2^-16 relative) from one, and rounding the fp32 value
+// decides as the exact quotient would.
+__device__ __forceinline__ uint32_t e4m3_code_nonneg(float v) {
+  if (!(v < 448.0f)) return 0x7Eu;
+  if (v < 0.015625f) {                       // below 2^-6: subnormal grid m * 2^-9
+    return (uint32_t)rintf(v * 512.0f);      // 0..8 (8 is 2^-6 = code 0x08)
+  }
+  uint32_t bits = __float_as_uint(v);
+  uint32_t e = (bits >> 23) - 120u;          // E4M3 exponent field, 1..15
+  uint32_t m = bits & 0x7FFFFFu;
+  uint32_t code = (e << 3) | (m >> 20);
+  uint32_t rem = m & 0xFFFFFu;
+  code += (rem > 0x80000u) || (rem == 0x80000u && (code & 1u));
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// E2M1 nibble of x given the block's decoded scale thresholds.  t[i] = mid_i *
+// scale for the midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 (exact in fp32);
+// at an exact midpoint the even neighbour wins, which is the upper one for
+// 0.75, 1.75, 3.5 (>=) and the lower one for the others (>).
+struct E2M1Thresholds {
+  float t0, t1, t2, t3, t4, t5, t6;
+};
+
+__device__ __forceinline__ E2M1Thresholds make_thresholds(float s) {
+  E2M1Thresholds t;
+  const float inf = __builtin_inff();
+  bool z = (s == 0.0f);
+  t.t0 = z ? inf : 0.25f * s;
+  t.t1 = z ? inf : 0.75f * s;
+  t.t2 = z ? inf : 1.25f * s;
+  t.t3 = z ? inf : 1.75f * s;
+  t.t4 = z ? inf : 2.5f * s;
+  t.t5 = z ? inf : 3.5f * s;
+  t.t6 = z ? inf : 5.0f * s;
+  return t;
+}
+
+__device__ __forceinline__ uint32_t e2m1_nibble(uint32_t xbits16, const E2M1Thresholds& t) {
+  float ax = __uint_as_float((xbits16 & 0x7FFFu) << 16);
+  uint32_t m = (uint32_t)(ax > t.t0) + (uint32_t)(ax >= t.t1) + (uint32_t)(ax > t.t2) +
+               (uint32_t)(ax >= t.t3) + (uint32_t)(ax > t.t4) + (uint32_t)(ax >= t.t5) +
+               (uint32_t)(ax > t.t6);
+  return m | ((xbits16 >> 12) & 8u);
+}
+
+// one 16-channel block: 8 dwords of packed bf16 pairs -> 2 dwords of nibbles + scale byte
+__device__ __forceinline__ void pack_block(const uint32_t* w, uint32_t& lo, uint32_t& hi, uint32_t& sc) {
+  uint32_t amax_bits = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t a = w[i] & 0x7FFFu, b = (w[i] >> 16) & 0x7FFFu;
+    amax_bits = max(amax_bits, max(a, b));    // |bf16| orders like its bit pattern
+  }
+  float amax = __uint_as_float(amax_bits << 16);
+  uint32_t code = e4m3_code_nonneg(__fdiv_rn(amax, 6.0f));
+  float s = e4m3_to_f32(code);
+  E2M1Thresholds t = make_thresholds(s);
+  uint32_t out[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t n0 = e2m1_nibble(w[i] & 0xFFFFu, t);
+    uint32_t n1 = e2m1_nibble(w[i] >> 16, t);
+    out[i >> 2] |= (n0 | (n1 << 4)) << (8 * (i & 3));
+  }
+  lo = out[0];
+  hi = out[1];
+  sc = code;
+}
+
+__global__ void __launch_bounds__(256)
+fp4_pack_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int parts_per_row, int64_t x_stride,
+                uint8_t* __restrict__ codes, int64_t codes_stride, uint8_t* __restrict__ scales,
+                int64_t scales_stride) {
+  const int64_t total = n_rows * parts_per_row;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
+       g += (int64_t)gridDim.x * blockDim.x) {
+    int64_t row = g / parts_per_row;
+    int part = (int)(g - row * parts_per_row);
+    const uint4* src = reinterpret_cast<const uint4*>(x + row * x_stride + part * 32);
+    uint4 v0 = ld_nt16(src + 0);
+    uint4 v1 = ld_nt16(src + 1);
+    uint4 v2 = ld_nt16(src + 2);
+    uint4 v3 = ld_nt16(src + 3);
+    uint32_t w0[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint32_t w1[8] = {v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
+    uint32_t c0, c1, c2, c3, s0, s1;
+    pack_block(w0, c0, c1, s0);
+    pack_block(w1, c2, c3, s1);
+    *reinterpret_cast<uint4*>(codes + row * codes_stride + part * 16) = make_uint4(c0, c1, c2, c3);
+    *reinterpret_cast<uint16_t*>(scales + row * scales_stride + part * 2) = (uint16_t)(s0 | (s1 << 8));
+  }
+}
+
+// Two E2M1 nibbles of a byte -> two fp32 values, exact.  Bit form of an E2M1
+// magnitude m: m = 0 -> 0, m = 1 -> 0.5, m >= 2 -> exponent (m >> 1) - 1 and
+// mantissa bit (m & 1), i.e. fp32 bits (m + 252) << 22.
+__device__ __forceinline__ float e2m1_to_f32(uint32_t nib) {
+  uint32_t mag = nib & 7u;
+  uint32_t b = (mag + 252u) << 22;
+  b = mag >= 2u ? b : (mag ? 0x3F000000u : 0u);
+  return __uint_as_float(b | ((nib & 8u) << 28));
+}
+
+__global__ void __launch_bounds__(256)
+fp4_unpack_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t n_rows,
+                  int parts_per_row, int C, uint16_t* __restrict__ x) {
+  const int64_t total = n_rows * parts_per_row;
+  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
+       g += (int64_t)gridDim.x * blockDim.x) {
+    int64_t row = g / parts_per_row;
+    int part = (int)(g - row * parts_per_row);
+    uint4 c = ld_nt16(codes + row * (C / 2) + part * 16);
+    uint32_t sc = *reinterpret_cast<const uint16_t*>(scales + row * (C / 16) + part * 2);
+    float s0 = e4m3_to_f32(sc & 0xFFu), s1 = e4m3_to_f32(sc >> 8);
+    uint32_t cw[4] = {c.x, c.y, c.z, c.w};
+    uint32_t out[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float s = i < 2 ? s0 : s1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t byte = (cw[i] >> (8 * j)) & 0xFFu;
+        float a = e2m1_to_f32(byte & 0xFu) * s;      // exact: <= 6 significant bits
+        float b = e2m1_to_f32(byte >> 4) * s;
+        out[i * 4 + j] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+      }
+    }
+    uint4* dst = reinterpret_cast<uint4*>(x + row * C + part * 32);
+    st_nt16(dst + 0, make_uint4(out[0], out[1], out[2], out[3]));
+    st_nt16(dst + 1, make_uint4(out[4], out[5], out[6], out[7]));
+    st_nt16(dst + 2, make_uint4(out[8], out[9], out[10], out[11]));
+    st_nt16(dst + 3, make_uint4(out[12], out[13], out[14], out[15]));
+  }
+}
+
+static int stream_grid(int64_t total_threads) {
+  int64_t blocks = (total_threads + 255) / 256;
+  const int64_t cap = 256 * 16;               // 16 workgroups per CU, grid-stride beyond
+  return (int)(blocks < cap ? (blocks > 0 ? blocks : 1) : cap);
+}
+
+}  // namespace csa2
+
+using namespace csa2;
+
+extern "C" csa2_status csa2_fp4_pack(const uint16_t* x, int64_t n_rows, int32_t C, int64_t x_row_stride,
+                                     uint8_t* codes, int64_t codes_row_stride, uint8_t* scales,
+                                     int64_t scales_row_stride, void* stream) {
+  if (n_rows < 0) return CSA2_EINVAL;
+  if (C <= 0 || C % 32 != 0) return CSA2_ESHAPE;
+  if (x_row_stride < C || x_row_stride % 8 != 0) return CSA2_EINVAL;
+  if (codes_row_stride < C / 2 || codes_row_stride % 16 != 0) return CSA2_EINVAL;
+  if (scales_row_stride < C / 16 || scales_row_stride % 2 != 0) return CSA2_EINVAL;
+  if (n_rows == 0) return CSA2_OK;
+  if (!x || !codes || !scales) return CSA2_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2)) return CSA2_EALIGN;
+  int parts = C / 32;
+  fp4_pack_kernel<<<stream_grid(n_rows * parts), 256, 0, (hipStream_t)stream>>>(
+      x, n_rows, parts, x_row_stride, codes, codes_row_stride, scales, scales_row_stride);
+  return launch_status();
+}
+
+extern "C" csa2_status csa2_fp4_unpack(const uint8_t* codes, const uint8_t* scales, int64_t n_rows, int32_t C,
+                                       uint16_t* x, void* stream) {
+  if (n_rows < 0) return CSA2_EINVAL;
+  if (C <= 0 || C % 32 != 0) return CSA2_ESHAPE;
+  if (n_rows == 0) return CSA2_OK;
+  if (!x || !codes || !scales) return CSA2_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2)) return CSA2_EALIGN;
+  int parts = C / 32;
+  fp4_unpack_kernel<<<stream_grid(n_rows * parts), 256, 0, (hipStream_t)stream>>>(
+      codes, scales, n_rows, parts, C, x);
+  return launch_status();
+}

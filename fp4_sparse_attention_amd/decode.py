@@ -1,0 +1,137 @@
+"""Composition of the libcsa2 calls into CSA2 decode layers.
+
+The MarkTechPost retelling of DeepSeek-V4.1-Flash (paragraph on CSA2) gives
+each layer a Full, Reindex or Reuse role: a Full layer builds fresh indices
+and, in the decoder, a candidate pool of up to 16,384 positions; a Reindex
+layer rescores that pool with its own indexer query; a Reuse layer takes the
+previous layer's Top-K indices.  Every layer then attends sparsely over the
+shared FP4 latent cache and merges a 128-token sliding window of its own
+(paragraph 2; the HN summary's key points).
+
+This module only allocates buffers and sequences the C calls on one stream;
+every arithmetic step runs in the HIP kernels of libcsa2.
+"""
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+import torch
+
+from . import (csa2_fp4_pack, csa2_index_full, csa2_index_reindex, csa2_topk, csa2_topk_workspace_size,
+               csa2_sparse_decode, csa2_sparse_decode_workspace_size, csa2_swa_merge,
+               csa2_swa_merge_workspace_size)
+
+LATENT = 512
+POOL_MAX = 16384
+
+
+def pack_cache(codes: torch.Tensor, scales: torch.Tensor, latent_chunk, chunk_rows: int, stream=None):
+    """Fill an FP4 cache codes [B, T, 256] / scales [B, T, 32] from bf16 latent rows.
+
+    latent_chunk(b, c) returns bf16 [rows, 512] for rows [c*chunk_rows, ...) of
+    sequence b (fewer rows for the last chunk).
+    """
+    B, T, _ = codes.shape
+    n_chunks = (T + chunk_rows - 1) // chunk_rows
+    for b in range(B):
+        for c in range(n_chunks):
+            x = latent_chunk(b, c)
+            r0 = c * chunk_rows
+            n = x.shape[0]
+            csa2_fp4_pack(x, codes[b, r0:r0 + n], scales[b, r0:r0 + n], stream=stream)
+
+
+@dataclass
+class LayerIO:
+    """Per-layer inputs: latent queries, indexer query, sliding-window state."""
+    q_lat: torch.Tensor          # bf16 [B, H, 512]
+    q_idx: torch.Tensor          # uint8 [B, 64]
+    swa: torch.Tensor            # bf16 [B, S, 512]
+    swa_start: torch.Tensor      # int32 [B]
+    swa_len: torch.Tensor        # int32 [B]
+
+
+class Csa2DecodeStack:
+    """Preallocated buffers and the call sequence of one decode step.
+
+    modes: e.g. ("full",) or ("full", "reindex", "reuse", "reuse").  A pool of
+    min(POOL_MAX, T) candidates is built by the Full layer only when a
+    Reindex layer follows it.
+    """
+
+    def __init__(self, B: int, T: int, H: int, K: int, modes: Sequence[str], device="cuda",
+                 pool_size: int = POOL_MAX):
+        self.B, self.T, self.H, self.K = B, T, H, K
+        self.modes = tuple(modes)
+        self.use_pool = "reindex" in self.modes
+        self.P = min(pool_size, T) if self.use_pool else 0
+        self.P = (self.P + 3) // 4 * 4
+        dev = torch.device(device)
+        f32, i32, u8 = torch.float32, torch.int32, torch.uint8
+        self.scores = torch.empty((B, T), dtype=f32, device=dev)
+        self.L = len(self.modes)
+        self.idx = torch.empty((self.L, B, K), dtype=i32, device=dev)
+        if self.use_pool:
+            self.pool = torch.empty((B, self.P), dtype=i32, device=dev)
+            self.pool_scores = torch.empty((B, self.P), dtype=f32, device=dev)
+            self.re_scores = torch.empty((B, self.P), dtype=f32, device=dev)
+        self.o = torch.empty((self.L, B, H, LATENT), dtype=f32, device=dev)
+        self.lse = torch.empty((self.L, B, H), dtype=f32, device=dev)
+        self.ws_topk_full = torch.empty(csa2_topk_workspace_size(B, T, max(K, self.P)), dtype=u8, device=dev)
+        self.ws_topk_pool = (torch.empty(csa2_topk_workspace_size(B, self.P, K), dtype=u8, device=dev)
+                             if self.use_pool else None)
+        self.ws_sparse = torch.empty(csa2_sparse_decode_workspace_size(B, H, K), dtype=u8, device=dev)
+        self.ws_swa = torch.empty(csa2_swa_merge_workspace_size(B, H), dtype=u8, device=dev)
+        self.index_events = None
+
+    def step(self, codes, scales, k_idx, layers: List[LayerIO], sigma: float, new_rows: Optional[torch.Tensor] = None,
+             stream=None, time_index: bool = False):
+        """Run every layer once.  new_rows (bf16 [B, 512]), if given, is packed
+        into position T-1 of each sequence first (the current token).
+
+        time_index: record HIP events around the Full-layer index call on the
+        stream (self.index_events holds the (start, end) pair)."""
+        B, T, K = self.B, self.T, self.K
+        if new_rows is not None:
+            csa2_fp4_pack(new_rows, codes[:, T - 1, :], scales[:, T - 1, :], stream=stream)
+        prev_idx = None
+        for li, (mode, io) in enumerate(zip(self.modes, layers)):
+            idx = self.idx[li]
+            if mode == "full":
+                if time_index:
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                csa2_index_full(io.q_idx, k_idx, self.scores, stream=stream)
+                if time_index:
+                    e1.record()
+                    self.index_events = (e0, e1)
+                if self.use_pool:
+                    csa2_topk(self.scores, self.P, self.pool, score_out=self.pool_scores,
+                              workspace=self.ws_topk_full, stream=stream)
+                    csa2_topk(self.pool_scores, K, idx, index_map=self.pool, workspace=self.ws_topk_pool,
+                              stream=stream)
+                else:
+                    csa2_topk(self.scores, K, idx, workspace=self.ws_topk_full, stream=stream)
+                prev_idx = idx
+            elif mode == "reindex":
+                csa2_index_reindex(io.q_idx, k_idx, self.pool, self.re_scores, stream=stream)
+                csa2_topk(self.re_scores, K, idx, index_map=self.pool, workspace=self.ws_topk_pool, stream=stream)
+                prev_idx = idx
+            elif mode == "reuse":
+                if prev_idx is None:
+                    raise ValueError("a Reuse layer needs a preceding Full or Reindex layer")
+                idx = prev_idx
+            else:
+                raise ValueError(mode)
+            csa2_sparse_decode(io.q_lat, codes, scales, idx, sigma, self.o[li], self.lse[li],
+                               workspace=self.ws_sparse, stream=stream)
+            csa2_swa_merge(io.q_lat, io.swa, io.swa_start, io.swa_len, sigma, self.o[li], self.lse[li],
+                           o_sparse=self.o[li], lse_sparse=self.lse[li], workspace=self.ws_swa, stream=stream)
+        return self.o, self.lse
+
+    def layer_idx(self, li: int) -> torch.Tensor:
+        """Indices used by layer li (a Reuse layer reports the indices it took)."""
+        j = li
+        while self.modes[j] == "reuse":
+            j -= 1
+        return self.idx[j]

@@ -1,0 +1,225 @@
+/*
+ * csa2.h -- C ABI of the CSA2 FP4 sparse-attention decode library (libcsa2.so).
+ *
+ * The library implements, for one MI355X (gfx950) GPU, the decode-time hot path
+ * of CSA2 compressed sparse attention over an FP4 global KV cache as the
+ * DeepSeek-V4.1-Flash write-ups describe it:
+ *   - "DeepSeek AI Released DeepSeek-V4.1-Flash with 1M Context, FP4 KV Cache,
+ *     and Cross-Layer Attention Reuse" (MarkTechPost retelling): paragraph 2
+ *     (sliding-window attention in every layer, 128-token window), paragraph 3
+ *     (Full / Reindex / Reuse layer roles, candidate pool of up to 16,384
+ *     positions), paragraph 4 (main KV cache in E2M1 with one E4M3 scale per 16
+ *     channels, NVFP4 without the global scale);
+ *   - "DeepSeek-v4.1 Flash: Pushing the Limits of KV Cache Compression"
+ *     (hackernews.kjhq.dev summary), key points: local sliding window plus
+ *     global sparse retrieval plus cross-layer reuse of the main KV and Top-K
+ *     indices; a shallow-layer candidate pool bounds the deeper layers' search.
+ *
+ * A decode layer is composed by the caller:
+ *   Full     csa2_index_full -> csa2_topk [-> pool: csa2_topk over the pool]
+ *            -> csa2_sparse_decode -> csa2_swa_merge
+ *   Reindex  csa2_index_reindex(pool) -> csa2_topk(index_map = pool)
+ *            -> csa2_sparse_decode -> csa2_swa_merge
+ *   Reuse    csa2_sparse_decode with the previous layer's indices -> csa2_swa_merge
+ *
+ * Conventions shared by every call:
+ *   - Every tensor argument is a DEVICE pointer allocated and owned by the
+ *     caller.  The library never allocates, frees or retains caller memory.
+ *     Calls that need scratch memory take a caller-provided `workspace` whose
+ *     size comes from the matching *_workspace_size() query.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on that stream and returns without synchronising.  The
+ *     library launches no memset/memcpy nodes, so calls may be captured into a
+ *     HIP graph.
+ *   - Every call checks its arguments on the host first.  On an argument error
+ *     it returns a non-zero status before launching anything and leaves the
+ *     outputs untouched.  CSA2_ELAUNCH reports a failed launch; device faults
+ *     surface at the caller's next synchronisation.
+ *   - Indices are int32 (positions < 2^31); lse values are natural logarithms.
+ *   - bf16 tensors are passed as uint16_t bit patterns, E4M3 as uint8_t.
+ *   - Unless stated otherwise, every pointer must be 16-byte aligned and every
+ *     row-major tensor is dense.
+ *   - Formats: E2M1 = OCP FP4 (1 sign, 2 exponent bits, 1 mantissa bit;
+ *     magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6); E4M3 = OCP FP8 E4M3FN (bias 7,
+ *     max 448, 0x7F/0xFF NaN).
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t csa2_status;
+enum {
+  CSA2_OK = 0,
+  CSA2_EINVAL = 1,     /* null pointer, non-positive size, bad value            */
+  CSA2_ESHAPE = 2,     /* a dimension outside what the kernels support          */
+  CSA2_EALIGN = 3,     /* a pointer or stride without the required alignment    */
+  CSA2_EWORKSPACE = 4, /* workspace pointer NULL or smaller than required       */
+  CSA2_ELAUNCH = 5     /* hipGetLastError() reported a failure after a launch  */
+};
+
+/* Version of this ABI (incremented on any incompatible change). */
+int32_t csa2_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* csa2_status_str(csa2_status status);
+
+/* ---------------------------------------------------------------------------
+ * FP4 pack: latent KV rows -> E2M1 codes + one E4M3 scale per 16 channels.
+ * (MarkTechPost retelling, paragraph 4: NVFP4 layout without the global scale.)
+ *
+ * For each row and each block of 16 channels [16b, 16b+16):
+ *   scale = E4M3 value nearest to amax/6 (amax = largest |x| in the block),
+ *           ties to the even code, values above 448 saturate to 448;
+ *   code  = E2M1 value nearest to x/scale, ties to the even code, clamped at
+ *           +-6, sign bit copied from x; a zero scale gives magnitude 0.
+ * Byte j of a packed row holds channel 2j in its low nibble, 2j+1 in its high
+ * nibble.  Scale byte b of a row covers channels [16b, 16b+16).
+ *
+ *   x        bf16 [n_rows][C] with row stride x_row_stride elements
+ *            (x_row_stride >= C, multiple of 8)
+ *   codes    uint8 [n_rows][C/2], row stride codes_row_stride bytes
+ *            (>= C/2, multiple of 16)
+ *   scales   uint8 [n_rows][C/16], row stride scales_row_stride bytes
+ *            (>= C/16, even)
+ *   C        channels, a positive multiple of 32
+ * The strided outputs let a decode step write its new rows straight into the
+ * cache at position T-1 of every sequence (stride T * C/2 bytes).
+ * Errors: EINVAL (null pointer, n_rows < 0, bad stride), ESHAPE (C), EALIGN.
+ * n_rows == 0 is a no-op.
+ * ------------------------------------------------------------------------- */
+csa2_status csa2_fp4_pack(const uint16_t* x, int64_t n_rows, int32_t C, int64_t x_row_stride,
+                          uint8_t* codes, int64_t codes_row_stride,
+                          uint8_t* scales, int64_t scales_row_stride, void* stream);
+
+/* FP4 unpack: x[r][c] = E2M1(code) * E4M3(scale) as bf16 (always exact).
+ *   codes uint8 [n_rows][C/2], scales uint8 [n_rows][C/16] (dense), x bf16
+ *   [n_rows][C] (dense).  Same errors as csa2_fp4_pack. */
+csa2_status csa2_fp4_unpack(const uint8_t* codes, const uint8_t* scales, int64_t n_rows, int32_t C,
+                            uint16_t* x, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Full-mode indexer scores (MarkTechPost retelling, paragraph 3: a Full layer
+ * builds fresh indices over the context).
+ *
+ *   scores[r][j] = sum_{d<64} q_idx[r][d] * k_idx[seq(r)][j][d]   (fp32)
+ * for every position j <= row_limit[r]; later positions get -inf.
+ *
+ *   q_idx      E4M3 [R][64]
+ *   k_idx      E4M3 [B][T][64], shared by all layers
+ *   row_seq    int32 [R] sequence of each query row, or NULL for row r -> r
+ *              (then R must equal B)
+ *   row_limit  int64 [R] last visible position of each row (causal prefill),
+ *              or NULL for all T positions
+ *   scores     fp32 [R][T]
+ * Products of E4M3 values are exact in fp32; the 64-term sum is accumulated in
+ * fp32 by the matrix cores.
+ * Errors: EINVAL (null pointer, R/B/T <= 0, R != B without row_seq), ESHAPE
+ * (T not a multiple of 4, T >= 2^31), EALIGN.
+ * ------------------------------------------------------------------------- */
+csa2_status csa2_index_full(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int32_t B, int64_t T,
+                            const int32_t* row_seq, const int64_t* row_limit, float* scores,
+                            void* stream);
+
+/* Reindex-mode scores (MarkTechPost retelling, paragraph 3: a Reindex layer
+ * rescores the shared candidate set; HN summary key points: the deeper layers'
+ * cost is bounded by the pool, not the context).
+ *
+ *   scores[r][p] = q_idx[r] . k_idx[seq(r)][pool[r][p]]  (same arithmetic as
+ *   csa2_index_full), and -inf where pool[r][p] < 0 or >= T.
+ *   pool int32 [R][P]; scores fp32 [R][P].  P must be a multiple of 4.
+ * Errors as csa2_index_full. */
+csa2_status csa2_index_reindex(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int32_t B, int64_t T,
+                               const int32_t* row_seq, const int32_t* pool, int32_t P, float* scores,
+                               void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Top-K selection (HN summary key points: layers share the same Top-K indices;
+ * MarkTechPost paragraph 3: the Full layer's candidate pool of up to 16,384).
+ *
+ * For each row r: the k_eff = min(k, visible) slots with the largest scores,
+ * equal scores going to the lower slot, listed in ascending slot order and
+ * padded with -1 up to k.  A slot is visible when its score is not -inf/NaN
+ * and (with index_map) its index_map entry is >= 0.
+ *
+ *   scores     fp32 [R][N], row stride row_stride elements (>= N, multiple of 4)
+ *   index_map  int32 [R][N] or NULL; with a map the outputs are index_map
+ *              values (positions) instead of slots.  With an ascending map,
+ *              "lower slot" is "lower position".
+ *   idx_out    int32 [R][k]
+ *   score_out  fp32 [R][k] or NULL: the selected scores, NaN in padded slots
+ *   workspace  >= csa2_topk_workspace_size(R, N, k) bytes, 256-byte aligned
+ * Errors: EINVAL (null, R/N/k <= 0), ESHAPE (N % 4, N >= 2^31), EWORKSPACE.
+ * ------------------------------------------------------------------------- */
+size_t csa2_topk_workspace_size(int32_t R, int64_t N, int32_t k);
+csa2_status csa2_topk(const float* scores, int32_t R, int64_t N, int64_t row_stride, int32_t k,
+                      const int32_t* index_map, int32_t* idx_out, float* score_out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Sparse attention over the FP4 cache (HN summary key points: global sparse
+ * retrieval over the shared main KV).
+ *
+ * For each row r and head h, over the valid entries j of idx[r] (0 <= j < T):
+ *   xhat_j = dequantised FP4 row j of sequence seq(r) (512 channels)
+ *   s_j    = softmax_scale * (q_lat[r][h] . xhat_j)
+ *   o[r][h]   = sum_j exp(s_j) xhat_j / sum_j exp(s_j)
+ *   lse[r][h] = log(sum_j exp(s_j))        (-inf and o = 0 with no valid j)
+ * Every head uses the same latent row as key and value (absorbed multi-head
+ * latent attention); queries come in absorbed form.
+ *
+ *   q_lat   bf16 [R][H][512]
+ *   codes   uint8 [B][T][256], scales uint8 [B][T][32]   (csa2_fp4_pack layout)
+ *   row_seq int32 [R] or NULL (row r -> sequence r, R == B)
+ *   idx     int32 [R][K]; entries < 0 or >= T are skipped
+ *   o       fp32 [R][H][512];  lse fp32 [R][H]
+ *   H       16, 32, 48 or 64
+ *   workspace >= csa2_sparse_decode_workspace_size(R, H, K) bytes
+ * Errors: EINVAL, ESHAPE (H), EWORKSPACE, EALIGN.
+ * ------------------------------------------------------------------------- */
+size_t csa2_sparse_decode_workspace_size(int32_t R, int32_t H, int32_t K);
+csa2_status csa2_sparse_decode(const uint16_t* q_lat, int32_t R, int32_t H,
+                               const uint8_t* codes, const uint8_t* scales, int32_t B, int64_t T,
+                               const int32_t* row_seq, const int32_t* idx, int32_t K,
+                               float softmax_scale, float* o, float* lse,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Sliding-window attention and merge (MarkTechPost retelling, paragraph 2:
+ * sliding-window attention runs in every layer over the last 128 tokens;
+ * fanout.sh lesson, "What you will learn": the window state is layer-local).
+ *
+ * For each row r: attention (same formula as csa2_sparse_decode) over the
+ * layer's own bf16 rows swa[seq(r)][swa_start[r] + i], i < swa_len[r]
+ * (swa_len <= 128), then one softmax over the union with the sparse result:
+ *   lse = log(exp(lse_sparse) + exp(lse_window))
+ *   o   = exp(lse_sparse - lse) o_sparse + exp(lse_window - lse) o_window
+ *
+ *   swa        bf16 [B][S][512]
+ *   swa_start  int32 [R], swa_len int32 [R]  (0 <= start, start + len <= S,
+ *              0 <= len <= 128; checked on the device: out-of-range rows are
+ *              skipped)
+ *   o_sparse   fp32 [R][H][512] and lse_sparse fp32 [R][H]: the
+ *              csa2_sparse_decode result, or both NULL for no sparse part
+ *   o_out      fp32 [R][H][512] (may be the same buffer as o_sparse)
+ *   lse_out    fp32 [R][H] or NULL (may be the same buffer as lse_sparse)
+ *   workspace  >= csa2_swa_merge_workspace_size(R, H) bytes
+ * Errors: EINVAL, ESHAPE (H, S), EWORKSPACE, EALIGN.
+ * ------------------------------------------------------------------------- */
+size_t csa2_swa_merge_workspace_size(int32_t R, int32_t H);
+csa2_status csa2_swa_merge(const uint16_t* q_lat, int32_t R, int32_t H,
+                           const uint16_t* swa, int32_t B, int32_t S, const int32_t* row_seq,
+                           const int32_t* swa_start, const int32_t* swa_len, float softmax_scale,
+                           const float* o_sparse, const float* lse_sparse,
+                           float* o_out, float* lse_out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA2_H */

@@ -1,0 +1,102 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp4_sparse_attention_amd as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _header_functions():
+    src = open(os.path.join(ROOT, "include", "csa2.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_functions_all_exported_and_bound():
+    names = _header_functions()
+    assert len(names) >= 12
+    L = F.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(F.exported_symbols()) == names
+
+
+def test_version_and_status_strings():
+    assert F.csa2_abi_version() == 1
+    L = F.lib()
+    for s in range(6):
+        assert L.csa2_status_str(s)
+    assert b"unknown" in L.csa2_status_str(99)
+
+
+NULL = None
+DUMMY = ctypes.c_void_p(256)     # never dereferenced: every call below fails its host checks first
+
+
+def test_pack_argument_errors():
+    L = F.lib()
+    assert L.csa2_fp4_pack(DUMMY, -1, 512, 512, DUMMY, 256, DUMMY, 32, NULL) == 1
+    assert L.csa2_fp4_pack(DUMMY, 4, 500, 512, DUMMY, 256, DUMMY, 32, NULL) == 2
+    assert L.csa2_fp4_pack(DUMMY, 4, 512, 100, DUMMY, 256, DUMMY, 32, NULL) == 1
+    assert L.csa2_fp4_pack(DUMMY, 4, 512, 512, DUMMY, 100, DUMMY, 32, NULL) == 1
+    assert L.csa2_fp4_pack(NULL, 4, 512, 512, DUMMY, 256, DUMMY, 32, NULL) == 1
+    assert L.csa2_fp4_pack(ctypes.c_void_p(258), 4, 512, 512, DUMMY, 256, DUMMY, 32, NULL) == 3
+    assert L.csa2_fp4_pack(DUMMY, 0, 512, 512, DUMMY, 256, DUMMY, 32, NULL) == 0      # empty: no-op
+    assert L.csa2_fp4_unpack(DUMMY, DUMMY, 4, 48, DUMMY, NULL) == 2
+    assert L.csa2_fp4_unpack(NULL, DUMMY, 4, 512, DUMMY, NULL) == 1
+
+
+def test_index_argument_errors():
+    L = F.lib()
+    assert L.csa2_index_full(NULL, DUMMY, 1, 1, 64, NULL, NULL, DUMMY, NULL) == 1
+    assert L.csa2_index_full(DUMMY, DUMMY, 2, 1, 64, NULL, NULL, DUMMY, NULL) == 1   # R != B, no row_seq
+    assert L.csa2_index_full(DUMMY, DUMMY, 1, 1, 66, NULL, NULL, DUMMY, NULL) == 2   # T % 4
+    assert L.csa2_index_full(DUMMY, DUMMY, 1, 1, 0, NULL, NULL, DUMMY, NULL) == 1
+    assert L.csa2_index_reindex(DUMMY, DUMMY, 1, 1, 64, NULL, DUMMY, 6, DUMMY, NULL) == 2
+    assert L.csa2_index_reindex(DUMMY, DUMMY, 1, 1, 64, NULL, NULL, 8, DUMMY, NULL) == 1
+
+
+def test_topk_argument_errors_and_workspace():
+    L = F.lib()
+    ws = F.csa2_topk_workspace_size(8, 1 << 20, 2048)
+    assert ws >= 8 * 2048 * 4
+    assert F.csa2_topk_workspace_size(0, 10, 1) == 0
+    assert L.csa2_topk(DUMMY, 1, 64, 64, 0, NULL, DUMMY, NULL, DUMMY, 1 << 20, NULL) == 1
+    assert L.csa2_topk(DUMMY, 1, 62, 64, 8, NULL, DUMMY, NULL, DUMMY, 1 << 20, NULL) == 2
+    assert L.csa2_topk(DUMMY, 1, 64, 60, 8, NULL, DUMMY, NULL, DUMMY, 1 << 20, NULL) == 1
+    assert L.csa2_topk(DUMMY, 1, 64, 64, 8, NULL, DUMMY, NULL, DUMMY, 16, NULL) == 4
+    assert L.csa2_topk(DUMMY, 1, 64, 64, 8, NULL, DUMMY, NULL, NULL, 1 << 20, NULL) == 4
+
+
+def test_attention_argument_errors_and_workspace():
+    L = F.lib()
+    assert F.csa2_sparse_decode_workspace_size(64, 64, 2048) > 64 * 64 * 512 * 4
+    assert F.csa2_swa_merge_workspace_size(8, 64) >= 8 * 4 * 64 * 512 * 4
+    args = [DUMMY, 1, 64, DUMMY, DUMMY, 1, 4096, NULL, DUMMY, 256, 0.1, DUMMY, DUMMY, DUMMY, 1 << 30, NULL]
+    bad_h = list(args); bad_h[2] = 20
+    assert L.csa2_sparse_decode(*bad_h) == 2
+    bad_k = list(args); bad_k[9] = 0
+    assert L.csa2_sparse_decode(*bad_k) == 1
+    small_ws = list(args); small_ws[14] = 100
+    assert L.csa2_sparse_decode(*small_ws) == 4
+    no_seq = list(args); no_seq[1] = 2
+    assert L.csa2_sparse_decode(*no_seq) == 1
+    sargs = [DUMMY, 1, 64, DUMMY, 1, 128, NULL, DUMMY, DUMMY, 0.1, DUMMY, NULL, DUMMY, NULL, DUMMY, 1 << 30, NULL]
+    assert L.csa2_swa_merge(*sargs) == 1          # o_sparse without lse_sparse
+    sargs[10] = NULL
+    sargs[1] = 1
+    sargs[2] = 8
+    assert L.csa2_swa_merge(*sargs) == 2          # H = 8
+
+
+def test_no_cpu_fallback_in_binding():
+    # the binding refuses CPU tensors instead of computing anything itself
+    import torch
+    x = torch.zeros((4, 512), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        F.csa2_fp4_pack(x, torch.zeros((4, 256), dtype=torch.uint8), torch.zeros((4, 32), dtype=torch.uint8))

@@ -1,0 +1,150 @@
+"""GPU parity: sparse attention over the FP4 cache and the sliding-window merge vs the oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import formats as OF, attention as OA
+import fp4_sparse_attention_amd as F
+from gpu_common import device, np_u8, bf16_to_f64, assert_attention_close
+
+pytestmark = pytest.mark.gpu
+SIGMA = 1.0 / math.sqrt(128)
+
+
+def _cache(B, T, seed):
+    lat = torch.stack([W.latent_rows(seed, T, chunk_index=b) for b in range(B)])      # bf16 [B,T,512] cpu
+    codes, scales = [], []
+    for b in range(B):
+        c, s = OF.fp4_pack(lat[b].to(torch.float64).numpy())      # oracle side
+        codes.append(c); scales.append(s)
+    ref_rows = [OF.fp4_unpack(codes[b], scales[b]) for b in range(B)]
+    return lat, ref_rows
+
+
+def _gpu_cache(lat, dev):
+    B, T, _ = lat.shape
+    codes = torch.empty((B, T, 256), dtype=torch.uint8, device=dev)
+    scales = torch.empty((B, T, 32), dtype=torch.uint8, device=dev)
+    x = lat.to(dev)
+    for b in range(B):
+        F.csa2_fp4_pack(x[b], codes[b], scales[b])
+    return codes, scales
+
+
+@pytest.mark.parametrize("B,T,H,K", [(1, 4096, 16, 256), (2, 1000, 64, 300), (3, 700, 32, 33),
+                                     (1, 300, 48, 512), (2, 5000, 64, 2048)])
+def test_sparse_decode_vs_oracle(B, T, H, K):
+    dev = device()
+    rng = np.random.default_rng(B * 1000 + K)
+    lat, ref_rows = _cache(B, T, seed=21)
+    codes, scales = _gpu_cache(lat, dev)
+    q = W.bf16_normal(22, (B, H, 512), std=0.5)
+    idx = np.full((B, K), -1, dtype=np.int32)
+    for b in range(B):
+        n = min(K, T) - (b % 2) * 7                              # some -1 padding
+        idx[b, :n] = np.sort(rng.choice(T, n, replace=False))
+    if K > 40:
+        idx[0, 5] = T + 3                                        # out of range: skipped
+    o = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    F.csa2_sparse_decode(q.to(dev), codes, scales, torch.from_numpy(idx).to(dev), SIGMA, o, lse)
+    qf = q.to(torch.float64).numpy()
+    for b in range(B):
+        valid = idx[b][(idx[b] >= 0) & (idx[b] < T)]
+        o_ref, l_ref = OA.sparse_attend(qf[b], ref_rows[b], valid, SIGMA)
+        assert_attention_close(o[b].cpu().numpy(), lse[b].cpu().numpy(), o_ref, l_ref, f"row {b}")
+
+
+def test_sparse_decode_empty_rows_and_row_seq():
+    dev = device()
+    T, H = 500, 16
+    lat, ref_rows = _cache(2, T, seed=23)
+    codes, scales = _gpu_cache(lat, dev)
+    R, K = 4, 64
+    row_seq = np.array([1, 0, 1, 0], dtype=np.int32)
+    q = W.bf16_normal(24, (R, H, 512), std=0.5)
+    idx = np.full((R, K), -1, dtype=np.int32)
+    idx[0, :10] = np.arange(10) * 7
+    idx[2, :K] = np.arange(K) + 100                      # row 1 and row 3 stay empty
+    o = torch.empty((R, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((R, H), dtype=torch.float32, device=dev)
+    F.csa2_sparse_decode(q.to(dev), codes, scales, torch.from_numpy(idx).to(dev), SIGMA, o, lse,
+                         row_seq=torch.from_numpy(row_seq).to(dev))
+    qf = q.to(torch.float64).numpy()
+    for r in range(R):
+        o_ref, l_ref = OA.sparse_attend(qf[r], ref_rows[row_seq[r]], idx[r], SIGMA)
+        assert_attention_close(o[r].cpu().numpy(), lse[r].cpu().numpy(), o_ref, l_ref, f"row {r}")
+    assert torch.all(o[1] == 0) and torch.all(torch.isneginf(lse[1]))
+
+
+@pytest.mark.parametrize("with_sparse", [True, False])
+def test_swa_merge_vs_oracle(with_sparse):
+    dev = device()
+    B, H, S = 4, 64, 160
+    q = W.bf16_normal(25, (B, H, 512), std=0.5)
+    swa = W.bf16_normal(26, (B, S, 512))
+    start = np.array([0, 5, 32, 150], dtype=np.int32)
+    length = np.array([128, 1, 77, 0], dtype=np.int32)
+    qf = q.to(torch.float64).numpy()
+    swf = swa.to(torch.float64).numpy()
+    rng = np.random.default_rng(5)
+    o_s = rng.standard_normal((B, H, 512)).astype(np.float32)
+    l_s = (rng.standard_normal((B, H)) * 3).astype(np.float32)
+    l_s[2, :5] = -np.inf
+    o_s[2, :5] = 0
+    o_out = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
+    lse_out = torch.empty((B, H), dtype=torch.float32, device=dev)
+    kw = {}
+    if with_sparse:
+        kw = dict(o_sparse=torch.from_numpy(o_s).to(dev), lse_sparse=torch.from_numpy(l_s).to(dev))
+    F.csa2_swa_merge(q.to(dev), swa.to(dev), torch.from_numpy(start).to(dev), torch.from_numpy(length).to(dev),
+                     SIGMA, o_out, lse_out, **kw)
+    for b in range(B):
+        o_w, l_w = OA.attend(qf[b], OA.window_rows(swf[b], int(start[b]), int(length[b])), SIGMA)
+        if with_sparse:
+            o_ref, l_ref = OA.merge(o_s[b].astype(np.float64), l_s[b].astype(np.float64), o_w, l_w)
+        else:
+            o_ref, l_ref = o_w, l_w
+        assert_attention_close(o_out[b].cpu().numpy(), lse_out[b].cpu().numpy(), o_ref, l_ref, f"row {b}")
+
+
+def test_swa_merge_in_place_and_window_bound():
+    # o_out aliases o_sparse; rows outside the window do not change the result
+    dev = device()
+    B, H, S = 2, 32, 300
+    q = W.bf16_normal(27, (B, H, 512), std=0.5).to(dev)
+    swa = W.bf16_normal(28, (B, S, 512)).to(dev)
+    start = torch.tensor([172, 0], dtype=torch.int32, device=dev)
+    length = torch.tensor([128, 128], dtype=torch.int32, device=dev)
+    o1 = torch.randn((B, H, 512), device=dev)
+    l1 = torch.randn((B, H), device=dev)
+    o_keep, l_keep = o1.clone(), l1.clone()
+    F.csa2_swa_merge(q, swa, start, length, SIGMA, o1, l1, o_sparse=o1, lse_sparse=l1)
+    o2, l2 = o_keep.clone(), l_keep.clone()
+    swa2 = swa.clone()
+    swa2[0, :172] = torch.randn_like(swa2[0, :172]).to(torch.bfloat16) * 50
+    swa2[1, 128:] = 1000
+    F.csa2_swa_merge(q, swa2, start, length, SIGMA, o2, l2, o_sparse=o2, lse_sparse=l2)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o3 = torch.empty_like(o1); l3 = torch.empty_like(l1)
+    F.csa2_swa_merge(q, swa, start, length, SIGMA, o3, l3, o_sparse=o_keep, lse_sparse=l_keep)
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+
+
+def test_sparse_decode_deterministic():
+    dev = device()
+    T, H, K = 3000, 64, 2048
+    lat, _ = _cache(1, T, seed=29)
+    codes, scales = _gpu_cache(lat, dev)
+    q = W.bf16_normal(30, (1, H, 512), std=0.5).to(dev)
+    idx = torch.from_numpy(np.sort(np.random.default_rng(0).choice(T, K, replace=False)).astype(np.int32)[None]).to(dev)
+    outs = []
+    for _ in range(2):
+        o = torch.empty((1, H, 512), dtype=torch.float32, device=dev)
+        lse = torch.empty((1, H), dtype=torch.float32, device=dev)
+        F.csa2_sparse_decode(q, codes, scales, idx, SIGMA, o, lse)
+        outs.append((o, lse))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])

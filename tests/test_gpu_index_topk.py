@@ -1,0 +1,166 @@
+"""GPU parity: indexer scoring (Full / Reindex) and Top-K selection vs the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import indexer as OI, topk as OT, formats as OF
+import fp4_sparse_attention_amd as F
+from gpu_common import device, np_u8, assert_topk_swap_rule
+
+pytestmark = pytest.mark.gpu
+
+
+def _score_bound(q, k):
+    """fp32-accumulation bound per score: 64 * 2^-24 * sum |q_d k_d|."""
+    qa = np.abs(OF.e4m3_decode(q))
+    ka = np.abs(OF.e4m3_decode(k))
+    return (ka @ qa.T if qa.ndim == 2 else ka @ qa) * 64 * 2.0 ** -24
+
+
+@pytest.mark.parametrize("B,T", [(1, 4096), (3, 100), (2, 4), (1, 4100)])
+def test_index_full_scores(B, T):
+    dev = device()
+    k = torch.stack([W.fp8_normal(7, (T, 64), chunk_index=b) for b in range(B)])
+    q = W.fp8_normal(8, (B, 64))
+    scores = torch.empty((B, T), dtype=torch.float32, device=dev)
+    F.csa2_index_full(q.to(dev), k.to(dev), scores)
+    got = scores.cpu().numpy().astype(np.float64)
+    n_exact = 0
+    for b in range(B):
+        exact = OI.full_scores(q[b].numpy(), k[b].numpy())
+        bound = _score_bound(q[b].numpy(), k[b].numpy())
+        assert np.all(np.abs(got[b] - exact) <= bound + 1e-30), (b, np.max(np.abs(got[b] - exact)))
+        n_exact += int(np.sum(got[b] == exact.astype(np.float32)))
+    print(f"scores equal to the fp32 rounding of the exact value: {n_exact}/{B * T}")
+
+
+def test_index_full_causal_rows_and_row_seq():
+    # 70 query rows over 2 sequences: row r belongs to sequence r % 2 and sees positions <= limit[r]
+    dev = device()
+    T, R = 1000, 70
+    k = torch.stack([W.fp8_normal(9, (T, 64), chunk_index=b) for b in range(2)])
+    q = W.fp8_normal(10, (R, 64))
+    row_seq = torch.arange(R, dtype=torch.int32) % 2
+    limit = torch.from_numpy(np.random.default_rng(0).integers(-1, T + 5, R)).to(torch.int64)
+    scores = torch.empty((R, T), dtype=torch.float32, device=dev)
+    F.csa2_index_full(q.to(dev), k.to(dev), scores, row_seq=row_seq.to(dev), row_limit=limit.to(dev))
+    got = scores.cpu().numpy()
+    for r in range(R):
+        b = int(row_seq[r])
+        exact = OI.full_scores(q[r].numpy(), k[b].numpy(), limit=int(limit[r]))
+        fin = np.isfinite(exact)
+        assert np.array_equal(np.isneginf(got[r]), ~fin), r
+        bound = _score_bound(q[r].numpy(), k[b].numpy())[fin]
+        assert np.all(np.abs(got[r][fin] - exact[fin]) <= bound + 1e-30), r
+
+
+def test_index_prefill_block_rows_same_sequence():
+    # 64 causal query rows of one sequence (the chunked-prefill layout)
+    dev = device()
+    T, R = 2048, 64
+    k = W.fp8_normal(11, (1, T, 64))
+    q = W.fp8_normal(12, (R, 64))
+    row_seq = torch.zeros(R, dtype=torch.int32)
+    limit = torch.arange(T - R, T, dtype=torch.int64)
+    scores = torch.empty((R, T), dtype=torch.float32, device=dev)
+    F.csa2_index_full(q.to(dev), k.to(dev), scores, row_seq=row_seq.to(dev), row_limit=limit.to(dev))
+    got = scores.cpu().numpy()
+    for r in range(R):
+        exact = OI.full_scores(q[r].numpy(), k[0].numpy(), limit=int(limit[r]))
+        fin = np.isfinite(exact)
+        assert np.array_equal(np.isneginf(got[r]), ~fin)
+        assert np.all(np.abs(got[r][fin] - exact[fin]) <= _score_bound(q[r].numpy(), k[0].numpy())[fin] + 1e-30)
+
+
+def test_reindex_matches_full_bitwise_on_pool():
+    dev = device()
+    B, T, P = 3, 3000, 520
+    k = torch.stack([W.fp8_normal(13, (T, 64), chunk_index=b) for b in range(B)]).to(dev)
+    q = W.fp8_normal(14, (B, 64)).to(dev)
+    full = torch.empty((B, T), dtype=torch.float32, device=dev)
+    F.csa2_index_full(q, k, full)
+    rng = np.random.default_rng(1)
+    pool = np.stack([np.sort(rng.choice(T, P, replace=False)) for _ in range(B)]).astype(np.int32)
+    pool[:, -7:] = -1
+    pool[1, 3] = T + 5                      # out of range -> -inf
+    pt = torch.from_numpy(pool).to(dev)
+    re = torch.empty((B, P), dtype=torch.float32, device=dev)
+    F.csa2_index_reindex(q, k, pt, re)
+    got = re.cpu().numpy()
+    fullh = full.cpu().numpy()
+    for b in range(B):
+        for p in range(P):
+            pos = pool[b, p]
+            if 0 <= pos < T:
+                assert got[b, p] == fullh[b, pos]
+            else:
+                assert np.isneginf(got[b, p])
+
+
+def _synthetic_scores(rng, R, N, tie_frac=0.3, ninf_frac=0.05):
+    s = rng.standard_normal((R, N)).astype(np.float32) * 8
+    ties = rng.random((R, N)) < tie_frac
+    s[ties] = np.round(s[ties])                     # many exact ties
+    s[rng.random((R, N)) < ninf_frac] = -np.inf
+    s[rng.random((R, N)) < 0.01] = np.nan
+    return s
+
+
+@pytest.mark.parametrize("R,N,k", [(1, 4096, 256), (5, 1000, 64), (3, 12, 20), (2, 65536, 16384),
+                                   (4, 131072, 2048), (1, 8, 1)])
+def test_topk_bit_exact(R, N, k):
+    dev = device()
+    rng = np.random.default_rng(N + k)
+    s = _synthetic_scores(rng, R, N)
+    st = torch.from_numpy(s).to(dev)
+    idx = torch.empty((R, k), dtype=torch.int32, device=dev)
+    so = torch.empty((R, k), dtype=torch.float32, device=dev)
+    F.csa2_topk(st, k, idx, score_out=so)
+    gi, gs = idx.cpu().numpy(), so.cpu().numpy()
+    for r in range(R):
+        ri, rs = OT.topk_with_scores(s[r].astype(np.float64), k)
+        assert np.array_equal(gi[r], ri), r
+        assert np.array_equal(np.isnan(gs[r]), np.isnan(rs))
+        assert np.array_equal(gs[r][~np.isnan(rs)], rs[~np.isnan(rs)].astype(np.float32))
+
+
+def test_topk_all_invisible_and_strided_rows():
+    dev = device()
+    s = np.full((2, 64), -np.inf, dtype=np.float32)
+    s[1, 10] = 1.0
+    big = torch.full((2, 80), 5.0, dtype=torch.float32, device=dev)
+    big[:, :64] = torch.from_numpy(s).to(dev)
+    idx = torch.empty((2, 4), dtype=torch.int32, device=dev)
+    F.csa2_topk(big[:, :64], 4, idx)
+    assert idx.cpu().tolist() == [[-1, -1, -1, -1], [10, -1, -1, -1]]
+
+
+def test_topk_with_index_map_and_padding():
+    dev = device()
+    rng = np.random.default_rng(3)
+    R, N, k = 3, 4000, 300
+    s = _synthetic_scores(rng, R, N, tie_frac=0.5)
+    pos = np.stack([np.sort(rng.choice(10 ** 6, N, replace=False)) for _ in range(R)]).astype(np.int32)
+    pos[:, -50:] = -1
+    idx = torch.empty((R, k), dtype=torch.int32, device=dev)
+    F.csa2_topk(torch.from_numpy(s).to(dev), k, idx, index_map=torch.from_numpy(pos).to(dev))
+    gi = idx.cpu().numpy()
+    for r in range(R):
+        assert np.array_equal(gi[r], OT.topk(s[r].astype(np.float64), k, index_map=pos[r]))
+
+
+def test_full_scores_then_topk_swap_rule():
+    """Top-K of the GPU's fp32 scores vs Top-K of the exact scores (1e-6 swap rule)."""
+    dev = device()
+    B, T, K = 2, 20000, 256
+    k = torch.stack([W.fp8_normal(15, (T, 64), chunk_index=b) for b in range(B)])
+    q = W.fp8_normal(16, (B, 64))
+    scores = torch.empty((B, T), dtype=torch.float32, device=dev)
+    F.csa2_index_full(q.to(dev), k.to(dev), scores)
+    idx = torch.empty((B, K), dtype=torch.int32, device=dev)
+    F.csa2_topk(scores, K, idx)
+    for b in range(B):
+        exact = OI.full_scores(q[b].numpy(), k[b].numpy())
+        ref = OT.topk(exact, K)
+        assert_topk_swap_rule(idx[b].cpu().numpy(), ref, lambda p: exact[p], f"row {b}")

@@ -1,0 +1,95 @@
+"""GPU parity: FP4 pack / unpack (csa2_fp4_pack, csa2_fp4_unpack) vs the oracle, bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import formats as OF
+import fp4_sparse_attention_amd as F
+from gpu_common import device, np_u8, bf16_to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_pack(x):
+    n, C = x.shape
+    codes = torch.empty((n, C // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((n, C // 16), dtype=torch.uint8, device=x.device)
+    F.csa2_fp4_pack(x, codes, scales)
+    return codes, scales
+
+
+def _special_rows():
+    """bf16 rows with E2M1 ties, zero / negative-zero blocks, saturation and subnormal scales."""
+    rng = np.random.default_rng(0)
+    rows = []
+    s = OF.e4m3_decode(rng.integers(1, 127, 64))
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 0.0, 0.5, 1.0])
+    for i in range(64):
+        e = rng.choice(mids, 512) * rng.choice([-1.0, 1.0], 512)
+        e[::16] = 6.0
+        rows.append(e * s[i])
+    z = np.zeros(512); z[16:32] = -0.0; z[40] = 6 * 2.0 ** -10; z[64] = 4096.0; z[65] = -1e30
+    z[80] = 3e-5; z[96:112] = -1e-3 * np.arange(16)
+    rows.append(z)
+    x = np.stack(rows)
+    return torch.from_numpy(x).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("n_rows", [1, 3, 17, 4096])
+def test_pack_unpack_bit_exact_small(n_rows):
+    dev = device()
+    x = W.latent_rows(0, n_rows, device="cpu", chunk_index=n_rows)
+    codes, scales = _gpu_pack(x.to(dev))
+    rc, rs = OF.fp4_pack(x.to(torch.float64).numpy())
+    assert np.array_equal(np_u8(codes), rc) and np.array_equal(np_u8(scales), rs)
+    out = torch.empty((n_rows, 512), dtype=torch.bfloat16, device=dev)
+    F.csa2_fp4_unpack(codes, scales, out)
+    ref = OF.fp4_unpack(rc, rs)
+    got = bf16_to_f64(out)
+    assert np.array_equal(got, ref) and np.array_equal(np.signbit(got), np.signbit(ref))
+
+
+def test_pack_special_values_bit_exact():
+    dev = device()
+    x = _special_rows()
+    codes, scales = _gpu_pack(x.to(dev))
+    rc, rs = OF.fp4_pack(x.to(torch.float64).numpy())
+    assert np.array_equal(np_u8(scales), rs)
+    assert np.array_equal(np_u8(codes), rc)
+
+
+def test_pack_strided_into_cache_rows():
+    # the decode step writes one new row per sequence at position T-1 of the cache
+    dev = device()
+    B, T = 5, 40
+    cache_c = torch.zeros((B, T, 256), dtype=torch.uint8, device=dev)
+    cache_s = torch.zeros((B, T, 32), dtype=torch.uint8, device=dev)
+    src = W.latent_rows(1, 2 * B, device="cpu")
+    x = src.to(dev)[::2]                   # strided input rows
+    F.csa2_fp4_pack(x, cache_c[:, T - 1, :], cache_s[:, T - 1, :])
+    rc, rs = OF.fp4_pack(src[::2].to(torch.float64).numpy())
+    assert np.array_equal(np_u8(cache_c[:, T - 1]), rc) and np.array_equal(np_u8(cache_s[:, T - 1]), rs)
+    assert int(cache_c[:, :T - 1].abs().sum()) == 0 and int(cache_s[:, :T - 1].abs().sum()) == 0
+
+
+def test_pack_stream_1m_rows_sampled_and_round_trip():
+    """FP4 pack then unpack of 1,048,576 x 512 (the memory-bound stream workload):
+    sampled rows against the oracle, and pack(unpack(pack(x))) == pack(x) on every row."""
+    dev = device()
+    cfg = W.PackStream()
+    out = W.outlier_channels(cfg.seed)
+    x = W.latent_rows(cfg.seed, cfg.rows, device=dev, outliers=out)
+    codes, scales = _gpu_pack(x)
+    xb = torch.empty_like(x)
+    F.csa2_fp4_unpack(codes, scales, xb)
+    c2, s2 = _gpu_pack(xb)
+    assert torch.equal(c2, codes) and torch.equal(s2, scales)
+    rng = np.random.default_rng(cfg.seed)
+    rows = np.sort(rng.choice(cfg.rows, 2048, replace=False))
+    rows = np.concatenate([[0, cfg.rows - 1], rows])
+    rt = torch.from_numpy(rows).to(dev)
+    xs = x[rt].to(torch.float64).cpu().numpy()
+    rc, rs = OF.fp4_pack(xs)
+    assert np.array_equal(np_u8(codes[rt]), rc) and np.array_equal(np_u8(scales[rt]), rs)
+    assert np.array_equal(bf16_to_f64(xb[rt]), OF.fp4_unpack(rc, rs))
