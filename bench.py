@@ -190,9 +190,9 @@ class Workload:
         out = np.empty((positions.shape[0], 512))
         chunk = positions // self.chunk_rows
         for c in np.unique(chunk):
-            rows = self.latent_chunk(b, int(c)).to(torch.float64).cpu().numpy()
             sel = chunk == c
-            out[sel] = rows[positions[sel] - c * self.chunk_rows]
+            local = torch.from_numpy(positions[sel] - c * self.chunk_rows).to(self.dev)
+            out[sel] = self.latent_chunk(b, int(c))[local].to(torch.float64).cpu().numpy()
         return out
 
 
@@ -246,7 +246,7 @@ def bench_decode(args, cfg):
                      "launch_ms": idx_ms, "bytes_per_launch": idx_bytes},
     }
     if not args.no_cpu_baseline:
-        n_seq = args.cpu_sample or (1 if T >= (1 << 20) else 2)
+        n_seq = args.cpu_sample or (4 if T >= (1 << 20) else 8)
         rec["cpu_baseline"] = cpu_baseline_decode(wl, cfg, min(n_seq, B))
     else:
         rec["cpu_baseline"] = None

@@ -37,6 +37,10 @@ _SIGS = {
     "csa2_sparse_decode": (_i32, [_c_void_p, _i32, _i32, _c_void_p, _c_void_p, _i32, _i64, _c_void_p, _c_void_p,
                                   _i32, _f32, _c_void_p, _c_void_p, _c_void_p, _size_t, _c_void_p]),
     "csa2_swa_merge_workspace_size": (_size_t, [_i32, _i32]),
+    "csa2_sparse_swa_decode_workspace_size": (_size_t, [_i32, _i32, _i32]),
+    "csa2_sparse_swa_decode": (_i32, [_c_void_p, _i32, _i32, _c_void_p, _c_void_p, _i32, _i64, _c_void_p, _c_void_p,
+                                      _i32, _c_void_p, _i32, _c_void_p, _c_void_p, _f32, _c_void_p, _c_void_p,
+                                      _c_void_p, _size_t, _c_void_p]),
     "csa2_swa_merge": (_i32, [_c_void_p, _i32, _i32, _c_void_p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _f32,
                               _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t, _c_void_p]),
 }
@@ -265,3 +269,41 @@ def csa2_swa_merge(q_lat, swa, swa_start, swa_len, softmax_scale, o_out, lse_out
                               float(softmax_scale), _p(o_sparse), _p(lse_sparse), _p(o_out), _p(lse_out),
                               _p(workspace), workspace.numel(), _stream(stream))
     _check("csa2_swa_merge", st)
+
+
+def csa2_sparse_swa_decode_workspace_size(R, H, K):
+    return int(lib().csa2_sparse_swa_decode_workspace_size(R, H, K))
+
+
+def csa2_sparse_swa_decode(q_lat, codes, scales, idx, swa, swa_start, swa_len, softmax_scale, o, lse,
+                           row_seq=None, workspace=None, stream=None):
+    """Sparse attention over idx plus the window rows, one softmax: q_lat bf16 [R, H, 512];
+    codes/scales [B, T, 256/32]; idx int32 [R, K]; swa bf16 [B, S, 512]; swa_start/swa_len int32 [R];
+    o fp32 [R, H, 512]; lse fp32 [R, H]."""
+    _need(q_lat, torch.bfloat16, "q_lat", 3)
+    _need(codes, torch.uint8, "codes", 3)
+    _need(scales, torch.uint8, "scales", 3)
+    _need(idx, torch.int32, "idx", 2)
+    _need(swa, torch.bfloat16, "swa", 3)
+    _need(swa_start, torch.int32, "swa_start", 1)
+    _need(swa_len, torch.int32, "swa_len", 1)
+    _need(o, torch.float32, "o", 3)
+    _need(lse, torch.float32, "lse", 2)
+    for t, nm in ((q_lat, "q_lat"), (codes, "codes"), (scales, "scales"), (idx, "idx"), (swa, "swa"),
+                  (swa_start, "swa_start"), (swa_len, "swa_len"), (o, "o"), (lse, "lse")):
+        _dense(t, nm)
+    R, H, C = q_lat.shape
+    B, T, cb = codes.shape
+    K = idx.shape[1]
+    S = swa.shape[1]
+    if C != 512 or cb != 256 or swa.shape != (B, S, 512) or o.shape != (R, H, 512) or lse.shape != (R, H):
+        raise ValueError("sparse_swa_decode shapes")
+    if row_seq is not None:
+        _need(row_seq, torch.int32, "row_seq", 1)
+    need = csa2_sparse_swa_decode_workspace_size(R, H, K)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_lat.device)
+    st = lib().csa2_sparse_swa_decode(_p(q_lat), R, H, _p(codes), _p(scales), B, T, _p(row_seq), _p(idx), K,
+                                      _p(swa), S, _p(swa_start), _p(swa_len), float(softmax_scale), _p(o), _p(lse),
+                                      _p(workspace), workspace.numel(), _stream(stream))
+    _check("csa2_sparse_swa_decode", st)

@@ -6,23 +6,28 @@
 // Absorbed multi-head latent attention: every head of a row attends over the
 // same 512-channel latent rows, used as key and as value.
 //
-// Work split (split-K, "flash-decoding"): a workgroup owns one query row, a
-// chunk of key tiles and NW*16 heads (one wave per 16 heads).  Per 32-key tile:
-//   1. gather: each thread fetches 32 bytes of codes + 4 scale bytes of one
-//      key (16-byte loads), or 128 bytes of a bf16 window row, for the NEXT
-//      tile while the current one is computed;
-//   2. dequantise to fp16 (exact: E2M1 x E4M3 has <= 6 significant bits and
-//      lies in [2^-10, 2688]) into LDS twice: key-major Xs[key][channel] and
-//      channel-major Xt[channel][key];
-//   3. S^T[key][head] = X . Q^T on v_mfma_f32_16x16x32_f16 (A = Xs rows,
-//      B = the wave's queries held in registers as fp16);
-//   4. online softmax in the exp2 domain: each lane owns one head's column,
-//      so the row max / sum need two cross-lane steps;
-//   5. O^T[channel][head] += Xt . P^T on the same MFMA (A = Xt rows, B = P
-//      straight from the softmax registers), fp32 accumulators in VGPRs.
+// Work split (split-K): a workgroup of four waves owns one query row and one
+// chunk of keys (a run of 32-key tiles from idx, or the row's window rows), for
+// all H <= 64 heads.  Wave w owns latent channels [128w, 128w+128):
+//   1. gather: lane (m = l%16, g = l/16) loads 16 code bytes + 2 scale bytes
+//      (32 channels) of keys m and 16+m of the tile -- each FP4 element is
+//      fetched and dequantised by exactly one lane; the next tile's loads are
+//      in flight during the current tile's math;
+//   2. dequantise in registers (v_cvt_scalef32_pk_f16_fp4 with unit scale,
+//      times the E4M3 block scale in f16: exact, <= 6 significant bits in
+//      [2^-10, 2688]) straight into the A operands of
+//      v_mfma_f32_16x16x32_f16, and store the slice key-major in LDS;
+//   3. partial scores S^T[key][head] over the wave's 128 channels (B = the
+//      wave's slice of the queries, kept in registers);
+//   4. the four partials meet in LDS; wave w sums them for heads [16w, 16w+16)
+//      and runs the online softmax in the exp2 domain (one head per lane
+//      column, two cross-lane steps), publishing P (f16) and the rescale factors;
+//   5. O^T[channel][head] += X^T P^T for the wave's channels: the A operand is
+//      read from the key-major slice with ds_read_b64_tr_b16 (gfx950 LDS
+//      transpose load), B = P from LDS; fp32 accumulators stay in VGPRs.
 // The chunk's unnormalised O, running max m and sum l go to the workspace; a
-// combine kernel merges chunks (and, for the window call, the sparse result)
-// into o and lse.
+// combine kernel merges the chunks (and, for a window merge, the sparse
+// result) into o and lse.
 #include <type_traits>
 
 #include "common.hpp"
@@ -30,33 +35,26 @@
 namespace csa2 {
 
 constexpr int kKT = 32;                  // keys per tile
-constexpr int kXsStride = kLatent + 8;   // halfs per key row of Xs
-constexpr int kXtStride = kKT + 8;       // halfs per channel row of Xt
+constexpr int kXwStride = 144;           // halfs per key row of a wave's slice (128 + 16 pad)
+constexpr int kSStride = 36;             // floats per head row of a partial-score tile
+constexpr int kPStride = 40;             // halfs per head row of P
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma16(const f16x8& a, const f16x8& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// 8 E2M1 nibbles (one code dword, channel 2j in the low nibble of byte j) ->
-// 4 dwords of fp16 pairs, multiplied by the block scale (fp16 pair).
-// The fp16 high byte of each E2M1 magnitude {0,.5,1,1.5,2,3,4,6} is
-// {00,38,3C,3E,40,42,44,46} and its low byte is 0, so a byte permute does the
-// table lookup.
-__device__ __forceinline__ void fp4x8_to_f16(uint32_t d, f16x2 s2, uint32_t* out) {
-  const uint32_t lut_lo = 0x3E3C3800u, lut_hi = 0x46444240u;
-  uint32_t me = d & 0x07070707u;
-  uint32_t mo = (d >> 4) & 0x07070707u;
-  uint32_t he = __builtin_amdgcn_perm(lut_hi, lut_lo, me) | ((d << 4) & 0x80808080u);
-  uint32_t ho = __builtin_amdgcn_perm(lut_hi, lut_lo, mo) | (d & 0x80808080u);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    uint32_t sel = 0x0Cu | ((uint32_t)k << 8) | (0x0Cu << 16) | ((uint32_t)(4 + k) << 24);
-    uint32_t v = __builtin_amdgcn_perm(ho, he, sel);
-    f16x2 h = __builtin_bit_cast(f16x2, v) * s2;
-    out[k] = __builtin_bit_cast(uint32_t, h);
-  }
+// 8 E2M1 nibbles (one code dword; channel 2j in the low nibble of byte j) times
+// the block scale -> f16x8, exact.
+__device__ __forceinline__ f16x8 fp4x8_to_f16(uint32_t d, f16x2 s2) {
+  f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0) * s2;
+  f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1) * s2;
+  f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2) * s2;
+  f16x2 e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3) * s2;
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
 }
 
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
@@ -65,38 +63,51 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// raw global data of one (key, 64-channel part) item
-struct RawFp4 {
-  uint4 c0, c1;
-  uint32_t sc;
-  int valid;
-};
-struct RawBf16 {
-  uint4 v[8];
-  int valid;
+__device__ __forceinline__ f16x8 bf16x8_to_f16(uint4 v) {
+  uint32_t w[4] = {bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w)};
+  return __builtin_bit_cast(f16x8, w);
+}
+
+__device__ __forceinline__ f16x4 lds_tr16(const _Float16* p) {
+  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(p));
+  return __builtin_bit_cast(f16x4, v);
+}
+
+struct AttnArgs {
+  const uint16_t* q_lat;          // bf16 [R][H][512]
+  int H;
+  const uint8_t* codes;           // [B][T][256]
+  const uint8_t* scales;          // [B][T][32]
+  int64_t T;
+  const int32_t* row_seq;         // [R] or null
+  const int32_t* idx;             // [R][K] (sparse chunks)
+  int K;
+  int n_sparse_chunks;
+  int tiles_per_chunk;
+  const uint16_t* swa;            // bf16 [B][S][512] (window chunk)
+  int S;
+  const int32_t* swa_start;
+  const int32_t* swa_len;
+  int n_chunks;                   // sparse chunks + (window ? 1 : 0)
+  float scale_log2;               // softmax scale * log2(e)
+  float* o_part;                  // [R][n_chunks][H][512]
+  float* ml_part;                 // [R][n_chunks][H][2]
 };
 
-template <int NW, bool kWindow>
-struct Loader {
-  static constexpr int kThreads = NW * 64;
-  static constexpr int kTotal = kKT * 8;                  // (key, 64-channel part) items per tile
-  static constexpr int kItems = (kTotal + kThreads - 1) / kThreads;    // items per thread
-  using Raw = typename std::conditional<kWindow, RawBf16, RawFp4>::type;
+// raw global data of the lane's two keys for one tile
+struct RawTile {
+  uint4 v[2][4];      // FP4: v[mt][0] = 16 code bytes; window: 64 bytes of bf16
+  uint32_t sc[2];     // FP4: 2 scale bytes
+  int valid[2];
 };
 
-template <int NW, bool kWindow>
-__global__ void __launch_bounds__(NW * 64)
-attn_partial_kernel(const uint16_t* __restrict__ q_lat, int H,
-                    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
-                    const uint16_t* __restrict__ swa, int S, int64_t T, const int32_t* __restrict__ row_seq,
-                    const int32_t* __restrict__ idx, int K,
-                    const int32_t* __restrict__ swa_start, const int32_t* __restrict__ swa_len,
-                    float scale_log2, int tiles_per_chunk, int n_chunks,
-                    float* __restrict__ o_part, float* __restrict__ ml_part) {
-  using L = Loader<NW, kWindow>;
-  using Raw = typename L::Raw;
-  __shared__ __attribute__((aligned(16))) _Float16 xs[kKT * kXsStride];
-  __shared__ __attribute__((aligned(16))) _Float16 xt[kLatent * kXtStride];
+template <int NT>
+__global__ void __launch_bounds__(256, 1)
+attn_chunk_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) _Float16 xw[4 * kKT * kXwStride];
+  __shared__ __attribute__((aligned(16))) float sp[4 * NT * 16 * kSStride];
+  __shared__ __attribute__((aligned(16))) _Float16 pp[NT * 16 * kPStride];
+  __shared__ float s_alpha[NT * 16];
   __shared__ int s_valid[kKT];
 
   const int chunk = blockIdx.x;
@@ -104,200 +115,197 @@ attn_partial_kernel(const uint16_t* __restrict__ q_lat, int H,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int n16 = lane & 15;
+  const int m = lane & 15;
   const int g = lane >> 4;
-  const int h = blockIdx.z * (NW * 16) + wave * 16 + n16;   // this lane's head (column)
-  const int seq = row_seq ? row_seq[r] : r;
+  const int H = a.H;
+  const int seq = a.row_seq ? a.row_seq[r] : r;
+  const bool is_window = chunk >= a.n_sparse_chunks;
 
-  // key range of this chunk
-  int n_keys, k_base, w_start = 0;
-  if (kWindow) {
-    int st = swa_start[r], ln = swa_len[r];
-    bool ok = st >= 0 && ln >= 0 && ln <= kWindowMax && (int64_t)st + ln <= S;
-    n_keys = ok ? ln : 0;
-    w_start = ok ? st : 0;
+  int k_begin, k_end, w_start = 0;
+  if (!is_window) {
+    k_begin = chunk * a.tiles_per_chunk * kKT;
+    k_end = min(a.K, k_begin + a.tiles_per_chunk * kKT);
   } else {
-    n_keys = K;
+    int st = a.swa_start[r], ln = a.swa_len[r];
+    bool ok = st >= 0 && ln >= 0 && ln <= kWindowMax && (int64_t)st + ln <= a.S;
+    k_begin = 0;
+    k_end = ok ? ln : 0;
+    w_start = ok ? st : 0;
   }
-  k_base = chunk * tiles_per_chunk * kKT;
-  const int k_end = min(n_keys, k_base + tiles_per_chunk * kKT);
-  const int n_tiles = k_end > k_base ? (k_end - k_base + kKT - 1) / kKT : 0;
+  const int n_tiles = k_end > k_begin ? (k_end - k_begin + kKT - 1) / kKT : 0;
+  const int cbase = 128 * wave;                  // this wave's channel slice
 
-  // queries: B operand of S^T = X . Q^T; k-step ks holds channels 32ks + 8g + [0,8)
-  f16x8 qreg[16];
-  {
-    const uint16_t* qrow = q_lat + ((int64_t)r * H + h) * kLatent;
+  // queries: B operand of S^T = X . Q^T; k-step ks holds channels cbase + 32g + 8ks + [0, 8)
+  f16x8 qb[NT][4];
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      uint4 v = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * g);
-      uint32_t w[4] = {bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w)};
-      qreg[ks] = __builtin_bit_cast(f16x8, w);
-    }
+  for (int nt = 0; nt < NT; ++nt) {
+    const uint16_t* qrow = a.q_lat + ((int64_t)r * H + 16 * nt + m) * kLatent + cbase + 32 * g;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qb[nt][ks] = bf16x8_to_f16(*reinterpret_cast<const uint4*>(qrow + 8 * ks));
   }
 
-  f32x4 o_acc[32];
+  f32x4 oacc[8][NT];
 #pragma unroll
-  for (int t = 0; t < 32; ++t) o_acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) oacc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -__builtin_inff();
   float l_run = 0.f;
 
-  Raw raw[L::kItems];
-
+  RawTile raw;
   auto load_tile = [&](int tile) {
-    const int k0 = k_base + tile * kKT;
 #pragma unroll
-    for (int it = 0; it < L::kItems; ++it) {
-      const int item = tid + it * L::kThreads;
-      if (item >= L::kTotal) break;
-      const int key = item >> 3, part = item & 7;
-      const int kk = k0 + key;
-      if constexpr (kWindow) {
-        bool ok = kk < k_end;
-        raw[it].valid = ok;
+    for (int mt = 0; mt < 2; ++mt) {
+      const int kk = k_begin + tile * kKT + 16 * mt + m;
+      if (!is_window) {
+        int pos = kk < k_end ? a.idx[(int64_t)r * a.K + kk] : -1;
+        bool ok = pos >= 0 && pos < a.T;
+        raw.valid[mt] = ok;
         if (ok) {
-          const uint4* p = reinterpret_cast<const uint4*>(
-              swa + ((int64_t)seq * S + w_start + kk) * kLatent + 64 * part);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) raw[it].v[j] = p[j];
+          const int64_t row = (int64_t)seq * a.T + pos;
+          raw.v[mt][0] = *reinterpret_cast<const uint4*>(a.codes + row * kCodesRow + 64 * wave + 16 * g);
+          raw.sc[mt] = *reinterpret_cast<const uint16_t*>(a.scales + row * kScalesRow + 8 * wave + 2 * g);
         } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) raw[it].v[j] = make_uint4(0, 0, 0, 0);
+          raw.v[mt][0] = make_uint4(0, 0, 0, 0);
+          raw.sc[mt] = 0;
         }
       } else {
-        int pos = kk < k_end ? idx[(int64_t)r * K + kk] : -1;
-        bool ok = pos >= 0 && pos < T;
-        raw[it].valid = ok;
-        if (ok) {
-          const int64_t row = (int64_t)seq * T + pos;
-          const uint4* pc = reinterpret_cast<const uint4*>(codes + row * kCodesRow + 32 * part);
-          raw[it].c0 = pc[0];
-          raw[it].c1 = pc[1];
-          raw[it].sc = *reinterpret_cast<const uint32_t*>(scales + row * kScalesRow + 4 * part);
-        } else {
-          raw[it].c0 = make_uint4(0, 0, 0, 0);
-          raw[it].c1 = make_uint4(0, 0, 0, 0);
-          raw[it].sc = 0;
-        }
+        bool ok = kk < k_end;
+        raw.valid[mt] = ok;
+        const uint4* p = reinterpret_cast<const uint4*>(
+            a.swa + ((int64_t)seq * a.S + w_start + (ok ? kk : 0)) * kLatent + cbase + 32 * g);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) raw.v[mt][j] = ok ? p[j] : make_uint4(0, 0, 0, 0);
       }
     }
   };
 
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int it = 0; it < L::kItems; ++it) {
-      const int item = tid + it * L::kThreads;
-      if (item >= L::kTotal) break;
-      const int key = item >> 3, part = item & 7;
-      uint32_t hv[32];                   // 64 fp16 values of this item
-      if constexpr (kWindow) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          hv[4 * j + 0] = bf16x2_to_f16x2(raw[it].v[j].x);
-          hv[4 * j + 1] = bf16x2_to_f16x2(raw[it].v[j].y);
-          hv[4 * j + 2] = bf16x2_to_f16x2(raw[it].v[j].z);
-          hv[4 * j + 3] = bf16x2_to_f16x2(raw[it].v[j].w);
-        }
-      } else {
-        uint32_t cw[8] = {raw[it].c0.x, raw[it].c0.y, raw[it].c0.z, raw[it].c0.w,
-                          raw[it].c1.x, raw[it].c1.y, raw[it].c1.z, raw[it].c1.w};
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {         // 4 scale blocks of 16 channels = 2 code dwords each
-          float sf = e4m3_to_f32((raw[it].sc >> (8 * b)) & 0xFFu);
-          f16x2 s2 = {(_Float16)sf, (_Float16)sf};
-          fp4x8_to_f16(cw[2 * b], s2, &hv[8 * b]);
-          fp4x8_to_f16(cw[2 * b + 1], s2, &hv[8 * b + 4]);
-        }
-      }
-      // key-major copy: 64 halfs = 8 x 16 bytes
-      uint4* dst = reinterpret_cast<uint4*>(&xs[key * kXsStride + 64 * part]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) dst[j] = make_uint4(hv[4 * j], hv[4 * j + 1], hv[4 * j + 2], hv[4 * j + 3]);
-      // channel-major copy
-      uint16_t* xt16 = reinterpret_cast<uint16_t*>(xt);
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        xt16[(64 * part + 2 * j) * kXtStride + key] = (uint16_t)(hv[j] & 0xFFFFu);
-        xt16[(64 * part + 2 * j + 1) * kXtStride + key] = (uint16_t)(hv[j] >> 16);
-      }
-      if (part == 0) s_valid[key] = raw[it].valid;
-    }
-  };
+  _Float16* xmine = xw + wave * kKT * kXwStride;
+  float* spmine = sp + wave * NT * 16 * kSStride;
+  const float neg_inf = -__builtin_inff();
 
   if (n_tiles > 0) load_tile(0);
   for (int tile = 0; tile < n_tiles; ++tile) {
-    __syncthreads();                 // previous tile's LDS reads are done
-    store_tile();
-    __syncthreads();
-    if (tile + 1 < n_tiles) load_tile(tile + 1);   // in flight during the math below
-
-    // ---- S^T = X . Q^T : two 16-key M-tiles
-    f32x4 sacc[2];
+    // ---- dequantise this tile's slice into A operands and the key-major LDS slice
+    f16x8 xa[2][4];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const _Float16* xrow = &xs[(16 * mt + n16) * kXsStride + 8 * g];
+      if (!is_window) {
+        uint32_t cw[4] = {raw.v[mt][0].x, raw.v[mt][0].y, raw.v[mt][0].z, raw.v[mt][0].w};
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) {
-        f16x8 a = *reinterpret_cast<const f16x8*>(xrow + 32 * ks);
-        acc = mfma16(a, qreg[ks], acc);
+        for (int ks = 0; ks < 4; ++ks) {
+          float sf = e4m3_to_f32((raw.sc[mt] >> (8 * (ks >> 1))) & 0xFFu);
+          f16x2 s2 = {(_Float16)sf, (_Float16)sf};
+          xa[mt][ks] = fp4x8_to_f16(cw[ks], s2);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) xa[mt][ks] = bf16x8_to_f16(raw.v[mt][ks]);
       }
-      sacc[mt] = acc;
+      f16x8* dst = reinterpret_cast<f16x8*>(xmine + (16 * mt + m) * kXwStride + 32 * g);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) dst[ks] = xa[mt][ks];
     }
-    // ---- online softmax (lane column = head h; rows = keys 16mt + 4g + i)
-    float s[8];
-    float mx = -__builtin_inff();
+    if (wave == 0 && g == 0) {
+      s_valid[m] = raw.valid[0];
+      s_valid[16 + m] = raw.valid[1];
+    }
+    if (tile + 1 < n_tiles) load_tile(tile + 1);      // in flight during the math below
+
+    // ---- partial scores over this wave's channels: S^T[16mt + 4g + i][16nt + m]
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int key = 16 * mt + 4 * g + i;
-        float v = s_valid[key] ? sacc[mt][i] * scale_log2 : -__builtin_inff();
-        s[4 * mt + i] = v;
-        mx = fmaxf(mx, v);
+      for (int nt = 0; nt < NT; ++nt) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = mfma16(xa[mt][ks], qb[nt][ks], acc);
+        *reinterpret_cast<f32x4*>(spmine + (16 * nt + m) * kSStride + 16 * mt + 4 * g) = acc;
       }
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const bool live = m_new != -__builtin_inff();
-    const float alpha = live ? exp2f(m_run - m_new) : 1.f;
-    float psum = 0.f;
-    float p[8];
+    __syncthreads();
+
+    // ---- softmax for heads [16w, 16w+16): lane (m, g) owns head 16w+m, keys 8g + [0, 8)
+    if (wave < NT) {
+      float s[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      p[j] = live ? exp2f(s[j] - m_new) : 0.f;
-      psum += p[j];
+      for (int j = 0; j < 8; ++j) s[j] = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < 4; ++w2) {
+        const float* src = sp + w2 * NT * 16 * kSStride + (16 * wave + m) * kSStride + 8 * g;
+        f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
+        f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { s[j] += v0[j]; s[4 + j] += v1[j]; }
+      }
+      float mx = neg_inf;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        s[j] = s_valid[8 * g + j] ? s[j] * a.scale_log2 : neg_inf;
+        mx = fmaxf(mx, s[j]);
+      }
+      mx = fmaxf(mx, shfl_xor_f(mx, 16));
+      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const bool live = m_new != neg_inf;
+      const float alpha = live ? exp2f(m_run - m_new) : 1.f;
+      float psum = 0.f;
+      f16x8 ph;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float pj = live ? exp2f(s[j] - m_new) : 0.f;
+        psum += pj;
+        ph[j] = (_Float16)pj;
+      }
+      psum += shfl_xor_f(psum, 16);
+      psum += shfl_xor_f(psum, 32);
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      *reinterpret_cast<f16x8*>(pp + (16 * wave + m) * kPStride + 8 * g) = ph;
+      if (g == 0) s_alpha[16 * wave + m] = alpha;
     }
-    psum += shfl_xor_f(psum, 16);
-    psum += shfl_xor_f(psum, 32);
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__any(alpha != 1.f)) {
+    __syncthreads();
+
+    // ---- rescale and accumulate O^T[cbase + 16t + 4g + i][16nt + m] += sum_k X[k][.] P[.][k]
+    float al[NT];
+    bool any_scale = false;
 #pragma unroll
-      for (int t = 0; t < 32; ++t) o_acc[t] *= alpha;
+    for (int nt = 0; nt < NT; ++nt) {
+      al[nt] = s_alpha[16 * nt + m];
+      any_scale |= al[nt] != 1.f;
     }
-    // ---- O^T += Xt . P^T ; slot j<4 -> key 4g+j, j>=4 -> key 16+4g+(j-4)
-    f16x8 pb;
+    if (__any(any_scale)) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) pb[j] = (_Float16)p[j];
+      for (int t = 0; t < 8; ++t)
 #pragma unroll
-    for (int t = 0; t < 32; ++t) {
-      const _Float16* xr = &xt[(16 * t + n16) * kXtStride];
-      f16x4 a0 = *reinterpret_cast<const f16x4*>(xr + 4 * g);
-      f16x4 a1 = *reinterpret_cast<const f16x4*>(xr + 16 + 4 * g);
-      f16x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      o_acc[t] = mfma16(a, pb, o_acc[t]);
+        for (int nt = 0; nt < NT; ++nt) oacc[t][nt] *= al[nt];
+    }
+    f16x8 pb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) pb[nt] = *reinterpret_cast<const f16x8*>(pp + (16 * nt + m) * kPStride + 8 * g);
+    // transpose-read rows: source lane m supplies keys 8g + (m>>2) (+4) and channels 16t + 4(m&3) .. +3
+    const _Float16* tr0 = xmine + (8 * g + (m >> 2)) * kXwStride + 4 * (m & 3);
+    const _Float16* tr1 = tr0 + 4 * kXwStride;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      f16x4 lo = lds_tr16(tr0 + 16 * t);
+      f16x4 hi = lds_tr16(tr1 + 16 * t);
+      f16x8 xt = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) oacc[t][nt] = mfma16(xt, pb[nt], oacc[t][nt]);
     }
   }
 
-  // ---- write this chunk's partial: O^T lane holds channels 16t + 4g + i of head h
-  const int64_t prow = ((int64_t)r * n_chunks + chunk) * H + h;
-  float* op = o_part + prow * kLatent;
+  // ---- this chunk's partial: unnormalised O, and (m, l) from the softmax owners
+  const int64_t prow = ((int64_t)r * a.n_chunks + chunk) * H;
 #pragma unroll
-  for (int t = 0; t < 32; ++t)
-    *reinterpret_cast<f32x4*>(op + 16 * t + 4 * g) = o_acc[t];
-  if (g == 0) {
-    ml_part[prow * 2 + 0] = m_run;
-    ml_part[prow * 2 + 1] = l_run;
+  for (int nt = 0; nt < NT; ++nt) {
+    float* op = a.o_part + (prow + 16 * nt + m) * kLatent + cbase + 4 * g;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4*>(op + 16 * t) = oacc[t][nt];
+  }
+  if (wave < NT && g == 0) {
+    a.ml_part[(prow + 16 * wave + m) * 2 + 0] = m_run;
+    a.ml_part[(prow + 16 * wave + m) * 2 + 1] = l_run;
   }
 }
 
@@ -350,22 +358,22 @@ attn_combine_kernel(const float* __restrict__ o_part, const float* __restrict__ 
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-struct SparsePlan {
+struct Plan {
   int tiles_per_chunk;
-  int n_chunks;
+  int n_sparse;
 };
 
-static SparsePlan sparse_plan(int32_t R, int32_t K) {
+// About one workgroup per CU in total (the kernel runs one four-wave workgroup
+// per CU), at least 4 tiles per chunk so that the partial outputs stay small
+// next to the gathered rows.
+static Plan sparse_plan(int32_t R, int32_t K) {
   int tiles = (K + kKT - 1) / kKT;
   if (tiles < 1) tiles = 1;
-  // about 512 workgroups in total, at least 4 tiles per chunk so that the
-  // partial outputs stay small next to the gathered rows
-  int want = (512 + R - 1) / R;
+  int want = (256 + R - 1) / R;
   int tpc = (tiles + want - 1) / want;
   if (tpc < 4) tpc = 4;
   if (tpc > tiles) tpc = tiles;
-  SparsePlan p{tpc, (tiles + tpc - 1) / tpc};
-  return p;
+  return Plan{tpc, (tiles + tpc - 1) / tpc};
 }
 
 static size_t partial_bytes(int32_t R, int32_t H, int n_chunks, size_t* off_ml) {
@@ -377,22 +385,40 @@ static size_t partial_bytes(int32_t R, int32_t H, int n_chunks, size_t* off_ml) 
 
 static bool heads_ok(int32_t H) { return H == 16 || H == 32 || H == 48 || H == 64; }
 
-template <bool kWindow>
-static void launch_partial(int NW, dim3 grid, hipStream_t s, const uint16_t* q_lat, int H, const uint8_t* codes,
-                           const uint8_t* scales, const uint16_t* swa, int S, int64_t T, const int32_t* row_seq,
-                           const int32_t* idx, int K, const int32_t* swa_start, const int32_t* swa_len,
-                           float scale_log2, int tpc, int n_chunks, float* o_part, float* ml_part) {
-#define CSA2_LAUNCH(NWV)                                                                                     \
-  attn_partial_kernel<NWV, kWindow><<<grid, NWV * 64, 0, s>>>(q_lat, H, codes, scales, swa, S, T, row_seq, \
-                                                             idx, K, swa_start, swa_len, scale_log2, tpc,   \
-                                                             n_chunks, o_part, ml_part)
-  switch (NW) {
-    case 1: CSA2_LAUNCH(1); break;
-    case 2: CSA2_LAUNCH(2); break;
-    case 3: CSA2_LAUNCH(3); break;
-    default: CSA2_LAUNCH(4); break;
+static void launch_chunks(const AttnArgs& a, int R, hipStream_t s) {
+  dim3 grid(a.n_chunks, R);
+  switch (a.H / 16) {
+    case 1: attn_chunk_kernel<1><<<grid, 256, 0, s>>>(a); break;
+    case 2: attn_chunk_kernel<2><<<grid, 256, 0, s>>>(a); break;
+    case 3: attn_chunk_kernel<3><<<grid, 256, 0, s>>>(a); break;
+    default: attn_chunk_kernel<4><<<grid, 256, 0, s>>>(a); break;
   }
-#undef CSA2_LAUNCH
+}
+
+// shared validation + launch of one attention call (sparse part, window part or both)
+static csa2_status attention_call(const uint16_t* q_lat, int32_t R, int32_t H, const uint8_t* codes,
+                                  const uint8_t* scales, int32_t B, int64_t T, const int32_t* row_seq,
+                                  const int32_t* idx, int32_t K, const uint16_t* swa, int32_t S,
+                                  const int32_t* swa_start, const int32_t* swa_len, float softmax_scale,
+                                  const float* o_prev, const float* lse_prev, float* o, float* lse,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p = idx ? sparse_plan(R, K) : Plan{0, 0};
+  AttnArgs a;
+  a.q_lat = q_lat; a.H = H; a.codes = codes; a.scales = scales; a.T = T; a.row_seq = row_seq;
+  a.idx = idx; a.K = K; a.n_sparse_chunks = p.n_sparse; a.tiles_per_chunk = p.tiles_per_chunk;
+  a.swa = swa; a.S = S; a.swa_start = swa_start; a.swa_len = swa_len;
+  a.n_chunks = p.n_sparse + (swa ? 1 : 0);
+  a.scale_log2 = softmax_scale * kLog2e;
+  size_t off_ml;
+  size_t need = partial_bytes(R, H, a.n_chunks, &off_ml);
+  if (!workspace || workspace_bytes < need) return CSA2_EWORKSPACE;
+  if (!aligned(workspace, 256)) return CSA2_EALIGN;
+  a.o_part = static_cast<float*>(workspace);
+  a.ml_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + off_ml);
+  hipStream_t s = (hipStream_t)stream;
+  launch_chunks(a, R, s);
+  attn_combine_kernel<<<dim3(H, R), 128, 0, s>>>(a.o_part, a.ml_part, a.n_chunks, H, o_prev, lse_prev, o, lse);
+  return launch_status();
 }
 
 }  // namespace csa2
@@ -401,8 +427,7 @@ using namespace csa2;
 
 extern "C" size_t csa2_sparse_decode_workspace_size(int32_t R, int32_t H, int32_t K) {
   if (R <= 0 || H <= 0 || K <= 0) return 0;
-  SparsePlan p = sparse_plan(R, K);
-  return partial_bytes(R, H, p.n_chunks, nullptr);
+  return partial_bytes(R, H, sparse_plan(R, K).n_sparse, nullptr);
 }
 
 extern "C" csa2_status csa2_sparse_decode(const uint16_t* q_lat, int32_t R, int32_t H, const uint8_t* codes,
@@ -417,25 +442,13 @@ extern "C" csa2_status csa2_sparse_decode(const uint16_t* q_lat, int32_t R, int3
   if (!aligned(q_lat, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(idx, 4) ||
       !aligned(o, 16) || !aligned(lse, 4))
     return CSA2_EALIGN;
-  SparsePlan p = sparse_plan(R, K);
-  size_t off_ml;
-  size_t need = partial_bytes(R, H, p.n_chunks, &off_ml);
-  if (!workspace || workspace_bytes < need) return CSA2_EWORKSPACE;
-  if (!aligned(workspace, 256)) return CSA2_EALIGN;
-  float* o_part = static_cast<float*>(workspace);
-  float* ml_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + off_ml);
-  hipStream_t s = (hipStream_t)stream;
-  const int NW = H / 16;
-  dim3 grid(p.n_chunks, R, 1);
-  launch_partial<false>(NW, grid, s, q_lat, H, codes, scales, nullptr, 0, T, row_seq, idx, K, nullptr, nullptr,
-                        softmax_scale * kLog2e, p.tiles_per_chunk, p.n_chunks, o_part, ml_part);
-  attn_combine_kernel<<<dim3(H, R), 128, 0, s>>>(o_part, ml_part, p.n_chunks, H, nullptr, nullptr, o, lse);
-  return launch_status();
+  return attention_call(q_lat, R, H, codes, scales, B, T, row_seq, idx, K, nullptr, 0, nullptr, nullptr,
+                        softmax_scale, nullptr, nullptr, o, lse, workspace, workspace_bytes, stream);
 }
 
 extern "C" size_t csa2_swa_merge_workspace_size(int32_t R, int32_t H) {
   if (R <= 0 || H <= 0) return 0;
-  return partial_bytes(R, H, kWindowMax / kKT, nullptr);
+  return partial_bytes(R, H, 1, nullptr);
 }
 
 extern "C" csa2_status csa2_swa_merge(const uint16_t* q_lat, int32_t R, int32_t H, const uint16_t* swa, int32_t B,
@@ -450,18 +463,29 @@ extern "C" csa2_status csa2_swa_merge(const uint16_t* q_lat, int32_t R, int32_t 
   if (!heads_ok(H)) return CSA2_ESHAPE;
   if (!aligned(q_lat, 16) || !aligned(swa, 16) || !aligned(o_out, 16) || (o_sparse && !aligned(o_sparse, 16)))
     return CSA2_EALIGN;
-  const int n_chunks = kWindowMax / kKT;
-  size_t off_ml;
-  size_t need = partial_bytes(R, H, n_chunks, &off_ml);
-  if (!workspace || workspace_bytes < need) return CSA2_EWORKSPACE;
-  if (!aligned(workspace, 256)) return CSA2_EALIGN;
-  float* o_part = static_cast<float*>(workspace);
-  float* ml_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + off_ml);
-  hipStream_t s = (hipStream_t)stream;
-  const int NW = H / 16;
-  dim3 grid(n_chunks, R, 1);
-  launch_partial<true>(NW, grid, s, q_lat, H, nullptr, nullptr, swa, S, 0, row_seq, nullptr, 0, swa_start, swa_len,
-                       softmax_scale * kLog2e, 1, n_chunks, o_part, ml_part);
-  attn_combine_kernel<<<dim3(H, R), 128, 0, s>>>(o_part, ml_part, n_chunks, H, o_sparse, lse_sparse, o_out, lse_out);
-  return launch_status();
+  return attention_call(q_lat, R, H, nullptr, nullptr, B, 0, row_seq, nullptr, 0, swa, S, swa_start, swa_len,
+                        softmax_scale, o_sparse, lse_sparse, o_out, lse_out, workspace, workspace_bytes, stream);
+}
+
+extern "C" size_t csa2_sparse_swa_decode_workspace_size(int32_t R, int32_t H, int32_t K) {
+  if (R <= 0 || H <= 0 || K <= 0) return 0;
+  return partial_bytes(R, H, sparse_plan(R, K).n_sparse + 1, nullptr);
+}
+
+extern "C" csa2_status csa2_sparse_swa_decode(const uint16_t* q_lat, int32_t R, int32_t H, const uint8_t* codes,
+                                              const uint8_t* scales, int32_t B, int64_t T, const int32_t* row_seq,
+                                              const int32_t* idx, int32_t K, const uint16_t* swa, int32_t S,
+                                              const int32_t* swa_start, const int32_t* swa_len,
+                                              float softmax_scale, float* o, float* lse, void* workspace,
+                                              size_t workspace_bytes, void* stream) {
+  if (!q_lat || !codes || !scales || !idx || !swa || !swa_start || !swa_len || !o || !lse) return CSA2_EINVAL;
+  if (R <= 0 || B <= 0 || T <= 0 || K <= 0 || S <= 0) return CSA2_EINVAL;
+  if (!row_seq && R != B) return CSA2_EINVAL;
+  if (!heads_ok(H)) return CSA2_ESHAPE;
+  if (T >= (int64_t(1) << 31)) return CSA2_ESHAPE;
+  if (!aligned(q_lat, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(idx, 4) || !aligned(swa, 16) ||
+      !aligned(o, 16) || !aligned(lse, 4))
+    return CSA2_EALIGN;
+  return attention_call(q_lat, R, H, codes, scales, B, T, row_seq, idx, K, swa, S, swa_start, swa_len,
+                        softmax_scale, nullptr, nullptr, o, lse, workspace, workspace_bytes, stream);
 }

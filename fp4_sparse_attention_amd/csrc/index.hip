@@ -2,20 +2,24 @@
 // (only the candidate-pool positions), per the CSA2 roles paragraph of the
 // MarkTechPost retelling of DeepSeek-V4.1-Flash.
 //
-// score(r, j) = sum_{d<64} q_idx[r][d] * k_idx[seq(r)][j][d], E4M3 x E4M3 with
-// fp32 accumulation, computed on the fp8 matrix cores:
-//   v_mfma_f32_32x32x64_f8f6f4:  C[32 x 32] += A[32 x 64] * B[64 x 32]
-// with A = up to 32 query rows of one sequence and B = 32 keys (one 64-byte key
-// per column).  Lane l owns row/column (l % 32) and one 32-byte half of the
-// 64-d contraction, so a wave loads a 2 KB tile of 32 consecutive keys with two
-// 16-byte loads per lane (fully coalesced); A and B use the same lane->k map.
+// score(r, j) = sum_{d<64} q_idx[r][d] * k_idx[seq(r)][j][d] with E4M3 inputs.
+// The E4M3 bytes are widened to f16 (exact, v_cvt_scalef32_pk_f16_fp8 with unit
+// scale) and multiplied on the f16 matrix cores:
+//   v_mfma_f32_32x32x16_f16:  C[32 x 32] += A[32 x 16] * B[16 x 32], four k-steps
+// with A = up to 32 query rows of one sequence and B = 32 keys.  On gfx950 this
+// instruction forms the 16-term dot product exactly and rounds once, so every
+// score equals the fp32 rounding of the exact sum (the fp8 matrix path does
+// not: its internal accumulation keeps only ~20 bits below the largest
+// product).  Lane l owns row/column (l % 32) and one 32-byte half of the 64-d
+// key, so a wave loads a 2 KB tile of 32 consecutive keys with two 16-byte
+// loads per lane (fully coalesced); A and B use the same lane->k map.
 // Output C: lane l, register v holds column l % 32 and row
-// 8*(v/4) + 4*(l/32) + (v%4); row 0 therefore sits in register 0 of lanes 0-31,
-// which store 32 consecutive scores as one 128-byte line.
+// 8*(v/4) + 4*(l/32) + (v%4); row 0 sits in register 0 of lanes 0-31, which
+// store 32 consecutive scores as one 128-byte line.
 //
-// Decode (one query per sequence) is HBM-bound: 64 bytes of key per score, and
-// the matrix cores are ~10% busy.  Chunked prefill fills all 32 rows of A and
-// is bound by the fp32 score writes.
+// Decode (one query per sequence) is HBM-bound: 64 bytes of key per score; the
+// matrix cores and the conversions use a small share of their peak.  Chunked
+// prefill fills all 32 rows of A and is bound by the fp32 score writes.
 #include "common.hpp"
 
 namespace csa2 {
@@ -23,9 +27,27 @@ namespace csa2 {
 constexpr int kTile = 32;          // keys per MFMA tile
 constexpr int kUnroll = 4;         // tiles in flight per wave
 
-__device__ __forceinline__ f32x16 mfma_fp8_32x32x64(const i32x8& a, const i32x8& b, f32x16 c) {
-  // scale operands 0 select the unscaled instruction (plain fp8 x fp8)
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+// 32 E4M3 bytes (8 dwords) -> four f16x8 MFMA operands, exact
+__device__ __forceinline__ void fp8x32_to_f16(const i32x8& v, f16x8* out) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    uint32_t w0 = (uint32_t)v[2 * ks], w1 = (uint32_t)v[2 * ks + 1];
+    f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+    f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+    f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+    f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+    out[ks] = f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  }
+}
+
+// score tile: sum over the four 16-element k-steps of the lane's 32-byte half
+__device__ __forceinline__ f32x16 mfma_score(const f16x8* a, const i32x8& kb) {
+  f16x8 b[4];
+  fp8x32_to_f16(kb, b);
+  f32x16 acc = {};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks], b[ks], acc, 0, 0, 0);
+  return acc;
 }
 
 __device__ __forceinline__ i32x8 load_half_key(const uint8_t* p) {
@@ -56,13 +78,15 @@ index_rows_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__
   float* out = scores + (int64_t)r * n_cols;
   const int32_t* prow = kGather ? pool + (int64_t)r * n_cols : nullptr;
 
-  i32x8 a = {0, 0, 0, 0, 0, 0, 0, 0};
+  i32x8 araw = {0, 0, 0, 0, 0, 0, 0, 0};
   if (col_in_tile == 0) {
     const uint4* q = reinterpret_cast<const uint4*>(q_idx + (int64_t)r * kIndexDim + 32 * half);
     uint4 x = q[0], y = q[1];
-    a[0] = x.x; a[1] = x.y; a[2] = x.z; a[3] = x.w;
-    a[4] = y.x; a[5] = y.y; a[6] = y.z; a[7] = y.w;
+    araw[0] = x.x; araw[1] = x.y; araw[2] = x.z; araw[3] = x.w;
+    araw[4] = y.x; araw[5] = y.y; araw[6] = y.z; araw[7] = y.w;
   }
+  f16x8 a[4];
+  fp8x32_to_f16(araw, a);
 
   const int64_t n_tiles = (n_cols + kTile - 1) / kTile;
   const int64_t t_begin = (int64_t)blockIdx.x * tiles_per_block;
@@ -87,8 +111,7 @@ index_rows_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       int64_t t = t0 + 4 * u;
-      f32x16 acc = {};
-      acc = mfma_fp8_32x32x64(a, b[u], acc);
+      f32x16 acc = mfma_score(a, b[u]);
       if (t < t_end && half == 0 && pos[u] < n_cols) out[pos[u]] = ok[u] ? acc[0] : neg_inf;
     }
   }
@@ -137,13 +160,15 @@ index_block_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict_
     for (int m = 0; m < 32; ++m)
       if (active >> m & 1u) max_lim = max(max_lim, s_lim[m]);
 
-    i32x8 a = {0, 0, 0, 0, 0, 0, 0, 0};
+    i32x8 araw = {0, 0, 0, 0, 0, 0, 0, 0};
     if (active >> l32 & 1u) {
       const uint4* q = reinterpret_cast<const uint4*>(q_idx + (int64_t)(r0 + l32) * kIndexDim + 32 * half);
       uint4 x = q[0], y = q[1];
-      a[0] = x.x; a[1] = x.y; a[2] = x.z; a[3] = x.w;
-      a[4] = y.x; a[5] = y.y; a[6] = y.z; a[7] = y.w;
+      araw[0] = x.x; araw[1] = x.y; araw[2] = x.z; araw[3] = x.w;
+      araw[4] = y.x; araw[5] = y.y; araw[6] = y.z; araw[7] = y.w;
     }
+    f16x8 a[4];
+    fp8x32_to_f16(araw, a);
     const uint8_t* kseq = k_idx + (int64_t)seq * T * kIndexDim;
 
     for (int64_t t0 = t_begin + wave; t0 < t_end; t0 += 4 * kUnroll) {
@@ -161,7 +186,7 @@ index_block_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict_
         if (t >= t_end) break;
         int64_t c = t * kTile + l32;
         f32x16 acc = {};
-        if (t * kTile <= max_lim) acc = mfma_fp8_32x32x64(a, b[u], acc);
+        if (t * kTile <= max_lim) acc = mfma_score(a, b[u]);
         if (c < T) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) {

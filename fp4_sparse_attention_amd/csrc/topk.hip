@@ -7,15 +7,25 @@
 // to the lower slot, output ascending, -1 padding.
 //
 // Each score maps to a key that orders like the float (sign flip for
-// positives, bitwise not for negatives); invisible slots (-inf, NaN, or a
-// negative index_map entry) map to key 0, which no visible score reaches
-// (the smallest, -FLT_MAX, maps to 0x00800000).  Three digit passes (11, 11 and
-// 10 bits) find the k-th largest key tau and how many slots equal to tau are
-// still needed; every pass is a segmented histogram (LDS atomics, then one
-// global atomic per non-empty bin and workgroup) followed by a one-workgroup
-// scan.  A counting pass and an ordered write pass then emit the selected slots
-// in slot order, so the output is sorted without a sort and ties go to the
-// lowest slots.  All integer work: the result is deterministic.
+// positives, bitwise not for negatives, -0 as +0); invisible slots (-inf, NaN,
+// or a negative index_map entry) map to key 0, which no visible score reaches
+// (the smallest, -FLT_MAX, maps to 0x00800000).  The k-th largest key tau is
+// found digit by digit (11, 11 and 10 bits) with histograms; the output is
+// then written in slot order (so it is sorted without a sort), taking every
+// key > tau and the lowest-slot keys == tau.  All integer work: deterministic.
+//
+// Three paths, chosen on the host from the row length N:
+//   small   (N <= 32768): one 1024-thread workgroup per row, keys in LDS,
+//           everything in one launch;
+//   compact (long rows): a histogram pass over the top digit; a pass that
+//           counts, per segment, the keys above the threshold bin and appends
+//           the keys inside it to a candidate list; one workgroup per row that
+//           finishes the selection on the candidates (and breaks ties by slot)
+//           and turns per-segment counts into output offsets; an ordered
+//           write pass -- three passes over the scores, five launches;
+//   multipass (long rows whose candidate lists would not fit the workspace
+//           budget): three histogram passes over the whole row, a counting
+//           pass and an ordered write pass.
 #include "common.hpp"
 
 namespace csa2 {
@@ -63,7 +73,7 @@ topk_hist_kernel(const float* __restrict__ scores, int64_t N, int64_t stride, co
   const int r = blockIdx.y;
   for (int i = threadIdx.x; i < kBins; i += kThreads) h[i] = 0u;
   __syncthreads();
-  const RowState s = st[r];
+  const RowState s = st ? st[r] : RowState{0u, 1u, 0u, 0u};
   const bool live = (D == 0) || s.need > 0;
   if (live) {
     const float* row = scores + (int64_t)r * stride;
@@ -299,7 +309,445 @@ topk_write_kernel(const float* __restrict__ scores, int64_t N, int64_t stride, c
   }
 }
 
+// block-wide exclusive scan for 1024 threads (16 waves)
+__device__ __forceinline__ uint32_t block_exclusive_scan_1024(uint32_t v, uint32_t* tmp /* >= 17 */,
+                                                              uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t acc = 0;
+    for (int w = 0; w < 16; ++w) { uint32_t t = tmp[w]; tmp[w] = acc; acc += t; }
+    tmp[16] = acc;
+  }
+  __syncthreads();
+  uint32_t res = tmp[wave] + x - v;
+  total = tmp[16];
+  __syncthreads();
+  return res;
+}
+
+// Digit search over a 2048-bin histogram held in LDS by a 1024-thread block:
+// the digit value holding the need-th largest key, and how many keys lie above it.
+__device__ __forceinline__ void find_digit_1024(const uint32_t* h, uint32_t need, bool skip_bin0, uint32_t* tmp,
+                                                uint32_t* s_digit, uint32_t* s_above, uint32_t& total) {
+  const int t = threadIdx.x;
+  const int b_hi = kBins - 1 - 2 * t, b_lo = kBins - 2 - 2 * t;
+  uint32_t c_hi = h[b_hi];
+  uint32_t c_lo = (skip_bin0 && b_lo == 0) ? 0u : h[b_lo];
+  uint32_t excl = block_exclusive_scan_1024(c_hi + c_lo, tmp, total);
+  if (t == 0) { *s_digit = 0xFFFFFFFFu; *s_above = 0u; }
+  __syncthreads();
+  if (need > 0) {
+    if (excl < need && need <= excl + c_hi) { *s_digit = b_hi; *s_above = excl; }
+    else if (excl + c_hi < need && need <= excl + c_hi + c_lo) { *s_digit = b_lo; *s_above = excl + c_hi; }
+  }
+  __syncthreads();
+}
+
+// ----------------------------------------------------------------------------
+// small path: one workgroup per row, keys resident in LDS
+// ----------------------------------------------------------------------------
+constexpr int kSmallMax = 32768;
+
+__global__ void __launch_bounds__(1024)
+topk_small_kernel(const float* __restrict__ scores, int N, int64_t stride, const int32_t* __restrict__ index_map,
+                  int32_t k, int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
+  __shared__ uint32_t keys[kSmallMax];
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t tmp[32];
+  __shared__ uint32_t s_digit, s_above;
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* row = scores + (int64_t)r * stride;
+  const int32_t* map_row = index_map ? index_map + (int64_t)r * N : nullptr;
+  for (int i = tid * 4; i < N; i += 4096) {
+    float4 v = *reinterpret_cast<const float4*>(row + i);
+    int4 mp = map_row ? *reinterpret_cast<const int4*>(map_row + i) : make_int4(0, 0, 0, 0);
+    keys[i + 0] = mp.x < 0 ? 0u : score_key(v.x);
+    keys[i + 1] = mp.y < 0 ? 0u : score_key(v.y);
+    keys[i + 2] = mp.z < 0 ? 0u : score_key(v.z);
+    keys[i + 3] = mp.w < 0 ? 0u : score_key(v.w);
+  }
+  uint32_t prefix = 0, need = 0, k_eff = 0;
+#pragma unroll 1
+  for (int d = 0; d < 3; ++d) {
+    for (int i = tid; i < kBins; i += 1024) h[i] = 0u;
+    __syncthreads();
+    const uint32_t mask = digit_mask_above(d);
+    const int shift = digit_shift(d);
+    if (d == 0 || need > 0) {
+      for (int i = tid; i < N; i += 1024) {
+        uint32_t key = keys[i];
+        if (key != 0u && (key & mask) == prefix) atomicAdd(&h[(key >> shift) & (kBins - 1)], 1u);
+      }
+    }
+    __syncthreads();
+    uint32_t total;
+    find_digit_1024(h, d == 0 ? 0xFFFFFFFFu : need, d == 0, tmp, &s_digit, &s_above, total);
+    if (d == 0) {
+      k_eff = total < (uint32_t)k ? total : (uint32_t)k;
+      need = k_eff;
+      find_digit_1024(h, need, true, tmp, &s_digit, &s_above, total);
+    }
+    if (need == 0 || s_digit == 0xFFFFFFFFu) { need = 0; prefix = 0xFFFFFFFFu; break; }
+    prefix |= s_digit << shift;
+    need -= s_above;
+  }
+  const uint32_t tau = prefix, need_eq = need;
+  int32_t* orow = idx_out + (int64_t)r * k;
+  float* srow = score_out ? score_out + (int64_t)r * k : nullptr;
+  // ordered write: thread t owns slots [t*E, t*E + E)
+  const int E = (N + 1023) / 1024;
+  const int i0 = tid * E, i1 = min(N, i0 + E);
+  uint32_t n_gt = 0, n_eq = 0;
+  if (k_eff > 0)
+    for (int i = i0; i < i1; ++i) {
+      uint32_t key = keys[i];
+      n_gt += key != 0u && key > tau;
+      n_eq += key != 0u && key == tau;
+    }
+  uint32_t tot;
+  uint32_t ex = block_exclusive_scan_1024((n_eq << 16) | n_gt, tmp, tot);
+  if (k_eff > 0) {
+    uint32_t e = ex >> 16;
+    uint32_t p = (ex & 0xFFFFu) + min(e, need_eq);
+    for (int i = i0; i < i1; ++i) {
+      uint32_t key = keys[i];
+      bool take = false;
+      if (key != 0u) {
+        if (key > tau) take = true;
+        else if (key == tau) { take = e < need_eq; ++e; }
+      }
+      if (take && p < k_eff) {
+        orow[p] = map_row ? map_row[i] : i;
+        if (srow) srow[p] = row[i];
+        ++p;
+      }
+    }
+  }
+  for (int i = (int)k_eff + tid; i < k; i += 1024) {
+    orow[i] = -1;
+    if (srow) srow[i] = __builtin_nanf("");
+  }
+}
+
+// ----------------------------------------------------------------------------
+// compact path
+// ----------------------------------------------------------------------------
+struct CompactState {
+  uint32_t b0;          // top digit of tau
+  uint32_t k_eff;
+  uint32_t tau;
+  uint32_t need_eq;
+  int32_t tie_slot_max; // equal keys at slots <= this are selected
+  uint32_t pad[3];
+};
+
+__global__ void __launch_bounds__(kThreads)
+topk_cinit_kernel(uint32_t* __restrict__ hist0, uint32_t* __restrict__ cand_count) {
+  const int r = blockIdx.x;
+  for (int i = threadIdx.x; i < kBins; i += kThreads) hist0[(int64_t)r * kBins + i] = 0u;
+  if (threadIdx.x == 0) cand_count[r] = 0u;
+}
+
+// derive (b0, need within bin b0, k_eff) from the row's top-digit histogram, 256 threads
+__device__ __forceinline__ void derive_b0(const uint32_t* g, int32_t k, uint32_t* tmp, uint32_t& b0, uint32_t& need1,
+                                          uint32_t& k_eff) {
+  __shared__ uint32_t s_digit, s_above;
+  uint32_t c[8];
+  uint32_t local = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int bin = kBins - 1 - (threadIdx.x * 8 + j);
+    c[j] = bin == 0 ? 0u : g[bin];
+    local += c[j];
+  }
+  uint32_t total;
+  uint32_t excl = block_exclusive_scan(local, tmp, total);
+  uint32_t need = total < (uint32_t)k ? total : (uint32_t)k;
+  if (threadIdx.x == 0) { s_digit = 0xFFFFFFFFu; s_above = 0u; }
+  __syncthreads();
+  if (need > 0 && excl < need && need <= excl + local) {
+    uint32_t acc = excl;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (acc < need && need <= acc + c[j]) { s_digit = (uint32_t)(kBins - 1 - (threadIdx.x * 8 + j)); s_above = acc; }
+      acc += c[j];
+    }
+  }
+  __syncthreads();
+  k_eff = need;
+  b0 = s_digit;
+  need1 = need - s_above;
+  __syncthreads();
+}
+
+// per segment: count keys above bin b0, append keys inside bin b0 to the candidates
+__global__ void __launch_bounds__(kThreads)
+topk_compact_kernel(const float* __restrict__ scores, int64_t N, int64_t stride, const int32_t* __restrict__ index_map,
+                    int32_t k, int seg, const uint32_t* __restrict__ hist0, uint32_t* __restrict__ cand_count,
+                    uint2* __restrict__ cand, int64_t cand_cap, uint32_t* __restrict__ seg_gt, int n_seg) {
+  __shared__ uint32_t tmp[8];
+  const int r = blockIdx.y;
+  uint32_t b0, need1, k_eff;
+  derive_b0(hist0 + (int64_t)r * kBins, k, tmp, b0, need1, k_eff);
+  const float* row = scores + (int64_t)r * stride;
+  const int32_t* map_row = index_map ? index_map + (int64_t)r * N : nullptr;
+  const int64_t s0 = (int64_t)blockIdx.x * seg;
+  const int64_t s1 = min(N, s0 + seg);
+  uint32_t gt = 0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint2* crow = cand + (int64_t)r * cand_cap;
+  if (k_eff > 0) {
+    for (int64_t base = s0; base < s1; base += kThreads * 4) {
+      const int64_t i = base + threadIdx.x * 4;
+      uint32_t k4[4] = {0u, 0u, 0u, 0u};
+      if (i < s1) {
+        float4 v = *reinterpret_cast<const float4*>(row + i);
+        int4 mp = map_row ? *reinterpret_cast<const int4*>(map_row + i) : make_int4(0, 0, 0, 0);
+        k4[0] = mp.x < 0 ? 0u : score_key(v.x);
+        k4[1] = mp.y < 0 ? 0u : score_key(v.y);
+        k4[2] = mp.z < 0 ? 0u : score_key(v.z);
+        k4[3] = mp.w < 0 ? 0u : score_key(v.w);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t d0 = k4[j] >> 21;
+        gt += k4[j] != 0u && d0 > b0;
+        const bool c = k4[j] != 0u && d0 == b0;
+        // wave-aggregated append
+        const uint64_t bal = __ballot(c);
+        if (bal) {
+          uint32_t base_slot = 0;
+          if (lane == 0) base_slot = atomicAdd(&cand_count[r], (uint32_t)__popcll(bal));
+          base_slot = __shfl(base_slot, 0, 64);
+          if (c) {
+            const uint32_t rank = (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+            crow[base_slot + rank] = make_uint2((uint32_t)(i + j), k4[j]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) gt += __shfl_xor(gt, o, 64);
+  if (lane == 0) tmp[wave] = gt;
+  __syncthreads();
+  if (threadIdx.x == 0) seg_gt[(int64_t)r * n_seg + blockIdx.x] = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+}
+
+// one workgroup per row: finish the selection on the candidates
+constexpr int kMaxSeg = 2048;
+
+__global__ void __launch_bounds__(1024)
+topk_refine_kernel(int32_t k, int seg, const uint32_t* __restrict__ hist0, const uint32_t* __restrict__ cand_count,
+                   const uint2* __restrict__ cand, int64_t cand_cap, const uint32_t* __restrict__ seg_gt,
+                   uint32_t* __restrict__ seg_off, int n_seg, CompactState* __restrict__ st) {
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t tmp[32];
+  __shared__ uint32_t s_digit, s_above;
+  __shared__ uint32_t sc[kMaxSeg];
+  __shared__ uint32_t s_b0, s_need1, s_keff;
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  // b0 / need1 / k_eff from the top-digit histogram (1024-thread version)
+  for (int i = tid; i < kBins; i += 1024) h[i] = hist0[(int64_t)r * kBins + i];
+  __syncthreads();
+  uint32_t total;
+  find_digit_1024(h, 0xFFFFFFFFu, true, tmp, &s_digit, &s_above, total);
+  {
+    uint32_t k_eff = total < (uint32_t)k ? total : (uint32_t)k;
+    find_digit_1024(h, k_eff, true, tmp, &s_digit, &s_above, total);
+    if (tid == 0) { s_keff = k_eff; s_b0 = s_digit; s_need1 = k_eff - s_above; }
+    __syncthreads();
+  }
+  const uint32_t k_eff = s_keff, b0 = s_b0;
+  uint32_t need = s_need1;
+  const uint32_t nc = cand_count[r];
+  const uint2* crow = cand + (int64_t)r * cand_cap;
+  uint32_t prefix = b0 << 21;
+  bool none = (k_eff == 0) || (b0 == 0xFFFFFFFFu);
+  if (none) prefix = 0xFFFFFFFFu;
+#pragma unroll 1
+  for (int d = 1; d < 3 && !none; ++d) {
+    for (int i = tid; i < kBins; i += 1024) h[i] = 0u;
+    __syncthreads();
+    const uint32_t mask = digit_mask_above(d);
+    const int shift = digit_shift(d);
+    for (uint32_t i = tid; i < nc; i += 1024) {
+      uint32_t key = crow[i].y;
+      if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & (kBins - 1)], 1u);
+    }
+    __syncthreads();
+    find_digit_1024(h, need, false, tmp, &s_digit, &s_above, total);
+    if (s_digit == 0xFFFFFFFFu) { none = true; prefix = 0xFFFFFFFFu; need = 0; break; }
+    prefix |= s_digit << shift;
+    need -= s_above;
+  }
+  const uint32_t tau = prefix, need_eq = none ? 0u : need;
+  // ties: the need_eq lowest slots among candidates with key == tau -> largest selected slot
+  int32_t tie_max = -1;
+  if (!none) {
+    uint32_t n_tie = 0;
+    for (uint32_t i = tid; i < nc; i += 1024) n_tie += crow[i].y == tau;
+    uint32_t tot;
+    block_exclusive_scan_1024(n_tie, tmp, tot);
+    if (tot <= need_eq) {
+      tie_max = 0x7FFFFFFF;
+    } else {
+      // radix select of the need_eq-th smallest slot among the ties (slots < 2^31; digits of 11/10/10 bits)
+      uint32_t sprefix = 0, sneed = need_eq;
+      const int shifts[3] = {20, 10, 0};
+      const uint32_t masks[3] = {0u, 0xFFF00000u, 0xFFFFFC00u};
+#pragma unroll 1
+      for (int d = 0; d < 3; ++d) {
+        for (int i = tid; i < kBins; i += 1024) h[i] = 0u;
+        __syncthreads();
+        for (uint32_t i = tid; i < nc; i += 1024) {
+          uint2 c = crow[i];
+          if (c.y == tau && (c.x & masks[d]) == sprefix) atomicAdd(&h[(c.x >> shifts[d]) & (kBins - 1)], 1u);
+        }
+        __syncthreads();
+        // ascending search: thread t owns bins 2t, 2t+1
+        const uint32_t c0 = h[2 * tid], c1 = h[2 * tid + 1];
+        uint32_t t2;
+        uint32_t ex = block_exclusive_scan_1024(c0 + c1, tmp, t2);
+        if (tid == 0) { s_digit = 0xFFFFFFFFu; s_above = 0u; }
+        __syncthreads();
+        if (ex < sneed && sneed <= ex + c0) { s_digit = 2 * tid; s_above = ex; }
+        else if (ex + c0 < sneed && sneed <= ex + c0 + c1) { s_digit = 2 * tid + 1; s_above = ex + c0; }
+        __syncthreads();
+        sprefix |= s_digit << shifts[d];
+        sneed -= s_above;
+        __syncthreads();
+      }
+      tie_max = (int32_t)sprefix;
+    }
+  }
+  // per-segment selected counts -> output offsets
+  for (int i = tid; i < n_seg; i += 1024) sc[i] = seg_gt[(int64_t)r * n_seg + i];
+  __syncthreads();
+  if (!none)
+    for (uint32_t i = tid; i < nc; i += 1024) {
+      uint2 c = crow[i];
+      bool take = c.y > tau || (c.y == tau && (int32_t)c.x <= tie_max);
+      if (take) atomicAdd(&sc[c.x / seg], 1u);
+    }
+  __syncthreads();
+  // exclusive scan over segments (n_seg <= 2048: two per thread)
+  {
+    const uint32_t a0 = 2 * tid < n_seg ? sc[2 * tid] : 0u;
+    const uint32_t a1 = 2 * tid + 1 < n_seg ? sc[2 * tid + 1] : 0u;
+    uint32_t tot;
+    uint32_t ex = block_exclusive_scan_1024(a0 + a1, tmp, tot);
+    if (2 * tid < n_seg) seg_off[(int64_t)r * n_seg + 2 * tid] = ex;
+    if (2 * tid + 1 < n_seg) seg_off[(int64_t)r * n_seg + 2 * tid + 1] = ex + a0;
+  }
+  if (tid == 0) {
+    CompactState cs;
+    cs.b0 = none ? 0xFFFFFFFFu : b0;
+    cs.k_eff = k_eff;
+    cs.tau = tau;
+    cs.need_eq = need_eq;
+    cs.tie_slot_max = tie_max;
+    cs.pad[0] = cs.pad[1] = cs.pad[2] = 0;
+    st[r] = cs;
+  }
+}
+
+// ordered write: thread t owns the 4*E consecutive slots of its part of the segment
+__global__ void __launch_bounds__(kThreads)
+topk_cwrite_kernel(const float* __restrict__ scores, int64_t N, int64_t stride, const int32_t* __restrict__ index_map,
+                   int seg, const CompactState* __restrict__ st, const uint32_t* __restrict__ seg_off, int n_seg,
+                   int32_t k, int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
+  __shared__ uint32_t tmp[8];
+  const int r = blockIdx.y;
+  const CompactState cs = st[r];
+  int32_t* orow = idx_out + (int64_t)r * k;
+  float* srow = score_out ? score_out + (int64_t)r * k : nullptr;
+  if (blockIdx.x == n_seg - 1) {
+    for (int i = (int)cs.k_eff + threadIdx.x; i < k; i += kThreads) {
+      orow[i] = -1;
+      if (srow) srow[i] = __builtin_nanf("");
+    }
+  }
+  if (cs.k_eff == 0) return;
+  const float* row = scores + (int64_t)r * stride;
+  const int32_t* map_row = index_map ? index_map + (int64_t)r * N : nullptr;
+  const int64_t s0 = (int64_t)blockIdx.x * seg;
+  const int64_t s1 = min(N, s0 + seg);
+  const int per = seg / kThreads;                    // slots per thread (multiple of 4)
+  const int64_t i0 = s0 + (int64_t)threadIdx.x * per;
+  const int64_t i1 = min(s1, i0 + per);
+  auto selected = [&](int64_t i, uint32_t key) -> bool {
+    if (key == 0u) return false;
+    if ((key >> 21) != cs.b0) return (key >> 21) > cs.b0;
+    return key > cs.tau || (key == cs.tau && (int32_t)i <= cs.tie_slot_max);
+  };
+  uint32_t n = 0;
+  for (int64_t i = i0; i < i1; i += 4) {
+    float4 v = *reinterpret_cast<const float4*>(row + i);
+    int4 mp = map_row ? *reinterpret_cast<const int4*>(map_row + i) : make_int4(0, 0, 0, 0);
+    n += selected(i + 0, mp.x < 0 ? 0u : score_key(v.x));
+    n += selected(i + 1, mp.y < 0 ? 0u : score_key(v.y));
+    n += selected(i + 2, mp.z < 0 ? 0u : score_key(v.z));
+    n += selected(i + 3, mp.w < 0 ? 0u : score_key(v.w));
+  }
+  uint32_t tot;
+  uint32_t p = seg_off[(int64_t)r * n_seg + blockIdx.x] + block_exclusive_scan(n, tmp, tot);
+  if (n == 0) return;
+  for (int64_t i = i0; i < i1; ++i) {
+    uint32_t key = score_key(row[i]);
+    if (map_row && map_row[i] < 0) key = 0u;
+    if (selected(i, key) && p < cs.k_eff) {
+      orow[p] = map_row ? map_row[i] : (int32_t)i;
+      if (srow) srow[p] = row[i];
+      ++p;
+    }
+  }
+}
+
 static int n_segments(int64_t N) { return (int)((N + kSeg - 1) / kSeg); }
+
+enum Path { kSmall, kCompact, kMultipass };
+constexpr int64_t kCandBudget = int64_t(1) << 30;     // candidate-list bytes allowed in the workspace
+
+static int compact_seg(int64_t N) {
+  int64_t seg = kSeg;
+  while ((N + seg - 1) / seg > kMaxSeg) seg *= 2;
+  return (int)seg;
+}
+
+static Path choose_path(int32_t R, int64_t N) {
+  if (N <= kSmallMax) return kSmall;
+  if ((int64_t)R * N * (int64_t)sizeof(uint2) <= kCandBudget) return kCompact;
+  return kMultipass;
+}
+
+struct CompactLayout {
+  size_t hist0, cand_count, seg_gt, seg_off, state, cand, total;
+};
+
+static CompactLayout compact_layout(int32_t R, int64_t N) {
+  CompactLayout L;
+  const int n_seg = (int)((N + compact_seg(N) - 1) / compact_seg(N));
+  size_t off = 0;
+  L.hist0 = off; off += align_up((size_t)R * kBins * 4, 256);
+  L.cand_count = off; off += align_up((size_t)R * 4, 256);
+  L.seg_gt = off; off += align_up((size_t)R * n_seg * 4, 256);
+  L.seg_off = off; off += align_up((size_t)R * n_seg * 4, 256);
+  L.state = off; off += align_up((size_t)R * sizeof(CompactState), 256);
+  L.cand = off; off += align_up((size_t)R * N * sizeof(uint2), 256);
+  L.total = off;
+  return L;
+}
 
 static size_t ws_layout(int32_t R, int64_t N, size_t* off_state, size_t* off_seg) {
   size_t hist = align_up((size_t)R * kBins * sizeof(uint32_t), 256);
@@ -310,6 +758,14 @@ static size_t ws_layout(int32_t R, int64_t N, size_t* off_state, size_t* off_seg
   return hist + state + seg;
 }
 
+static size_t workspace_for(int32_t R, int64_t N) {
+  switch (choose_path(R, N)) {
+    case kSmall: return 256;
+    case kCompact: return compact_layout(R, N).total;
+    default: return ws_layout(R, N, nullptr, nullptr);
+  }
+}
+
 }  // namespace csa2
 
 using namespace csa2;
@@ -317,7 +773,7 @@ using namespace csa2;
 extern "C" size_t csa2_topk_workspace_size(int32_t R, int64_t N, int32_t k) {
   (void)k;
   if (R <= 0 || N <= 0) return 0;
-  return ws_layout(R, N, nullptr, nullptr);
+  return workspace_for(R, N);
 }
 
 extern "C" csa2_status csa2_topk(const float* scores, int32_t R, int64_t N, int64_t row_stride, int32_t k,
@@ -329,15 +785,41 @@ extern "C" csa2_status csa2_topk(const float* scores, int32_t R, int64_t N, int6
   if (row_stride < N || row_stride % 4 != 0) return CSA2_EINVAL;
   if (!aligned(scores, 16) || (index_map && !aligned(index_map, 16)) || !aligned(idx_out, 4))
     return CSA2_EALIGN;
-  size_t off_state, off_seg;
-  size_t need = ws_layout(R, N, &off_state, &off_seg);
+  const size_t need = workspace_for(R, N);
   if (!workspace || workspace_bytes < need) return CSA2_EWORKSPACE;
   if (!aligned(workspace, 256)) return CSA2_EALIGN;
+  hipStream_t s = (hipStream_t)stream;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const Path path = choose_path(R, N);
+  if (path == kSmall) {
+    topk_small_kernel<<<R, 1024, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out);
+    return launch_status();
+  }
+  if (path == kCompact) {
+    const CompactLayout L = compact_layout(R, N);
+    const int seg = compact_seg(N);
+    const int nseg = (int)((N + seg - 1) / seg);
+    uint32_t* hist0 = reinterpret_cast<uint32_t*>(ws + L.hist0);
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + L.cand_count);
+    uint32_t* seg_gt = reinterpret_cast<uint32_t*>(ws + L.seg_gt);
+    uint32_t* seg_off = reinterpret_cast<uint32_t*>(ws + L.seg_off);
+    CompactState* st = reinterpret_cast<CompactState*>(ws + L.state);
+    uint2* cand = reinterpret_cast<uint2*>(ws + L.cand);
+    dim3 g2(nseg, R);
+    topk_cinit_kernel<<<R, kThreads, 0, s>>>(hist0, cnt);
+    topk_hist_kernel<0><<<dim3(n_segments(N), R), kThreads, 0, s>>>(scores, N, row_stride, index_map, hist0, nullptr);
+    topk_compact_kernel<<<g2, kThreads, 0, s>>>(scores, N, row_stride, index_map, k, seg, hist0, cnt, cand, N, seg_gt,
+                                                nseg);
+    topk_refine_kernel<<<R, 1024, 0, s>>>(k, seg, hist0, cnt, cand, N, seg_gt, seg_off, nseg, st);
+    topk_cwrite_kernel<<<g2, kThreads, 0, s>>>(scores, N, row_stride, index_map, seg, st, seg_off, nseg, k, idx_out,
+                                               score_out);
+    return launch_status();
+  }
+  size_t off_state, off_seg;
+  ws_layout(R, N, &off_state, &off_seg);
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws);
   RowState* st = reinterpret_cast<RowState*>(ws + off_state);
   uint32_t* seg = reinterpret_cast<uint32_t*>(ws + off_seg);
-  hipStream_t s = (hipStream_t)stream;
   const int nseg = n_segments(N);
   dim3 g2(nseg, R);
   topk_init_kernel<<<R, kThreads, 0, s>>>(hist, st);

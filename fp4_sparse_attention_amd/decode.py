@@ -18,7 +18,7 @@ import torch
 
 from . import (csa2_fp4_pack, csa2_index_full, csa2_index_reindex, csa2_topk, csa2_topk_workspace_size,
                csa2_sparse_decode, csa2_sparse_decode_workspace_size, csa2_swa_merge,
-               csa2_swa_merge_workspace_size)
+               csa2_swa_merge_workspace_size, csa2_sparse_swa_decode, csa2_sparse_swa_decode_workspace_size)
 
 LATENT = 512
 POOL_MAX = 16384
@@ -59,7 +59,7 @@ class Csa2DecodeStack:
     """
 
     def __init__(self, B: int, T: int, H: int, K: int, modes: Sequence[str], device="cuda",
-                 pool_size: int = POOL_MAX):
+                 pool_size: int = POOL_MAX, fused_attention: bool = True):
         self.B, self.T, self.H, self.K = B, T, H, K
         self.modes = tuple(modes)
         self.use_pool = "reindex" in self.modes
@@ -81,6 +81,8 @@ class Csa2DecodeStack:
                              if self.use_pool else None)
         self.ws_sparse = torch.empty(csa2_sparse_decode_workspace_size(B, H, K), dtype=u8, device=dev)
         self.ws_swa = torch.empty(csa2_swa_merge_workspace_size(B, H), dtype=u8, device=dev)
+        self.fused_attention = fused_attention
+        self.ws_fused = torch.empty(csa2_sparse_swa_decode_workspace_size(B, H, K), dtype=u8, device=dev)
         self.index_events = None
 
     def step(self, codes, scales, k_idx, layers: List[LayerIO], sigma: float, new_rows: Optional[torch.Tensor] = None,
@@ -123,10 +125,14 @@ class Csa2DecodeStack:
                 idx = prev_idx
             else:
                 raise ValueError(mode)
-            csa2_sparse_decode(io.q_lat, codes, scales, idx, sigma, self.o[li], self.lse[li],
-                               workspace=self.ws_sparse, stream=stream)
-            csa2_swa_merge(io.q_lat, io.swa, io.swa_start, io.swa_len, sigma, self.o[li], self.lse[li],
-                           o_sparse=self.o[li], lse_sparse=self.lse[li], workspace=self.ws_swa, stream=stream)
+            if self.fused_attention:
+                csa2_sparse_swa_decode(io.q_lat, codes, scales, idx, io.swa, io.swa_start, io.swa_len, sigma,
+                                       self.o[li], self.lse[li], workspace=self.ws_fused, stream=stream)
+            else:
+                csa2_sparse_decode(io.q_lat, codes, scales, idx, sigma, self.o[li], self.lse[li],
+                                   workspace=self.ws_sparse, stream=stream)
+                csa2_swa_merge(io.q_lat, io.swa, io.swa_start, io.swa_len, sigma, self.o[li], self.lse[li],
+                               o_sparse=self.o[li], lse_sparse=self.lse[li], workspace=self.ws_swa, stream=stream)
         return self.o, self.lse
 
     def layer_idx(self, li: int) -> torch.Tensor:

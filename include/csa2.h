@@ -117,8 +117,9 @@ csa2_status csa2_fp4_unpack(const uint8_t* codes, const uint8_t* scales, int64_t
  *   row_limit  int64 [R] last visible position of each row (causal prefill),
  *              or NULL for all T positions
  *   scores     fp32 [R][T]
- * Products of E4M3 values are exact in fp32; the 64-term sum is accumulated in
- * fp32 by the matrix cores.
+ * Every score is the exact sum rounded once to fp32 (E4M3 products are exact
+ * and the f16 matrix-core path sums the 64 terms without intermediate
+ * rounding), so equal exact scores give equal fp32 scores.
  * Errors: EINVAL (null pointer, R/B/T <= 0, R != B without row_seq), ESHAPE
  * (T not a multiple of 4, T >= 2^31), EALIGN.
  * ------------------------------------------------------------------------- */
@@ -218,6 +219,26 @@ csa2_status csa2_swa_merge(const uint16_t* q_lat, int32_t R, int32_t H,
                            const float* o_sparse, const float* lse_sparse,
                            float* o_out, float* lse_out,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Sparse attention and window merge in one call: the result equals
+ * csa2_sparse_decode followed by csa2_swa_merge with that sparse result (one
+ * softmax over the union of the selected cache rows and the window rows), but
+ * the window rows are processed as one more key chunk of the same launch and a
+ * single combine step produces o and lse (two launches instead of four).
+ *
+ * Arguments as in csa2_sparse_decode and csa2_swa_merge; o fp32 [R][H][512],
+ * lse fp32 [R][H].
+ *   workspace >= csa2_sparse_swa_decode_workspace_size(R, H, K) bytes
+ * Errors: EINVAL, ESHAPE (H), EWORKSPACE, EALIGN.
+ * ------------------------------------------------------------------------- */
+size_t csa2_sparse_swa_decode_workspace_size(int32_t R, int32_t H, int32_t K);
+csa2_status csa2_sparse_swa_decode(const uint16_t* q_lat, int32_t R, int32_t H,
+                                   const uint8_t* codes, const uint8_t* scales, int32_t B, int64_t T,
+                                   const int32_t* row_seq, const int32_t* idx, int32_t K,
+                                   const uint16_t* swa, int32_t S, const int32_t* swa_start,
+                                   const int32_t* swa_len, float softmax_scale, float* o, float* lse,
+                                   void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -107,9 +107,9 @@ class DecodeWorkload:
         out = np.empty((positions.shape[0], 512))
         chunk = positions // self.chunk_rows
         for c in np.unique(chunk):
-            rows = self.latent_chunk(b, int(c)).to(torch.float64).cpu().numpy()
             sel = chunk == c
-            out[sel] = rows[positions[sel] - c * self.chunk_rows]
+            local = torch.from_numpy(positions[sel] - c * self.chunk_rows).to(self.dev)
+            out[sel] = self.latent_chunk(b, int(c))[local].to(torch.float64).cpu().numpy()
         return out
 
     def k_idx_host(self, b):

@@ -76,7 +76,8 @@ def test_topk_argument_errors_and_workspace():
 def test_attention_argument_errors_and_workspace():
     L = F.lib()
     assert F.csa2_sparse_decode_workspace_size(64, 64, 2048) > 64 * 64 * 512 * 4
-    assert F.csa2_swa_merge_workspace_size(8, 64) >= 8 * 4 * 64 * 512 * 4
+    assert F.csa2_swa_merge_workspace_size(8, 64) >= 8 * 64 * 512 * 4
+    assert F.csa2_sparse_swa_decode_workspace_size(8, 64, 2048) > F.csa2_sparse_decode_workspace_size(8, 64, 2048)
     args = [DUMMY, 1, 64, DUMMY, DUMMY, 1, 4096, NULL, DUMMY, 256, 0.1, DUMMY, DUMMY, DUMMY, 1 << 30, NULL]
     bad_h = list(args); bad_h[2] = 20
     assert L.csa2_sparse_decode(*bad_h) == 2

@@ -148,3 +148,32 @@ def test_sparse_decode_deterministic():
         F.csa2_sparse_decode(q, codes, scales, idx, SIGMA, o, lse)
         outs.append((o, lse))
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("B,T,H,K", [(2, 3000, 64, 2048), (3, 700, 16, 100)])
+def test_fused_sparse_window_vs_oracle(B, T, H, K):
+    """csa2_sparse_swa_decode = sparse attention over idx and the window rows in one softmax."""
+    dev = device()
+    rng = np.random.default_rng(T + K)
+    lat, ref_rows = _cache(B, T, seed=31)
+    codes, scales = _gpu_cache(lat, dev)
+    q = W.bf16_normal(32, (B, H, 512), std=0.5)
+    S = 140
+    swa = W.bf16_normal(33, (B, S, 512))
+    start = np.array([12, 0, 3][:B], dtype=np.int32)
+    length = np.array([128, 0, 57][:B], dtype=np.int32)
+    idx = np.full((B, K), -1, dtype=np.int32)
+    for b in range(B):
+        n = min(K, T) - 5 * b
+        idx[b, :n] = np.sort(rng.choice(T, n, replace=False))
+    o = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    F.csa2_sparse_swa_decode(q.to(dev), codes, scales, torch.from_numpy(idx).to(dev), swa.to(dev),
+                             torch.from_numpy(start).to(dev), torch.from_numpy(length).to(dev), SIGMA, o, lse)
+    qf = q.to(torch.float64).numpy()
+    swf = swa.to(torch.float64).numpy()
+    for b in range(B):
+        o_s, l_s = OA.sparse_attend(qf[b], ref_rows[b], idx[b], SIGMA)
+        o_w, l_w = OA.attend(qf[b], OA.window_rows(swf[b], int(start[b]), int(length[b])), SIGMA)
+        o_ref, l_ref = OA.merge(o_s, l_s, o_w, l_w)
+        assert_attention_close(o[b].cpu().numpy(), lse[b].cpu().numpy(), o_ref, l_ref, f"row {b}")

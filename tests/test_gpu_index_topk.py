@@ -31,8 +31,23 @@ def test_index_full_scores(B, T):
         exact = OI.full_scores(q[b].numpy(), k[b].numpy())
         bound = _score_bound(q[b].numpy(), k[b].numpy())
         assert np.all(np.abs(got[b] - exact) <= bound + 1e-30), (b, np.max(np.abs(got[b] - exact)))
-        n_exact += int(np.sum(got[b] == exact.astype(np.float32)))
-    print(f"scores equal to the fp32 rounding of the exact value: {n_exact}/{B * T}")
+        # the f16 matrix path sums exactly and rounds once: bit-equal to fp32(exact)
+        assert np.array_equal(got[b].astype(np.float32), exact.astype(np.float32)), b
+
+
+def test_index_scores_exact_on_wide_range_keys():
+    # keys spanning the whole E4M3 range (subnormals to 448): the sums need far more
+    # than 24 bits, yet every score must be the fp32 rounding of the exact value
+    dev = device()
+    g = torch.Generator().manual_seed(17)
+    T = 8192
+    x = torch.randn((1, T, 64), generator=g) * torch.exp2(torch.randint(-10, 8, (1, T, 64), generator=g).float())
+    k = x.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    q = (torch.randn((1, 64), generator=g) * 4).to(torch.float8_e4m3fn).view(torch.uint8)
+    scores = torch.empty((1, T), dtype=torch.float32, device=dev)
+    F.csa2_index_full(q.to(dev), k.to(dev), scores)
+    exact = OI.full_scores(q[0].numpy(), k[0].numpy())
+    assert np.array_equal(scores[0].cpu().numpy(), exact.astype(np.float32))
 
 
 def test_index_full_causal_rows_and_row_seq():
@@ -51,8 +66,7 @@ def test_index_full_causal_rows_and_row_seq():
         exact = OI.full_scores(q[r].numpy(), k[b].numpy(), limit=int(limit[r]))
         fin = np.isfinite(exact)
         assert np.array_equal(np.isneginf(got[r]), ~fin), r
-        bound = _score_bound(q[r].numpy(), k[b].numpy())[fin]
-        assert np.all(np.abs(got[r][fin] - exact[fin]) <= bound + 1e-30), r
+        assert np.array_equal(got[r][fin], exact[fin].astype(np.float32)), r
 
 
 def test_index_prefill_block_rows_same_sequence():
@@ -70,7 +84,7 @@ def test_index_prefill_block_rows_same_sequence():
         exact = OI.full_scores(q[r].numpy(), k[0].numpy(), limit=int(limit[r]))
         fin = np.isfinite(exact)
         assert np.array_equal(np.isneginf(got[r]), ~fin)
-        assert np.all(np.abs(got[r][fin] - exact[fin]) <= _score_bound(q[r].numpy(), k[0].numpy())[fin] + 1e-30)
+        assert np.array_equal(got[r][fin], exact[fin].astype(np.float32)), r
 
 
 def test_reindex_matches_full_bitwise_on_pool():
@@ -164,3 +178,50 @@ def test_full_scores_then_topk_swap_rule():
         exact = OI.full_scores(q[b].numpy(), k[b].numpy())
         ref = OT.topk(exact, K)
         assert_topk_swap_rule(idx[b].cpu().numpy(), ref, lambda p: exact[p], f"row {b}")
+
+
+@pytest.mark.parametrize("R,N,k", [(2, 32768, 2048), (3, 32772, 100), (8, 1 << 20, 16384)])
+def test_topk_paths_boundaries_bit_exact(R, N, k):
+    # 32768 = largest LDS-resident row; 32772 and 1M take the candidate-compaction path
+    dev = device()
+    rng = np.random.default_rng(N % 1000 + k)
+    s = _synthetic_scores(rng, R, N)
+    idx = torch.empty((R, k), dtype=torch.int32, device=dev)
+    so = torch.empty((R, k), dtype=torch.float32, device=dev)
+    F.csa2_topk(torch.from_numpy(s).to(dev), k, idx, score_out=so)
+    gi, gs = idx.cpu().numpy(), so.cpu().numpy()
+    for r in range(R):
+        ri, rs = OT.topk_with_scores(s[r].astype(np.float64), k)
+        assert np.array_equal(gi[r], ri), r
+        assert np.array_equal(gs[r][~np.isnan(rs)], rs[~np.isnan(rs)].astype(np.float32))
+
+
+@pytest.mark.parametrize("N", [4096, 65536])
+def test_topk_massive_ties(N):
+    # few distinct values: the k-th key is shared by thousands of slots, ties go to the lowest slots
+    dev = device()
+    rng = np.random.default_rng(N)
+    R, k = 3, 1000
+    s = rng.integers(0, 4, (R, N)).astype(np.float32)
+    s[1] = 7.0                                           # every slot equal
+    s[2, ::3] = -np.inf
+    idx = torch.empty((R, k), dtype=torch.int32, device=dev)
+    F.csa2_topk(torch.from_numpy(s).to(dev), k, idx)
+    gi = idx.cpu().numpy()
+    for r in range(R):
+        assert np.array_equal(gi[r], OT.topk(s[r].astype(np.float64), k)), r
+    assert gi[1].tolist() == list(range(k))
+
+
+def test_topk_multipass_path_sampled_rows():
+    # R * N * 8 bytes above the candidate budget -> three full histogram passes
+    dev = device()
+    R, N, k = 1040, 131072, 2048
+    g = torch.Generator(device=dev).manual_seed(5)
+    s = torch.randn((R, N), generator=g, device=dev) * 8
+    s[:, ::7] = torch.round(s[:, ::7])
+    idx = torch.empty((R, k), dtype=torch.int32, device=dev)
+    F.csa2_topk(s, k, idx)
+    for r in (0, 519, R - 1):
+        row = s[r].cpu().numpy().astype(np.float64)
+        assert np.array_equal(idx[r].cpu().numpy(), OT.topk(row, k)), r
