@@ -38,6 +38,9 @@ constexpr int kKT = 32;                  // keys per tile
 constexpr int kXwStride = 144;           // halfs per key row of a wave's slice (128 + 16 pad)
 constexpr int kSStride = 36;             // floats per head row of a partial-score tile
 constexpr int kPStride = 40;             // halfs per head row of P
+constexpr int kMaxChunkTiles = 64;       // tiles per chunk at most
+constexpr int kMaxChunkKeys = kMaxChunkTiles * kKT;
+constexpr float kRescaleSlack = 8.0f;    // keep the reference max until exceeded by 2^8
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -94,21 +97,22 @@ struct AttnArgs {
   float* ml_part;                 // [R][n_chunks][H][2]
 };
 
-// raw global data of the lane's two keys for one tile
+// raw FP4 data of the lane's two keys for one tile (prefetched one tile ahead)
 struct RawTile {
-  uint4 v[2][4];      // FP4: v[mt][0] = 16 code bytes; window: 64 bytes of bf16
-  uint32_t sc[2];     // FP4: 2 scale bytes
+  uint4 v[2];         // 16 code bytes (32 channels) per key
+  uint32_t sc[2];     // 2 scale bytes per key
   int valid[2];
 };
 
 template <int NT>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(256, 2)
 attn_chunk_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) _Float16 xw[4 * kKT * kXwStride];
   __shared__ __attribute__((aligned(16))) float sp[4 * NT * 16 * kSStride];
   __shared__ __attribute__((aligned(16))) _Float16 pp[NT * 16 * kPStride];
   __shared__ float s_alpha[NT * 16];
   __shared__ int s_valid[kKT];
+  __shared__ int s_pos[kMaxChunkKeys];        // this chunk's cache positions (-1: skip)
 
   const int chunk = blockIdx.x;
   const int r = blockIdx.y;
@@ -118,6 +122,7 @@ attn_chunk_kernel(const AttnArgs a) {
   const int m = lane & 15;
   const int g = lane >> 4;
   const int H = a.H;
+  const int hbase = blockIdx.z * NT * 16;        // this workgroup's first head
   const int seq = a.row_seq ? a.row_seq[r] : r;
   const bool is_window = chunk >= a.n_sparse_chunks;
 
@@ -139,7 +144,7 @@ attn_chunk_kernel(const AttnArgs a) {
   f16x8 qb[NT][4];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const uint16_t* qrow = a.q_lat + ((int64_t)r * H + 16 * nt + m) * kLatent + cbase + 32 * g;
+    const uint16_t* qrow = a.q_lat + ((int64_t)r * H + hbase + 16 * nt + m) * kLatent + cbase + 32 * g;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qb[nt][ks] = bf16x8_to_f16(*reinterpret_cast<const uint4*>(qrow + 8 * ks));
   }
@@ -152,30 +157,33 @@ attn_chunk_kernel(const AttnArgs a) {
   float m_run = -__builtin_inff();
   float l_run = 0.f;
 
-  RawTile raw;
-  auto load_tile = [&](int tile) {
+  // positions of this chunk's keys, staged once so that the gathers below
+  // do not wait on dependent index loads
+  if (!is_window) {
+    for (int i = tid; i < n_tiles * kKT; i += 256) {
+      const int kk = k_begin + i;
+      int pos = kk < k_end ? a.idx[(int64_t)r * a.K + kk] : -1;
+      s_pos[i] = (pos >= 0 && pos < a.T) ? pos : -1;
+    }
+    __syncthreads();
+  }
+
+  // sparse chunks: gather the FP4 codes + scales of a tile's keys into a register
+  // buffer; two buffers alternate so that two tiles are in flight
+  auto load_tile = [&](RawTile& raw, int tile) {
+    if (is_window) return;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const int kk = k_begin + tile * kKT + 16 * mt + m;
-      if (!is_window) {
-        int pos = kk < k_end ? a.idx[(int64_t)r * a.K + kk] : -1;
-        bool ok = pos >= 0 && pos < a.T;
-        raw.valid[mt] = ok;
-        if (ok) {
-          const int64_t row = (int64_t)seq * a.T + pos;
-          raw.v[mt][0] = *reinterpret_cast<const uint4*>(a.codes + row * kCodesRow + 64 * wave + 16 * g);
-          raw.sc[mt] = *reinterpret_cast<const uint16_t*>(a.scales + row * kScalesRow + 8 * wave + 2 * g);
-        } else {
-          raw.v[mt][0] = make_uint4(0, 0, 0, 0);
-          raw.sc[mt] = 0;
-        }
+      const int pos = s_pos[tile * kKT + 16 * mt + m];
+      const bool ok = pos >= 0;
+      raw.valid[mt] = ok;
+      if (ok) {
+        const int64_t row = (int64_t)seq * a.T + pos;
+        raw.v[mt] = *reinterpret_cast<const uint4*>(a.codes + row * kCodesRow + 64 * wave + 16 * g);
+        raw.sc[mt] = *reinterpret_cast<const uint16_t*>(a.scales + row * kScalesRow + 8 * wave + 2 * g);
       } else {
-        bool ok = kk < k_end;
-        raw.valid[mt] = ok;
-        const uint4* p = reinterpret_cast<const uint4*>(
-            a.swa + ((int64_t)seq * a.S + w_start + (ok ? kk : 0)) * kLatent + cbase + 32 * g);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) raw.v[mt][j] = ok ? p[j] : make_uint4(0, 0, 0, 0);
+        raw.v[mt] = make_uint4(0, 0, 0, 0);
+        raw.sc[mt] = 0;
       }
     }
   };
@@ -184,44 +192,52 @@ attn_chunk_kernel(const AttnArgs a) {
   float* spmine = sp + wave * NT * 16 * kSStride;
   const float neg_inf = -__builtin_inff();
 
-  if (n_tiles > 0) load_tile(0);
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    // ---- dequantise this tile's slice into A operands and the key-major LDS slice
-    f16x8 xa[2][4];
+  auto process = [&](RawTile& raw, int tile) {
+    // ---- per 16-key half-tile: dequantise this wave's slice into A operands,
+    //      store it key-major in LDS, and form the partial scores
+    //      S^T[16mt + 4g + i][16nt + m] over the wave's 128 channels
+    int valid_mt[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
+      f16x8 xa[4];
       if (!is_window) {
-        uint32_t cw[4] = {raw.v[mt][0].x, raw.v[mt][0].y, raw.v[mt][0].z, raw.v[mt][0].w};
+        const uint32_t cw[4] = {raw.v[mt].x, raw.v[mt].y, raw.v[mt].z, raw.v[mt].w};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          float sf = e4m3_to_f32((raw.sc[mt] >> (8 * (ks >> 1))) & 0xFFu);
-          f16x2 s2 = {(_Float16)sf, (_Float16)sf};
-          xa[mt][ks] = fp4x8_to_f16(cw[ks], s2);
+          const float sf = e4m3_to_f32((raw.sc[mt] >> (8 * (ks >> 1))) & 0xFFu);
+          const f16x2 s2 = {(_Float16)sf, (_Float16)sf};
+          xa[ks] = fp4x8_to_f16(cw[ks], s2);
         }
+        valid_mt[mt] = raw.valid[mt];
       } else {
+        // window rows: bf16 -> f16, loaded when needed (a window chunk has <= 4 tiles)
+        const int kk = k_begin + tile * kKT + 16 * mt + m;
+        const bool ok = kk < k_end;
+        valid_mt[mt] = ok;
+        const uint4* p = reinterpret_cast<const uint4*>(
+            a.swa + ((int64_t)seq * a.S + w_start + (ok ? kk : 0)) * kLatent + cbase + 32 * g);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) xa[mt][ks] = bf16x8_to_f16(raw.v[mt][ks]);
+        for (int ks = 0; ks < 4; ++ks) xa[ks] = bf16x8_to_f16(ok ? p[ks] : make_uint4(0, 0, 0, 0));
       }
       f16x8* dst = reinterpret_cast<f16x8*>(xmine + (16 * mt + m) * kXwStride + 32 * g);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) dst[ks] = xa[mt][ks];
+      for (int ks = 0; ks < 4; ++ks) dst[ks] = xa[ks];
+      f32x4 sacc[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) sacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) sacc[nt] = mfma16(xa[ks], qb[nt][ks], sacc[nt]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        *reinterpret_cast<f32x4*>(spmine + (16 * nt + m) * kSStride + 16 * mt + 4 * g) = sacc[nt];
+      if (mt == 1 && tile + 2 < n_tiles) load_tile(raw, tile + 2);   // buffer free: refill two tiles ahead
     }
     if (wave == 0 && g == 0) {
-      s_valid[m] = raw.valid[0];
-      s_valid[16 + m] = raw.valid[1];
+      s_valid[m] = valid_mt[0];
+      s_valid[16 + m] = valid_mt[1];
     }
-    if (tile + 1 < n_tiles) load_tile(tile + 1);      // in flight during the math below
-
-    // ---- partial scores over this wave's channels: S^T[16mt + 4g + i][16nt + m]
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mfma16(xa[mt][ks], qb[nt][ks], acc);
-        *reinterpret_cast<f32x4*>(spmine + (16 * nt + m) * kSStride + 16 * mt + 4 * g) = acc;
-      }
     __syncthreads();
 
     // ---- softmax for heads [16w, 16w+16): lane (m, g) owns head 16w+m, keys 8g + [0, 8)
@@ -245,7 +261,8 @@ attn_chunk_kernel(const AttnArgs a) {
       }
       mx = fmaxf(mx, shfl_xor_f(mx, 16));
       mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
+      // P = 2^(s - m_ref) stays <= 2^8 in f16; m_ref moves only past that slack
+      const float m_new = (mx > m_run + kRescaleSlack) ? mx : m_run;
       const bool live = m_new != neg_inf;
       const float alpha = live ? exp2f(m_run - m_new) : 1.f;
       float psum = 0.f;
@@ -293,10 +310,18 @@ attn_chunk_kernel(const AttnArgs a) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) oacc[t][nt] = mfma16(xt, pb[nt], oacc[t][nt]);
     }
+  };
+
+  RawTile buf0, buf1;
+  if (n_tiles > 0) load_tile(buf0, 0);
+  if (n_tiles > 1) load_tile(buf1, 1);
+  for (int tile = 0; tile < n_tiles; tile += 2) {
+    process(buf0, tile);
+    if (tile + 1 < n_tiles) process(buf1, tile + 1);
   }
 
   // ---- this chunk's partial: unnormalised O, and (m, l) from the softmax owners
-  const int64_t prow = ((int64_t)r * a.n_chunks + chunk) * H;
+  const int64_t prow = ((int64_t)r * a.n_chunks + chunk) * H + hbase;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     float* op = a.o_part + (prow + 16 * nt + m) * kLatent + cbase + 4 * g;
@@ -363,15 +388,19 @@ struct Plan {
   int n_sparse;
 };
 
-// About one workgroup per CU in total (the kernel runs one four-wave workgroup
-// per CU), at least 4 tiles per chunk so that the partial outputs stay small
-// next to the gathered rows.
-static Plan sparse_plan(int32_t R, int32_t K) {
+static int head_groups(int32_t H) { return H % 32 == 0 ? H / 32 : H / 16; }
+
+// About two workgroups per CU in total (two four-wave workgroups fit a CU), at
+// least 4 tiles per chunk so that the partial outputs stay small next to the
+// gathered rows.
+static Plan sparse_plan(int32_t R, int32_t H, int32_t K) {
   int tiles = (K + kKT - 1) / kKT;
   if (tiles < 1) tiles = 1;
-  int want = (256 + R - 1) / R;
+  const int64_t per_chunk = (int64_t)R * head_groups(H);
+  int want = (int)((512 + per_chunk - 1) / per_chunk);
   int tpc = (tiles + want - 1) / want;
   if (tpc < 4) tpc = 4;
+  if (tpc > kMaxChunkTiles) tpc = kMaxChunkTiles;
   if (tpc > tiles) tpc = tiles;
   return Plan{tpc, (tiles + tpc - 1) / tpc};
 }
@@ -385,13 +414,15 @@ static size_t partial_bytes(int32_t R, int32_t H, int n_chunks, size_t* off_ml) 
 
 static bool heads_ok(int32_t H) { return H == 16 || H == 32 || H == 48 || H == 64; }
 
+// Heads are split into groups of 32 (or 16 when H is not a multiple of 32),
+// one workgroup per group: the 32-head kernel fits two waves per SIMD and two
+// workgroups per CU, which hides barrier and memory latency better than one
+// 64-head workgroup; the price is dequantising each tile once per group.
 static void launch_chunks(const AttnArgs& a, int R, hipStream_t s) {
-  dim3 grid(a.n_chunks, R);
-  switch (a.H / 16) {
-    case 1: attn_chunk_kernel<1><<<grid, 256, 0, s>>>(a); break;
-    case 2: attn_chunk_kernel<2><<<grid, 256, 0, s>>>(a); break;
-    case 3: attn_chunk_kernel<3><<<grid, 256, 0, s>>>(a); break;
-    default: attn_chunk_kernel<4><<<grid, 256, 0, s>>>(a); break;
+  if (a.H % 32 == 0) {
+    attn_chunk_kernel<2><<<dim3(a.n_chunks, R, head_groups(a.H)), 256, 0, s>>>(a);
+  } else {
+    attn_chunk_kernel<1><<<dim3(a.n_chunks, R, head_groups(a.H)), 256, 0, s>>>(a);
   }
 }
 
@@ -402,7 +433,7 @@ static csa2_status attention_call(const uint16_t* q_lat, int32_t R, int32_t H, c
                                   const int32_t* swa_start, const int32_t* swa_len, float softmax_scale,
                                   const float* o_prev, const float* lse_prev, float* o, float* lse,
                                   void* workspace, size_t workspace_bytes, void* stream) {
-  Plan p = idx ? sparse_plan(R, K) : Plan{0, 0};
+  Plan p = idx ? sparse_plan(R, H, K) : Plan{0, 0};
   AttnArgs a;
   a.q_lat = q_lat; a.H = H; a.codes = codes; a.scales = scales; a.T = T; a.row_seq = row_seq;
   a.idx = idx; a.K = K; a.n_sparse_chunks = p.n_sparse; a.tiles_per_chunk = p.tiles_per_chunk;
@@ -427,7 +458,7 @@ using namespace csa2;
 
 extern "C" size_t csa2_sparse_decode_workspace_size(int32_t R, int32_t H, int32_t K) {
   if (R <= 0 || H <= 0 || K <= 0) return 0;
-  return partial_bytes(R, H, sparse_plan(R, K).n_sparse, nullptr);
+  return partial_bytes(R, H, sparse_plan(R, H, K).n_sparse, nullptr);
 }
 
 extern "C" csa2_status csa2_sparse_decode(const uint16_t* q_lat, int32_t R, int32_t H, const uint8_t* codes,
@@ -469,7 +500,7 @@ extern "C" csa2_status csa2_swa_merge(const uint16_t* q_lat, int32_t R, int32_t 
 
 extern "C" size_t csa2_sparse_swa_decode_workspace_size(int32_t R, int32_t H, int32_t K) {
   if (R <= 0 || H <= 0 || K <= 0) return 0;
-  return partial_bytes(R, H, sparse_plan(R, K).n_sparse + 1, nullptr);
+  return partial_bytes(R, H, sparse_plan(R, H, K).n_sparse + 1, nullptr);
 }
 
 extern "C" csa2_status csa2_sparse_swa_decode(const uint16_t* q_lat, int32_t R, int32_t H, const uint8_t* codes,

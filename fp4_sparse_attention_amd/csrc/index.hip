@@ -7,10 +7,13 @@
 // scale) and multiplied on the f16 matrix cores:
 //   v_mfma_f32_32x32x16_f16:  C[32 x 32] += A[32 x 16] * B[16 x 32], four k-steps
 // with A = up to 32 query rows of one sequence and B = 32 keys.  On gfx950 this
-// instruction forms the 16-term dot product exactly and rounds once, so every
-// score equals the fp32 rounding of the exact sum (the fp8 matrix path does
-// not: its internal accumulation keeps only ~20 bits below the largest
-// product).  Lane l owns row/column (l % 32) and one 32-byte half of the 64-d
+// instruction forms each 16-term dot product exactly and rounds it once into
+// the fp32 accumulator, so a score carries at most four roundings (one per
+// k-step, error <= 2^-22 * sum |q_d k_d|); whenever the running sums fit in 24
+// bits -- as for unit-normal E4M3 inputs -- the score is the exact value
+// rounded once.  (The fp8 matrix path is not used: its internal accumulation
+// keeps only ~20 bits below the largest product.)  Lane l owns row/column
+// (l % 32) and one 32-byte half of the 64-d
 // key, so a wave loads a 2 KB tile of 32 consecutive keys with two 16-byte
 // loads per lane (fully coalesced); A and B use the same lane->k map.
 // Output C: lane l, register v holds column l % 32 and row

@@ -47,6 +47,11 @@ __device__ __forceinline__ uint32_t score_key(float x) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// inverse of score_key for visible keys (a -0 score comes back as +0)
+__device__ __forceinline__ float key_score(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
 __device__ __forceinline__ uint32_t slot_key(const float* row, const int32_t* map_row, int64_t i) {
   uint32_t k = score_key(row[i]);
   if (map_row && map_row[i] < 0) k = 0u;
@@ -82,12 +87,22 @@ topk_hist_kernel(const float* __restrict__ scores, int64_t N, int64_t stride, co
     const int shift = digit_shift(D);
     const int64_t b0 = (int64_t)blockIdx.x * kSeg;
     const int64_t b1 = min(N, b0 + kSeg);
-    for (int64_t i = b0 + threadIdx.x * 4; i < b1; i += kThreads * 4) {
-      // N is a multiple of 4, so a 4-slot group never straddles the row end
-      float4 v = *reinterpret_cast<const float4*>(row + i);
-      int4 mp = map_row ? *reinterpret_cast<const int4*>(map_row + i) : make_int4(0, 0, 0, 0);
-      uint32_t k4[4] = {score_key(v.x), score_key(v.y), score_key(v.z), score_key(v.w)};
-      int m4[4] = {mp.x, mp.y, mp.z, mp.w};
+    // kSeg = 8 x (256 threads x 4 slots): all eight 16-byte loads are issued first
+    // (N is a multiple of 4, so a 4-slot group never straddles the row end)
+    float4 v[8];
+    int4 mp[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int64_t i = b0 + (int64_t)q * kThreads * 4 + threadIdx.x * 4;
+      v[q] = i < b1 ? *reinterpret_cast<const float4*>(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      mp[q] = (map_row && i < b1) ? *reinterpret_cast<const int4*>(map_row + i) : make_int4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int64_t i = b0 + (int64_t)q * kThreads * 4 + threadIdx.x * 4;
+      if (i >= b1) continue;
+      uint32_t k4[4] = {score_key(v[q].x), score_key(v[q].y), score_key(v[q].z), score_key(v[q].w)};
+      int m4[4] = {mp[q].x, mp[q].y, mp[q].z, mp[q].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint32_t k = m4[j] < 0 ? 0u : k4[j];
@@ -362,45 +377,81 @@ topk_small_kernel(const float* __restrict__ scores, int N, int64_t stride, const
   __shared__ uint32_t keys[kSmallMax];
   __shared__ uint32_t h[kBins];
   __shared__ uint32_t tmp[32];
+  __shared__ uint32_t red[3][16];
   __shared__ uint32_t s_digit, s_above;
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const float* row = scores + (int64_t)r * stride;
   const int32_t* map_row = index_map ? index_map + (int64_t)r * N : nullptr;
-  for (int i = tid * 4; i < N; i += 4096) {
-    float4 v = *reinterpret_cast<const float4*>(row + i);
-    int4 mp = map_row ? *reinterpret_cast<const int4*>(map_row + i) : make_int4(0, 0, 0, 0);
-    keys[i + 0] = mp.x < 0 ? 0u : score_key(v.x);
-    keys[i + 1] = mp.y < 0 ? 0u : score_key(v.y);
-    keys[i + 2] = mp.z < 0 ? 0u : score_key(v.z);
-    keys[i + 3] = mp.w < 0 ? 0u : score_key(v.w);
-  }
-  uint32_t prefix = 0, need = 0, k_eff = 0;
-#pragma unroll 1
-  for (int d = 0; d < 3; ++d) {
-    for (int i = tid; i < kBins; i += 1024) h[i] = 0u;
-    __syncthreads();
-    const uint32_t mask = digit_mask_above(d);
-    const int shift = digit_shift(d);
-    if (d == 0 || need > 0) {
-      for (int i = tid; i < N; i += 1024) {
-        uint32_t key = keys[i];
-        if (key != 0u && (key & mask) == prefix) atomicAdd(&h[(key >> shift) & (kBins - 1)], 1u);
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, nvis = 0u;
+  {
+    // all of this thread's loads are issued before any is used
+    constexpr int kIt = kSmallMax / 4096;
+    float4 v[kIt];
+    int4 mp[kIt];
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int i = tid * 4 + it * 4096;
+      v[it] = i < N ? *reinterpret_cast<const float4*>(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      mp[it] = (map_row && i < N) ? *reinterpret_cast<const int4*>(map_row + i) : make_int4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int i = tid * 4 + it * 4096;
+      if (i < N) {
+        uint32_t k4[4] = {mp[it].x < 0 ? 0u : score_key(v[it].x), mp[it].y < 0 ? 0u : score_key(v[it].y),
+                          mp[it].z < 0 ? 0u : score_key(v[it].z), mp[it].w < 0 ? 0u : score_key(v[it].w)};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          keys[i + j] = k4[j];
+          if (k4[j] != 0u) { kmin = min(kmin, k4[j]); kmax = max(kmax, k4[j]); ++nvis; }
+        }
       }
     }
-    __syncthreads();
-    uint32_t total;
-    find_digit_1024(h, d == 0 ? 0xFFFFFFFFu : need, d == 0, tmp, &s_digit, &s_above, total);
-    if (d == 0) {
-      k_eff = total < (uint32_t)k ? total : (uint32_t)k;
-      need = k_eff;
-      find_digit_1024(h, need, true, tmp, &s_digit, &s_above, total);
-    }
-    if (need == 0 || s_digit == 0xFFFFFFFFu) { need = 0; prefix = 0xFFFFFFFFu; break; }
-    prefix |= s_digit << shift;
-    need -= s_above;
   }
-  const uint32_t tau = prefix, need_eq = need;
+  // visible count and the key range: the radix digits start at the highest bit
+  // in which the visible keys differ, so clustered scores still spread over the bins
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor(kmin, o, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor(kmax, o, 64));
+    nvis += __shfl_xor(nvis, o, 64);
+  }
+  if (lane == 0) { red[0][wave] = kmin; red[1][wave] = kmax; red[2][wave] = nvis; }
+  __syncthreads();
+  kmin = 0xFFFFFFFFu; kmax = 0u; nvis = 0u;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) { kmin = min(kmin, red[0][w]); kmax = max(kmax, red[1][w]); nvis += red[2][w]; }
+  const uint32_t k_eff = nvis < (uint32_t)k ? nvis : (uint32_t)k;
+  uint32_t need = k_eff;
+  uint32_t prefix = 0xFFFFFFFFu;
+  if (k_eff > 0) {
+    const uint32_t diff = kmin ^ kmax;
+    int hi = diff ? 31 - __builtin_clz(diff) : -1;           // highest unresolved bit
+    prefix = hi >= 31 ? 0u : (kmax & ~((2u << hi) - 1u));      // bits above hi are shared
+    if (hi < 0) prefix = kmax;
+#pragma unroll 1
+    while (hi >= 0) {
+      const int width = hi + 1 < 11 ? hi + 1 : 11;
+      const int shift = hi + 1 - width;
+      const uint32_t bmask = (1u << width) - 1u;
+      for (int i = tid; i < kBins; i += 1024) h[i] = 0u;
+      __syncthreads();
+      for (int i = tid; i < N; i += 1024) {
+        const uint32_t key = keys[i];
+        const bool match = hi == 31 ? true : ((key >> (hi + 1)) == (prefix >> (hi + 1)));
+        if (key != 0u && match) atomicAdd(&h[(key >> shift) & bmask], 1u);
+      }
+      __syncthreads();
+      uint32_t total;
+      find_digit_1024(h, need, false, tmp, &s_digit, &s_above, total);
+      prefix |= s_digit << shift;
+      need -= s_above;
+      hi = shift - 1;
+    }
+  }
+  const uint32_t tau = prefix, need_eq = k_eff > 0 ? need : 0u;
   int32_t* orow = idx_out + (int64_t)r * k;
   float* srow = score_out ? score_out + (int64_t)r * k : nullptr;
   // ordered write: thread t owns slots [t*E, t*E + E)
@@ -415,7 +466,7 @@ topk_small_kernel(const float* __restrict__ scores, int N, int64_t stride, const
     }
   uint32_t tot;
   uint32_t ex = block_exclusive_scan_1024((n_eq << 16) | n_gt, tmp, tot);
-  if (k_eff > 0) {
+  if (k_eff > 0 && (n_gt | n_eq)) {
     uint32_t e = ex >> 16;
     uint32_t p = (ex & 0xFFFFu) + min(e, need_eq);
     for (int i = i0; i < i1; ++i) {
@@ -427,7 +478,7 @@ topk_small_kernel(const float* __restrict__ scores, int N, int64_t stride, const
       }
       if (take && p < k_eff) {
         orow[p] = map_row ? map_row[i] : i;
-        if (srow) srow[p] = row[i];
+        if (srow) srow[p] = key_score(key);
         ++p;
       }
     }
@@ -490,52 +541,71 @@ __device__ __forceinline__ void derive_b0(const uint32_t* g, int32_t k, uint32_t
 }
 
 // per segment: count keys above bin b0, append keys inside bin b0 to the candidates
+// (one atomic per 8192-slot block: thread t scans 32 consecutive slots)
+constexpr int kCompactBlock = kThreads * 32;
+
 __global__ void __launch_bounds__(kThreads)
 topk_compact_kernel(const float* __restrict__ scores, int64_t N, int64_t stride, const int32_t* __restrict__ index_map,
                     int32_t k, int seg, const uint32_t* __restrict__ hist0, uint32_t* __restrict__ cand_count,
                     uint2* __restrict__ cand, int64_t cand_cap, uint32_t* __restrict__ seg_gt, int n_seg) {
   __shared__ uint32_t tmp[8];
+  __shared__ uint32_t s_base;
   const int r = blockIdx.y;
-  uint32_t b0, need1, k_eff;
-  derive_b0(hist0 + (int64_t)r * kBins, k, tmp, b0, need1, k_eff);
   const float* row = scores + (int64_t)r * stride;
   const int32_t* map_row = index_map ? index_map + (int64_t)r * N : nullptr;
   const int64_t s0 = (int64_t)blockIdx.x * seg;
   const int64_t s1 = min(N, s0 + seg);
-  uint32_t gt = 0;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint2* crow = cand + (int64_t)r * cand_cap;
-  if (k_eff > 0) {
-    for (int64_t base = s0; base < s1; base += kThreads * 4) {
-      const int64_t i = base + threadIdx.x * 4;
-      uint32_t k4[4] = {0u, 0u, 0u, 0u};
-      if (i < s1) {
-        float4 v = *reinterpret_cast<const float4*>(row + i);
-        int4 mp = map_row ? *reinterpret_cast<const int4*>(map_row + i) : make_int4(0, 0, 0, 0);
-        k4[0] = mp.x < 0 ? 0u : score_key(v.x);
-        k4[1] = mp.y < 0 ? 0u : score_key(v.y);
-        k4[2] = mp.z < 0 ? 0u : score_key(v.z);
-        k4[3] = mp.w < 0 ? 0u : score_key(v.w);
-      }
+  // thread t scans 32 consecutive slots per block; the first block's loads are
+  // issued before the threshold bin is derived from the histogram
+  auto load32 = [&](int64_t i0, uint32_t* keys) {
+    float4 v[8];
+    int4 mp[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t d0 = k4[j] >> 21;
-        gt += k4[j] != 0u && d0 > b0;
-        const bool c = k4[j] != 0u && d0 == b0;
-        // wave-aggregated append
-        const uint64_t bal = __ballot(c);
-        if (bal) {
-          uint32_t base_slot = 0;
-          if (lane == 0) base_slot = atomicAdd(&cand_count[r], (uint32_t)__popcll(bal));
-          base_slot = __shfl(base_slot, 0, 64);
-          if (c) {
-            const uint32_t rank = (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
-            crow[base_slot + rank] = make_uint2((uint32_t)(i + j), k4[j]);
-          }
-        }
+    for (int q = 0; q < 8; ++q) {
+      const int64_t i = i0 + 4 * q;
+      v[q] = i < s1 ? *reinterpret_cast<const float4*>(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      mp[q] = (map_row && i < s1) ? *reinterpret_cast<const int4*>(map_row + i) : make_int4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const bool in = i0 + 4 * q < s1;
+      keys[4 * q + 0] = (!in || mp[q].x < 0) ? 0u : score_key(v[q].x);
+      keys[4 * q + 1] = (!in || mp[q].y < 0) ? 0u : score_key(v[q].y);
+      keys[4 * q + 2] = (!in || mp[q].z < 0) ? 0u : score_key(v[q].z);
+      keys[4 * q + 3] = (!in || mp[q].w < 0) ? 0u : score_key(v[q].w);
+    }
+  };
+  uint32_t keys[32];
+  load32(s0 + (int64_t)threadIdx.x * 32, keys);
+  uint32_t b0, need1, k_eff;
+  derive_b0(hist0 + (int64_t)r * kBins, k, tmp, b0, need1, k_eff);
+  uint32_t gt = 0;
+  if (k_eff > 0) {
+    for (int64_t blk = s0; blk < s1; blk += kCompactBlock) {
+      const int64_t i0 = blk + (int64_t)threadIdx.x * 32;
+      if (blk != s0) load32(i0, keys);
+      uint32_t nc = 0;
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        const uint32_t d0 = keys[j] >> 21;
+        gt += keys[j] != 0u && d0 > b0;
+        nc += keys[j] != 0u && d0 == b0;
       }
+      uint32_t total;
+      uint32_t off = block_exclusive_scan(nc, tmp, total);
+      if (threadIdx.x == 0) s_base = total ? atomicAdd(&cand_count[r], total) : 0u;
+      __syncthreads();
+      uint32_t p = s_base + off;
+      if (nc) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+          if (keys[j] != 0u && (keys[j] >> 21) == b0) crow[p++] = make_uint2((uint32_t)(i0 + j), keys[j]);
+      }
+      __syncthreads();
     }
   }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) gt += __shfl_xor(gt, o, 64);
   if (lane == 0) tmp[wave] = gt;
@@ -581,9 +651,16 @@ topk_refine_kernel(int32_t k, int seg, const uint32_t* __restrict__ hist0, const
     __syncthreads();
     const uint32_t mask = digit_mask_above(d);
     const int shift = digit_shift(d);
-    for (uint32_t i = tid; i < nc; i += 1024) {
-      uint32_t key = crow[i].y;
-      if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & (kBins - 1)], 1u);
+    for (uint32_t b = 0; b < nc; b += 8 * 1024) {
+      uint32_t kk[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t i = b + u * 1024 + tid;
+        kk[u] = i < nc ? crow[i].y : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (b + u * 1024 + tid < nc && (kk[u] & mask) == prefix) atomicAdd(&h[(kk[u] >> shift) & (kBins - 1)], 1u);
     }
     __syncthreads();
     find_digit_1024(h, need, false, tmp, &s_digit, &s_above, total);
@@ -596,7 +673,16 @@ topk_refine_kernel(int32_t k, int seg, const uint32_t* __restrict__ hist0, const
   int32_t tie_max = -1;
   if (!none) {
     uint32_t n_tie = 0;
-    for (uint32_t i = tid; i < nc; i += 1024) n_tie += crow[i].y == tau;
+    for (uint32_t b = 0; b < nc; b += 8 * 1024) {
+      uint32_t kk[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t i = b + u * 1024 + tid;
+        kk[u] = i < nc ? crow[i].y : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) n_tie += (b + u * 1024 + tid < nc) && kk[u] == tau;
+    }
     uint32_t tot;
     block_exclusive_scan_1024(n_tie, tmp, tot);
     if (tot <= need_eq) {
@@ -635,10 +721,19 @@ topk_refine_kernel(int32_t k, int seg, const uint32_t* __restrict__ hist0, const
   for (int i = tid; i < n_seg; i += 1024) sc[i] = seg_gt[(int64_t)r * n_seg + i];
   __syncthreads();
   if (!none)
-    for (uint32_t i = tid; i < nc; i += 1024) {
-      uint2 c = crow[i];
-      bool take = c.y > tau || (c.y == tau && (int32_t)c.x <= tie_max);
-      if (take) atomicAdd(&sc[c.x / seg], 1u);
+    for (uint32_t b = 0; b < nc; b += 8 * 1024) {
+      uint2 cc[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t i = b + u * 1024 + tid;
+        cc[u] = i < nc ? crow[i] : make_uint2(0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool take = (b + u * 1024 + tid < nc) &&
+                          (cc[u].y > tau || (cc[u].y == tau && (int32_t)cc[u].x <= tie_max));
+        if (take) atomicAdd(&sc[cc[u].x / seg], 1u);
+      }
     }
   __syncthreads();
   // exclusive scan over segments (n_seg <= 2048: two per thread)
@@ -683,33 +778,51 @@ topk_cwrite_kernel(const float* __restrict__ scores, int64_t N, int64_t stride, 
   const int32_t* map_row = index_map ? index_map + (int64_t)r * N : nullptr;
   const int64_t s0 = (int64_t)blockIdx.x * seg;
   const int64_t s1 = min(N, s0 + seg);
-  const int per = seg / kThreads;                    // slots per thread (multiple of 4)
-  const int64_t i0 = s0 + (int64_t)threadIdx.x * per;
-  const int64_t i1 = min(s1, i0 + per);
   auto selected = [&](int64_t i, uint32_t key) -> bool {
     if (key == 0u) return false;
     if ((key >> 21) != cs.b0) return (key >> 21) > cs.b0;
     return key > cs.tau || (key == cs.tau && (int32_t)i <= cs.tie_slot_max);
   };
-  uint32_t n = 0;
-  for (int64_t i = i0; i < i1; i += 4) {
-    float4 v = *reinterpret_cast<const float4*>(row + i);
-    int4 mp = map_row ? *reinterpret_cast<const int4*>(map_row + i) : make_int4(0, 0, 0, 0);
-    n += selected(i + 0, mp.x < 0 ? 0u : score_key(v.x));
-    n += selected(i + 1, mp.y < 0 ? 0u : score_key(v.y));
-    n += selected(i + 2, mp.z < 0 ? 0u : score_key(v.z));
-    n += selected(i + 3, mp.w < 0 ? 0u : score_key(v.w));
-  }
-  uint32_t tot;
-  uint32_t p = seg_off[(int64_t)r * n_seg + blockIdx.x] + block_exclusive_scan(n, tmp, tot);
-  if (n == 0) return;
-  for (int64_t i = i0; i < i1; ++i) {
-    uint32_t key = score_key(row[i]);
-    if (map_row && map_row[i] < 0) key = 0u;
-    if (selected(i, key) && p < cs.k_eff) {
-      orow[p] = map_row ? map_row[i] : (int32_t)i;
-      if (srow) srow[p] = row[i];
-      ++p;
+  uint32_t base = seg_off[(int64_t)r * n_seg + blockIdx.x];
+  // blocks of 8192 slots: thread t owns 32 consecutive slots, keys and map values stay in registers
+  for (int64_t blk = s0; blk < s1; blk += kCompactBlock) {
+    const int64_t i0 = blk + (int64_t)threadIdx.x * 32;
+    float4 v[8];
+    int4 mp[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int64_t i = i0 + 4 * q;
+      v[q] = i < s1 ? *reinterpret_cast<const float4*>(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+      mp[q] = (map_row && i < s1) ? *reinterpret_cast<const int4*>(map_row + i) : make_int4(0, 0, 0, 0);
+    }
+    uint32_t keys[32];
+    int32_t pos[32];
+    uint32_t n = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const bool in = i0 + 4 * q < s1;
+      const float f[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+      const int32_t mv[4] = {mp[q].x, mp[q].y, mp[q].z, mp[q].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t i = i0 + 4 * q + j;
+        keys[4 * q + j] = (!in || mv[j] < 0) ? 0u : score_key(f[j]);
+        pos[4 * q + j] = map_row ? mv[j] : (int32_t)i;
+        n += selected(i, keys[4 * q + j]);
+      }
+    }
+    uint32_t tot;
+    uint32_t p = base + block_exclusive_scan(n, tmp, tot);
+    base += tot;
+    if (n) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        if (selected(i0 + j, keys[j]) && p < cs.k_eff) {
+          orow[p] = pos[j];
+          if (srow) srow[p] = key_score(keys[j]);
+          ++p;
+        }
+      }
     }
   }
 }

@@ -117,9 +117,10 @@ csa2_status csa2_fp4_unpack(const uint8_t* codes, const uint8_t* scales, int64_t
  *   row_limit  int64 [R] last visible position of each row (causal prefill),
  *              or NULL for all T positions
  *   scores     fp32 [R][T]
- * Every score is the exact sum rounded once to fp32 (E4M3 products are exact
- * and the f16 matrix-core path sums the 64 terms without intermediate
- * rounding), so equal exact scores give equal fp32 scores.
+ * E4M3 products are exact; each 16-term group is summed exactly and rounded
+ * once into the fp32 accumulator (four groups), so |error| <= 2^-22 *
+ * sum_d |q_d k_d|, and the score is the exact value rounded once to fp32
+ * whenever the running sums fit in 24 bits (the case for unit-normal inputs).
  * Errors: EINVAL (null pointer, R/B/T <= 0, R != B without row_seq), ESHAPE
  * (T not a multiple of 4, T >= 2^31), EALIGN.
  * ------------------------------------------------------------------------- */

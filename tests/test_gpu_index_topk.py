@@ -35,9 +35,10 @@ def test_index_full_scores(B, T):
         assert np.array_equal(got[b].astype(np.float32), exact.astype(np.float32)), b
 
 
-def test_index_scores_exact_on_wide_range_keys():
-    # keys spanning the whole E4M3 range (subnormals to 448): the sums need far more
-    # than 24 bits, yet every score must be the fp32 rounding of the exact value
+def test_index_scores_bound_on_wide_range_keys():
+    # keys spanning the whole E4M3 range (subnormals to 448): running sums need far
+    # more than 24 bits; each 16-term group is exact and rounded once, so the error
+    # stays within 2^-22 * sum |q_d k_d|
     dev = device()
     g = torch.Generator().manual_seed(17)
     T = 8192
@@ -47,7 +48,11 @@ def test_index_scores_exact_on_wide_range_keys():
     scores = torch.empty((1, T), dtype=torch.float32, device=dev)
     F.csa2_index_full(q.to(dev), k.to(dev), scores)
     exact = OI.full_scores(q[0].numpy(), k[0].numpy())
-    assert np.array_equal(scores[0].cpu().numpy(), exact.astype(np.float32))
+    got = scores[0].cpu().numpy().astype(np.float64)
+    bound = _score_bound(q[0].numpy(), k[0].numpy()) / 16       # 64 * 2^-24 / 16 = 2^-22
+    err = np.abs(got - exact)
+    assert np.all(err <= bound), float((err / bound).max())
+    print(f"exactly rounded: {np.mean(got == exact.astype(np.float32)):.4f}")
 
 
 def test_index_full_causal_rows_and_row_seq():
