@@ -309,9 +309,11 @@ def bench_pack(args, cfg):
 
 
 def copy_calibration():
+    """A plain 1 GiB device-to-device copy (read 1 GiB, write 1 GiB), run 3 times:
+    the reference for scaling the FETCH_SIZE / WRITE_SIZE hardware counters."""
     import torch
     dev = torch.device("cuda:0")
-    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    a = torch.full((1 << 28,), 1.0, dtype=torch.float32, device=dev)
     b = torch.empty_like(a)
     for _ in range(3):
         b.copy_(a)

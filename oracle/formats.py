@@ -11,7 +11,7 @@ The element formats are the OCP ones:
 
 Readings where the pages are silent (each listed in the design notes):
   * the block scale is the E4M3 value nearest to amax/6 (ties to even code),
-    saturating at 448 -- the plain reading of "following NVFP4";
+    saturating at 448 -- the plain reading of the NVFP4 layout the page names;
   * an element is the E2M1 value nearest to x/scale (ties to even code),
     clamped at 6, with the sign bit copied from x (so a small negative value
     encodes as 0x8, "negative zero");
