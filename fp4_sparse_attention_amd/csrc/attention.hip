@@ -336,48 +336,93 @@ attn_chunk_kernel(const AttnArgs a) {
 
 // Merge the chunk partials of each (row, head), optionally with a finished
 // prior result (o_prev normalised, lse_prev natural log), into o and lse.
-__global__ void __launch_bounds__(128)
+// Thread t owns channels [4t, 4t+4).  The chunk weights 2^(m_c - M) go through
+// LDS in batches of 128 chunks so that every partial-row load of a batch is
+// independent of the others (no load waits on the previous chunk's).
+constexpr int kCombineThreads = 128;
+
+__device__ __forceinline__ float block_max_128(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, shfl_xor_f(v, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = fmaxf(red[0], red[1]);
+  __syncthreads();
+  return v;
+}
+
+__device__ __forceinline__ float block_sum_128(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += shfl_xor_f(v, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = red[0] + red[1];
+  __syncthreads();
+  return v;
+}
+
+__global__ void __launch_bounds__(kCombineThreads)
 attn_combine_kernel(const float* __restrict__ o_part, const float* __restrict__ ml_part, int n_chunks, int H,
                     const float* __restrict__ o_prev, const float* __restrict__ lse_prev,
                     float* __restrict__ o_out, float* __restrict__ lse_out) {
+  __shared__ float s_w[kCombineThreads];
+  __shared__ float red[2];
   const int h = blockIdx.x, r = blockIdx.y;
-  const int c4 = threadIdx.x * 4;
+  const int tid = threadIdx.x;
+  const int c4 = tid * 4;
   const int64_t base = ((int64_t)r * n_chunks) * H + h;       // + chunk * H
-  float M = -__builtin_inff();
-  for (int c = 0; c < n_chunks; ++c) {
-    float m = ml_part[(base + (int64_t)c * H) * 2];
-    float l = ml_part[(base + (int64_t)c * H) * 2 + 1];
-    if (l > 0.f) M = fmaxf(M, m);
+  const float neg_inf = -__builtin_inff();
+  float M = neg_inf;
+  for (int c = tid; c < n_chunks; c += kCombineThreads) {
+    const float2 ml = *reinterpret_cast<const float2*>(ml_part + (base + (int64_t)c * H) * 2);
+    if (ml.y > 0.f) M = fmaxf(M, ml.x);
   }
-  float mp = -__builtin_inff();
+  M = block_max_128(M, red);
+  float mp = neg_inf;
   if (lse_prev) {
     mp = lse_prev[(int64_t)r * H + h] * kLog2e;
     M = fmaxf(M, mp);
   }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float Lsum = 0.f;
-  if (M != -__builtin_inff()) {
-    for (int c = 0; c < n_chunks; ++c) {
-      float m = ml_part[(base + (int64_t)c * H) * 2];
-      float l = ml_part[(base + (int64_t)c * H) * 2 + 1];
-      if (!(l > 0.f)) continue;
-      float w = exp2f(m - M);
-      Lsum += l * w;
-      f32x4 v = *reinterpret_cast<const f32x4*>(o_part + (base + (int64_t)c * H) * kLatent + c4);
-      acc += v * w;
-    }
-    if (lse_prev && mp != -__builtin_inff()) {
-      float w = exp2f(mp - M);
-      Lsum += w;
-      f32x4 v = *reinterpret_cast<const f32x4*>(o_prev + ((int64_t)r * H + h) * kLatent + c4);
-      acc += v * w;
+  float lpart = 0.f;
+  if (M != neg_inf) {
+    for (int c0 = 0; c0 < n_chunks; c0 += kCombineThreads) {
+      const int c = c0 + tid;
+      float w = 0.f;
+      if (c < n_chunks) {
+        const float2 ml = *reinterpret_cast<const float2*>(ml_part + (base + (int64_t)c * H) * 2);
+        if (ml.y > 0.f) {
+          w = exp2f(ml.x - M);
+          lpart += ml.y * w;
+        }
+      }
+      s_w[tid] = w;
+      __syncthreads();
+      const int n = min(kCombineThreads, n_chunks - c0);
+      const float* src = o_part + (base + (int64_t)c0 * H) * kLatent + c4;
+      const int64_t step = (int64_t)H * kLatent;
+      int j = 0;
+      for (; j + 4 <= n; j += 4) {
+        f32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const f32x4*>(src + (j + u) * step);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc += v[u] * s_w[j + u];
+      }
+      for (; j < n; ++j) acc += *reinterpret_cast<const f32x4*>(src + j * step) * s_w[j];
+      __syncthreads();
     }
   }
-  f32x4 res = Lsum > 0.f ? acc * (1.f / Lsum) : f32x4{0.f, 0.f, 0.f, 0.f};
+  float Lsum = block_sum_128(lpart, red);
+  if (lse_prev && mp != neg_inf) {
+    const float w = exp2f(mp - M);
+    Lsum += w;
+    acc += *reinterpret_cast<const f32x4*>(o_prev + ((int64_t)r * H + h) * kLatent + c4) * w;
+  }
+  const f32x4 res = Lsum > 0.f ? acc * (1.f / Lsum) : f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();                 // o_out / lse_out may alias o_prev / lse_prev
   *reinterpret_cast<f32x4*>(o_out + ((int64_t)r * H + h) * kLatent + c4) = res;
-  if (lse_out && threadIdx.x == 0)
-    lse_out[(int64_t)r * H + h] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : -__builtin_inff();
+  if (lse_out && tid == 0) lse_out[(int64_t)r * H + h] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : neg_inf;
 }
 
 // ---------------------------------------------------------------------------
@@ -448,7 +493,7 @@ static csa2_status attention_call(const uint16_t* q_lat, int32_t R, int32_t H, c
   a.ml_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + off_ml);
   hipStream_t s = (hipStream_t)stream;
   launch_chunks(a, R, s);
-  attn_combine_kernel<<<dim3(H, R), 128, 0, s>>>(a.o_part, a.ml_part, a.n_chunks, H, o_prev, lse_prev, o, lse);
+  attn_combine_kernel<<<dim3(H, R), kCombineThreads, 0, s>>>(a.o_part, a.ml_part, a.n_chunks, H, o_prev, lse_prev, o, lse);
   return launch_status();
 }
 

@@ -58,6 +58,47 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// v from the lane selected by a DPP control (0 where the source lane is
+// outside the row or the destination row is masked off)
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, kRowMask, 0xF, true);
+}
+
+// inclusive prefix sum over the 64 lanes of a wave: shifts within each row of
+// 16 lanes, then the row totals broadcast forward (row_bcast:15, row_bcast:31)
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  x += dpp_u32<0x111>(x);          // row_shr:1
+  x += dpp_u32<0x112>(x);          // row_shr:2
+  x += dpp_u32<0x114>(x);          // row_shr:4
+  x += dpp_u32<0x118>(x);          // row_shr:8
+  x += dpp_u32<0x142, 0xA>(x);     // row_bcast:15 -> rows 1, 3
+  x += dpp_u32<0x143, 0xC>(x);     // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
+// a value that is the same in every lane, moved to a scalar register so that
+// tests on it compile to scalar compares and branches
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan(x), 63);
+}
+
+// number of set bits of a wave-wide mask in the lanes below this one
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// exclusive prefix over the wave of a per-lane count in [0, 7] (three ballots)
+__device__ __forceinline__ uint32_t wave_exclusive_small(uint32_t c, uint32_t& total) {
+  const uint64_t b0 = __ballot(c & 1u), b1 = __ballot(c & 2u), b2 = __ballot(c & 4u);
+  total = (uint32_t)__popcll(b0) + 2u * (uint32_t)__popcll(b1) + 4u * (uint32_t)__popcll(b2);
+  return lanes_below(b0) + 2u * lanes_below(b1) + 4u * lanes_below(b2);
+}
+
 // ----------------------------------------------------------------------------
 // host-side checks
 // ----------------------------------------------------------------------------

@@ -15,8 +15,9 @@
 // key > tau and the lowest-slot keys == tau.  All integer work: deterministic.
 //
 // Three paths, chosen on the host from the row length N:
-//   small   (N <= 32768): one 1024-thread workgroup per row, keys in LDS,
-//           everything in one launch;
+//   small   (N <= 32768): one 1024-thread workgroup per row, keys in
+//           registers, 12-bit digits starting at the highest bit in which the
+//           row's keys differ, everything in one launch;
 //   compact (long rows): a histogram pass over the top digit; a pass that
 //           counts, per segment, the keys above the threshold bin and appends
 //           the keys inside it to a candidate list; one workgroup per row that
@@ -367,123 +368,224 @@ __device__ __forceinline__ void find_digit_1024(const uint32_t* h, uint32_t need
 }
 
 // ----------------------------------------------------------------------------
-// small path: one workgroup per row, keys resident in LDS
+// small path: one 1024-thread workgroup per row, keys held in registers
 // ----------------------------------------------------------------------------
 constexpr int kSmallMax = 32768;
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallBits = 12;
+constexpr int kSmallBins = 1 << kSmallBits;
 
-__global__ void __launch_bounds__(1024)
+// block-wide exclusive prefix sum, 1024 threads (16 waves); wt holds >= 16 words
+__device__ __forceinline__ uint32_t block_scan_1024(uint32_t v, uint32_t* wt, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t inc = wave_inclusive_scan(v);
+  if (lane == 63) wt[wave] = inc;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const uint32_t t = wt[w];
+    base += w < wave ? t : 0u;
+    tot += t;
+  }
+  total = tot;
+  __syncthreads();
+  return base + inc - v;
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+
+// Wave w owns the slots [256 J w, 256 J (w+1)) of the row, 4096 J >= N;
+// in step it, lane l holds slots 256 (J w + it) + 4l + [0, 4).  So every wave
+// reads 1 KiB runs, and the ordered write walks the row in slot order with
+// ballot prefix counts.  The radix digits are 12 bits wide and start at the
+// highest bit in which the row's visible keys differ.
+template <int J>
+__global__ void __launch_bounds__(kSmallThreads)
 topk_small_kernel(const float* __restrict__ scores, int N, int64_t stride, const int32_t* __restrict__ index_map,
                   int32_t k, int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
-  __shared__ uint32_t keys[kSmallMax];
-  __shared__ uint32_t h[kBins];
-  __shared__ uint32_t tmp[32];
+  __shared__ uint32_t h[kSmallBins];
+  __shared__ uint32_t wt[16], wt2[16];
   __shared__ uint32_t red[3][16];
   __shared__ uint32_t s_digit, s_above;
+  __shared__ __attribute__((aligned(16))) int32_t s_map[J * kSmallThreads * 4];   // index_map row (if any)
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int wbase = wave * J * 256;
   const float* row = scores + (int64_t)r * stride;
   const int32_t* map_row = index_map ? index_map + (int64_t)r * N : nullptr;
+
+  uint32_t key[J][4];
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, nvis = 0u;
   {
-    // all of this thread's loads are issued before any is used
-    constexpr int kIt = kSmallMax / 4096;
-    float4 v[kIt];
-    int4 mp[kIt];
+    float4 v[J];
+    int4 mp[J];
 #pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int i = tid * 4 + it * 4096;
-      v[it] = i < N ? *reinterpret_cast<const float4*>(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
-      mp[it] = (map_row && i < N) ? *reinterpret_cast<const int4*>(map_row + i) : make_int4(0, 0, 0, 0);
+    for (int it = 0; it < J; ++it) {
+      const int s = wbase + it * 256 + 4 * lane;
+      const bool in = s < N;
+      v[it] = in ? *reinterpret_cast<const float4*>(row + s) : make_float4(0.f, 0.f, 0.f, 0.f);
+      mp[it] = in ? (map_row ? *reinterpret_cast<const int4*>(map_row + s) : make_int4(0, 0, 0, 0))
+                  : make_int4(-1, -1, -1, -1);
     }
 #pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int i = tid * 4 + it * 4096;
-      if (i < N) {
-        uint32_t k4[4] = {mp[it].x < 0 ? 0u : score_key(v[it].x), mp[it].y < 0 ? 0u : score_key(v[it].y),
-                          mp[it].z < 0 ? 0u : score_key(v[it].z), mp[it].w < 0 ? 0u : score_key(v[it].w)};
+    for (int it = 0; it < J; ++it) {
+      const float f[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
+      const int32_t m4[4] = {mp[it].x, mp[it].y, mp[it].z, mp[it].w};
+      if (map_row) *reinterpret_cast<int4*>(s_map + wbase + it * 256 + 4 * lane) = mp[it];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          keys[i + j] = k4[j];
-          if (k4[j] != 0u) { kmin = min(kmin, k4[j]); kmax = max(kmax, k4[j]); ++nvis; }
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t kk = m4[j] < 0 ? 0u : score_key(f[j]);
+        key[it][j] = kk;
+        if (kk != 0u) {
+          kmin = min(kmin, kk);
+          kmax = max(kmax, kk);
+          ++nvis;
         }
       }
     }
   }
-  // visible count and the key range: the radix digits start at the highest bit
-  // in which the visible keys differ, so clustered scores still spread over the bins
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kmin = min(kmin, (uint32_t)__shfl_xor(kmin, o, 64));
-    kmax = max(kmax, (uint32_t)__shfl_xor(kmax, o, 64));
-    nvis += __shfl_xor(nvis, o, 64);
-  }
+  kmin = wave_min_u32(kmin);
+  kmax = wave_max_u32(kmax);
+  nvis = wave_sum_u32(nvis);
   if (lane == 0) { red[0][wave] = kmin; red[1][wave] = kmax; red[2][wave] = nvis; }
   __syncthreads();
   kmin = 0xFFFFFFFFu; kmax = 0u; nvis = 0u;
 #pragma unroll
   for (int w = 0; w < 16; ++w) { kmin = min(kmin, red[0][w]); kmax = max(kmax, red[1][w]); nvis += red[2][w]; }
+  kmin = uniform_u32(kmin);
+  kmax = uniform_u32(kmax);
+  nvis = uniform_u32(nvis);
   const uint32_t k_eff = nvis < (uint32_t)k ? nvis : (uint32_t)k;
-  uint32_t need = k_eff;
-  uint32_t prefix = 0xFFFFFFFFu;
+
+  // radix select of tau, the k_eff-th largest visible key
+  uint32_t need = k_eff, prefix = 0u;
   if (k_eff > 0) {
-    const uint32_t diff = kmin ^ kmax;
-    int hi = diff ? 31 - __builtin_clz(diff) : -1;           // highest unresolved bit
-    prefix = hi >= 31 ? 0u : (kmax & ~((2u << hi) - 1u));      // bits above hi are shared
-    if (hi < 0) prefix = kmax;
+    // bits shared by every visible key: those above the highest set bit of
+    // kmin ^ kmax.  Smearing the difference down avoids a select on
+    // kmin == kmax: this compiler's post-RA instruction shrinking can drop the
+    // exec-mask AND whose SCC such a select reads.
+    uint32_t below = kmin ^ kmax;
+    below |= below >> 1;
+    below |= below >> 2;
+    below |= below >> 4;
+    below |= below >> 8;
+    below |= below >> 16;
+    prefix = kmax & ~below;
+    int hi = __popc(below) - 1;             // highest unresolved bit (below = 2^(hi+1) - 1), -1 if none
 #pragma unroll 1
     while (hi >= 0) {
-      const int width = hi + 1 < 11 ? hi + 1 : 11;
+      const int width = hi + 1 < kSmallBits ? hi + 1 : kSmallBits;
       const int shift = hi + 1 - width;
       const uint32_t bmask = (1u << width) - 1u;
-      for (int i = tid; i < kBins; i += 1024) h[i] = 0u;
+      const uint32_t hp = hi >= 31 ? 0u : (prefix >> (hi + 1));
+      for (int i = tid; i < kSmallBins; i += kSmallThreads) h[i] = 0u;
       __syncthreads();
-      for (int i = tid; i < N; i += 1024) {
-        const uint32_t key = keys[i];
-        const bool match = hi == 31 ? true : ((key >> (hi + 1)) == (prefix >> (hi + 1)));
-        if (key != 0u && match) atomicAdd(&h[(key >> shift) & bmask], 1u);
+#pragma unroll
+      for (int it = 0; it < J; ++it) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t kk = key[it][j];
+          const bool match = kk != 0u && (hi >= 31 || (kk >> (hi + 1)) == hp);
+          if (match) atomicAdd(&h[(kk >> shift) & bmask], 1u);
+        }
       }
       __syncthreads();
+      // thread t owns bins kSmallBins-1-4t-j (j = 0..3): a descending walk
+      uint32_t c[4], local = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = h[kSmallBins - 1 - 4 * tid - j];
+        local += c[j];
+      }
       uint32_t total;
-      find_digit_1024(h, need, false, tmp, &s_digit, &s_above, total);
+      const uint32_t excl = block_scan_1024(local, wt, total);
+      if (excl < need && need <= excl + local) {
+        uint32_t acc = excl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (acc < need && need <= acc + c[j]) {
+            s_digit = (uint32_t)(kSmallBins - 1 - 4 * tid - j);
+            s_above = acc;
+          }
+          acc += c[j];
+        }
+      }
+      __syncthreads();
       prefix |= s_digit << shift;
       need -= s_above;
       hi = shift - 1;
     }
   }
-  const uint32_t tau = prefix, need_eq = k_eff > 0 ? need : 0u;
+  const uint32_t tau = prefix, need_eq = need;
+
+  // ordered write: a slot's output index is (#keys > tau before it) + min(#keys == tau before it, need_eq)
+  uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int it = 0; it < J; ++it)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t kk = key[it][j];
+      n_gt += kk != 0u && kk > tau;
+      n_eq += kk != 0u && kk == tau;
+    }
+  n_gt = wave_sum_u32(n_gt);
+  n_eq = wave_sum_u32(n_eq);
+  if (lane == 0) { wt[wave] = n_gt; wt2[wave] = n_eq; }
+  __syncthreads();
+  uint32_t G = 0, E = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    G += w < wave ? wt[w] : 0u;
+    E += w < wave ? wt2[w] : 0u;
+  }
   int32_t* orow = idx_out + (int64_t)r * k;
   float* srow = score_out ? score_out + (int64_t)r * k : nullptr;
-  // ordered write: thread t owns slots [t*E, t*E + E)
-  const int E = (N + 1023) / 1024;
-  const int i0 = tid * E, i1 = min(N, i0 + E);
-  uint32_t n_gt = 0, n_eq = 0;
-  if (k_eff > 0)
-    for (int i = i0; i < i1; ++i) {
-      uint32_t key = keys[i];
-      n_gt += key != 0u && key > tau;
-      n_eq += key != 0u && key == tau;
-    }
-  uint32_t tot;
-  uint32_t ex = block_exclusive_scan_1024((n_eq << 16) | n_gt, tmp, tot);
-  if (k_eff > 0 && (n_gt | n_eq)) {
-    uint32_t e = ex >> 16;
-    uint32_t p = (ex & 0xFFFFu) + min(e, need_eq);
-    for (int i = i0; i < i1; ++i) {
-      uint32_t key = keys[i];
-      bool take = false;
-      if (key != 0u) {
-        if (key > tau) take = true;
-        else if (key == tau) { take = e < need_eq; ++e; }
+  if (k_eff > 0) {
+#pragma unroll
+    for (int it = 0; it < J; ++it) {
+      uint32_t cg = 0, ce = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t kk = key[it][j];
+        cg += kk != 0u && kk > tau;
+        ce += kk != 0u && kk == tau;
       }
-      if (take && p < k_eff) {
-        orow[p] = map_row ? map_row[i] : i;
-        if (srow) srow[p] = key_score(key);
-        ++p;
+      uint32_t tg, te;
+      const int s = wbase + it * 256 + 4 * lane;
+      uint32_t g = G + wave_exclusive_small(cg, tg);
+      uint32_t e = E + wave_exclusive_small(ce, te);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t kk = key[it][j];
+        const bool is_gt = kk != 0u && kk > tau;
+        const bool is_eq = kk != 0u && kk == tau;
+        const bool take = is_gt || (is_eq && e < need_eq);
+        const uint32_t o = g + (is_gt ? min(e, need_eq) : e);
+        const int32_t pv = map_row ? s_map[s + j] : s + j;
+        g += is_gt ? 1u : 0u;
+        e += is_eq ? 1u : 0u;
+        if (take && o < k_eff) {
+          orow[o] = pv;
+          if (srow) srow[o] = key_score(kk);
+        }
       }
+      G += tg;
+      E += te;
     }
   }
-  for (int i = (int)k_eff + tid; i < k; i += 1024) {
+  for (int i = (int)k_eff + tid; i < k; i += kSmallThreads) {
     orow[i] = -1;
     if (srow) srow[i] = __builtin_nanf("");
   }
@@ -905,7 +1007,15 @@ extern "C" csa2_status csa2_topk(const float* scores, int32_t R, int64_t N, int6
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const Path path = choose_path(R, N);
   if (path == kSmall) {
-    topk_small_kernel<<<R, 1024, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out);
+    const int J = (int)((N + kSmallThreads * 4 - 1) / (kSmallThreads * 4));
+    if (J <= 1)
+      topk_small_kernel<1><<<R, kSmallThreads, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out);
+    else if (J <= 2)
+      topk_small_kernel<2><<<R, kSmallThreads, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out);
+    else if (J <= 4)
+      topk_small_kernel<4><<<R, kSmallThreads, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out);
+    else
+      topk_small_kernel<8><<<R, kSmallThreads, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out);
     return launch_status();
   }
   if (path == kCompact) {

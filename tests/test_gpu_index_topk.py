@@ -201,12 +201,17 @@ def test_topk_paths_boundaries_bit_exact(R, N, k):
         assert np.array_equal(gs[r][~np.isnan(rs)], rs[~np.isnan(rs)].astype(np.float32))
 
 
-@pytest.mark.parametrize("N", [4096, 65536])
-def test_topk_massive_ties(N):
-    # few distinct values: the k-th key is shared by thousands of slots, ties go to the lowest slots
+@pytest.mark.parametrize("N", [4096, 8192, 16384, 32768, 65536])
+@pytest.mark.parametrize("kind", ["k1000", "cut", "all"])
+def test_topk_massive_ties(N, kind):
+    # few distinct values: the k-th key is shared by thousands of slots and,
+    # for "cut" and "all", larger keys are selected beside the tied ones;
+    # ties go to the lowest slots.  Covers every register-layout width of the
+    # one-workgroup path (N <= 32768) and the long-row path.
     dev = device()
     rng = np.random.default_rng(N)
-    R, k = 3, 1000
+    R = 3
+    k = {"k1000": 1000, "cut": N * 3 // 8, "all": N}[kind]
     s = rng.integers(0, 4, (R, N)).astype(np.float32)
     s[1] = 7.0                                           # every slot equal
     s[2, ::3] = -np.inf
