@@ -72,8 +72,7 @@ def decode_step_bytes(B, T, H, K, P, modes, W=128):
         if mode == "full":
             total += B * T * (64 + 4) + B * 64          # keys + score write + query
             if P:
-                total += B * T * 4 + B * P * 8          # pool selection: read scores, write pool + scores
-                total += B * P * 8 + B * K * 4          # top-K of the pool
+                total += B * T * 4 + B * P * 8 + B * K * 4   # one selection: read scores, write pool + scores, top-K
             else:
                 total += B * T * 4 + B * K * 4
         elif mode == "reindex":

@@ -33,6 +33,9 @@ _SIGS = {
     "csa2_topk_workspace_size": (_size_t, [_i32, _i64, _i32]),
     "csa2_topk": (_i32, [_c_void_p, _i32, _i64, _i64, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t,
                          _c_void_p]),
+    "csa2_topk_pool_workspace_size": (_size_t, [_i32, _i64, _i32]),
+    "csa2_topk_pool": (_i32, [_c_void_p, _i32, _i64, _i64, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                              _c_void_p, _size_t, _c_void_p]),
     "csa2_sparse_decode_workspace_size": (_size_t, [_i32, _i32, _i32]),
     "csa2_sparse_decode": (_i32, [_c_void_p, _i32, _i32, _c_void_p, _c_void_p, _i32, _i64, _c_void_p, _c_void_p,
                                   _i32, _f32, _c_void_p, _c_void_p, _c_void_p, _size_t, _c_void_p]),
@@ -201,6 +204,41 @@ def csa2_topk(scores, k, idx_out, score_out=None, index_map=None, workspace=None
     st = lib().csa2_topk(_p(scores), R, N, scores.stride(0), k, _p(index_map), _p(idx_out), _p(score_out),
                          _p(workspace), workspace.numel(), _stream(stream))
     _check("csa2_topk", st)
+
+
+def csa2_topk_pool_workspace_size(R, N, k_pool):
+    return int(lib().csa2_topk_pool_workspace_size(R, N, k_pool))
+
+
+def csa2_topk_pool(scores, k_pool, k_top, pool_idx, top_idx, pool_scores=None, index_map=None, workspace=None,
+                   stream=None):
+    """The k_pool and the k_top <= k_pool highest scores of each row in one selection.
+    scores fp32 [R, N]; pool_idx int32 [R, k_pool]; top_idx int32 [R, k_top];
+    pool_scores fp32 [R, k_pool] or None; index_map int32 [R, N] or None."""
+    _need(scores, torch.float32, "scores", 2)
+    _need(pool_idx, torch.int32, "pool_idx", 2)
+    _need(top_idx, torch.int32, "top_idx", 2)
+    if scores.stride(1) != 1:
+        raise ValueError("scores: columns must be contiguous")
+    R, N = scores.shape
+    if pool_idx.shape != (R, k_pool) or top_idx.shape != (R, k_top):
+        raise ValueError("pool_idx / top_idx shape")
+    _dense(pool_idx, "pool_idx")
+    _dense(top_idx, "top_idx")
+    if pool_scores is not None:
+        _need(pool_scores, torch.float32, "pool_scores", 2)
+        if pool_scores.shape != (R, k_pool):
+            raise ValueError("pool_scores shape")
+        _dense(pool_scores, "pool_scores")
+    if index_map is not None:
+        _need(index_map, torch.int32, "index_map", 2)
+        _dense(index_map, "index_map")
+    need = csa2_topk_pool_workspace_size(R, N, k_pool)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    st = lib().csa2_topk_pool(_p(scores), R, N, scores.stride(0), k_pool, k_top, _p(index_map), _p(pool_idx),
+                              _p(pool_scores), _p(top_idx), _p(workspace), workspace.numel(), _stream(stream))
+    _check("csa2_topk_pool", st)
 
 
 def csa2_sparse_decode_workspace_size(R, H, K):

@@ -592,347 +592,500 @@ topk_small_kernel(const float* __restrict__ scores, int N, int64_t stride, const
 }
 
 // ----------------------------------------------------------------------------
-// compact path
+// compact path (long rows)
 // ----------------------------------------------------------------------------
-struct CompactState {
-  uint32_t b0;          // top digit of tau
-  uint32_t k_eff;
-  uint32_t tau;
-  uint32_t need_eq;
-  int32_t tie_slot_max; // equal keys at slots <= this are selected
-  uint32_t pad[3];
-};
+constexpr int kTopBits = 12;                    // top digit: key bits 31..20
+constexpr int kTopBins = 1 << kTopBits;
+constexpr int kTopShift = 32 - kTopBits;
+
+// histogram of the top 12 key bits of every visible slot (one 8192-slot segment per workgroup)
+__global__ void __launch_bounds__(kThreads)
+topk_top_hist_kernel(const float* __restrict__ scores, int64_t N, int64_t stride, const int32_t* __restrict__ index_map,
+                     uint32_t* __restrict__ hist) {
+  __shared__ uint32_t h[kTopBins];
+  const int r = blockIdx.y;
+  for (int i = threadIdx.x; i < kTopBins; i += kThreads) h[i] = 0u;
+  __syncthreads();
+  const float* row = scores + (int64_t)r * stride;
+  const int32_t* map_row = index_map ? index_map + (int64_t)r * N : nullptr;
+  const int64_t b0 = (int64_t)blockIdx.x * kSeg;
+  const int64_t b1 = min(N, b0 + kSeg);
+  float4 v[8];
+  int4 mp[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int64_t i = b0 + (int64_t)q * kThreads * 4 + threadIdx.x * 4;
+    v[q] = i < b1 ? *reinterpret_cast<const float4*>(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+    mp[q] = (map_row && i < b1) ? *reinterpret_cast<const int4*>(map_row + i) : make_int4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int64_t i = b0 + (int64_t)q * kThreads * 4 + threadIdx.x * 4;
+    if (i >= b1) continue;
+    const float f[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+    const int m4[4] = {mp[q].x, mp[q].y, mp[q].z, mp[q].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t k = m4[j] < 0 ? 0u : score_key(f[j]);
+      if (k != 0u) atomicAdd(&h[k >> kTopShift], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* g = hist + (int64_t)r * kTopBins;
+  for (int i = threadIdx.x; i < kTopBins; i += kThreads)
+    if (h[i]) atomicAdd(&g[i], h[i]);
+}
+// The top digit b0 of the k-th largest key comes from the 12-bit histogram.
+// Every visible key whose top digit is >= b0 is a candidate: keys above bin b0
+// are all selected, keys inside it are resolved by the two lower digits.  Each
+// segment writes its candidates (key, output position) in slot order into its
+// own slot range, the segments are concatenated into one slot-ordered list per
+// row, and one workgroup per row finishes the selection on that list -- about
+// k plus one bin's worth of entries instead of N.  A second, smaller k2 can be
+// selected from the same candidates (the top k2 lie inside the top k).
 
 __global__ void __launch_bounds__(kThreads)
-topk_cinit_kernel(uint32_t* __restrict__ hist0, uint32_t* __restrict__ cand_count) {
-  const int r = blockIdx.x;
-  for (int i = threadIdx.x; i < kBins; i += kThreads) hist0[(int64_t)r * kBins + i] = 0u;
-  if (threadIdx.x == 0) cand_count[r] = 0u;
+topk_zero_kernel(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (int64_t)gridDim.x * kThreads) p[i] = 0u;
 }
 
-// derive (b0, need within bin b0, k_eff) from the row's top-digit histogram, 256 threads
-__device__ __forceinline__ void derive_b0(const uint32_t* g, int32_t k, uint32_t* tmp, uint32_t& b0, uint32_t& need1,
-                                          uint32_t& k_eff) {
-  __shared__ uint32_t s_digit, s_above;
-  uint32_t c[8];
+// top digit b0 of the k-th largest visible key, and k_eff = min(k, visible), from a
+// row's 12-bit top-digit histogram (256 threads; bin 0 holds only invisible keys)
+__device__ __forceinline__ void derive_b0(const uint32_t* g, int32_t k, uint32_t* tmp, uint32_t& b0, uint32_t& k_eff) {
+  __shared__ uint32_t s_digit;
+  constexpr int kPer = kTopBins / kThreads;
+  uint32_t c[kPer];
   uint32_t local = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    int bin = kBins - 1 - (threadIdx.x * 8 + j);
+  for (int j = 0; j < kPer; ++j) {
+    const int bin = kTopBins - 1 - (threadIdx.x * kPer + j);
     c[j] = bin == 0 ? 0u : g[bin];
     local += c[j];
   }
   uint32_t total;
-  uint32_t excl = block_exclusive_scan(local, tmp, total);
-  uint32_t need = total < (uint32_t)k ? total : (uint32_t)k;
-  if (threadIdx.x == 0) { s_digit = 0xFFFFFFFFu; s_above = 0u; }
+  const uint32_t excl = block_exclusive_scan(local, tmp, total);
+  const uint32_t need = total < (uint32_t)k ? total : (uint32_t)k;
+  if (threadIdx.x == 0) s_digit = 0xFFFFFFFFu;
   __syncthreads();
   if (need > 0 && excl < need && need <= excl + local) {
     uint32_t acc = excl;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (acc < need && need <= acc + c[j]) { s_digit = (uint32_t)(kBins - 1 - (threadIdx.x * 8 + j)); s_above = acc; }
+    for (int j = 0; j < kPer; ++j) {
+      if (acc < need && need <= acc + c[j]) s_digit = (uint32_t)(kTopBins - 1 - (threadIdx.x * kPer + j));
       acc += c[j];
     }
   }
   __syncthreads();
   k_eff = need;
   b0 = s_digit;
-  need1 = need - s_above;
   __syncthreads();
 }
 
-// per segment: count keys above bin b0, append keys inside bin b0 to the candidates
-// (one atomic per 8192-slot block: thread t scans 32 consecutive slots)
-constexpr int kCompactBlock = kThreads * 32;
+constexpr int kCompactBlock = kThreads * 32;     // slots per block step: thread t takes 32 consecutive slots
 
+// per segment: the candidates (top digit >= b0) in slot order, written to the
+// segment's own slot range of seg_key / seg_pos; their count to seg_cnt
 __global__ void __launch_bounds__(kThreads)
 topk_compact_kernel(const float* __restrict__ scores, int64_t N, int64_t stride, const int32_t* __restrict__ index_map,
-                    int32_t k, int seg, const uint32_t* __restrict__ hist0, uint32_t* __restrict__ cand_count,
-                    uint2* __restrict__ cand, int64_t cand_cap, uint32_t* __restrict__ seg_gt, int n_seg) {
+                    int32_t k, int seg, const uint32_t* __restrict__ hist0, uint32_t* __restrict__ seg_key,
+                    int32_t* __restrict__ seg_pos, uint32_t* __restrict__ seg_cnt, int n_seg) {
   __shared__ uint32_t tmp[8];
-  __shared__ uint32_t s_base;
   const int r = blockIdx.y;
   const float* row = scores + (int64_t)r * stride;
   const int32_t* map_row = index_map ? index_map + (int64_t)r * N : nullptr;
   const int64_t s0 = (int64_t)blockIdx.x * seg;
   const int64_t s1 = min(N, s0 + seg);
-  uint2* crow = cand + (int64_t)r * cand_cap;
-  // thread t scans 32 consecutive slots per block; the first block's loads are
-  // issued before the threshold bin is derived from the histogram
-  auto load32 = [&](int64_t i0, uint32_t* keys) {
+  uint32_t* okey = seg_key + (int64_t)r * N + s0;
+  int32_t* opos = seg_pos + (int64_t)r * N + s0;
+  auto load32 = [&](int64_t i0, uint32_t* keys, int32_t* pos) {
     float4 v[8];
     int4 mp[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int64_t i = i0 + 4 * q;
       v[q] = i < s1 ? *reinterpret_cast<const float4*>(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
-      mp[q] = (map_row && i < s1) ? *reinterpret_cast<const int4*>(map_row + i) : make_int4(0, 0, 0, 0);
+      mp[q] = (map_row && i < s1) ? *reinterpret_cast<const int4*>(map_row + i)
+                                  : make_int4((int)i, (int)i + 1, (int)i + 2, (int)i + 3);
     }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const bool in = i0 + 4 * q < s1;
-      keys[4 * q + 0] = (!in || mp[q].x < 0) ? 0u : score_key(v[q].x);
-      keys[4 * q + 1] = (!in || mp[q].y < 0) ? 0u : score_key(v[q].y);
-      keys[4 * q + 2] = (!in || mp[q].z < 0) ? 0u : score_key(v[q].z);
-      keys[4 * q + 3] = (!in || mp[q].w < 0) ? 0u : score_key(v[q].w);
-    }
-  };
-  uint32_t keys[32];
-  load32(s0 + (int64_t)threadIdx.x * 32, keys);
-  uint32_t b0, need1, k_eff;
-  derive_b0(hist0 + (int64_t)r * kBins, k, tmp, b0, need1, k_eff);
-  uint32_t gt = 0;
-  if (k_eff > 0) {
-    for (int64_t blk = s0; blk < s1; blk += kCompactBlock) {
-      const int64_t i0 = blk + (int64_t)threadIdx.x * 32;
-      if (blk != s0) load32(i0, keys);
-      uint32_t nc = 0;
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        const uint32_t d0 = keys[j] >> 21;
-        gt += keys[j] != 0u && d0 > b0;
-        nc += keys[j] != 0u && d0 == b0;
-      }
-      uint32_t total;
-      uint32_t off = block_exclusive_scan(nc, tmp, total);
-      if (threadIdx.x == 0) s_base = total ? atomicAdd(&cand_count[r], total) : 0u;
-      __syncthreads();
-      uint32_t p = s_base + off;
-      if (nc) {
-#pragma unroll
-        for (int j = 0; j < 32; ++j)
-          if (keys[j] != 0u && (keys[j] >> 21) == b0) crow[p++] = make_uint2((uint32_t)(i0 + j), keys[j]);
-      }
-      __syncthreads();
-    }
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) gt += __shfl_xor(gt, o, 64);
-  if (lane == 0) tmp[wave] = gt;
-  __syncthreads();
-  if (threadIdx.x == 0) seg_gt[(int64_t)r * n_seg + blockIdx.x] = tmp[0] + tmp[1] + tmp[2] + tmp[3];
-}
-
-// one workgroup per row: finish the selection on the candidates
-constexpr int kMaxSeg = 2048;
-
-__global__ void __launch_bounds__(1024)
-topk_refine_kernel(int32_t k, int seg, const uint32_t* __restrict__ hist0, const uint32_t* __restrict__ cand_count,
-                   const uint2* __restrict__ cand, int64_t cand_cap, const uint32_t* __restrict__ seg_gt,
-                   uint32_t* __restrict__ seg_off, int n_seg, CompactState* __restrict__ st) {
-  __shared__ uint32_t h[kBins];
-  __shared__ uint32_t tmp[32];
-  __shared__ uint32_t s_digit, s_above;
-  __shared__ uint32_t sc[kMaxSeg];
-  __shared__ uint32_t s_b0, s_need1, s_keff;
-  const int r = blockIdx.x;
-  const int tid = threadIdx.x;
-  // b0 / need1 / k_eff from the top-digit histogram (1024-thread version)
-  for (int i = tid; i < kBins; i += 1024) h[i] = hist0[(int64_t)r * kBins + i];
-  __syncthreads();
-  uint32_t total;
-  find_digit_1024(h, 0xFFFFFFFFu, true, tmp, &s_digit, &s_above, total);
-  {
-    uint32_t k_eff = total < (uint32_t)k ? total : (uint32_t)k;
-    find_digit_1024(h, k_eff, true, tmp, &s_digit, &s_above, total);
-    if (tid == 0) { s_keff = k_eff; s_b0 = s_digit; s_need1 = k_eff - s_above; }
-    __syncthreads();
-  }
-  const uint32_t k_eff = s_keff, b0 = s_b0;
-  uint32_t need = s_need1;
-  const uint32_t nc = cand_count[r];
-  const uint2* crow = cand + (int64_t)r * cand_cap;
-  uint32_t prefix = b0 << 21;
-  bool none = (k_eff == 0) || (b0 == 0xFFFFFFFFu);
-  if (none) prefix = 0xFFFFFFFFu;
-#pragma unroll 1
-  for (int d = 1; d < 3 && !none; ++d) {
-    for (int i = tid; i < kBins; i += 1024) h[i] = 0u;
-    __syncthreads();
-    const uint32_t mask = digit_mask_above(d);
-    const int shift = digit_shift(d);
-    for (uint32_t b = 0; b < nc; b += 8 * 1024) {
-      uint32_t kk[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint32_t i = b + u * 1024 + tid;
-        kk[u] = i < nc ? crow[i].y : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (b + u * 1024 + tid < nc && (kk[u] & mask) == prefix) atomicAdd(&h[(kk[u] >> shift) & (kBins - 1)], 1u);
-    }
-    __syncthreads();
-    find_digit_1024(h, need, false, tmp, &s_digit, &s_above, total);
-    if (s_digit == 0xFFFFFFFFu) { none = true; prefix = 0xFFFFFFFFu; need = 0; break; }
-    prefix |= s_digit << shift;
-    need -= s_above;
-  }
-  const uint32_t tau = prefix, need_eq = none ? 0u : need;
-  // ties: the need_eq lowest slots among candidates with key == tau -> largest selected slot
-  int32_t tie_max = -1;
-  if (!none) {
-    uint32_t n_tie = 0;
-    for (uint32_t b = 0; b < nc; b += 8 * 1024) {
-      uint32_t kk[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint32_t i = b + u * 1024 + tid;
-        kk[u] = i < nc ? crow[i].y : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) n_tie += (b + u * 1024 + tid < nc) && kk[u] == tau;
-    }
-    uint32_t tot;
-    block_exclusive_scan_1024(n_tie, tmp, tot);
-    if (tot <= need_eq) {
-      tie_max = 0x7FFFFFFF;
-    } else {
-      // radix select of the need_eq-th smallest slot among the ties (slots < 2^31; digits of 11/10/10 bits)
-      uint32_t sprefix = 0, sneed = need_eq;
-      const int shifts[3] = {20, 10, 0};
-      const uint32_t masks[3] = {0u, 0xFFF00000u, 0xFFFFFC00u};
-#pragma unroll 1
-      for (int d = 0; d < 3; ++d) {
-        for (int i = tid; i < kBins; i += 1024) h[i] = 0u;
-        __syncthreads();
-        for (uint32_t i = tid; i < nc; i += 1024) {
-          uint2 c = crow[i];
-          if (c.y == tau && (c.x & masks[d]) == sprefix) atomicAdd(&h[(c.x >> shifts[d]) & (kBins - 1)], 1u);
-        }
-        __syncthreads();
-        // ascending search: thread t owns bins 2t, 2t+1
-        const uint32_t c0 = h[2 * tid], c1 = h[2 * tid + 1];
-        uint32_t t2;
-        uint32_t ex = block_exclusive_scan_1024(c0 + c1, tmp, t2);
-        if (tid == 0) { s_digit = 0xFFFFFFFFu; s_above = 0u; }
-        __syncthreads();
-        if (ex < sneed && sneed <= ex + c0) { s_digit = 2 * tid; s_above = ex; }
-        else if (ex + c0 < sneed && sneed <= ex + c0 + c1) { s_digit = 2 * tid + 1; s_above = ex + c0; }
-        __syncthreads();
-        sprefix |= s_digit << shifts[d];
-        sneed -= s_above;
-        __syncthreads();
-      }
-      tie_max = (int32_t)sprefix;
-    }
-  }
-  // per-segment selected counts -> output offsets
-  for (int i = tid; i < n_seg; i += 1024) sc[i] = seg_gt[(int64_t)r * n_seg + i];
-  __syncthreads();
-  if (!none)
-    for (uint32_t b = 0; b < nc; b += 8 * 1024) {
-      uint2 cc[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const uint32_t i = b + u * 1024 + tid;
-        cc[u] = i < nc ? crow[i] : make_uint2(0u, 0u);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const bool take = (b + u * 1024 + tid < nc) &&
-                          (cc[u].y > tau || (cc[u].y == tau && (int32_t)cc[u].x <= tie_max));
-        if (take) atomicAdd(&sc[cc[u].x / seg], 1u);
-      }
-    }
-  __syncthreads();
-  // exclusive scan over segments (n_seg <= 2048: two per thread)
-  {
-    const uint32_t a0 = 2 * tid < n_seg ? sc[2 * tid] : 0u;
-    const uint32_t a1 = 2 * tid + 1 < n_seg ? sc[2 * tid + 1] : 0u;
-    uint32_t tot;
-    uint32_t ex = block_exclusive_scan_1024(a0 + a1, tmp, tot);
-    if (2 * tid < n_seg) seg_off[(int64_t)r * n_seg + 2 * tid] = ex;
-    if (2 * tid + 1 < n_seg) seg_off[(int64_t)r * n_seg + 2 * tid + 1] = ex + a0;
-  }
-  if (tid == 0) {
-    CompactState cs;
-    cs.b0 = none ? 0xFFFFFFFFu : b0;
-    cs.k_eff = k_eff;
-    cs.tau = tau;
-    cs.need_eq = need_eq;
-    cs.tie_slot_max = tie_max;
-    cs.pad[0] = cs.pad[1] = cs.pad[2] = 0;
-    st[r] = cs;
-  }
-}
-
-// ordered write: thread t owns the 4*E consecutive slots of its part of the segment
-__global__ void __launch_bounds__(kThreads)
-topk_cwrite_kernel(const float* __restrict__ scores, int64_t N, int64_t stride, const int32_t* __restrict__ index_map,
-                   int seg, const CompactState* __restrict__ st, const uint32_t* __restrict__ seg_off, int n_seg,
-                   int32_t k, int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
-  __shared__ uint32_t tmp[8];
-  const int r = blockIdx.y;
-  const CompactState cs = st[r];
-  int32_t* orow = idx_out + (int64_t)r * k;
-  float* srow = score_out ? score_out + (int64_t)r * k : nullptr;
-  if (blockIdx.x == n_seg - 1) {
-    for (int i = (int)cs.k_eff + threadIdx.x; i < k; i += kThreads) {
-      orow[i] = -1;
-      if (srow) srow[i] = __builtin_nanf("");
-    }
-  }
-  if (cs.k_eff == 0) return;
-  const float* row = scores + (int64_t)r * stride;
-  const int32_t* map_row = index_map ? index_map + (int64_t)r * N : nullptr;
-  const int64_t s0 = (int64_t)blockIdx.x * seg;
-  const int64_t s1 = min(N, s0 + seg);
-  auto selected = [&](int64_t i, uint32_t key) -> bool {
-    if (key == 0u) return false;
-    if ((key >> 21) != cs.b0) return (key >> 21) > cs.b0;
-    return key > cs.tau || (key == cs.tau && (int32_t)i <= cs.tie_slot_max);
-  };
-  uint32_t base = seg_off[(int64_t)r * n_seg + blockIdx.x];
-  // blocks of 8192 slots: thread t owns 32 consecutive slots, keys and map values stay in registers
-  for (int64_t blk = s0; blk < s1; blk += kCompactBlock) {
-    const int64_t i0 = blk + (int64_t)threadIdx.x * 32;
-    float4 v[8];
-    int4 mp[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int64_t i = i0 + 4 * q;
-      v[q] = i < s1 ? *reinterpret_cast<const float4*>(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
-      mp[q] = (map_row && i < s1) ? *reinterpret_cast<const int4*>(map_row + i) : make_int4(0, 0, 0, 0);
-    }
-    uint32_t keys[32];
-    int32_t pos[32];
-    uint32_t n = 0;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const bool in = i0 + 4 * q < s1;
       const float f[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
-      const int32_t mv[4] = {mp[q].x, mp[q].y, mp[q].z, mp[q].w};
+      const int32_t m4[4] = {mp[q].x, mp[q].y, mp[q].z, mp[q].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int64_t i = i0 + 4 * q + j;
-        keys[4 * q + j] = (!in || mv[j] < 0) ? 0u : score_key(f[j]);
-        pos[4 * q + j] = map_row ? mv[j] : (int32_t)i;
-        n += selected(i, keys[4 * q + j]);
+        keys[4 * q + j] = (!in || m4[j] < 0) ? 0u : score_key(f[j]);
+        pos[4 * q + j] = m4[j];
       }
     }
-    uint32_t tot;
-    uint32_t p = base + block_exclusive_scan(n, tmp, tot);
-    base += tot;
-    if (n) {
+  };
+  uint32_t keys[32];
+  int32_t pos[32];
+  load32(s0 + (int64_t)threadIdx.x * 32, keys, pos);      // in flight while b0 is derived
+  uint32_t b0, k_eff;
+  derive_b0(hist0 + (int64_t)r * kTopBins, k, tmp, b0, k_eff);
+  uint32_t running = 0;
+  if (k_eff > 0) {
+    for (int64_t blk = s0; blk < s1; blk += kCompactBlock) {
+      const int64_t i0 = blk + (int64_t)threadIdx.x * 32;
+      if (blk != s0) load32(i0, keys, pos);
+      uint32_t n = 0;
 #pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        if (selected(i0 + j, keys[j]) && p < cs.k_eff) {
-          orow[p] = pos[j];
-          if (srow) srow[p] = key_score(keys[j]);
-          ++p;
+      for (int j = 0; j < 32; ++j) n += keys[j] != 0u && (keys[j] >> kTopShift) >= b0;
+      uint32_t total;
+      uint32_t p = running + block_exclusive_scan(n, tmp, total);
+      if (n) {
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+          if (keys[j] != 0u && (keys[j] >> kTopShift) >= b0) {
+            okey[p] = keys[j];
+            opos[p] = pos[j];
+            ++p;
+          }
+        }
+      }
+      running += total;
+    }
+  }
+  if (threadIdx.x == 0) seg_cnt[(int64_t)r * n_seg + blockIdx.x] = running;
+}
+
+// concatenate the segments' candidate runs into one slot-ordered list per row
+__global__ void __launch_bounds__(kThreads)
+topk_flatten_kernel(int64_t N, int seg, const uint32_t* __restrict__ seg_key, const int32_t* __restrict__ seg_pos,
+                    const uint32_t* __restrict__ seg_cnt, int n_seg, uint32_t* __restrict__ cand_key,
+                    int32_t* __restrict__ cand_pos, uint32_t* __restrict__ cand_total) {
+  __shared__ uint32_t red[4];
+  const int r = blockIdx.y;
+  const int si = blockIdx.x;
+  const uint32_t* cnt = seg_cnt + (int64_t)r * n_seg;
+  uint32_t part = 0;
+  for (int i = threadIdx.x; i < si; i += kThreads) part += cnt[i];
+  part = wave_sum_u32(part);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = part;
+  __syncthreads();
+  const uint32_t base = red[0] + red[1] + red[2] + red[3];
+  const uint32_t n = cnt[si];
+  const int64_t src = (int64_t)r * N + (int64_t)si * seg;
+  const int64_t dst = (int64_t)r * N + base;
+  for (uint32_t i = threadIdx.x; i < n; i += kThreads) {
+    cand_key[dst + i] = seg_key[src + i];
+    cand_pos[dst + i] = seg_pos[src + i];
+  }
+  if (si == n_seg - 1 && threadIdx.x == 0) cand_total[r] = base + n;
+}
+
+// digit search over a histogram in LDS by 1024 threads: bins are walked from the
+// top, thread t owns bins nb-1-(nb/1024)t-j; returns the bin holding the need-th
+// largest entry and the count above it (need >= 1 and <= the histogram total)
+template <int kNB>
+__device__ __forceinline__ void find_bin_1024(const uint32_t* hh, uint32_t need, uint32_t* wt, uint32_t* out2) {
+  constexpr int kPer = kNB / 1024;
+  uint32_t c[kPer], local = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    c[j] = hh[kNB - 1 - kPer * threadIdx.x - j];
+    local += c[j];
+  }
+  uint32_t total;
+  const uint32_t excl = block_scan_1024(local, wt, total);
+  if (excl < need && need <= excl + local) {
+    uint32_t acc = excl;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (acc < need && need <= acc + c[j]) {
+        out2[0] = (uint32_t)(kNB - 1 - kPer * threadIdx.x - j);
+        out2[1] = acc;
+      }
+      acc += c[j];
+    }
+  }
+}
+
+// Finishing the selection(s) on a row's slot-ordered candidate list takes two
+// kernels: one workgroup per row stages the keys in LDS (when they fit), finds
+// tau and the number of ties to take for each selection, and counts, per chunk
+// of 1024 list entries, the keys above and equal to tau; then many workgroups
+// write the outputs chunk by chunk, each starting from the counts of the chunks
+// before it.  Selection 0 takes k (idx_out [+ score_out]); selection 1, if
+// present, k2 <= k (idx2_out).
+constexpr int kFinishThreads = 1024;
+constexpr int kFinishLds = 32768;
+constexpr int kLowBins = 1024;                  // digits 1 and 2: key bits 19..10 and 9..0
+constexpr int kChunk = 1024;                    // list entries per write chunk
+constexpr int kWriteBlocks = 64;                // write workgroups per row (grid-stride over chunks)
+
+struct SelState {
+  uint32_t tau[2];
+  uint32_t need_eq[2];
+  uint32_t k_eff[2];
+  uint32_t pad[2];
+};
+
+template <int NS, bool kLds>
+__device__ __forceinline__ void select_passes(const uint32_t* keys, uint32_t C, uint32_t (*h)[kLowBins], uint32_t* wt,
+                                              uint32_t (*s_res)[2], uint32_t* tau, uint32_t* need) {
+  const int tid = threadIdx.x;
+#pragma unroll 1
+  for (int d = 1; d <= 2; ++d) {
+    const int shift = d == 1 ? 10 : 0;
+    const int hi_shift = d == 1 ? kTopShift : 10;
+    for (int i = tid; i < kLowBins; i += kFinishThreads) {
+#pragma unroll
+      for (int s = 0; s < NS; ++s) h[s][i] = 0u;
+    }
+    __syncthreads();
+    uint32_t pfx[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) pfx[s] = tau[s] >> hi_shift;
+    // 16-byte reads: entries [4 (u 1024 + t), +4) of each 16384-entry block
+    for (uint32_t b = 0; b < C; b += 4u * 4u * kFinishThreads) {
+      uint4 kv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t v = b + 4u * (u * kFinishThreads + tid);
+        kv[u] = v < C ? *reinterpret_cast<const uint4*>(keys + v) : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t v = b + 4u * (u * kFinishThreads + tid);
+        const uint32_t k4[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int s = 0; s < NS; ++s)
+            if (v + j < C && (k4[j] >> hi_shift) == pfx[s]) atomicAdd(&h[s][(k4[j] >> shift) & (kLowBins - 1)], 1u);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      find_bin_1024<kLowBins>(h[s], need[s], wt, s_res[s]);
+      __syncthreads();
+      tau[s] |= s_res[s][0] << shift;
+      need[s] -= s_res[s][1];
+      __syncthreads();
+    }
+  }
+}
+
+template <int NS, bool kLds>
+__device__ __forceinline__ void chunk_counts(const uint32_t* keys, uint32_t C, const uint32_t* tau,
+                                             uint32_t* chunk_cnt /* [n_chunks][2 NS] of this row */) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t n_chunks = (C + kChunk - 1) / kChunk;
+  for (uint32_t c = wave; c < n_chunks; c += 16) {
+    uint32_t cg[NS], ce[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) { cg[s] = 0u; ce[s] = 0u; }
+    uint4 kv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t v = c * kChunk + u * 256 + 4 * lane;
+      kv[u] = v < C ? *reinterpret_cast<const uint4*>(keys + v) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint32_t v = c * kChunk + u * 256 + 4 * lane;
+      const uint32_t k4[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          cg[s] += v + j < C && k4[j] > tau[s];
+          ce[s] += v + j < C && k4[j] == tau[s];
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const uint32_t a = wave_sum_u32(cg[s]), b = wave_sum_u32(ce[s]);
+      if (lane == 0) { chunk_cnt[c * 2 * NS + 2 * s] = a; chunk_cnt[c * 2 * NS + 2 * s + 1] = b; }
+    }
+  }
+}
+
+template <int NS>
+__global__ void __launch_bounds__(kFinishThreads)
+topk_select_cand_kernel(int64_t N, const uint32_t* __restrict__ hist0, const uint32_t* __restrict__ cand_key,
+                        const uint32_t* __restrict__ cand_total, int32_t k, int32_t k2,
+                        SelState* __restrict__ st, uint32_t* __restrict__ chunk_cnt) {
+  __shared__ __attribute__((aligned(16))) uint32_t s_keys[kFinishLds];
+  __shared__ uint32_t h[NS][kLowBins];
+  __shared__ uint32_t wt[16];
+  __shared__ uint32_t s_res[NS][2];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint32_t* ck = cand_key + (int64_t)r * N;
+  const uint32_t C = uniform_u32(cand_total[r]);
+  const bool in_lds = C <= (uint32_t)kFinishLds;
+  const int32_t kk_[2] = {k, NS == 2 ? k2 : 0};
+
+  // top-digit histogram loads issued before the key staging
+  constexpr int kPer = kTopBins / kFinishThreads;
+  uint32_t c[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int bin = kTopBins - 1 - kPer * tid - j;
+    c[j] = bin == 0 ? 0u : hist0[(int64_t)r * kTopBins + bin];
+  }
+  if (in_lds) {
+    for (uint32_t b = 0; b < C; b += 4u * 4u * kFinishThreads) {
+      uint4 kv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t v = b + 4u * (u * kFinishThreads + tid);
+        kv[u] = v < C ? *reinterpret_cast<const uint4*>(ck + v) : make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t v = b + 4u * (u * kFinishThreads + tid);
+        if (v < C) *reinterpret_cast<uint4*>(s_keys + v) = kv[u];
+      }
+    }
+  }
+  // visible count and the top digit of each selection's k-th key
+  uint32_t k_eff[NS], need[NS], tau[NS];
+  {
+    uint32_t local = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) local += c[j];
+    uint32_t V;
+    const uint32_t excl = block_scan_1024(local, wt, V);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      k_eff[s] = V < (uint32_t)kk_[s] ? V : (uint32_t)kk_[s];
+      const uint32_t nd = k_eff[s];
+      if (nd > 0 && excl < nd && nd <= excl + local) {
+        uint32_t acc = excl;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          if (acc < nd && nd <= acc + c[j]) { s_res[s][0] = kTopBins - 1 - kPer * tid - j; s_res[s][1] = acc; }
+          acc += c[j];
         }
       }
     }
+  }
+  __syncthreads();
+  const bool live = k_eff[0] > 0;               // k_eff[1] > 0 exactly when k_eff[0] > 0
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    tau[s] = live ? s_res[s][0] << kTopShift : 0u;
+    need[s] = live ? k_eff[s] - s_res[s][1] : 0u;
+  }
+  uint32_t* cc = chunk_cnt + (int64_t)r * ((N + kChunk - 1) / kChunk) * 2 * NS;
+  if (live) {
+    if (in_lds) {
+      select_passes<NS, true>(s_keys, C, h, wt, s_res, tau, need);
+      chunk_counts<NS, true>(s_keys, C, tau, cc);
+    } else {
+      select_passes<NS, false>(ck, C, h, wt, s_res, tau, need);
+      chunk_counts<NS, false>(ck, C, tau, cc);
+    }
+  }
+  if (tid == 0) {
+    SelState o;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      o.tau[s] = s < NS ? tau[s] : 0u;
+      o.need_eq[s] = s < NS ? need[s] : 0u;
+      o.k_eff[s] = s < NS ? k_eff[s] : 0u;
+    }
+    o.pad[0] = o.pad[1] = 0u;
+    st[r] = o;
+  }
+}
+
+// write kernel: 256 threads, thread t holds list entries [4t, 4t+4) of a chunk
+template <int NS>
+__global__ void __launch_bounds__(kThreads)
+topk_write_cand_kernel(int64_t N, const uint32_t* __restrict__ cand_key, const int32_t* __restrict__ cand_pos,
+                       const uint32_t* __restrict__ cand_total, const SelState* __restrict__ st,
+                       const uint32_t* __restrict__ chunk_cnt, int32_t k, int32_t* __restrict__ idx_out,
+                       float* __restrict__ score_out, int32_t k2, int32_t* __restrict__ idx2_out) {
+  __shared__ uint32_t tmp[8];
+  __shared__ uint32_t red[2 * NS][4];
+  const int r = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const SelState S = st[r];
+  const uint32_t C = uniform_u32(cand_total[r]);
+  const uint32_t n_chunks = (C + kChunk - 1) / kChunk;
+  const int32_t kk_[2] = {k, NS == 2 ? k2 : 0};
+  int32_t* orow[2] = {idx_out + (int64_t)r * k, NS == 2 ? idx2_out + (int64_t)r * k2 : nullptr};
+  float* srow = score_out ? score_out + (int64_t)r * k : nullptr;
+  if (blockIdx.x == 0) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      for (int i = (int)S.k_eff[s] + tid; i < kk_[s]; i += kThreads) {
+        orow[s][i] = -1;
+        if (s == 0 && srow) srow[i] = __builtin_nanf("");
+      }
+  }
+  if (S.k_eff[0] == 0) return;
+  const uint32_t* cc = chunk_cnt + (int64_t)r * ((N + kChunk - 1) / kChunk) * 2 * NS;
+  const uint32_t* ck = cand_key + (int64_t)r * N;
+  const int32_t* cp = cand_pos + (int64_t)r * N;
+  for (uint32_t c = blockIdx.x; c < n_chunks; c += gridDim.x) {
+    // counts of the chunks before this one
+    uint32_t pre[2 * NS];
+#pragma unroll
+    for (int q = 0; q < 2 * NS; ++q) pre[q] = 0u;
+    for (uint32_t i = tid; i < c; i += kThreads)
+#pragma unroll
+      for (int q = 0; q < 2 * NS; ++q) pre[q] += cc[i * 2 * NS + q];
+#pragma unroll
+    for (int q = 0; q < 2 * NS; ++q) {
+      const uint32_t a = wave_sum_u32(pre[q]);
+      if (lane == 0) red[q][wave] = a;
+    }
+    const uint32_t v0 = c * kChunk + 4 * tid;
+    uint4 kv = make_uint4(0u, 0u, 0u, 0u);
+    int4 pv = make_int4(0, 0, 0, 0);
+    if (v0 < C) {
+      kv = *reinterpret_cast<const uint4*>(ck + v0);
+      pv = *reinterpret_cast<const int4*>(cp + v0);
+    }
+    __syncthreads();
+    const uint32_t k4[4] = {kv.x, kv.y, kv.z, kv.w};
+    const int32_t p4[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const uint32_t base_g = red[2 * s][0] + red[2 * s][1] + red[2 * s][2] + red[2 * s][3];
+      const uint32_t base_e = red[2 * s + 1][0] + red[2 * s + 1][1] + red[2 * s + 1][2] + red[2 * s + 1][3];
+      uint32_t ng = 0, ne = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        ng += v0 + j < C && k4[j] > S.tau[s];
+        ne += v0 + j < C && k4[j] == S.tau[s];
+      }
+      uint32_t tot;
+      uint32_t g = base_g + block_exclusive_scan(ng, tmp, tot);
+      uint32_t e = base_e + block_exclusive_scan(ne, tmp, tot);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool in = v0 + j < C;
+        const bool is_gt = in && k4[j] > S.tau[s];
+        const bool is_eq = in && k4[j] == S.tau[s];
+        const bool take = is_gt || (is_eq && e < S.need_eq[s]);
+        const uint32_t o = g + (is_gt ? min(e, S.need_eq[s]) : e);
+        g += is_gt ? 1u : 0u;
+        e += is_eq ? 1u : 0u;
+        if (take && o < S.k_eff[s]) {
+          orow[s][o] = p4[j];
+          if (s == 0 && srow) srow[o] = key_score(k4[j]);
+        }
+      }
+    }
+    __syncthreads();
   }
 }
 
 static int n_segments(int64_t N) { return (int)((N + kSeg - 1) / kSeg); }
 
 enum Path { kSmall, kCompact, kMultipass };
+constexpr int kMaxSeg = 2048;                           // segments per row in the compact path
 constexpr int64_t kCandBudget = int64_t(1) << 30;     // candidate-list bytes allowed in the workspace
+constexpr int64_t kCandBytesPerSlot = 16;             // per-segment and flat (key, position) lists
 
 static int compact_seg(int64_t N) {
   int64_t seg = kSeg;
@@ -942,24 +1095,29 @@ static int compact_seg(int64_t N) {
 
 static Path choose_path(int32_t R, int64_t N) {
   if (N <= kSmallMax) return kSmall;
-  if ((int64_t)R * N * (int64_t)sizeof(uint2) <= kCandBudget) return kCompact;
+  if ((int64_t)R * N * kCandBytesPerSlot <= kCandBudget) return kCompact;
   return kMultipass;
 }
 
 struct CompactLayout {
-  size_t hist0, cand_count, seg_gt, seg_off, state, cand, total;
+  size_t hist0, seg_cnt, cand_total, state, chunk_cnt, seg_key, seg_pos, cand_key, cand_pos, total;
 };
 
 static CompactLayout compact_layout(int32_t R, int64_t N) {
   CompactLayout L;
-  const int n_seg = (int)((N + compact_seg(N) - 1) / compact_seg(N));
+  const int seg = compact_seg(N);
+  const int n_seg = (int)((N + seg - 1) / seg);
+  const size_t slots = (size_t)R * N * 4;
   size_t off = 0;
-  L.hist0 = off; off += align_up((size_t)R * kBins * 4, 256);
-  L.cand_count = off; off += align_up((size_t)R * 4, 256);
-  L.seg_gt = off; off += align_up((size_t)R * n_seg * 4, 256);
-  L.seg_off = off; off += align_up((size_t)R * n_seg * 4, 256);
-  L.state = off; off += align_up((size_t)R * sizeof(CompactState), 256);
-  L.cand = off; off += align_up((size_t)R * N * sizeof(uint2), 256);
+  L.hist0 = off; off += align_up((size_t)R * kTopBins * 4, 256);
+  L.seg_cnt = off; off += align_up((size_t)R * n_seg * 4, 256);
+  L.cand_total = off; off += align_up((size_t)R * 4, 256);
+  L.state = off; off += align_up((size_t)R * sizeof(SelState), 256);
+  L.chunk_cnt = off; off += align_up((size_t)R * ((N + kChunk - 1) / kChunk) * 4 * sizeof(uint32_t), 256);
+  L.seg_key = off; off += align_up(slots, 256);
+  L.seg_pos = off; off += align_up(slots, 256);
+  L.cand_key = off; off += align_up(slots, 256);
+  L.cand_pos = off; off += align_up(slots, 256);
   L.total = off;
   return L;
 }
@@ -981,63 +1139,58 @@ static size_t workspace_for(int32_t R, int64_t N) {
   }
 }
 
-}  // namespace csa2
-
-using namespace csa2;
-
-extern "C" size_t csa2_topk_workspace_size(int32_t R, int64_t N, int32_t k) {
-  (void)k;
-  if (R <= 0 || N <= 0) return 0;
-  return workspace_for(R, N);
+static void launch_small(const float* scores, int32_t R, int64_t N, int64_t row_stride, int32_t k,
+                         const int32_t* index_map, int32_t* idx_out, float* score_out, hipStream_t s) {
+  const int J = (int)((N + kSmallThreads * 4 - 1) / (kSmallThreads * 4));
+  if (J <= 1)
+    topk_small_kernel<1><<<R, kSmallThreads, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out);
+  else if (J <= 2)
+    topk_small_kernel<2><<<R, kSmallThreads, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out);
+  else if (J <= 4)
+    topk_small_kernel<4><<<R, kSmallThreads, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out);
+  else
+    topk_small_kernel<8><<<R, kSmallThreads, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out);
 }
 
-extern "C" csa2_status csa2_topk(const float* scores, int32_t R, int64_t N, int64_t row_stride, int32_t k,
-                                 const int32_t* index_map, int32_t* idx_out, float* score_out, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
-  if (!scores || !idx_out) return CSA2_EINVAL;
-  if (R <= 0 || N <= 0 || k <= 0) return CSA2_EINVAL;
-  if (N % 4 != 0 || N >= (int64_t(1) << 31)) return CSA2_ESHAPE;
-  if (row_stride < N || row_stride % 4 != 0) return CSA2_EINVAL;
-  if (!aligned(scores, 16) || (index_map && !aligned(index_map, 16)) || !aligned(idx_out, 4))
-    return CSA2_EALIGN;
-  const size_t need = workspace_for(R, N);
-  if (!workspace || workspace_bytes < need) return CSA2_EWORKSPACE;
-  if (!aligned(workspace, 256)) return CSA2_EALIGN;
-  hipStream_t s = (hipStream_t)stream;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const Path path = choose_path(R, N);
-  if (path == kSmall) {
-    const int J = (int)((N + kSmallThreads * 4 - 1) / (kSmallThreads * 4));
-    if (J <= 1)
-      topk_small_kernel<1><<<R, kSmallThreads, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out);
-    else if (J <= 2)
-      topk_small_kernel<2><<<R, kSmallThreads, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out);
-    else if (J <= 4)
-      topk_small_kernel<4><<<R, kSmallThreads, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out);
-    else
-      topk_small_kernel<8><<<R, kSmallThreads, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out);
-    return launch_status();
+// compact path; a second selection (k2 <= k, positions only) when idx2_out is set
+static void launch_compact(const float* scores, int32_t R, int64_t N, int64_t row_stride, int32_t k,
+                           const int32_t* index_map, int32_t* idx_out, float* score_out, int32_t k2,
+                           int32_t* idx2_out, uint8_t* ws, hipStream_t s) {
+  const CompactLayout L = compact_layout(R, N);
+  const int seg = compact_seg(N);
+  const int nseg = (int)((N + seg - 1) / seg);
+  uint32_t* hist0 = reinterpret_cast<uint32_t*>(ws + L.hist0);
+  uint32_t* seg_cnt = reinterpret_cast<uint32_t*>(ws + L.seg_cnt);
+  uint32_t* cand_total = reinterpret_cast<uint32_t*>(ws + L.cand_total);
+  uint32_t* seg_key = reinterpret_cast<uint32_t*>(ws + L.seg_key);
+  int32_t* seg_pos = reinterpret_cast<int32_t*>(ws + L.seg_pos);
+  uint32_t* cand_key = reinterpret_cast<uint32_t*>(ws + L.cand_key);
+  int32_t* cand_pos = reinterpret_cast<int32_t*>(ws + L.cand_pos);
+  const int64_t nh = (int64_t)R * kTopBins;
+  topk_zero_kernel<<<(int)((nh + kThreads - 1) / kThreads), kThreads, 0, s>>>(hist0, nh);
+  topk_top_hist_kernel<<<dim3(n_segments(N), R), kThreads, 0, s>>>(scores, N, row_stride, index_map, hist0);
+  topk_compact_kernel<<<dim3(nseg, R), kThreads, 0, s>>>(scores, N, row_stride, index_map, k, seg, hist0, seg_key,
+                                                         seg_pos, seg_cnt, nseg);
+  topk_flatten_kernel<<<dim3(nseg, R), kThreads, 0, s>>>(N, seg, seg_key, seg_pos, seg_cnt, nseg, cand_key, cand_pos,
+                                                         cand_total);
+  SelState* st = reinterpret_cast<SelState*>(ws + L.state);
+  uint32_t* chunk_cnt = reinterpret_cast<uint32_t*>(ws + L.chunk_cnt);
+  if (idx2_out) {
+    topk_select_cand_kernel<2><<<R, kFinishThreads, 0, s>>>(N, hist0, cand_key, cand_total, k, k2, st, chunk_cnt);
+    topk_write_cand_kernel<2><<<dim3(kWriteBlocks, R), kThreads, 0, s>>>(N, cand_key, cand_pos, cand_total, st,
+                                                                         chunk_cnt, k, idx_out, score_out, k2,
+                                                                         idx2_out);
+  } else {
+    topk_select_cand_kernel<1><<<R, kFinishThreads, 0, s>>>(N, hist0, cand_key, cand_total, k, 0, st, chunk_cnt);
+    topk_write_cand_kernel<1><<<dim3(kWriteBlocks, R), kThreads, 0, s>>>(N, cand_key, cand_pos, cand_total, st,
+                                                                         chunk_cnt, k, idx_out, score_out, 0,
+                                                                         nullptr);
   }
-  if (path == kCompact) {
-    const CompactLayout L = compact_layout(R, N);
-    const int seg = compact_seg(N);
-    const int nseg = (int)((N + seg - 1) / seg);
-    uint32_t* hist0 = reinterpret_cast<uint32_t*>(ws + L.hist0);
-    uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + L.cand_count);
-    uint32_t* seg_gt = reinterpret_cast<uint32_t*>(ws + L.seg_gt);
-    uint32_t* seg_off = reinterpret_cast<uint32_t*>(ws + L.seg_off);
-    CompactState* st = reinterpret_cast<CompactState*>(ws + L.state);
-    uint2* cand = reinterpret_cast<uint2*>(ws + L.cand);
-    dim3 g2(nseg, R);
-    topk_cinit_kernel<<<R, kThreads, 0, s>>>(hist0, cnt);
-    topk_hist_kernel<0><<<dim3(n_segments(N), R), kThreads, 0, s>>>(scores, N, row_stride, index_map, hist0, nullptr);
-    topk_compact_kernel<<<g2, kThreads, 0, s>>>(scores, N, row_stride, index_map, k, seg, hist0, cnt, cand, N, seg_gt,
-                                                nseg);
-    topk_refine_kernel<<<R, 1024, 0, s>>>(k, seg, hist0, cnt, cand, N, seg_gt, seg_off, nseg, st);
-    topk_cwrite_kernel<<<g2, kThreads, 0, s>>>(scores, N, row_stride, index_map, seg, st, seg_off, nseg, k, idx_out,
-                                               score_out);
-    return launch_status();
-  }
+}
+
+static void launch_multipass(const float* scores, int32_t R, int64_t N, int64_t row_stride, int32_t k,
+                             const int32_t* index_map, int32_t* idx_out, float* score_out, uint8_t* ws,
+                             hipStream_t s) {
   size_t off_state, off_seg;
   ws_layout(R, N, &off_state, &off_seg);
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws);
@@ -1054,5 +1207,75 @@ extern "C" csa2_status csa2_topk(const float* scores, int32_t R, int64_t N, int6
   topk_select_kernel<2><<<R, kThreads, 0, s>>>(hist, st, k);
   topk_count_kernel<<<g2, kThreads, 0, s>>>(scores, N, row_stride, index_map, st, seg, nseg);
   topk_write_kernel<<<g2, kThreads, 0, s>>>(scores, N, row_stride, index_map, st, seg, nseg, k, idx_out, score_out);
+}
+
+static csa2_status check_scores(const float* scores, int32_t R, int64_t N, int64_t row_stride,
+                                const int32_t* index_map) {
+  if (!scores) return CSA2_EINVAL;
+  if (R <= 0 || N <= 0) return CSA2_EINVAL;
+  if (N % 4 != 0 || N >= (int64_t(1) << 31)) return CSA2_ESHAPE;
+  if (row_stride < N || row_stride % 4 != 0) return CSA2_EINVAL;
+  if (!aligned(scores, 16) || (index_map && !aligned(index_map, 16))) return CSA2_EALIGN;
+  return CSA2_OK;
+}
+
+}  // namespace csa2
+
+using namespace csa2;
+
+extern "C" size_t csa2_topk_workspace_size(int32_t R, int64_t N, int32_t k) {
+  (void)k;
+  if (R <= 0 || N <= 0) return 0;
+  return workspace_for(R, N);
+}
+
+extern "C" csa2_status csa2_topk(const float* scores, int32_t R, int64_t N, int64_t row_stride, int32_t k,
+                                 const int32_t* index_map, int32_t* idx_out, float* score_out, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  csa2_status st = check_scores(scores, R, N, row_stride, index_map);
+  if (st != CSA2_OK) return st;
+  if (!idx_out || k <= 0) return CSA2_EINVAL;
+  if (!aligned(idx_out, 4) || (score_out && !aligned(score_out, 4))) return CSA2_EALIGN;
+  if (!workspace || workspace_bytes < workspace_for(R, N)) return CSA2_EWORKSPACE;
+  if (!aligned(workspace, 256)) return CSA2_EALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  switch (choose_path(R, N)) {
+    case kSmall: launch_small(scores, R, N, row_stride, k, index_map, idx_out, score_out, s); break;
+    case kCompact: launch_compact(scores, R, N, row_stride, k, index_map, idx_out, score_out, 0, nullptr, ws, s); break;
+    default: launch_multipass(scores, R, N, row_stride, k, index_map, idx_out, score_out, ws, s); break;
+  }
+  return launch_status();
+}
+
+extern "C" size_t csa2_topk_pool_workspace_size(int32_t R, int64_t N, int32_t k_pool) {
+  return csa2_topk_workspace_size(R, N, k_pool);
+}
+
+extern "C" csa2_status csa2_topk_pool(const float* scores, int32_t R, int64_t N, int64_t row_stride, int32_t k_pool,
+                                      int32_t k_top, const int32_t* index_map, int32_t* pool_idx,
+                                      float* pool_scores, int32_t* top_idx, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  csa2_status st = check_scores(scores, R, N, row_stride, index_map);
+  if (st != CSA2_OK) return st;
+  if (!pool_idx || !top_idx || k_pool <= 0 || k_top <= 0 || k_top > k_pool) return CSA2_EINVAL;
+  if (!aligned(pool_idx, 4) || !aligned(top_idx, 4) || (pool_scores && !aligned(pool_scores, 4))) return CSA2_EALIGN;
+  if (!workspace || workspace_bytes < workspace_for(R, N)) return CSA2_EWORKSPACE;
+  if (!aligned(workspace, 256)) return CSA2_EALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  switch (choose_path(R, N)) {
+    case kSmall:
+      launch_small(scores, R, N, row_stride, k_pool, index_map, pool_idx, pool_scores, s);
+      launch_small(scores, R, N, row_stride, k_top, index_map, top_idx, nullptr, s);
+      break;
+    case kCompact:
+      launch_compact(scores, R, N, row_stride, k_pool, index_map, pool_idx, pool_scores, k_top, top_idx, ws, s);
+      break;
+    default:
+      launch_multipass(scores, R, N, row_stride, k_pool, index_map, pool_idx, pool_scores, ws, s);
+      launch_multipass(scores, R, N, row_stride, k_top, index_map, top_idx, nullptr, ws, s);
+      break;
+  }
   return launch_status();
 }

@@ -17,6 +17,7 @@ from typing import List, Optional, Sequence
 import torch
 
 from . import (csa2_fp4_pack, csa2_index_full, csa2_index_reindex, csa2_topk, csa2_topk_workspace_size,
+               csa2_topk_pool, csa2_topk_pool_workspace_size,
                csa2_sparse_decode, csa2_sparse_decode_workspace_size, csa2_swa_merge,
                csa2_swa_merge_workspace_size, csa2_sparse_swa_decode, csa2_sparse_swa_decode_workspace_size)
 
@@ -76,7 +77,9 @@ class Csa2DecodeStack:
             self.re_scores = torch.empty((B, self.P), dtype=f32, device=dev)
         self.o = torch.empty((self.L, B, H, LATENT), dtype=f32, device=dev)
         self.lse = torch.empty((self.L, B, H), dtype=f32, device=dev)
-        self.ws_topk_full = torch.empty(csa2_topk_workspace_size(B, T, max(K, self.P)), dtype=u8, device=dev)
+        self.ws_topk_full = torch.empty(max(csa2_topk_workspace_size(B, T, K),
+                                            csa2_topk_pool_workspace_size(B, T, self.P) if self.use_pool else 0),
+                                        dtype=u8, device=dev)
         self.ws_topk_pool = (torch.empty(csa2_topk_workspace_size(B, self.P, K), dtype=u8, device=dev)
                              if self.use_pool else None)
         self.ws_sparse = torch.empty(csa2_sparse_decode_workspace_size(B, H, K), dtype=u8, device=dev)
@@ -107,11 +110,14 @@ class Csa2DecodeStack:
                 if time_index:
                     e1.record()
                     self.index_events = (e0, e1)
-                if self.use_pool:
+                if self.use_pool and K <= self.P:
+                    # the pool and this layer's Top-K (the top K of the pool) in one selection
+                    csa2_topk_pool(self.scores, self.P, K, self.pool, idx, pool_scores=self.pool_scores,
+                                   workspace=self.ws_topk_full, stream=stream)
+                elif self.use_pool:
                     csa2_topk(self.scores, self.P, self.pool, score_out=self.pool_scores,
                               workspace=self.ws_topk_full, stream=stream)
-                    csa2_topk(self.pool_scores, K, idx, index_map=self.pool, workspace=self.ws_topk_pool,
-                              stream=stream)
+                    csa2_topk(self.scores, K, idx, workspace=self.ws_topk_full, stream=stream)
                 else:
                     csa2_topk(self.scores, K, idx, workspace=self.ws_topk_full, stream=stream)
                 prev_idx = idx

@@ -164,6 +164,29 @@ csa2_status csa2_topk(const float* scores, int32_t R, int64_t N, int64_t row_str
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Candidate pool and its Top-K in one selection (MarkTechPost retelling,
+ * paragraph 3: a decoder Full layer fills a pool of up to 16,384 positions
+ * for the Reindex layers and takes its own Top-K; the HN summary key points:
+ * the deeper layers search only that pool).
+ *
+ * Equivalent to two csa2_topk calls on the same scores:
+ *   pool_idx / pool_scores = csa2_topk(scores, k_pool, index_map, score_out)
+ *   top_idx                = csa2_topk(scores, k_top,  index_map)
+ * (the top k_top entries are the top k_top of the pool, since k_top <= k_pool),
+ * but long rows are read and reduced to candidates only once.
+ *
+ *   pool_idx    int32 [R][k_pool];  pool_scores fp32 [R][k_pool] or NULL
+ *   top_idx     int32 [R][k_top]
+ *   workspace   >= csa2_topk_pool_workspace_size(R, N, k_pool) bytes
+ * Other arguments and the selection rule as for csa2_topk.
+ * Errors: as csa2_topk, and EINVAL when k_top > k_pool.
+ * ------------------------------------------------------------------------- */
+size_t csa2_topk_pool_workspace_size(int32_t R, int64_t N, int32_t k_pool);
+csa2_status csa2_topk_pool(const float* scores, int32_t R, int64_t N, int64_t row_stride, int32_t k_pool,
+                           int32_t k_top, const int32_t* index_map, int32_t* pool_idx, float* pool_scores,
+                           int32_t* top_idx, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Sparse attention over the FP4 cache (HN summary key points: global sparse
  * retrieval over the shared main KV).
  *

@@ -73,6 +73,18 @@ def test_topk_argument_errors_and_workspace():
     assert L.csa2_topk(DUMMY, 1, 64, 64, 8, NULL, DUMMY, NULL, NULL, 1 << 20, NULL) == 4
 
 
+def test_topk_pool_argument_errors():
+    L = F.lib()
+    ws = 1 << 20
+    assert F.csa2_topk_pool_workspace_size(8, 1 << 20, 16384) == F.csa2_topk_workspace_size(8, 1 << 20, 16384)
+    # k_top > k_pool, k_top <= 0, missing top_idx, small workspace
+    assert L.csa2_topk_pool(DUMMY, 1, 64, 64, 8, 9, NULL, DUMMY, NULL, DUMMY, DUMMY, ws, NULL) == 1
+    assert L.csa2_topk_pool(DUMMY, 1, 64, 64, 8, 0, NULL, DUMMY, NULL, DUMMY, DUMMY, ws, NULL) == 1
+    assert L.csa2_topk_pool(DUMMY, 1, 64, 64, 8, 4, NULL, DUMMY, NULL, NULL, DUMMY, ws, NULL) == 1
+    assert L.csa2_topk_pool(DUMMY, 1, 62, 64, 8, 4, NULL, DUMMY, NULL, DUMMY, DUMMY, ws, NULL) == 2
+    assert L.csa2_topk_pool(DUMMY, 1, 64, 64, 8, 4, NULL, DUMMY, NULL, DUMMY, DUMMY, 16, NULL) == 4
+
+
 def test_attention_argument_errors_and_workspace():
     L = F.lib()
     assert F.csa2_sparse_decode_workspace_size(64, 64, 2048) > 64 * 64 * 512 * 4

@@ -235,3 +235,50 @@ def test_topk_multipass_path_sampled_rows():
     for r in (0, 519, R - 1):
         row = s[r].cpu().numpy().astype(np.float64)
         assert np.array_equal(idx[r].cpu().numpy(), OT.topk(row, k)), r
+
+
+@pytest.mark.parametrize("R,N,k_pool,k_top,ties", [
+    (8, 16384, 4096, 512, False),          # one-workgroup path (two selections)
+    (4, 131072, 16384, 2048, False),       # candidate-list path, both selections from one list
+    (3, 65536, 20000, 20000, True),        # k_top == k_pool, heavy ties
+    (2, 1 << 20, 16384, 2048, False),      # the 1M-context pool shape
+])
+def test_topk_pool_matches_two_selections(R, N, k_pool, k_top, ties):
+    dev = device()
+    g = torch.Generator(device=dev).manual_seed(N + k_pool)
+    if ties:
+        s = torch.randint(0, 6, (R, N), device=dev, generator=g).to(torch.float32)
+        s[0, ::5] = -float("inf")
+    else:
+        s = torch.randn((R, N), device=dev, generator=g) * 8
+    pool = torch.empty((R, k_pool), dtype=torch.int32, device=dev)
+    pool_s = torch.empty((R, k_pool), dtype=torch.float32, device=dev)
+    top = torch.empty((R, k_top), dtype=torch.int32, device=dev)
+    F.csa2_topk_pool(s, k_pool, k_top, pool, top, pool_scores=pool_s)
+    sh = s.cpu().numpy().astype(np.float64)
+    gp, gs, gt = pool.cpu().numpy(), pool_s.cpu().numpy(), top.cpu().numpy()
+    for r in range(R):
+        ref_pool = OT.topk(sh[r], k_pool)
+        assert np.array_equal(gp[r], ref_pool), r
+        valid = ref_pool >= 0
+        assert np.array_equal(gs[r][valid], sh[r][ref_pool[valid]].astype(np.float32)), r
+        assert np.all(np.isnan(gs[r][~valid]))
+        assert np.array_equal(gt[r], OT.topk(sh[r], k_top)), r
+
+
+def test_topk_pool_with_index_map_and_long_rows_path():
+    # long rows beyond the candidate-list budget (two multipass selections), sampled rows
+    dev = device()
+    R, N, k_pool, k_top = 520, 131072, 4096, 256
+    g = torch.Generator(device=dev).manual_seed(77)
+    s = torch.randn((R, N), device=dev, generator=g)
+    imap = torch.arange(N, dtype=torch.int32, device=dev).repeat(R, 1) * 3 + 1
+    imap[:, 7::11] = -1
+    pool = torch.empty((R, k_pool), dtype=torch.int32, device=dev)
+    top = torch.empty((R, k_top), dtype=torch.int32, device=dev)
+    F.csa2_topk_pool(s, k_pool, k_top, pool, top, index_map=imap)
+    for r in (0, 259, 519):
+        sh = s[r].cpu().numpy().astype(np.float64)
+        mh = imap[r].cpu().numpy()
+        assert np.array_equal(pool[r].cpu().numpy(), OT.topk(sh, k_pool, index_map=mh)), r
+        assert np.array_equal(top[r].cpu().numpy(), OT.topk(sh, k_top, index_map=mh)), r
