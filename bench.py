@@ -149,7 +149,7 @@ class Workload:
     def __init__(self, cfg, dev, chunk_rows=65536):
         import torch
         import workloads as W
-        from fp4_sparse_attention_amd.decode import LayerIO, pack_cache
+        from fp4_sparse_attention_amd.decode import StackIO, pack_cache
         B, T = cfg.batch, cfg.context
         self.T = T
         self.cfg = cfg
@@ -161,12 +161,12 @@ class Workload:
         self.scales = torch.empty((B, T, 32), dtype=torch.uint8, device=dev)
         pack_cache(self.codes, self.scales, self.latent_chunk, self.chunk_rows)
         self.k_idx = torch.stack([W.fp8_normal(cfg.seed, (T, 64), device=dev, chunk_index=b) for b in range(B)])
-        self.layers = []
-        for li in range(len(cfg.modes)):
-            d = W.decode_layer_inputs(cfg.seed, li, B, cfg.heads, cfg.window, B, device=dev, outliers=self.outliers)
-            self.layers.append(LayerIO(d["q_lat"], d["q_idx"], d["swa"],
-                                       torch.zeros(B, dtype=torch.int32, device=dev),
-                                       torch.full((B,), min(cfg.window, T), dtype=torch.int32, device=dev)))
+        L = len(cfg.modes)
+        ds = [W.decode_layer_inputs(cfg.seed, li, B, cfg.heads, cfg.window, B, device=dev, outliers=self.outliers)
+              for li in range(L)]
+        self.layers = StackIO(torch.stack([d["q_lat"] for d in ds]), torch.stack([d["q_idx"] for d in ds]),
+                              torch.stack([d["swa"] for d in ds]), torch.zeros((L, B), dtype=torch.int32, device=dev),
+                              torch.full((L, B), min(cfg.window, T), dtype=torch.int32, device=dev))
         # the current token's latent row, packed into position T-1 by every step
         self.new_rows = self.latent_chunk_rows_at(T - 1)
         torch.cuda.synchronize()

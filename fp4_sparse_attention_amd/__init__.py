@@ -44,6 +44,10 @@ _SIGS = {
     "csa2_sparse_swa_decode": (_i32, [_c_void_p, _i32, _i32, _c_void_p, _c_void_p, _i32, _i64, _c_void_p, _c_void_p,
                                       _i32, _c_void_p, _i32, _c_void_p, _c_void_p, _f32, _c_void_p, _c_void_p,
                                       _c_void_p, _size_t, _c_void_p]),
+    "csa2_sparse_swa_decode_layers_workspace_size": (_size_t, [_i32, _i32, _i32, _i32]),
+    "csa2_sparse_swa_decode_layers": (_i32, [_i32, _c_void_p, _i32, _i32, _c_void_p, _c_void_p, _i32, _i64, _c_void_p,
+                                             _c_void_p, _c_void_p, _i32, _c_void_p, _i32, _c_void_p, _c_void_p, _f32,
+                                             _c_void_p, _c_void_p, _c_void_p, _size_t, _c_void_p]),
     "csa2_swa_merge": (_i32, [_c_void_p, _i32, _i32, _c_void_p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _f32,
                               _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t, _c_void_p]),
 }
@@ -345,3 +349,48 @@ def csa2_sparse_swa_decode(q_lat, codes, scales, idx, swa, swa_start, swa_len, s
                                       _p(swa), S, _p(swa_start), _p(swa_len), float(softmax_scale), _p(o), _p(lse),
                                       _p(workspace), workspace.numel(), _stream(stream))
     _check("csa2_sparse_swa_decode", st)
+
+
+def csa2_sparse_swa_decode_layers_workspace_size(L, R, H, K):
+    return int(lib().csa2_sparse_swa_decode_layers_workspace_size(L, R, H, K))
+
+
+def csa2_sparse_swa_decode_layers(q_lat, codes, scales, idx, layer_idx, swa, swa_start, swa_len, softmax_scale, o,
+                                  lse, row_seq=None, workspace=None, stream=None):
+    """L layers of csa2_sparse_swa_decode in one launch: q_lat bf16 [L, R, H, 512]; idx int32 [n, R, K];
+    layer_idx: L ints (host) selecting each layer's idx slice; swa bf16 [L, B, S, 512];
+    swa_start/swa_len int32 [L, R]; o fp32 [L, R, H, 512]; lse fp32 [L, R, H]."""
+    _need(q_lat, torch.bfloat16, "q_lat", 4)
+    _need(codes, torch.uint8, "codes", 3)
+    _need(scales, torch.uint8, "scales", 3)
+    _need(idx, torch.int32, "idx", 3)
+    _need(swa, torch.bfloat16, "swa", 4)
+    _need(swa_start, torch.int32, "swa_start", 2)
+    _need(swa_len, torch.int32, "swa_len", 2)
+    _need(o, torch.float32, "o", 4)
+    _need(lse, torch.float32, "lse", 3)
+    for t, nm in ((q_lat, "q_lat"), (codes, "codes"), (scales, "scales"), (idx, "idx"), (swa, "swa"),
+                  (swa_start, "swa_start"), (swa_len, "swa_len"), (o, "o"), (lse, "lse")):
+        _dense(t, nm)
+    L, R, H, C = q_lat.shape
+    B, T, cb = codes.shape
+    n, Ri, K = idx.shape
+    S = swa.shape[2]
+    layer_idx = [int(v) for v in layer_idx]
+    if (C != 512 or cb != 256 or Ri != R or len(layer_idx) != L or swa.shape != (L, B, S, 512)
+            or swa_start.shape != (L, R) or swa_len.shape != (L, R) or o.shape != (L, R, H, 512)
+            or lse.shape != (L, R, H)):
+        raise ValueError("sparse_swa_decode_layers shapes")
+    if any(v < 0 or v >= n for v in layer_idx):
+        raise ValueError("layer_idx entries must select one of the idx slices")
+    if row_seq is not None:
+        _need(row_seq, torch.int32, "row_seq", 1)
+    need = csa2_sparse_swa_decode_layers_workspace_size(L, R, H, K)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_lat.device)
+    host_idx = (ctypes.c_int32 * L)(*layer_idx)
+    st = lib().csa2_sparse_swa_decode_layers(L, _p(q_lat), R, H, _p(codes), _p(scales), B, T, _p(row_seq), _p(idx),
+                                             ctypes.cast(host_idx, ctypes.c_void_p), K, _p(swa), S, _p(swa_start),
+                                             _p(swa_len), float(softmax_scale), _p(o), _p(lse), _p(workspace),
+                                             workspace.numel(), _stream(stream))
+    _check("csa2_sparse_swa_decode_layers", st)

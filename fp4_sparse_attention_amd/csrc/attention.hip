@@ -7,7 +7,7 @@
 // same 512-channel latent rows, used as key and as value.
 //
 // Work split (split-K): a workgroup of four waves owns one query row and one
-// chunk of keys (a run of 32-key tiles from idx, or the row's window rows), for
+// chunk of keys (a run of 32-key tiles from idx, or one 32-row tile of the row's window), for
 // all H <= 64 heads.  Wave w owns latent channels [128w, 128w+128):
 //   1. gather: lane (m = l%16, g = l/16) loads 16 code bytes + 2 scale bytes
 //      (32 channels) of keys m and 16+m of the tile -- each FP4 element is
@@ -40,6 +40,7 @@ constexpr int kSStride = 36;             // floats per head row of a partial-sco
 constexpr int kPStride = 40;             // halfs per head row of P
 constexpr int kMaxChunkTiles = 64;       // tiles per chunk at most
 constexpr int kMaxChunkKeys = kMaxChunkTiles * kKT;
+constexpr int kWindowChunks = kWindowMax / kKT;   // one-tile chunks covering the longest window
 constexpr float kRescaleSlack = 8.0f;    // keep the reference max until exceeded by 2^8
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -76,28 +77,39 @@ __device__ __forceinline__ f16x4 lds_tr16(const _Float16* p) {
   return __builtin_bit_cast(f16x4, v);
 }
 
+constexpr int kMaxLayers = 8;
+
+// One launch covers L layers.  Layer l has its own queries, window rows and
+// outputs, and reads the index slice at idx + idx_off[l] (layers may share one).
+// Each (layer, row) splits its keys into n_chunks chunks: chunk c takes the
+// window tiles [c wpc, (c+1) wpc) (tile w: rows [32w, 32w+32) of the window)
+// and the sparse tiles [c spc, (c+1) spc).  Window tiles go first; the loads of
+// the first one are issued at the start of the workgroup.
 struct AttnArgs {
-  const uint16_t* q_lat;          // bf16 [R][H][512]
-  int H;
+  const uint16_t* q_lat;          // bf16 [L][R][H][512]
+  int R, H, L, head_groups;
   const uint8_t* codes;           // [B][T][256]
   const uint8_t* scales;          // [B][T][32]
   int64_t T;
   const int32_t* row_seq;         // [R] or null
-  const int32_t* idx;             // [R][K] (sparse chunks)
+  const int32_t* idx;             // index slices [.][R][K]
+  int64_t idx_off[kMaxLayers];    // element offset of layer l's slice
   int K;
-  int n_sparse_chunks;
-  int tiles_per_chunk;
-  const uint16_t* swa;            // bf16 [B][S][512] (window chunk)
-  int S;
-  const int32_t* swa_start;
-  const int32_t* swa_len;
-  int n_chunks;                   // sparse chunks + (window ? 1 : 0)
+  int n_sparse_tiles;             // ceil(K / 32), 0 without sparse keys
+  int n_window_tiles;             // tiles covering the longest window, 0 without a window
+  int window_per_chunk;           // window tiles per chunk
+  int sparse_per_chunk;           // sparse tiles per chunk
+  int n_chunks;
+  const uint16_t* swa;            // bf16 [L][B][S][512]
+  int B, S;
+  const int32_t* swa_start;       // [L][R]
+  const int32_t* swa_len;         // [L][R]
   float scale_log2;               // softmax scale * log2(e)
-  float* o_part;                  // [R][n_chunks][H][512]
-  float* ml_part;                 // [R][n_chunks][H][2]
+  float* o_part;                  // [L][R][n_chunks][H][512]
+  float* ml_part;                 // [L][R][n_chunks][H][2]
 };
 
-// raw FP4 data of the lane's two keys for one tile (prefetched one tile ahead)
+// raw FP4 data of the lane's two keys for one tile (prefetched two tiles ahead)
 struct RawTile {
   uint4 v[2];         // 16 code bytes (32 channels) per key
   uint32_t sc[2];     // 2 scale bytes per key
@@ -116,35 +128,56 @@ attn_chunk_kernel(const AttnArgs a) {
 
   const int chunk = blockIdx.x;
   const int r = blockIdx.y;
+  const int layer = blockIdx.z / a.head_groups;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int m = lane & 15;
   const int g = lane >> 4;
   const int H = a.H;
-  const int hbase = blockIdx.z * NT * 16;        // this workgroup's first head
+  const int hbase = (blockIdx.z % a.head_groups) * NT * 16;      // this workgroup's first head
   const int seq = a.row_seq ? a.row_seq[r] : r;
-  const bool is_window = chunk >= a.n_sparse_chunks;
+  const int cbase = 128 * wave;                                   // this wave's channel slice
 
-  int k_begin, k_end, w_start = 0;
-  if (!is_window) {
-    k_begin = chunk * a.tiles_per_chunk * kKT;
-    k_end = min(a.K, k_begin + a.tiles_per_chunk * kKT);
-  } else {
-    int st = a.swa_start[r], ln = a.swa_len[r];
-    bool ok = st >= 0 && ln >= 0 && ln <= kWindowMax && (int64_t)st + ln <= a.S;
-    k_begin = 0;
-    k_end = ok ? ln : 0;
-    w_start = ok ? st : 0;
+  // this chunk's tiles: window tiles [w0, w0 + n_wt), then sparse tiles [sp0, sp0 + n_sp)
+  const int w0 = chunk * a.window_per_chunk;
+  const int n_wt = max(0, min(a.n_window_tiles, w0 + a.window_per_chunk) - w0);
+  const int sp0 = chunk * a.sparse_per_chunk;
+  const int n_sp = max(0, min(a.n_sparse_tiles, sp0 + a.sparse_per_chunk) - sp0);
+  const int k0 = sp0 * kKT;
+  const int k1 = min(a.K, (sp0 + n_sp) * kKT);
+
+  // window rows of tile w: lane (m, g) takes channels cbase + 32g + [0, 32) of rows 32w + 16mt + m
+  uint4 wv[2][4];
+  int wvalid[2] = {0, 0};
+  int w_st = 0, w_ln = 0;
+  const uint16_t* swa_l = nullptr;
+  if (n_wt > 0) {
+    const int st = a.swa_start[layer * a.R + r], ln = a.swa_len[layer * a.R + r];
+    const bool ok = st >= 0 && ln >= 0 && ln <= kWindowMax && (int64_t)st + ln <= a.S;
+    w_st = ok ? st : 0;
+    w_ln = ok ? ln : 0;
+    swa_l = a.swa + (int64_t)layer * a.B * a.S * kLatent;
   }
-  const int n_tiles = k_end > k_begin ? (k_end - k_begin + kKT - 1) / kKT : 0;
-  const int cbase = 128 * wave;                  // this wave's channel slice
+  auto load_window = [&](int w) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int kk = w * kKT + 16 * mt + m;
+      wvalid[mt] = kk < w_ln;
+      const uint4* p = reinterpret_cast<const uint4*>(swa_l + ((int64_t)seq * a.S + (wvalid[mt] ? w_st + kk : 0)) *
+                                                      kLatent + cbase + 32 * g);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) wv[mt][ks] = wvalid[mt] ? p[ks] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  if (n_wt > 0) load_window(w0);
 
   // queries: B operand of S^T = X . Q^T; k-step ks holds channels cbase + 32g + 8ks + [0, 8)
+  const uint16_t* q_l = a.q_lat + (int64_t)layer * a.R * H * kLatent;
   f16x8 qb[NT][4];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const uint16_t* qrow = a.q_lat + ((int64_t)r * H + hbase + 16 * nt + m) * kLatent + cbase + 32 * g;
+    const uint16_t* qrow = q_l + ((int64_t)r * H + hbase + 16 * nt + m) * kLatent + cbase + 32 * g;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qb[nt][ks] = bf16x8_to_f16(*reinterpret_cast<const uint4*>(qrow + 8 * ks));
   }
@@ -157,24 +190,23 @@ attn_chunk_kernel(const AttnArgs a) {
   float m_run = -__builtin_inff();
   float l_run = 0.f;
 
-  // positions of this chunk's keys, staged once so that the gathers below
-  // do not wait on dependent index loads
-  if (!is_window) {
-    for (int i = tid; i < n_tiles * kKT; i += 256) {
-      const int kk = k_begin + i;
-      int pos = kk < k_end ? a.idx[(int64_t)r * a.K + kk] : -1;
+  // positions of this chunk's sparse keys, staged once so that the gathers
+  // below do not wait on dependent index loads
+  if (n_sp > 0) {
+    const int32_t* idx_row = a.idx + a.idx_off[layer] + (int64_t)r * a.K;
+    for (int i = tid; i < n_sp * kKT; i += 256) {
+      const int kk = k0 + i;
+      const int pos = kk < k1 ? idx_row[kk] : -1;
       s_pos[i] = (pos >= 0 && pos < a.T) ? pos : -1;
     }
     __syncthreads();
   }
 
-  // sparse chunks: gather the FP4 codes + scales of a tile's keys into a register
-  // buffer; two buffers alternate so that two tiles are in flight
-  auto load_tile = [&](RawTile& raw, int tile) {
-    if (is_window) return;
+  // gather the FP4 codes + scales of sparse tile j's keys into a register buffer
+  auto load_tile = [&](RawTile& raw, int j) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
-      const int pos = s_pos[tile * kKT + 16 * mt + m];
+      const int pos = s_pos[j * kKT + 16 * mt + m];
       const bool ok = pos >= 0;
       raw.valid[mt] = ok;
       if (ok) {
@@ -192,7 +224,8 @@ attn_chunk_kernel(const AttnArgs a) {
   float* spmine = sp + wave * NT * 16 * kSStride;
   const float neg_inf = -__builtin_inff();
 
-  auto process = [&](RawTile& raw, int tile) {
+  // one tile: the window tile (win) or sparse tile j, whose buffer is refilled with j + 2
+  auto process = [&](RawTile& raw, bool win, int j) {
     // ---- per 16-key half-tile: dequantise this wave's slice into A operands,
     //      store it key-major in LDS, and form the partial scores
     //      S^T[16mt + 4g + i][16nt + m] over the wave's 128 channels
@@ -200,7 +233,7 @@ attn_chunk_kernel(const AttnArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       f16x8 xa[4];
-      if (!is_window) {
+      if (!win) {
         const uint32_t cw[4] = {raw.v[mt].x, raw.v[mt].y, raw.v[mt].z, raw.v[mt].w};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -210,14 +243,10 @@ attn_chunk_kernel(const AttnArgs a) {
         }
         valid_mt[mt] = raw.valid[mt];
       } else {
-        // window rows: bf16 -> f16, loaded when needed (a window chunk has <= 4 tiles)
-        const int kk = k_begin + tile * kKT + 16 * mt + m;
-        const bool ok = kk < k_end;
-        valid_mt[mt] = ok;
-        const uint4* p = reinterpret_cast<const uint4*>(
-            a.swa + ((int64_t)seq * a.S + w_start + (ok ? kk : 0)) * kLatent + cbase + 32 * g);
+        // window rows: bf16 -> f16
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) xa[ks] = bf16x8_to_f16(ok ? p[ks] : make_uint4(0, 0, 0, 0));
+        for (int ks = 0; ks < 4; ++ks) xa[ks] = bf16x8_to_f16(wv[mt][ks]);
+        valid_mt[mt] = wvalid[mt];
       }
       f16x8* dst = reinterpret_cast<f16x8*>(xmine + (16 * mt + m) * kXwStride + 32 * g);
 #pragma unroll
@@ -232,7 +261,7 @@ attn_chunk_kernel(const AttnArgs a) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         *reinterpret_cast<f32x4*>(spmine + (16 * nt + m) * kSStride + 16 * mt + 4 * g) = sacc[nt];
-      if (mt == 1 && tile + 2 < n_tiles) load_tile(raw, tile + 2);   // buffer free: refill two tiles ahead
+      if (!win && mt == 1 && j + 2 < n_sp) load_tile(raw, j + 2);   // buffer free: refill two tiles ahead
     }
     if (wave == 0 && g == 0) {
       s_valid[m] = valid_mt[0];
@@ -244,20 +273,20 @@ attn_chunk_kernel(const AttnArgs a) {
     if (wave < NT) {
       float s[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s[j] = 0.f;
+      for (int q = 0; q < 8; ++q) s[q] = 0.f;
 #pragma unroll
       for (int w2 = 0; w2 < 4; ++w2) {
         const float* src = sp + w2 * NT * 16 * kSStride + (16 * wave + m) * kSStride + 8 * g;
         f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
         f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) { s[j] += v0[j]; s[4 + j] += v1[j]; }
+        for (int q = 0; q < 4; ++q) { s[q] += v0[q]; s[4 + q] += v1[q]; }
       }
       float mx = neg_inf;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        s[j] = s_valid[8 * g + j] ? s[j] * a.scale_log2 : neg_inf;
-        mx = fmaxf(mx, s[j]);
+      for (int q = 0; q < 8; ++q) {
+        s[q] = s_valid[8 * g + q] ? s[q] * a.scale_log2 : neg_inf;
+        mx = fmaxf(mx, s[q]);
       }
       mx = fmaxf(mx, shfl_xor_f(mx, 16));
       mx = fmaxf(mx, shfl_xor_f(mx, 32));
@@ -268,10 +297,10 @@ attn_chunk_kernel(const AttnArgs a) {
       float psum = 0.f;
       f16x8 ph;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float pj = live ? exp2f(s[j] - m_new) : 0.f;
+      for (int q = 0; q < 8; ++q) {
+        float pj = live ? exp2f(s[q] - m_new) : 0.f;
         psum += pj;
-        ph[j] = (_Float16)pj;
+        ph[q] = (_Float16)pj;
       }
       psum += shfl_xor_f(psum, 16);
       psum += shfl_xor_f(psum, 32);
@@ -313,15 +342,19 @@ attn_chunk_kernel(const AttnArgs a) {
   };
 
   RawTile buf0, buf1;
-  if (n_tiles > 0) load_tile(buf0, 0);
-  if (n_tiles > 1) load_tile(buf1, 1);
-  for (int tile = 0; tile < n_tiles; tile += 2) {
-    process(buf0, tile);
-    if (tile + 1 < n_tiles) process(buf1, tile + 1);
+  if (n_sp > 0) load_tile(buf0, 0);
+  if (n_sp > 1) load_tile(buf1, 1);
+  for (int i = 0; i < n_wt; ++i) {
+    if (i > 0) load_window(w0 + i);
+    process(buf0, true, -1);
+  }
+  for (int j = 0; j < n_sp; j += 2) {
+    process(buf0, false, j);
+    if (j + 1 < n_sp) process(buf1, false, j + 1);
   }
 
   // ---- this chunk's partial: unnormalised O, and (m, l) from the softmax owners
-  const int64_t prow = ((int64_t)r * a.n_chunks + chunk) * H + hbase;
+  const int64_t prow = (((int64_t)layer * a.R + r) * a.n_chunks + chunk) * H + hbase;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     float* op = a.o_part + (prow + 16 * nt + m) * kLatent + cbase + 4 * g;
@@ -362,15 +395,16 @@ __device__ __forceinline__ float block_sum_128(float v, float* red) {
 }
 
 __global__ void __launch_bounds__(kCombineThreads)
-attn_combine_kernel(const float* __restrict__ o_part, const float* __restrict__ ml_part, int n_chunks, int H,
+attn_combine_kernel(const float* __restrict__ o_part, const float* __restrict__ ml_part, int n_chunks, int R, int H,
                     const float* __restrict__ o_prev, const float* __restrict__ lse_prev,
                     float* __restrict__ o_out, float* __restrict__ lse_out) {
   __shared__ float s_w[kCombineThreads];
   __shared__ float red[2];
-  const int h = blockIdx.x, r = blockIdx.y;
+  const int h = blockIdx.x, r = blockIdx.y, layer = blockIdx.z;
   const int tid = threadIdx.x;
   const int c4 = tid * 4;
-  const int64_t base = ((int64_t)r * n_chunks) * H + h;       // + chunk * H
+  const int64_t base = (((int64_t)layer * R + r) * n_chunks) * H + h;       // + chunk * H
+  const int64_t orow = ((int64_t)layer * R + r) * H + h;                   // output (row, head) of this layer
   const float neg_inf = -__builtin_inff();
   float M = neg_inf;
   for (int c = tid; c < n_chunks; c += kCombineThreads) {
@@ -380,7 +414,7 @@ attn_combine_kernel(const float* __restrict__ o_part, const float* __restrict__ 
   M = block_max_128(M, red);
   float mp = neg_inf;
   if (lse_prev) {
-    mp = lse_prev[(int64_t)r * H + h] * kLog2e;
+    mp = lse_prev[orow] * kLog2e;
     M = fmaxf(M, mp);
   }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -417,42 +451,56 @@ attn_combine_kernel(const float* __restrict__ o_part, const float* __restrict__ 
   if (lse_prev && mp != neg_inf) {
     const float w = exp2f(mp - M);
     Lsum += w;
-    acc += *reinterpret_cast<const f32x4*>(o_prev + ((int64_t)r * H + h) * kLatent + c4) * w;
+    acc += *reinterpret_cast<const f32x4*>(o_prev + orow * kLatent + c4) * w;
   }
   const f32x4 res = Lsum > 0.f ? acc * (1.f / Lsum) : f32x4{0.f, 0.f, 0.f, 0.f};
   __syncthreads();                 // o_out / lse_out may alias o_prev / lse_prev
-  *reinterpret_cast<f32x4*>(o_out + ((int64_t)r * H + h) * kLatent + c4) = res;
-  if (lse_out && tid == 0) lse_out[(int64_t)r * H + h] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : neg_inf;
+  *reinterpret_cast<f32x4*>(o_out + orow * kLatent + c4) = res;
+  if (lse_out && tid == 0) lse_out[orow] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : neg_inf;
 }
 
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 struct Plan {
-  int tiles_per_chunk;
-  int n_sparse;
+  int n_sparse_tiles, n_window_tiles;
+  int sparse_per_chunk, window_per_chunk, n_chunks;
 };
 
 static int head_groups(int32_t H) { return H % 32 == 0 ? H / 32 : H / 16; }
 
-// About two workgroups per CU in total (two four-wave workgroups fit a CU), at
-// least 4 tiles per chunk so that the partial outputs stay small next to the
-// gathered rows.
-static Plan sparse_plan(int32_t R, int32_t H, int32_t K) {
-  int tiles = (K + kKT - 1) / kKT;
-  if (tiles < 1) tiles = 1;
-  const int64_t per_chunk = (int64_t)R * head_groups(H);
-  int want = (int)((512 + per_chunk - 1) / per_chunk);
-  int tpc = (tiles + want - 1) / want;
-  if (tpc < 4) tpc = 4;
-  if (tpc > kMaxChunkTiles) tpc = kMaxChunkTiles;
-  if (tpc > tiles) tpc = tiles;
-  return Plan{tpc, (tiles + tpc - 1) / tpc};
+constexpr int kTargetWorkgroups = 512;         // two four-wave workgroups per CU
+constexpr int kMinChunkTiles = 4;              // partial outputs stay small next to the gathered rows
+
+// Chunks per (layer, row): about kTargetWorkgroups workgroups in total, at least
+// kMinChunkTiles sparse tiles per chunk; the window tiles are spread one per
+// chunk where there are enough chunks.
+static Plan chunk_plan(int32_t L, int32_t R, int32_t H, int32_t K, bool sparse, bool window) {
+  Plan p;
+  p.n_sparse_tiles = sparse ? (K + kKT - 1) / kKT : 0;
+  p.n_window_tiles = window ? kWindowChunks : 0;
+  if (p.n_sparse_tiles == 0) {
+    p.sparse_per_chunk = 0;
+    p.n_chunks = p.n_window_tiles;
+    p.window_per_chunk = 1;
+    return p;
+  }
+  const int64_t per_chunk = (int64_t)L * R * head_groups(H);
+  const int64_t want = (kTargetWorkgroups + per_chunk - 1) / per_chunk;
+  int64_t spc = (p.n_sparse_tiles + want - 1) / want;
+  if (spc < kMinChunkTiles) spc = kMinChunkTiles;
+  if (spc > kMaxChunkTiles) spc = kMaxChunkTiles;
+  if (spc > p.n_sparse_tiles) spc = p.n_sparse_tiles;
+  p.sparse_per_chunk = (int)spc;
+  p.n_chunks = (int)((p.n_sparse_tiles + spc - 1) / spc);
+  p.window_per_chunk = p.n_window_tiles ? (p.n_window_tiles + p.n_chunks - 1) / p.n_chunks : 0;
+  return p;
 }
 
-static size_t partial_bytes(int32_t R, int32_t H, int n_chunks, size_t* off_ml) {
-  size_t o = align_up((size_t)R * n_chunks * H * kLatent * sizeof(float), 256);
-  size_t ml = align_up((size_t)R * n_chunks * H * 2 * sizeof(float), 256);
+static size_t partial_bytes(int32_t L, int32_t R, int32_t H, int n_chunks, size_t* off_ml) {
+  const size_t rows = (size_t)L * R * n_chunks * H;
+  size_t o = align_up(rows * kLatent * sizeof(float), 256);
+  size_t ml = align_up(rows * 2 * sizeof(float), 256);
   if (off_ml) *off_ml = o;
   return o + ml;
 }
@@ -463,47 +511,56 @@ static bool heads_ok(int32_t H) { return H == 16 || H == 32 || H == 48 || H == 6
 // one workgroup per group: the 32-head kernel fits two waves per SIMD and two
 // workgroups per CU, which hides barrier and memory latency better than one
 // 64-head workgroup; the price is dequantising each tile once per group.
-static void launch_chunks(const AttnArgs& a, int R, hipStream_t s) {
-  if (a.H % 32 == 0) {
-    attn_chunk_kernel<2><<<dim3(a.n_chunks, R, head_groups(a.H)), 256, 0, s>>>(a);
-  } else {
-    attn_chunk_kernel<1><<<dim3(a.n_chunks, R, head_groups(a.H)), 256, 0, s>>>(a);
-  }
+static void launch_chunks(const AttnArgs& a, hipStream_t s) {
+  const dim3 grid(a.n_chunks, a.R, a.head_groups * a.L);
+  if (a.H % 32 == 0) attn_chunk_kernel<2><<<grid, 256, 0, s>>>(a);
+  else attn_chunk_kernel<1><<<grid, 256, 0, s>>>(a);
 }
 
-// shared validation + launch of one attention call (sparse part, window part or both)
-static csa2_status attention_call(const uint16_t* q_lat, int32_t R, int32_t H, const uint8_t* codes,
+// shared launch of L layers of one attention form (sparse part, window part or both);
+// idx_off[l] is the element offset of layer l's index slice
+static csa2_status attention_call(int32_t L, const uint16_t* q_lat, int32_t R, int32_t H, const uint8_t* codes,
                                   const uint8_t* scales, int32_t B, int64_t T, const int32_t* row_seq,
-                                  const int32_t* idx, int32_t K, const uint16_t* swa, int32_t S,
-                                  const int32_t* swa_start, const int32_t* swa_len, float softmax_scale,
+                                  const int32_t* idx, const int64_t* idx_off, int32_t K, const uint16_t* swa,
+                                  int32_t S, const int32_t* swa_start, const int32_t* swa_len, float softmax_scale,
                                   const float* o_prev, const float* lse_prev, float* o, float* lse,
                                   void* workspace, size_t workspace_bytes, void* stream) {
-  Plan p = idx ? sparse_plan(R, H, K) : Plan{0, 0};
+  const Plan p = chunk_plan(L, R, H, K, idx != nullptr, swa != nullptr);
   AttnArgs a;
-  a.q_lat = q_lat; a.H = H; a.codes = codes; a.scales = scales; a.T = T; a.row_seq = row_seq;
-  a.idx = idx; a.K = K; a.n_sparse_chunks = p.n_sparse; a.tiles_per_chunk = p.tiles_per_chunk;
-  a.swa = swa; a.S = S; a.swa_start = swa_start; a.swa_len = swa_len;
-  a.n_chunks = p.n_sparse + (swa ? 1 : 0);
+  a.q_lat = q_lat; a.R = R; a.H = H; a.L = L; a.head_groups = head_groups(H);
+  a.codes = codes; a.scales = scales; a.T = T; a.row_seq = row_seq;
+  a.idx = idx; a.K = K;
+  for (int l = 0; l < kMaxLayers; ++l) a.idx_off[l] = (idx && l < L) ? idx_off[l] : 0;
+  a.n_sparse_tiles = p.n_sparse_tiles; a.n_window_tiles = p.n_window_tiles;
+  a.window_per_chunk = p.window_per_chunk; a.sparse_per_chunk = p.sparse_per_chunk; a.n_chunks = p.n_chunks;
+  a.swa = swa; a.B = B; a.S = S; a.swa_start = swa_start; a.swa_len = swa_len;
   a.scale_log2 = softmax_scale * kLog2e;
   size_t off_ml;
-  size_t need = partial_bytes(R, H, a.n_chunks, &off_ml);
+  const size_t need = partial_bytes(L, R, H, a.n_chunks, &off_ml);
   if (!workspace || workspace_bytes < need) return CSA2_EWORKSPACE;
   if (!aligned(workspace, 256)) return CSA2_EALIGN;
   a.o_part = static_cast<float*>(workspace);
   a.ml_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + off_ml);
   hipStream_t s = (hipStream_t)stream;
-  launch_chunks(a, R, s);
-  attn_combine_kernel<<<dim3(H, R), kCombineThreads, 0, s>>>(a.o_part, a.ml_part, a.n_chunks, H, o_prev, lse_prev, o, lse);
+  launch_chunks(a, s);
+  attn_combine_kernel<<<dim3(H, R, L), kCombineThreads, 0, s>>>(a.o_part, a.ml_part, a.n_chunks, R, H, o_prev,
+                                                                lse_prev, o, lse);
   return launch_status();
+}
+
+static size_t attention_workspace(int32_t L, int32_t R, int32_t H, int32_t K, bool sparse, bool window) {
+  return partial_bytes(L, R, H, chunk_plan(L, R, H, K, sparse, window).n_chunks, nullptr);
 }
 
 }  // namespace csa2
 
 using namespace csa2;
 
+static const int64_t kNoOffset[1] = {0};
+
 extern "C" size_t csa2_sparse_decode_workspace_size(int32_t R, int32_t H, int32_t K) {
   if (R <= 0 || H <= 0 || K <= 0) return 0;
-  return partial_bytes(R, H, sparse_plan(R, H, K).n_sparse, nullptr);
+  return attention_workspace(1, R, H, K, true, false);
 }
 
 extern "C" csa2_status csa2_sparse_decode(const uint16_t* q_lat, int32_t R, int32_t H, const uint8_t* codes,
@@ -518,13 +575,13 @@ extern "C" csa2_status csa2_sparse_decode(const uint16_t* q_lat, int32_t R, int3
   if (!aligned(q_lat, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(idx, 4) ||
       !aligned(o, 16) || !aligned(lse, 4))
     return CSA2_EALIGN;
-  return attention_call(q_lat, R, H, codes, scales, B, T, row_seq, idx, K, nullptr, 0, nullptr, nullptr,
-                        softmax_scale, nullptr, nullptr, o, lse, workspace, workspace_bytes, stream);
+  return attention_call(1, q_lat, R, H, codes, scales, B, T, row_seq, idx, kNoOffset, K, nullptr, 0, nullptr,
+                        nullptr, softmax_scale, nullptr, nullptr, o, lse, workspace, workspace_bytes, stream);
 }
 
 extern "C" size_t csa2_swa_merge_workspace_size(int32_t R, int32_t H) {
   if (R <= 0 || H <= 0) return 0;
-  return partial_bytes(R, H, 1, nullptr);
+  return attention_workspace(1, R, H, 0, false, true);
 }
 
 extern "C" csa2_status csa2_swa_merge(const uint16_t* q_lat, int32_t R, int32_t H, const uint16_t* swa, int32_t B,
@@ -539,13 +596,31 @@ extern "C" csa2_status csa2_swa_merge(const uint16_t* q_lat, int32_t R, int32_t 
   if (!heads_ok(H)) return CSA2_ESHAPE;
   if (!aligned(q_lat, 16) || !aligned(swa, 16) || !aligned(o_out, 16) || (o_sparse && !aligned(o_sparse, 16)))
     return CSA2_EALIGN;
-  return attention_call(q_lat, R, H, nullptr, nullptr, B, 0, row_seq, nullptr, 0, swa, S, swa_start, swa_len,
-                        softmax_scale, o_sparse, lse_sparse, o_out, lse_out, workspace, workspace_bytes, stream);
+  return attention_call(1, q_lat, R, H, nullptr, nullptr, B, 0, row_seq, nullptr, nullptr, 0, swa, S, swa_start,
+                        swa_len, softmax_scale, o_sparse, lse_sparse, o_out, lse_out, workspace, workspace_bytes,
+                        stream);
 }
 
 extern "C" size_t csa2_sparse_swa_decode_workspace_size(int32_t R, int32_t H, int32_t K) {
   if (R <= 0 || H <= 0 || K <= 0) return 0;
-  return partial_bytes(R, H, sparse_plan(R, H, K).n_sparse + 1, nullptr);
+  return attention_workspace(1, R, H, K, true, true);
+}
+
+static csa2_status check_sparse_swa(int32_t L, const uint16_t* q_lat, int32_t R, int32_t H, const uint8_t* codes,
+                                    const uint8_t* scales, int32_t B, int64_t T, const int32_t* row_seq,
+                                    const int32_t* idx, int32_t K, const uint16_t* swa, int32_t S,
+                                    const int32_t* swa_start, const int32_t* swa_len, const float* o,
+                                    const float* lse) {
+  if (!q_lat || !codes || !scales || !idx || !swa || !swa_start || !swa_len || !o || !lse) return CSA2_EINVAL;
+  if (L <= 0 || R <= 0 || B <= 0 || T <= 0 || K <= 0 || S <= 0) return CSA2_EINVAL;
+  if (L > kMaxLayers) return CSA2_ESHAPE;
+  if (!row_seq && R != B) return CSA2_EINVAL;
+  if (!heads_ok(H)) return CSA2_ESHAPE;
+  if (T >= (int64_t(1) << 31)) return CSA2_ESHAPE;
+  if (!aligned(q_lat, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(idx, 4) || !aligned(swa, 16) ||
+      !aligned(o, 16) || !aligned(lse, 4))
+    return CSA2_EALIGN;
+  return CSA2_OK;
 }
 
 extern "C" csa2_status csa2_sparse_swa_decode(const uint16_t* q_lat, int32_t R, int32_t H, const uint8_t* codes,
@@ -554,14 +629,34 @@ extern "C" csa2_status csa2_sparse_swa_decode(const uint16_t* q_lat, int32_t R, 
                                               const int32_t* swa_start, const int32_t* swa_len,
                                               float softmax_scale, float* o, float* lse, void* workspace,
                                               size_t workspace_bytes, void* stream) {
-  if (!q_lat || !codes || !scales || !idx || !swa || !swa_start || !swa_len || !o || !lse) return CSA2_EINVAL;
-  if (R <= 0 || B <= 0 || T <= 0 || K <= 0 || S <= 0) return CSA2_EINVAL;
-  if (!row_seq && R != B) return CSA2_EINVAL;
-  if (!heads_ok(H)) return CSA2_ESHAPE;
-  if (T >= (int64_t(1) << 31)) return CSA2_ESHAPE;
-  if (!aligned(q_lat, 16) || !aligned(codes, 16) || !aligned(scales, 4) || !aligned(idx, 4) || !aligned(swa, 16) ||
-      !aligned(o, 16) || !aligned(lse, 4))
-    return CSA2_EALIGN;
-  return attention_call(q_lat, R, H, codes, scales, B, T, row_seq, idx, K, swa, S, swa_start, swa_len,
+  const csa2_status st = check_sparse_swa(1, q_lat, R, H, codes, scales, B, T, row_seq, idx, K, swa, S, swa_start,
+                                          swa_len, o, lse);
+  if (st != CSA2_OK) return st;
+  return attention_call(1, q_lat, R, H, codes, scales, B, T, row_seq, idx, kNoOffset, K, swa, S, swa_start, swa_len,
+                        softmax_scale, nullptr, nullptr, o, lse, workspace, workspace_bytes, stream);
+}
+
+extern "C" size_t csa2_sparse_swa_decode_layers_workspace_size(int32_t L, int32_t R, int32_t H, int32_t K) {
+  if (L <= 0 || L > kMaxLayers || R <= 0 || H <= 0 || K <= 0) return 0;
+  return attention_workspace(L, R, H, K, true, true);
+}
+
+extern "C" csa2_status csa2_sparse_swa_decode_layers(int32_t L, const uint16_t* q_lat, int32_t R, int32_t H,
+                                                     const uint8_t* codes, const uint8_t* scales, int32_t B,
+                                                     int64_t T, const int32_t* row_seq, const int32_t* idx,
+                                                     const int32_t* layer_idx, int32_t K, const uint16_t* swa,
+                                                     int32_t S, const int32_t* swa_start, const int32_t* swa_len,
+                                                     float softmax_scale, float* o, float* lse, void* workspace,
+                                                     size_t workspace_bytes, void* stream) {
+  const csa2_status st = check_sparse_swa(L, q_lat, R, H, codes, scales, B, T, row_seq, idx, K, swa, S, swa_start,
+                                          swa_len, o, lse);
+  if (st != CSA2_OK) return st;
+  if (!layer_idx) return CSA2_EINVAL;
+  int64_t off[kMaxLayers];
+  for (int l = 0; l < L; ++l) {
+    if (layer_idx[l] < 0) return CSA2_EINVAL;
+    off[l] = (int64_t)layer_idx[l] * R * K;
+  }
+  return attention_call(L, q_lat, R, H, codes, scales, B, T, row_seq, idx, off, K, swa, S, swa_start, swa_len,
                         softmax_scale, nullptr, nullptr, o, lse, workspace, workspace_bytes, stream);
 }

@@ -12,12 +12,13 @@ This module only allocates buffers and sequences the C calls on one stream;
 every arithmetic step runs in the HIP kernels of libcsa2.
 """
 from dataclasses import dataclass
-from typing import List, Optional, Sequence
+from typing import Optional, Sequence
 
 import torch
 
 from . import (csa2_fp4_pack, csa2_index_full, csa2_index_reindex, csa2_topk, csa2_topk_workspace_size,
-               csa2_topk_pool, csa2_topk_pool_workspace_size,
+               csa2_topk_pool, csa2_topk_pool_workspace_size, csa2_sparse_swa_decode_layers,
+               csa2_sparse_swa_decode_layers_workspace_size,
                csa2_sparse_decode, csa2_sparse_decode_workspace_size, csa2_swa_merge,
                csa2_swa_merge_workspace_size, csa2_sparse_swa_decode, csa2_sparse_swa_decode_workspace_size)
 
@@ -49,6 +50,23 @@ class LayerIO:
     swa: torch.Tensor            # bf16 [B, S, 512]
     swa_start: torch.Tensor      # int32 [B]
     swa_len: torch.Tensor        # int32 [B]
+
+
+class StackIO:
+    """The per-layer inputs of all L layers in stacked tensors (layer-major):
+    q_lat bf16 [L, B, H, 512], q_idx uint8 [L, B, 64], swa bf16 [L, B, S, 512],
+    swa_start / swa_len int32 [L, B].  With stacked inputs every layer's
+    attention runs in one launch; .layers gives per-layer views."""
+
+    def __init__(self, q_lat, q_idx, swa, swa_start, swa_len):
+        self.q_lat, self.q_idx, self.swa, self.swa_start, self.swa_len = q_lat, q_idx, swa, swa_start, swa_len
+        self.layers = [LayerIO(q_lat[l], q_idx[l], swa[l], swa_start[l], swa_len[l]) for l in range(q_lat.shape[0])]
+
+    def __len__(self):
+        return len(self.layers)
+
+    def __getitem__(self, l):
+        return self.layers[l]
 
 
 class Csa2DecodeStack:
@@ -86,20 +104,26 @@ class Csa2DecodeStack:
         self.ws_swa = torch.empty(csa2_swa_merge_workspace_size(B, H), dtype=u8, device=dev)
         self.fused_attention = fused_attention
         self.ws_fused = torch.empty(csa2_sparse_swa_decode_workspace_size(B, H, K), dtype=u8, device=dev)
+        self.ws_layers = torch.empty(csa2_sparse_swa_decode_layers_workspace_size(self.L, B, H, K), dtype=u8,
+                                     device=dev)
         self.index_events = None
 
-    def step(self, codes, scales, k_idx, layers: List[LayerIO], sigma: float, new_rows: Optional[torch.Tensor] = None,
+    def step(self, codes, scales, k_idx, layers, sigma: float, new_rows: Optional[torch.Tensor] = None,
              stream=None, time_index: bool = False):
-        """Run every layer once.  new_rows (bf16 [B, 512]), if given, is packed
-        into position T-1 of each sequence first (the current token).
+        """Run every layer once.  layers: a StackIO (all layers' attention in one
+        launch, after the selections) or a list of LayerIO (one attention call
+        per layer).  new_rows (bf16 [B, 512]), if given, is packed into position
+        T-1 of each sequence first (the current token).
 
         time_index: record HIP events around the Full-layer index call on the
         stream (self.index_events holds the (start, end) pair)."""
         B, T, K = self.B, self.T, self.K
+        stacked = layers if isinstance(layers, StackIO) else None
+        ios = layers.layers if stacked is not None else list(layers)
         if new_rows is not None:
             csa2_fp4_pack(new_rows, codes[:, T - 1, :], scales[:, T - 1, :], stream=stream)
-        prev_idx = None
-        for li, (mode, io) in enumerate(zip(self.modes, layers)):
+        src = []                       # index slice used by each layer
+        for li, (mode, io) in enumerate(zip(self.modes, ios)):
             idx = self.idx[li]
             if mode == "full":
                 if time_index:
@@ -120,17 +144,24 @@ class Csa2DecodeStack:
                     csa2_topk(self.scores, K, idx, workspace=self.ws_topk_full, stream=stream)
                 else:
                     csa2_topk(self.scores, K, idx, workspace=self.ws_topk_full, stream=stream)
-                prev_idx = idx
+                src.append(li)
             elif mode == "reindex":
                 csa2_index_reindex(io.q_idx, k_idx, self.pool, self.re_scores, stream=stream)
                 csa2_topk(self.re_scores, K, idx, index_map=self.pool, workspace=self.ws_topk_pool, stream=stream)
-                prev_idx = idx
+                src.append(li)
             elif mode == "reuse":
-                if prev_idx is None:
+                if not src:
                     raise ValueError("a Reuse layer needs a preceding Full or Reindex layer")
-                idx = prev_idx
+                src.append(src[-1])
             else:
                 raise ValueError(mode)
+        if stacked is not None and self.fused_attention:
+            csa2_sparse_swa_decode_layers(stacked.q_lat, codes, scales, self.idx, src, stacked.swa, stacked.swa_start,
+                                          stacked.swa_len, sigma, self.o, self.lse, workspace=self.ws_layers,
+                                          stream=stream)
+            return self.o, self.lse
+        for li, io in enumerate(ios):
+            idx = self.idx[src[li]]
             if self.fused_attention:
                 csa2_sparse_swa_decode(io.q_lat, codes, scales, idx, io.swa, io.swa_start, io.swa_len, sigma,
                                        self.o[li], self.lse[li], workspace=self.ws_fused, stream=stream)

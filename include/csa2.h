@@ -248,7 +248,7 @@ csa2_status csa2_swa_merge(const uint16_t* q_lat, int32_t R, int32_t H,
  * Sparse attention and window merge in one call: the result equals
  * csa2_sparse_decode followed by csa2_swa_merge with that sparse result (one
  * softmax over the union of the selected cache rows and the window rows), but
- * the window rows are processed as one more key chunk of the same launch and a
+ * the window rows are processed as more key tiles of the same launch and a
  * single combine step produces o and lse (two launches instead of four).
  *
  * Arguments as in csa2_sparse_decode and csa2_swa_merge; o fp32 [R][H][512],
@@ -263,6 +263,33 @@ csa2_status csa2_sparse_swa_decode(const uint16_t* q_lat, int32_t R, int32_t H,
                                    const uint16_t* swa, int32_t S, const int32_t* swa_start,
                                    const int32_t* swa_len, float softmax_scale, float* o, float* lse,
                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Several layers' csa2_sparse_swa_decode in one launch (HN summary key points:
+ * the CSA2 layers reuse one main KV and share Top-K indices across layers;
+ * MarkTechPost retelling, paragraph 3: Reuse layers take the previous layer's
+ * indices unchanged).  Layer l computes exactly what csa2_sparse_swa_decode
+ * computes with its own queries, window and outputs and the index slice
+ * idx[layer_idx[l]]; layers that share a slice gather the same cache rows.
+ *
+ *   L          1 .. 8 layers
+ *   q_lat      bf16 [L][R][H][512]
+ *   idx        int32 [n][R][K], n > max(layer_idx)
+ *   layer_idx  int32 [L], HOST memory: the idx slice of each layer (>= 0)
+ *   swa        bf16 [L][B][S][512];  swa_start, swa_len int32 [L][R]
+ *   o          fp32 [L][R][H][512];  lse fp32 [L][R][H]
+ *   workspace  >= csa2_sparse_swa_decode_layers_workspace_size(L, R, H, K) bytes
+ * Other arguments as in csa2_sparse_swa_decode.
+ * Errors: EINVAL (also a negative layer_idx entry), ESHAPE (H, L > 8),
+ * EWORKSPACE, EALIGN.
+ * ------------------------------------------------------------------------- */
+size_t csa2_sparse_swa_decode_layers_workspace_size(int32_t L, int32_t R, int32_t H, int32_t K);
+csa2_status csa2_sparse_swa_decode_layers(int32_t L, const uint16_t* q_lat, int32_t R, int32_t H,
+                                          const uint8_t* codes, const uint8_t* scales, int32_t B, int64_t T,
+                                          const int32_t* row_seq, const int32_t* idx, const int32_t* layer_idx,
+                                          int32_t K, const uint16_t* swa, int32_t S, const int32_t* swa_start,
+                                          const int32_t* swa_len, float softmax_scale, float* o, float* lse,
+                                          void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import workloads as W
-from fp4_sparse_attention_amd.decode import LayerIO, pack_cache
+from fp4_sparse_attention_amd.decode import LayerIO, StackIO, pack_cache
 
 ATTN_RTOL = 2e-3
 LSE_TOL = 1e-4
@@ -87,13 +87,13 @@ class DecodeWorkload:
         pack_cache(self.codes, self.scales, self.latent_chunk, self.chunk_rows)
         self.k_idx = torch.stack([W.fp8_normal(seed, (T, 64), device=self.dev, chunk_index=b) for b in range(B)])
         S = window
-        self.layers = []
-        for li in range(n_layers):
-            d = W.decode_layer_inputs(seed, li, B, H, S, B, device=self.dev, outliers=self.outliers)
-            ln = min(window, T)
-            self.layers.append(LayerIO(d["q_lat"], d["q_idx"], d["swa"],
-                                       torch.zeros(B, dtype=torch.int32, device=self.dev),
-                                       torch.full((B,), ln, dtype=torch.int32, device=self.dev)))
+        ds = [W.decode_layer_inputs(seed, li, B, H, S, B, device=self.dev, outliers=self.outliers)
+              for li in range(n_layers)]
+        ln = min(window, T)
+        self.layers = [] if n_layers == 0 else StackIO(torch.stack([d["q_lat"] for d in ds]), torch.stack([d["q_idx"] for d in ds]),
+                              torch.stack([d["swa"] for d in ds]),
+                              torch.zeros((n_layers, B), dtype=torch.int32, device=self.dev),
+                              torch.full((n_layers, B), ln, dtype=torch.int32, device=self.dev))
         torch.cuda.synchronize()
 
     def latent_chunk(self, b, c):

@@ -89,7 +89,10 @@ def test_attention_argument_errors_and_workspace():
     L = F.lib()
     assert F.csa2_sparse_decode_workspace_size(64, 64, 2048) > 64 * 64 * 512 * 4
     assert F.csa2_swa_merge_workspace_size(8, 64) >= 8 * 64 * 512 * 4
-    assert F.csa2_sparse_swa_decode_workspace_size(8, 64, 2048) > F.csa2_sparse_decode_workspace_size(8, 64, 2048)
+    assert F.csa2_sparse_swa_decode_workspace_size(8, 64, 2048) >= F.csa2_sparse_decode_workspace_size(8, 64, 2048)
+    assert F.csa2_sparse_swa_decode_layers_workspace_size(4, 8, 64, 2048) >= \
+        4 * F.csa2_sparse_swa_decode_workspace_size(8, 64, 2048) // 2
+    assert F.csa2_sparse_swa_decode_layers_workspace_size(9, 8, 64, 2048) == 0
     args = [DUMMY, 1, 64, DUMMY, DUMMY, 1, 4096, NULL, DUMMY, 256, 0.1, DUMMY, DUMMY, DUMMY, 1 << 30, NULL]
     bad_h = list(args); bad_h[2] = 20
     assert L.csa2_sparse_decode(*bad_h) == 2
@@ -113,3 +116,21 @@ def test_no_cpu_fallback_in_binding():
     x = torch.zeros((4, 512), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         F.csa2_fp4_pack(x, torch.zeros((4, 256), dtype=torch.uint8), torch.zeros((4, 32), dtype=torch.uint8))
+
+
+def test_layers_call_argument_errors():
+    L = F.lib()
+    good = (ctypes.c_int32 * 4)(0, 1, 1, 1)
+    bad = (ctypes.c_int32 * 4)(0, -1, 1, 1)
+    args = [4, DUMMY, 8, 64, DUMMY, DUMMY, 8, 1 << 20, NULL, DUMMY, ctypes.cast(good, ctypes.c_void_p), 2048, DUMMY, 128,
+            DUMMY, DUMMY, 0.1, DUMMY, DUMMY, DUMMY, 1 << 30, NULL]
+    a = list(args); a[10] = ctypes.cast(bad, ctypes.c_void_p)
+    assert L.csa2_sparse_swa_decode_layers(*a) == 1          # negative layer_idx entry
+    a = list(args); a[10] = NULL
+    assert L.csa2_sparse_swa_decode_layers(*a) == 1          # no layer_idx
+    a = list(args); a[0] = 9
+    assert L.csa2_sparse_swa_decode_layers(*a) == 2          # more than 8 layers
+    a = list(args); a[3] = 20
+    assert L.csa2_sparse_swa_decode_layers(*a) == 2          # H = 20
+    a = list(args); a[20] = 100
+    assert L.csa2_sparse_swa_decode_layers(*a) == 4          # workspace too small

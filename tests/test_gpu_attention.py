@@ -177,3 +177,63 @@ def test_fused_sparse_window_vs_oracle(B, T, H, K):
         o_w, l_w = OA.attend(qf[b], OA.window_rows(swf[b], int(start[b]), int(length[b])), SIGMA)
         o_ref, l_ref = OA.merge(o_s, l_s, o_w, l_w)
         assert_attention_close(o[b].cpu().numpy(), lse[b].cpu().numpy(), o_ref, l_ref, f"row {b}")
+
+
+def test_layers_call_matches_oracle_per_layer():
+    """csa2_sparse_swa_decode_layers: each layer = sparse attention over its idx
+    slice plus its own window, one softmax; layers 1 and 2 share slice 1."""
+    dev = device()
+    L, B, T, H, K, S = 3, 3, 2500, 64, 300, 140
+    rng = np.random.default_rng(41)
+    lat, ref_rows = _cache(B, T, seed=43)
+    codes, scales = _gpu_cache(lat, dev)
+    q = W.bf16_normal(44, (L, B, H, 512), std=0.5)
+    swa = W.bf16_normal(45, (L, B, S, 512))
+    start = np.array([[12, 0, 3], [0, 5, 7], [2, 0, 11]], dtype=np.int32)
+    length = np.array([[128, 0, 57], [1, 128, 33], [77, 128, 0]], dtype=np.int32)
+    idx = np.full((2, B, K), -1, dtype=np.int32)
+    for sl in range(2):
+        for b in range(B):
+            n = K - 7 * b - sl
+            idx[sl, b, :n] = np.sort(rng.choice(T, n, replace=False))
+    layer_idx = [0, 1, 1]
+    o = torch.empty((L, B, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((L, B, H), dtype=torch.float32, device=dev)
+    F.csa2_sparse_swa_decode_layers(q.to(dev), codes, scales, torch.from_numpy(idx).to(dev), layer_idx, swa.to(dev),
+                                    torch.from_numpy(start).to(dev), torch.from_numpy(length).to(dev), SIGMA, o, lse)
+    qf = q.to(torch.float64).numpy()
+    swf = swa.to(torch.float64).numpy()
+    for l in range(L):
+        for b in range(B):
+            o_s, l_s = OA.sparse_attend(qf[l, b], ref_rows[b], idx[layer_idx[l], b], SIGMA)
+            o_w, l_w = OA.attend(qf[l, b], OA.window_rows(swf[l, b], int(start[l, b]), int(length[l, b])), SIGMA)
+            o_ref, l_ref = OA.merge(o_s, l_s, o_w, l_w)
+            assert_attention_close(o[l, b].cpu().numpy(), lse[l, b].cpu().numpy(), o_ref, l_ref, f"layer {l} row {b}")
+
+
+def test_layers_call_equals_single_layer_calls():
+    # the multi-layer launch and per-layer csa2_sparse_swa_decode give the same bits
+    dev = device()
+    L, B, T, H, K, S = 4, 8, 4096, 64, 2048, 128
+    lat, _ = _cache(B, T, seed=47)
+    codes, scales = _gpu_cache(lat, dev)
+    q = W.bf16_normal(48, (L, B, H, 512), std=0.5).to(dev)
+    swa = W.bf16_normal(49, (L, B, S, 512)).to(dev)
+    st = torch.zeros((L, B), dtype=torch.int32, device=dev)
+    ln = torch.full((L, B), 128, dtype=torch.int32, device=dev)
+    g = torch.Generator(device=dev).manual_seed(50)
+    idx = torch.sort(torch.randperm(T, device=dev, generator=g)[:K].repeat(2, B, 1).to(torch.int32), dim=2).values
+    layer_idx = [0, 1, 1, 1]
+    o = torch.empty((L, B, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((L, B, H), dtype=torch.float32, device=dev)
+    F.csa2_sparse_swa_decode_layers(q, codes, scales, idx, layer_idx, swa, st, ln, SIGMA, o, lse)
+    for l in range(L):
+        o1 = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
+        l1 = torch.empty((B, H), dtype=torch.float32, device=dev)
+        F.csa2_sparse_swa_decode(q[l].contiguous(), codes, scales, idx[layer_idx[l]].contiguous(), swa[l].contiguous(),
+                                 st[l].contiguous(), ln[l].contiguous(), SIGMA, o1, l1)
+        # chunking differs between the two launches: compare to the attention tolerance
+        ref_o = o1.cpu().numpy().astype(np.float64)
+        ref_l = l1.cpu().numpy().astype(np.float64)
+        for b in range(B):
+            assert_attention_close(o[l, b].cpu().numpy(), lse[l, b].cpu().numpy(), ref_o[b], ref_l[b], f"layer {l} b {b}")

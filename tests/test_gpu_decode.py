@@ -92,7 +92,8 @@ def test_tiny_full_decode_whole_chain():
     cfg = W.TinyDecode()
     wl = DecodeWorkload(cfg.batch, cfg.context, cfg.heads, 1, cfg.seed)
     stack = Csa2DecodeStack(cfg.batch, cfg.context, cfg.heads, cfg.topk, cfg.modes)
-    stack.step(wl.codes, wl.scales, wl.k_idx, wl.layers, SIGMA)
+    # a list of per-layer inputs: one attention call per layer
+    stack.step(wl.codes, wl.scales, wl.k_idx, wl.layers.layers, SIGMA)
     torch.cuda.synchronize()
     # oracle over the whole context through its own pipeline
     lat = wl.latent_host(0, np.arange(cfg.context))
