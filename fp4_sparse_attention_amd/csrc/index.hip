@@ -23,6 +23,8 @@
 // Decode (one query per sequence) is HBM-bound: 64 bytes of key per score; the
 // matrix cores and the conversions use a small share of their peak.  Chunked
 // prefill fills all 32 rows of A and is bound by the fp32 score writes.
+#include <algorithm>
+
 #include "common.hpp"
 
 namespace csa2 {
@@ -120,6 +122,78 @@ index_rows_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__
   }
 }
 
+// Full-mode decode scan as a persistent kernel: the grid holds as many
+// workgroups as the chip keeps resident, and each loops over units of 16
+// consecutive tiles (512 positions) of one row, unit u = (row u / units_per_row,
+// tiles 16 (u % units_per_row) + 4i + wave for i < 4).  The next unit's keys are
+// loaded before the current unit's products, so every wave keeps 8 KB in flight.
+constexpr int kUnitTiles = 16;
+
+__global__ void __launch_bounds__(256)
+index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx, int64_t T,
+                    const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit,
+                    float* __restrict__ scores, int64_t units_per_row, int64_t n_units) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int half = lane >> 5;
+  const int col_in_tile = lane & 31;
+  const float neg_inf = -__builtin_inff();
+
+  struct Unit {
+    i32x8 b[kUnroll];
+    bool ok[kUnroll];
+  };
+  auto fetch = [&](int64_t u, Unit& x) {
+    const int64_t r = u / units_per_row;
+    const int64_t t0 = (u % units_per_row) * kUnitTiles + wave;
+    const int seq = row_seq ? row_seq[r] : (int)r;
+    const int64_t limit = row_limit ? row_limit[r] : T - 1;
+    const uint8_t* kseq = k_idx + (int64_t)seq * T * kIndexDim;
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      const int64_t p = (t0 + 4 * i) * kTile + col_in_tile;
+      x.ok[i] = p < T && p <= limit;
+      x.b[i] = x.ok[i] ? load_half_key(kseq + p * kIndexDim + 32 * half) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  };
+  auto query = [&](int64_t u, f16x8* a) {
+    const int64_t r = u / units_per_row;
+    i32x8 araw = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (col_in_tile == 0) {
+      const uint4* q = reinterpret_cast<const uint4*>(q_idx + r * kIndexDim + 32 * half);
+      const uint4 x = q[0], y = q[1];
+      araw[0] = x.x; araw[1] = x.y; araw[2] = x.z; araw[3] = x.w;
+      araw[4] = y.x; araw[5] = y.y; araw[6] = y.z; araw[7] = y.w;
+    }
+    fp8x32_to_f16(araw, a);
+  };
+
+  int64_t u = blockIdx.x;
+  if (u >= n_units) return;
+  Unit cur, nxt;
+  fetch(u, cur);
+  int64_t row = -1;
+  f16x8 a[4];
+  for (; u < n_units; u += gridDim.x) {
+    const int64_t un = u + gridDim.x;
+    if (un < n_units) fetch(un, nxt);
+    const int64_t r = u / units_per_row;
+    if (r != row) {
+      query(u, a);
+      row = r;
+    }
+    const int64_t t0 = (u % units_per_row) * kUnitTiles + wave;
+    float* out = scores + r * T;
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      const f32x16 acc = mfma_score(a, cur.b[i]);
+      const int64_t p = (t0 + 4 * i) * kTile + col_in_tile;
+      if (half == 0 && p < T) out[p] = cur.ok[i] ? acc[0] : neg_inf;
+    }
+    cur = nxt;
+  }
+}
+
 // Up to 32 query rows per workgroup (grid.y = ceil(R/32)): chunked prefill.
 // Rows of one workgroup that share a sequence are scored together; a
 // workgroup whose rows span several sequences handles one sequence at a time.
@@ -205,6 +279,22 @@ index_block_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict_
   }
 }
 
+// workgroups of index_stream_kernel the device keeps resident at once
+static int64_t resident_blocks() {
+  static int64_t cached = 0;
+  if (cached == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+        hipSuccess)
+      cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(index_stream_kernel), 256,
+                                                      0) != hipSuccess || per_cu < 1)
+      per_cu = 4;
+    cached = (int64_t)cus * per_cu;
+  }
+  return cached;
+}
+
 static int tiles_per_block_for(int64_t n_tiles, int64_t rows) {
   // aim for >= ~2048 workgroups in total, at least 16 tiles (2 KB/wave-tile) each
   int64_t want_blocks_per_row = (2048 + rows - 1) / rows;
@@ -233,9 +323,11 @@ extern "C" csa2_status csa2_index_full(const uint8_t* q_idx, const uint8_t* k_id
     dim3 grid(ceil_div(n_tiles, tpb), ceil_div(R, 32));
     index_block_kernel<<<grid, 256, 0, s>>>(q_idx, k_idx, R, T, row_seq, row_limit, scores, tpb);
   } else {
-    int tpb = tiles_per_block_for(n_tiles, R);
-    dim3 grid(ceil_div(n_tiles, tpb), R);
-    index_rows_kernel<false><<<grid, 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, nullptr, T, scores, tpb);
+    const int64_t units_per_row = (n_tiles + kUnitTiles - 1) / kUnitTiles;
+    const int64_t n_units = units_per_row * R;
+    const int64_t grid = std::min<int64_t>(n_units, resident_blocks());
+    index_stream_kernel<<<(int)grid, 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, scores, units_per_row,
+                                                  n_units);
   }
   return launch_status();
 }

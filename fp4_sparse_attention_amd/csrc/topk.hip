@@ -697,15 +697,16 @@ topk_compact_kernel(const float* __restrict__ scores, int64_t N, int64_t stride,
   const int64_t s1 = min(N, s0 + seg);
   uint32_t* okey = seg_key + (int64_t)r * N + s0;
   int32_t* opos = seg_pos + (int64_t)r * N + s0;
-  auto load32 = [&](int64_t i0, uint32_t* keys, int32_t* pos) {
+  // thread t takes 32 consecutive slots of each 8192-slot block; positions are
+  // recomputed (or read from the map) only for the candidates
+  auto load32 = [&](int64_t i0, uint32_t* keys) {
     float4 v[8];
     int4 mp[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int64_t i = i0 + 4 * q;
       v[q] = i < s1 ? *reinterpret_cast<const float4*>(row + i) : make_float4(0.f, 0.f, 0.f, 0.f);
-      mp[q] = (map_row && i < s1) ? *reinterpret_cast<const int4*>(map_row + i)
-                                  : make_int4((int)i, (int)i + 1, (int)i + 2, (int)i + 3);
+      mp[q] = (map_row && i < s1) ? *reinterpret_cast<const int4*>(map_row + i) : make_int4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
@@ -713,36 +714,30 @@ topk_compact_kernel(const float* __restrict__ scores, int64_t N, int64_t stride,
       const float f[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
       const int32_t m4[4] = {mp[q].x, mp[q].y, mp[q].z, mp[q].w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        keys[4 * q + j] = (!in || m4[j] < 0) ? 0u : score_key(f[j]);
-        pos[4 * q + j] = m4[j];
-      }
+      for (int j = 0; j < 4; ++j) keys[4 * q + j] = (!in || m4[j] < 0) ? 0u : score_key(f[j]);
     }
   };
   uint32_t keys[32];
-  int32_t pos[32];
-  load32(s0 + (int64_t)threadIdx.x * 32, keys, pos);      // in flight while b0 is derived
+  load32(s0 + (int64_t)threadIdx.x * 32, keys);      // in flight while b0 is derived
   uint32_t b0, k_eff;
   derive_b0(hist0 + (int64_t)r * kTopBins, k, tmp, b0, k_eff);
   uint32_t running = 0;
   if (k_eff > 0) {
     for (int64_t blk = s0; blk < s1; blk += kCompactBlock) {
       const int64_t i0 = blk + (int64_t)threadIdx.x * 32;
-      if (blk != s0) load32(i0, keys, pos);
-      uint32_t n = 0;
+      if (blk != s0) load32(i0, keys);
+      uint32_t sel = 0;                       // bit j: slot i0 + j is a candidate
 #pragma unroll
-      for (int j = 0; j < 32; ++j) n += keys[j] != 0u && (keys[j] >> kTopShift) >= b0;
+      for (int j = 0; j < 32; ++j) sel |= (keys[j] != 0u && (keys[j] >> kTopShift) >= b0) ? (1u << j) : 0u;
       uint32_t total;
-      uint32_t p = running + block_exclusive_scan(n, tmp, total);
-      if (n) {
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-          if (keys[j] != 0u && (keys[j] >> kTopShift) >= b0) {
-            okey[p] = keys[j];
-            opos[p] = pos[j];
-            ++p;
-          }
-        }
+      uint32_t p = running + block_exclusive_scan((uint32_t)__popc(sel), tmp, total);
+      while (sel) {
+        const int j = __builtin_ctz(sel);
+        sel &= sel - 1u;
+        const int64_t i = i0 + j;
+        okey[p] = keys[j];
+        opos[p] = map_row ? map_row[i] : (int32_t)i;
+        ++p;
       }
       running += total;
     }
