@@ -239,7 +239,7 @@ def bench_decode(args, cfg):
                    "layers": list(cfg.modes), "pool": P, "window": cfg.window, "latent_channels": 512},
         "achieved_hbm_gbps": step_bytes / (ms * 1e-3) / 1e9,
         "step_algorithmic_bytes": step_bytes,
-        "roofline": {"kernel": "csa2_index_full (index_stream_kernel)", "bound": "hbm", "achieved": achieved,
+        "roofline": {"kernel": "csa2_index_full_pool scan (index_stream_kernel<true>)", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic("index_full", digest),
                      "launch_ms": idx_ms, "bytes_per_launch": idx_bytes},

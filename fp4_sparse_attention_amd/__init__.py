@@ -36,6 +36,10 @@ _SIGS = {
     "csa2_topk_pool_workspace_size": (_size_t, [_i32, _i64, _i32]),
     "csa2_topk_pool": (_i32, [_c_void_p, _i32, _i64, _i64, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                               _c_void_p, _size_t, _c_void_p]),
+    "csa2_index_full_pool_workspace_size": (_size_t, [_i32, _i64, _i32]),
+    "csa2_index_full_pool": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i64, _c_void_p, _c_void_p, _c_void_p, _i32,
+                                    _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t, _c_void_p, _c_void_p,
+                                    _c_void_p]),
     "csa2_sparse_decode_workspace_size": (_size_t, [_i32, _i32, _i32]),
     "csa2_sparse_decode": (_i32, [_c_void_p, _i32, _i32, _c_void_p, _c_void_p, _i32, _i64, _c_void_p, _c_void_p,
                                   _i32, _f32, _c_void_p, _c_void_p, _c_void_p, _size_t, _c_void_p]),
@@ -394,3 +398,49 @@ def csa2_sparse_swa_decode_layers(q_lat, codes, scales, idx, layer_idx, swa, swa
                                              _p(swa_len), float(softmax_scale), _p(o), _p(lse), _p(workspace),
                                              workspace.numel(), _stream(stream))
     _check("csa2_sparse_swa_decode_layers", st)
+
+
+def csa2_index_full_pool_workspace_size(R, T, k_pool):
+    return int(lib().csa2_index_full_pool_workspace_size(R, T, k_pool))
+
+
+def csa2_index_full_pool(q_idx, k_idx, scores, k_pool, k_top, pool_idx, top_idx, pool_scores=None, row_seq=None,
+                         row_limit=None, workspace=None, scan_events=None, stream=None):
+    """Full-mode scores and the pool / Top-K selection in one call: q_idx uint8 [R, 64]; k_idx uint8 [B, T, 64];
+    scores fp32 [R, T] (written); pool_idx int32 [R, k_pool]; top_idx int32 [R, k_top];
+    pool_scores fp32 [R, k_pool] or None.  scan_events: an optional (start, end) pair of already-created
+    torch.cuda.Event objects, recorded by the library around the scoring kernel."""
+    _need(q_idx, torch.uint8, "q_idx", 2)
+    _need(k_idx, torch.uint8, "k_idx", 3)
+    _need(scores, torch.float32, "scores", 2)
+    _need(pool_idx, torch.int32, "pool_idx", 2)
+    _need(top_idx, torch.int32, "top_idx", 2)
+    for t, nm in ((q_idx, "q_idx"), (k_idx, "k_idx"), (scores, "scores"), (pool_idx, "pool_idx"), (top_idx, "top_idx")):
+        _dense(t, nm)
+    R = q_idx.shape[0]
+    B, T, d = k_idx.shape
+    if q_idx.shape[1] != 64 or d != 64 or scores.shape != (R, T):
+        raise ValueError("index_full_pool shapes")
+    if pool_idx.shape != (R, k_pool) or top_idx.shape != (R, k_top):
+        raise ValueError("pool_idx / top_idx shape")
+    if pool_scores is not None:
+        _need(pool_scores, torch.float32, "pool_scores", 2)
+        _dense(pool_scores, "pool_scores")
+        if pool_scores.shape != (R, k_pool):
+            raise ValueError("pool_scores shape")
+    if row_seq is not None:
+        _need(row_seq, torch.int32, "row_seq", 1)
+    if row_limit is not None:
+        _need(row_limit, torch.int64, "row_limit", 1)
+    need = csa2_index_full_pool_workspace_size(R, T, k_pool)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+    ev0 = ev1 = None
+    if scan_events is not None:
+        ev0, ev1 = (ctypes.c_void_p(int(e.cuda_event)) for e in scan_events)
+        if not ev0.value or not ev1.value:
+            raise ValueError("scan_events must be created (recorded once) before use")
+    st = lib().csa2_index_full_pool(_p(q_idx), _p(k_idx), R, B, T, _p(row_seq), _p(row_limit), _p(scores), k_pool,
+                                    k_top, _p(pool_idx), _p(pool_scores), _p(top_idx), _p(workspace),
+                                    workspace.numel(), ev0, ev1, _stream(stream))
+    _check("csa2_index_full_pool", st)

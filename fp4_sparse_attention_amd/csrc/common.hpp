@@ -100,6 +100,23 @@ __device__ __forceinline__ uint32_t wave_exclusive_small(uint32_t c, uint32_t& t
 }
 
 // ----------------------------------------------------------------------------
+// order-preserving 32-bit keys of fp32 scores (Top-K selection): positive
+// scores get the sign bit set, negative ones are bit-inverted, -0 ranks as +0;
+// -inf and NaN map to key 0, which no visible score reaches (the smallest,
+// -FLT_MAX, maps to 0x00800000)
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t score_key(float x) {
+  uint32_t b = x == 0.0f ? 0u : __float_as_uint(x);     // -0 ranks equal to +0
+  if (x != x || x == -__builtin_inff()) return 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// inverse of score_key for visible keys (a -0 score comes back as +0)
+__device__ __forceinline__ float key_score(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// ----------------------------------------------------------------------------
 // host-side checks
 // ----------------------------------------------------------------------------
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }

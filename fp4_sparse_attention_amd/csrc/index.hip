@@ -25,7 +25,7 @@
 // prefill fills all 32 rows of A and is bound by the fp32 score writes.
 #include <algorithm>
 
-#include "common.hpp"
+#include "internal.hpp"
 
 namespace csa2 {
 
@@ -122,31 +122,90 @@ index_rows_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__
   }
 }
 
-// Full-mode decode scan as a persistent kernel: the grid holds as many
-// workgroups as the chip keeps resident, and each loops over units of 16
-// consecutive tiles (512 positions) of one row, unit u = (row u / units_per_row,
-// tiles 16 (u % units_per_row) + 4i + wave for i < 4).  The next unit's keys are
-// loaded before the current unit's products, so every wave keeps 8 KB in flight.
+// Full-mode decode scan as a persistent kernel over units of 16 tiles (512
+// positions; unit j of row r: tiles 16j + 4i + wave, i < 4).  The grid holds
+// as many workgroups as the chip keeps resident.  The next unit's keys are
+// loaded before the current unit's products, so every wave keeps 8 KB in
+// flight.  Two unit orders:
+//  - scores only: units row-major over all rows, workgroup b takes units b,
+//    b + G, b + 2G, ...; at any time the grid reads one contiguous stretch of
+//    the keys (the fastest order measured).
+//  - kHist: each workgroup stays within one row (with R <= G, workgroup b
+//    serves row b % R and takes its units b / R, b / R + G / R, ...; with
+//    R > G, whole rows b, b + G, ...), and also counts the top 12 bits of each
+//    visible score's order-preserving key in LDS.  It adds the counts of the
+//    bins it touched to top_hist [R][4096] when it leaves a row, so every
+//    workgroup flushes about once; these counts feed the Top-K selection, which
+//    then needs no histogram pass of its own.  (Row-major order here would
+//    flush at every row boundary and contend on the hot bins many times over.)
 constexpr int kUnitTiles = 16;
+constexpr int kHistBins = 4096;
 
+template <bool kHist>
 __global__ void __launch_bounds__(256)
 index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx, int64_t T,
                     const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit,
-                    float* __restrict__ scores, int64_t units_per_row, int64_t n_units) {
+                    float* __restrict__ scores, int R, int64_t units_per_row, uint32_t* __restrict__ top_hist) {
+  __shared__ uint32_t h[kHist ? kHistBins : 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int half = lane >> 5;
   const int col_in_tile = lane & 31;
   const float neg_inf = -__builtin_inff();
+  const int G = gridDim.x;
+  const int b = blockIdx.x;
+
+  // the unit order (r = row, j = unit within the row; r reaches R at the end)
+  int r;
+  int64_t j;
+  int row_step = 0;
+  int64_t j0 = 0, j_step = 0;
+  if (!kHist) {
+    // all units row-major, workgroup b takes units b, b + G, ...
+    if ((int64_t)b >= (int64_t)R * units_per_row) return;
+    r = (int)(b / units_per_row);
+    j = b - (int64_t)r * units_per_row;
+  } else if (R <= G) {
+    // workgroup b serves row b % R, units b / R, b / R + G / R, ...
+    r = b % R;
+    row_step = R;
+    j0 = b / R;
+    j_step = G / R;
+    if (j0 >= units_per_row) return;
+    j = j0;
+  } else {
+    // workgroup b scores the whole rows b, b + G, ...
+    r = b;
+    row_step = G;
+    j_step = 1;
+    j = 0;
+  }
+  auto advance = [&](int& rr, int64_t& jj) {
+    if (!kHist) {
+      jj += G;
+      if (jj >= units_per_row) {
+        rr += (int)(jj / units_per_row);
+        jj %= units_per_row;
+      }
+    } else {
+      jj += j_step;
+      if (jj >= units_per_row) {
+        rr += row_step;
+        jj = j0;
+      }
+    }
+    if (rr > R) rr = R;
+  };
+  __shared__ uint32_t n_used;
+  __shared__ uint32_t used[kHist ? kHistBins : 1];   // bins of h that are nonzero, in the order first hit
 
   struct Unit {
     i32x8 b[kUnroll];
     bool ok[kUnroll];
   };
-  auto fetch = [&](int64_t u, Unit& x) {
-    const int64_t r = u / units_per_row;
-    const int64_t t0 = (u % units_per_row) * kUnitTiles + wave;
-    const int seq = row_seq ? row_seq[r] : (int)r;
+  auto fetch = [&](int r, int64_t j, Unit& x) {
+    const int64_t t0 = j * kUnitTiles + wave;
+    const int seq = row_seq ? row_seq[r] : r;
     const int64_t limit = row_limit ? row_limit[r] : T - 1;
     const uint8_t* kseq = k_idx + (int64_t)seq * T * kIndexDim;
 #pragma unroll
@@ -156,40 +215,64 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
       x.b[i] = x.ok[i] ? load_half_key(kseq + p * kIndexDim + 32 * half) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
   };
-  auto query = [&](int64_t u, f16x8* a) {
-    const int64_t r = u / units_per_row;
+  auto query = [&](int r, f16x8* a) {
     i32x8 araw = {0, 0, 0, 0, 0, 0, 0, 0};
     if (col_in_tile == 0) {
-      const uint4* q = reinterpret_cast<const uint4*>(q_idx + r * kIndexDim + 32 * half);
+      const uint4* q = reinterpret_cast<const uint4*>(q_idx + (int64_t)r * kIndexDim + 32 * half);
       const uint4 x = q[0], y = q[1];
       araw[0] = x.x; araw[1] = x.y; araw[2] = x.z; araw[3] = x.w;
       araw[4] = y.x; araw[5] = y.y; araw[6] = y.z; araw[7] = y.w;
     }
     fp8x32_to_f16(araw, a);
   };
-
-  int64_t u = blockIdx.x;
-  if (u >= n_units) return;
-  Unit cur, nxt;
-  fetch(u, cur);
-  int64_t row = -1;
-  f16x8 a[4];
-  for (; u < n_units; u += gridDim.x) {
-    const int64_t un = u + gridDim.x;
-    if (un < n_units) fetch(un, nxt);
-    const int64_t r = u / units_per_row;
-    if (r != row) {
-      query(u, a);
-      row = r;
+  auto flush = [&](int r) {
+    __syncthreads();
+    uint32_t* g = top_hist + (int64_t)r * kHistBins;
+    const uint32_t n = n_used;
+    for (uint32_t i = threadIdx.x; i < n; i += 256) {
+      const uint32_t bin = used[i];
+      atomicAdd(&g[bin], h[bin]);
+      h[bin] = 0u;
     }
-    const int64_t t0 = (u % units_per_row) * kUnitTiles + wave;
-    float* out = scores + r * T;
+    __syncthreads();
+    if (threadIdx.x == 0) n_used = 0u;   // every thread has read n_used before the barrier above
+    __syncthreads();
+  };
+
+  if (kHist) {
+    for (int i = threadIdx.x; i < kHistBins; i += 256) h[i] = 0u;
+    if (threadIdx.x == 0) n_used = 0u;
+    __syncthreads();
+  }
+  Unit cur, nxt;
+  fetch(r, j, cur);
+  f16x8 a[4];
+  query(r, a);
+  while (r < R) {
+    int rn = r;
+    int64_t jn = j;
+    advance(rn, jn);
+    if (rn < R) fetch(rn, jn, nxt);
+    const int64_t t0 = j * kUnitTiles + wave;
+    float* out = scores + (int64_t)r * T;
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
       const f32x16 acc = mfma_score(a, cur.b[i]);
       const int64_t p = (t0 + 4 * i) * kTile + col_in_tile;
-      if (half == 0 && p < T) out[p] = cur.ok[i] ? acc[0] : neg_inf;
+      if (half == 0 && p < T) {
+        out[p] = cur.ok[i] ? acc[0] : neg_inf;
+        if (kHist && cur.ok[i]) {
+          const uint32_t key = score_key(acc[0]);
+          if (key != 0u && atomicAdd(&h[key >> 20], 1u) == 0u) used[atomicAdd(&n_used, 1u)] = key >> 20;
+        }
+      }
     }
+    if (rn != r) {
+      if (kHist) flush(r);
+      if (rn < R) query(rn, a);
+    }
+    r = rn;
+    j = jn;
     cur = nxt;
   }
 }
@@ -287,7 +370,7 @@ static int64_t resident_blocks() {
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
         hipSuccess)
       cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(index_stream_kernel), 256,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(index_stream_kernel<true>), 256,
                                                       0) != hipSuccess || per_cu < 1)
       per_cu = 4;
     cached = (int64_t)cus * per_cu;
@@ -304,6 +387,22 @@ static int tiles_per_block_for(int64_t n_tiles, int64_t rows) {
   return (int)tpb;
 }
 
+void launch_index_scan(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int64_t T, const int32_t* row_seq,
+                       const int64_t* row_limit, float* scores, uint32_t* top_hist, hipStream_t s) {
+  const int64_t n_tiles = (T + kTile - 1) / kTile;
+  const int64_t units_per_row = (n_tiles + kUnitTiles - 1) / kUnitTiles;
+  int64_t grid = std::min<int64_t>(resident_blocks(), (int64_t)R * units_per_row);
+  if (top_hist && R <= grid) grid = std::min<int64_t>(grid / R, units_per_row) * R;   // whole groups per row
+  if (top_hist)
+    index_stream_kernel<true><<<(int)grid, 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, scores, R,
+                                                        units_per_row, top_hist);
+  else
+    index_stream_kernel<false><<<(int)grid, 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, scores, R,
+                                                         units_per_row, nullptr);
+}
+
+bool index_scan_streams(int32_t R, const int32_t* row_seq) { return !(row_seq && R >= 32); }
+
 }  // namespace csa2
 
 using namespace csa2;
@@ -318,16 +417,12 @@ extern "C" csa2_status csa2_index_full(const uint8_t* q_idx, const uint8_t* k_id
   if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(scores, 16)) return CSA2_EALIGN;
   const int64_t n_tiles = (T + kTile - 1) / kTile;
   hipStream_t s = (hipStream_t)stream;
-  if (row_seq && R >= 32) {
+  if (!index_scan_streams(R, row_seq)) {
     int tpb = tiles_per_block_for(n_tiles, (R + 31) / 32);
     dim3 grid(ceil_div(n_tiles, tpb), ceil_div(R, 32));
     index_block_kernel<<<grid, 256, 0, s>>>(q_idx, k_idx, R, T, row_seq, row_limit, scores, tpb);
   } else {
-    const int64_t units_per_row = (n_tiles + kUnitTiles - 1) / kUnitTiles;
-    const int64_t n_units = units_per_row * R;
-    const int64_t grid = std::min<int64_t>(n_units, resident_blocks());
-    index_stream_kernel<<<(int)grid, 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, scores, units_per_row,
-                                                  n_units);
+    launch_index_scan(q_idx, k_idx, R, T, row_seq, row_limit, scores, nullptr, s);
   }
   return launch_status();
 }

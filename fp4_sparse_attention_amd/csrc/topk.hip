@@ -27,7 +27,7 @@
 //   multipass (long rows whose candidate lists would not fit the workspace
 //           budget): three histogram passes over the whole row, a counting
 //           pass and an ordered write pass.
-#include "common.hpp"
+#include "internal.hpp"
 
 namespace csa2 {
 
@@ -41,17 +41,6 @@ struct RowState {
   uint32_t k_eff;     // min(k, visible)
   uint32_t pad;
 };
-
-__device__ __forceinline__ uint32_t score_key(float x) {
-  uint32_t b = x == 0.0f ? 0u : __float_as_uint(x);     // -0 ranks equal to +0
-  if (x != x || x == -__builtin_inff()) return 0u;
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-
-// inverse of score_key for visible keys (a -0 score comes back as +0)
-__device__ __forceinline__ float key_score(uint32_t key) {
-  return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
-}
 
 __device__ __forceinline__ uint32_t slot_key(const float* row, const int32_t* map_row, int64_t i) {
   uint32_t k = score_key(row[i]);
@@ -1150,7 +1139,7 @@ static void launch_small(const float* scores, int32_t R, int64_t N, int64_t row_
 // compact path; a second selection (k2 <= k, positions only) when idx2_out is set
 static void launch_compact(const float* scores, int32_t R, int64_t N, int64_t row_stride, int32_t k,
                            const int32_t* index_map, int32_t* idx_out, float* score_out, int32_t k2,
-                           int32_t* idx2_out, uint8_t* ws, hipStream_t s) {
+                           int32_t* idx2_out, uint8_t* ws, hipStream_t s, bool hist_ready = false) {
   const CompactLayout L = compact_layout(R, N);
   const int seg = compact_seg(N);
   const int nseg = (int)((N + seg - 1) / seg);
@@ -1161,9 +1150,11 @@ static void launch_compact(const float* scores, int32_t R, int64_t N, int64_t ro
   int32_t* seg_pos = reinterpret_cast<int32_t*>(ws + L.seg_pos);
   uint32_t* cand_key = reinterpret_cast<uint32_t*>(ws + L.cand_key);
   int32_t* cand_pos = reinterpret_cast<int32_t*>(ws + L.cand_pos);
-  const int64_t nh = (int64_t)R * kTopBins;
-  topk_zero_kernel<<<(int)((nh + kThreads - 1) / kThreads), kThreads, 0, s>>>(hist0, nh);
-  topk_top_hist_kernel<<<dim3(n_segments(N), R), kThreads, 0, s>>>(scores, N, row_stride, index_map, hist0);
+  if (!hist_ready) {
+    const int64_t nh = (int64_t)R * kTopBins;
+    topk_zero_kernel<<<(int)((nh + kThreads - 1) / kThreads), kThreads, 0, s>>>(hist0, nh);
+    topk_top_hist_kernel<<<dim3(n_segments(N), R), kThreads, 0, s>>>(scores, N, row_stride, index_map, hist0);
+  }
   topk_compact_kernel<<<dim3(nseg, R), kThreads, 0, s>>>(scores, N, row_stride, index_map, k, seg, hist0, seg_key,
                                                          seg_pos, seg_cnt, nseg);
   topk_flatten_kernel<<<dim3(nseg, R), kThreads, 0, s>>>(N, seg, seg_key, seg_pos, seg_cnt, nseg, cand_key, cand_pos,
@@ -1272,5 +1263,46 @@ extern "C" csa2_status csa2_topk_pool(const float* scores, int32_t R, int64_t N,
       launch_multipass(scores, R, N, row_stride, k_top, index_map, top_idx, nullptr, ws, s);
       break;
   }
+  return launch_status();
+}
+
+extern "C" size_t csa2_index_full_pool_workspace_size(int32_t R, int64_t T, int32_t k_pool) {
+  return csa2_topk_workspace_size(R, T, k_pool);
+}
+
+extern "C" csa2_status csa2_index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int32_t B,
+                                            int64_t T, const int32_t* row_seq, const int64_t* row_limit,
+                                            float* scores, int32_t k_pool, int32_t k_top, int32_t* pool_idx,
+                                            float* pool_scores, int32_t* top_idx, void* workspace,
+                                            size_t workspace_bytes, void* scan_start, void* scan_end,
+                                            void* stream) {
+  if (!q_idx || !k_idx || !scores || !pool_idx || !top_idx) return CSA2_EINVAL;
+  if (R <= 0 || B <= 0 || T <= 0 || k_pool <= 0 || k_top <= 0 || k_top > k_pool) return CSA2_EINVAL;
+  if (!row_seq && R != B) return CSA2_EINVAL;
+  if (T % 4 != 0 || T >= (int64_t(1) << 31)) return CSA2_ESHAPE;
+  if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(scores, 16) || !aligned(pool_idx, 4) ||
+      !aligned(top_idx, 4) || (pool_scores && !aligned(pool_scores, 4)))
+    return CSA2_EALIGN;
+  if (!workspace || workspace_bytes < workspace_for(R, T)) return CSA2_EWORKSPACE;
+  if (!aligned(workspace, 256)) return CSA2_EALIGN;
+  if (choose_path(R, T) != kCompact || !index_scan_streams(R, row_seq)) {
+    // short rows, very long R x T, or query blocks: scores first, then the selection
+    if (scan_start && hipEventRecord((hipEvent_t)scan_start, (hipStream_t)stream) != hipSuccess) return CSA2_ELAUNCH;
+    csa2_status st = csa2_index_full(q_idx, k_idx, R, B, T, row_seq, row_limit, scores, stream);
+    if (st != CSA2_OK) return st;
+    if (scan_end && hipEventRecord((hipEvent_t)scan_end, (hipStream_t)stream) != hipSuccess) return CSA2_ELAUNCH;
+    return csa2_topk_pool(scores, R, T, T, k_pool, k_top, nullptr, pool_idx, pool_scores, top_idx, workspace,
+                          workspace_bytes, stream);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const CompactLayout L = compact_layout(R, T);
+  uint32_t* hist0 = reinterpret_cast<uint32_t*>(ws + L.hist0);
+  const int64_t nh = (int64_t)R * kTopBins;
+  topk_zero_kernel<<<(int)((nh + kThreads - 1) / kThreads), kThreads, 0, s>>>(hist0, nh);
+  if (scan_start && hipEventRecord((hipEvent_t)scan_start, s) != hipSuccess) return CSA2_ELAUNCH;
+  launch_index_scan(q_idx, k_idx, R, T, row_seq, row_limit, scores, hist0, s);
+  if (scan_end && hipEventRecord((hipEvent_t)scan_end, s) != hipSuccess) return CSA2_ELAUNCH;
+  launch_compact(scores, R, T, T, k_pool, nullptr, pool_idx, pool_scores, k_top, top_idx, ws, s, true);
   return launch_status();
 }

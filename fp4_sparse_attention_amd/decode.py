@@ -18,6 +18,7 @@ import torch
 
 from . import (csa2_fp4_pack, csa2_index_full, csa2_index_reindex, csa2_topk, csa2_topk_workspace_size,
                csa2_topk_pool, csa2_topk_pool_workspace_size, csa2_sparse_swa_decode_layers,
+               csa2_index_full_pool, csa2_index_full_pool_workspace_size,
                csa2_sparse_swa_decode_layers_workspace_size,
                csa2_sparse_decode, csa2_sparse_decode_workspace_size, csa2_swa_merge,
                csa2_swa_merge_workspace_size, csa2_sparse_swa_decode, csa2_sparse_swa_decode_workspace_size)
@@ -96,7 +97,7 @@ class Csa2DecodeStack:
         self.o = torch.empty((self.L, B, H, LATENT), dtype=f32, device=dev)
         self.lse = torch.empty((self.L, B, H), dtype=f32, device=dev)
         self.ws_topk_full = torch.empty(max(csa2_topk_workspace_size(B, T, K),
-                                            csa2_topk_pool_workspace_size(B, T, self.P) if self.use_pool else 0),
+                                            csa2_index_full_pool_workspace_size(B, T, self.P) if self.use_pool else 0),
                                         dtype=u8, device=dev)
         self.ws_topk_pool = (torch.empty(csa2_topk_workspace_size(B, self.P, K), dtype=u8, device=dev)
                              if self.use_pool else None)
@@ -126,6 +127,16 @@ class Csa2DecodeStack:
         for li, (mode, io) in enumerate(zip(self.modes, ios)):
             idx = self.idx[li]
             if mode == "full":
+                if self.use_pool and K <= self.P:
+                    # scores, the pool and this layer's Top-K (the top K of the pool) in one call
+                    ev = self._scan_events() if time_index else None
+                    csa2_index_full_pool(io.q_idx, k_idx, self.scores, self.P, K, self.pool, idx,
+                                         pool_scores=self.pool_scores, workspace=self.ws_topk_full,
+                                         scan_events=ev, stream=stream)
+                    if time_index:
+                        self.index_events = ev
+                    src.append(li)
+                    continue
                 if time_index:
                     e0 = torch.cuda.Event(enable_timing=True)
                     e1 = torch.cuda.Event(enable_timing=True)
@@ -134,11 +145,7 @@ class Csa2DecodeStack:
                 if time_index:
                     e1.record()
                     self.index_events = (e0, e1)
-                if self.use_pool and K <= self.P:
-                    # the pool and this layer's Top-K (the top K of the pool) in one selection
-                    csa2_topk_pool(self.scores, self.P, K, self.pool, idx, pool_scores=self.pool_scores,
-                                   workspace=self.ws_topk_full, stream=stream)
-                elif self.use_pool:
+                if self.use_pool:
                     csa2_topk(self.scores, self.P, self.pool, score_out=self.pool_scores,
                               workspace=self.ws_topk_full, stream=stream)
                     csa2_topk(self.scores, K, idx, workspace=self.ws_topk_full, stream=stream)
@@ -171,6 +178,14 @@ class Csa2DecodeStack:
                 csa2_swa_merge(io.q_lat, io.swa, io.swa_start, io.swa_len, sigma, self.o[li], self.lse[li],
                                o_sparse=self.o[li], lse_sparse=self.lse[li], workspace=self.ws_swa, stream=stream)
         return self.o, self.lse
+
+    def _scan_events(self):
+        # a fresh, already-created pair of timing events (the library records them)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        e1.record()
+        return e0, e1
 
     def layer_idx(self, li: int) -> torch.Tensor:
         """Indices used by layer li (a Reuse layer reports the indices it took)."""

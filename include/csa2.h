@@ -187,6 +187,32 @@ csa2_status csa2_topk_pool(const float* scores, int32_t R, int64_t N, int64_t ro
                            int32_t* top_idx, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Full-mode scoring and the candidate pool with its Top-K in one call
+ * (MarkTechPost retelling, paragraph 3: a decoder Full layer scores the whole
+ * context, fills the pool of up to 16,384 positions and takes its Top-K).
+ *
+ * Equivalent to csa2_index_full(q_idx, k_idx, R, B, T, row_seq, row_limit,
+ * scores) followed by csa2_topk_pool(scores, R, T, T, k_pool, k_top, NULL,
+ * pool_idx, pool_scores, top_idx): same scores, same selections.  For long
+ * rows the scoring pass also counts the scores' top key digits, so the
+ * selection skips its own histogram pass over the scores.
+ *
+ *   scores     fp32 [R][T], written (masked positions -inf)
+ *   workspace  >= csa2_index_full_pool_workspace_size(R, T, k_pool) bytes
+ *   scan_start, scan_end  hipEvent_t handles or NULL: when given, recorded on
+ *              the stream right before and right after the scoring kernel
+ *              (to time it apart from the selection)
+ * Other arguments as for csa2_index_full and csa2_topk_pool.
+ * Errors: as those two calls; ELAUNCH also when an event cannot be recorded.
+ * ------------------------------------------------------------------------- */
+size_t csa2_index_full_pool_workspace_size(int32_t R, int64_t T, int32_t k_pool);
+csa2_status csa2_index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int32_t B, int64_t T,
+                                 const int32_t* row_seq, const int64_t* row_limit, float* scores,
+                                 int32_t k_pool, int32_t k_top, int32_t* pool_idx, float* pool_scores,
+                                 int32_t* top_idx, void* workspace, size_t workspace_bytes, void* scan_start,
+                                 void* scan_end, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Sparse attention over the FP4 cache (HN summary key points: global sparse
  * retrieval over the shared main KV).
  *

@@ -134,3 +134,20 @@ def test_layers_call_argument_errors():
     assert L.csa2_sparse_swa_decode_layers(*a) == 2          # H = 20
     a = list(args); a[20] = 100
     assert L.csa2_sparse_swa_decode_layers(*a) == 4          # workspace too small
+
+
+def test_index_full_pool_argument_errors():
+    L = F.lib()
+    ws = 1 << 20
+    base = [DUMMY, DUMMY, 1, 1, 4096, NULL, NULL, DUMMY, 16, 4, DUMMY, NULL, DUMMY, DUMMY, ws, NULL, NULL, NULL]
+    a = list(base); a[9] = 17
+    assert L.csa2_index_full_pool(*a) == 1        # k_top > k_pool
+    a = list(base); a[12] = NULL
+    assert L.csa2_index_full_pool(*a) == 1        # no top_idx
+    a = list(base); a[4] = 4098
+    assert L.csa2_index_full_pool(*a) == 2        # T % 4
+    a = list(base); a[2] = 2
+    assert L.csa2_index_full_pool(*a) == 1        # R != B without row_seq
+    a = list(base); a[14] = 16
+    assert L.csa2_index_full_pool(*a) == 4        # workspace
+    assert F.csa2_index_full_pool_workspace_size(8, 1 << 20, 16384) == F.csa2_topk_workspace_size(8, 1 << 20, 16384)

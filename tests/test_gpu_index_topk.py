@@ -282,3 +282,34 @@ def test_topk_pool_with_index_map_and_long_rows_path():
         mh = imap[r].cpu().numpy()
         assert np.array_equal(pool[r].cpu().numpy(), OT.topk(sh, k_pool, index_map=mh)), r
         assert np.array_equal(top[r].cpu().numpy(), OT.topk(sh, k_top, index_map=mh)), r
+
+
+@pytest.mark.parametrize("R,T,k_pool,k_top", [(8, 1 << 20, 16384, 2048), (3, 8192, 2048, 256), (2, 65540, 4000, 4000)])
+def test_index_full_pool_equals_separate_calls(R, T, k_pool, k_top):
+    """Scores, pool (with scores) and Top-K of the fused call are bit-identical to
+    csa2_index_full followed by csa2_topk_pool (long rows: the scoring pass builds
+    the selection's histogram; short rows: the two calls)."""
+    dev = device()
+    k = torch.stack([W.fp8_normal(61, (T, 64), device=dev, chunk_index=b) for b in range(R)])
+    q = W.fp8_normal(62, (R, 64), device=dev)
+    s1 = torch.empty((R, T), dtype=torch.float32, device=dev)
+    p1 = torch.empty((R, k_pool), dtype=torch.int32, device=dev)
+    ps1 = torch.empty((R, k_pool), dtype=torch.float32, device=dev)
+    t1 = torch.empty((R, k_top), dtype=torch.int32, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for e in ev:
+        e.record()
+    F.csa2_index_full_pool(q, k, s1, k_pool, k_top, p1, t1, pool_scores=ps1, scan_events=ev)
+    s2 = torch.empty_like(s1)
+    p2, ps2, t2 = torch.empty_like(p1), torch.empty_like(ps1), torch.empty_like(t1)
+    F.csa2_index_full(q, k, s2)
+    F.csa2_topk_pool(s2, k_pool, k_top, p2, t2, pool_scores=ps2)
+    torch.cuda.synchronize()
+    assert ev[0].elapsed_time(ev[1]) > 0.0
+    assert torch.equal(s1, s2)
+    assert torch.equal(p1, p2) and torch.equal(t1, t2)
+    assert torch.equal(torch.nan_to_num(ps1, nan=7.0), torch.nan_to_num(ps2, nan=7.0))
+    # and against the oracle on one row
+    sh = s1[0].cpu().numpy().astype(np.float64)
+    assert np.array_equal(p1[0].cpu().numpy(), OT.topk(sh, k_pool))
+    assert np.array_equal(t1[0].cpu().numpy(), OT.topk(sh, k_top))
