@@ -99,6 +99,63 @@ __device__ __forceinline__ uint32_t wave_exclusive_small(uint32_t c, uint32_t& t
   return lanes_below(b0) + 2u * lanes_below(b1) + 4u * lanes_below(b2);
 }
 
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+  return v;
+}
+
+// block-wide exclusive prefix sum, 1024 threads (16 waves); wt holds >= 16 words
+__device__ __forceinline__ uint32_t block_scan_1024(uint32_t v, uint32_t* wt, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t inc = wave_inclusive_scan(v);
+  if (lane == 63) wt[wave] = inc;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const uint32_t t = wt[w];
+    base += w < wave ? t : 0u;
+    tot += t;
+  }
+  total = tot;
+  __syncthreads();
+  return base + inc - v;
+}
+
+// digit search over a histogram in LDS by 1024 threads: bins are walked from the
+// top, thread t owns bins nb-1-(nb/1024)t-j; returns the bin holding the need-th
+// largest entry and the count above it (need >= 1 and <= the histogram total)
+template <int kNB>
+__device__ __forceinline__ void find_bin_1024(const uint32_t* hh, uint32_t need, uint32_t* wt, uint32_t* out2) {
+  constexpr int kPer = kNB / 1024;
+  uint32_t c[kPer], local = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    c[j] = hh[kNB - 1 - kPer * threadIdx.x - j];
+    local += c[j];
+  }
+  uint32_t total;
+  const uint32_t excl = block_scan_1024(local, wt, total);
+  if (excl < need && need <= excl + local) {
+    uint32_t acc = excl;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (acc < need && need <= acc + c[j]) {
+        out2[0] = (uint32_t)(kNB - 1 - kPer * threadIdx.x - j);
+        out2[1] = acc;
+      }
+      acc += c[j];
+    }
+  }
+}
+
 // ----------------------------------------------------------------------------
 // order-preserving 32-bit keys of fp32 scores (Top-K selection): positive
 // scores get the sign bit set, negative ones are bit-inverted, -0 ranks as +0;

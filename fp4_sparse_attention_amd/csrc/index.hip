@@ -123,30 +123,32 @@ index_rows_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__
 }
 
 // Full-mode decode scan as a persistent kernel over units of 16 tiles (512
-// positions; unit j of row r: tiles 16j + 4i + wave, i < 4).  The grid holds
-// as many workgroups as the chip keeps resident.  The next unit's keys are
-// loaded before the current unit's products, so every wave keeps 8 KB in
-// flight.  Two unit orders:
+// positions).  The grid holds as many workgroups as the chip keeps resident.
+// The next unit's keys are loaded before the current unit's products, so every
+// wave keeps 8 KB in flight.  Wave w of unit j scores tiles 16j + 4w + i,
+// i < 4: the 128-position block 4j + w.  Two unit orders:
 //  - scores only: units row-major over all rows, workgroup b takes units b,
 //    b + G, b + 2G, ...; at any time the grid reads one contiguous stretch of
 //    the keys (the fastest order measured).
-//  - kHist: each workgroup stays within one row (with R <= G, workgroup b
+//  - kCand: each workgroup stays within one row (with R <= G, workgroup b
 //    serves row b % R and takes its units b / R, b / R + G / R, ...; with
-//    R > G, whole rows b, b + G, ...), and also counts the top 12 bits of each
-//    visible score's order-preserving key in LDS.  It adds the counts of the
-//    bins it touched to top_hist [R][4096] when it leaves a row, so every
-//    workgroup flushes about once; these counts feed the Top-K selection, which
-//    then needs no histogram pass of its own.  (Row-major order here would
-//    flush at every row boundary and contend on the hot bins many times over.)
+//    R > G, whole rows b, b + G, ...).  Besides the scores, each wave stores
+//    its block's candidates (visible keys >= tau_s) in position order at the
+//    block's start as (key, position) pairs (ballot ranks, no atomics), with the
+//    block's count; the workgroup counts the candidates' histogram digits in
+//    LDS, keeps the list of bins it touched and adds those counts to the row's
+//    histogram when it leaves the row (once per workgroup; with row-major
+//    order every workgroup would flush at each row boundary, measured slower).
 constexpr int kUnitTiles = 16;
-constexpr int kHistBins = 4096;
 
-template <bool kHist>
+template <bool kCand>
 __global__ void __launch_bounds__(256)
 index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx, int64_t T,
                     const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit,
-                    float* __restrict__ scores, int R, int64_t units_per_row, uint32_t* __restrict__ top_hist) {
-  __shared__ uint32_t h[kHist ? kHistBins : 1];
+                    float* __restrict__ scores, int R, int64_t units_per_row, CandOut cand) {
+  __shared__ uint32_t h[kCand ? kStreamBins : 1];
+  __shared__ uint32_t used[kCand ? kStreamBins : 1];   // bins of h that are nonzero, in the order first hit
+  __shared__ uint32_t n_used;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int half = lane >> 5;
@@ -160,7 +162,7 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
   int64_t j;
   int row_step = 0;
   int64_t j0 = 0, j_step = 0;
-  if (!kHist) {
+  if (!kCand) {
     // all units row-major, workgroup b takes units b, b + G, ...
     if ((int64_t)b >= (int64_t)R * units_per_row) return;
     r = (int)(b / units_per_row);
@@ -181,7 +183,7 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
     j = 0;
   }
   auto advance = [&](int& rr, int64_t& jj) {
-    if (!kHist) {
+    if (!kCand) {
       jj += G;
       if (jj >= units_per_row) {
         rr += (int)(jj / units_per_row);
@@ -196,38 +198,42 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
     }
     if (rr > R) rr = R;
   };
-  __shared__ uint32_t n_used;
-  __shared__ uint32_t used[kHist ? kHistBins : 1];   // bins of h that are nonzero, in the order first hit
+  auto tile_of = [&](int64_t jj) -> int64_t { return jj * kUnitTiles + 4 * wave; };
 
   struct Unit {
     i32x8 b[kUnroll];
     bool ok[kUnroll];
   };
-  auto fetch = [&](int r, int64_t j, Unit& x) {
-    const int64_t t0 = j * kUnitTiles + wave;
-    const int seq = row_seq ? row_seq[r] : r;
-    const int64_t limit = row_limit ? row_limit[r] : T - 1;
+  auto fetch = [&](int rr, int64_t jj, Unit& x) {
+    const int64_t t0 = tile_of(jj);
+    const int seq = row_seq ? row_seq[rr] : rr;
+    const int64_t limit = row_limit ? row_limit[rr] : T - 1;
     const uint8_t* kseq = k_idx + (int64_t)seq * T * kIndexDim;
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
-      const int64_t p = (t0 + 4 * i) * kTile + col_in_tile;
+      const int64_t p = (t0 + i) * kTile + col_in_tile;
       x.ok[i] = p < T && p <= limit;
       x.b[i] = x.ok[i] ? load_half_key(kseq + p * kIndexDim + 32 * half) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
   };
-  auto query = [&](int r, f16x8* a) {
+  uint32_t tau = 0, sh = 0;
+  auto query = [&](int rr, f16x8* a) {
     i32x8 araw = {0, 0, 0, 0, 0, 0, 0, 0};
     if (col_in_tile == 0) {
-      const uint4* q = reinterpret_cast<const uint4*>(q_idx + (int64_t)r * kIndexDim + 32 * half);
+      const uint4* q = reinterpret_cast<const uint4*>(q_idx + (int64_t)rr * kIndexDim + 32 * half);
       const uint4 x = q[0], y = q[1];
       araw[0] = x.x; araw[1] = x.y; araw[2] = x.z; araw[3] = x.w;
       araw[4] = y.x; araw[5] = y.y; araw[6] = y.z; araw[7] = y.w;
     }
     fp8x32_to_f16(araw, a);
+    if (kCand) {
+      tau = uniform_u32(cand.row[rr].tau_s);
+      sh = uniform_u32(cand.row[rr].sh);
+    }
   };
-  auto flush = [&](int r) {
+  auto flush = [&](int rr) {
     __syncthreads();
-    uint32_t* g = top_hist + (int64_t)r * kHistBins;
+    uint32_t* g = cand.hist + (int64_t)rr * kStreamBins;
     const uint32_t n = n_used;
     for (uint32_t i = threadIdx.x; i < n; i += 256) {
       const uint32_t bin = used[i];
@@ -239,8 +245,8 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
     __syncthreads();
   };
 
-  if (kHist) {
-    for (int i = threadIdx.x; i < kHistBins; i += 256) h[i] = 0u;
+  if (kCand) {
+    for (int i = threadIdx.x; i < kStreamBins; i += 256) h[i] = 0u;
     if (threadIdx.x == 0) n_used = 0u;
     __syncthreads();
   }
@@ -253,27 +259,177 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
     int64_t jn = j;
     advance(rn, jn);
     if (rn < R) fetch(rn, jn, nxt);
-    const int64_t t0 = j * kUnitTiles + wave;
+    const int64_t t0 = tile_of(j);
     float* out = scores + (int64_t)r * T;
+    uint32_t key[kUnroll];
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
       const f32x16 acc = mfma_score(a, cur.b[i]);
-      const int64_t p = (t0 + 4 * i) * kTile + col_in_tile;
+      const int64_t p = (t0 + i) * kTile + col_in_tile;
+      key[i] = 0u;
       if (half == 0 && p < T) {
         out[p] = cur.ok[i] ? acc[0] : neg_inf;
-        if (kHist && cur.ok[i]) {
-          const uint32_t key = score_key(acc[0]);
-          if (key != 0u && atomicAdd(&h[key >> 20], 1u) == 0u) used[atomicAdd(&n_used, 1u)] = key >> 20;
-        }
+        if (kCand && cur.ok[i]) key[i] = score_key(acc[0]);
       }
     }
+    if (kCand) {
+      // this wave's block: 4 j + wave, positions [128 (4 j + wave), + 128)
+      const int64_t blk = 4 * j + wave;
+      uint2* oc = cand.kp + (int64_t)r * T + blk * kBlockPositions;
+      uint32_t at = 0;
+#pragma unroll
+      for (int i = 0; i < kUnroll; ++i) {
+        const bool c = key[i] != 0u && key[i] >= tau;
+        const uint64_t m = __ballot(c);
+        if (c) {
+          const uint32_t o = at + lanes_below(m);
+          oc[o] = make_uint2(key[i], (uint32_t)((t0 + i) * kTile + col_in_tile));
+          const uint32_t bin = min((key[i] - tau) >> sh, (uint32_t)(kStreamBins - 1));
+          if (atomicAdd(&h[bin], 1u) == 0u) used[atomicAdd(&n_used, 1u)] = bin;
+        }
+        at += (uint32_t)__popcll(m);
+      }
+      if (lane == 0) cand.cnt[(int64_t)r * cand.n_blocks + blk] = at;
+    }
     if (rn != r) {
-      if (kHist) flush(r);
+      if (kCand) flush(r);
       if (rn < R) query(rn, a);
     }
     r = rn;
     j = jn;
     cur = nxt;
+  }
+}
+
+// Candidate threshold of the streaming pool selection, in two kernels.
+//
+// Sample: S = 4096 keys per row in 512 runs of 8 adjacent positions; run u
+// starts at ((2u + 1) V) / 1024 - 4 (clamped to the visible range [0, V),
+// V = min(T, row_limit + 1)), so the runs cover the row evenly and each costs
+// one 512-byte read.  Each wave scores two 32-sample tiles with the scan's
+// tile arithmetic; the keys go to samp [R][S].  Grid (S / 256, R).
+constexpr int kSampleN = 4096;
+constexpr int kSampleRun = 8;
+
+__global__ void __launch_bounds__(256)
+index_sample_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx, int64_t T,
+                    const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit,
+                    uint32_t* __restrict__ samp) {
+  const int r = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, col_in_tile = lane & 31;
+  const int64_t limit = row_limit ? row_limit[r] : T - 1;
+  const int64_t V = limit < 0 ? 0 : (limit + 1 < T ? limit + 1 : T);
+  const int seq = row_seq ? row_seq[r] : r;
+  const uint8_t* kseq = k_idx + (int64_t)seq * T * kIndexDim;
+  constexpr int kRuns = kSampleN / kSampleRun;
+  i32x8 kb[2];
+  bool ok[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int64_t i = ((int64_t)(blockIdx.x * 4 + wave) * 2 + u) * kTile + col_in_tile;
+    const int64_t run = i / kSampleRun;
+    int64_t p0 = ((2 * run + 1) * V) / (2 * kRuns) - kSampleRun / 2;
+    p0 = p0 < 0 ? 0 : (p0 > V - kSampleRun ? V - kSampleRun : p0);
+    int64_t p = p0 + i % kSampleRun;
+    ok[u] = V > 0;
+    p = p < 0 ? 0 : (p >= V ? V - 1 : p);
+    kb[u] = ok[u] ? load_half_key(kseq + p * kIndexDim + 32 * half) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+  }
+  i32x8 araw = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (col_in_tile == 0) {
+    const uint4* q = reinterpret_cast<const uint4*>(q_idx + (int64_t)r * kIndexDim + 32 * half);
+    const uint4 x = q[0], y = q[1];
+    araw[0] = x.x; araw[1] = x.y; araw[2] = x.z; araw[3] = x.w;
+    araw[4] = y.x; araw[5] = y.y; araw[6] = y.z; araw[7] = y.w;
+  }
+  f16x8 a[4];
+  fp8x32_to_f16(araw, a);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const f32x16 acc = mfma_score(a, kb[u]);
+    const int64_t i = ((int64_t)(blockIdx.x * 4 + wave) * 2 + u) * kTile + col_in_tile;
+    if (half == 0) samp[(int64_t)r * kSampleN + i] = ok[u] ? score_key(acc[0]) : 0u;
+  }
+}
+
+// Threshold: one 1024-thread workgroup per row.  tau_s is the lower edge of
+// the 22-bit key prefix holding the m-th largest sample key, m = ceil(mu +
+// 4 sqrt(mu) + 8) with mu = k S / V: about m V / S positions score at or above
+// it, at least k unless the sample misleads by four standard deviations (the
+// selection checks the count and recovers).  tau_s = 0 (every visible
+// position) when m > S.  The candidate histogram's digit shift sh puts the
+// sample's largest key at digit < 2048.  Also clears the row's histogram and
+// selection state before the scan.
+__device__ __forceinline__ uint32_t sample_rank(int32_t k, int64_t V) {
+  if (V <= 0) return 0u;
+  const double mu = (double)k * (double)kSampleN / (double)V;
+  const double m = ceil(mu + 4.0 * sqrt(mu) + 8.0);
+  return m > (double)kSampleN ? 0u : (uint32_t)m;
+}
+
+__global__ void __launch_bounds__(1024)
+index_tau_kernel(const uint32_t* __restrict__ samp, int64_t T, const int64_t* __restrict__ row_limit, int32_t k,
+                 StreamRow* __restrict__ rows, uint32_t* __restrict__ hist) {
+  constexpr int kBins = 4096;
+  __shared__ uint32_t h[kBins];
+  __shared__ uint32_t wt[16];
+  __shared__ uint32_t res[2];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t limit = row_limit ? row_limit[r] : T - 1;
+  const int64_t V = limit < 0 ? 0 : (limit + 1 < T ? limit + 1 : T);
+  for (int i = tid; i < kStreamBins; i += 1024) hist[(int64_t)r * kStreamBins + i] = 0u;
+  const uint32_t m = sample_rank(k, V);
+  if (m == 0u) {
+    if (tid == 0) {
+      StreamRow st = {};
+      st.tau_s = 0u;
+      st.sh = 21u;           // (key >> 21) < 2048 for every key
+      rows[r] = st;
+    }
+    return;
+  }
+  constexpr int kPer = kSampleN / 1024;
+  const uint4 kv = *reinterpret_cast<const uint4*>(samp + (int64_t)r * kSampleN + 4 * tid);
+  const uint32_t key[kPer] = {kv.x, kv.y, kv.z, kv.w};
+  for (int i = tid; i < kBins; i += 1024) h[i] = 0u;
+  __syncthreads();
+  uint32_t kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    kmax = max(kmax, key[j]);
+    atomicAdd(&h[key[j] >> 20], 1u);
+  }
+  __syncthreads();
+  uint32_t need = m;
+  find_bin_1024<kBins>(h, need, wt, res);
+  __syncthreads();
+  uint32_t prefix = res[0] << 20;
+  need -= res[1];
+  __syncthreads();
+  h[tid] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if ((key[j] >> 20) == (prefix >> 20)) atomicAdd(&h[(key[j] >> 10) & 1023u], 1u);
+  __syncthreads();
+  find_bin_1024<1024>(h, need, wt, res);
+  __syncthreads();
+  prefix |= res[0] << 10;
+  // the sample's largest key
+  kmax = wave_max_u32(kmax);
+  if (lane == 0) wt[wave] = kmax;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t mx = 0u;
+    for (int w = 0; w < 16; ++w) mx = max(mx, wt[w]);
+    const uint32_t span = mx - prefix;      // mx >= prefix: prefix is at most a sample key
+    const int bits = span ? 32 - __builtin_clz(span) : 0;
+    StreamRow st = {};
+    st.tau_s = prefix;
+    st.sh = (uint32_t)(bits > 11 ? bits - 11 : 0);
+    rows[r] = st;
   }
 }
 
@@ -388,17 +544,31 @@ static int tiles_per_block_for(int64_t n_tiles, int64_t rows) {
 }
 
 void launch_index_scan(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int64_t T, const int32_t* row_seq,
-                       const int64_t* row_limit, float* scores, uint32_t* top_hist, hipStream_t s) {
+                       const int64_t* row_limit, float* scores, const CandOut* cand, hipStream_t s) {
   const int64_t n_tiles = (T + kTile - 1) / kTile;
   const int64_t units_per_row = (n_tiles + kUnitTiles - 1) / kUnitTiles;
   int64_t grid = std::min<int64_t>(resident_blocks(), (int64_t)R * units_per_row);
-  if (top_hist && R <= grid) grid = std::min<int64_t>(grid / R, units_per_row) * R;   // whole groups per row
-  if (top_hist)
+  if (cand && R <= grid) grid = std::min<int64_t>(grid / R, units_per_row) * R;   // whole groups per row
+  if (cand)
     index_stream_kernel<true><<<(int)grid, 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, scores, R,
-                                                        units_per_row, top_hist);
+                                                        units_per_row, *cand);
   else
     index_stream_kernel<false><<<(int)grid, 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, scores, R,
-                                                         units_per_row, nullptr);
+                                                         units_per_row, CandOut{});
+}
+
+void launch_index_sample_tau(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int64_t T,
+                             const int32_t* row_seq, const int64_t* row_limit, int32_t k, StreamRow* rows,
+                             uint32_t* hist, uint32_t* samp, hipStream_t s) {
+  index_sample_kernel<<<dim3(kSampleN / 256, R), 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, samp);
+  index_tau_kernel<<<R, 1024, 0, s>>>(samp, T, row_limit, k, rows, hist);
+}
+
+int64_t index_sample_words() { return kSampleN; }
+
+int64_t index_scan_blocks(int64_t T) {
+  const int64_t n_tiles = (T + kTile - 1) / kTile;
+  return (n_tiles + kUnitTiles - 1) / kUnitTiles * 4;
 }
 
 bool index_scan_streams(int32_t R, const int32_t* row_seq) { return !(row_seq && R >= 32); }

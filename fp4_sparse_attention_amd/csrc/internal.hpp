@@ -5,10 +5,50 @@
 
 namespace csa2 {
 
-// Full-mode index scan on `s`; with top_hist (uint32 [R][4096], zeroed), also
-// counts the top 12 bits of every visible score's order-preserving key.
+// Streaming pool selection.  The Full scan splits each row into blocks of 128
+// positions (block b: positions [128 b, 128 b + 128)) and, for every visible
+// score whose order-preserving key reaches the row's threshold tau_s, stores
+// the pair (key, position) at kp [r][128 b + i] in position order, with the
+// count of block b in cnt [r][b]; it also counts each candidate's digit
+// min((key - tau_s) >> sh, 4095) in hist [r][4096].
+constexpr int kBlockPositions = 128;
+constexpr int kStreamBins = 4096;
+
+struct StreamRow {
+  uint32_t tau_s;       // candidate threshold; 0 = every visible position
+  uint32_t sh;          // digit shift of the candidate histogram
+  uint32_t n_list[2];   // entries in each selection's boundary-bin list
+  uint32_t ticket;      // gather workgroups finished
+  uint32_t mode;        // 0: candidates from the blocks; 1: from the scores row
+  uint32_t pad0[2];
+  uint32_t tau[2];      // each selection's k-th key
+  uint32_t need_eq[2];  // keys equal to tau it takes, lowest positions first
+  uint32_t k_eff[2];    // entries it writes
+  uint32_t pad1[2];
+};
+
+struct CandOut {
+  StreamRow* row;
+  uint32_t* hist;       // [R][kStreamBins], zero before the scan
+  uint2* kp;            // [R][T] (key, position)
+  uint32_t* cnt;        // [R][n_blocks]
+  int64_t n_blocks;     // blocks per row the scan writes counts for (4 per 512-position unit)
+};
+
+// Full-mode index scan on `s`; with cand, also emits the candidates.
 void launch_index_scan(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int64_t T, const int32_t* row_seq,
-                       const int64_t* row_limit, float* scores, uint32_t* top_hist, hipStream_t s);
+                       const int64_t* row_limit, float* scores, const CandOut* cand, hipStream_t s);
+
+// per-row threshold tau_s and digit shift for a selection of k from a
+// strided sample of the row's scores (samp: [R][index_sample_words()]
+// scratch); clears the row's histogram and state
+void launch_index_sample_tau(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int64_t T,
+                             const int32_t* row_seq, const int64_t* row_limit, int32_t k, StreamRow* rows,
+                             uint32_t* hist, uint32_t* samp, hipStream_t s);
+int64_t index_sample_words();
+
+// blocks per row whose counts the candidate scan writes
+int64_t index_scan_blocks(int64_t T);
 
 // whether csa2_index_full uses the streaming scan (decode) rather than the
 // query-block kernel (chunked prefill) for this row layout

@@ -27,6 +27,8 @@
 //   multipass (long rows whose candidate lists would not fit the workspace
 //           budget): three histogram passes over the whole row, a counting
 //           pass and an ordered write pass.
+#include <algorithm>
+
 #include "internal.hpp"
 
 namespace csa2 {
@@ -364,35 +366,6 @@ constexpr int kSmallThreads = 1024;
 constexpr int kSmallBits = 12;
 constexpr int kSmallBins = 1 << kSmallBits;
 
-// block-wide exclusive prefix sum, 1024 threads (16 waves); wt holds >= 16 words
-__device__ __forceinline__ uint32_t block_scan_1024(uint32_t v, uint32_t* wt, uint32_t& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t inc = wave_inclusive_scan(v);
-  if (lane == 63) wt[wave] = inc;
-  __syncthreads();
-  uint32_t base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < 16; ++w) {
-    const uint32_t t = wt[w];
-    base += w < wave ? t : 0u;
-    tot += t;
-  }
-  total = tot;
-  __syncthreads();
-  return base + inc - v;
-}
-
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
-  return v;
-}
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
-  return v;
-}
 
 // Wave w owns the slots [256 J w, 256 J (w+1)) of the row, 4096 J >= N;
 // in step it, lane l holds slots 256 (J w + it) + 4l + [0, 4).  So every wave
@@ -759,33 +732,6 @@ topk_flatten_kernel(int64_t N, int seg, const uint32_t* __restrict__ seg_key, co
   if (si == n_seg - 1 && threadIdx.x == 0) cand_total[r] = base + n;
 }
 
-// digit search over a histogram in LDS by 1024 threads: bins are walked from the
-// top, thread t owns bins nb-1-(nb/1024)t-j; returns the bin holding the need-th
-// largest entry and the count above it (need >= 1 and <= the histogram total)
-template <int kNB>
-__device__ __forceinline__ void find_bin_1024(const uint32_t* hh, uint32_t need, uint32_t* wt, uint32_t* out2) {
-  constexpr int kPer = kNB / 1024;
-  uint32_t c[kPer], local = 0;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    c[j] = hh[kNB - 1 - kPer * threadIdx.x - j];
-    local += c[j];
-  }
-  uint32_t total;
-  const uint32_t excl = block_scan_1024(local, wt, total);
-  if (excl < need && need <= excl + local) {
-    uint32_t acc = excl;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      if (acc < need && need <= acc + c[j]) {
-        out2[0] = (uint32_t)(kNB - 1 - kPer * threadIdx.x - j);
-        out2[1] = acc;
-      }
-      acc += c[j];
-    }
-  }
-}
-
 // Finishing the selection(s) on a row's slot-ordered candidate list takes two
 // kernels: one workgroup per row stages the keys in LDS (when they fit), finds
 // tau and the number of ties to take for each selection, and counts, per chunk
@@ -1064,6 +1010,530 @@ topk_write_cand_kernel(int64_t N, const uint32_t* __restrict__ cand_key, const i
   }
 }
 
+// ----------------------------------------------------------------------------
+// streaming path of the Full scan + pool selection
+//
+// Before the scan, a strided sample bounds each row's k-th largest key from
+// below (tau_s); the scan stores every visible key >= tau_s, block by block in
+// position order, and the histogram of the candidates' digits
+// min((key - tau_s) >> sh, 4095).  Two multi-workgroup passes finish both
+// selections (k and k2 <= k), each workgroup owning a run of blocks:
+//  - gather: each workgroup finds each selection's boundary bin b0 (the bin of
+//    the k-th candidate) from the histogram, counts its candidates in higher
+//    bins and appends those in bin b0 (typically a few dozen per row) to a
+//    short list;
+//  - finish (one workgroup per row): the k-th key tau exactly from the list,
+//    the number of keys equal to tau to take, and every gather workgroup's
+//    output base (keys above tau and ties at tau in the blocks before it);
+//  - write: each workgroup writes its selected candidates in position order,
+//    ties at tau to the lowest positions.
+// The result does not depend on tau_s.  When fewer than k candidates arrive
+// (tau_s was above the k-th key) or a boundary bin overflows its list (massive
+// ties), the finish workgroup selects from the row's scores instead and the
+// write pass reads the scores too.  (The passes are separate launches: a
+// device-scope fence per workgroup, to let the last gather workgroup finish the
+// row, costs more than a launch here, and so does resolving the row again in
+// every write workgroup.)
+// ----------------------------------------------------------------------------
+constexpr int kStreamGroups = 64;        // gather / write workgroups per row
+constexpr int kListCap = 4096;           // boundary-bin list entries per row and selection
+constexpr int kSG = 256;                 // threads per gather / write workgroup
+
+struct StreamBase {
+  uint32_t gt[2];                        // keys > tau in the workgroups before this one
+  uint32_t eq[2];                        // keys == tau in the workgroups before this one
+};
+
+// the need-th largest of n keys (need in [1, n]); returns it and sets rank_gt
+// to the number of keys above it.  256 threads; keys in LDS or global memory.
+__device__ uint32_t kth_largest_256(const uint32_t* keys, uint32_t n, uint32_t need, uint32_t* h /* 4096 */,
+                                    uint32_t* tmp /* 8 */, uint32_t* res /* 2 */, uint32_t& rank_gt) {
+  const int tid = threadIdx.x;
+  if (n <= (uint32_t)kSG) {
+    // rank by counting: thread i holds key i
+    const uint32_t mine = tid < (int)n ? keys[tid] : 0u;
+    uint32_t gt = 0u, eq = 0u;
+    for (uint32_t j = 0; j < n; ++j) {
+      const uint32_t o = keys[j];
+      gt += o > mine;
+      eq += o == mine;
+    }
+    if (tid == 0) res[0] = 0u;
+    __syncthreads();
+    if (tid < (int)n && gt < need && need <= gt + eq) {
+      res[0] = mine;
+      res[1] = gt;
+    }
+    __syncthreads();
+    const uint32_t tau = res[0];
+    rank_gt = res[1];
+    __syncthreads();
+    return tau;
+  }
+  uint32_t prefix = 0u, above = 0u;
+#pragma unroll 1
+  for (int d = 0; d < 3; ++d) {
+    const int shift = d == 0 ? 20 : (d == 1 ? 10 : 0);
+    const int hi = d == 0 ? 32 : (d == 1 ? 20 : 10);
+    const int nb = d == 0 ? 4096 : 1024;
+    for (int i = tid; i < nb; i += kSG) h[i] = 0u;
+    __syncthreads();
+    for (uint32_t i = tid; i < n; i += kSG) {
+      const uint32_t kx = keys[i];
+      if (hi == 32 || (kx >> hi) == (prefix >> hi)) atomicAdd(&h[(kx >> shift) & (nb - 1)], 1u);
+    }
+    __syncthreads();
+    // bins from the top, nb / 256 per thread
+    const int per = nb / kSG;
+    uint32_t local = 0;
+    for (int j = 0; j < per; ++j) local += h[nb - 1 - per * tid - j];
+    uint32_t total;
+    const uint32_t excl = block_exclusive_scan(local, tmp, total);
+    if (excl < need && need <= excl + local) {
+      uint32_t acc = excl;
+      for (int j = 0; j < per; ++j) {
+        const uint32_t c = h[nb - 1 - per * tid - j];
+        if (acc < need && need <= acc + c) {
+          res[0] = (uint32_t)(nb - 1 - per * tid - j);
+          res[1] = acc;
+        }
+        acc += c;
+      }
+    }
+    __syncthreads();
+    prefix |= res[0] << shift;
+    need -= res[1];
+    above += res[1];
+    __syncthreads();
+  }
+  rank_gt = above;
+  return prefix;
+}
+
+// The first 8 candidates of a block and its count, loaded together (one round
+// trip for the common block of a few candidates); the entries beyond the count
+// are ignored (the candidate array carries 64 bytes of tail padding, so the
+// reads stay inside the workspace).
+struct BlockHead {
+  uint32_t c;
+  uint4 e[4];                             // (key, position) pairs 0-7
+};
+
+__device__ __forceinline__ BlockHead load_head(const uint2* kp, const uint32_t* cnt, int64_t blk) {
+  BlockHead h;
+  const uint4* b = reinterpret_cast<const uint4*>(kp + blk * kBlockPositions);
+  h.c = cnt[blk];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) h.e[u] = b[u];
+  return h;
+}
+
+// entries of block blk in position order, f(key, position): from the candidate
+// block (mode 0; hd = its head) or every visible position of the block from the
+// scores row (mode 1)
+template <class F>
+__device__ __forceinline__ void for_block(uint32_t mode, const BlockHead& hd, const float* row, int64_t T,
+                                          const uint2* kp, int64_t blk, F&& f) {
+  if (mode == 0u) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if ((uint32_t)(2 * u) < hd.c) f(hd.e[u].x, (int32_t)hd.e[u].y);
+      if ((uint32_t)(2 * u + 1) < hd.c) f(hd.e[u].z, (int32_t)hd.e[u].w);
+    }
+    const uint4* b = reinterpret_cast<const uint4*>(kp + blk * kBlockPositions);
+    for (uint32_t e = 8; e < hd.c; e += 2) {
+      const uint4 v = b[e / 2];
+      f(v.x, (int32_t)v.y);
+      if (e + 1 < hd.c) f(v.z, (int32_t)v.w);
+    }
+  } else {
+    const int64_t p0 = blk * kBlockPositions;
+    const int64_t p1 = min(T, p0 + kBlockPositions);
+    for (int64_t i = p0; i < p1; i += 4) {
+      const float4 v = *reinterpret_cast<const float4*>(row + i);
+      const float f4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t kx = score_key(f4[q]);
+        if (kx != 0u) f(kx, (int32_t)(i + q));
+      }
+    }
+  }
+}
+
+// C = the row's candidate count, each selection's k_eff, boundary bin b0, the
+// candidates above it (above) and in it (cb0), and whether the row must be
+// selected from its scores; 256 threads, bins walked from the top
+struct RowBins {
+  uint32_t C, k_eff[2], b0[2], above[2], cb0[2];
+  bool fallback;
+};
+
+__device__ __forceinline__ RowBins row_bins(const uint32_t* hr, uint32_t tau_s, int32_t k, int32_t k2, uint32_t* tmp,
+                                            uint32_t* s_b /* 6 */) {
+  const int tid = threadIdx.x;
+  constexpr int kPer = kStreamBins / kSG;
+  uint32_t c[kPer], local = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    c[j] = hr[kStreamBins - 1 - kPer * tid - j];
+    local += c[j];
+  }
+  RowBins rb;
+  const uint32_t excl = block_exclusive_scan(local, tmp, rb.C);
+  const uint32_t kk[2] = {(uint32_t)k, (uint32_t)k2};
+#pragma unroll
+  for (int s = 0; s < 2; ++s) rb.k_eff[s] = tau_s == 0u ? min(kk[s], rb.C) : kk[s];
+  if (tid == 0)
+    for (int i = 0; i < 6; ++i) s_b[i] = 0u;
+  __syncthreads();
+  rb.fallback = tau_s != 0u && rb.C < kk[0];
+  if (!rb.fallback) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint32_t need = rb.k_eff[s];
+      if (need > 0u && excl < need && need <= excl + local) {
+        uint32_t acc = excl;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          if (acc < need && need <= acc + c[j]) {
+            s_b[3 * s] = (uint32_t)(kStreamBins - 1 - kPer * tid - j);
+            s_b[3 * s + 1] = acc;
+            s_b[3 * s + 2] = c[j];
+          }
+          acc += c[j];
+        }
+      }
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    rb.b0[s] = s_b[3 * s];
+    rb.above[s] = s_b[3 * s + 1];
+    rb.cb0[s] = s_b[3 * s + 2];
+  }
+  __syncthreads();
+  if (!rb.fallback && rb.k_eff[0] > 0u) rb.fallback = rb.cb0[0] > (uint32_t)kListCap || rb.cb0[1] > (uint32_t)kListCap;
+  return rb;
+}
+
+// gather: per workgroup, the candidates above each boundary bin in its blocks,
+// and the candidates inside the boundary bin appended to the row's short list
+__global__ void __launch_bounds__(kSG)
+stream_gather_kernel(int64_t nbk, int bpw, StreamRow* __restrict__ rows, const uint32_t* __restrict__ hist,
+                     const uint2* __restrict__ cand, const uint32_t* __restrict__ cand_cnt, int64_t T,
+                     uint32_t* __restrict__ above_out, uint2* __restrict__ list, int32_t k, int32_t k2) {
+  __shared__ uint32_t tmp[8];
+  __shared__ uint32_t s_b[6];
+  const int r = blockIdx.y, g = blockIdx.x, G = gridDim.x, tid = threadIdx.x;
+  const int R = gridDim.y;
+  const uint32_t tau_s = rows[r].tau_s, sh = rows[r].sh;
+  const uint2* kp = cand + (int64_t)r * T;
+  const uint32_t* cn = cand_cnt + (int64_t)r * nbk;
+  // the first block's head is loaded with the histogram
+  const int64_t blk0 = (int64_t)g * bpw, blk1 = min(nbk, blk0 + bpw);
+  BlockHead hd0 = {};
+  if (blk0 + tid < blk1) hd0 = load_head(kp, cn, blk0 + tid);
+  const RowBins rb = row_bins(hist + (int64_t)r * kStreamBins, tau_s, k, k2, tmp, s_b);
+  if (rb.fallback || rb.k_eff[0] == 0u) return;
+  uint32_t ab[2] = {0u, 0u};
+  for (int64_t blk = blk0 + tid; blk < blk1; blk += kSG) {
+    const BlockHead hd = blk == blk0 + tid ? hd0 : load_head(kp, cn, blk);
+    for_block(0u, hd, nullptr, T, kp, blk, [&](uint32_t kx, int32_t p) {
+      const uint32_t d = min((kx - tau_s) >> sh, (uint32_t)(kStreamBins - 1));
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (d > rb.b0[s]) ++ab[s];
+        if (d == rb.b0[s]) {
+          const uint32_t i = atomicAdd(&rows[r].n_list[s], 1u);
+          list[((int64_t)s * R + r) * kListCap + i] = make_uint2(kx, (uint32_t)p);
+        }
+      }
+    });
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    uint32_t tot;
+    block_exclusive_scan(ab[s], tmp, tot);
+    if (tid == 0) above_out[((int64_t)r * G + g) * 2 + s] = tot;
+  }
+}
+
+// finish: one workgroup per row.  From the short lists: each selection's k-th
+// key tau (kth_largest_256), the ties at tau it takes, and for every gather
+// workgroup the keys above tau and equal to tau in the blocks before it.  In
+// fallback rows the same from the whole scores row: the k-th keys by three
+// radix digits, the per-workgroup counts by a pass over the positions.
+__global__ void __launch_bounds__(kSG)
+stream_finish_kernel(const float* __restrict__ scores, int64_t T, int bpw, int G, StreamRow* __restrict__ rows,
+                     const uint32_t* __restrict__ hist, const uint32_t* __restrict__ above_out,
+                     const uint2* __restrict__ list, StreamBase* __restrict__ base_out, int32_t k, int32_t k2) {
+  __shared__ uint32_t tmp[8];
+  __shared__ uint32_t s_b[6];
+  __shared__ uint32_t res[2];
+  __shared__ uint32_t h[kStreamBins];
+  __shared__ uint32_t s_lk[kListCap];
+  __shared__ uint32_t s_gt[kStreamGroups], s_eq[kStreamGroups];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int R = gridDim.x;
+  const StreamRow st = rows[r];
+  const float* row = scores + (int64_t)r * T;
+  // entry tid of each list and workgroup tid's gather counts, loaded with the histogram
+  uint2 le0[2];
+  uint32_t ab0[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    le0[s] = list[((int64_t)s * R + r) * kListCap + tid];
+    ab0[s] = tid < G ? above_out[((int64_t)r * G + tid) * 2 + s] : 0u;
+  }
+  const RowBins rb = row_bins(hist + (int64_t)r * kStreamBins, st.tau_s, k, k2, tmp, s_b);
+  StreamBase* bo = base_out + (int64_t)r * G;
+  uint32_t tau[2] = {0u, 0u}, need_eq[2] = {0u, 0u}, k_eff[2] = {rb.k_eff[0], rb.k_eff[1]};
+  if (!rb.fallback && rb.k_eff[0] == 0u) {
+    for (int i = tid; i < G; i += kSG) bo[i] = StreamBase{{0u, 0u}, {0u, 0u}};
+  } else if (!rb.fallback) {
+#pragma unroll 1
+    for (int s = 0; s < 2; ++s) {
+      const uint32_t n = st.n_list[s];
+      const uint2* ls = list + ((int64_t)s * R + r) * kListCap;
+      for (uint32_t i = tid; i < n; i += kSG) s_lk[i] = i == (uint32_t)tid ? le0[s].x : ls[i].x;
+      for (int i = tid; i < G; i += kSG) { s_gt[i] = 0u; s_eq[i] = 0u; }
+      __syncthreads();
+      const uint32_t need = rb.k_eff[s] - rb.above[s];
+      uint32_t gt_in_list;
+      tau[s] = kth_largest_256(s_lk, n, need, h, tmp, res, gt_in_list);
+      need_eq[s] = need - gt_in_list;
+      for (uint32_t i = tid; i < n; i += kSG) {
+        const int32_t p = (int32_t)(i == (uint32_t)tid ? le0[s].y : ls[i].y);
+        const uint32_t wg = (uint32_t)(((int64_t)p / kBlockPositions) / bpw);
+        if (s_lk[i] > tau[s]) atomicAdd(&s_gt[wg], 1u);
+        else if (s_lk[i] == tau[s]) atomicAdd(&s_eq[wg], 1u);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        // G <= 64: one wave scans the workgroups' counts
+        const uint32_t gtc = tid < G ? s_gt[tid] + ab0[s] : 0u;
+        const uint32_t eqc = tid < G ? s_eq[tid] : 0u;
+        const uint32_t gi = wave_inclusive_scan(gtc) - gtc, ei = wave_inclusive_scan(eqc) - eqc;
+        if (tid < G) {
+          bo[tid].gt[s] = gi;
+          bo[tid].eq[s] = ei;
+        }
+      }
+      __syncthreads();
+    }
+  } else {
+    // every visible position of the row: 12-bit histogram of all keys, the
+    // k-th key of each selection by two more digits, per-workgroup counts
+    constexpr int kPer = kStreamBins / kSG;
+    for (int i = tid; i < kStreamBins; i += kSG) h[i] = 0u;
+    __syncthreads();
+    for (int64_t i = 4 * (int64_t)tid; i < T; i += 4 * kSG) {
+      const float4 v = *reinterpret_cast<const float4*>(row + i);
+      const float f4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t kx = score_key(f4[q]);
+        if (kx != 0u) atomicAdd(&h[kx >> 20], 1u);
+      }
+    }
+    __syncthreads();
+    uint32_t V;
+    {
+      uint32_t loc = 0;
+      for (int j = 0; j < kPer; ++j) loc += h[kPer * tid + j];
+      block_exclusive_scan(loc, tmp, V);
+    }
+    const uint32_t kk[2] = {(uint32_t)k, (uint32_t)k2};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) k_eff[s] = min(kk[s], V);
+    if (k_eff[0] == 0u) {
+      for (int i = tid; i < G; i += kSG) bo[i] = StreamBase{{0u, 0u}, {0u, 0u}};
+    } else {
+      uint32_t prefix[2], need[2];
+#pragma unroll 1
+      for (int s = 0; s < 2; ++s) {
+        uint32_t lc[kPer], lsum = 0;
+        for (int j = 0; j < kPer; ++j) { lc[j] = h[kStreamBins - 1 - kPer * tid - j]; lsum += lc[j]; }
+        uint32_t tot;
+        const uint32_t ex = block_exclusive_scan(lsum, tmp, tot);
+        if (ex < k_eff[s] && k_eff[s] <= ex + lsum) {
+          uint32_t acc = ex;
+          for (int j = 0; j < kPer; ++j) {
+            if (acc < k_eff[s] && k_eff[s] <= acc + lc[j]) { res[0] = kStreamBins - 1 - kPer * tid - j; res[1] = acc; }
+            acc += lc[j];
+          }
+        }
+        __syncthreads();
+        prefix[s] = res[0] << 20;
+        need[s] = k_eff[s] - res[1];
+        __syncthreads();
+      }
+#pragma unroll 1
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll 1
+        for (int d = 1; d <= 2; ++d) {
+          const int shift = d == 1 ? 10 : 0, hi = d == 1 ? 20 : 10;
+          for (int i = tid; i < 1024; i += kSG) s_lk[i] = 0u;
+          __syncthreads();
+          for (int64_t i = 4 * (int64_t)tid; i < T; i += 4 * kSG) {
+            const float4 v = *reinterpret_cast<const float4*>(row + i);
+            const float f4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t kx = score_key(f4[q]);
+              if (kx != 0u && (kx >> hi) == (prefix[s] >> hi)) atomicAdd(&s_lk[(kx >> shift) & 1023u], 1u);
+            }
+          }
+          __syncthreads();
+          uint32_t lc[4], lsum = 0;
+          for (int j = 0; j < 4; ++j) { lc[j] = s_lk[1023 - 4 * tid - j]; lsum += lc[j]; }
+          uint32_t tot;
+          const uint32_t ex = block_exclusive_scan(lsum, tmp, tot);
+          if (ex < need[s] && need[s] <= ex + lsum) {
+            uint32_t acc = ex;
+            for (int j = 0; j < 4; ++j) {
+              if (acc < need[s] && need[s] <= acc + lc[j]) { res[0] = 1023 - 4 * tid - j; res[1] = acc; }
+              acc += lc[j];
+            }
+          }
+          __syncthreads();
+          prefix[s] |= res[0] << shift;
+          need[s] -= res[1];
+          __syncthreads();
+        }
+        tau[s] = prefix[s];
+        need_eq[s] = need[s];
+      }
+      // per-workgroup counts of keys > tau and == tau (thread-contiguous position runs)
+#pragma unroll 1
+      for (int s = 0; s < 2; ++s) {
+        for (int i = tid; i < G; i += kSG) { s_gt[i] = 0u; s_eq[i] = 0u; }
+        __syncthreads();
+        const int64_t run = (T + kSG - 1) / kSG;
+        const int64_t i0 = min(T, (int64_t)tid * run), i1 = min(T, i0 + run);
+        uint32_t wg_cur = 0xFFFFFFFFu, gt = 0u, eq = 0u;
+        for (int64_t i = i0; i < i1; ++i) {
+          const uint32_t wg = (uint32_t)((i / kBlockPositions) / bpw);
+          if (wg != wg_cur) {
+            if (wg_cur != 0xFFFFFFFFu) { atomicAdd(&s_gt[wg_cur], gt); atomicAdd(&s_eq[wg_cur], eq); }
+            wg_cur = wg; gt = 0u; eq = 0u;
+          }
+          const uint32_t kx = score_key(row[i]);
+          gt += kx > tau[s];
+          eq += kx == tau[s];
+        }
+        if (wg_cur != 0xFFFFFFFFu) { atomicAdd(&s_gt[wg_cur], gt); atomicAdd(&s_eq[wg_cur], eq); }
+        __syncthreads();
+        if (tid < 64) {
+          const uint32_t gtc = tid < G ? s_gt[tid] : 0u;
+          const uint32_t eqc = tid < G ? s_eq[tid] : 0u;
+          const uint32_t gi = wave_inclusive_scan(gtc) - gtc, ei = wave_inclusive_scan(eqc) - eqc;
+          if (tid < G) {
+            bo[tid].gt[s] = gi;
+            bo[tid].eq[s] = ei;
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+  if (tid == 0) {
+    StreamRow* o = &rows[r];
+    o->mode = rb.fallback ? 1u : 0u;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      o->tau[s] = tau[s];
+      o->need_eq[s] = need_eq[s];
+      o->k_eff[s] = k_eff[s];
+    }
+  }
+}
+
+// ordered write: each workgroup's blocks, thread t taking a contiguous run of them
+__global__ void __launch_bounds__(kSG)
+stream_write_kernel(const float* __restrict__ scores, int64_t T, int64_t nbk, int bpw,
+                    const StreamRow* __restrict__ rows, const StreamBase* __restrict__ base,
+                    const uint2* __restrict__ cand, const uint32_t* __restrict__ cand_cnt, int32_t k, int32_t k2,
+                    int32_t* __restrict__ idx_out, float* __restrict__ score_out, int32_t* __restrict__ idx2_out) {
+  __shared__ uint32_t tmp[8];
+  const int r = blockIdx.y, g = blockIdx.x, G = gridDim.x, tid = threadIdx.x;
+  const float* row = scores + (int64_t)r * T;
+  const uint2* kp = cand + (int64_t)r * T;
+  const uint32_t* cn = cand_cnt + (int64_t)r * nbk;
+  const int64_t blk0 = (int64_t)g * bpw, blk1 = min(nbk, blk0 + bpw);
+  const int64_t per = (blk1 - blk0 + kSG - 1) / kSG;
+  const int64_t my0 = min(blk1, blk0 + tid * per), my1 = min(blk1, my0 + per);
+  BlockHead hd0 = {};
+  if (my0 < my1) hd0 = load_head(kp, cn, my0);
+  const StreamRow st = rows[r];
+  const StreamBase bs = base[(int64_t)r * G + g];
+  const uint32_t kk[2] = {(uint32_t)k, (uint32_t)k2};
+  int32_t* orow[2] = {idx_out + (int64_t)r * k, idx2_out + (int64_t)r * k2};
+  float* srow = score_out ? score_out + (int64_t)r * k : nullptr;
+  if (g == 0) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      for (uint32_t i = st.k_eff[s] + tid; i < kk[s]; i += kSG) {
+        orow[s][i] = -1;
+        if (s == 0 && srow) srow[i] = __builtin_nanf("");
+      }
+  }
+  if (st.k_eff[0] == 0u) return;
+  uint32_t gt[2] = {0u, 0u}, eq[2] = {0u, 0u};
+  for (int64_t blk = my0; blk < my1; ++blk)
+    for_block(st.mode, blk == my0 ? hd0 : load_head(kp, cn, blk), row, T, kp, blk, [&](uint32_t kx, int32_t) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        gt[s] += kx > st.tau[s];
+        eq[s] += kx == st.tau[s];
+      }
+    });
+  uint32_t gs[2], es[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    uint32_t tot;
+    gs[s] = bs.gt[s] + block_exclusive_scan(gt[s], tmp, tot);
+    es[s] = bs.eq[s] + block_exclusive_scan(eq[s], tmp, tot);
+  }
+  for (int64_t blk = my0; blk < my1; ++blk)
+    for_block(st.mode, blk == my0 ? hd0 : load_head(kp, cn, blk), row, T, kp, blk, [&](uint32_t kx, int32_t p) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bool is_gt = kx > st.tau[s], is_eq = kx == st.tau[s];
+        const bool take = is_gt || (is_eq && es[s] < st.need_eq[s]);
+        const uint32_t o = gs[s] + (is_gt ? min(es[s], st.need_eq[s]) : es[s]);
+        if (take && o < st.k_eff[s]) {
+          orow[s][o] = p;
+          if (s == 0 && srow) srow[o] = key_score(kx);
+        }
+        gs[s] += is_gt ? 1u : 0u;
+        es[s] += is_eq ? 1u : 0u;
+      }
+    });
+}
+
+struct StreamLayout {
+  size_t rows, hist, samp, cnt, above, base, list, cand, total;
+};
+
+static StreamLayout stream_layout(int32_t R, int64_t T) {
+  StreamLayout L;
+  const int64_t nbk = index_scan_blocks(T);
+  size_t off = 0;
+  L.rows = off; off += align_up((size_t)R * sizeof(StreamRow), 256);
+  L.hist = off; off += align_up((size_t)R * kStreamBins * 4, 256);
+  L.samp = off; off += align_up((size_t)R * index_sample_words() * 4, 256);
+  L.cnt = off; off += align_up((size_t)R * nbk * 4, 256);
+  L.above = off; off += align_up((size_t)R * kStreamGroups * 2 * 4, 256);
+  L.base = off; off += align_up((size_t)R * kStreamGroups * sizeof(StreamBase), 256);
+  L.list = off; off += align_up((size_t)2 * R * kListCap * 8, 256);
+  L.cand = off; off += align_up((size_t)R * T * 8 + 64, 256);
+  L.total = off;
+  return L;
+}
+
 static int n_segments(int64_t N) { return (int)((N + kSeg - 1) / kSeg); }
 
 enum Path { kSmall, kCompact, kMultipass };
@@ -1139,7 +1609,7 @@ static void launch_small(const float* scores, int32_t R, int64_t N, int64_t row_
 // compact path; a second selection (k2 <= k, positions only) when idx2_out is set
 static void launch_compact(const float* scores, int32_t R, int64_t N, int64_t row_stride, int32_t k,
                            const int32_t* index_map, int32_t* idx_out, float* score_out, int32_t k2,
-                           int32_t* idx2_out, uint8_t* ws, hipStream_t s, bool hist_ready = false) {
+                           int32_t* idx2_out, uint8_t* ws, hipStream_t s) {
   const CompactLayout L = compact_layout(R, N);
   const int seg = compact_seg(N);
   const int nseg = (int)((N + seg - 1) / seg);
@@ -1150,7 +1620,7 @@ static void launch_compact(const float* scores, int32_t R, int64_t N, int64_t ro
   int32_t* seg_pos = reinterpret_cast<int32_t*>(ws + L.seg_pos);
   uint32_t* cand_key = reinterpret_cast<uint32_t*>(ws + L.cand_key);
   int32_t* cand_pos = reinterpret_cast<int32_t*>(ws + L.cand_pos);
-  if (!hist_ready) {
+  {
     const int64_t nh = (int64_t)R * kTopBins;
     topk_zero_kernel<<<(int)((nh + kThreads - 1) / kThreads), kThreads, 0, s>>>(hist0, nh);
     topk_top_hist_kernel<<<dim3(n_segments(N), R), kThreads, 0, s>>>(scores, N, row_stride, index_map, hist0);
@@ -1267,7 +1737,8 @@ extern "C" csa2_status csa2_topk_pool(const float* scores, int32_t R, int64_t N,
 }
 
 extern "C" size_t csa2_index_full_pool_workspace_size(int32_t R, int64_t T, int32_t k_pool) {
-  return csa2_topk_workspace_size(R, T, k_pool);
+  if (R <= 0 || T <= 0) return 0;
+  return std::max(csa2_topk_workspace_size(R, T, k_pool), stream_layout(R, T).total);
 }
 
 extern "C" csa2_status csa2_index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int32_t B,
@@ -1283,26 +1754,40 @@ extern "C" csa2_status csa2_index_full_pool(const uint8_t* q_idx, const uint8_t*
   if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(scores, 16) || !aligned(pool_idx, 4) ||
       !aligned(top_idx, 4) || (pool_scores && !aligned(pool_scores, 4)))
     return CSA2_EALIGN;
-  if (!workspace || workspace_bytes < workspace_for(R, T)) return CSA2_EWORKSPACE;
+  if (!workspace || workspace_bytes < csa2_index_full_pool_workspace_size(R, T, k_pool)) return CSA2_EWORKSPACE;
   if (!aligned(workspace, 256)) return CSA2_EALIGN;
+  hipStream_t s = (hipStream_t)stream;
   if (choose_path(R, T) != kCompact || !index_scan_streams(R, row_seq)) {
     // short rows, very long R x T, or query blocks: scores first, then the selection
-    if (scan_start && hipEventRecord((hipEvent_t)scan_start, (hipStream_t)stream) != hipSuccess) return CSA2_ELAUNCH;
+    if (scan_start && hipEventRecord((hipEvent_t)scan_start, s) != hipSuccess) return CSA2_ELAUNCH;
     csa2_status st = csa2_index_full(q_idx, k_idx, R, B, T, row_seq, row_limit, scores, stream);
     if (st != CSA2_OK) return st;
-    if (scan_end && hipEventRecord((hipEvent_t)scan_end, (hipStream_t)stream) != hipSuccess) return CSA2_ELAUNCH;
+    if (scan_end && hipEventRecord((hipEvent_t)scan_end, s) != hipSuccess) return CSA2_ELAUNCH;
     return csa2_topk_pool(scores, R, T, T, k_pool, k_top, nullptr, pool_idx, pool_scores, top_idx, workspace,
                           workspace_bytes, stream);
   }
-  hipStream_t s = (hipStream_t)stream;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const CompactLayout L = compact_layout(R, T);
-  uint32_t* hist0 = reinterpret_cast<uint32_t*>(ws + L.hist0);
-  const int64_t nh = (int64_t)R * kTopBins;
-  topk_zero_kernel<<<(int)((nh + kThreads - 1) / kThreads), kThreads, 0, s>>>(hist0, nh);
+  const StreamLayout L = stream_layout(R, T);
+  StreamRow* rows = reinterpret_cast<StreamRow*>(ws + L.rows);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
+  uint32_t* samp = reinterpret_cast<uint32_t*>(ws + L.samp);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + L.cnt);
+  uint32_t* above = reinterpret_cast<uint32_t*>(ws + L.above);
+  StreamBase* base = reinterpret_cast<StreamBase*>(ws + L.base);
+  uint2* list = reinterpret_cast<uint2*>(ws + L.list);
+  uint2* cand = reinterpret_cast<uint2*>(ws + L.cand);
+  const int64_t nbk = index_scan_blocks(T);
+  const int groups = (int)std::min<int64_t>(kStreamGroups, nbk);
+  const int bpw = (int)((nbk + groups - 1) / groups);
+  launch_index_sample_tau(q_idx, k_idx, R, T, row_seq, row_limit, k_pool, rows, hist, samp, s);
   if (scan_start && hipEventRecord((hipEvent_t)scan_start, s) != hipSuccess) return CSA2_ELAUNCH;
-  launch_index_scan(q_idx, k_idx, R, T, row_seq, row_limit, scores, hist0, s);
+  const CandOut co{rows, hist, cand, cnt, nbk};
+  launch_index_scan(q_idx, k_idx, R, T, row_seq, row_limit, scores, &co, s);
   if (scan_end && hipEventRecord((hipEvent_t)scan_end, s) != hipSuccess) return CSA2_ELAUNCH;
-  launch_compact(scores, R, T, T, k_pool, nullptr, pool_idx, pool_scores, k_top, top_idx, ws, s, true);
+  stream_gather_kernel<<<dim3(groups, R), kSG, 0, s>>>(nbk, bpw, rows, hist, cand, cnt, T, above, list, k_pool,
+                                                       k_top);
+  stream_finish_kernel<<<R, kSG, 0, s>>>(scores, T, bpw, groups, rows, hist, above, list, base, k_pool, k_top);
+  stream_write_kernel<<<dim3(groups, R), kSG, 0, s>>>(scores, T, nbk, bpw, rows, base, cand, cnt, k_pool, k_top,
+                                                      pool_idx, pool_scores, top_idx);
   return launch_status();
 }

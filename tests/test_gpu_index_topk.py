@@ -313,3 +313,71 @@ def test_index_full_pool_equals_separate_calls(R, T, k_pool, k_top):
     sh = s1[0].cpu().numpy().astype(np.float64)
     assert np.array_equal(p1[0].cpu().numpy(), OT.topk(sh, k_pool))
     assert np.array_equal(t1[0].cpu().numpy(), OT.topk(sh, k_top))
+
+
+def _stream_case_keys(kind, R, T, q, dev, S=4096):
+    """Index keys for the streaming selection's special cases (uint8 E4M3 codes [R, T, 64])."""
+    g = torch.Generator(device="cpu").manual_seed(71)
+    small = ((torch.randint(0, 256, (R, T, 64), generator=g, dtype=torch.uint8) & 0x87) | 0x08)
+    if kind == "fallback":
+        # strided positions carry the query itself (large positive score), the rest tiny keys:
+        # the sampled threshold lands above the k-th score and the row is rebuilt from its scores
+        k = small.clone()
+        i = torch.arange(S, dtype=torch.int64)
+        pos = ((2 * i + 1) * T) // (2 * S)
+        k[:, pos, :] = q.cpu()[:, None, :]
+        return k.to(dev)
+    if kind == "ties_all":
+        return q.cpu()[:, None, :].expand(R, T, 64).contiguous().to(dev)
+    if kind in ("ties_few", "ties_256"):
+        n = 16 if kind == "ties_few" else 256
+        pal = torch.randint(0, 256, (n, 64), generator=g, dtype=torch.uint8)
+        pal[(pal & 0x7F) == 0x7F] = 0
+        return pal[torch.randint(0, n, (R, T), generator=g)].to(dev)
+    if kind == "nan_keys":
+        k = torch.stack([W.fp8_normal(73, (T, 64), chunk_index=b) for b in range(R)])
+        nan_rows = torch.rand((R, T), generator=g) < 0.2
+        k[nan_rows, 5] = 0x7F
+        return k.to(dev)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["fallback", "ties_all", "ties_few", "ties_256", "nan_keys", "limits"])
+def test_index_full_pool_streaming_cases(kind):
+    """The streaming pool selection (sampled threshold, candidates from the scan, bitmap ordered
+    write) gives the same pool, pool scores and Top-K as csa2_index_full + csa2_topk_pool, and
+    the oracle's selection on sampled rows, when the threshold misses (fallback), under massive
+    ties (more candidates than fit in LDS; ties cut by position), with NaN keys and with row
+    limits (empty rows, rows shorter than the pool)."""
+    dev = device()
+    R, T, k_pool, k_top = 4, 131072, 16384, 2048
+    q = W.fp8_normal(72, (R, 64), device=dev)
+    lim = None
+    if kind == "limits":
+        k = torch.stack([W.fp8_normal(74, (T, 64), device=dev, chunk_index=b) for b in range(R)])
+        lim = torch.tensor([T - 1, 5000, -1, 40000], dtype=torch.int64, device=dev)
+    else:
+        k = _stream_case_keys(kind, R, T, q, dev)
+    s1 = torch.empty((R, T), dtype=torch.float32, device=dev)
+    p1 = torch.empty((R, k_pool), dtype=torch.int32, device=dev)
+    ps1 = torch.empty((R, k_pool), dtype=torch.float32, device=dev)
+    t1 = torch.empty((R, k_top), dtype=torch.int32, device=dev)
+    F.csa2_index_full_pool(q, k, s1, k_pool, k_top, p1, t1, pool_scores=ps1, row_limit=lim)
+    s2 = torch.empty_like(s1)
+    p2, ps2, t2 = torch.empty_like(p1), torch.empty_like(ps1), torch.empty_like(t1)
+    F.csa2_index_full(q, k, s2, row_limit=lim)
+    F.csa2_topk_pool(s2, k_pool, k_top, p2, t2, pool_scores=ps2)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.nan_to_num(s1, nan=7.0), torch.nan_to_num(s2, nan=7.0))
+    assert torch.equal(s1.isnan(), s2.isnan())
+    assert torch.equal(p1, p2) and torch.equal(t1, t2)
+    assert torch.equal(torch.nan_to_num(ps1, nan=7.0), torch.nan_to_num(ps2, nan=7.0))
+    for r in (0, R - 1):
+        sh = s1[r].cpu().numpy().astype(np.float64)
+        assert np.array_equal(p1[r].cpu().numpy(), OT.topk(sh, k_pool))
+        assert np.array_equal(t1[r].cpu().numpy(), OT.topk(sh, k_top))
+    if kind == "ties_all":
+        assert np.array_equal(p1.cpu().numpy(), np.tile(np.arange(k_pool, dtype=np.int32), (R, 1)))
+    if kind == "limits":
+        assert (p1[2] == -1).all() and (t1[2] == -1).all()
+        assert (p1[1, :5001] >= 0).all() and (p1[1, 5001:] == -1).all()
