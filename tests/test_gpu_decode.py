@@ -186,3 +186,38 @@ def test_chunked_prefill_sampled_rows():
         o_w, l_w = OA.attend(qf, OA.window_rows(bf16_to_f64(swa[0]), r, 128), SIGMA)
         o_ref, l_ref = OA.merge(o_s, l_s, o_w, l_w)
         assert_attention_close(o[r].cpu().numpy(), lse[r].cpu().numpy(), o_ref, l_ref, f"prefill row {r}")
+
+
+def test_decode_step_graph_replay_matches_eager():
+    """A whole 4-layer step (streaming Full-layer selection, Reindex, Reuse, one attention launch) captured
+    into a HIP graph: every replay, with eager steps and synchronizations between replays, reproduces the
+    eager outputs bit for bit (no memset or copy nodes are recorded: all clearing is done by kernels)."""
+    dev = device()
+    B, T, H, K, P = 2, 65536, 16, 256, 4096
+    modes = ("full", "reindex", "reuse", "reuse")
+    wl = DecodeWorkload(B, T, H, len(modes), seed=52)
+    stack = Csa2DecodeStack(B, T, H, K, modes, pool_size=P)
+    new = W.latent_rows(53, B, device=dev)
+    step = lambda: stack.step(wl.codes, wl.scales, wl.k_idx, wl.layers, SIGMA, new_rows=new)
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (stack.o, stack.lse, stack.idx[:2], stack.pool)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (stack.o, stack.lse, stack.idx, stack.pool):
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (stack.o, stack.lse, stack.idx[:2], stack.pool)
+        assert all(torch.equal(a, b) for a, b in zip(got, ref)), f"replay {rep}"
+        step()
+        torch.cuda.synchronize()
