@@ -70,11 +70,13 @@ def decode_step_bytes(B, T, H, K, P, modes, W=128):
     total = B * (2 * C + 288)                          # pack the current token's row
     for mode in modes:
         if mode == "full":
-            total += B * T * (64 + 4) + B * 64          # keys + score write + query
             if P:
-                total += B * T * 4 + B * P * 8 + B * K * 4   # one selection: read scores, write pool + scores, top-K
+                # keys + query read; pool (positions + scores) and Top-K written: the streaming selection
+                # needs no score array
+                total += B * T * 64 + B * 64 + B * P * 8 + B * K * 4
             else:
-                total += B * T * 4 + B * K * 4
+                # keys + query, scores written and read back by the selection, Top-K written
+                total += B * T * (64 + 4) + B * 64 + B * T * 4 + B * K * 4
         elif mode == "reindex":
             total += B * P * (4 + 64 + 4) + B * 64      # pool ids, gathered keys, scores
             total += B * P * 8 + B * K * 4
@@ -219,7 +221,9 @@ def bench_decode(args, cfg):
     B, T, H, K = cfg.batch, cfg.context, cfg.heads, cfg.topk
     P = min(cfg.pool, T) if "reindex" in cfg.modes else 0
     step_bytes = decode_step_bytes(B, T, H, K, P, cfg.modes, cfg.window)
-    idx_bytes = B * T * (64 + 4) + B * 64
+    # the Full-layer scan: 64-byte keys per position and the query; with a pool (streaming selection) it
+    # writes no scores, otherwise 4 bytes of score per position
+    idx_bytes = B * T * (64 if P else 64 + 4) + B * 64
     achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
     digest = kernel_source_digest(["index.hip", "common.hpp"])
     rec = {
@@ -239,7 +243,7 @@ def bench_decode(args, cfg):
                    "layers": list(cfg.modes), "pool": P, "window": cfg.window, "latent_channels": 512},
         "achieved_hbm_gbps": step_bytes / (ms * 1e-3) / 1e9,
         "step_algorithmic_bytes": step_bytes,
-        "roofline": {"kernel": "csa2_index_full_pool scan (index_stream_kernel<true>)", "bound": "hbm", "achieved": achieved,
+        "roofline": {"kernel": "csa2_index_full_pool scan (index_stream_kernel<true>, no score output)", "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic("index_full", digest),
                      "launch_ms": idx_ms, "bytes_per_launch": idx_bytes},

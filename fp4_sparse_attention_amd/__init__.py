@@ -407,19 +407,21 @@ def csa2_index_full_pool_workspace_size(R, T, k_pool):
 def csa2_index_full_pool(q_idx, k_idx, scores, k_pool, k_top, pool_idx, top_idx, pool_scores=None, row_seq=None,
                          row_limit=None, workspace=None, scan_events=None, stream=None):
     """Full-mode scores and the pool / Top-K selection in one call: q_idx uint8 [R, 64]; k_idx uint8 [B, T, 64];
-    scores fp32 [R, T] (written); pool_idx int32 [R, k_pool]; top_idx int32 [R, k_top];
-    pool_scores fp32 [R, k_pool] or None.  scan_events: an optional (start, end) pair of already-created
+    scores fp32 [R, T] (written) or None (not written: the selection needs no scores); pool_idx int32
+    [R, k_pool]; top_idx int32 [R, k_top]; pool_scores fp32 [R, k_pool] or None.  scan_events: an optional (start, end) pair of already-created
     torch.cuda.Event objects, recorded by the library around the scoring kernel."""
     _need(q_idx, torch.uint8, "q_idx", 2)
     _need(k_idx, torch.uint8, "k_idx", 3)
-    _need(scores, torch.float32, "scores", 2)
+    if scores is not None:
+        _need(scores, torch.float32, "scores", 2)
+        _dense(scores, "scores")
     _need(pool_idx, torch.int32, "pool_idx", 2)
     _need(top_idx, torch.int32, "top_idx", 2)
-    for t, nm in ((q_idx, "q_idx"), (k_idx, "k_idx"), (scores, "scores"), (pool_idx, "pool_idx"), (top_idx, "top_idx")):
+    for t, nm in ((q_idx, "q_idx"), (k_idx, "k_idx"), (pool_idx, "pool_idx"), (top_idx, "top_idx")):
         _dense(t, nm)
     R = q_idx.shape[0]
     B, T, d = k_idx.shape
-    if q_idx.shape[1] != 64 or d != 64 or scores.shape != (R, T):
+    if q_idx.shape[1] != 64 or d != 64 or (scores is not None and scores.shape != (R, T)):
         raise ValueError("index_full_pool shapes")
     if pool_idx.shape != (R, k_pool) or top_idx.shape != (R, k_top):
         raise ValueError("pool_idx / top_idx shape")
@@ -434,7 +436,7 @@ def csa2_index_full_pool(q_idx, k_idx, scores, k_pool, k_top, pool_idx, top_idx,
         _need(row_limit, torch.int64, "row_limit", 1)
     need = csa2_index_full_pool_workspace_size(R, T, k_pool)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=scores.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_idx.device)
     ev0 = ev1 = None
     if scan_events is not None:
         ev0, ev1 = (ctypes.c_void_p(int(e.cuda_event)) for e in scan_events)

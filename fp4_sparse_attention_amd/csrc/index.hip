@@ -26,43 +26,9 @@
 #include <algorithm>
 
 #include "internal.hpp"
+#include "tile.hpp"
 
 namespace csa2 {
-
-constexpr int kTile = 32;          // keys per MFMA tile
-constexpr int kUnroll = 4;         // tiles in flight per wave
-
-// 32 E4M3 bytes (8 dwords) -> four f16x8 MFMA operands, exact
-__device__ __forceinline__ void fp8x32_to_f16(const i32x8& v, f16x8* out) {
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    uint32_t w0 = (uint32_t)v[2 * ks], w1 = (uint32_t)v[2 * ks + 1];
-    f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
-    f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
-    f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
-    f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
-    out[ks] = f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-  }
-}
-
-// score tile: sum over the four 16-element k-steps of the lane's 32-byte half
-__device__ __forceinline__ f32x16 mfma_score(const f16x8* a, const i32x8& kb) {
-  f16x8 b[4];
-  fp8x32_to_f16(kb, b);
-  f32x16 acc = {};
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks], b[ks], acc, 0, 0, 0);
-  return acc;
-}
-
-__device__ __forceinline__ i32x8 load_half_key(const uint8_t* p) {
-  uint4 x = ld_nt16(p);
-  uint4 y = ld_nt16(p + 16);
-  i32x8 r;
-  r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
-  r[4] = y.x; r[5] = y.y; r[6] = y.z; r[7] = y.w;
-  return r;
-}
 
 // One query row per workgroup row (grid.y = R).  Used for decode (Full and
 // Reindex).  kGather: column c of row r scores position pool[r][c].
@@ -233,7 +199,7 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
   };
   auto flush = [&](int rr) {
     __syncthreads();
-    uint32_t* g = cand.hist + (int64_t)rr * kStreamBins;
+    uint32_t* g = cand.hist + (int64_t)rr * kStreamHistWords;
     const uint32_t n = n_used;
     for (uint32_t i = threadIdx.x; i < n; i += 256) {
       const uint32_t bin = used[i];
@@ -260,7 +226,7 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
     advance(rn, jn);
     if (rn < R) fetch(rn, jn, nxt);
     const int64_t t0 = tile_of(j);
-    float* out = scores + (int64_t)r * T;
+    float* out = scores ? scores + (int64_t)r * T : nullptr;
     uint32_t key[kUnroll];
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
@@ -268,7 +234,7 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
       const int64_t p = (t0 + i) * kTile + col_in_tile;
       key[i] = 0u;
       if (half == 0 && p < T) {
-        out[p] = cur.ok[i] ? acc[0] : neg_inf;
+        if (!kCand || scores) out[p] = cur.ok[i] ? acc[0] : neg_inf;
         if (kCand && cur.ok[i]) key[i] = score_key(acc[0]);
       }
     }
@@ -379,7 +345,7 @@ index_tau_kernel(const uint32_t* __restrict__ samp, int64_t T, const int64_t* __
   const int lane = tid & 63, wave = tid >> 6;
   const int64_t limit = row_limit ? row_limit[r] : T - 1;
   const int64_t V = limit < 0 ? 0 : (limit + 1 < T ? limit + 1 : T);
-  for (int i = tid; i < kStreamBins; i += 1024) hist[(int64_t)r * kStreamBins + i] = 0u;
+  for (int i = tid; i < kStreamHistWords; i += 1024) hist[(int64_t)r * kStreamHistWords + i] = 0u;
   const uint32_t m = sample_rank(k, V);
   if (m == 0u) {
     if (tid == 0) {

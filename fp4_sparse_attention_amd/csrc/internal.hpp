@@ -10,9 +10,12 @@ namespace csa2 {
 // score whose order-preserving key reaches the row's threshold tau_s, stores
 // the pair (key, position) at kp [r][128 b + i] in position order, with the
 // count of block b in cnt [r][b]; it also counts each candidate's digit
-// min((key - tau_s) >> sh, 4095) in hist [r][4096].
+// min((key - tau_s) >> sh, 4095) in hist [r][0 .. 4096).  hist [r][4096 .. 8192)
+// is the selection's second histogram (the top 12 bits of every visible key,
+// filled only when a row is rebuilt).
 constexpr int kBlockPositions = 128;
 constexpr int kStreamBins = 4096;
+constexpr int kStreamHistWords = 2 * kStreamBins;   // per row
 
 struct StreamRow {
   uint32_t tau_s;       // candidate threshold; 0 = every visible position
@@ -29,13 +32,14 @@ struct StreamRow {
 
 struct CandOut {
   StreamRow* row;
-  uint32_t* hist;       // [R][kStreamBins], zero before the scan
+  uint32_t* hist;       // [R][kStreamHistWords], zero before the scan
   uint2* kp;            // [R][T] (key, position)
   uint32_t* cnt;        // [R][n_blocks]
   int64_t n_blocks;     // blocks per row the scan writes counts for (4 per 512-position unit)
 };
 
-// Full-mode index scan on `s`; with cand, also emits the candidates.
+// Full-mode index scan on `s`; with cand, also emits the candidates (and then
+// scores may be null: no scores are written).
 void launch_index_scan(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int64_t T, const int32_t* row_seq,
                        const int64_t* row_limit, float* scores, const CandOut* cand, hipStream_t s);
 

@@ -30,6 +30,7 @@
 #include <algorithm>
 
 #include "internal.hpp"
+#include "tile.hpp"
 
 namespace csa2 {
 
@@ -1027,10 +1028,14 @@ topk_write_cand_kernel(int64_t N, const uint32_t* __restrict__ cand_key, const i
 //    output base (keys above tau and ties at tau in the blocks before it);
 //  - write: each workgroup writes its selected candidates in position order,
 //    ties at tau to the lowest positions.
-// The result does not depend on tau_s.  When fewer than k candidates arrive
-// (tau_s was above the k-th key) or a boundary bin overflows its list (massive
-// ties), the finish workgroup selects from the row's scores instead and the
-// write pass reads the scores too.  (The passes are separate launches: a
+// The result does not depend on tau_s and needs no scores (the call may skip
+// writing them).  When fewer than k candidates arrive (tau_s was above the k-th
+// key), the row is rebuilt: each gather workgroup rescores its positions with
+// the scan's tile arithmetic and stores every visible key in its blocks, with a
+// histogram of their top 12 bits; the finish workgroup then selects by radix
+// passes over the blocks.  When a boundary bin overflows its list (massive
+// ties), the blocks already hold every candidate and the finish workgroup
+// selects by radix passes over them.  (The passes are separate launches: a
 // device-scope fence per workgroup, to let the last gather workgroup finish the
 // row, costs more than a launch here, and so does resolving the row again in
 // every write workgroup.)
@@ -1128,49 +1133,33 @@ __device__ __forceinline__ BlockHead load_head(const uint2* kp, const uint32_t* 
   return h;
 }
 
-// entries of block blk in position order, f(key, position): from the candidate
-// block (mode 0; hd = its head) or every visible position of the block from the
-// scores row (mode 1)
+// candidates of block blk in position order, f(key, position); hd = its head
 template <class F>
-__device__ __forceinline__ void for_block(uint32_t mode, const BlockHead& hd, const float* row, int64_t T,
-                                          const uint2* kp, int64_t blk, F&& f) {
-  if (mode == 0u) {
+__device__ __forceinline__ void for_block(const BlockHead& hd, const uint2* kp, int64_t blk, F&& f) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if ((uint32_t)(2 * u) < hd.c) f(hd.e[u].x, (int32_t)hd.e[u].y);
-      if ((uint32_t)(2 * u + 1) < hd.c) f(hd.e[u].z, (int32_t)hd.e[u].w);
-    }
-    const uint4* b = reinterpret_cast<const uint4*>(kp + blk * kBlockPositions);
-    for (uint32_t e = 8; e < hd.c; e += 2) {
-      const uint4 v = b[e / 2];
-      f(v.x, (int32_t)v.y);
-      if (e + 1 < hd.c) f(v.z, (int32_t)v.w);
-    }
-  } else {
-    const int64_t p0 = blk * kBlockPositions;
-    const int64_t p1 = min(T, p0 + kBlockPositions);
-    for (int64_t i = p0; i < p1; i += 4) {
-      const float4 v = *reinterpret_cast<const float4*>(row + i);
-      const float f4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t kx = score_key(f4[q]);
-        if (kx != 0u) f(kx, (int32_t)(i + q));
-      }
-    }
+  for (int u = 0; u < 4; ++u) {
+    if ((uint32_t)(2 * u) < hd.c) f(hd.e[u].x, (int32_t)hd.e[u].y);
+    if ((uint32_t)(2 * u + 1) < hd.c) f(hd.e[u].z, (int32_t)hd.e[u].w);
+  }
+  const uint4* b = reinterpret_cast<const uint4*>(kp + blk * kBlockPositions);
+  for (uint32_t e = 8; e < hd.c; e += 2) {
+    const uint4 v = b[e / 2];
+    f(v.x, (int32_t)v.y);
+    if (e + 1 < hd.c) f(v.z, (int32_t)v.w);
   }
 }
 
 // C = the row's candidate count, each selection's k_eff, boundary bin b0, the
-// candidates above it (above) and in it (cb0), and whether the row must be
-// selected from its scores; 256 threads, bins walked from the top
+// candidates above it (above) and in it (cb0); rebuild: fewer than k
+// candidates (tau_s above the k-th key); overflow: a boundary bin holds more
+// than a list takes.  256 threads, bins walked from the top.
 struct RowBins {
   uint32_t C, k_eff[2], b0[2], above[2], cb0[2];
-  bool fallback;
+  bool rebuild, overflow;
 };
 
-__device__ __forceinline__ RowBins row_bins(const uint32_t* hr, uint32_t tau_s, int32_t k, int32_t k2, uint32_t* tmp,
-                                            uint32_t* s_b /* 6 */) {
+__device__ __forceinline__ void bins_from_top(const uint32_t* hr, const uint32_t* need, uint32_t* tmp, uint32_t* s_b,
+                                              uint32_t& total) {
   const int tid = threadIdx.x;
   constexpr int kPer = kStreamBins / kSG;
   uint32_t c[kPer], local = 0;
@@ -1179,68 +1168,125 @@ __device__ __forceinline__ RowBins row_bins(const uint32_t* hr, uint32_t tau_s, 
     c[j] = hr[kStreamBins - 1 - kPer * tid - j];
     local += c[j];
   }
-  RowBins rb;
-  const uint32_t excl = block_exclusive_scan(local, tmp, rb.C);
-  const uint32_t kk[2] = {(uint32_t)k, (uint32_t)k2};
-#pragma unroll
-  for (int s = 0; s < 2; ++s) rb.k_eff[s] = tau_s == 0u ? min(kk[s], rb.C) : kk[s];
+  const uint32_t excl = block_exclusive_scan(local, tmp, total);
   if (tid == 0)
     for (int i = 0; i < 6; ++i) s_b[i] = 0u;
   __syncthreads();
-  rb.fallback = tau_s != 0u && rb.C < kk[0];
-  if (!rb.fallback) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const uint32_t need = rb.k_eff[s];
-      if (need > 0u && excl < need && need <= excl + local) {
-        uint32_t acc = excl;
+  for (int s = 0; s < 2; ++s) {
+    const uint32_t nd = min(need[s], total);
+    if (nd > 0u && excl < nd && nd <= excl + local) {
+      uint32_t acc = excl;
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-          if (acc < need && need <= acc + c[j]) {
-            s_b[3 * s] = (uint32_t)(kStreamBins - 1 - kPer * tid - j);
-            s_b[3 * s + 1] = acc;
-            s_b[3 * s + 2] = c[j];
-          }
-          acc += c[j];
+      for (int j = 0; j < kPer; ++j) {
+        if (acc < nd && nd <= acc + c[j]) {
+          s_b[3 * s] = (uint32_t)(kStreamBins - 1 - kPer * tid - j);
+          s_b[3 * s + 1] = acc;
+          s_b[3 * s + 2] = c[j];
         }
+        acc += c[j];
       }
     }
   }
   __syncthreads();
+}
+
+__device__ __forceinline__ RowBins row_bins(const uint32_t* hr, uint32_t tau_s, int32_t k, int32_t k2, uint32_t* tmp,
+                                            uint32_t* s_b /* 6 */) {
+  const uint32_t kk[2] = {(uint32_t)k, (uint32_t)k2};
+  RowBins rb;
+  bins_from_top(hr, kk, tmp, s_b, rb.C);
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
+    rb.k_eff[s] = tau_s == 0u ? min(kk[s], rb.C) : kk[s];
     rb.b0[s] = s_b[3 * s];
     rb.above[s] = s_b[3 * s + 1];
     rb.cb0[s] = s_b[3 * s + 2];
   }
   __syncthreads();
-  if (!rb.fallback && rb.k_eff[0] > 0u) rb.fallback = rb.cb0[0] > (uint32_t)kListCap || rb.cb0[1] > (uint32_t)kListCap;
+  rb.rebuild = tau_s != 0u && rb.C < kk[0];
+  rb.overflow = !rb.rebuild && rb.k_eff[0] > 0u &&
+                (rb.cb0[0] > (uint32_t)kListCap || rb.cb0[1] > (uint32_t)kListCap);
   return rb;
 }
 
+// Rebuild of a row whose threshold missed: the workgroup's blocks get every
+// visible key of their positions (scored as in the scan: wave w takes blocks
+// blk0 + w, blk0 + w + 4, ...), and hist_abs the top 12 bits of those keys.
+__device__ void rebuild_blocks(const uint8_t* q_idx, const uint8_t* k_idx, int64_t T, int r, const int32_t* row_seq,
+                               const int64_t* row_limit, int64_t blk0, int64_t blk1, uint2* kp, uint32_t* cn,
+                               uint32_t* hist_abs, uint32_t* h /* 4096, LDS */) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int half = lane >> 5, col = lane & 31;
+  for (int i = tid; i < kStreamBins; i += kSG) h[i] = 0u;
+  __syncthreads();
+  const int seq = row_seq ? row_seq[r] : r;
+  const int64_t limit = row_limit ? row_limit[r] : T - 1;
+  const uint8_t* kseq = k_idx + (int64_t)seq * T * kIndexDim;
+  f16x8 a[4];
+  query_operands(q_idx + (int64_t)r * kIndexDim, lane, a);
+  for (int64_t blk = blk0 + wave; blk < blk1; blk += 4) {
+    i32x8 kb[4];
+    bool ok[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t p = blk * kBlockPositions + 32 * i + col;
+      ok[i] = p < T && p <= limit;
+      kb[i] = ok[i] ? load_half_key(kseq + p * kIndexDim + 32 * half) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+    uint32_t at = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x16 acc = mfma_score(a, kb[i]);
+      const uint32_t key = (half == 0 && ok[i]) ? score_key(acc[0]) : 0u;
+      const bool c = key != 0u;
+      const uint64_t m = __ballot(c);
+      if (c) {
+        kp[blk * kBlockPositions + at + lanes_below(m)] =
+            make_uint2(key, (uint32_t)(blk * kBlockPositions + 32 * i + col));
+        atomicAdd(&h[key >> 20], 1u);
+      }
+      at += (uint32_t)__popcll(m);
+    }
+    if (lane == 0) cn[blk] = at;
+  }
+  __syncthreads();
+  for (int i = tid; i < kStreamBins; i += kSG)
+    if (h[i]) atomicAdd(&hist_abs[i], h[i]);
+}
+
 // gather: per workgroup, the candidates above each boundary bin in its blocks,
-// and the candidates inside the boundary bin appended to the row's short list
+// and the candidates inside the boundary bin appended to the row's short list;
+// in a row to rebuild, the rebuild of its blocks instead
 __global__ void __launch_bounds__(kSG)
-stream_gather_kernel(int64_t nbk, int bpw, StreamRow* __restrict__ rows, const uint32_t* __restrict__ hist,
-                     const uint2* __restrict__ cand, const uint32_t* __restrict__ cand_cnt, int64_t T,
-                     uint32_t* __restrict__ above_out, uint2* __restrict__ list, int32_t k, int32_t k2) {
+stream_gather_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx, int64_t T,
+                     const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit, int64_t nbk, int bpw,
+                     StreamRow* __restrict__ rows, uint32_t* __restrict__ hist, uint2* __restrict__ cand,
+                     uint32_t* __restrict__ cand_cnt, uint32_t* __restrict__ above_out, uint2* __restrict__ list,
+                     int32_t k, int32_t k2) {
   __shared__ uint32_t tmp[8];
   __shared__ uint32_t s_b[6];
+  __shared__ uint32_t h[kStreamBins];
   const int r = blockIdx.y, g = blockIdx.x, G = gridDim.x, tid = threadIdx.x;
   const int R = gridDim.y;
   const uint32_t tau_s = rows[r].tau_s, sh = rows[r].sh;
-  const uint2* kp = cand + (int64_t)r * T;
-  const uint32_t* cn = cand_cnt + (int64_t)r * nbk;
+  uint2* kp = cand + (int64_t)r * T;
+  uint32_t* cn = cand_cnt + (int64_t)r * nbk;
+  uint32_t* hr = hist + (int64_t)r * kStreamHistWords;
   // the first block's head is loaded with the histogram
   const int64_t blk0 = (int64_t)g * bpw, blk1 = min(nbk, blk0 + bpw);
   BlockHead hd0 = {};
   if (blk0 + tid < blk1) hd0 = load_head(kp, cn, blk0 + tid);
-  const RowBins rb = row_bins(hist + (int64_t)r * kStreamBins, tau_s, k, k2, tmp, s_b);
-  if (rb.fallback || rb.k_eff[0] == 0u) return;
+  const RowBins rb = row_bins(hr, tau_s, k, k2, tmp, s_b);
+  if (rb.rebuild) {
+    rebuild_blocks(q_idx, k_idx, T, r, row_seq, row_limit, blk0, blk1, kp, cn, hr + kStreamBins, h);
+    return;
+  }
+  if (rb.overflow || rb.k_eff[0] == 0u) return;
   uint32_t ab[2] = {0u, 0u};
   for (int64_t blk = blk0 + tid; blk < blk1; blk += kSG) {
     const BlockHead hd = blk == blk0 + tid ? hd0 : load_head(kp, cn, blk);
-    for_block(0u, hd, nullptr, T, kp, blk, [&](uint32_t kx, int32_t p) {
+    for_block(hd, kp, blk, [&](uint32_t kx, int32_t p) {
       const uint32_t d = min((kx - tau_s) >> sh, (uint32_t)(kStreamBins - 1));
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -1260,15 +1306,71 @@ stream_gather_kernel(int64_t nbk, int bpw, StreamRow* __restrict__ rows, const u
   }
 }
 
+// the need-th largest key among a row's candidate blocks that pass `keep`,
+// starting from a known prefix: radix digits of the bits below bit `hi`
+// (11 bits and then 10 at a time), prefix bits at and above `hi` must match.
+// Returns tau; need becomes the number of keys equal to tau to take.
+template <class Keep>
+__device__ uint32_t select_in_blocks(const uint2* kp, const uint32_t* cn, int64_t nbk, Keep keep, int hi,
+                                     uint32_t prefix, uint32_t& need, uint32_t* h /* 2048 */, uint32_t* tmp,
+                                     uint32_t* res) {
+  const int tid = threadIdx.x;
+#pragma unroll 1
+  while (hi > 0) {
+    const int width = hi > 10 ? (hi >= 21 ? 11 : hi - 10) : hi;
+    const int shift = hi - width;
+    const uint32_t mask = (1u << width) - 1u;
+    const int nb = 1 << width;
+    for (int i = tid; i < nb; i += kSG) h[i] = 0u;
+    __syncthreads();
+    for (int64_t blk = tid; blk < nbk; blk += kSG) {
+      const BlockHead hd = load_head(kp, cn, blk);
+      for_block(hd, kp, blk, [&](uint32_t kx, int32_t) {
+        if (keep(kx) && (hi >= 32 || (kx >> hi) == (prefix >> hi))) atomicAdd(&h[(kx >> shift) & mask], 1u);
+      });
+    }
+    __syncthreads();
+    // bins from the top, nb / 256 (at least 1) per thread
+    const int per = nb >= kSG ? nb / kSG : 1;
+    uint32_t local = 0;
+    for (int j = 0; j < per; ++j) {
+      const int bin = nb - 1 - per * tid - j;
+      local += bin >= 0 ? h[bin] : 0u;
+    }
+    uint32_t total;
+    const uint32_t excl = block_exclusive_scan(local, tmp, total);
+    if (excl < need && need <= excl + local) {
+      uint32_t acc = excl;
+      for (int j = 0; j < per; ++j) {
+        const int bin = nb - 1 - per * tid - j;
+        const uint32_t c = bin >= 0 ? h[bin] : 0u;
+        if (acc < need && need <= acc + c) {
+          res[0] = (uint32_t)bin;
+          res[1] = acc;
+        }
+        acc += c;
+      }
+    }
+    __syncthreads();
+    prefix |= res[0] << shift;
+    need -= res[1];
+    hi = shift;
+    __syncthreads();
+  }
+  return prefix;
+}
+
 // finish: one workgroup per row.  From the short lists: each selection's k-th
 // key tau (kth_largest_256), the ties at tau it takes, and for every gather
-// workgroup the keys above tau and equal to tau in the blocks before it.  In
-// fallback rows the same from the whole scores row: the k-th keys by three
-// radix digits, the per-workgroup counts by a pass over the positions.
+// workgroup the keys above tau and equal to tau in the blocks before it.  In a
+// rebuilt or overflowing row, the k-th keys by radix passes over the blocks and
+// the per-workgroup counts by a pass over them.
 __global__ void __launch_bounds__(kSG)
-stream_finish_kernel(const float* __restrict__ scores, int64_t T, int bpw, int G, StreamRow* __restrict__ rows,
+stream_finish_kernel(int64_t T, int64_t nbk, int bpw, int G, StreamRow* __restrict__ rows,
                      const uint32_t* __restrict__ hist, const uint32_t* __restrict__ above_out,
-                     const uint2* __restrict__ list, StreamBase* __restrict__ base_out, int32_t k, int32_t k2) {
+                     const uint2* __restrict__ list, const uint2* __restrict__ cand,
+                     const uint32_t* __restrict__ cand_cnt, StreamBase* __restrict__ base_out, int32_t k,
+                     int32_t k2) {
   __shared__ uint32_t tmp[8];
   __shared__ uint32_t s_b[6];
   __shared__ uint32_t res[2];
@@ -1278,7 +1380,9 @@ stream_finish_kernel(const float* __restrict__ scores, int64_t T, int bpw, int G
   const int r = blockIdx.x, tid = threadIdx.x;
   const int R = gridDim.x;
   const StreamRow st = rows[r];
-  const float* row = scores + (int64_t)r * T;
+  const uint32_t* hr = hist + (int64_t)r * kStreamHistWords;
+  const uint2* kp = cand + (int64_t)r * T;
+  const uint32_t* cn = cand_cnt + (int64_t)r * nbk;
   // entry tid of each list and workgroup tid's gather counts, loaded with the histogram
   uint2 le0[2];
   uint32_t ab0[2];
@@ -1287,12 +1391,14 @@ stream_finish_kernel(const float* __restrict__ scores, int64_t T, int bpw, int G
     le0[s] = list[((int64_t)s * R + r) * kListCap + tid];
     ab0[s] = tid < G ? above_out[((int64_t)r * G + tid) * 2 + s] : 0u;
   }
-  const RowBins rb = row_bins(hist + (int64_t)r * kStreamBins, st.tau_s, k, k2, tmp, s_b);
+  const RowBins rb = row_bins(hr, st.tau_s, k, k2, tmp, s_b);
   StreamBase* bo = base_out + (int64_t)r * G;
+  const uint32_t kk[2] = {(uint32_t)k, (uint32_t)k2};
   uint32_t tau[2] = {0u, 0u}, need_eq[2] = {0u, 0u}, k_eff[2] = {rb.k_eff[0], rb.k_eff[1]};
-  if (!rb.fallback && rb.k_eff[0] == 0u) {
+  const uint32_t mode = rb.rebuild ? 1u : (rb.overflow ? 2u : 0u);
+  if (mode == 0u && rb.k_eff[0] == 0u) {
     for (int i = tid; i < G; i += kSG) bo[i] = StreamBase{{0u, 0u}, {0u, 0u}};
-  } else if (!rb.fallback) {
+  } else if (mode == 0u) {
 #pragma unroll 1
     for (int s = 0; s < 2; ++s) {
       const uint32_t n = st.n_list[s];
@@ -1324,107 +1430,55 @@ stream_finish_kernel(const float* __restrict__ scores, int64_t T, int bpw, int G
       __syncthreads();
     }
   } else {
-    // every visible position of the row: 12-bit histogram of all keys, the
-    // k-th key of each selection by two more digits, per-workgroup counts
-    constexpr int kPer = kStreamBins / kSG;
-    for (int i = tid; i < kStreamBins; i += kSG) h[i] = 0u;
-    __syncthreads();
-    for (int64_t i = 4 * (int64_t)tid; i < T; i += 4 * kSG) {
-      const float4 v = *reinterpret_cast<const float4*>(row + i);
-      const float f4[4] = {v.x, v.y, v.z, v.w};
+    uint32_t b0[2], above[2];
+    if (mode == 1u) {
+      // every visible key is in the blocks; the second histogram holds their top 12 bits
+      uint32_t V;
+      bins_from_top(hr + kStreamBins, kk, tmp, s_b, V);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t kx = score_key(f4[q]);
-        if (kx != 0u) atomicAdd(&h[kx >> 20], 1u);
+      for (int s = 0; s < 2; ++s) {
+        k_eff[s] = min(kk[s], V);
+        b0[s] = s_b[3 * s];
+        above[s] = s_b[3 * s + 1];
+      }
+      __syncthreads();
+    } else {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        b0[s] = rb.b0[s];
+        above[s] = rb.above[s];
       }
     }
-    __syncthreads();
-    uint32_t V;
-    {
-      uint32_t loc = 0;
-      for (int j = 0; j < kPer; ++j) loc += h[kPer * tid + j];
-      block_exclusive_scan(loc, tmp, V);
-    }
-    const uint32_t kk[2] = {(uint32_t)k, (uint32_t)k2};
-#pragma unroll
-    for (int s = 0; s < 2; ++s) k_eff[s] = min(kk[s], V);
     if (k_eff[0] == 0u) {
       for (int i = tid; i < G; i += kSG) bo[i] = StreamBase{{0u, 0u}, {0u, 0u}};
     } else {
-      uint32_t prefix[2], need[2];
+      const uint32_t tau_s = st.tau_s, sh = st.sh;
 #pragma unroll 1
       for (int s = 0; s < 2; ++s) {
-        uint32_t lc[kPer], lsum = 0;
-        for (int j = 0; j < kPer; ++j) { lc[j] = h[kStreamBins - 1 - kPer * tid - j]; lsum += lc[j]; }
-        uint32_t tot;
-        const uint32_t ex = block_exclusive_scan(lsum, tmp, tot);
-        if (ex < k_eff[s] && k_eff[s] <= ex + lsum) {
-          uint32_t acc = ex;
-          for (int j = 0; j < kPer; ++j) {
-            if (acc < k_eff[s] && k_eff[s] <= acc + lc[j]) { res[0] = kStreamBins - 1 - kPer * tid - j; res[1] = acc; }
-            acc += lc[j];
-          }
-        }
-        __syncthreads();
-        prefix[s] = res[0] << 20;
-        need[s] = k_eff[s] - res[1];
-        __syncthreads();
+        uint32_t need = k_eff[s] - above[s];
+        const uint32_t bs = b0[s];
+        if (mode == 1u)
+          tau[s] = select_in_blocks(kp, cn, nbk, [](uint32_t) { return true; }, 20, bs << 20, need, h, tmp, res);
+        else
+          tau[s] = select_in_blocks(
+              kp, cn, nbk, [=](uint32_t kx) { return min((kx - tau_s) >> sh, (uint32_t)(kStreamBins - 1)) == bs; },
+              32, 0u, need, h, tmp, res);
+        need_eq[s] = need;
       }
-#pragma unroll 1
-      for (int s = 0; s < 2; ++s) {
-#pragma unroll 1
-        for (int d = 1; d <= 2; ++d) {
-          const int shift = d == 1 ? 10 : 0, hi = d == 1 ? 20 : 10;
-          for (int i = tid; i < 1024; i += kSG) s_lk[i] = 0u;
-          __syncthreads();
-          for (int64_t i = 4 * (int64_t)tid; i < T; i += 4 * kSG) {
-            const float4 v = *reinterpret_cast<const float4*>(row + i);
-            const float f4[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const uint32_t kx = score_key(f4[q]);
-              if (kx != 0u && (kx >> hi) == (prefix[s] >> hi)) atomicAdd(&s_lk[(kx >> shift) & 1023u], 1u);
-            }
-          }
-          __syncthreads();
-          uint32_t lc[4], lsum = 0;
-          for (int j = 0; j < 4; ++j) { lc[j] = s_lk[1023 - 4 * tid - j]; lsum += lc[j]; }
-          uint32_t tot;
-          const uint32_t ex = block_exclusive_scan(lsum, tmp, tot);
-          if (ex < need[s] && need[s] <= ex + lsum) {
-            uint32_t acc = ex;
-            for (int j = 0; j < 4; ++j) {
-              if (acc < need[s] && need[s] <= acc + lc[j]) { res[0] = 1023 - 4 * tid - j; res[1] = acc; }
-              acc += lc[j];
-            }
-          }
-          __syncthreads();
-          prefix[s] |= res[0] << shift;
-          need[s] -= res[1];
-          __syncthreads();
-        }
-        tau[s] = prefix[s];
-        need_eq[s] = need[s];
-      }
-      // per-workgroup counts of keys > tau and == tau (thread-contiguous position runs)
+      // keys > tau and == tau in each gather workgroup's blocks, then the bases
 #pragma unroll 1
       for (int s = 0; s < 2; ++s) {
         for (int i = tid; i < G; i += kSG) { s_gt[i] = 0u; s_eq[i] = 0u; }
         __syncthreads();
-        const int64_t run = (T + kSG - 1) / kSG;
-        const int64_t i0 = min(T, (int64_t)tid * run), i1 = min(T, i0 + run);
-        uint32_t wg_cur = 0xFFFFFFFFu, gt = 0u, eq = 0u;
-        for (int64_t i = i0; i < i1; ++i) {
-          const uint32_t wg = (uint32_t)((i / kBlockPositions) / bpw);
-          if (wg != wg_cur) {
-            if (wg_cur != 0xFFFFFFFFu) { atomicAdd(&s_gt[wg_cur], gt); atomicAdd(&s_eq[wg_cur], eq); }
-            wg_cur = wg; gt = 0u; eq = 0u;
-          }
-          const uint32_t kx = score_key(row[i]);
-          gt += kx > tau[s];
-          eq += kx == tau[s];
+        for (int64_t blk = tid; blk < nbk; blk += kSG) {
+          uint32_t gt = 0u, eq = 0u;
+          for_block(load_head(kp, cn, blk), kp, blk, [&](uint32_t kx, int32_t) {
+            gt += kx > tau[s];
+            eq += kx == tau[s];
+          });
+          if (gt) atomicAdd(&s_gt[blk / bpw], gt);
+          if (eq) atomicAdd(&s_eq[blk / bpw], eq);
         }
-        if (wg_cur != 0xFFFFFFFFu) { atomicAdd(&s_gt[wg_cur], gt); atomicAdd(&s_eq[wg_cur], eq); }
         __syncthreads();
         if (tid < 64) {
           const uint32_t gtc = tid < G ? s_gt[tid] : 0u;
@@ -1441,7 +1495,7 @@ stream_finish_kernel(const float* __restrict__ scores, int64_t T, int bpw, int G
   }
   if (tid == 0) {
     StreamRow* o = &rows[r];
-    o->mode = rb.fallback ? 1u : 0u;
+    o->mode = mode;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       o->tau[s] = tau[s];
@@ -1453,13 +1507,12 @@ stream_finish_kernel(const float* __restrict__ scores, int64_t T, int bpw, int G
 
 // ordered write: each workgroup's blocks, thread t taking a contiguous run of them
 __global__ void __launch_bounds__(kSG)
-stream_write_kernel(const float* __restrict__ scores, int64_t T, int64_t nbk, int bpw,
-                    const StreamRow* __restrict__ rows, const StreamBase* __restrict__ base,
-                    const uint2* __restrict__ cand, const uint32_t* __restrict__ cand_cnt, int32_t k, int32_t k2,
-                    int32_t* __restrict__ idx_out, float* __restrict__ score_out, int32_t* __restrict__ idx2_out) {
+stream_write_kernel(int64_t T, int64_t nbk, int bpw, const StreamRow* __restrict__ rows,
+                    const StreamBase* __restrict__ base, const uint2* __restrict__ cand,
+                    const uint32_t* __restrict__ cand_cnt, int32_t k, int32_t k2, int32_t* __restrict__ idx_out,
+                    float* __restrict__ score_out, int32_t* __restrict__ idx2_out) {
   __shared__ uint32_t tmp[8];
   const int r = blockIdx.y, g = blockIdx.x, G = gridDim.x, tid = threadIdx.x;
-  const float* row = scores + (int64_t)r * T;
   const uint2* kp = cand + (int64_t)r * T;
   const uint32_t* cn = cand_cnt + (int64_t)r * nbk;
   const int64_t blk0 = (int64_t)g * bpw, blk1 = min(nbk, blk0 + bpw);
@@ -1483,7 +1536,7 @@ stream_write_kernel(const float* __restrict__ scores, int64_t T, int64_t nbk, in
   if (st.k_eff[0] == 0u) return;
   uint32_t gt[2] = {0u, 0u}, eq[2] = {0u, 0u};
   for (int64_t blk = my0; blk < my1; ++blk)
-    for_block(st.mode, blk == my0 ? hd0 : load_head(kp, cn, blk), row, T, kp, blk, [&](uint32_t kx, int32_t) {
+    for_block(blk == my0 ? hd0 : load_head(kp, cn, blk), kp, blk, [&](uint32_t kx, int32_t) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         gt[s] += kx > st.tau[s];
@@ -1498,7 +1551,7 @@ stream_write_kernel(const float* __restrict__ scores, int64_t T, int64_t nbk, in
     es[s] = bs.eq[s] + block_exclusive_scan(eq[s], tmp, tot);
   }
   for (int64_t blk = my0; blk < my1; ++blk)
-    for_block(st.mode, blk == my0 ? hd0 : load_head(kp, cn, blk), row, T, kp, blk, [&](uint32_t kx, int32_t p) {
+    for_block(blk == my0 ? hd0 : load_head(kp, cn, blk), kp, blk, [&](uint32_t kx, int32_t p) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const bool is_gt = kx > st.tau[s], is_eq = kx == st.tau[s];
@@ -1523,7 +1576,7 @@ static StreamLayout stream_layout(int32_t R, int64_t T) {
   const int64_t nbk = index_scan_blocks(T);
   size_t off = 0;
   L.rows = off; off += align_up((size_t)R * sizeof(StreamRow), 256);
-  L.hist = off; off += align_up((size_t)R * kStreamBins * 4, 256);
+  L.hist = off; off += align_up((size_t)R * kStreamHistWords * 4, 256);
   L.samp = off; off += align_up((size_t)R * index_sample_words() * 4, 256);
   L.cnt = off; off += align_up((size_t)R * nbk * 4, 256);
   L.above = off; off += align_up((size_t)R * kStreamGroups * 2 * 4, 256);
@@ -1736,9 +1789,21 @@ extern "C" csa2_status csa2_topk_pool(const float* scores, int32_t R, int64_t N,
   return launch_status();
 }
 
+// Whether csa2_index_full_pool can take its streaming path for this shape, and
+// the scratch it needs for scores when the caller passes none and the path is
+// not the streaming one.
+static bool pool_may_stream(int32_t R, int64_t T) { return choose_path(R, T) == kCompact; }
+
+static size_t pool_scores_scratch(int32_t R, int64_t T) {
+  // rows of up to 32 with a compact-path length always stream
+  if (pool_may_stream(R, T) && R < 32) return 0;
+  return align_up((size_t)R * T * 4, 256);
+}
+
 extern "C" size_t csa2_index_full_pool_workspace_size(int32_t R, int64_t T, int32_t k_pool) {
   if (R <= 0 || T <= 0) return 0;
-  return std::max(csa2_topk_workspace_size(R, T, k_pool), stream_layout(R, T).total);
+  const size_t other = align_up(csa2_topk_workspace_size(R, T, k_pool), 256) + pool_scores_scratch(R, T);
+  return std::max(other, pool_may_stream(R, T) ? stream_layout(R, T).total : (size_t)0);
 }
 
 extern "C" csa2_status csa2_index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int32_t B,
@@ -1747,24 +1812,27 @@ extern "C" csa2_status csa2_index_full_pool(const uint8_t* q_idx, const uint8_t*
                                             float* pool_scores, int32_t* top_idx, void* workspace,
                                             size_t workspace_bytes, void* scan_start, void* scan_end,
                                             void* stream) {
-  if (!q_idx || !k_idx || !scores || !pool_idx || !top_idx) return CSA2_EINVAL;
+  if (!q_idx || !k_idx || !pool_idx || !top_idx) return CSA2_EINVAL;
   if (R <= 0 || B <= 0 || T <= 0 || k_pool <= 0 || k_top <= 0 || k_top > k_pool) return CSA2_EINVAL;
   if (!row_seq && R != B) return CSA2_EINVAL;
   if (T % 4 != 0 || T >= (int64_t(1) << 31)) return CSA2_ESHAPE;
-  if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(scores, 16) || !aligned(pool_idx, 4) ||
+  if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || (scores && !aligned(scores, 16)) || !aligned(pool_idx, 4) ||
       !aligned(top_idx, 4) || (pool_scores && !aligned(pool_scores, 4)))
     return CSA2_EALIGN;
   if (!workspace || workspace_bytes < csa2_index_full_pool_workspace_size(R, T, k_pool)) return CSA2_EWORKSPACE;
   if (!aligned(workspace, 256)) return CSA2_EALIGN;
   hipStream_t s = (hipStream_t)stream;
-  if (choose_path(R, T) != kCompact || !index_scan_streams(R, row_seq)) {
-    // short rows, very long R x T, or query blocks: scores first, then the selection
+  if (!pool_may_stream(R, T) || !index_scan_streams(R, row_seq)) {
+    // short rows, very long R x T, or query blocks: scores first (into the
+    // workspace when the caller takes none), then the selection
+    const size_t tk = align_up(csa2_topk_workspace_size(R, T, k_pool), 256);
+    float* sc = scores ? scores : reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + tk);
     if (scan_start && hipEventRecord((hipEvent_t)scan_start, s) != hipSuccess) return CSA2_ELAUNCH;
-    csa2_status st = csa2_index_full(q_idx, k_idx, R, B, T, row_seq, row_limit, scores, stream);
+    csa2_status st = csa2_index_full(q_idx, k_idx, R, B, T, row_seq, row_limit, sc, stream);
     if (st != CSA2_OK) return st;
     if (scan_end && hipEventRecord((hipEvent_t)scan_end, s) != hipSuccess) return CSA2_ELAUNCH;
-    return csa2_topk_pool(scores, R, T, T, k_pool, k_top, nullptr, pool_idx, pool_scores, top_idx, workspace,
-                          workspace_bytes, stream);
+    return csa2_topk_pool(sc, R, T, T, k_pool, k_top, nullptr, pool_idx, pool_scores, top_idx, workspace, tk,
+                          stream);
   }
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const StreamLayout L = stream_layout(R, T);
@@ -1784,10 +1852,10 @@ extern "C" csa2_status csa2_index_full_pool(const uint8_t* q_idx, const uint8_t*
   const CandOut co{rows, hist, cand, cnt, nbk};
   launch_index_scan(q_idx, k_idx, R, T, row_seq, row_limit, scores, &co, s);
   if (scan_end && hipEventRecord((hipEvent_t)scan_end, s) != hipSuccess) return CSA2_ELAUNCH;
-  stream_gather_kernel<<<dim3(groups, R), kSG, 0, s>>>(nbk, bpw, rows, hist, cand, cnt, T, above, list, k_pool,
-                                                       k_top);
-  stream_finish_kernel<<<R, kSG, 0, s>>>(scores, T, bpw, groups, rows, hist, above, list, base, k_pool, k_top);
-  stream_write_kernel<<<dim3(groups, R), kSG, 0, s>>>(scores, T, nbk, bpw, rows, base, cand, cnt, k_pool, k_top,
-                                                      pool_idx, pool_scores, top_idx);
+  stream_gather_kernel<<<dim3(groups, R), kSG, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, nbk, bpw, rows, hist,
+                                                       cand, cnt, above, list, k_pool, k_top);
+  stream_finish_kernel<<<R, kSG, 0, s>>>(T, nbk, bpw, groups, rows, hist, above, list, cand, cnt, base, k_pool, k_top);
+  stream_write_kernel<<<dim3(groups, R), kSG, 0, s>>>(T, nbk, bpw, rows, base, cand, cnt, k_pool, k_top, pool_idx,
+                                                      pool_scores, top_idx);
   return launch_status();
 }

@@ -128,9 +128,10 @@ class Csa2DecodeStack:
             idx = self.idx[li]
             if mode == "full":
                 if self.use_pool and K <= self.P:
-                    # scores, the pool and this layer's Top-K (the top K of the pool) in one call
+                    # the pool and this layer's Top-K (the top K of the pool) in one call; the
+                    # scores themselves are not needed and not written
                     ev = self._scan_events() if time_index else None
-                    csa2_index_full_pool(io.q_idx, k_idx, self.scores, self.P, K, self.pool, idx,
+                    csa2_index_full_pool(io.q_idx, k_idx, None, self.P, K, self.pool, idx,
                                          pool_scores=self.pool_scores, workspace=self.ws_topk_full,
                                          scan_events=ev, stream=stream)
                     if time_index:

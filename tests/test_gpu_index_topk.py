@@ -309,6 +309,12 @@ def test_index_full_pool_equals_separate_calls(R, T, k_pool, k_top):
     assert torch.equal(s1, s2)
     assert torch.equal(p1, p2) and torch.equal(t1, t2)
     assert torch.equal(torch.nan_to_num(ps1, nan=7.0), torch.nan_to_num(ps2, nan=7.0))
+    # without a scores output: the same selections
+    p3, ps3, t3 = torch.empty_like(p1), torch.empty_like(ps1), torch.empty_like(t1)
+    F.csa2_index_full_pool(q, k, None, k_pool, k_top, p3, t3, pool_scores=ps3)
+    torch.cuda.synchronize()
+    assert torch.equal(p1, p3) and torch.equal(t1, t3)
+    assert torch.equal(torch.nan_to_num(ps1, nan=7.0), torch.nan_to_num(ps3, nan=7.0))
     # and against the oracle on one row
     sh = s1[0].cpu().numpy().astype(np.float64)
     assert np.array_equal(p1[0].cpu().numpy(), OT.topk(sh, k_pool))
@@ -344,11 +350,12 @@ def _stream_case_keys(kind, R, T, q, dev, S=4096):
 
 @pytest.mark.parametrize("kind", ["fallback", "ties_all", "ties_few", "ties_256", "nan_keys", "limits"])
 def test_index_full_pool_streaming_cases(kind):
-    """The streaming pool selection (sampled threshold, candidates from the scan, bitmap ordered
-    write) gives the same pool, pool scores and Top-K as csa2_index_full + csa2_topk_pool, and
-    the oracle's selection on sampled rows, when the threshold misses (fallback), under massive
-    ties (more candidates than fit in LDS; ties cut by position), with NaN keys and with row
-    limits (empty rows, rows shorter than the pool)."""
+    """The streaming pool selection (sampled threshold, block-ordered candidates from the scan,
+    gather / finish / write) gives the same pool, pool scores and Top-K as csa2_index_full +
+    csa2_topk_pool, with and without a scores output, and the oracle's selection on sampled rows:
+    when the threshold misses (the row is rebuilt), under massive ties (a boundary bin larger than
+    its list; ties go to the lowest positions), with NaN keys and with row limits (empty rows,
+    rows shorter than the pool)."""
     dev = device()
     R, T, k_pool, k_top = 4, 131072, 16384, 2048
     q = W.fp8_normal(72, (R, 64), device=dev)
@@ -376,6 +383,12 @@ def test_index_full_pool_streaming_cases(kind):
         sh = s1[r].cpu().numpy().astype(np.float64)
         assert np.array_equal(p1[r].cpu().numpy(), OT.topk(sh, k_pool))
         assert np.array_equal(t1[r].cpu().numpy(), OT.topk(sh, k_top))
+    # without a scores output (the rebuild and overflow paths then rescore or read candidates only)
+    p3, ps3, t3 = torch.empty_like(p1), torch.empty_like(ps1), torch.empty_like(t1)
+    F.csa2_index_full_pool(q, k, None, k_pool, k_top, p3, t3, pool_scores=ps3, row_limit=lim)
+    torch.cuda.synchronize()
+    assert torch.equal(p1, p3) and torch.equal(t1, t3)
+    assert torch.equal(torch.nan_to_num(ps1, nan=7.0), torch.nan_to_num(ps3, nan=7.0))
     if kind == "ties_all":
         assert np.array_equal(p1.cpu().numpy(), np.tile(np.arange(k_pool, dtype=np.int32), (R, 1)))
     if kind == "limits":
