@@ -179,7 +179,7 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
     for (int i = 0; i < kUnroll; ++i) {
       const int64_t p = (t0 + i) * kTile + col_in_tile;
       x.ok[i] = p < T && p <= limit;
-      x.b[i] = x.ok[i] ? load_half_key(kseq + p * kIndexDim + 32 * half) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      x.b[i] = x.ok[i] ? load_half_key<kCand>(kseq + p * kIndexDim + 32 * half) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
   };
   uint32_t tau = 0, sh = 0;
