@@ -368,167 +368,126 @@ constexpr int kSmallBits = 12;
 constexpr int kSmallBins = 1 << kSmallBits;
 
 
-// Wave w owns the slots [256 J w, 256 J (w+1)) of the row, 4096 J >= N;
-// in step it, lane l holds slots 256 (J w + it) + 4l + [0, 4).  So every wave
-// reads 1 KiB runs, and the ordered write walks the row in slot order with
-// ballot prefix counts.  The radix digits are 12 bits wide and start at the
-// highest bit in which the row's visible keys differ.
+// Thread t owns the 4J consecutive slots [4J t, 4J t + 4J) of the row (4096 J
+// >= N), with their index_map entries, in registers.  The k-th largest visible
+// key tau is found by three radix digits of 12, 10 and 10 bits (from bit 31;
+// the first histogram's total is the visible count); the ordered write then
+// needs one block scan of the threads' (above tau, equal to tau) counts, since
+// thread order is slot order.
 template <int J>
 __global__ void __launch_bounds__(kSmallThreads)
 topk_small_kernel(const float* __restrict__ scores, int N, int64_t stride, const int32_t* __restrict__ index_map,
                   int32_t k, int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
   __shared__ uint32_t h[kSmallBins];
-  __shared__ uint32_t wt[16], wt2[16];
-  __shared__ uint32_t red[3][16];
+  __shared__ uint32_t wt[16];
   __shared__ uint32_t s_digit, s_above;
-  __shared__ __attribute__((aligned(16))) int32_t s_map[J * kSmallThreads * 4];   // index_map row (if any)
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wbase = wave * J * 256;
   const float* row = scores + (int64_t)r * stride;
   const int32_t* map_row = index_map ? index_map + (int64_t)r * N : nullptr;
+  const int s0 = 4 * J * tid;
 
+  for (int i = tid; i < kSmallBins; i += kSmallThreads) h[i] = 0u;
   uint32_t key[J][4];
-  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u, nvis = 0u;
+  int32_t pos[J][4];
   {
     float4 v[J];
     int4 mp[J];
 #pragma unroll
     for (int it = 0; it < J; ++it) {
-      const int s = wbase + it * 256 + 4 * lane;
+      const int s = s0 + 4 * it;
       const bool in = s < N;
       v[it] = in ? *reinterpret_cast<const float4*>(row + s) : make_float4(0.f, 0.f, 0.f, 0.f);
-      mp[it] = in ? (map_row ? *reinterpret_cast<const int4*>(map_row + s) : make_int4(0, 0, 0, 0))
+      mp[it] = in ? (map_row ? *reinterpret_cast<const int4*>(map_row + s) : make_int4(s, s + 1, s + 2, s + 3))
                   : make_int4(-1, -1, -1, -1);
     }
 #pragma unroll
     for (int it = 0; it < J; ++it) {
       const float f[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
       const int32_t m4[4] = {mp[it].x, mp[it].y, mp[it].z, mp[it].w};
-      if (map_row) *reinterpret_cast<int4*>(s_map + wbase + it * 256 + 4 * lane) = mp[it];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const uint32_t kk = m4[j] < 0 ? 0u : score_key(f[j]);
-        key[it][j] = kk;
-        if (kk != 0u) {
-          kmin = min(kmin, kk);
-          kmax = max(kmax, kk);
-          ++nvis;
-        }
+        key[it][j] = m4[j] < 0 ? 0u : score_key(f[j]);
+        pos[it][j] = m4[j];
       }
     }
   }
-  kmin = wave_min_u32(kmin);
-  kmax = wave_max_u32(kmax);
-  nvis = wave_sum_u32(nvis);
-  if (lane == 0) { red[0][wave] = kmin; red[1][wave] = kmax; red[2][wave] = nvis; }
   __syncthreads();
-  kmin = 0xFFFFFFFFu; kmax = 0u; nvis = 0u;
-#pragma unroll
-  for (int w = 0; w < 16; ++w) { kmin = min(kmin, red[0][w]); kmax = max(kmax, red[1][w]); nvis += red[2][w]; }
-  kmin = uniform_u32(kmin);
-  kmax = uniform_u32(kmax);
-  nvis = uniform_u32(nvis);
-  const uint32_t k_eff = nvis < (uint32_t)k ? nvis : (uint32_t)k;
 
   // radix select of tau, the k_eff-th largest visible key
-  uint32_t need = k_eff, prefix = 0u;
-  if (k_eff > 0) {
-    // bits shared by every visible key: those above the highest set bit of
-    // kmin ^ kmax.  Smearing the difference down avoids a select on
-    // kmin == kmax: this compiler's post-RA instruction shrinking can drop the
-    // exec-mask AND whose SCC such a select reads.
-    uint32_t below = kmin ^ kmax;
-    below |= below >> 1;
-    below |= below >> 2;
-    below |= below >> 4;
-    below |= below >> 8;
-    below |= below >> 16;
-    prefix = kmax & ~below;
-    int hi = __popc(below) - 1;             // highest unresolved bit (below = 2^(hi+1) - 1), -1 if none
+  uint32_t need = 0, prefix = 0u, k_eff = 0;
 #pragma unroll 1
-    while (hi >= 0) {
-      const int width = hi + 1 < kSmallBits ? hi + 1 : kSmallBits;
-      const int shift = hi + 1 - width;
-      const uint32_t bmask = (1u << width) - 1u;
-      const uint32_t hp = hi >= 31 ? 0u : (prefix >> (hi + 1));
-      for (int i = tid; i < kSmallBins; i += kSmallThreads) h[i] = 0u;
+  for (int d = 0; d < 3; ++d) {
+    const int shift = d == 0 ? 20 : (d == 1 ? 10 : 0);
+    const int hi = d == 0 ? 32 : (d == 1 ? 20 : 10);
+    const uint32_t bmask = d == 0 ? 4095u : 1023u;
+    if (d > 0) {
+      for (int i = tid; i < 1024; i += kSmallThreads) h[i] = 0u;
       __syncthreads();
+    }
 #pragma unroll
-      for (int it = 0; it < J; ++it) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t kk = key[it][j];
-          const bool match = kk != 0u && (hi >= 31 || (kk >> (hi + 1)) == hp);
-          if (match) atomicAdd(&h[(kk >> shift) & bmask], 1u);
-        }
-      }
-      __syncthreads();
-      // thread t owns bins kSmallBins-1-4t-j (j = 0..3): a descending walk
-      uint32_t c[4], local = 0;
+    for (int it = 0; it < J; ++it)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        c[j] = h[kSmallBins - 1 - 4 * tid - j];
+        const uint32_t kk = key[it][j];
+        if (kk != 0u && (hi == 32 || (kk >> hi) == (prefix >> hi))) atomicAdd(&h[(kk >> shift) & bmask], 1u);
+      }
+    __syncthreads();
+    // bins walked from the top: 4 per thread at the first digit, 1 after
+    const int per = d == 0 ? 4 : 1;
+    const int nb = d == 0 ? 4096 : 1024;
+    uint32_t c[4] = {0u, 0u, 0u, 0u}, local = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < per) {
+        c[j] = h[nb - 1 - per * tid - j];
         local += c[j];
       }
-      uint32_t total;
-      const uint32_t excl = block_scan_1024(local, wt, total);
-      if (excl < need && need <= excl + local) {
-        uint32_t acc = excl;
+    uint32_t total;
+    const uint32_t excl = block_scan_1024(local, wt, total);
+    if (d == 0) {
+      k_eff = total < (uint32_t)k ? total : (uint32_t)k;     // total = visible keys
+      need = k_eff;
+    }
+    if (need == 0u) break;
+    if (excl < need && need <= excl + local) {
+      uint32_t acc = excl;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 4; ++j)
+        if (j < per) {
           if (acc < need && need <= acc + c[j]) {
-            s_digit = (uint32_t)(kSmallBins - 1 - 4 * tid - j);
+            s_digit = (uint32_t)(nb - 1 - per * tid - j);
             s_above = acc;
           }
           acc += c[j];
         }
-      }
-      __syncthreads();
-      prefix |= s_digit << shift;
-      need -= s_above;
-      hi = shift - 1;
     }
+    __syncthreads();
+    prefix |= s_digit << shift;
+    need -= s_above;
+    __syncthreads();
   }
   const uint32_t tau = prefix, need_eq = need;
 
   // ordered write: a slot's output index is (#keys > tau before it) + min(#keys == tau before it, need_eq)
-  uint32_t n_gt = 0, n_eq = 0;
-#pragma unroll
-  for (int it = 0; it < J; ++it)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t kk = key[it][j];
-      n_gt += kk != 0u && kk > tau;
-      n_eq += kk != 0u && kk == tau;
-    }
-  n_gt = wave_sum_u32(n_gt);
-  n_eq = wave_sum_u32(n_eq);
-  if (lane == 0) { wt[wave] = n_gt; wt2[wave] = n_eq; }
-  __syncthreads();
-  uint32_t G = 0, E = 0;
-#pragma unroll
-  for (int w = 0; w < 16; ++w) {
-    G += w < wave ? wt[w] : 0u;
-    E += w < wave ? wt2[w] : 0u;
-  }
   int32_t* orow = idx_out + (int64_t)r * k;
   float* srow = score_out ? score_out + (int64_t)r * k : nullptr;
   if (k_eff > 0) {
+    uint32_t cg = 0, ce = 0;
 #pragma unroll
-    for (int it = 0; it < J; ++it) {
-      uint32_t cg = 0, ce = 0;
+    for (int it = 0; it < J; ++it)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t kk = key[it][j];
         cg += kk != 0u && kk > tau;
         ce += kk != 0u && kk == tau;
       }
-      uint32_t tg, te;
-      const int s = wbase + it * 256 + 4 * lane;
-      uint32_t g = G + wave_exclusive_small(cg, tg);
-      uint32_t e = E + wave_exclusive_small(ce, te);
+    // both counts in one scan: each stays below 2^16 (N <= 32768)
+    uint32_t tot;
+    const uint32_t pre = block_scan_1024((cg << 16) | ce, wt, tot);
+    uint32_t g = pre >> 16, e = pre & 0xFFFFu;
+#pragma unroll
+    for (int it = 0; it < J; ++it)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t kk = key[it][j];
@@ -536,17 +495,13 @@ topk_small_kernel(const float* __restrict__ scores, int N, int64_t stride, const
         const bool is_eq = kk != 0u && kk == tau;
         const bool take = is_gt || (is_eq && e < need_eq);
         const uint32_t o = g + (is_gt ? min(e, need_eq) : e);
-        const int32_t pv = map_row ? s_map[s + j] : s + j;
         g += is_gt ? 1u : 0u;
         e += is_eq ? 1u : 0u;
         if (take && o < k_eff) {
-          orow[o] = pv;
+          orow[o] = pos[it][j];
           if (srow) srow[o] = key_score(kk);
         }
       }
-      G += tg;
-      E += te;
-    }
   }
   for (int i = (int)k_eff + tid; i < k; i += kSmallThreads) {
     orow[i] = -1;
