@@ -1332,6 +1332,7 @@ stream_finish_kernel(int64_t T, int64_t nbk, int bpw, int G, StreamRow* __restri
   __shared__ uint32_t h[kStreamBins];
   __shared__ uint32_t s_lk[kListCap];
   __shared__ uint32_t s_gt[kStreamGroups], s_eq[kStreamGroups];
+  __shared__ uint32_t res2[4];
   const int r = blockIdx.x, tid = threadIdx.x;
   const int R = gridDim.x;
   const StreamRow st = rows[r];
@@ -1353,6 +1354,62 @@ stream_finish_kernel(int64_t T, int64_t nbk, int bpw, int G, StreamRow* __restri
   const uint32_t mode = rb.rebuild ? 1u : (rb.overflow ? 2u : 0u);
   if (mode == 0u && rb.k_eff[0] == 0u) {
     for (int i = tid; i < G; i += kSG) bo[i] = StreamBase{{0u, 0u}, {0u, 0u}};
+  } else if (mode == 0u && st.n_list[0] <= (uint32_t)kSG && st.n_list[1] <= (uint32_t)kSG) {
+    // both short lists at once (the usual case): thread i holds entry i of each,
+    // ranks it by counting, and the workgroup counts follow in the same pass
+    uint32_t* lk1 = s_lk + kSG;
+    uint32_t* gts = s_gt;                         // [2][kStreamGroups] in s_gt / s_eq pairs below
+    if (tid < (int)st.n_list[0]) s_lk[tid] = le0[0].x;
+    if (tid < (int)st.n_list[1]) lk1[tid] = le0[1].x;
+    for (int i = tid; i < kStreamGroups; i += kSG) { s_gt[i] = 0u; s_eq[i] = 0u; h[i] = 0u; h[kStreamGroups + i] = 0u; }
+    if (tid < 4) res2[tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const uint32_t n = st.n_list[s], need = rb.k_eff[s] - rb.above[s];
+      const uint32_t* lk = s == 0 ? s_lk : lk1;
+      const uint32_t mine = le0[s].x;
+      uint32_t gt = 0u, eq = 0u;
+      for (uint32_t j = 0; j < n; ++j) {
+        const uint32_t o = lk[j];
+        gt += o > mine;
+        eq += o == mine;
+      }
+      if (tid < (int)n && gt < need && need <= gt + eq) {
+        res2[2 * s] = mine;
+        res2[2 * s + 1] = gt;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      tau[s] = res2[2 * s];
+      need_eq[s] = rb.k_eff[s] - rb.above[s] - res2[2 * s + 1];
+      if (tid < (int)st.n_list[s]) {
+        const uint32_t wg = (uint32_t)(((int64_t)(int32_t)le0[s].y / kBlockPositions) / bpw);
+        uint32_t* cg = s == 0 ? s_gt : h;
+        uint32_t* ce = s == 0 ? s_eq : h + kStreamGroups;
+        if (le0[s].x > tau[s]) atomicAdd(&cg[wg], 1u);
+        else if (le0[s].x == tau[s]) atomicAdd(&ce[wg], 1u);
+      }
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // G <= 64: one wave scans the workgroups' counts of both selections
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint32_t* cg = s == 0 ? s_gt : h;
+        const uint32_t* ce = s == 0 ? s_eq : h + kStreamGroups;
+        const uint32_t gtc = tid < G ? cg[tid] + ab0[s] : 0u;
+        const uint32_t eqc = tid < G ? ce[tid] : 0u;
+        const uint32_t gi = wave_inclusive_scan(gtc) - gtc, ei = wave_inclusive_scan(eqc) - eqc;
+        if (tid < G) {
+          bo[tid].gt[s] = gi;
+          bo[tid].eq[s] = ei;
+        }
+      }
+    }
+    (void)gts;
   } else if (mode == 0u) {
 #pragma unroll 1
     for (int s = 0; s < 2; ++s) {
