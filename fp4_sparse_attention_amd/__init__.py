@@ -54,6 +54,21 @@ _SIGS = {
                                              _c_void_p, _c_void_p, _c_void_p, _size_t, _c_void_p]),
     "csa2_swa_merge": (_i32, [_c_void_p, _i32, _i32, _c_void_p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _f32,
                               _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t, _c_void_p]),
+    # paged global KV
+    "csa2_fp4_pack_rows": (_i32, [_c_void_p, _i64, _i32, _i64, _c_void_p, _c_void_p, _i64, _c_void_p, _i64,
+                                  _c_void_p]),
+    "csa2_index_full_paged": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i64, _c_void_p, _c_void_p, _c_void_p, _i64,
+                                     _i32, _c_void_p, _c_void_p]),
+    "csa2_index_reindex_paged": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i64, _c_void_p, _c_void_p, _i64, _i32,
+                                        _c_void_p, _i32, _c_void_p, _c_void_p]),
+    "csa2_index_full_pool_paged_workspace_size": (_size_t, [_i32, _i64, _i32]),
+    "csa2_index_full_pool_paged": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i64, _c_void_p, _c_void_p, _c_void_p,
+                                          _i64, _i32, _c_void_p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
+                                          _c_void_p, _size_t, _c_void_p]),
+    "csa2_sparse_swa_decode_layers_paged": (_i32, [_i32, _c_void_p, _i32, _i32, _c_void_p, _c_void_p, _i32, _i64,
+                                                   _c_void_p, _c_void_p, _i64, _i32, _c_void_p, _c_void_p, _i32,
+                                                   _c_void_p, _i32, _c_void_p, _c_void_p, _f32, _c_void_p, _c_void_p,
+                                                   _c_void_p, _size_t, _c_void_p]),
 }
 
 _lib = None
@@ -446,3 +461,153 @@ def csa2_index_full_pool(q_idx, k_idx, scores, k_pool, k_top, pool_idx, top_idx,
                                     k_top, _p(pool_idx), _p(pool_scores), _p(top_idx), _p(workspace),
                                     workspace.numel(), ev0, ev1, _stream(stream))
     _check("csa2_index_full_pool", st)
+
+
+# ---------------------------------------------------------------------------
+# paged global KV: pools of pages of `page` positions; block_table int32 [B, max_blocks]
+# maps each sequence's logical block to its page (negative: unmapped)
+# ---------------------------------------------------------------------------
+def _table(block_table, page, T):
+    _need(block_table, torch.int32, "block_table", 2)
+    _dense(block_table, "block_table")
+    return block_table.shape  # page size and capacity are checked by the library
+
+
+def csa2_fp4_pack_rows(x, out_rows, codes, scales, stream=None):
+    """x bf16 [n, C] (rows may be strided); out_rows int64 [n] (negative: skip); codes uint8 [N_rows, C/2] and
+    scales uint8 [N_rows, C/16] (row-strided pools): row i of x is packed into row out_rows[i]."""
+    _need(x, torch.bfloat16, "x", 2)
+    _need(out_rows, torch.int64, "out_rows", 1)
+    _need(codes, torch.uint8, "codes", 2)
+    _need(scales, torch.uint8, "scales", 2)
+    n, C = x.shape
+    if out_rows.shape != (n,) or codes.shape[1] != C // 2 or scales.shape[1] != C // 16:
+        raise ValueError("pack_rows shapes")
+    for t, nm in ((x, "x"), (codes, "codes"), (scales, "scales")):
+        if t.stride(1) != 1:
+            raise ValueError(f"{nm}: channels must be contiguous")
+    _dense(out_rows, "out_rows")
+    st = lib().csa2_fp4_pack_rows(_p(x), n, C, x.stride(0), _p(out_rows), _p(codes), codes.stride(0), _p(scales),
+                                  scales.stride(0), _stream(stream))
+    _check("csa2_fp4_pack_rows", st)
+
+
+def csa2_index_full_paged(q_idx, k_pages, block_table, page, T, scores, row_seq=None, row_limit=None, stream=None):
+    """csa2_index_full over paged keys: k_pages uint8 [n_pages * page, 64]; scores fp32 [R, T]."""
+    _need(q_idx, torch.uint8, "q_idx", 2)
+    _need(k_pages, torch.uint8, "k_pages", 2)
+    _need(scores, torch.float32, "scores", 2)
+    for t, nm in ((q_idx, "q_idx"), (k_pages, "k_pages"), (scores, "scores")):
+        _dense(t, nm)
+    B, max_blocks = _table(block_table, page, T)
+    R = q_idx.shape[0]
+    if q_idx.shape[1] != 64 or k_pages.shape[1] != 64 or scores.shape != (R, T):
+        raise ValueError("index_full_paged shapes")
+    if row_seq is not None:
+        _need(row_seq, torch.int32, "row_seq", 1)
+    if row_limit is not None:
+        _need(row_limit, torch.int64, "row_limit", 1)
+    st = lib().csa2_index_full_paged(_p(q_idx), _p(k_pages), R, B, T, _p(row_seq), _p(row_limit), _p(block_table),
+                                     max_blocks, page, _p(scores), _stream(stream))
+    _check("csa2_index_full_paged", st)
+
+
+def csa2_index_reindex_paged(q_idx, k_pages, block_table, page, T, pool, scores, row_seq=None, stream=None):
+    """csa2_index_reindex over paged keys; pool int32 [R, P] of logical positions; scores fp32 [R, P]."""
+    _need(q_idx, torch.uint8, "q_idx", 2)
+    _need(k_pages, torch.uint8, "k_pages", 2)
+    _need(pool, torch.int32, "pool", 2)
+    _need(scores, torch.float32, "scores", 2)
+    for t, nm in ((q_idx, "q_idx"), (k_pages, "k_pages"), (pool, "pool"), (scores, "scores")):
+        _dense(t, nm)
+    B, max_blocks = _table(block_table, page, T)
+    R, P = pool.shape
+    if scores.shape != (R, P) or q_idx.shape != (R, 64) or k_pages.shape[1] != 64:
+        raise ValueError("reindex_paged shapes")
+    if row_seq is not None:
+        _need(row_seq, torch.int32, "row_seq", 1)
+    st = lib().csa2_index_reindex_paged(_p(q_idx), _p(k_pages), R, B, T, _p(row_seq), _p(block_table), max_blocks,
+                                        page, _p(pool), P, _p(scores), _stream(stream))
+    _check("csa2_index_reindex_paged", st)
+
+
+def csa2_index_full_pool_paged_workspace_size(R, T, k_pool):
+    return int(lib().csa2_index_full_pool_paged_workspace_size(R, T, k_pool))
+
+
+def csa2_index_full_pool_paged(q_idx, k_pages, block_table, page, T, scores, k_pool, k_top, pool_idx, top_idx,
+                               pool_scores=None, row_seq=None, row_limit=None, workspace=None, stream=None):
+    """csa2_index_full_pool over paged keys; scores fp32 [R, T] or None; outputs are logical positions."""
+    _need(q_idx, torch.uint8, "q_idx", 2)
+    _need(k_pages, torch.uint8, "k_pages", 2)
+    if scores is not None:
+        _need(scores, torch.float32, "scores", 2)
+        _dense(scores, "scores")
+    _need(pool_idx, torch.int32, "pool_idx", 2)
+    _need(top_idx, torch.int32, "top_idx", 2)
+    for t, nm in ((q_idx, "q_idx"), (k_pages, "k_pages"), (pool_idx, "pool_idx"), (top_idx, "top_idx")):
+        _dense(t, nm)
+    B, max_blocks = _table(block_table, page, T)
+    R = q_idx.shape[0]
+    if (q_idx.shape[1] != 64 or k_pages.shape[1] != 64 or (scores is not None and scores.shape != (R, T))
+            or pool_idx.shape != (R, k_pool) or top_idx.shape != (R, k_top)):
+        raise ValueError("index_full_pool_paged shapes")
+    if pool_scores is not None:
+        _need(pool_scores, torch.float32, "pool_scores", 2)
+        _dense(pool_scores, "pool_scores")
+        if pool_scores.shape != (R, k_pool):
+            raise ValueError("pool_scores shape")
+    if row_seq is not None:
+        _need(row_seq, torch.int32, "row_seq", 1)
+    if row_limit is not None:
+        _need(row_limit, torch.int64, "row_limit", 1)
+    if workspace is None:
+        workspace = torch.empty(csa2_index_full_pool_paged_workspace_size(R, T, k_pool), dtype=torch.uint8,
+                                device=q_idx.device)
+    st = lib().csa2_index_full_pool_paged(_p(q_idx), _p(k_pages), R, B, T, _p(row_seq), _p(row_limit),
+                                          _p(block_table), max_blocks, page, _p(scores), k_pool, k_top, _p(pool_idx),
+                                          _p(pool_scores), _p(top_idx), _p(workspace), workspace.numel(),
+                                          _stream(stream))
+    _check("csa2_index_full_pool_paged", st)
+
+
+def csa2_sparse_swa_decode_layers_paged(q_lat, code_pages, scale_pages, block_table, page, T, idx, layer_idx, swa,
+                                        swa_start, swa_len, softmax_scale, o, lse, row_seq=None, workspace=None,
+                                        stream=None):
+    """csa2_sparse_swa_decode_layers over paged FP4 rows: code_pages uint8 [n_pages * page, 256], scale_pages
+    uint8 [n_pages * page, 32]; idx holds logical positions."""
+    _need(q_lat, torch.bfloat16, "q_lat", 4)
+    _need(code_pages, torch.uint8, "code_pages", 2)
+    _need(scale_pages, torch.uint8, "scale_pages", 2)
+    _need(idx, torch.int32, "idx", 3)
+    _need(swa, torch.bfloat16, "swa", 4)
+    _need(swa_start, torch.int32, "swa_start", 2)
+    _need(swa_len, torch.int32, "swa_len", 2)
+    _need(o, torch.float32, "o", 4)
+    _need(lse, torch.float32, "lse", 3)
+    for t, nm in ((q_lat, "q_lat"), (code_pages, "code_pages"), (scale_pages, "scale_pages"), (idx, "idx"),
+                  (swa, "swa"), (swa_start, "swa_start"), (swa_len, "swa_len"), (o, "o"), (lse, "lse")):
+        _dense(t, nm)
+    B, max_blocks = _table(block_table, page, T)
+    L, R, H, C = q_lat.shape
+    n, Ri, K = idx.shape
+    S = swa.shape[2]
+    layer_idx = [int(v) for v in layer_idx]
+    if (C != 512 or code_pages.shape[1] != 256 or scale_pages.shape[1] != 32 or Ri != R or len(layer_idx) != L
+            or swa.shape != (L, B, S, 512) or swa_start.shape != (L, R) or swa_len.shape != (L, R)
+            or o.shape != (L, R, H, 512) or lse.shape != (L, R, H)):
+        raise ValueError("sparse_swa_decode_layers_paged shapes")
+    if any(v < 0 or v >= n for v in layer_idx):
+        raise ValueError("layer_idx entries must select one of the idx slices")
+    if row_seq is not None:
+        _need(row_seq, torch.int32, "row_seq", 1)
+    if workspace is None:
+        workspace = torch.empty(csa2_sparse_swa_decode_layers_workspace_size(L, R, H, K), dtype=torch.uint8,
+                                device=q_lat.device)
+    host_idx = (ctypes.c_int32 * L)(*layer_idx)
+    st = lib().csa2_sparse_swa_decode_layers_paged(L, _p(q_lat), R, H, _p(code_pages), _p(scale_pages), B, T,
+                                                   _p(row_seq), _p(block_table), max_blocks, page, _p(idx),
+                                                   ctypes.cast(host_idx, ctypes.c_void_p), K, _p(swa), S,
+                                                   _p(swa_start), _p(swa_len), float(softmax_scale), _p(o), _p(lse),
+                                                   _p(workspace), workspace.numel(), _stream(stream))
+    _check("csa2_sparse_swa_decode_layers_paged", st)

@@ -30,7 +30,7 @@
 // result) into o and lse.
 #include <type_traits>
 
-#include "common.hpp"
+#include "internal.hpp"
 
 namespace csa2 {
 
@@ -107,6 +107,7 @@ struct AttnArgs {
   float scale_log2;               // softmax scale * log2(e)
   float* o_part;                  // [L][R][n_chunks][H][512]
   float* ml_part;                 // [L][R][n_chunks][H][2]
+  PageMap pm;                     // codes / scales as page pools (table null: [B][T] rows)
 };
 
 // raw FP4 data of the lane's two keys for one tile (prefetched two tiles ahead)
@@ -207,10 +208,10 @@ attn_chunk_kernel(const AttnArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       const int pos = s_pos[j * kKT + 16 * mt + m];
-      const bool ok = pos >= 0;
+      const int64_t row = pos >= 0 ? phys_row(a.pm, seq, a.T, pos) : -1;
+      const bool ok = row >= 0;
       raw.valid[mt] = ok;
       if (ok) {
-        const int64_t row = (int64_t)seq * a.T + pos;
         raw.v[mt] = *reinterpret_cast<const uint4*>(a.codes + row * kCodesRow + 64 * wave + 16 * g);
         raw.sc[mt] = *reinterpret_cast<const uint16_t*>(a.scales + row * kScalesRow + 8 * wave + 2 * g);
       } else {
@@ -524,9 +525,11 @@ static csa2_status attention_call(int32_t L, const uint16_t* q_lat, int32_t R, i
                                   const int32_t* idx, const int64_t* idx_off, int32_t K, const uint16_t* swa,
                                   int32_t S, const int32_t* swa_start, const int32_t* swa_len, float softmax_scale,
                                   const float* o_prev, const float* lse_prev, float* o, float* lse,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
+                                  void* workspace, size_t workspace_bytes, void* stream,
+                                  const PageMap& pm = PageMap{}) {
   const Plan p = chunk_plan(L, R, H, K, idx != nullptr, swa != nullptr);
   AttnArgs a;
+  a.pm = pm;
   a.q_lat = q_lat; a.R = R; a.H = H; a.L = L; a.head_groups = head_groups(H);
   a.codes = codes; a.scales = scales; a.T = T; a.row_seq = row_seq;
   a.idx = idx; a.K = K;
@@ -659,4 +662,26 @@ extern "C" csa2_status csa2_sparse_swa_decode_layers(int32_t L, const uint16_t* 
   }
   return attention_call(L, q_lat, R, H, codes, scales, B, T, row_seq, idx, off, K, swa, S, swa_start, swa_len,
                         softmax_scale, nullptr, nullptr, o, lse, workspace, workspace_bytes, stream);
+}
+
+extern "C" csa2_status csa2_sparse_swa_decode_layers_paged(
+    int32_t L, const uint16_t* q_lat, int32_t R, int32_t H, const uint8_t* code_pages, const uint8_t* scale_pages,
+    int32_t B, int64_t T, const int32_t* row_seq, const int32_t* block_table, int64_t max_blocks, int32_t page,
+    const int32_t* idx, const int32_t* layer_idx, int32_t K, const uint16_t* swa, int32_t S, const int32_t* swa_start,
+    const int32_t* swa_len, float softmax_scale, float* o, float* lse, void* workspace, size_t workspace_bytes,
+    void* stream) {
+  csa2_status st = check_sparse_swa(L, q_lat, R, H, code_pages, scale_pages, B, T, row_seq, idx, K, swa, S,
+                                    swa_start, swa_len, o, lse);
+  if (st != CSA2_OK) return st;
+  st = check_pages(block_table, max_blocks, page, T);
+  if (st != CSA2_OK) return st;
+  if (!layer_idx) return CSA2_EINVAL;
+  int64_t off[kMaxLayers];
+  for (int l = 0; l < L; ++l) {
+    if (layer_idx[l] < 0) return CSA2_EINVAL;
+    off[l] = (int64_t)layer_idx[l] * R * K;
+  }
+  return attention_call(L, q_lat, R, H, code_pages, scale_pages, B, T, row_seq, idx, off, K, swa, S, swa_start,
+                        swa_len, softmax_scale, nullptr, nullptr, o, lse, workspace, workspace_bytes, stream,
+                        PageMap{block_table, max_blocks, page});
 }

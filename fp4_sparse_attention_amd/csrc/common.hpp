@@ -174,6 +174,25 @@ __device__ __forceinline__ float key_score(uint32_t key) {
 }
 
 // ----------------------------------------------------------------------------
+// paged caches: sequence b's logical position p lives in physical row
+// table[b][p / page] * page + p % page of a page pool (table == null: the dense
+// layout, row b T + p).  Unmapped blocks (negative entries) hold no positions.
+// ----------------------------------------------------------------------------
+struct PageMap {
+  const int32_t* table;   // [B][max_blocks] or null
+  int64_t max_blocks;
+  int32_t page;           // positions per page, a multiple of 128
+};
+
+__device__ __forceinline__ int64_t phys_row(const PageMap& pm, int seq, int64_t T, int64_t p) {
+  if (!pm.table) return (int64_t)seq * T + p;
+  const int64_t blk = p / pm.page;
+  if (blk >= pm.max_blocks) return -1;
+  const int32_t pg = pm.table[(int64_t)seq * pm.max_blocks + blk];
+  return pg < 0 ? -1 : (int64_t)pg * pm.page + (p - blk * pm.page);
+}
+
+// ----------------------------------------------------------------------------
 // host-side checks
 // ----------------------------------------------------------------------------
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }

@@ -37,14 +37,13 @@ __global__ void __launch_bounds__(256)
 index_rows_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx, int64_t T,
                   const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit,
                   const int32_t* __restrict__ pool, int64_t n_cols, float* __restrict__ scores,
-                  int tiles_per_block) {
+                  int tiles_per_block, PageMap pm) {
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int half = lane >> 5;
   const int col_in_tile = lane & 31;
   const int seq = row_seq ? row_seq[r] : r;
-  const uint8_t* kseq = k_idx + (int64_t)seq * T * kIndexDim;
   const int64_t limit = row_limit ? row_limit[r] : T - 1;
   float* out = scores + (int64_t)r * n_cols;
   const int32_t* prow = kGather ? pool + (int64_t)r * n_cols : nullptr;
@@ -75,9 +74,11 @@ index_rows_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__
       int64_t p = -1;
       if (t < t_end && c < n_cols) p = kGather ? (int64_t)prow[c] : c;
       ok[u] = p >= 0 && p < T && p <= limit;
+      const int64_t row = ok[u] ? phys_row(pm, seq, T, p) : -1;
+      ok[u] = row >= 0;
       pos[u] = c;
       b[u] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (ok[u]) b[u] = load_half_key(kseq + p * kIndexDim + 32 * half);
+      if (ok[u]) b[u] = load_half_key(k_idx + row * kIndexDim + 32 * half);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -111,7 +112,7 @@ template <bool kCand>
 __global__ void __launch_bounds__(256)
 index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx, int64_t T,
                     const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit,
-                    float* __restrict__ scores, int R, int64_t units_per_row, CandOut cand) {
+                    float* __restrict__ scores, int R, int64_t units_per_row, CandOut cand, PageMap pm) {
   __shared__ uint32_t h[kCand ? kStreamBins : 1];
   __shared__ uint32_t used[kCand ? kStreamBins : 1];   // bins of h that are nonzero, in the order first hit
   __shared__ uint32_t n_used;
@@ -174,12 +175,15 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
     const int64_t t0 = tile_of(jj);
     const int seq = row_seq ? row_seq[rr] : rr;
     const int64_t limit = row_limit ? row_limit[rr] : T - 1;
-    const uint8_t* kseq = k_idx + (int64_t)seq * T * kIndexDim;
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
-      const int64_t p = (t0 + i) * kTile + col_in_tile;
-      x.ok[i] = p < T && p <= limit;
-      x.b[i] = x.ok[i] ? load_half_key<kCand>(kseq + p * kIndexDim + 32 * half) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      // a tile never straddles a page: one translation per tile
+      const int64_t p0 = (t0 + i) * kTile;
+      const int64_t row0 = p0 < T ? phys_row(pm, seq, T, p0) : -1;
+      const int64_t p = p0 + col_in_tile;
+      x.ok[i] = row0 >= 0 && p < T && p <= limit;
+      x.b[i] = x.ok[i] ? load_half_key<kCand>(k_idx + (row0 + col_in_tile) * kIndexDim + 32 * half)
+                       : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
   };
   uint32_t tau = 0, sh = 0;
@@ -280,14 +284,13 @@ constexpr int kSampleRun = 8;
 __global__ void __launch_bounds__(256)
 index_sample_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx, int64_t T,
                     const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit,
-                    uint32_t* __restrict__ samp) {
+                    uint32_t* __restrict__ samp, PageMap pm) {
   const int r = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col_in_tile = lane & 31;
   const int64_t limit = row_limit ? row_limit[r] : T - 1;
   const int64_t V = limit < 0 ? 0 : (limit + 1 < T ? limit + 1 : T);
   const int seq = row_seq ? row_seq[r] : r;
-  const uint8_t* kseq = k_idx + (int64_t)seq * T * kIndexDim;
   constexpr int kRuns = kSampleN / kSampleRun;
   i32x8 kb[2];
   bool ok[2];
@@ -298,9 +301,10 @@ index_sample_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
     int64_t p0 = ((2 * run + 1) * V) / (2 * kRuns) - kSampleRun / 2;
     p0 = p0 < 0 ? 0 : (p0 > V - kSampleRun ? V - kSampleRun : p0);
     int64_t p = p0 + i % kSampleRun;
-    ok[u] = V > 0;
     p = p < 0 ? 0 : (p >= V ? V - 1 : p);
-    kb[u] = ok[u] ? load_half_key(kseq + p * kIndexDim + 32 * half) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    const int64_t row = V > 0 ? phys_row(pm, seq, T, p) : -1;
+    ok[u] = row >= 0;
+    kb[u] = ok[u] ? load_half_key(k_idx + row * kIndexDim + 32 * half) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
   }
   i32x8 araw = {0, 0, 0, 0, 0, 0, 0, 0};
   if (col_in_tile == 0) {
@@ -510,23 +514,24 @@ static int tiles_per_block_for(int64_t n_tiles, int64_t rows) {
 }
 
 void launch_index_scan(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int64_t T, const int32_t* row_seq,
-                       const int64_t* row_limit, float* scores, const CandOut* cand, hipStream_t s) {
+                       const int64_t* row_limit, float* scores, const CandOut* cand, hipStream_t s,
+                       const PageMap& pm) {
   const int64_t n_tiles = (T + kTile - 1) / kTile;
   const int64_t units_per_row = (n_tiles + kUnitTiles - 1) / kUnitTiles;
   int64_t grid = std::min<int64_t>(resident_blocks(), (int64_t)R * units_per_row);
   if (cand && R <= grid) grid = std::min<int64_t>(grid / R, units_per_row) * R;   // whole groups per row
   if (cand)
     index_stream_kernel<true><<<(int)grid, 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, scores, R,
-                                                        units_per_row, *cand);
+                                                        units_per_row, *cand, pm);
   else
     index_stream_kernel<false><<<(int)grid, 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, scores, R,
-                                                         units_per_row, CandOut{});
+                                                         units_per_row, CandOut{}, pm);
 }
 
 void launch_index_sample_tau(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int64_t T,
                              const int32_t* row_seq, const int64_t* row_limit, int32_t k, StreamRow* rows,
-                             uint32_t* hist, uint32_t* samp, hipStream_t s) {
-  index_sample_kernel<<<dim3(kSampleN / 256, R), 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, samp);
+                             uint32_t* hist, uint32_t* samp, hipStream_t s, const PageMap& pm) {
+  index_sample_kernel<<<dim3(kSampleN / 256, R), 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, samp, pm);
   index_tau_kernel<<<R, 1024, 0, s>>>(samp, T, row_limit, k, rows, hist);
 }
 
@@ -558,7 +563,7 @@ extern "C" csa2_status csa2_index_full(const uint8_t* q_idx, const uint8_t* k_id
     dim3 grid(ceil_div(n_tiles, tpb), ceil_div(R, 32));
     index_block_kernel<<<grid, 256, 0, s>>>(q_idx, k_idx, R, T, row_seq, row_limit, scores, tpb);
   } else {
-    launch_index_scan(q_idx, k_idx, R, T, row_seq, row_limit, scores, nullptr, s);
+    launch_index_scan(q_idx, k_idx, R, T, row_seq, row_limit, scores, nullptr, s, PageMap{});
   }
   return launch_status();
 }
@@ -575,6 +580,47 @@ extern "C" csa2_status csa2_index_reindex(const uint8_t* q_idx, const uint8_t* k
   int tpb = tiles_per_block_for(n_tiles, R);
   dim3 grid(ceil_div(n_tiles, tpb), R);
   index_rows_kernel<true><<<grid, 256, 0, (hipStream_t)stream>>>(q_idx, k_idx, T, row_seq, nullptr, pool, P,
-                                                                 scores, tpb);
+                                                                 scores, tpb, PageMap{});
+  return launch_status();
+}
+
+csa2_status csa2::check_pages(const int32_t* block_table, int64_t max_blocks, int32_t page, int64_t T) {
+  if (!block_table || max_blocks <= 0 || page <= 0) return CSA2_EINVAL;
+  if (page % kPageQuantum != 0 || T > max_blocks * (int64_t)page) return CSA2_ESHAPE;
+  return CSA2_OK;
+}
+
+extern "C" csa2_status csa2_index_full_paged(const uint8_t* q_idx, const uint8_t* k_pages, int32_t R, int32_t B,
+                                             int64_t T, const int32_t* row_seq, const int64_t* row_limit,
+                                             const int32_t* block_table, int64_t max_blocks, int32_t page,
+                                             float* scores, void* stream) {
+  if (!q_idx || !k_pages || !scores) return CSA2_EINVAL;
+  if (R <= 0 || B <= 0 || T <= 0) return CSA2_EINVAL;
+  if (!row_seq && R != B) return CSA2_EINVAL;
+  if (T % 4 != 0 || T >= (int64_t(1) << 31)) return CSA2_ESHAPE;
+  csa2_status st = check_pages(block_table, max_blocks, page, T);
+  if (st != CSA2_OK) return st;
+  if (!aligned(q_idx, 16) || !aligned(k_pages, 16) || !aligned(scores, 16)) return CSA2_EALIGN;
+  launch_index_scan(q_idx, k_pages, R, T, row_seq, row_limit, scores, nullptr, (hipStream_t)stream,
+                    PageMap{block_table, max_blocks, page});
+  return launch_status();
+}
+
+extern "C" csa2_status csa2_index_reindex_paged(const uint8_t* q_idx, const uint8_t* k_pages, int32_t R, int32_t B,
+                                                int64_t T, const int32_t* row_seq, const int32_t* block_table,
+                                                int64_t max_blocks, int32_t page, const int32_t* pool, int32_t P,
+                                                float* scores, void* stream) {
+  if (!q_idx || !k_pages || !scores || !pool) return CSA2_EINVAL;
+  if (R <= 0 || B <= 0 || T <= 0 || P <= 0) return CSA2_EINVAL;
+  if (!row_seq && R != B) return CSA2_EINVAL;
+  if (P % 4 != 0 || T >= (int64_t(1) << 31)) return CSA2_ESHAPE;
+  csa2_status st = check_pages(block_table, max_blocks, page, T);
+  if (st != CSA2_OK) return st;
+  if (!aligned(q_idx, 16) || !aligned(k_pages, 16) || !aligned(scores, 16) || !aligned(pool, 16)) return CSA2_EALIGN;
+  const int64_t n_tiles = (P + kTile - 1) / kTile;
+  int tpb = tiles_per_block_for(n_tiles, R);
+  dim3 grid(ceil_div(n_tiles, tpb), R);
+  index_rows_kernel<true><<<grid, 256, 0, (hipStream_t)stream>>>(q_idx, k_pages, T, row_seq, nullptr, pool, P,
+                                                                 scores, tpb, PageMap{block_table, max_blocks, page});
   return launch_status();
 }

@@ -41,18 +41,24 @@ struct CandOut {
 // Full-mode index scan on `s`; with cand, also emits the candidates (and then
 // scores may be null: no scores are written).
 void launch_index_scan(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int64_t T, const int32_t* row_seq,
-                       const int64_t* row_limit, float* scores, const CandOut* cand, hipStream_t s);
+                       const int64_t* row_limit, float* scores, const CandOut* cand, hipStream_t s,
+                       const PageMap& pm);
 
 // per-row threshold tau_s and digit shift for a selection of k from a
 // strided sample of the row's scores (samp: [R][index_sample_words()]
 // scratch); clears the row's histogram and state
 void launch_index_sample_tau(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int64_t T,
                              const int32_t* row_seq, const int64_t* row_limit, int32_t k, StreamRow* rows,
-                             uint32_t* hist, uint32_t* samp, hipStream_t s);
+                             uint32_t* hist, uint32_t* samp, hipStream_t s, const PageMap& pm);
 int64_t index_sample_words();
 
 // blocks per row whose counts the candidate scan writes
 int64_t index_scan_blocks(int64_t T);
+
+// page-table arguments of the paged entry points: a table, a page size that is a
+// multiple of kPageQuantum positions, and room for T positions
+constexpr int32_t kPageQuantum = 128;
+csa2_status check_pages(const int32_t* block_table, int64_t max_blocks, int32_t page, int64_t T);
 
 // whether csa2_index_full uses the streaming scan (decode) rather than the
 // query-block kernel (chunked prefill) for this row layout

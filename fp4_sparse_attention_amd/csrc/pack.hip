@@ -88,12 +88,15 @@ __device__ __forceinline__ void pack_block(const uint32_t* w, uint32_t& lo, uint
 __global__ void __launch_bounds__(256)
 fp4_pack_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int parts_per_row, int64_t x_stride,
                 uint8_t* __restrict__ codes, int64_t codes_stride, uint8_t* __restrict__ scales,
-                int64_t scales_stride) {
+                int64_t scales_stride, const int64_t* __restrict__ out_rows) {
   const int64_t total = n_rows * parts_per_row;
   for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
        g += (int64_t)gridDim.x * blockDim.x) {
     int64_t row = g / parts_per_row;
     int part = (int)(g - row * parts_per_row);
+    // output row: the input row's own, or (scatter) out_rows[row]; a negative entry skips the row
+    const int64_t orow = out_rows ? out_rows[row] : row;
+    if (orow < 0) continue;
     const uint4* src = reinterpret_cast<const uint4*>(x + row * x_stride + part * 32);
     uint4 v0 = ld_nt16(src + 0);
     uint4 v1 = ld_nt16(src + 1);
@@ -104,8 +107,8 @@ fp4_pack_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int parts_per_ro
     uint32_t c0, c1, c2, c3, s0, s1;
     pack_block(w0, c0, c1, s0);
     pack_block(w1, c2, c3, s1);
-    *reinterpret_cast<uint4*>(codes + row * codes_stride + part * 16) = make_uint4(c0, c1, c2, c3);
-    *reinterpret_cast<uint16_t*>(scales + row * scales_stride + part * 2) = (uint16_t)(s0 | (s1 << 8));
+    *reinterpret_cast<uint4*>(codes + orow * codes_stride + part * 16) = make_uint4(c0, c1, c2, c3);
+    *reinterpret_cast<uint16_t*>(scales + orow * scales_stride + part * 2) = (uint16_t)(s0 | (s1 << 8));
   }
 }
 
@@ -174,7 +177,24 @@ extern "C" csa2_status csa2_fp4_pack(const uint16_t* x, int64_t n_rows, int32_t 
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2)) return CSA2_EALIGN;
   int parts = C / 32;
   fp4_pack_kernel<<<stream_grid(n_rows * parts), 256, 0, (hipStream_t)stream>>>(
-      x, n_rows, parts, x_row_stride, codes, codes_row_stride, scales, scales_row_stride);
+      x, n_rows, parts, x_row_stride, codes, codes_row_stride, scales, scales_row_stride, nullptr);
+  return launch_status();
+}
+
+extern "C" csa2_status csa2_fp4_pack_rows(const uint16_t* x, int64_t n_rows, int32_t C, int64_t x_row_stride,
+                                          const int64_t* out_rows, uint8_t* codes, int64_t codes_row_stride,
+                                          uint8_t* scales, int64_t scales_row_stride, void* stream) {
+  if (n_rows < 0) return CSA2_EINVAL;
+  if (C <= 0 || C % 32 != 0) return CSA2_ESHAPE;
+  if (x_row_stride < C || x_row_stride % 8 != 0) return CSA2_EINVAL;
+  if (codes_row_stride < C / 2 || codes_row_stride % 16 != 0) return CSA2_EINVAL;
+  if (scales_row_stride < C / 16 || scales_row_stride % 2 != 0) return CSA2_EINVAL;
+  if (n_rows == 0) return CSA2_OK;
+  if (!x || !out_rows || !codes || !scales) return CSA2_EINVAL;
+  if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(out_rows, 8)) return CSA2_EALIGN;
+  int parts = C / 32;
+  fp4_pack_kernel<<<stream_grid(n_rows * parts), 256, 0, (hipStream_t)stream>>>(
+      x, n_rows, parts, x_row_stride, codes, codes_row_stride, scales, scales_row_stride, out_rows);
   return launch_status();
 }
 

@@ -1170,14 +1170,13 @@ __device__ __forceinline__ RowBins row_bins(const uint32_t* hr, uint32_t tau_s, 
 // blk0 + w, blk0 + w + 4, ...), and hist_abs the top 12 bits of those keys.
 __device__ void rebuild_blocks(const uint8_t* q_idx, const uint8_t* k_idx, int64_t T, int r, const int32_t* row_seq,
                                const int64_t* row_limit, int64_t blk0, int64_t blk1, uint2* kp, uint32_t* cn,
-                               uint32_t* hist_abs, uint32_t* h /* 4096, LDS */) {
+                               uint32_t* hist_abs, uint32_t* h /* 4096, LDS */, const PageMap& pm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int half = lane >> 5, col = lane & 31;
   for (int i = tid; i < kStreamBins; i += kSG) h[i] = 0u;
   __syncthreads();
   const int seq = row_seq ? row_seq[r] : r;
   const int64_t limit = row_limit ? row_limit[r] : T - 1;
-  const uint8_t* kseq = k_idx + (int64_t)seq * T * kIndexDim;
   f16x8 a[4];
   query_operands(q_idx + (int64_t)r * kIndexDim, lane, a);
   for (int64_t blk = blk0 + wave; blk < blk1; blk += 4) {
@@ -1185,9 +1184,11 @@ __device__ void rebuild_blocks(const uint8_t* q_idx, const uint8_t* k_idx, int64
     bool ok[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t p = blk * kBlockPositions + 32 * i + col;
-      ok[i] = p < T && p <= limit;
-      kb[i] = ok[i] ? load_half_key(kseq + p * kIndexDim + 32 * half) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      const int64_t p0 = blk * kBlockPositions + 32 * i;
+      const int64_t row0 = p0 < T ? phys_row(pm, seq, T, p0) : -1;
+      const int64_t p = p0 + col;
+      ok[i] = row0 >= 0 && p < T && p <= limit;
+      kb[i] = ok[i] ? load_half_key(k_idx + (row0 + col) * kIndexDim + 32 * half) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
     }
     uint32_t at = 0;
 #pragma unroll
@@ -1218,7 +1219,7 @@ stream_gather_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restric
                      const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit, int64_t nbk, int bpw,
                      StreamRow* __restrict__ rows, uint32_t* __restrict__ hist, uint2* __restrict__ cand,
                      uint32_t* __restrict__ cand_cnt, uint32_t* __restrict__ above_out, uint2* __restrict__ list,
-                     int32_t k, int32_t k2) {
+                     int32_t k, int32_t k2, PageMap pm) {
   __shared__ uint32_t tmp[8];
   __shared__ uint32_t s_b[6];
   __shared__ uint32_t h[kStreamBins];
@@ -1234,7 +1235,7 @@ stream_gather_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restric
   if (blk0 + tid < blk1) hd0 = load_head(kp, cn, blk0 + tid);
   const RowBins rb = row_bins(hr, tau_s, k, k2, tmp, s_b);
   if (rb.rebuild) {
-    rebuild_blocks(q_idx, k_idx, T, r, row_seq, row_limit, blk0, blk1, kp, cn, hr + kStreamBins, h);
+    rebuild_blocks(q_idx, k_idx, T, r, row_seq, row_limit, blk0, blk1, kp, cn, hr + kStreamBins, h, pm);
     return;
   }
   if (rb.overflow || rb.k_eff[0] == 0u) return;
@@ -1818,12 +1819,11 @@ extern "C" size_t csa2_index_full_pool_workspace_size(int32_t R, int64_t T, int3
   return std::max(other, pool_may_stream(R, T) ? stream_layout(R, T).total : (size_t)0);
 }
 
-extern "C" csa2_status csa2_index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int32_t B,
-                                            int64_t T, const int32_t* row_seq, const int64_t* row_limit,
-                                            float* scores, int32_t k_pool, int32_t k_top, int32_t* pool_idx,
-                                            float* pool_scores, int32_t* top_idx, void* workspace,
-                                            size_t workspace_bytes, void* scan_start, void* scan_end,
-                                            void* stream) {
+static csa2_status index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int32_t B, int64_t T,
+                                   const int32_t* row_seq, const int64_t* row_limit, float* scores, int32_t k_pool,
+                                   int32_t k_top, int32_t* pool_idx, float* pool_scores, int32_t* top_idx,
+                                   void* workspace, size_t workspace_bytes, void* scan_start, void* scan_end,
+                                   void* stream, const PageMap& pm) {
   if (!q_idx || !k_idx || !pool_idx || !top_idx) return CSA2_EINVAL;
   if (R <= 0 || B <= 0 || T <= 0 || k_pool <= 0 || k_top <= 0 || k_top > k_pool) return CSA2_EINVAL;
   if (!row_seq && R != B) return CSA2_EINVAL;
@@ -1834,13 +1834,19 @@ extern "C" csa2_status csa2_index_full_pool(const uint8_t* q_idx, const uint8_t*
   if (!workspace || workspace_bytes < csa2_index_full_pool_workspace_size(R, T, k_pool)) return CSA2_EWORKSPACE;
   if (!aligned(workspace, 256)) return CSA2_EALIGN;
   hipStream_t s = (hipStream_t)stream;
-  if (!pool_may_stream(R, T) || !index_scan_streams(R, row_seq)) {
+  if (!pool_may_stream(R, T) || (!pm.table && !index_scan_streams(R, row_seq))) {
     // short rows, very long R x T, or query blocks: scores first (into the
     // workspace when the caller takes none), then the selection
     const size_t tk = align_up(csa2_topk_workspace_size(R, T, k_pool), 256);
     float* sc = scores ? scores : reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + tk);
     if (scan_start && hipEventRecord((hipEvent_t)scan_start, s) != hipSuccess) return CSA2_ELAUNCH;
-    csa2_status st = csa2_index_full(q_idx, k_idx, R, B, T, row_seq, row_limit, sc, stream);
+    csa2_status st = CSA2_OK;
+    if (pm.table) {
+      launch_index_scan(q_idx, k_idx, R, T, row_seq, row_limit, sc, nullptr, s, pm);
+      st = launch_status();
+    } else {
+      st = csa2_index_full(q_idx, k_idx, R, B, T, row_seq, row_limit, sc, stream);
+    }
     if (st != CSA2_OK) return st;
     if (scan_end && hipEventRecord((hipEvent_t)scan_end, s) != hipSuccess) return CSA2_ELAUNCH;
     return csa2_topk_pool(sc, R, T, T, k_pool, k_top, nullptr, pool_idx, pool_scores, top_idx, workspace, tk,
@@ -1859,15 +1865,42 @@ extern "C" csa2_status csa2_index_full_pool(const uint8_t* q_idx, const uint8_t*
   const int64_t nbk = index_scan_blocks(T);
   const int groups = (int)std::min<int64_t>(kStreamGroups, nbk);
   const int bpw = (int)((nbk + groups - 1) / groups);
-  launch_index_sample_tau(q_idx, k_idx, R, T, row_seq, row_limit, k_pool, rows, hist, samp, s);
+  launch_index_sample_tau(q_idx, k_idx, R, T, row_seq, row_limit, k_pool, rows, hist, samp, s, pm);
   if (scan_start && hipEventRecord((hipEvent_t)scan_start, s) != hipSuccess) return CSA2_ELAUNCH;
   const CandOut co{rows, hist, cand, cnt, nbk};
-  launch_index_scan(q_idx, k_idx, R, T, row_seq, row_limit, scores, &co, s);
+  launch_index_scan(q_idx, k_idx, R, T, row_seq, row_limit, scores, &co, s, pm);
   if (scan_end && hipEventRecord((hipEvent_t)scan_end, s) != hipSuccess) return CSA2_ELAUNCH;
   stream_gather_kernel<<<dim3(groups, R), kSG, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, nbk, bpw, rows, hist,
-                                                       cand, cnt, above, list, k_pool, k_top);
+                                                       cand, cnt, above, list, k_pool, k_top, pm);
   stream_finish_kernel<<<R, kSG, 0, s>>>(T, nbk, bpw, groups, rows, hist, above, list, cand, cnt, base, k_pool, k_top);
   stream_write_kernel<<<dim3(groups, R), kSG, 0, s>>>(T, nbk, bpw, rows, base, cand, cnt, k_pool, k_top, pool_idx,
                                                       pool_scores, top_idx);
   return launch_status();
+}
+
+extern "C" csa2_status csa2_index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int32_t B,
+                                            int64_t T, const int32_t* row_seq, const int64_t* row_limit,
+                                            float* scores, int32_t k_pool, int32_t k_top, int32_t* pool_idx,
+                                            float* pool_scores, int32_t* top_idx, void* workspace,
+                                            size_t workspace_bytes, void* scan_start, void* scan_end,
+                                            void* stream) {
+  return index_full_pool(q_idx, k_idx, R, B, T, row_seq, row_limit, scores, k_pool, k_top, pool_idx, pool_scores,
+                         top_idx, workspace, workspace_bytes, scan_start, scan_end, stream, PageMap{});
+}
+
+extern "C" size_t csa2_index_full_pool_paged_workspace_size(int32_t R, int64_t T, int32_t k_pool) {
+  return csa2_index_full_pool_workspace_size(R, T, k_pool);
+}
+
+extern "C" csa2_status csa2_index_full_pool_paged(const uint8_t* q_idx, const uint8_t* k_pages, int32_t R, int32_t B,
+                                                  int64_t T, const int32_t* row_seq, const int64_t* row_limit,
+                                                  const int32_t* block_table, int64_t max_blocks, int32_t page,
+                                                  float* scores, int32_t k_pool, int32_t k_top, int32_t* pool_idx,
+                                                  float* pool_scores, int32_t* top_idx, void* workspace,
+                                                  size_t workspace_bytes, void* stream) {
+  csa2_status st = check_pages(block_table, max_blocks, page, T);
+  if (st != CSA2_OK) return st;
+  return index_full_pool(q_idx, k_pages, R, B, T, row_seq, row_limit, scores, k_pool, k_top, pool_idx, pool_scores,
+                         top_idx, workspace, workspace_bytes, nullptr, nullptr, stream,
+                         PageMap{block_table, max_blocks, page});
 }

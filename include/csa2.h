@@ -323,6 +323,68 @@ csa2_status csa2_sparse_swa_decode_layers(int32_t L, const uint16_t* q_lat, int3
                                           const int32_t* swa_len, float softmax_scale, float* o, float* lse,
                                           void* workspace, size_t workspace_bytes, void* stream);
 
+
+/* ===========================================================================
+ * Paged global KV (the Hugging Face paper page's abstract: the global KV cache
+ * is kept whole in HBM for serving; mixed serving batches hold sequences of
+ * different lengths).  The layout is this library's: every per-position
+ * tensor of the cache (the index keys, the FP4 codes and scales) lives in a
+ * page pool of n_pages pages of `page` positions, and sequence b's logical
+ * position p sits in physical row block_table[b][p / page] * page + p % page
+ * of each pool.
+ *
+ *   block_table  int32 [B][max_blocks] (device): the page of each logical
+ *                block of each sequence; a negative entry leaves the block
+ *                unmapped (its positions count as invisible)
+ *   page         positions per page, a positive multiple of 128 (every
+ *                32-position scoring tile lies in one page)
+ *   T            the logical capacity, T <= max_blocks * page; a sequence's
+ *                own length goes in row_limit / swa_len as in the dense calls
+ * The paged calls compute exactly what their dense counterparts compute on
+ * the logical sequences.  Extra errors: EINVAL (null table, max_blocks <= 0,
+ * page <= 0), ESHAPE (page not a multiple of 128, T > max_blocks * page).
+ * ------------------------------------------------------------------------- */
+
+/* csa2_fp4_pack with scattered output rows: input row i goes to row
+ * out_rows[i] of codes / scales (a negative entry skips the row), e.g. each
+ * sequence's new token into its page slot.  out_rows int64 [n_rows] (device,
+ * 8-byte aligned).  Other arguments and errors as csa2_fp4_pack. */
+csa2_status csa2_fp4_pack_rows(const uint16_t* x, int64_t n_rows, int32_t C, int64_t x_row_stride,
+                               const int64_t* out_rows, uint8_t* codes, int64_t codes_row_stride,
+                               uint8_t* scales, int64_t scales_row_stride, void* stream);
+
+/* csa2_index_full over paged keys: k_pages uint8 [n_pages * page][64]. */
+csa2_status csa2_index_full_paged(const uint8_t* q_idx, const uint8_t* k_pages, int32_t R, int32_t B, int64_t T,
+                                  const int32_t* row_seq, const int64_t* row_limit, const int32_t* block_table,
+                                  int64_t max_blocks, int32_t page, float* scores, void* stream);
+
+/* csa2_index_reindex over paged keys (pool entries are logical positions). */
+csa2_status csa2_index_reindex_paged(const uint8_t* q_idx, const uint8_t* k_pages, int32_t R, int32_t B,
+                                     int64_t T, const int32_t* row_seq, const int32_t* block_table,
+                                     int64_t max_blocks, int32_t page, const int32_t* pool, int32_t P,
+                                     float* scores, void* stream);
+
+/* csa2_index_full_pool over paged keys (scores may be NULL as there; outputs
+ * are logical positions).  Workspace as for the dense call. */
+size_t csa2_index_full_pool_paged_workspace_size(int32_t R, int64_t T, int32_t k_pool);
+csa2_status csa2_index_full_pool_paged(const uint8_t* q_idx, const uint8_t* k_pages, int32_t R, int32_t B,
+                                       int64_t T, const int32_t* row_seq, const int64_t* row_limit,
+                                       const int32_t* block_table, int64_t max_blocks, int32_t page,
+                                       float* scores, int32_t k_pool, int32_t k_top, int32_t* pool_idx,
+                                       float* pool_scores, int32_t* top_idx, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/* csa2_sparse_swa_decode_layers over paged FP4 rows: code_pages uint8
+ * [n_pages * page][256], scale_pages uint8 [n_pages * page][32]; idx holds
+ * logical positions.  Workspace: csa2_sparse_swa_decode_layers_workspace_size. */
+csa2_status csa2_sparse_swa_decode_layers_paged(int32_t L, const uint16_t* q_lat, int32_t R, int32_t H,
+                                                const uint8_t* code_pages, const uint8_t* scale_pages, int32_t B,
+                                                int64_t T, const int32_t* row_seq, const int32_t* block_table,
+                                                int64_t max_blocks, int32_t page, const int32_t* idx,
+                                                const int32_t* layer_idx, int32_t K, const uint16_t* swa, int32_t S,
+                                                const int32_t* swa_start, const int32_t* swa_len,
+                                                float softmax_scale, float* o, float* lse, void* workspace,
+                                                size_t workspace_bytes, void* stream);
 #ifdef __cplusplus
 }
 #endif

@@ -26,9 +26,10 @@ Module map:
   topk       Top-K / candidate-pool selection                         [HN], [MTP] ¶3
   attention  sparse attention, sliding window, log-sum-exp merge      [HN], [MTP] ¶2, [FO]
   pipeline   one decode layer in Full / Reindex / Reuse role          [MTP] ¶3, [FO]
+  paging     logical view of a paged global KV pool                    [HF] abstract
 
 Parity pins: every function is checked by tests marked "not gpu" against
 closed forms, brute force, library routines or invariants; see the test files
 named test_oracle_*.py.  No function here is "parity unpinned".
 """
-from . import formats, indexer, topk, attention, pipeline  # noqa: F401
+from . import formats, indexer, topk, attention, pipeline, paging  # noqa: F401

@@ -157,3 +157,36 @@ def test_index_full_pool_argument_errors():
     # scores may be null: the argument checks still run (and fail here on the workspace, before any launch)
     a = list(base); a[7] = NULL; a[14] = 16
     assert L.csa2_index_full_pool(*a) == 4
+
+
+def test_paged_argument_errors():
+    L = F.lib()
+    # page map: null table / max_blocks <= 0 / page <= 0 -> EINVAL; page % 128, T > capacity -> ESHAPE
+    assert L.csa2_index_full_paged(DUMMY, DUMMY, 1, 1, 256, NULL, NULL, NULL, 2, 128, DUMMY, NULL) == 1
+    assert L.csa2_index_full_paged(DUMMY, DUMMY, 1, 1, 256, NULL, NULL, DUMMY, 0, 128, DUMMY, NULL) == 1
+    assert L.csa2_index_full_paged(DUMMY, DUMMY, 1, 1, 256, NULL, NULL, DUMMY, 2, 0, DUMMY, NULL) == 1
+    assert L.csa2_index_full_paged(DUMMY, DUMMY, 1, 1, 256, NULL, NULL, DUMMY, 2, 192, DUMMY, NULL) == 2
+    assert L.csa2_index_full_paged(DUMMY, DUMMY, 1, 1, 384, NULL, NULL, DUMMY, 2, 128, DUMMY, NULL) == 2
+    assert L.csa2_index_full_paged(DUMMY, DUMMY, 2, 1, 256, NULL, NULL, DUMMY, 2, 128, DUMMY, NULL) == 1
+    assert L.csa2_index_reindex_paged(DUMMY, DUMMY, 1, 1, 256, NULL, DUMMY, 1, 128, DUMMY, 8, DUMMY, NULL) == 2
+    assert L.csa2_index_reindex_paged(DUMMY, DUMMY, 1, 1, 256, NULL, NULL, 2, 128, DUMMY, 8, DUMMY, NULL) == 1
+    ws = F.csa2_index_full_pool_paged_workspace_size(1, 4096, 512)
+    assert ws == F.csa2_index_full_pool_workspace_size(1, 4096, 512)
+    assert L.csa2_index_full_pool_paged(DUMMY, DUMMY, 1, 1, 4096, NULL, NULL, DUMMY, 8, 256, DUMMY, 512, 64,
+                                        DUMMY, NULL, DUMMY, DUMMY, ws, NULL) == 2        # 8 x 256 < 4096
+    assert L.csa2_index_full_pool_paged(DUMMY, DUMMY, 1, 1, 4096, NULL, NULL, NULL, 16, 256, DUMMY, 512, 64,
+                                        DUMMY, NULL, DUMMY, DUMMY, ws, NULL) == 1
+    assert L.csa2_index_full_pool_paged(DUMMY, DUMMY, 1, 1, 4096, NULL, NULL, DUMMY, 16, 256, DUMMY, 512, 64,
+                                        DUMMY, NULL, DUMMY, DUMMY, 16, NULL) == 4        # workspace too small
+    # scattered pack: output-row list must be given (and 8-byte aligned)
+    assert L.csa2_fp4_pack_rows(DUMMY, 2, 512, 512, NULL, DUMMY, 256, DUMMY, 32, NULL) == 1
+    assert L.csa2_fp4_pack_rows(DUMMY, 2, 512, 512, ctypes.c_void_p(260), DUMMY, 256, DUMMY, 32, NULL) == 3
+    assert L.csa2_fp4_pack_rows(DUMMY, 2, 500, 512, DUMMY, DUMMY, 256, DUMMY, 32, NULL) == 2
+    assert L.csa2_fp4_pack_rows(DUMMY, 0, 512, 512, NULL, NULL, 256, NULL, 32, NULL) == 0
+    # attention over pages: null table, then a page size off the quantum
+    host_idx = (ctypes.c_int32 * 1)(0)
+    args = lambda table, page: (1, DUMMY, 1, 64, DUMMY, DUMMY, 1, 256, NULL, table, 2, page, DUMMY,
+                                ctypes.cast(host_idx, ctypes.c_void_p), 64, DUMMY, 128, DUMMY, DUMMY,
+                                ctypes.c_float(0.05), DUMMY, DUMMY, DUMMY, 1 << 30, NULL)
+    assert L.csa2_sparse_swa_decode_layers_paged(*args(NULL, 128)) == 1
+    assert L.csa2_sparse_swa_decode_layers_paged(*args(DUMMY, 100)) == 2
