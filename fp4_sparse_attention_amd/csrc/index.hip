@@ -4,21 +4,18 @@
 //
 // score(r, j) = sum_{d<64} q_idx[r][d] * k_idx[seq(r)][j][d] with E4M3 inputs.
 // The E4M3 bytes are widened to f16 (exact, v_cvt_scalef32_pk_f16_fp8 with unit
-// scale) and multiplied on the f16 matrix cores:
-//   v_mfma_f32_32x32x16_f16:  C[32 x 32] += A[32 x 16] * B[16 x 32], four k-steps
-// with A = up to 32 query rows of one sequence and B = 32 keys.  On gfx950 this
-// instruction forms each 16-term dot product exactly and rounds it once into
-// the fp32 accumulator, so a score carries at most four roundings (one per
-// k-step, error <= 2^-22 * sum |q_d k_d|); whenever the running sums fit in 24
-// bits -- as for unit-normal E4M3 inputs -- the score is the exact value
-// rounded once.  (The fp8 matrix path is not used: its internal accumulation
-// keeps only ~20 bits below the largest product.)  Lane l owns row/column
-// (l % 32) and one 32-byte half of the 64-d
-// key, so a wave loads a 2 KB tile of 32 consecutive keys with two 16-byte
-// loads per lane (fully coalesced); A and B use the same lane->k map.
-// Output C: lane l, register v holds column l % 32 and row
-// 8*(v/4) + 4*(l/32) + (v%4); row 0 sits in register 0 of lanes 0-31, which
-// store 32 consecutive scores as one 128-byte line.
+// scale) and multiplied on the f16 matrix cores, v_mfma_f32_16x16x32_f16
+// (C[16 x 16] += A[16 x 32] * B[32 x 16]), in the tile layout of tile.hpp: a
+// tile is 32 keys, each 16-key half takes two k-steps of 32 channels, and A
+// holds the query in row 0 (decode) or 16 query rows of one sequence (chunked
+// prefill), so every kernel forms a score from the same two steps and all of
+// them agree bit for bit.  The products are exact; the matrix core adds a
+// step's 32 products and the accumulator, rounding to fp32.  For unit-normal
+// E4M3 inputs the score is the exact value rounded once; over the whole E4M3
+// range the error measured stays below 2^-21 * sum |q_d k_d|.  (The fp8 matrix
+// path is not used: its internal accumulation keeps only ~20 bits below the
+// largest product.)  Each of a lane's two 16-byte loads per tile lies in a 1 KB
+// stretch of 16 whole keys that the wave reads together.
 //
 // Decode (one query per sequence) is HBM-bound: 64 bytes of key per score; the
 // matrix cores and the conversions use a small share of their peak.  Chunked
@@ -41,22 +38,15 @@ index_rows_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__
   const int r = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int half = lane >> 5;
-  const int col_in_tile = lane & 31;
+  const int kn = lane & 15;          // the lane's keys kn and kn + 16 of each tile
+  const int part = 16 * (lane >> 4); // and its 16 bytes of them
   const int seq = row_seq ? row_seq[r] : r;
   const int64_t limit = row_limit ? row_limit[r] : T - 1;
   float* out = scores + (int64_t)r * n_cols;
   const int32_t* prow = kGather ? pool + (int64_t)r * n_cols : nullptr;
 
-  i32x8 araw = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (col_in_tile == 0) {
-    const uint4* q = reinterpret_cast<const uint4*>(q_idx + (int64_t)r * kIndexDim + 32 * half);
-    uint4 x = q[0], y = q[1];
-    araw[0] = x.x; araw[1] = x.y; araw[2] = x.z; araw[3] = x.w;
-    araw[4] = y.x; araw[5] = y.y; araw[6] = y.z; araw[7] = y.w;
-  }
-  f16x8 a[4];
-  fp8x32_to_f16(araw, a);
+  f16x8 a[2];
+  query_operands(q_idx + (int64_t)r * kIndexDim, lane, a);
 
   const int64_t n_tiles = (n_cols + kTile - 1) / kTile;
   const int64_t t_begin = (int64_t)blockIdx.x * tiles_per_block;
@@ -65,26 +55,31 @@ index_rows_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__
 
   for (int64_t t0 = t_begin + wave; t0 < t_end; t0 += 4 * kUnroll) {
     i32x8 b[kUnroll];
-    int64_t pos[kUnroll];
-    bool ok[kUnroll];
+    bool ok[kUnroll][2];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      int64_t t = t0 + 4 * u;
-      int64_t c = t * kTile + col_in_tile;
-      int64_t p = -1;
-      if (t < t_end && c < n_cols) p = kGather ? (int64_t)prow[c] : c;
-      ok[u] = p >= 0 && p < T && p <= limit;
-      const int64_t row = ok[u] ? phys_row(pm, seq, T, p) : -1;
-      ok[u] = row >= 0;
-      pos[u] = c;
-      b[u] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-      if (ok[u]) b[u] = load_half_key(k_idx + row * kIndexDim + 32 * half);
+      const int64_t t = t0 + 4 * u;
+      uint4 v[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t c = t * kTile + 16 * h + kn;
+        int64_t p = -1;
+        if (t < t_end && c < n_cols) p = kGather ? (int64_t)prow[c] : c;
+        const int64_t row = (p >= 0 && p < T && p <= limit) ? phys_row(pm, seq, T, p) : -1;
+        ok[u][h] = row >= 0;
+        v[h] = ok[u][h] ? load_key_part(k_idx + row * kIndexDim + part) : make_uint4(0, 0, 0, 0);
+      }
+      b[u] = tile_pair(v[0], v[1]);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      int64_t t = t0 + 4 * u;
-      f32x16 acc = mfma_score(a, b[u]);
-      if (t < t_end && half == 0 && pos[u] < n_cols) out[pos[u]] = ok[u] ? acc[0] : neg_inf;
+      const int64_t t = t0 + 4 * u;
+      const float2 sc = mfma_score(a, b[u]);
+      const int64_t c = t * kTile + kn;
+      if (t < t_end && lane < 16) {
+        if (c < n_cols) out[c] = ok[u][0] ? sc.x : neg_inf;
+        if (c + 16 < n_cols) out[c + 16] = ok[u][1] ? sc.y : neg_inf;
+      }
     }
   }
 }
@@ -103,7 +98,8 @@ index_rows_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__
 //    its block's candidates (visible keys >= tau_s) in position order at the
 //    block's start as (key, position) pairs (ballot ranks, no atomics), with the
 //    block's count; the workgroup counts the candidates' histogram digits in
-//    LDS, keeps the list of bins it touched and adds those counts to the row's
+//    LDS (atomics without return: a returning atomic per candidate tile stalled
+//    the wave, 17 us of the 8 x 1M scan) and adds its nonzero bins to the row's
 //    histogram when it leaves the row (once per workgroup; with row-major
 //    order every workgroup would flush at each row boundary, measured slower).
 constexpr int kUnitTiles = 16;
@@ -114,12 +110,10 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
                     const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit,
                     float* __restrict__ scores, int R, int64_t units_per_row, CandOut cand, PageMap pm) {
   __shared__ uint32_t h[kCand ? kStreamBins : 1];
-  __shared__ uint32_t used[kCand ? kStreamBins : 1];   // bins of h that are nonzero, in the order first hit
-  __shared__ uint32_t n_used;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int half = lane >> 5;
-  const int col_in_tile = lane & 31;
+  const int kn = lane & 15;          // the lane's keys kn and kn + 16 of each tile
+  const int part = 16 * (lane >> 4); // and its 16 bytes of them
   const float neg_inf = -__builtin_inff();
   const int G = gridDim.x;
   const int b = blockIdx.x;
@@ -169,7 +163,7 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
 
   struct Unit {
     i32x8 b[kUnroll];
-    bool ok[kUnroll];
+    bool ok[kUnroll][2];
   };
   auto fetch = [&](int rr, int64_t jj, Unit& x) {
     const int64_t t0 = tile_of(jj);
@@ -180,22 +174,20 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
       // a tile never straddles a page: one translation per tile
       const int64_t p0 = (t0 + i) * kTile;
       const int64_t row0 = p0 < T ? phys_row(pm, seq, T, p0) : -1;
-      const int64_t p = p0 + col_in_tile;
-      x.ok[i] = row0 >= 0 && p < T && p <= limit;
-      x.b[i] = x.ok[i] ? load_half_key<kCand>(k_idx + (row0 + col_in_tile) * kIndexDim + 32 * half)
-                       : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      uint4 v[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int64_t p = p0 + 16 * hh + kn;
+        x.ok[i][hh] = row0 >= 0 && p < T && p <= limit;
+        v[hh] = x.ok[i][hh] ? load_key_part<kCand>(k_idx + (row0 + 16 * hh + kn) * kIndexDim + part)
+                            : make_uint4(0, 0, 0, 0);
+      }
+      x.b[i] = tile_pair(v[0], v[1]);
     }
   };
   uint32_t tau = 0, sh = 0;
   auto query = [&](int rr, f16x8* a) {
-    i32x8 araw = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (col_in_tile == 0) {
-      const uint4* q = reinterpret_cast<const uint4*>(q_idx + (int64_t)rr * kIndexDim + 32 * half);
-      const uint4 x = q[0], y = q[1];
-      araw[0] = x.x; araw[1] = x.y; araw[2] = x.z; araw[3] = x.w;
-      araw[4] = y.x; araw[5] = y.y; araw[6] = y.z; araw[7] = y.w;
-    }
-    fp8x32_to_f16(araw, a);
+    query_operands(q_idx + (int64_t)rr * kIndexDim, lane, a);
     if (kCand) {
       tau = uniform_u32(cand.row[rr].tau_s);
       sh = uniform_u32(cand.row[rr].sh);
@@ -204,25 +196,23 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
   auto flush = [&](int rr) {
     __syncthreads();
     uint32_t* g = cand.hist + (int64_t)rr * kStreamHistWords;
-    const uint32_t n = n_used;
-    for (uint32_t i = threadIdx.x; i < n; i += 256) {
-      const uint32_t bin = used[i];
-      atomicAdd(&g[bin], h[bin]);
-      h[bin] = 0u;
+    for (int i = threadIdx.x; i < kStreamBins; i += 256) {
+      const uint32_t v = h[i];
+      if (v) {
+        atomicAdd(&g[i], v);
+        h[i] = 0u;
+      }
     }
-    __syncthreads();
-    if (threadIdx.x == 0) n_used = 0u;   // every thread has read n_used before the barrier above
     __syncthreads();
   };
 
   if (kCand) {
     for (int i = threadIdx.x; i < kStreamBins; i += 256) h[i] = 0u;
-    if (threadIdx.x == 0) n_used = 0u;
     __syncthreads();
   }
   Unit cur, nxt;
   fetch(r, j, cur);
-  f16x8 a[4];
+  f16x8 a[2];
   query(r, a);
   while (r < R) {
     int rn = r;
@@ -231,15 +221,19 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
     if (rn < R) fetch(rn, jn, nxt);
     const int64_t t0 = tile_of(j);
     float* out = scores ? scores + (int64_t)r * T : nullptr;
-    uint32_t key[kUnroll];
+    uint32_t key[kUnroll][2];
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
-      const f32x16 acc = mfma_score(a, cur.b[i]);
-      const int64_t p = (t0 + i) * kTile + col_in_tile;
-      key[i] = 0u;
-      if (half == 0 && p < T) {
-        if (!kCand || scores) out[p] = cur.ok[i] ? acc[0] : neg_inf;
-        if (kCand && cur.ok[i]) key[i] = score_key(acc[0]);
+      const float2 sc = mfma_score(a, cur.b[i]);
+      const float sv[2] = {sc.x, sc.y};
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int64_t p = (t0 + i) * kTile + 16 * hh + kn;
+        key[i][hh] = 0u;
+        if (lane < 16 && p < T) {
+          if (!kCand || scores) out[p] = cur.ok[i][hh] ? sv[hh] : neg_inf;
+          if (kCand && cur.ok[i][hh]) key[i][hh] = score_key(sv[hh]);
+        }
       }
     }
     if (kCand) {
@@ -249,15 +243,17 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
       uint32_t at = 0;
 #pragma unroll
       for (int i = 0; i < kUnroll; ++i) {
-        const bool c = key[i] != 0u && key[i] >= tau;
-        const uint64_t m = __ballot(c);
-        if (c) {
-          const uint32_t o = at + lanes_below(m);
-          oc[o] = make_uint2(key[i], (uint32_t)((t0 + i) * kTile + col_in_tile));
-          const uint32_t bin = min((key[i] - tau) >> sh, (uint32_t)(kStreamBins - 1));
-          if (atomicAdd(&h[bin], 1u) == 0u) used[atomicAdd(&n_used, 1u)] = bin;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const uint32_t kk = key[i][hh];
+          const bool c = kk != 0u && kk >= tau;
+          const uint64_t m = __ballot(c);
+          if (c) {
+            oc[at + lanes_below(m)] = make_uint2(kk, (uint32_t)((t0 + i) * kTile + 16 * hh + kn));
+            atomicAdd(&h[min((kk - tau) >> sh, (uint32_t)(kStreamBins - 1))], 1u);
+          }
+          at += (uint32_t)__popcll(m);
         }
-        at += (uint32_t)__popcll(m);
       }
       if (lane == 0) cand.cnt[(int64_t)r * cand.n_blocks + blk] = at;
     }
@@ -287,39 +283,40 @@ index_sample_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
                     uint32_t* __restrict__ samp, PageMap pm) {
   const int r = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int half = lane >> 5, col_in_tile = lane & 31;
+  const int kn = lane & 15, part = 16 * (lane >> 4);
   const int64_t limit = row_limit ? row_limit[r] : T - 1;
   const int64_t V = limit < 0 ? 0 : (limit + 1 < T ? limit + 1 : T);
   const int seq = row_seq ? row_seq[r] : r;
   constexpr int kRuns = kSampleN / kSampleRun;
   i32x8 kb[2];
-  bool ok[2];
+  bool ok[2][2];
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int64_t i = ((int64_t)(blockIdx.x * 4 + wave) * 2 + u) * kTile + col_in_tile;
-    const int64_t run = i / kSampleRun;
-    int64_t p0 = ((2 * run + 1) * V) / (2 * kRuns) - kSampleRun / 2;
-    p0 = p0 < 0 ? 0 : (p0 > V - kSampleRun ? V - kSampleRun : p0);
-    int64_t p = p0 + i % kSampleRun;
-    p = p < 0 ? 0 : (p >= V ? V - 1 : p);
-    const int64_t row = V > 0 ? phys_row(pm, seq, T, p) : -1;
-    ok[u] = row >= 0;
-    kb[u] = ok[u] ? load_half_key(k_idx + row * kIndexDim + 32 * half) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+    uint4 v[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int64_t i = ((int64_t)(blockIdx.x * 4 + wave) * 2 + u) * kTile + 16 * hh + kn;
+      const int64_t run = i / kSampleRun;
+      int64_t p0 = ((2 * run + 1) * V) / (2 * kRuns) - kSampleRun / 2;
+      p0 = p0 < 0 ? 0 : (p0 > V - kSampleRun ? V - kSampleRun : p0);
+      int64_t p = p0 + i % kSampleRun;
+      p = p < 0 ? 0 : (p >= V ? V - 1 : p);
+      const int64_t row = V > 0 ? phys_row(pm, seq, T, p) : -1;
+      ok[u][hh] = row >= 0;
+      v[hh] = ok[u][hh] ? load_key_part(k_idx + row * kIndexDim + part) : make_uint4(0, 0, 0, 0);
+    }
+    kb[u] = tile_pair(v[0], v[1]);
   }
-  i32x8 araw = {0, 0, 0, 0, 0, 0, 0, 0};
-  if (col_in_tile == 0) {
-    const uint4* q = reinterpret_cast<const uint4*>(q_idx + (int64_t)r * kIndexDim + 32 * half);
-    const uint4 x = q[0], y = q[1];
-    araw[0] = x.x; araw[1] = x.y; araw[2] = x.z; araw[3] = x.w;
-    araw[4] = y.x; araw[5] = y.y; araw[6] = y.z; araw[7] = y.w;
-  }
-  f16x8 a[4];
-  fp8x32_to_f16(araw, a);
+  f16x8 a[2];
+  query_operands(q_idx + (int64_t)r * kIndexDim, lane, a);
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const f32x16 acc = mfma_score(a, kb[u]);
-    const int64_t i = ((int64_t)(blockIdx.x * 4 + wave) * 2 + u) * kTile + col_in_tile;
-    if (half == 0) samp[(int64_t)r * kSampleN + i] = ok[u] ? score_key(acc[0]) : 0u;
+    const float2 sc = mfma_score(a, kb[u]);
+    const int64_t i = ((int64_t)(blockIdx.x * 4 + wave) * 2 + u) * kTile + kn;
+    if (lane < 16) {
+      samp[(int64_t)r * kSampleN + i] = ok[u][0] ? score_key(sc.x) : 0u;
+      samp[(int64_t)r * kSampleN + i + 16] = ok[u][1] ? score_key(sc.y) : 0u;
+    }
   }
 }
 
@@ -415,8 +412,7 @@ index_block_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict_
   const int r0 = blockIdx.y * 32;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int half = lane >> 5;
-  const int l32 = lane & 31;
+  const int kn = lane & 15, g = lane >> 4;
   if (threadIdx.x < 32) {
     int r = r0 + threadIdx.x;
     s_seq[threadIdx.x] = r < R ? (row_seq ? row_seq[r] : r) : -1;
@@ -429,7 +425,6 @@ index_block_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict_
   const int64_t t_end = min(n_tiles, t_begin + tiles_per_block);
   const float neg_inf = -__builtin_inff();
 
-  // rows m held by this lane's output registers
   uint32_t done = 0;
   for (int m = 0; m < 32; ++m)
     if (s_seq[m] < 0) done |= 1u << m;
@@ -446,40 +441,56 @@ index_block_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict_
     for (int m = 0; m < 32; ++m)
       if (active >> m & 1u) max_lim = max(max_lim, s_lim[m]);
 
-    i32x8 araw = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (active >> l32 & 1u) {
-      const uint4* q = reinterpret_cast<const uint4*>(q_idx + (int64_t)(r0 + l32) * kIndexDim + 32 * half);
-      uint4 x = q[0], y = q[1];
-      araw[0] = x.x; araw[1] = x.y; araw[2] = x.z; araw[3] = x.w;
-      araw[4] = y.x; araw[5] = y.y; araw[6] = y.z; araw[7] = y.w;
+    // A operands of the two 16-row halves: lane 16 g + m holds bytes 16 g ..
+    // 16 g + 15 of query row 16 mt + m (the decode layout with every row filled)
+    f16x8 a[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (active >> (16 * mt + kn) & 1u)
+        x = *reinterpret_cast<const uint4*>(q_idx + (int64_t)(r0 + 16 * mt + kn) * kIndexDim + 16 * g);
+      fp8x16_to_f16(x.x, x.y, x.z, x.w, a[mt]);
     }
-    f16x8 a[4];
-    fp8x32_to_f16(araw, a);
     const uint8_t* kseq = k_idx + (int64_t)seq * T * kIndexDim;
 
     for (int64_t t0 = t_begin + wave; t0 < t_end; t0 += 4 * kUnroll) {
       i32x8 b[kUnroll];
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        int64_t t = t0 + 4 * u;
-        int64_t c = t * kTile + l32;
-        b[u] = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
-        if (t < t_end && c < T && t * kTile <= max_lim) b[u] = load_half_key(kseq + c * kIndexDim + 32 * half);
+        const int64_t t = t0 + 4 * u;
+        uint4 v[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int64_t c = t * kTile + 16 * hh + kn;
+          v[hh] = (t < t_end && c < T && t * kTile <= max_lim) ? load_key_part(kseq + c * kIndexDim + 16 * g)
+                                                                 : make_uint4(0, 0, 0, 0);
+        }
+        b[u] = tile_pair(v[0], v[1]);
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        int64_t t = t0 + 4 * u;
+        const int64_t t = t0 + 4 * u;
         if (t >= t_end) break;
-        int64_t c = t * kTile + l32;
-        f32x16 acc = {};
-        if (t * kTile <= max_lim) acc = mfma_score(a, b[u]);
-        if (c < T) {
+        f16x8 kb[2][2];
+        fp8x16_to_f16((uint32_t)b[u][0], (uint32_t)b[u][1], (uint32_t)b[u][2], (uint32_t)b[u][3], kb[0]);
+        fp8x16_to_f16((uint32_t)b[u][4], (uint32_t)b[u][5], (uint32_t)b[u][6], (uint32_t)b[u][7], kb[1]);
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            int m = 8 * (v >> 2) + 4 * half + (v & 3);
-            if ((active >> m & 1u) && r0 + m < R) {
-              float s = c <= s_lim[m] ? acc[v] : neg_inf;
-              scores[(int64_t)(r0 + m) * T + c] = s;
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (t * kTile <= max_lim) {
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][0], kb[hh][0], acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][1], kb[hh][1], acc, 0, 0, 0);
+            }
+            const int64_t c = t * kTile + 16 * hh + kn;
+            if (c < T) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int m = 16 * mt + 4 * g + i;
+                if ((active >> m & 1u) && r0 + m < R)
+                  scores[(int64_t)(r0 + m) * T + c] = c <= s_lim[m] ? acc[i] : neg_inf;
+              }
             }
           }
         }

@@ -1,62 +1,72 @@
-// Indexer tile arithmetic shared by the scoring kernels: 32 keys per
-// v_mfma_f32_32x32x16_f16 tile, E4M3 widened to f16 exactly, the query in one
-// column of A.  Lane l owns key column l % 32 and one 32-byte half of the
-// 64-byte key; the score of key column c sits in register 0 of lane c.
+// Indexer tile arithmetic shared by every scoring kernel, so that all of them
+// round identically: 32 keys per tile on v_mfma_f32_16x16x32_f16, E4M3 widened
+// to f16 exactly.
+//
+// Layout.  Lane l = 16 g + n (g = l / 16, n = l % 16) holds bytes
+// [16 g, 16 g + 16) of the tile's keys n and n + 16: a wave reads the tile's
+// 2 KB as two 1 KB loads that each cover 16 whole keys.  Each half of the tile
+// (keys 0-15, keys 16-31) takes two k-steps; in k-step s the lane supplies its
+// bytes 8 s .. 8 s + 7 as k = 8 g .. 8 g + 7 (the query operand uses the same
+// map in row 0 of A, rows 1-15 zero).  So a score sums channels
+// {16 g + 8 s + j : g < 4, j < 8} in step s and adds the two steps in fp32.
+// Output: C[m][n] sits in register m % 4 of lane 16 (m / 4) + n, so the tile's
+// scores are register 0 of lanes 0-15 (key n in the first accumulator, key
+// n + 16 in the second).
 #pragma once
 
 #include "common.hpp"
 
 namespace csa2 {
 
-constexpr int kTile = 32;          // keys per MFMA tile
+constexpr int kTile = 32;          // keys per tile
 constexpr int kUnroll = 4;         // tiles in flight per wave
 
-// 32 E4M3 bytes (8 dwords) -> four f16x8 MFMA operands, exact
-__device__ __forceinline__ void fp8x32_to_f16(const i32x8& v, f16x8* out) {
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    uint32_t w0 = (uint32_t)v[2 * ks], w1 = (uint32_t)v[2 * ks + 1];
-    f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
-    f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
-    f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
-    f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
-    out[ks] = f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-  }
+// 16 E4M3 bytes -> two f16x8 operands (bytes 0-7, bytes 8-15), exact
+__device__ __forceinline__ void fp8x16_to_f16(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, f16x8* out) {
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  const f16x2 e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w2, 1.0f, false);
+  const f16x2 f = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w2, 1.0f, true);
+  const f16x2 g = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w3, 1.0f, false);
+  const f16x2 h = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w3, 1.0f, true);
+  out[0] = f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  out[1] = f16x8{e[0], e[1], f[0], f[1], g[0], g[1], h[0], h[1]};
 }
 
-// score tile: sum over the four 16-element k-steps of the lane's 32-byte half
-__device__ __forceinline__ f32x16 mfma_score(const f16x8* a, const i32x8& kb) {
-  f16x8 b[4];
-  fp8x32_to_f16(kb, b);
-  f32x16 acc = {};
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks], b[ks], acc, 0, 0, 0);
-  return acc;
-}
-
-// the lane's 32 bytes of a key: nontemporal loads by default (measured best for
-// the candidate scan and the gathers), plain loads with kNT = false (best for
-// the scores-only scan, 108 vs 115 us at 8 x 1M)
+// the lane's 16 bytes of one key (p already offset by 16 g): nontemporal loads
+// by default (measured best for the candidate scan and the gathers), plain
+// loads with kNT = false (best for the scores-only scan)
 template <bool kNT = true>
-__device__ __forceinline__ i32x8 load_half_key(const uint8_t* p) {
-  uint4 x = kNT ? ld_nt16(p) : *reinterpret_cast<const uint4*>(p);
-  uint4 y = kNT ? ld_nt16(p + 16) : *reinterpret_cast<const uint4*>(p + 16);
-  i32x8 r;
-  r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
-  r[4] = y.x; r[5] = y.y; r[6] = y.z; r[7] = y.w;
-  return r;
+__device__ __forceinline__ uint4 load_key_part(const uint8_t* p) {
+  return kNT ? ld_nt16(p) : *reinterpret_cast<const uint4*>(p);
 }
 
-// the query row's four A operands (its 64 bytes in column 0, zero elsewhere)
+// a tile's B data in one register set: part of key n, then part of key n + 16
+__device__ __forceinline__ i32x8 tile_pair(uint4 lo, uint4 hi) {
+  return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+// scores of keys n and n + 16 (valid in lanes 0-15)
+__device__ __forceinline__ float2 mfma_score(const f16x8* a, const i32x8& kb) {
+  f16x8 lo[2], hi[2];
+  fp8x16_to_f16((uint32_t)kb[0], (uint32_t)kb[1], (uint32_t)kb[2], (uint32_t)kb[3], lo);
+  fp8x16_to_f16((uint32_t)kb[4], (uint32_t)kb[5], (uint32_t)kb[6], (uint32_t)kb[7], hi);
+  f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+  c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], lo[0], c0, 0, 0, 0);
+  c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[1], lo[1], c0, 0, 0, 0);
+  c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[0], hi[0], c1, 0, 0, 0);
+  c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[1], hi[1], c1, 0, 0, 0);
+  return make_float2(c0[0], c1[0]);
+}
+
+// the A operands of one query row: lanes 0, 16, 32, 48 hold its bytes 16 g ..
+// 16 g + 15, every other lane zero
 __device__ __forceinline__ void query_operands(const uint8_t* q_row, int lane, f16x8* a) {
-  i32x8 araw = {0, 0, 0, 0, 0, 0, 0, 0};
-  if ((lane & 31) == 0) {
-    const uint4* q = reinterpret_cast<const uint4*>(q_row + 32 * (lane >> 5));
-    const uint4 x = q[0], y = q[1];
-    araw[0] = x.x; araw[1] = x.y; araw[2] = x.z; araw[3] = x.w;
-    araw[4] = y.x; araw[5] = y.y; araw[6] = y.z; araw[7] = y.w;
-  }
-  fp8x32_to_f16(araw, a);
+  uint4 x = make_uint4(0, 0, 0, 0);
+  if ((lane & 15) == 0) x = *reinterpret_cast<const uint4*>(q_row + 16 * (lane >> 4));
+  fp8x16_to_f16(x.x, x.y, x.z, x.w, a);
 }
 
 }  // namespace csa2

@@ -1172,37 +1172,46 @@ __device__ void rebuild_blocks(const uint8_t* q_idx, const uint8_t* k_idx, int64
                                const int64_t* row_limit, int64_t blk0, int64_t blk1, uint2* kp, uint32_t* cn,
                                uint32_t* hist_abs, uint32_t* h /* 4096, LDS */, const PageMap& pm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int half = lane >> 5, col = lane & 31;
+  const int kn = lane & 15, part = 16 * (lane >> 4);
   for (int i = tid; i < kStreamBins; i += kSG) h[i] = 0u;
   __syncthreads();
   const int seq = row_seq ? row_seq[r] : r;
   const int64_t limit = row_limit ? row_limit[r] : T - 1;
-  f16x8 a[4];
+  f16x8 a[2];
   query_operands(q_idx + (int64_t)r * kIndexDim, lane, a);
   for (int64_t blk = blk0 + wave; blk < blk1; blk += 4) {
     i32x8 kb[4];
-    bool ok[4];
+    bool ok[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t p0 = blk * kBlockPositions + 32 * i;
       const int64_t row0 = p0 < T ? phys_row(pm, seq, T, p0) : -1;
-      const int64_t p = p0 + col;
-      ok[i] = row0 >= 0 && p < T && p <= limit;
-      kb[i] = ok[i] ? load_half_key(k_idx + (row0 + col) * kIndexDim + 32 * half) : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+      uint4 v[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int64_t p = p0 + 16 * hh + kn;
+        ok[i][hh] = row0 >= 0 && p < T && p <= limit;
+        v[hh] = ok[i][hh] ? load_key_part(k_idx + (row0 + 16 * hh + kn) * kIndexDim + part) : make_uint4(0, 0, 0, 0);
+      }
+      kb[i] = tile_pair(v[0], v[1]);
     }
     uint32_t at = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const f32x16 acc = mfma_score(a, kb[i]);
-      const uint32_t key = (half == 0 && ok[i]) ? score_key(acc[0]) : 0u;
-      const bool c = key != 0u;
-      const uint64_t m = __ballot(c);
-      if (c) {
-        kp[blk * kBlockPositions + at + lanes_below(m)] =
-            make_uint2(key, (uint32_t)(blk * kBlockPositions + 32 * i + col));
-        atomicAdd(&h[key >> 20], 1u);
+      const float2 sc = mfma_score(a, kb[i]);
+      const float sv[2] = {sc.x, sc.y};
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const uint32_t key = (lane < 16 && ok[i][hh]) ? score_key(sv[hh]) : 0u;
+        const bool c = key != 0u;
+        const uint64_t m = __ballot(c);
+        if (c) {
+          kp[blk * kBlockPositions + at + lanes_below(m)] =
+              make_uint2(key, (uint32_t)(blk * kBlockPositions + 32 * i + 16 * hh + kn));
+          atomicAdd(&h[key >> 20], 1u);
+        }
+        at += (uint32_t)__popcll(m);
       }
-      at += (uint32_t)__popcll(m);
     }
     if (lane == 0) cn[blk] = at;
   }
