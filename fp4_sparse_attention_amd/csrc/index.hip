@@ -174,13 +174,20 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
       // a tile never straddles a page: one translation per tile
       const int64_t p0 = (t0 + i) * kTile;
       const int64_t row0 = p0 < T ? phys_row(pm, seq, T, p0) : -1;
+      const uint8_t* kp = k_idx + (row0 + kn) * kIndexDim + part;
       uint4 v[2];
+      if (row0 >= 0 && p0 + kTile <= T && p0 + kTile - 1 <= limit) {
+        // the whole tile is visible (the wave-uniform common case)
+        x.ok[i][0] = x.ok[i][1] = true;
+        v[0] = load_key_part<kCand>(kp);
+        v[1] = load_key_part<kCand>(kp + 16 * kIndexDim);
+      } else {
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int64_t p = p0 + 16 * hh + kn;
-        x.ok[i][hh] = row0 >= 0 && p < T && p <= limit;
-        v[hh] = x.ok[i][hh] ? load_key_part<kCand>(k_idx + (row0 + 16 * hh + kn) * kIndexDim + part)
-                            : make_uint4(0, 0, 0, 0);
+        for (int hh = 0; hh < 2; ++hh) {
+          const int64_t p = p0 + 16 * hh + kn;
+          x.ok[i][hh] = row0 >= 0 && p < T && p <= limit;
+          v[hh] = x.ok[i][hh] ? load_key_part<kCand>(kp + 16 * hh * kIndexDim) : make_uint4(0, 0, 0, 0);
+        }
       }
       x.b[i] = tile_pair(v[0], v[1]);
     }
@@ -229,11 +236,8 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int64_t p = (t0 + i) * kTile + 16 * hh + kn;
-        key[i][hh] = 0u;
-        if (lane < 16 && p < T) {
-          if (!kCand || scores) out[p] = cur.ok[i][hh] ? sv[hh] : neg_inf;
-          if (kCand && cur.ok[i][hh]) key[i][hh] = score_key(sv[hh]);
-        }
+        key[i][hh] = (kCand && lane < 16 && cur.ok[i][hh]) ? score_key(sv[hh]) : 0u;
+        if ((!kCand || scores) && lane < 16 && p < T) out[p] = cur.ok[i][hh] ? sv[hh] : neg_inf;
       }
     }
     if (kCand) {
@@ -499,7 +503,9 @@ index_block_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict_
   }
 }
 
-// workgroups of index_stream_kernel the device keeps resident at once
+// workgroups of index_stream_kernel to launch: the resident count, at most 3
+// per CU (3 beat 4 and 2 in a same-box sweep of the 8 x 1M candidate scan:
+// 95.6 vs 98.4 and 102 us; more concurrent key streams than that contend)
 static int64_t resident_blocks() {
   static int64_t cached = 0;
   if (cached == 0) {
@@ -509,8 +515,8 @@ static int64_t resident_blocks() {
       cus = 256;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(index_stream_kernel<true>), 256,
                                                       0) != hipSuccess || per_cu < 1)
-      per_cu = 4;
-    cached = (int64_t)cus * per_cu;
+      per_cu = 3;
+    cached = (int64_t)cus * std::min(per_cu, 3);
   }
   return cached;
 }
