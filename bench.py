@@ -37,6 +37,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="stack_1m_b8")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP graph replay)")
     ap.add_argument("--cpu-sample", type=int, default=0, help="sequences in the CPU-baseline sample (0 = auto)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
@@ -204,9 +205,11 @@ def bench_decode(args, cfg):
     wl = Workload(cfg, dev)
     stack = Csa2DecodeStack(cfg.batch, cfg.context, cfg.heads, cfg.topk, cfg.modes,
                             pool_size=cfg.pool if cfg.pool else 16384)
+    step = lambda: stack.step(wl.codes, wl.scales, wl.k_idx, wl.layers, SIGMA, new_rows=wl.new_rows)
     for _ in range(args.warmup):
-        stack.step(wl.codes, wl.scales, wl.k_idx, wl.layers, SIGMA, new_rows=wl.new_rows)
+        step()
     torch.cuda.synchronize()
+    # eager steps, with events around the Full-layer scan for its roofline figure
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     index_ev = []
@@ -216,8 +219,31 @@ def bench_decode(args, cfg):
         index_ev.append(stack.index_events)
     t_end.record()
     torch.cuda.synchronize()
-    ms = t_start.elapsed_time(t_end) / args.steps
+    ms_eager = t_start.elapsed_time(t_end) / args.steps
     idx_ms = sum(a.elapsed_time(b) for a, b in index_ev) / len(index_ev)
+    ms = ms_eager
+    graph = None
+    if not args.no_graph:
+        # the same step captured once into a HIP graph and replayed: every kernel of every step still
+        # runs; only the per-launch host overhead goes
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t_start.record()
+        for _ in range(args.steps):
+            graph.replay()
+        t_end.record()
+        torch.cuda.synchronize()
+        ms = t_start.elapsed_time(t_end) / args.steps
     B, T, H, K = cfg.batch, cfg.context, cfg.heads, cfg.topk
     P = min(cfg.pool, T) if "reindex" in cfg.modes else 0
     step_bytes = decode_step_bytes(B, T, H, K, P, cfg.modes, cfg.window)
@@ -225,7 +251,7 @@ def bench_decode(args, cfg):
     # writes no scores, otherwise 4 bytes of score per position
     idx_bytes = B * T * (64 if P else 64 + 4) + B * 64
     achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
-    digest = kernel_source_digest(["index.hip", "common.hpp"])
+    digest = kernel_source_digest(["index.hip", "tile.hpp", "internal.hpp", "common.hpp"])
     rec = {
         "metric": METRIC,
         "value": B / (ms * 1e-3),
@@ -234,6 +260,8 @@ def bench_decode(args, cfg):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_eager": ms_eager,
+        "launch": "hip graph replay of the captured step" if graph is not None else "eager",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
