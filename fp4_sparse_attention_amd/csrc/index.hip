@@ -104,7 +104,10 @@ index_rows_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__
 //    order every workgroup would flush at each row boundary, measured slower).
 constexpr int kUnitTiles = 16;
 
-template <bool kCand>
+// kPaged: keys in a page pool (pm.table set); kOut: scores written (always
+// for the scores-only scan).  Both are template switches so that the common
+// decode scan carries no page translation and no score stores.
+template <bool kCand, bool kPaged, bool kOut>
 __global__ void __launch_bounds__(256)
 index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx, int64_t T,
                     const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit,
@@ -173,7 +176,7 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
     for (int i = 0; i < kUnroll; ++i) {
       // a tile never straddles a page: one translation per tile
       const int64_t p0 = (t0 + i) * kTile;
-      const int64_t row0 = p0 < T ? phys_row(pm, seq, T, p0) : -1;
+      const int64_t row0 = p0 >= T ? -1 : (kPaged ? phys_row(pm, seq, T, p0) : (int64_t)seq * T + p0);
       const uint8_t* kp = k_idx + (row0 + kn) * kIndexDim + part;
       uint4 v[2];
       if (row0 >= 0 && p0 + kTile <= T && p0 + kTile - 1 <= limit) {
@@ -237,7 +240,7 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
       for (int hh = 0; hh < 2; ++hh) {
         const int64_t p = (t0 + i) * kTile + 16 * hh + kn;
         key[i][hh] = (kCand && lane < 16 && cur.ok[i][hh]) ? score_key(sv[hh]) : 0u;
-        if ((!kCand || scores) && lane < 16 && p < T) out[p] = cur.ok[i][hh] ? sv[hh] : neg_inf;
+        if (kOut && lane < 16 && p < T) out[p] = cur.ok[i][hh] ? sv[hh] : neg_inf;
       }
     }
     if (kCand) {
@@ -513,7 +516,7 @@ static int64_t resident_blocks() {
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
         hipSuccess)
       cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(index_stream_kernel<true>), 256,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(index_stream_kernel<true, false, false>), 256,
                                                       0) != hipSuccess || per_cu < 1)
       per_cu = 3;
     cached = (int64_t)cus * std::min(per_cu, 3);
@@ -537,12 +540,22 @@ void launch_index_scan(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, in
   const int64_t units_per_row = (n_tiles + kUnitTiles - 1) / kUnitTiles;
   int64_t grid = std::min<int64_t>(resident_blocks(), (int64_t)R * units_per_row);
   if (cand && R <= grid) grid = std::min<int64_t>(grid / R, units_per_row) * R;   // whole groups per row
-  if (cand)
-    index_stream_kernel<true><<<(int)grid, 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, scores, R,
-                                                        units_per_row, *cand, pm);
-  else
-    index_stream_kernel<false><<<(int)grid, 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, scores, R,
-                                                         units_per_row, CandOut{}, pm);
+  const dim3 g((unsigned)grid), blk(256);
+  const bool paged = pm.table != nullptr;
+  if (cand) {
+    const CandOut& c = *cand;
+    if (paged) {
+      if (scores) index_stream_kernel<true, true, true><<<g, blk, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, scores, R, units_per_row, c, pm);
+      else index_stream_kernel<true, true, false><<<g, blk, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, scores, R, units_per_row, c, pm);
+    } else {
+      if (scores) index_stream_kernel<true, false, true><<<g, blk, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, scores, R, units_per_row, c, pm);
+      else index_stream_kernel<true, false, false><<<g, blk, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, scores, R, units_per_row, c, pm);
+    }
+  } else if (paged) {
+    index_stream_kernel<false, true, true><<<g, blk, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, scores, R, units_per_row, CandOut{}, pm);
+  } else {
+    index_stream_kernel<false, false, true><<<g, blk, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, scores, R, units_per_row, CandOut{}, pm);
+  }
 }
 
 void launch_index_sample_tau(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int64_t T,
