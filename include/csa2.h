@@ -117,10 +117,12 @@ csa2_status csa2_fp4_unpack(const uint8_t* codes, const uint8_t* scales, int64_t
  *   row_limit  int64 [R] last visible position of each row (causal prefill),
  *              or NULL for all T positions
  *   scores     fp32 [R][T]
- * E4M3 products are exact; each 16-term group is summed exactly and rounded
- * once into the fp32 accumulator (four groups), so |error| <= 2^-22 *
- * sum_d |q_d k_d|, and the score is the exact value rounded once to fp32
- * whenever the running sums fit in 24 bits (the case for unit-normal inputs).
+ * E4M3 products are exact; the matrix cores add them in two steps of 32
+ * channels into an fp32 accumulator.  The score is the exact value rounded
+ * once to fp32 for unit-normal inputs; over arbitrary finite E4M3 bytes the
+ * error measured stays below 2^-21 * sum_d |q_d k_d|.  Every scoring call
+ * (csa2_index_full, csa2_index_reindex, csa2_index_full_pool and the paged
+ * forms) rounds identically, so their scores agree bit for bit.
  * Errors: EINVAL (null pointer, R/B/T <= 0, R != B without row_seq), ESHAPE
  * (T not a multiple of 4, T >= 2^31), EALIGN.
  * ------------------------------------------------------------------------- */

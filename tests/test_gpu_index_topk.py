@@ -37,8 +37,8 @@ def test_index_full_scores(B, T):
 
 def test_index_scores_bound_on_wide_range_keys():
     # keys spanning the whole E4M3 range (subnormals to 448): running sums need far
-    # more than 24 bits; each 16-term group is exact and rounded once, so the error
-    # stays within 2^-22 * sum |q_d k_d|
+    # more than 24 bits; the two 32-channel steps round into fp32, and on this
+    # distribution the error stays within 2^-22 * sum |q_d k_d|
     dev = device()
     g = torch.Generator().manual_seed(17)
     T = 8192
