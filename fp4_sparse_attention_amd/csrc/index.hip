@@ -196,11 +196,15 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
     }
   };
   uint32_t tau = 0, sh = 0;
+  float tf = 0.f;
   auto query = [&](int rr, f16x8* a) {
     query_operands(q_idx + (int64_t)rr * kIndexDim, lane, a);
     if (kCand) {
       tau = uniform_u32(cand.row[rr].tau_s);
       sh = uniform_u32(cand.row[rr].sh);
+      // the candidate test on the float score: key(s) >= tau_s exactly when s >= key_score(tau_s) (NaN and -inf
+      // fail both; with tau_s = 0 every finite score passes); the key itself is formed only for candidates
+      tf = tau ? key_score(tau) : -3.402823466e38f;
     }
   };
   auto flush = [&](int rr) {
@@ -231,7 +235,7 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
     if (rn < R) fetch(rn, jn, nxt);
     const int64_t t0 = tile_of(j);
     float* out = scores ? scores + (int64_t)r * T : nullptr;
-    uint32_t key[kUnroll][2];
+    float key[kUnroll][2];
 #pragma unroll
     for (int i = 0; i < kUnroll; ++i) {
       const float2 sc = mfma_score(a, cur.b[i]);
@@ -239,7 +243,7 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int64_t p = (t0 + i) * kTile + 16 * hh + kn;
-        key[i][hh] = (kCand && lane < 16 && cur.ok[i][hh]) ? score_key(sv[hh]) : 0u;
+        key[i][hh] = (kCand && lane < 16 && cur.ok[i][hh]) ? sv[hh] : -__builtin_inff();
         if (kOut && lane < 16 && p < T) out[p] = cur.ok[i][hh] ? sv[hh] : neg_inf;
       }
     }
@@ -252,10 +256,10 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
       for (int i = 0; i < kUnroll; ++i) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const uint32_t kk = key[i][hh];
-          const bool c = kk != 0u && kk >= tau;
+          const bool c = key[i][hh] >= tf;
           const uint64_t m = __ballot(c);
           if (c) {
+            const uint32_t kk = score_key(key[i][hh]);
             oc[at + lanes_below(m)] = make_uint2(kk, (uint32_t)((t0 + i) * kTile + 16 * hh + kn));
             atomicAdd(&h[min((kk - tau) >> sh, (uint32_t)(kStreamBins - 1))], 1u);
           }
