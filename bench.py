@@ -69,6 +69,7 @@ def decode_step_bytes(B, T, H, K, P, modes, W=128):
     """Compulsory bytes of one decode step (each call's inputs read once, outputs written once)."""
     C = 512
     total = B * (2 * C + 288)                          # pack the current token's row
+    total += B * 2 * 64 + B * len(modes) * 3 * 2 * C  # its key copied; each layer's window row into both ring slots
     for mode in modes:
         if mode == "full":
             if P:
@@ -165,13 +166,18 @@ class Workload:
         pack_cache(self.codes, self.scales, self.latent_chunk, self.chunk_rows)
         self.k_idx = torch.stack([W.fp8_normal(cfg.seed, (T, 64), device=dev, chunk_index=b) for b in range(B)])
         L = len(cfg.modes)
-        ds = [W.decode_layer_inputs(cfg.seed, li, B, cfg.heads, cfg.window, B, device=dev, outliers=self.outliers)
+        # each layer's window is a mirrored ring of 2 x 128 rows (the decode-time append writes the current
+        # token's window row into it every step)
+        ds = [W.decode_layer_inputs(cfg.seed, li, B, cfg.heads, 2 * cfg.window, B, device=dev, outliers=self.outliers)
               for li in range(L)]
         self.layers = StackIO(torch.stack([d["q_lat"] for d in ds]), torch.stack([d["q_idx"] for d in ds]),
                               torch.stack([d["swa"] for d in ds]), torch.zeros((L, B), dtype=torch.int32, device=dev),
                               torch.full((L, B), min(cfg.window, T), dtype=torch.int32, device=dev))
-        # the current token's latent row, packed into position T-1 by every step
+        # the current token: its latent row, indexer key and per-layer window rows, appended at position T-1
+        # by every step
         self.new_rows = self.latent_chunk_rows_at(T - 1)
+        self.new_keys = self.k_idx[:, T - 1].clone()
+        self.new_window = W.bf16_normal(cfg.seed, (L, B, 512), device=dev, chunk_index=7919)
         torch.cuda.synchronize()
 
     def latent_chunk(self, b, c):
@@ -205,7 +211,8 @@ def bench_decode(args, cfg):
     wl = Workload(cfg, dev)
     stack = Csa2DecodeStack(cfg.batch, cfg.context, cfg.heads, cfg.topk, cfg.modes,
                             pool_size=cfg.pool if cfg.pool else 16384)
-    step = lambda: stack.step(wl.codes, wl.scales, wl.k_idx, wl.layers, SIGMA, new_rows=wl.new_rows)
+    step = lambda: stack.step(wl.codes, wl.scales, wl.k_idx, wl.layers, SIGMA, new_rows=wl.new_rows,
+                              new_keys=wl.new_keys, new_window=wl.new_window)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -215,7 +222,8 @@ def bench_decode(args, cfg):
     index_ev = []
     t_start.record()
     for _ in range(args.steps):
-        stack.step(wl.codes, wl.scales, wl.k_idx, wl.layers, SIGMA, new_rows=wl.new_rows, time_index=True)
+        stack.step(wl.codes, wl.scales, wl.k_idx, wl.layers, SIGMA, new_rows=wl.new_rows, new_keys=wl.new_keys,
+                   new_window=wl.new_window, time_index=True)
         index_ev.append(stack.index_events)
     t_end.record()
     torch.cuda.synchronize()

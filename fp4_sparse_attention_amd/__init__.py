@@ -65,6 +65,8 @@ _SIGS = {
     "csa2_index_full_pool_paged": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i64, _c_void_p, _c_void_p, _c_void_p,
                                           _i64, _i32, _c_void_p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p,
                                           _c_void_p, _size_t, _c_void_p]),
+    "csa2_decode_append": (_i32, [_i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                  _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "csa2_sparse_swa_decode_layers_paged": (_i32, [_i32, _c_void_p, _i32, _i32, _c_void_p, _c_void_p, _i32, _i64,
                                                    _c_void_p, _c_void_p, _i64, _i32, _c_void_p, _c_void_p, _i32,
                                                    _c_void_p, _i32, _c_void_p, _c_void_p, _f32, _c_void_p, _c_void_p,
@@ -611,3 +613,46 @@ def csa2_sparse_swa_decode_layers_paged(q_lat, code_pages, scale_pages, block_ta
                                                    _p(swa_start), _p(swa_len), float(softmax_scale), _p(o), _p(lse),
                                                    _p(workspace), workspace.numel(), _stream(stream))
     _check("csa2_sparse_swa_decode_layers_paged", st)
+
+
+def csa2_decode_append(new_latent, cache_rows, codes, scales, new_keys=None, k_idx=None, new_window=None, swa=None,
+                       tok_pos=None, swa_start=None, swa_len=None, stream=None):
+    """Decode-time append: new_latent bf16 [B, 512] packed into rows cache_rows (int64 [B]) of codes
+    uint8 [N, 256] / scales uint8 [N, 32]; new_keys uint8 [B, 64] copied into those rows of k_idx uint8 [N, 64];
+    new_window bf16 [L, B, 512] written into the mirrored window rings swa bf16 [L, B, S >= 256, 512] at
+    position tok_pos (int64 [B]), with swa_start / swa_len int32 [L, B] updated."""
+    _need(new_latent, torch.bfloat16, "new_latent", 2)
+    _need(cache_rows, torch.int64, "cache_rows", 1)
+    _need(codes, torch.uint8, "codes", 2)
+    _need(scales, torch.uint8, "scales", 2)
+    for t, nm in ((new_latent, "new_latent"), (cache_rows, "cache_rows"), (codes, "codes"), (scales, "scales")):
+        _dense(t, nm)
+    B = new_latent.shape[0]
+    if new_latent.shape[1] != 512 or cache_rows.shape != (B,) or codes.shape[1] != 256 or scales.shape[1] != 32:
+        raise ValueError("decode_append shapes")
+    L, S = 0, 0
+    if new_keys is not None:
+        _need(new_keys, torch.uint8, "new_keys", 2)
+        _need(k_idx, torch.uint8, "k_idx", 2)
+        _dense(new_keys, "new_keys")
+        _dense(k_idx, "k_idx")
+        if new_keys.shape != (B, 64) or k_idx.shape[1] != 64:
+            raise ValueError("key shapes")
+    if new_window is not None:
+        _need(new_window, torch.bfloat16, "new_window", 3)
+        _need(swa, torch.bfloat16, "swa", 4)
+        _need(tok_pos, torch.int64, "tok_pos", 1)
+        _need(swa_start, torch.int32, "swa_start", 2)
+        _need(swa_len, torch.int32, "swa_len", 2)
+        for t, nm in ((new_window, "new_window"), (swa, "swa"), (tok_pos, "tok_pos"), (swa_start, "swa_start"),
+                      (swa_len, "swa_len")):
+            _dense(t, nm)
+        L = new_window.shape[0]
+        S = swa.shape[2]
+        if (new_window.shape != (L, B, 512) or swa.shape != (L, B, S, 512) or tok_pos.shape != (B,)
+                or swa_start.shape != (L, B) or swa_len.shape != (L, B)):
+            raise ValueError("window shapes")
+    st = lib().csa2_decode_append(B, L, _p(new_latent), _p(cache_rows), _p(codes), _p(scales), _p(new_keys),
+                                  _p(k_idx), _p(new_window), _p(swa), S, _p(tok_pos), _p(swa_start), _p(swa_len),
+                                  _stream(stream))
+    _check("csa2_decode_append", st)

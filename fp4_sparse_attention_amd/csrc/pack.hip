@@ -154,6 +154,55 @@ fp4_unpack_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__
   }
 }
 
+// Decode-time append, one workgroup per sequence: the new token's latent row
+// packed into its cache row (16 threads x 32 channels), its indexer key copied
+// (4 x 16 bytes), and for each layer its window row written to both slots of a
+// mirrored ring of 2 W rows (slots t mod W and t mod W + W), so that the last
+// min(W, t + 1) rows always sit contiguously at [start, start + len) with
+// start = (t + 1) mod W once t >= W - 1 (0 before) -- the contiguous window the
+// attention calls read.  The window bounds of every layer are updated too.
+__global__ void __launch_bounds__(256)
+decode_append_kernel(int B, int L, const uint16_t* __restrict__ new_latent, const int64_t* __restrict__ cache_rows,
+                     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const uint8_t* __restrict__ new_keys,
+                     uint8_t* __restrict__ k_idx, const uint16_t* __restrict__ new_window, uint16_t* __restrict__ swa,
+                     int S, const int64_t* __restrict__ tok_pos, int32_t* __restrict__ swa_start,
+                     int32_t* __restrict__ swa_len) {
+  constexpr int W = kWindowMax;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int64_t row = cache_rows[b];
+  if (row >= 0 && tid < 16) {
+    const uint4* src = reinterpret_cast<const uint4*>(new_latent + (int64_t)b * kLatent + tid * 32);
+    const uint4 v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
+    const uint32_t w0[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    const uint32_t w1[8] = {v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
+    uint32_t c0, c1, c2, c3, s0, s1;
+    pack_block(w0, c0, c1, s0);
+    pack_block(w1, c2, c3, s1);
+    *reinterpret_cast<uint4*>(codes + row * kCodesRow + tid * 16) = make_uint4(c0, c1, c2, c3);
+    *reinterpret_cast<uint16_t*>(scales + row * kScalesRow + tid * 2) = (uint16_t)(s0 | (s1 << 8));
+  } else if (row >= 0 && tid < 20 && new_keys) {
+    const int q = tid - 16;
+    *reinterpret_cast<uint4*>(k_idx + row * kIndexDim + 16 * q) =
+        *reinterpret_cast<const uint4*>(new_keys + (int64_t)b * kIndexDim + 16 * q);
+  }
+  if (!new_window) return;
+  const int64_t t = tok_pos[b];
+  if (t < 0) return;
+  const int slot = (int)(t % W);
+  for (int e = tid; e < L * 64; e += 256) {
+    const int l = e >> 6, c = e & 63;
+    const int64_t lb = (int64_t)l * B + b;
+    const uint4 v = reinterpret_cast<const uint4*>(new_window + lb * kLatent)[c];
+    uint16_t* ring = swa + lb * S * kLatent;
+    reinterpret_cast<uint4*>(ring + (int64_t)slot * kLatent)[c] = v;
+    reinterpret_cast<uint4*>(ring + (int64_t)(slot + W) * kLatent)[c] = v;
+  }
+  for (int l = tid; l < L; l += 256) {
+    swa_start[(int64_t)l * B + b] = t >= W - 1 ? (int32_t)((t + 1) % W) : 0;
+    swa_len[(int64_t)l * B + b] = (int32_t)(t + 1 < W ? t + 1 : W);
+  }
+}
+
 static int stream_grid(int64_t total_threads) {
   int64_t blocks = (total_threads + 255) / 256;
   const int64_t cap = 256 * 16;               // 16 workgroups per CU, grid-stride beyond
@@ -208,5 +257,28 @@ extern "C" csa2_status csa2_fp4_unpack(const uint8_t* codes, const uint8_t* scal
   int parts = C / 32;
   fp4_unpack_kernel<<<stream_grid(n_rows * parts), 256, 0, (hipStream_t)stream>>>(
       codes, scales, n_rows, parts, C, x);
+  return launch_status();
+}
+
+extern "C" csa2_status csa2_decode_append(int32_t B, int32_t L, const uint16_t* new_latent, const int64_t* cache_rows,
+                                          uint8_t* codes, uint8_t* scales, const uint8_t* new_keys, uint8_t* k_idx,
+                                          const uint16_t* new_window, uint16_t* swa, int32_t S,
+                                          const int64_t* tok_pos, int32_t* swa_start, int32_t* swa_len,
+                                          void* stream) {
+  if (B < 0 || L < 0) return CSA2_EINVAL;
+  if (B == 0) return CSA2_OK;
+  if (!new_latent || !cache_rows || !codes || !scales) return CSA2_EINVAL;
+  if (new_keys && !k_idx) return CSA2_EINVAL;
+  if (new_window) {
+    if (L == 0 || !swa || !tok_pos || !swa_start || !swa_len) return CSA2_EINVAL;
+    if (S < 2 * kWindowMax) return CSA2_ESHAPE;
+  }
+  if (!aligned(new_latent, 16) || !aligned(cache_rows, 8) || !aligned(codes, 16) || !aligned(scales, 2) ||
+      (new_keys && (!aligned(new_keys, 16) || !aligned(k_idx, 16))) ||
+      (new_window && (!aligned(new_window, 16) || !aligned(swa, 16) || !aligned(tok_pos, 8) ||
+                      !aligned(swa_start, 4) || !aligned(swa_len, 4))))
+    return CSA2_EALIGN;
+  decode_append_kernel<<<B, 256, 0, (hipStream_t)stream>>>(B, L, new_latent, cache_rows, codes, scales, new_keys,
+                                                            k_idx, new_window, swa, S, tok_pos, swa_start, swa_len);
   return launch_status();
 }

@@ -16,8 +16,8 @@ from typing import Optional, Sequence
 
 import torch
 
-from . import (csa2_fp4_pack, csa2_index_full, csa2_index_reindex, csa2_topk, csa2_topk_workspace_size,
-               csa2_topk_pool, csa2_topk_pool_workspace_size, csa2_sparse_swa_decode_layers,
+from . import (csa2_fp4_pack, csa2_decode_append, csa2_index_full, csa2_index_reindex, csa2_topk,
+               csa2_topk_workspace_size, csa2_topk_pool, csa2_topk_pool_workspace_size, csa2_sparse_swa_decode_layers,
                csa2_index_full_pool, csa2_index_full_pool_workspace_size,
                csa2_sparse_swa_decode_layers_workspace_size,
                csa2_sparse_decode, csa2_sparse_decode_workspace_size, csa2_swa_merge,
@@ -108,13 +108,21 @@ class Csa2DecodeStack:
         self.ws_layers = torch.empty(csa2_sparse_swa_decode_layers_workspace_size(self.L, B, H, K), dtype=u8,
                                      device=dev)
         self.index_events = None
+        # the current token's cache row (position T - 1) and position, for the decode-time append
+        self.tok_rows = torch.arange(B, dtype=torch.int64, device=dev) * T + (T - 1)
+        self.tok_pos = torch.full((B,), T - 1, dtype=torch.int64, device=dev)
 
     def step(self, codes, scales, k_idx, layers, sigma: float, new_rows: Optional[torch.Tensor] = None,
-             stream=None, time_index: bool = False):
+             stream=None, time_index: bool = False, new_keys: Optional[torch.Tensor] = None,
+             new_window: Optional[torch.Tensor] = None):
         """Run every layer once.  layers: a StackIO (all layers' attention in one
         launch, after the selections) or a list of LayerIO (one attention call
-        per layer).  new_rows (bf16 [B, 512]), if given, is packed into position
-        T-1 of each sequence first (the current token).
+        per layer).  new_rows (bf16 [B, 512]), if given, is the current token's
+        latent row, appended first at position T-1 of each sequence
+        (csa2_decode_append): packed into the FP4 cache, with its indexer key
+        new_keys (E4M3 [B, 64]) copied into k_idx and, with a StackIO whose
+        window rings hold 256 rows, its window rows new_window (bf16 [L, B, 512])
+        written into each layer's ring (the window bounds are updated).
 
         time_index: record HIP events around the Full-layer index call on the
         stream (self.index_events holds the (start, end) pair)."""
@@ -122,7 +130,18 @@ class Csa2DecodeStack:
         stacked = layers if isinstance(layers, StackIO) else None
         ios = layers.layers if stacked is not None else list(layers)
         if new_rows is not None:
-            csa2_fp4_pack(new_rows, codes[:, T - 1, :], scales[:, T - 1, :], stream=stream)
+            win = None
+            if new_window is not None:
+                if stacked is None:
+                    raise ValueError("window rows are appended through a StackIO")
+                win = stacked
+            csa2_decode_append(new_rows, self.tok_rows, codes.view(-1, codes.shape[-1]),
+                               scales.view(-1, scales.shape[-1]), new_keys=new_keys,
+                               k_idx=k_idx.view(-1, k_idx.shape[-1]) if new_keys is not None else None,
+                               new_window=new_window, swa=win.swa if win is not None else None,
+                               tok_pos=self.tok_pos if win is not None else None,
+                               swa_start=win.swa_start if win is not None else None,
+                               swa_len=win.swa_len if win is not None else None, stream=stream)
         src = []                       # index slice used by each layer
         for li, (mode, io) in enumerate(zip(self.modes, ios)):
             idx = self.idx[li]

@@ -387,6 +387,36 @@ csa2_status csa2_sparse_swa_decode_layers_paged(int32_t L, const uint16_t* q_lat
                                                 const int32_t* swa_start, const int32_t* swa_len,
                                                 float softmax_scale, float* o, float* lse, void* workspace,
                                                 size_t workspace_bytes, void* stream);
+/* -------------------------------------------------------------------------
+ * Decode-time append (the step before the path: each new token enters the
+ * global FP4 cache, its indexer key enters the key cache, and every layer's
+ * sliding window gains its row -- the KV-cache paragraph of the MarkTechPost
+ * retelling and the HN summary's key points).  One call per decode step:
+ *
+ *   new_latent  bf16 [B][512]: the token's latent row, packed as csa2_fp4_pack
+ *               into row cache_rows[b] of codes ([.][256]) and scales ([.][32])
+ *   cache_rows  int64 [B] (device): the cache row of sequence b's new position
+ *               (dense [B][T] caches: b T + t_b; a page pool: its page slot);
+ *               a negative entry skips the sequence's cache and key writes
+ *   new_keys    E4M3 [B][64] or NULL: copied to row cache_rows[b] of k_idx
+ *   new_window  bf16 [L][B][512] or NULL: layer l's window row of the token
+ *   swa         bf16 [L][B][S][512], S >= 256: each layer's window kept as a
+ *               mirrored ring of 2 x 128 rows: position t is written to rows
+ *               t mod 128 and t mod 128 + 128, so the last min(128, t + 1)
+ *               positions are rows [start, start + len) with
+ *               start = (t + 1) mod 128 once t >= 127 (0 before) and
+ *               len = min(128, t + 1), the contiguous window every attention
+ *               call of this library reads
+ *   tok_pos     int64 [B] (device): t, the new token's position in its sequence
+ *               (negative: leave that sequence's window alone)
+ *   swa_start, swa_len  int32 [L][B] (device), written with those bounds
+ * Errors: EINVAL (B or L < 0, null pointer a given input needs, new_window
+ * with L = 0), ESHAPE (S < 256), EALIGN (16-byte rows; 8-byte int64 arrays).
+ * ------------------------------------------------------------------------- */
+csa2_status csa2_decode_append(int32_t B, int32_t L, const uint16_t* new_latent, const int64_t* cache_rows,
+                               uint8_t* codes, uint8_t* scales, const uint8_t* new_keys, uint8_t* k_idx,
+                               const uint16_t* new_window, uint16_t* swa, int32_t S, const int64_t* tok_pos,
+                               int32_t* swa_start, int32_t* swa_len, void* stream);
 #ifdef __cplusplus
 }
 #endif

@@ -190,3 +190,18 @@ def test_paged_argument_errors():
                                 ctypes.c_float(0.05), DUMMY, DUMMY, DUMMY, 1 << 30, NULL)
     assert L.csa2_sparse_swa_decode_layers_paged(*args(NULL, 128)) == 1
     assert L.csa2_sparse_swa_decode_layers_paged(*args(DUMMY, 100)) == 2
+
+
+def test_decode_append_argument_errors():
+    L = F.lib()
+    assert L.csa2_decode_append(-1, 0, DUMMY, DUMMY, DUMMY, DUMMY, NULL, NULL, NULL, NULL, 0, NULL, NULL, NULL, NULL) == 1
+    assert L.csa2_decode_append(0, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL, NULL, NULL, NULL) == 0
+    assert L.csa2_decode_append(2, 0, NULL, DUMMY, DUMMY, DUMMY, NULL, NULL, NULL, NULL, 0, NULL, NULL, NULL, NULL) == 1
+    assert L.csa2_decode_append(2, 0, DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, NULL, NULL, NULL, 0, NULL, NULL, NULL, NULL) == 1
+    # a window row without layers, then a ring shorter than two windows
+    assert L.csa2_decode_append(2, 0, DUMMY, DUMMY, DUMMY, DUMMY, NULL, NULL, DUMMY, DUMMY, 256, DUMMY, DUMMY, DUMMY,
+                                NULL) == 1
+    assert L.csa2_decode_append(2, 3, DUMMY, DUMMY, DUMMY, DUMMY, NULL, NULL, DUMMY, DUMMY, 128, DUMMY, DUMMY, DUMMY,
+                                NULL) == 2
+    assert L.csa2_decode_append(2, 0, ctypes.c_void_p(264), DUMMY, DUMMY, DUMMY, NULL, NULL, NULL, NULL, 0, NULL, NULL,
+                                NULL, NULL) == 3
