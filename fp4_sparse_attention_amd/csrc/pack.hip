@@ -2,11 +2,12 @@
 // channels, no global scale -- the NVFP4-style layout of the KV-cache paragraph
 // of the MarkTechPost retelling of DeepSeek-V4.1-Flash).
 //
-// Work split: one thread owns 32 consecutive channels of one row (two scale
-// blocks): 64 bytes of bf16 in, 16 bytes of codes + 2 scale bytes out, all as
-// vector loads/stores.  Sixteen threads cover a 512-channel row, so a wave
-// streams four whole rows per step.  The kernels are HBM-bound; the arithmetic
-// is kept to integer/compare work (about a dozen lane-ops per element).
+// Work split: the pack gives a thread 32 consecutive channels (two scale
+// blocks); the unpack gives a lane 8 channels, so that every wave store writes
+// a contiguous 1 KB of bf16 (with 32 channels per lane each store instruction
+// covered a 64-byte-strided quarter of 4 KB, and with nontemporal stores the
+// unpack ran at 1.4 TB/s).  The kernels are HBM-bound; the arithmetic is kept
+// to integer/compare work (about a dozen lane-ops per element).
 #include "common.hpp"
 
 namespace csa2 {
@@ -85,25 +86,36 @@ __device__ __forceinline__ void pack_block(const uint32_t* w, uint32_t& lo, uint
   sc = code;
 }
 
+// Pack: one thread owns 32 consecutive channels of one row (two scale
+// blocks): 64 bytes of bf16 in (plain loads: nontemporal ones were 8% slower),
+// 16 bytes of codes and 2 scale bytes out.  (8 channels per lane, with fully
+// contiguous wave accesses and the block amax shared across a lane pair, ran
+// slower: the per-block scale and threshold work then repeats every 8
+// channels, and the pack is issue-bound at this rate.)
 __global__ void __launch_bounds__(256)
 fp4_pack_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int parts_per_row, int64_t x_stride,
                 uint8_t* __restrict__ codes, int64_t codes_stride, uint8_t* __restrict__ scales,
                 int64_t scales_stride, const int64_t* __restrict__ out_rows) {
-  const int64_t total = n_rows * parts_per_row;
-  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
-       g += (int64_t)gridDim.x * blockDim.x) {
-    int64_t row = g / parts_per_row;
-    int part = (int)(g - row * parts_per_row);
+  // (row, part) of this thread's index, advanced by the grid stride without a division per step
+  const int64_t g0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  const int64_t step_rows = step / parts_per_row;
+  const int step_p = (int)(step - step_rows * parts_per_row);
+  int64_t row = g0 / parts_per_row;
+  int part = (int)(g0 - row * parts_per_row);
+  for (; row < n_rows; row += step_rows, part += step_p) {
+    if (part >= parts_per_row) {
+      part -= parts_per_row;
+      ++row;
+      if (row >= n_rows) break;
+    }
     // output row: the input row's own, or (scatter) out_rows[row]; a negative entry skips the row
     const int64_t orow = out_rows ? out_rows[row] : row;
     if (orow < 0) continue;
     const uint4* src = reinterpret_cast<const uint4*>(x + row * x_stride + part * 32);
-    uint4 v0 = ld_nt16(src + 0);
-    uint4 v1 = ld_nt16(src + 1);
-    uint4 v2 = ld_nt16(src + 2);
-    uint4 v3 = ld_nt16(src + 3);
-    uint32_t w0[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    uint32_t w1[8] = {v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
+    const uint4 v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
+    const uint32_t w0[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    const uint32_t w1[8] = {v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
     uint32_t c0, c1, c2, c3, s0, s1;
     pack_block(w0, c0, c1, s0);
     pack_block(w1, c2, c3, s1);
@@ -122,35 +134,34 @@ __device__ __forceinline__ float e2m1_to_f32(uint32_t nib) {
   return __uint_as_float(b | ((nib & 8u) << 28));
 }
 
+// Unpack: lane g owns 8 channels of one row (4 code bytes + the block's scale
+// byte in, 16 bytes of bf16 out), so every wave store writes 1 KB contiguously.
 __global__ void __launch_bounds__(256)
 fp4_unpack_kernel(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t n_rows,
-                  int parts_per_row, int C, uint16_t* __restrict__ x) {
-  const int64_t total = n_rows * parts_per_row;
-  for (int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; g < total;
-       g += (int64_t)gridDim.x * blockDim.x) {
-    int64_t row = g / parts_per_row;
-    int part = (int)(g - row * parts_per_row);
-    uint4 c = ld_nt16(codes + row * (C / 2) + part * 16);
-    uint32_t sc = *reinterpret_cast<const uint16_t*>(scales + row * (C / 16) + part * 2);
-    float s0 = e4m3_to_f32(sc & 0xFFu), s1 = e4m3_to_f32(sc >> 8);
-    uint32_t cw[4] = {c.x, c.y, c.z, c.w};
-    uint32_t out[16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float s = i < 2 ? s0 : s1;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t byte = (cw[i] >> (8 * j)) & 0xFFu;
-        float a = e2m1_to_f32(byte & 0xFu) * s;      // exact: <= 6 significant bits
-        float b = e2m1_to_f32(byte >> 4) * s;
-        out[i * 4 + j] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
-      }
+                  int chunks_per_row, int C, uint16_t* __restrict__ x) {
+  const int64_t g0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t step = (int64_t)gridDim.x * blockDim.x;
+  const int64_t step_rows = step / chunks_per_row;
+  const int step_c = (int)(step - step_rows * chunks_per_row);
+  int64_t row = g0 / chunks_per_row;
+  int c = (int)(g0 - row * chunks_per_row);
+  for (; row < n_rows; row += step_rows, c += step_c) {
+    if (c >= chunks_per_row) {
+      c -= chunks_per_row;
+      ++row;
+      if (row >= n_rows) break;
     }
-    uint4* dst = reinterpret_cast<uint4*>(x + row * C + part * 32);
-    st_nt16(dst + 0, make_uint4(out[0], out[1], out[2], out[3]));
-    st_nt16(dst + 1, make_uint4(out[4], out[5], out[6], out[7]));
-    st_nt16(dst + 2, make_uint4(out[8], out[9], out[10], out[11]));
-    st_nt16(dst + 3, make_uint4(out[12], out[13], out[14], out[15]));
+    const uint32_t cw = *reinterpret_cast<const uint32_t*>(codes + row * (C / 2) + 4 * c);
+    const float s = e4m3_to_f32(scales[row * (C / 16) + (c >> 1)]);
+    uint32_t out[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t byte = (cw >> (8 * j)) & 0xFFu;
+      const float a = e2m1_to_f32(byte & 0xFu) * s;      // exact: <= 6 significant bits
+      const float b = e2m1_to_f32(byte >> 4) * s;
+      out[j] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+    }
+    *reinterpret_cast<uint4*>(x + row * C + 8 * c) = make_uint4(out[0], out[1], out[2], out[3]);
   }
 }
 
@@ -224,7 +235,7 @@ extern "C" csa2_status csa2_fp4_pack(const uint16_t* x, int64_t n_rows, int32_t 
   if (n_rows == 0) return CSA2_OK;
   if (!x || !codes || !scales) return CSA2_EINVAL;
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2)) return CSA2_EALIGN;
-  int parts = C / 32;
+  const int parts = C / 32;
   fp4_pack_kernel<<<stream_grid(n_rows * parts), 256, 0, (hipStream_t)stream>>>(
       x, n_rows, parts, x_row_stride, codes, codes_row_stride, scales, scales_row_stride, nullptr);
   return launch_status();
@@ -241,7 +252,7 @@ extern "C" csa2_status csa2_fp4_pack_rows(const uint16_t* x, int64_t n_rows, int
   if (n_rows == 0) return CSA2_OK;
   if (!x || !out_rows || !codes || !scales) return CSA2_EINVAL;
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(out_rows, 8)) return CSA2_EALIGN;
-  int parts = C / 32;
+  const int parts = C / 32;
   fp4_pack_kernel<<<stream_grid(n_rows * parts), 256, 0, (hipStream_t)stream>>>(
       x, n_rows, parts, x_row_stride, codes, codes_row_stride, scales, scales_row_stride, out_rows);
   return launch_status();
@@ -254,9 +265,9 @@ extern "C" csa2_status csa2_fp4_unpack(const uint8_t* codes, const uint8_t* scal
   if (n_rows == 0) return CSA2_OK;
   if (!x || !codes || !scales) return CSA2_EINVAL;
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2)) return CSA2_EALIGN;
-  int parts = C / 32;
-  fp4_unpack_kernel<<<stream_grid(n_rows * parts), 256, 0, (hipStream_t)stream>>>(
-      codes, scales, n_rows, parts, C, x);
+  const int chunks = C / 8;
+  fp4_unpack_kernel<<<stream_grid(n_rows * chunks), 256, 0, (hipStream_t)stream>>>(
+      codes, scales, n_rows, chunks, C, x);
   return launch_status();
 }
 
