@@ -52,15 +52,15 @@ def kernel_source_digest(files):
     return h.hexdigest()
 
 
-def measured_traffic(name, digest):
-    """HBM bytes per launch from committed counter runs, if taken on this kernel source."""
+def measured_traffic(name, digest, workload):
+    """HBM bytes per launch from committed counter runs, if taken on this kernel source and workload."""
     path = os.path.join(HERE, "profiles", f"{name}_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != digest:
+    if rec.get("kernel_source_sha256") != digest or rec.get("workload") != workload:
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -76,8 +76,11 @@ def decode_step_bytes(B, T, H, K, P, modes, W=128):
                 # keys + query read; pool (positions + scores) and Top-K written: the streaming selection
                 # needs no score array
                 total += B * T * 64 + B * 64 + B * P * 8 + B * K * 4
+            elif T > 32768 and B * T * 16 <= (1 << 30):
+                # the streaming selection cuts the Top-K during the scan: keys + query read, Top-K written
+                total += B * T * 64 + B * 64 + B * K * 4
             else:
-                # keys + query, scores written and read back by the selection, Top-K written
+                # short rows: keys + query, scores written and read back by the selection, Top-K written
                 total += B * T * (64 + 4) + B * 64 + B * T * 4 + B * K * 4
         elif mode == "reindex":
             total += B * P * (4 + 64 + 4) + B * 64      # pool ids, gathered keys, scores
@@ -255,9 +258,10 @@ def bench_decode(args, cfg):
     B, T, H, K = cfg.batch, cfg.context, cfg.heads, cfg.topk
     P = min(cfg.pool, T) if "reindex" in cfg.modes else 0
     step_bytes = decode_step_bytes(B, T, H, K, P, cfg.modes, cfg.window)
-    # the Full-layer scan: 64-byte keys per position and the query; with a pool (streaming selection) it
-    # writes no scores, otherwise 4 bytes of score per position
-    idx_bytes = B * T * (64 if P else 64 + 4) + B * 64
+    # the Full-layer scan: 64-byte keys per position and the query; the streaming selection (rows longer than
+    # 32,768 positions) writes no scores, shorter rows write 4 bytes of score per position
+    streams = T > 32768 and B * T * 16 <= (1 << 30)
+    idx_bytes = B * T * (64 if streams else 64 + 4) + B * 64
     achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
     digest = kernel_source_digest(["index.hip", "tile.hpp", "internal.hpp", "common.hpp"])
     rec = {
@@ -279,9 +283,10 @@ def bench_decode(args, cfg):
                    "layers": list(cfg.modes), "pool": P, "window": cfg.window, "latent_channels": 512},
         "achieved_hbm_gbps": step_bytes / (ms * 1e-3) / 1e9,
         "step_algorithmic_bytes": step_bytes,
-        "roofline": {"kernel": "csa2_index_full_pool scan (index_stream_kernel<true>, no score output)", "bound": "hbm", "achieved": achieved,
+        "roofline": {"kernel": ("csa2_index_full_pool scan (index_stream_kernel<true>, no score output)" if streams
+                               else "csa2_index_full_pool scoring pass (scores written)"), "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic("index_full", digest),
+                     "traffic": measured_traffic("index_full", digest, cfg.name),
                      "launch_ms": idx_ms, "bytes_per_launch": idx_bytes},
     }
     if not args.no_cpu_baseline:
@@ -329,7 +334,7 @@ def bench_pack(args, cfg):
         "unpack_gbps": bytes_dir / (unpack_ms * 1e-3) / 1e9,
         "roofline": {"kernel": "csa2_fp4_pack", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic("fp4_pack", digest), "launch_ms": pack_ms,
+                     "traffic": measured_traffic("fp4_pack", digest, cfg.name), "launch_ms": pack_ms,
                      "bytes_per_launch": bytes_dir},
         "cpu_baseline": None,
     }

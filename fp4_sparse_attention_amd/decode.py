@@ -97,8 +97,11 @@ class Csa2DecodeStack:
         self.o = torch.empty((self.L, B, H, LATENT), dtype=f32, device=dev)
         self.lse = torch.empty((self.L, B, H), dtype=f32, device=dev)
         self.ws_topk_full = torch.empty(max(csa2_topk_workspace_size(B, T, K),
-                                            csa2_index_full_pool_workspace_size(B, T, self.P) if self.use_pool else 0),
+                                            csa2_index_full_pool_workspace_size(B, T, max(self.P, K))),
                                         dtype=u8, device=dev)
+        # a Full layer with no Reindex after it selects its Top-K in the same streaming call (pool = Top-K);
+        # the call's second output lands here
+        self.top_twin = torch.empty((B, K), dtype=i32, device=dev)
         self.ws_topk_pool = (torch.empty(csa2_topk_workspace_size(B, self.P, K), dtype=u8, device=dev)
                              if self.use_pool else None)
         self.ws_sparse = torch.empty(csa2_sparse_decode_workspace_size(B, H, K), dtype=u8, device=dev)
@@ -153,6 +156,15 @@ class Csa2DecodeStack:
                     csa2_index_full_pool(io.q_idx, k_idx, None, self.P, K, self.pool, idx,
                                          pool_scores=self.pool_scores, workspace=self.ws_topk_full,
                                          scan_events=ev, stream=stream)
+                    if time_index:
+                        self.index_events = ev
+                    src.append(li)
+                    continue
+                if not self.use_pool:
+                    # the Top-K straight from the streaming selection: no score array is written
+                    ev = self._scan_events() if time_index else None
+                    csa2_index_full_pool(io.q_idx, k_idx, None, K, K, idx, self.top_twin,
+                                         workspace=self.ws_topk_full, scan_events=ev, stream=stream)
                     if time_index:
                         self.index_events = ev
                     src.append(li)

@@ -284,7 +284,8 @@ def test_topk_pool_with_index_map_and_long_rows_path():
         assert np.array_equal(top[r].cpu().numpy(), OT.topk(sh, k_top, index_map=mh)), r
 
 
-@pytest.mark.parametrize("R,T,k_pool,k_top", [(8, 1 << 20, 16384, 2048), (3, 8192, 2048, 256), (2, 65540, 4000, 4000)])
+@pytest.mark.parametrize("R,T,k_pool,k_top", [(8, 1 << 20, 16384, 2048), (3, 8192, 2048, 256), (2, 65540, 4000, 4000),
+                                             (64, 131072, 2048, 2048)])
 def test_index_full_pool_equals_separate_calls(R, T, k_pool, k_top):
     """Scores, pool (with scores) and Top-K of the fused call are bit-identical to
     csa2_index_full followed by csa2_topk_pool (long rows: the scoring pass builds
