@@ -289,8 +289,7 @@ attn_chunk_kernel(const AttnArgs a) {
         s[q] = s_valid[8 * g + q] ? s[q] * a.scale_log2 : neg_inf;
         mx = fmaxf(mx, s[q]);
       }
-      mx = fmaxf(mx, shfl_xor_f(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      mx = xor32_max(xor16_max(mx));
       // P = 2^(s - m_ref) stays <= 2^8 in f16; m_ref moves only past that slack
       const float m_new = (mx > m_run + kRescaleSlack) ? mx : m_run;
       const bool live = m_new != neg_inf;
@@ -303,8 +302,7 @@ attn_chunk_kernel(const AttnArgs a) {
         psum += pj;
         ph[q] = (_Float16)pj;
       }
-      psum += shfl_xor_f(psum, 16);
-      psum += shfl_xor_f(psum, 32);
+      psum = xor32_sum(xor16_sum(psum));
       l_run = l_run * alpha + psum;
       m_run = m_new;
       *reinterpret_cast<f16x8*>(pp + (16 * wave + m) * kPStride + 8 * g) = ph;

@@ -58,6 +58,28 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// lane l's value and lane (l ^ 16)'s, resp. (l ^ 32)'s, in one VALU step each
+// (gfx950's v_permlane16_swap / v_permlane32_swap on two copies of v: every
+// lane ends with the pair, in an order that depends on the lane), so a
+// reduction over those lanes needs no LDS round trip; a + b and max(a, b)
+// give both lanes of a pair the same bits
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // v from the lane selected by a DPP control (0 where the source lane is
 // outside the row or the destination row is masked off)
 template <int kCtrl, int kRowMask = 0xF>
