@@ -18,14 +18,10 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// 16-byte streaming (non-temporal) load / store
+// 16-byte streaming (non-temporal) load
 __device__ __forceinline__ uint4 ld_nt16(const void* p) {
   u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v[0], v[1], v[2], v[3]);
-}
-__device__ __forceinline__ void st_nt16(void* p, uint4 v) {
-  u32x4 w = {v.x, v.y, v.z, v.w};
-  __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
 }
 
 constexpr int kLatent = 512;        // latent KV channels
@@ -37,10 +33,6 @@ constexpr int kWindowMax = 128;     // sliding-window bound
 // ----------------------------------------------------------------------------
 // scalar conversions
 // ----------------------------------------------------------------------------
-__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
-  return __uint_as_float(bits16 << 16);
-}
-
 // E4M3FN byte (non-NaN) -> fp32, exact.  Normal codes: exponent e (bias 7) and
 // mantissa m map to fp32 exponent e+120; subnormal codes are m * 2^-9.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
@@ -112,19 +104,6 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
 // number of set bits of a wave-wide mask in the lanes below this one
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
-
-// exclusive prefix over the wave of a per-lane count in [0, 7] (three ballots)
-__device__ __forceinline__ uint32_t wave_exclusive_small(uint32_t c, uint32_t& total) {
-  const uint64_t b0 = __ballot(c & 1u), b1 = __ballot(c & 2u), b2 = __ballot(c & 4u);
-  total = (uint32_t)__popcll(b0) + 2u * (uint32_t)__popcll(b1) + 4u * (uint32_t)__popcll(b2);
-  return lanes_below(b0) + 2u * lanes_below(b1) + 4u * lanes_below(b2);
-}
-
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
-  return v;
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
