@@ -510,6 +510,181 @@ index_block_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict_
   }
 }
 
+// Query-block candidate scan: the rows of index_block_kernel (up to 32 per
+// workgroup, rows of one sequence scored together) with the candidate output
+// of index_stream_kernel in place of the scores.  Workgroup x covers the
+// candidate blocks [x bpc, (x + 1) bpc) (bsz positions each), wave w the
+// blocks x bpc + w, + 4, ..., each block's tiles in order.  The products take
+// the keys as the A operand and the queries as B, so lane 16 g + n holds
+// keys 4 g .. 4 g + 3 of a 16-key half tile for query row n (16 per
+// matrix-core pass): a lane tests four scores of one row, the row's four
+// lanes (n, n + 16, n + 32, n + 48) order their candidates with two lane-pair
+// exchanges, and the row's running count for the block stays in a register.
+// The dot products are the same as with the operands the other way round.
+constexpr int kCandUnroll = 2;     // tiles in flight per wave
+
+// v of lane l ^ 16 and of lane l ^ 32 (the swaps leave the lane's own value
+// and its partner's, in some order)
+__device__ __forceinline__ uint32_t lane_xor16(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return r[0] + r[1] - v;
+}
+__device__ __forceinline__ uint32_t lane_xor32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return r[0] + r[1] - v;
+}
+
+template <bool kPaged, bool kOut>
+__global__ void __launch_bounds__(256, 4)
+index_block_cand_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx, int R, int64_t T,
+                        const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit,
+                        float* __restrict__ scores, CandOut cand, int bsz, int bpc, PageMap pm) {
+  __shared__ int s_seq[32];
+  __shared__ int s_lim[32];
+  __shared__ float s_tf[32];
+  const int r0 = blockIdx.y * 32;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int kn = lane & 15, g = lane >> 4;
+  if (threadIdx.x < 32) {
+    const int r = r0 + threadIdx.x;
+    int64_t lim = r < R ? (row_limit ? row_limit[r] : T - 1) : -1;
+    lim = lim < -1 ? -1 : (lim > T - 1 ? T - 1 : lim);
+    s_seq[threadIdx.x] = r < R ? (row_seq ? row_seq[r] : r) : -1;
+    s_lim[threadIdx.x] = (int)lim;
+    float tf = 0.f;
+    if (r < R) {
+      // as in the streaming scan: score >= key_score(tau_s) exactly when its key >= tau_s
+      const uint32_t tau = cand.row[r].tau_s;
+      tf = tau ? key_score(tau) : -3.402823466e38f;
+    }
+    s_tf[threadIdx.x] = tf;
+  }
+  __syncthreads();
+
+  const int64_t blk_begin = (int64_t)blockIdx.x * bpc;
+  const int64_t blk_end = min(cand.n_blocks, blk_begin + bpc);
+  const int tiles_per_blk = bsz / kTile;
+  const int Ti = (int)T;
+  const float neg_inf = -__builtin_inff();
+
+  uint32_t done = 0;
+  for (int m = 0; m < 32; ++m)
+    if (s_seq[m] < 0) done |= 1u << m;
+
+  while (done != 0xFFFFFFFFu) {
+    const int first = __builtin_ctz(~done);
+    const int seq = s_seq[first];
+    uint32_t active = 0;
+    for (int m = 0; m < 32; ++m)
+      if (!(done >> m & 1u) && s_seq[m] == seq) active |= 1u << m;
+    done |= active;
+    int max_lim = -1;
+    for (int m = 0; m < 32; ++m)
+      if (active >> m & 1u) max_lim = max(max_lim, s_lim[m]);
+
+    // B operands: lane 16 g + n holds bytes 16 g .. 16 g + 15 of query row 16 mt + n
+    f16x8 a[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (active >> (16 * mt + kn) & 1u)
+        x = *reinterpret_cast<const uint4*>(q_idx + (int64_t)(r0 + 16 * mt + kn) * kIndexDim + 16 * g);
+      fp8x16_to_f16(x.x, x.y, x.z, x.w, a[mt]);
+    }
+    // the lane's rows 16 mt + n: liveness, limit (-1: none visible), threshold, candidate row
+    bool live[2];
+    int lim[2];
+    float tf[2];
+    uint2* kp_row[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int m = 16 * mt + kn;
+      live[mt] = active >> m & 1u;
+      lim[mt] = live[mt] ? s_lim[m] : -1;
+      tf[mt] = s_tf[m];
+      kp_row[mt] = cand.kp + (int64_t)(r0 + m) * T;
+    }
+
+    for (int64_t blk = blk_begin + wave; blk < blk_end; blk += 4) {
+      uint32_t at[2] = {0u, 0u};
+      const int pb = (int)(blk * bsz);
+      if (kOut || pb <= max_lim) {
+        for (int t = 0; t < tiles_per_blk; t += kCandUnroll) {
+          i32x8 b[kCandUnroll];
+          bool mapped[kCandUnroll];
+#pragma unroll
+          for (int u = 0; u < kCandUnroll; ++u) {
+            const int p0 = pb + (t + u) * kTile;
+            int64_t row0 = -1;
+            if (p0 <= max_lim) row0 = kPaged ? phys_row(pm, seq, T, p0) : (int64_t)seq * T + p0;
+            mapped[u] = row0 >= 0;
+            uint4 v[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+              v[hh] = (row0 >= 0 && p0 + 16 * hh + kn < Ti)
+                          ? load_key_part<false>(k_idx + (row0 + 16 * hh + kn) * kIndexDim + 16 * g)
+                          : make_uint4(0, 0, 0, 0);
+            b[u] = tile_pair(v[0], v[1]);
+          }
+#pragma unroll
+          for (int u = 0; u < kCandUnroll; ++u) {
+            const int p0 = pb + (t + u) * kTile;
+            if (!kOut && p0 > max_lim) break;
+            f16x8 kb[2][2];
+            fp8x16_to_f16((uint32_t)b[u][0], (uint32_t)b[u][1], (uint32_t)b[u][2], (uint32_t)b[u][3], kb[0]);
+            fp8x16_to_f16((uint32_t)b[u][4], (uint32_t)b[u][5], (uint32_t)b[u][6], (uint32_t)b[u][7], kb[1]);
+            f32x4 acc[2][2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+              for (int mt = 0; mt < 2; ++mt) {
+                acc[hh][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[hh][0], a[mt][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                acc[hh][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[hh][1], a[mt][1], acc[hh][mt], 0, 0, 0);
+              }
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int pl = p0 + 16 * hh + 4 * g;
+              const int n_t = min(4, max(0, Ti - pl));
+              const int n_in = mapped[u] ? n_t : 0;
+#pragma unroll
+              for (int mt = 0; mt < 2; ++mt) {
+                const int n_vis = min(n_in, max(0, lim[mt] - pl + 1));
+                uint32_t m4 = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) m4 |= (uint32_t)((j < n_vis) & (acc[hh][mt][j] >= tf[mt])) << j;
+                const uint32_t cnt = (uint32_t)__popc(m4);
+                const uint32_t x16 = lane_xor16(cnt);
+                const uint32_t pair = cnt + x16;
+                const uint32_t x32 = lane_xor32(pair);
+                uint32_t o = at[mt] + ((g & 1) ? x16 : 0u) + ((g & 2) ? x32 : 0u);
+                at[mt] += pair + x32;
+                while (m4) {
+                  const int j = __builtin_ctz(m4);
+                  m4 &= m4 - 1u;
+                  const float sv = j == 0 ? acc[hh][mt][0] : (j == 1 ? acc[hh][mt][1] : (j == 2 ? acc[hh][mt][2] : acc[hh][mt][3]));
+                  kp_row[mt][pb + o] = make_uint2(score_key(sv), (uint32_t)(pl + j));
+                  ++o;
+                }
+                if (kOut && live[mt]) {
+#pragma unroll
+                  for (int j = 0; j < 4; ++j)
+                    if (j < n_t) scores[(int64_t)(r0 + 16 * mt + kn) * T + pl + j] = j < n_vis ? acc[hh][mt][j] : neg_inf;
+                }
+              }
+            }
+          }
+        }
+      }
+      if (g == 0) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+          if (live[mt]) cand.cnt[(int64_t)(r0 + 16 * mt + kn) * cand.n_blocks + blk] = at[mt];
+      }
+    }
+  }
+}
+
 // workgroups of index_stream_kernel to launch: the resident count, at most 3
 // per CU (3 beat 4 and 2 in a same-box sweep of the 8 x 1M candidate scan:
 // 95.6 vs 98.4 and 102 us; more concurrent key streams than that contend)
@@ -559,6 +734,26 @@ void launch_index_scan(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, in
     index_stream_kernel<false, true, true><<<g, blk, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, scores, R, units_per_row, CandOut{}, pm);
   } else {
     index_stream_kernel<false, false, true><<<g, blk, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, scores, R, units_per_row, CandOut{}, pm);
+  }
+}
+
+void launch_index_block_cand(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int64_t T,
+                             const int32_t* row_seq, const int64_t* row_limit, float* scores, const CandOut& cand,
+                             int bsz, hipStream_t s, const PageMap& pm) {
+  // about 2,048 workgroups, at least 4 blocks (one per wave) each; when grid.x
+  // is a multiple of 8, the workgroups of one key range (same x, every row
+  // group) land on one XCD and share its L2
+  const int64_t row_groups = ((int64_t)R + 31) / 32;
+  int64_t bpc = (cand.n_blocks * row_groups + 2047) / 2048;
+  bpc = (std::max<int64_t>(bpc, 4) + 3) / 4 * 4;
+  const dim3 grid((unsigned)((cand.n_blocks + bpc - 1) / bpc), (unsigned)row_groups), blk(256);
+  const bool paged = pm.table != nullptr;
+  if (paged) {
+    if (scores) index_block_cand_kernel<true, true><<<grid, blk, 0, s>>>(q_idx, k_idx, R, T, row_seq, row_limit, scores, cand, bsz, (int)bpc, pm);
+    else index_block_cand_kernel<true, false><<<grid, blk, 0, s>>>(q_idx, k_idx, R, T, row_seq, row_limit, scores, cand, bsz, (int)bpc, pm);
+  } else {
+    if (scores) index_block_cand_kernel<false, true><<<grid, blk, 0, s>>>(q_idx, k_idx, R, T, row_seq, row_limit, scores, cand, bsz, (int)bpc, pm);
+    else index_block_cand_kernel<false, false><<<grid, blk, 0, s>>>(q_idx, k_idx, R, T, row_seq, row_limit, scores, cand, bsz, (int)bpc, pm);
   }
 }
 

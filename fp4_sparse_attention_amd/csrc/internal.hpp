@@ -44,6 +44,16 @@ void launch_index_scan(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, in
                        const int64_t* row_limit, float* scores, const CandOut* cand, hipStream_t s,
                        const PageMap& pm);
 
+// Query-block form of the candidate scan (chunked prefill: runs of query rows
+// of one sequence share every key tile): candidates in blocks of bsz
+// positions (a multiple of 128), kp [r][bsz b + i] and cnt [r][b] as above for
+// all cand.n_blocks = ceil(T / bsz) blocks of every row; hist is not touched
+// (a pass over the blocks builds it).  scores, if given, receives every score.
+constexpr int kQueryBlockPositions = 1024;
+void launch_index_block_cand(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int64_t T,
+                             const int32_t* row_seq, const int64_t* row_limit, float* scores, const CandOut& cand,
+                             int bsz, hipStream_t s, const PageMap& pm);
+
 // per-row threshold tau_s and digit shift for a selection of k from a
 // strided sample of the row's scores (samp: [R][index_sample_words()]
 // scratch); clears the row's histogram and state

@@ -1072,35 +1072,54 @@ __device__ uint32_t kth_largest_256(const uint32_t* keys, uint32_t n, uint32_t n
 
 // The first 8 candidates of a block and its count, loaded together (one round
 // trip for the common block of a few candidates); the entries beyond the count
-// are ignored (the candidate array carries 64 bytes of tail padding, so the
-// reads stay inside the workspace).
+// are ignored.  Later entries are read 8 at a time, also past the count (the
+// candidate array carries 64 bytes of tail padding, so every read stays inside
+// the workspace).
 struct BlockHead {
   uint32_t c;
   uint4 e[4];                             // (key, position) pairs 0-7
 };
 
-__device__ __forceinline__ BlockHead load_head(const uint2* kp, const uint32_t* cnt, int64_t blk) {
+// Holds a loaded value at this point.  Without it the compiler moves each load
+// of a block head into the branch that first uses it (the entries are used
+// only below the count), so a thread waits for one memory round trip per
+// candidate instead of one per block.
+__device__ __forceinline__ void keep_loaded(const uint4& v) {
+  asm volatile("" ::"v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
+}
+
+__device__ __forceinline__ BlockHead load_head(const uint2* kp, const uint32_t* cnt, int64_t blk, int bsz) {
   BlockHead h;
-  const uint4* b = reinterpret_cast<const uint4*>(kp + blk * kBlockPositions);
+  const uint4* b = reinterpret_cast<const uint4*>(kp + blk * bsz);
   h.c = cnt[blk];
 #pragma unroll
   for (int u = 0; u < 4; ++u) h.e[u] = b[u];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) keep_loaded(h.e[u]);
   return h;
 }
 
-// candidates of block blk in position order, f(key, position); hd = its head
+// candidates of block blk (bsz positions) in position order, f(key, position); hd = its head
 template <class F>
-__device__ __forceinline__ void for_block(const BlockHead& hd, const uint2* kp, int64_t blk, F&& f) {
+__device__ __forceinline__ void for_block(const BlockHead& hd, const uint2* kp, int64_t blk, int bsz, F&& f) {
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     if ((uint32_t)(2 * u) < hd.c) f(hd.e[u].x, (int32_t)hd.e[u].y);
     if ((uint32_t)(2 * u + 1) < hd.c) f(hd.e[u].z, (int32_t)hd.e[u].w);
   }
-  const uint4* b = reinterpret_cast<const uint4*>(kp + blk * kBlockPositions);
-  for (uint32_t e = 8; e < hd.c; e += 2) {
-    const uint4 v = b[e / 2];
-    f(v.x, (int32_t)v.y);
-    if (e + 1 < hd.c) f(v.z, (int32_t)v.w);
+  // the rest eight entries at a time, all four loads in flight together
+  const uint4* b = reinterpret_cast<const uint4*>(kp + blk * bsz);
+  for (uint32_t e = 8; e < hd.c; e += 8) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = b[e / 2 + u];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) keep_loaded(v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (e + 2 * u < hd.c) f(v[u].x, (int32_t)v[u].y);
+      if (e + 2 * u + 1 < hd.c) f(v[u].z, (int32_t)v[u].w);
+    }
   }
 }
 
@@ -1167,9 +1186,10 @@ __device__ __forceinline__ RowBins row_bins(const uint32_t* hr, uint32_t tau_s, 
 
 // Rebuild of a row whose threshold missed: the workgroup's blocks get every
 // visible key of their positions (scored as in the scan: wave w takes blocks
-// blk0 + w, blk0 + w + 4, ...), and hist_abs the top 12 bits of those keys.
+// blk0 + w, blk0 + w + 4, ..., each block's tiles in order), and hist_abs the
+// top 12 bits of those keys.
 __device__ void rebuild_blocks(const uint8_t* q_idx, const uint8_t* k_idx, int64_t T, int r, const int32_t* row_seq,
-                               const int64_t* row_limit, int64_t blk0, int64_t blk1, uint2* kp, uint32_t* cn,
+                               const int64_t* row_limit, int64_t blk0, int64_t blk1, int bsz, uint2* kp, uint32_t* cn,
                                uint32_t* hist_abs, uint32_t* h /* 4096, LDS */, const PageMap& pm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int kn = lane & 15, part = 16 * (lane >> 4);
@@ -1180,37 +1200,39 @@ __device__ void rebuild_blocks(const uint8_t* q_idx, const uint8_t* k_idx, int64
   f16x8 a[2];
   query_operands(q_idx + (int64_t)r * kIndexDim, lane, a);
   for (int64_t blk = blk0 + wave; blk < blk1; blk += 4) {
-    i32x8 kb[4];
-    bool ok[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t p0 = blk * kBlockPositions + 32 * i;
-      const int64_t row0 = p0 < T ? phys_row(pm, seq, T, p0) : -1;
-      uint4 v[2];
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int64_t p = p0 + 16 * hh + kn;
-        ok[i][hh] = row0 >= 0 && p < T && p <= limit;
-        v[hh] = ok[i][hh] ? load_key_part(k_idx + (row0 + 16 * hh + kn) * kIndexDim + part) : make_uint4(0, 0, 0, 0);
-      }
-      kb[i] = tile_pair(v[0], v[1]);
-    }
     uint32_t at = 0;
+    for (int t = 0; t < bsz / kTile; t += 4) {
+      i32x8 kb[4];
+      bool ok[4][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float2 sc = mfma_score(a, kb[i]);
-      const float sv[2] = {sc.x, sc.y};
+      for (int i = 0; i < 4; ++i) {
+        const int64_t p0 = blk * bsz + kTile * (t + i);
+        const int64_t row0 = p0 < T ? phys_row(pm, seq, T, p0) : -1;
+        uint4 v[2];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const uint32_t key = (lane < 16 && ok[i][hh]) ? score_key(sv[hh]) : 0u;
-        const bool c = key != 0u;
-        const uint64_t m = __ballot(c);
-        if (c) {
-          kp[blk * kBlockPositions + at + lanes_below(m)] =
-              make_uint2(key, (uint32_t)(blk * kBlockPositions + 32 * i + 16 * hh + kn));
-          atomicAdd(&h[key >> 20], 1u);
+        for (int hh = 0; hh < 2; ++hh) {
+          const int64_t p = p0 + 16 * hh + kn;
+          ok[i][hh] = row0 >= 0 && p < T && p <= limit;
+          v[hh] = ok[i][hh] ? load_key_part(k_idx + (row0 + 16 * hh + kn) * kIndexDim + part) : make_uint4(0, 0, 0, 0);
         }
-        at += (uint32_t)__popcll(m);
+        kb[i] = tile_pair(v[0], v[1]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float2 sc = mfma_score(a, kb[i]);
+        const float sv[2] = {sc.x, sc.y};
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const uint32_t key = (lane < 16 && ok[i][hh]) ? score_key(sv[hh]) : 0u;
+          const bool c = key != 0u;
+          const uint64_t m = __ballot(c);
+          if (c) {
+            kp[blk * bsz + at + lanes_below(m)] =
+                make_uint2(key, (uint32_t)(blk * bsz + kTile * (t + i) + 16 * hh + kn));
+            atomicAdd(&h[key >> 20], 1u);
+          }
+          at += (uint32_t)__popcll(m);
+        }
       }
     }
     if (lane == 0) cn[blk] = at;
@@ -1220,13 +1242,36 @@ __device__ void rebuild_blocks(const uint8_t* q_idx, const uint8_t* k_idx, int64
     if (h[i]) atomicAdd(&hist_abs[i], h[i]);
 }
 
+// The candidate histogram of each row when the query-block scan produced the
+// candidates (32 rows' 4,096-bin histograms do not fit one workgroup's LDS):
+// one workgroup per row counts the digits of its blocks' candidates in LDS
+// and stores the row's bins.
+__global__ void __launch_bounds__(kSG)
+stream_hist_kernel(int64_t T, int64_t nbk, int bsz, const StreamRow* __restrict__ rows, uint32_t* __restrict__ hist,
+                   const uint2* __restrict__ cand, const uint32_t* __restrict__ cand_cnt) {
+  __shared__ uint32_t h[kStreamBins];
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const uint32_t tau_s = rows[r].tau_s, sh = rows[r].sh;
+  const uint2* kp = cand + (int64_t)r * T;
+  const uint32_t* cn = cand_cnt + (int64_t)r * nbk;
+  for (int i = tid; i < kStreamBins; i += kSG) h[i] = 0u;
+  __syncthreads();
+  for (int64_t blk = tid; blk < nbk; blk += kSG)
+    for_block(load_head(kp, cn, blk, bsz), kp, blk, bsz, [&](uint32_t kx, int32_t) {
+      atomicAdd(&h[min((kx - tau_s) >> sh, (uint32_t)(kStreamBins - 1))], 1u);
+    });
+  __syncthreads();
+  uint32_t* hr = hist + (int64_t)r * kStreamHistWords;
+  for (int i = tid; i < kStreamBins; i += kSG) hr[i] = h[i];
+}
+
 // gather: per workgroup, the candidates above each boundary bin in its blocks,
 // and the candidates inside the boundary bin appended to the row's short list;
 // in a row to rebuild, the rebuild of its blocks instead
 __global__ void __launch_bounds__(kSG)
 stream_gather_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx, int64_t T,
                      const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit, int64_t nbk, int bpw,
-                     StreamRow* __restrict__ rows, uint32_t* __restrict__ hist, uint2* __restrict__ cand,
+                     int bsz, StreamRow* __restrict__ rows, uint32_t* __restrict__ hist, uint2* __restrict__ cand,
                      uint32_t* __restrict__ cand_cnt, uint32_t* __restrict__ above_out, uint2* __restrict__ list,
                      int32_t k, int32_t k2, PageMap pm) {
   __shared__ uint32_t tmp[8];
@@ -1241,17 +1286,17 @@ stream_gather_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restric
   // the first block's head is loaded with the histogram
   const int64_t blk0 = (int64_t)g * bpw, blk1 = min(nbk, blk0 + bpw);
   BlockHead hd0 = {};
-  if (blk0 + tid < blk1) hd0 = load_head(kp, cn, blk0 + tid);
+  if (blk0 + tid < blk1) hd0 = load_head(kp, cn, blk0 + tid, bsz);
   const RowBins rb = row_bins(hr, tau_s, k, k2, tmp, s_b);
   if (rb.rebuild) {
-    rebuild_blocks(q_idx, k_idx, T, r, row_seq, row_limit, blk0, blk1, kp, cn, hr + kStreamBins, h, pm);
+    rebuild_blocks(q_idx, k_idx, T, r, row_seq, row_limit, blk0, blk1, bsz, kp, cn, hr + kStreamBins, h, pm);
     return;
   }
   if (rb.overflow || rb.k_eff[0] == 0u) return;
   uint32_t ab[2] = {0u, 0u};
   for (int64_t blk = blk0 + tid; blk < blk1; blk += kSG) {
-    const BlockHead hd = blk == blk0 + tid ? hd0 : load_head(kp, cn, blk);
-    for_block(hd, kp, blk, [&](uint32_t kx, int32_t p) {
+    const BlockHead hd = blk == blk0 + tid ? hd0 : load_head(kp, cn, blk, bsz);
+    for_block(hd, kp, blk, bsz, [&](uint32_t kx, int32_t p) {
       const uint32_t d = min((kx - tau_s) >> sh, (uint32_t)(kStreamBins - 1));
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -1276,7 +1321,7 @@ stream_gather_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restric
 // (11 bits and then 10 at a time), prefix bits at and above `hi` must match.
 // Returns tau; need becomes the number of keys equal to tau to take.
 template <class Keep>
-__device__ uint32_t select_in_blocks(const uint2* kp, const uint32_t* cn, int64_t nbk, Keep keep, int hi,
+__device__ uint32_t select_in_blocks(const uint2* kp, const uint32_t* cn, int64_t nbk, int bsz, Keep keep, int hi,
                                      uint32_t prefix, uint32_t& need, uint32_t* h /* 2048 */, uint32_t* tmp,
                                      uint32_t* res) {
   const int tid = threadIdx.x;
@@ -1289,8 +1334,8 @@ __device__ uint32_t select_in_blocks(const uint2* kp, const uint32_t* cn, int64_
     for (int i = tid; i < nb; i += kSG) h[i] = 0u;
     __syncthreads();
     for (int64_t blk = tid; blk < nbk; blk += kSG) {
-      const BlockHead hd = load_head(kp, cn, blk);
-      for_block(hd, kp, blk, [&](uint32_t kx, int32_t) {
+      const BlockHead hd = load_head(kp, cn, blk, bsz);
+      for_block(hd, kp, blk, bsz, [&](uint32_t kx, int32_t) {
         if (keep(kx) && (hi >= 32 || (kx >> hi) == (prefix >> hi))) atomicAdd(&h[(kx >> shift) & mask], 1u);
       });
     }
@@ -1331,7 +1376,7 @@ __device__ uint32_t select_in_blocks(const uint2* kp, const uint32_t* cn, int64_
 // rebuilt or overflowing row, the k-th keys by radix passes over the blocks and
 // the per-workgroup counts by a pass over them.
 __global__ void __launch_bounds__(kSG)
-stream_finish_kernel(int64_t T, int64_t nbk, int bpw, int G, StreamRow* __restrict__ rows,
+stream_finish_kernel(int64_t T, int64_t nbk, int bpw, int bsz, int G, StreamRow* __restrict__ rows,
                      const uint32_t* __restrict__ hist, const uint32_t* __restrict__ above_out,
                      const uint2* __restrict__ list, const uint2* __restrict__ cand,
                      const uint32_t* __restrict__ cand_cnt, StreamBase* __restrict__ base_out, int32_t k,
@@ -1396,7 +1441,7 @@ stream_finish_kernel(int64_t T, int64_t nbk, int bpw, int G, StreamRow* __restri
       tau[s] = res2[2 * s];
       need_eq[s] = rb.k_eff[s] - rb.above[s] - res2[2 * s + 1];
       if (tid < (int)st.n_list[s]) {
-        const uint32_t wg = (uint32_t)(((int64_t)(int32_t)le0[s].y / kBlockPositions) / bpw);
+        const uint32_t wg = (uint32_t)(((int64_t)(int32_t)le0[s].y / bsz) / bpw);
         uint32_t* cg = s == 0 ? s_gt : h;
         uint32_t* ce = s == 0 ? s_eq : h + kStreamGroups;
         if (le0[s].x > tau[s]) atomicAdd(&cg[wg], 1u);
@@ -1434,7 +1479,7 @@ stream_finish_kernel(int64_t T, int64_t nbk, int bpw, int G, StreamRow* __restri
       need_eq[s] = need - gt_in_list;
       for (uint32_t i = tid; i < n; i += kSG) {
         const int32_t p = (int32_t)(i == (uint32_t)tid ? le0[s].y : ls[i].y);
-        const uint32_t wg = (uint32_t)(((int64_t)p / kBlockPositions) / bpw);
+        const uint32_t wg = (uint32_t)(((int64_t)p / bsz) / bpw);
         if (s_lk[i] > tau[s]) atomicAdd(&s_gt[wg], 1u);
         else if (s_lk[i] == tau[s]) atomicAdd(&s_eq[wg], 1u);
       }
@@ -1480,10 +1525,10 @@ stream_finish_kernel(int64_t T, int64_t nbk, int bpw, int G, StreamRow* __restri
         uint32_t need = k_eff[s] - above[s];
         const uint32_t bs = b0[s];
         if (mode == 1u)
-          tau[s] = select_in_blocks(kp, cn, nbk, [](uint32_t) { return true; }, 20, bs << 20, need, h, tmp, res);
+          tau[s] = select_in_blocks(kp, cn, nbk, bsz, [](uint32_t) { return true; }, 20, bs << 20, need, h, tmp, res);
         else
           tau[s] = select_in_blocks(
-              kp, cn, nbk, [=](uint32_t kx) { return min((kx - tau_s) >> sh, (uint32_t)(kStreamBins - 1)) == bs; },
+              kp, cn, nbk, bsz, [=](uint32_t kx) { return min((kx - tau_s) >> sh, (uint32_t)(kStreamBins - 1)) == bs; },
               32, 0u, need, h, tmp, res);
         need_eq[s] = need;
       }
@@ -1494,7 +1539,7 @@ stream_finish_kernel(int64_t T, int64_t nbk, int bpw, int G, StreamRow* __restri
         __syncthreads();
         for (int64_t blk = tid; blk < nbk; blk += kSG) {
           uint32_t gt = 0u, eq = 0u;
-          for_block(load_head(kp, cn, blk), kp, blk, [&](uint32_t kx, int32_t) {
+          for_block(load_head(kp, cn, blk, bsz), kp, blk, bsz, [&](uint32_t kx, int32_t) {
             gt += kx > tau[s];
             eq += kx == tau[s];
           });
@@ -1529,7 +1574,7 @@ stream_finish_kernel(int64_t T, int64_t nbk, int bpw, int G, StreamRow* __restri
 
 // ordered write: each workgroup's blocks, thread t taking a contiguous run of them
 __global__ void __launch_bounds__(kSG)
-stream_write_kernel(int64_t T, int64_t nbk, int bpw, const StreamRow* __restrict__ rows,
+stream_write_kernel(int64_t T, int64_t nbk, int bpw, int bsz, const StreamRow* __restrict__ rows,
                     const StreamBase* __restrict__ base, const uint2* __restrict__ cand,
                     const uint32_t* __restrict__ cand_cnt, int32_t k, int32_t k2, int32_t* __restrict__ idx_out,
                     float* __restrict__ score_out, int32_t* __restrict__ idx2_out) {
@@ -1541,7 +1586,7 @@ stream_write_kernel(int64_t T, int64_t nbk, int bpw, const StreamRow* __restrict
   const int64_t per = (blk1 - blk0 + kSG - 1) / kSG;
   const int64_t my0 = min(blk1, blk0 + tid * per), my1 = min(blk1, my0 + per);
   BlockHead hd0 = {};
-  if (my0 < my1) hd0 = load_head(kp, cn, my0);
+  if (my0 < my1) hd0 = load_head(kp, cn, my0, bsz);
   const StreamRow st = rows[r];
   const StreamBase bs = base[(int64_t)r * G + g];
   const uint32_t kk[2] = {(uint32_t)k, (uint32_t)k2};
@@ -1558,7 +1603,7 @@ stream_write_kernel(int64_t T, int64_t nbk, int bpw, const StreamRow* __restrict
   if (st.k_eff[0] == 0u) return;
   uint32_t gt[2] = {0u, 0u}, eq[2] = {0u, 0u};
   for (int64_t blk = my0; blk < my1; ++blk)
-    for_block(blk == my0 ? hd0 : load_head(kp, cn, blk), kp, blk, [&](uint32_t kx, int32_t) {
+    for_block(blk == my0 ? hd0 : load_head(kp, cn, blk, bsz), kp, blk, bsz, [&](uint32_t kx, int32_t) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         gt[s] += kx > st.tau[s];
@@ -1573,7 +1618,7 @@ stream_write_kernel(int64_t T, int64_t nbk, int bpw, const StreamRow* __restrict
     es[s] = bs.eq[s] + block_exclusive_scan(eq[s], tmp, tot);
   }
   for (int64_t blk = my0; blk < my1; ++blk)
-    for_block(blk == my0 ? hd0 : load_head(kp, cn, blk), kp, blk, [&](uint32_t kx, int32_t p) {
+    for_block(blk == my0 ? hd0 : load_head(kp, cn, blk, bsz), kp, blk, bsz, [&](uint32_t kx, int32_t p) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const bool is_gt = kx > st.tau[s], is_eq = kx == st.tau[s];
@@ -1593,9 +1638,10 @@ struct StreamLayout {
   size_t rows, hist, samp, cnt, above, base, list, cand, total;
 };
 
-static StreamLayout stream_layout(int32_t R, int64_t T) {
+// nbk: candidate blocks per row (the streaming scan's index_scan_blocks(T),
+// the most of any producer)
+static StreamLayout stream_layout(int32_t R, int64_t T, int64_t nbk) {
   StreamLayout L;
-  const int64_t nbk = index_scan_blocks(T);
   size_t off = 0;
   L.rows = off; off += align_up((size_t)R * sizeof(StreamRow), 256);
   L.hist = off; off += align_up((size_t)R * kStreamHistWords * 4, 256);
@@ -1816,21 +1862,15 @@ extern "C" csa2_status csa2_topk_pool(const float* scores, int32_t R, int64_t N,
   return launch_status();
 }
 
-// Whether csa2_index_full_pool can take its streaming path for this shape, and
-// the scratch it needs for scores when the caller passes none and the path is
-// not the streaming one.
+// Whether csa2_index_full_pool takes its streaming path for this shape (every
+// row layout does when the compact selection fits; otherwise scores go to
+// the caller's array or the workspace first, and csa2_topk_pool selects).
 static bool pool_may_stream(int32_t R, int64_t T) { return choose_path(R, T) == kCompact; }
-
-static size_t pool_scores_scratch(int32_t R, int64_t T) {
-  // rows of up to 32 with a compact-path length always stream
-  if (pool_may_stream(R, T) && R < 32) return 0;
-  return align_up((size_t)R * T * 4, 256);
-}
 
 extern "C" size_t csa2_index_full_pool_workspace_size(int32_t R, int64_t T, int32_t k_pool) {
   if (R <= 0 || T <= 0) return 0;
-  const size_t other = align_up(csa2_topk_workspace_size(R, T, k_pool), 256) + pool_scores_scratch(R, T);
-  return std::max(other, pool_may_stream(R, T) ? stream_layout(R, T).total : (size_t)0);
+  if (pool_may_stream(R, T)) return stream_layout(R, T, index_scan_blocks(T)).total;
+  return align_up(csa2_topk_workspace_size(R, T, k_pool), 256) + align_up((size_t)R * T * 4, 256);
 }
 
 static csa2_status index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int32_t B, int64_t T,
@@ -1848,9 +1888,9 @@ static csa2_status index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, i
   if (!workspace || workspace_bytes < csa2_index_full_pool_workspace_size(R, T, k_pool)) return CSA2_EWORKSPACE;
   if (!aligned(workspace, 256)) return CSA2_EALIGN;
   hipStream_t s = (hipStream_t)stream;
-  if (!pool_may_stream(R, T) || (!pm.table && !index_scan_streams(R, row_seq))) {
-    // short rows, very long R x T, or query blocks: scores first (into the
-    // workspace when the caller takes none), then the selection
+  if (!pool_may_stream(R, T)) {
+    // short rows or very long R x T: scores first (into the workspace when the
+    // caller takes none), then the selection
     const size_t tk = align_up(csa2_topk_workspace_size(R, T, k_pool), 256);
     float* sc = scores ? scores : reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + tk);
     if (scan_start && hipEventRecord((hipEvent_t)scan_start, s) != hipSuccess) return CSA2_ELAUNCH;
@@ -1866,8 +1906,14 @@ static csa2_status index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, i
     return csa2_topk_pool(sc, R, T, T, k_pool, k_top, nullptr, pool_idx, pool_scores, top_idx, workspace, tk,
                           stream);
   }
+  // Streaming selection.  Rows of one sequence in runs (chunked prefill) share
+  // key tiles in the query-block scan, with candidate blocks of 1,024
+  // positions; otherwise each row streams its keys, blocks of 128.
+  const bool qblocks = !index_scan_streams(R, row_seq);
+  const int bsz = qblocks ? kQueryBlockPositions : kBlockPositions;
+  const int64_t nbk = qblocks ? (T + bsz - 1) / bsz : index_scan_blocks(T);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const StreamLayout L = stream_layout(R, T);
+  const StreamLayout L = stream_layout(R, T, nbk);
   StreamRow* rows = reinterpret_cast<StreamRow*>(ws + L.rows);
   uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
   uint32_t* samp = reinterpret_cast<uint32_t*>(ws + L.samp);
@@ -1876,19 +1922,25 @@ static csa2_status index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, i
   StreamBase* base = reinterpret_cast<StreamBase*>(ws + L.base);
   uint2* list = reinterpret_cast<uint2*>(ws + L.list);
   uint2* cand = reinterpret_cast<uint2*>(ws + L.cand);
-  const int64_t nbk = index_scan_blocks(T);
-  const int groups = (int)std::min<int64_t>(kStreamGroups, nbk);
+  // gather / write workgroups per row: up to 64, fewer when many rows fill the chip anyway
+  const int groups = (int)std::min<int64_t>(std::min<int64_t>(kStreamGroups, nbk), std::max<int64_t>(1, 8192 / R));
   const int bpw = (int)((nbk + groups - 1) / groups);
   launch_index_sample_tau(q_idx, k_idx, R, T, row_seq, row_limit, k_pool, rows, hist, samp, s, pm);
   if (scan_start && hipEventRecord((hipEvent_t)scan_start, s) != hipSuccess) return CSA2_ELAUNCH;
   const CandOut co{rows, hist, cand, cnt, nbk};
-  launch_index_scan(q_idx, k_idx, R, T, row_seq, row_limit, scores, &co, s, pm);
+  if (qblocks) {
+    launch_index_block_cand(q_idx, k_idx, R, T, row_seq, row_limit, scores, co, bsz, s, pm);
+    stream_hist_kernel<<<R, kSG, 0, s>>>(T, nbk, bsz, rows, hist, cand, cnt);
+  } else {
+    launch_index_scan(q_idx, k_idx, R, T, row_seq, row_limit, scores, &co, s, pm);
+  }
   if (scan_end && hipEventRecord((hipEvent_t)scan_end, s) != hipSuccess) return CSA2_ELAUNCH;
-  stream_gather_kernel<<<dim3(groups, R), kSG, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, nbk, bpw, rows, hist,
-                                                       cand, cnt, above, list, k_pool, k_top, pm);
-  stream_finish_kernel<<<R, kSG, 0, s>>>(T, nbk, bpw, groups, rows, hist, above, list, cand, cnt, base, k_pool, k_top);
-  stream_write_kernel<<<dim3(groups, R), kSG, 0, s>>>(T, nbk, bpw, rows, base, cand, cnt, k_pool, k_top, pool_idx,
-                                                      pool_scores, top_idx);
+  stream_gather_kernel<<<dim3(groups, R), kSG, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, nbk, bpw, bsz, rows,
+                                                       hist, cand, cnt, above, list, k_pool, k_top, pm);
+  stream_finish_kernel<<<R, kSG, 0, s>>>(T, nbk, bpw, bsz, groups, rows, hist, above, list, cand, cnt, base, k_pool,
+                                          k_top);
+  stream_write_kernel<<<dim3(groups, R), kSG, 0, s>>>(T, nbk, bpw, bsz, rows, base, cand, cnt, k_pool, k_top,
+                                                      pool_idx, pool_scores, top_idx);
   return launch_status();
 }
 

@@ -195,18 +195,21 @@ csa2_status csa2_topk_pool(const float* scores, int32_t R, int64_t N, int64_t ro
  *
  * Equivalent to csa2_index_full(q_idx, k_idx, R, B, T, row_seq, row_limit,
  * scores) followed by csa2_topk_pool(scores, R, T, T, k_pool, k_top, NULL,
- * pool_idx, pool_scores, top_idx): same scores, same selections.  For long
- * rows the selection streams: a strided sample of each row bounds its k_pool-th
- * score from below, the scoring pass keeps only the positions at or above that
- * bound (in position order, block by block) and the selection finishes on
- * them; the result is exact whatever the bound (too few candidates or massive
- * ties take a slower path inside the call).
+ * pool_idx, pool_scores, top_idx): same scores, same selections.  Unless R x T
+ * is too large for the candidate lists (R * T > 2^30), the selection streams:
+ * a strided sample of each row bounds its k_pool-th score from below, the
+ * scoring pass keeps only the positions at or above that bound (in position
+ * order, block by block) and the selection finishes on them; the result is
+ * exact whatever the bound (too few candidates or massive ties take a slower
+ * path inside the call).  With row_seq given and R >= 32 (chunked prefill),
+ * runs of rows of one sequence share each key tile in the scoring pass.
  *
  *   scores     fp32 [R][T], written (masked positions -inf), or NULL: no
  *              scores are written (the selection does not need them)
  *   workspace  >= csa2_index_full_pool_workspace_size(R, T, k_pool) bytes
- *              (for shapes that do not stream, this includes room for the
- *              scores when the caller passes none)
+ *              (when the selection streams: about R * T * 8 bytes for the
+ *              candidate blocks; otherwise the Top-K workspace and room for
+ *              the scores when the caller passes none)
  *   scan_start, scan_end  hipEvent_t handles or NULL: when given, recorded on
  *              the stream right before and right after the scoring kernel
  *              (to time it apart from the selection)

@@ -150,10 +150,13 @@ def test_index_full_pool_argument_errors():
     assert L.csa2_index_full_pool(*a) == 1        # R != B without row_seq
     a = list(base); a[14] = 16
     assert L.csa2_index_full_pool(*a) == 4        # workspace
-    assert F.csa2_index_full_pool_workspace_size(8, 1 << 20, 16384) >= F.csa2_topk_workspace_size(8, 1 << 20, 16384)
-    # rows that may not stream (query blocks) get room for the scores the caller may not take
-    assert (F.csa2_index_full_pool_workspace_size(64, 1 << 16, 4096)
-            >= F.csa2_topk_workspace_size(64, 1 << 16, 4096) + 64 * (1 << 16) * 4)
+    # streaming shapes (rows longer than 32,768, R x T <= 2^30): room for the candidate blocks
+    assert F.csa2_index_full_pool_workspace_size(8, 1 << 20, 16384) >= 8 * (1 << 20) * 8
+    assert F.csa2_index_full_pool_workspace_size(4096, 1 << 18, 2048) >= 4096 * (1 << 18) * 8
+    # shapes that select from scores get room for the scores the caller may not take
+    for R, T in ((64, 1 << 15), (5000, 1 << 18)):
+        assert (F.csa2_index_full_pool_workspace_size(R, T, 2048)
+                >= F.csa2_topk_workspace_size(R, T, 2048) + R * T * 4)
     # scores may be null: the argument checks still run (and fail here on the workspace, before any launch)
     a = list(base); a[7] = NULL; a[14] = 16
     assert L.csa2_index_full_pool(*a) == 4

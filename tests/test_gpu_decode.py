@@ -161,17 +161,17 @@ def test_chunked_prefill_sampled_rows():
     limit = torch.arange(p0, T, dtype=torch.int64, device=dev)
     swa_start = torch.arange(Q, dtype=torch.int32, device=dev)     # swa row i <-> position p0 - 127 + i
     swa_len = torch.full((Q,), 128, dtype=torch.int32, device=dev)
-    scores = torch.empty((Q, T), dtype=torch.float32, device=dev)
-    F.csa2_index_full(q_idx, wl.k_idx, scores, row_seq=row_seq, row_limit=limit)
+    # the Full-layer scoring and Top-K as one streaming call (query-block scan, no score array)
     idx = torch.empty((Q, K), dtype=torch.int32, device=dev)
-    F.csa2_topk(scores, K, idx)
-    del scores
+    twin = torch.empty((Q, K), dtype=torch.int32, device=dev)
+    F.csa2_index_full_pool(q_idx, wl.k_idx, None, K, K, idx, twin, row_seq=row_seq, row_limit=limit)
     o = torch.empty((Q, H, 512), dtype=torch.float32, device=dev)
     lse = torch.empty((Q, H), dtype=torch.float32, device=dev)
     F.csa2_sparse_decode(q_lat, wl.codes, wl.scales, idx, SIGMA, o, lse, row_seq=row_seq)
     F.csa2_swa_merge(q_lat, swa, swa_start, swa_len, SIGMA, o, lse, o_sparse=o, lse_sparse=lse, row_seq=row_seq)
     torch.cuda.synchronize()
     k_host = wl.k_idx_host(0)
+    assert torch.equal(idx, twin)
     for r in (0, 1, 777, 2048, 4000, Q - 1):
         p = p0 + r
         s = OI.full_scores(np_u8(q_idx[r]), k_host, limit=p)

@@ -322,6 +322,69 @@ def test_index_full_pool_equals_separate_calls(R, T, k_pool, k_top):
     assert np.array_equal(t1[0].cpu().numpy(), OT.topk(sh, k_top))
 
 
+@pytest.mark.parametrize("R,B,T,k_pool,k_top", [(96, 3, 40000, 4000, 1000), (64, 1, 65536, 2048, 2048),
+                                                 (40, 2, 131072, 16384, 2048)])
+def test_index_full_pool_query_blocks_equal_separate_calls(R, B, T, k_pool, k_top):
+    """Chunked-prefill rows (row_seq given, R >= 32): the query-block scan with 1,024-position
+    candidate blocks gives the scores, pool (with scores) and Top-K of csa2_index_full +
+    csa2_topk_pool bit for bit: interleaved sequences, a partial row group, a ragged last block,
+    causal limits, an empty row, rows shorter than either selection, a limit beyond T."""
+    dev = device()
+    k = torch.stack([W.fp8_normal(81, (T, 64), device=dev, chunk_index=b) for b in range(B)])
+    q = W.fp8_normal(82, (R, 64), device=dev)
+    row_seq = (torch.arange(R, dtype=torch.int32) % B).to(dev)
+    rng = np.random.default_rng(R + T)
+    lim_h = (T - 1 - rng.integers(0, T // 3, R)).astype(np.int64)
+    lim_h[:4] = [-1, 100, k_pool + 5, T + 7]
+    lim = torch.from_numpy(lim_h).to(dev)
+    s1 = torch.empty((R, T), dtype=torch.float32, device=dev)
+    p1 = torch.empty((R, k_pool), dtype=torch.int32, device=dev)
+    ps1 = torch.empty((R, k_pool), dtype=torch.float32, device=dev)
+    t1 = torch.empty((R, k_top), dtype=torch.int32, device=dev)
+    F.csa2_index_full_pool(q, k, s1, k_pool, k_top, p1, t1, pool_scores=ps1, row_seq=row_seq, row_limit=lim)
+    s2 = torch.empty_like(s1)
+    p2, ps2, t2 = torch.empty_like(p1), torch.empty_like(ps1), torch.empty_like(t1)
+    F.csa2_index_full(q, k, s2, row_seq=row_seq, row_limit=lim)
+    F.csa2_topk_pool(s2, k_pool, k_top, p2, t2, pool_scores=ps2)
+    p3, ps3, t3 = torch.empty_like(p1), torch.empty_like(ps1), torch.empty_like(t1)
+    F.csa2_index_full_pool(q, k, None, k_pool, k_top, p3, t3, pool_scores=ps3, row_seq=row_seq, row_limit=lim)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    for p, ps, t in ((p1, ps1, t1), (p3, ps3, t3)):
+        assert torch.equal(p, p2) and torch.equal(t, t2)
+        assert torch.equal(torch.nan_to_num(ps, nan=7.0), torch.nan_to_num(ps2, nan=7.0))
+    assert (p1[0] == -1).all() and (t1[0] == -1).all()
+    assert (p1[1, :101] >= 0).all() and (p1[1, 101:] == -1).all()
+    # two rows against the oracle's exact scores (bit-equal to the GPU's for unit-normal keys)
+    for r in (2, R - 1):
+        b = r % B
+        exact = OI.full_scores(np_u8(q[r]), np_u8(k[b]), limit=int(lim_h[r]))
+        sh = exact.astype(np.float32).astype(np.float64)
+        assert np.array_equal(p1[r].cpu().numpy(), OT.topk(sh, k_pool)), r
+        assert np.array_equal(t1[r].cpu().numpy(), OT.topk(sh, k_top)), r
+
+
+def test_index_full_pool_prefill_shape_equals_scores_first():
+    """4,096 causal rows over 262,144 positions, Top-2,048 (chunked prefill): the streaming
+    selection over the query-block scan equals csa2_index_full + csa2_topk on every row."""
+    dev = device()
+    R, T, K = 4096, 262144, 2048
+    k = W.fp8_normal(93, (1, T, 64), device=dev)
+    q = W.fp8_normal(94, (R, 64), device=dev)
+    row_seq = torch.zeros(R, dtype=torch.int32, device=dev)
+    lim = torch.arange(T - R, T, dtype=torch.int64, device=dev)
+    pool = torch.empty((R, K), dtype=torch.int32, device=dev)
+    top = torch.empty((R, K), dtype=torch.int32, device=dev)
+    F.csa2_index_full_pool(q, k, None, K, K, pool, top, row_seq=row_seq, row_limit=lim)
+    s = torch.empty((R, T), dtype=torch.float32, device=dev)
+    F.csa2_index_full(q, k, s, row_seq=row_seq, row_limit=lim)
+    ref = torch.empty((R, K), dtype=torch.int32, device=dev)
+    F.csa2_topk(s, K, ref)
+    torch.cuda.synchronize()
+    del s
+    assert torch.equal(top, ref) and torch.equal(pool, ref)
+
+
 def _stream_case_keys(kind, R, T, q, dev, S=4096):
     """Index keys for the streaming selection's special cases (uint8 E4M3 codes [R, T, 64])."""
     g = torch.Generator(device="cpu").manual_seed(71)
@@ -395,3 +458,39 @@ def test_index_full_pool_streaming_cases(kind):
     if kind == "limits":
         assert (p1[2] == -1).all() and (t1[2] == -1).all()
         assert (p1[1, :5001] >= 0).all() and (p1[1, 5001:] == -1).all()
+
+
+@pytest.mark.parametrize("kind", ["fallback", "ties_all", "ties_256", "nan_keys"])
+def test_index_full_pool_query_blocks_streaming_cases(kind):
+    """The streaming selection's special cases through the query-block scan (64 rows over 2
+    sequences, each row with its sequence's query, so that what misleads one row's sample
+    misleads all of them): threshold misses, massive ties, NaN keys; same outputs as
+    csa2_index_full + csa2_topk_pool, with and without a scores output."""
+    dev = device()
+    B, R, T, k_pool, k_top = 2, 64, 131072, 16384, 2048
+    qb = W.fp8_normal(72, (B, 64), device=dev)
+    k = _stream_case_keys(kind, B, T, qb, dev)
+    row_seq = (torch.arange(R, dtype=torch.int32) % B).to(dev)
+    q = qb[row_seq.long()].contiguous()
+    s1 = torch.empty((R, T), dtype=torch.float32, device=dev)
+    p1 = torch.empty((R, k_pool), dtype=torch.int32, device=dev)
+    ps1 = torch.empty((R, k_pool), dtype=torch.float32, device=dev)
+    t1 = torch.empty((R, k_top), dtype=torch.int32, device=dev)
+    F.csa2_index_full_pool(q, k, s1, k_pool, k_top, p1, t1, pool_scores=ps1, row_seq=row_seq)
+    s2 = torch.empty_like(s1)
+    p2, ps2, t2 = torch.empty_like(p1), torch.empty_like(ps1), torch.empty_like(t1)
+    F.csa2_index_full(q, k, s2, row_seq=row_seq)
+    F.csa2_topk_pool(s2, k_pool, k_top, p2, t2, pool_scores=ps2)
+    p3, ps3, t3 = torch.empty_like(p1), torch.empty_like(ps1), torch.empty_like(t1)
+    F.csa2_index_full_pool(q, k, None, k_pool, k_top, p3, t3, pool_scores=ps3, row_seq=row_seq)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.nan_to_num(s1, nan=7.0), torch.nan_to_num(s2, nan=7.0))
+    assert torch.equal(s1.isnan(), s2.isnan())
+    for p, ps, t in ((p1, ps1, t1), (p3, ps3, t3)):
+        assert torch.equal(p, p2) and torch.equal(t, t2)
+        assert torch.equal(torch.nan_to_num(ps, nan=7.0), torch.nan_to_num(ps2, nan=7.0))
+    sh = s1[R - 1].cpu().numpy().astype(np.float64)
+    assert np.array_equal(p1[R - 1].cpu().numpy(), OT.topk(sh, k_pool))
+    assert np.array_equal(t1[R - 1].cpu().numpy(), OT.topk(sh, k_top))
+    if kind == "ties_all":
+        assert np.array_equal(p1.cpu().numpy(), np.tile(np.arange(k_pool, dtype=np.int32), (R, 1)))

@@ -200,6 +200,46 @@ def test_index_full_pool_paged_holes_equal_separate_calls():
         assert (rows[r, sel[sel >= 0]] >= 0).all()
 
 
+def test_index_full_pool_paged_query_blocks():
+    """Chunked-prefill rows (row_seq, R >= 32) over paged keys: the query-block scan translates
+    each tile through the table; scores, pool and Top-K equal csa2_index_full_paged +
+    csa2_topk_pool, and no selected position lies in an unmapped block."""
+    dev = device()
+    rng = np.random.default_rng(131)
+    B, R, T, page, k_pool, k_top = 2, 48, 40960, 256, 4096, 1024
+    max_blocks = T // page
+    lengths = [T, T - 5 * page - 31]
+    table, n_pages = _page_table(rng, B, max_blocks, lengths=lengths, page=page, holes=[(0, 9), (1, 40)])
+    k_pool_t = W.fp8_normal(132, (n_pages * page, 64)).to(dev)
+    q = W.fp8_normal(133, (R, 64)).to(dev)
+    tab = _dev(table, dev)
+    row_seq = (np.arange(R) % B).astype(np.int32)
+    limit = np.array([lengths[b] - 1 - int(rng.integers(0, 9000)) for b in row_seq], dtype=np.int64)
+    limit[:2] = [-1, 700]
+    rs, lm = _dev(row_seq, dev), _dev(limit, dev)
+    s1 = torch.empty((R, T), dtype=torch.float32, device=dev)
+    p1 = torch.empty((R, k_pool), dtype=torch.int32, device=dev)
+    ps1 = torch.empty((R, k_pool), dtype=torch.float32, device=dev)
+    t1 = torch.empty((R, k_top), dtype=torch.int32, device=dev)
+    F.csa2_index_full_pool_paged(q, k_pool_t, tab, page, T, s1, k_pool, k_top, p1, t1, pool_scores=ps1,
+                                 row_seq=rs, row_limit=lm)
+    p3, t3 = torch.empty_like(p1), torch.empty_like(t1)
+    F.csa2_index_full_pool_paged(q, k_pool_t, tab, page, T, None, k_pool, k_top, p3, t3, row_seq=rs, row_limit=lm)
+    s2 = torch.empty_like(s1)
+    F.csa2_index_full_paged(q, k_pool_t, tab, page, T, s2, row_seq=rs, row_limit=lm)
+    p2, ps2, t2 = torch.empty_like(p1), torch.empty_like(ps1), torch.empty_like(t1)
+    F.csa2_topk_pool(s2, k_pool, k_top, p2, t2, pool_scores=ps2)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2)
+    assert torch.equal(p1, p2) and torch.equal(t1, t2) and torch.equal(p3, p2) and torch.equal(t3, t2)
+    assert torch.equal(torch.nan_to_num(ps1, nan=7.0), torch.nan_to_num(ps2, nan=7.0))
+    rows = _rows_of(table, page, T)
+    for r in range(R):
+        sel = p1[r].cpu().numpy()
+        assert (rows[row_seq[r], sel[sel >= 0]] >= 0).all(), r
+    assert (p1[0] == -1).all()
+
+
 def test_decode_layers_paged_equals_dense_and_oracle():
     """Paged attention over a cache written by the scattered pack equals the
     dense call bit for bit; entries that fall in unmapped blocks count as
