@@ -12,7 +12,8 @@ algorithmic HBM GB/s, the roofline of the dominant kernel (the Full-layer
 index scan) timed with HIP events on the launch stream, and the CPU oracle
 timed on a bounded sample of the same workload.
 
-  python bench.py [--steps K] [--warmup W] [--workload stack_1m_b8|full_decode_b64|tiny_decode|pack_1m]
+  python bench.py [--steps K] [--warmup W]
+                  [--workload stack_1m_b8|full_decode_b64|tiny_decode|pack_1m|prefill_4k_256k]
 """
 import argparse
 import hashlib
@@ -297,6 +298,148 @@ def bench_decode(args, cfg):
     return rec
 
 
+class PrefillWorkload:
+    """Seeded chunked-prefill inputs on the GPU: one sequence's FP4 cache and indexer keys, and the
+    last `queries` positions as causal query rows with their indexer queries, absorbed queries and
+    sliding-window rows (row i sees positions <= T - queries + i and the 128 window rows before it)."""
+
+    def __init__(self, cfg, dev, chunk_rows=65536):
+        import torch
+        import workloads as W
+        from fp4_sparse_attention_amd.decode import pack_cache
+        T, Q, H = cfg.context, cfg.queries, cfg.heads
+        self.T, self.cfg, self.dev = T, cfg, dev
+        self.chunk_rows = min(chunk_rows, T)
+        self.n_chunks = (T + self.chunk_rows - 1) // self.chunk_rows
+        self.outliers = W.outlier_channels(cfg.seed)
+        self.codes = torch.empty((1, T, 256), dtype=torch.uint8, device=dev)
+        self.scales = torch.empty((1, T, 32), dtype=torch.uint8, device=dev)
+        pack_cache(self.codes, self.scales, self.latent_chunk, self.chunk_rows)
+        self.k_idx = W.fp8_normal(cfg.seed, (T, 64), device=dev, chunk_index=0)[None]
+        self.q_idx = W.fp8_normal(cfg.seed, (Q, 64), device=dev, role=3, chunk_index=100)
+        self.q_lat = W.bf16_normal(cfg.seed, (Q, H, 512), std=0.5, device=dev, role=4, chunk_index=100)
+        self.swa = W.bf16_normal(cfg.seed, (1, Q + cfg.window - 1, 512), device=dev, role=5, chunk_index=100)
+        self.row_seq = torch.zeros(Q, dtype=torch.int32, device=dev)
+        self.limit = torch.arange(T - Q, T, dtype=torch.int64, device=dev)
+        self.swa_start = torch.arange(Q, dtype=torch.int32, device=dev)
+        self.swa_len = torch.full((Q,), cfg.window, dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+
+    latent_chunk = Workload.latent_chunk
+    latent_host = Workload.latent_host
+
+
+def cpu_baseline_prefill(wl, cfg, n_rows):
+    """Time the CPU oracle on n_rows of the prefill rows (scores over the row's visible positions,
+    Top-K, FP4 round trip of the selected rows, sparse and window attention, merge)."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+    from oracle import formats as OF, indexer as OI, topk as OT, attention as OA
+
+    cores = len(os.sched_getaffinity(0))
+    blas = [p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max(blas) if blas else 1
+    Q, T = cfg.queries, cfg.context
+    k_host = wl.k_idx[0].cpu().numpy()
+    swa_host = wl.swa[0].to(torch.float64).cpu().numpy()
+    rows = np.linspace(0, Q - 1, n_rows).astype(np.int64)
+    elapsed = 0.0
+    for r in rows:
+        q_idx = wl.q_idx[r].cpu().numpy()
+        q_lat = wl.q_lat[r].to(torch.float64).cpu().numpy()
+        t0 = time.perf_counter()
+        idx = OT.topk(OI.full_scores(q_idx, k_host, limit=T - Q + int(r)), cfg.topk)
+        elapsed += time.perf_counter() - t0
+        lat = wl.latent_host(0, idx[idx >= 0])            # regenerating the rows is input generation
+        t0 = time.perf_counter()
+        c, s_ = OF.fp4_pack(lat)
+        o_s, l_s = OA.attend(q_lat, OF.fp4_unpack(c, s_), SIGMA)
+        o_w, l_w = OA.attend(q_lat, OA.window_rows(swa_host, int(r), cfg.window), SIGMA)
+        OA.merge(o_s, l_s, o_w, l_w)
+        elapsed += time.perf_counter() - t0
+    return {"value": n_rows / elapsed, "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_rows} of {Q} prefill rows (numpy; BLAS pool {threads} threads of {cores} allowed cores; "
+                      f"index scan single-threaded int64)",
+            "seconds": elapsed}
+
+
+def bench_prefill(args, cfg):
+    """One chunked-prefill layer per step: the Full-layer scores and Top-K of every query row
+    (csa2_index_full_pool, the streaming selection over the query-block scan, no score array), then
+    the sparse + window attention of every row (csa2_sparse_swa_decode)."""
+    import torch
+    import fp4_sparse_attention_amd as F
+    dev = torch.device("cuda:0")
+    wl = PrefillWorkload(cfg, dev)
+    T, Q, H, K = cfg.context, cfg.queries, cfg.heads, cfg.topk
+    idx = torch.empty((Q, K), dtype=torch.int32, device=dev)
+    twin = torch.empty((Q, K), dtype=torch.int32, device=dev)
+    o = torch.empty((Q, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((Q, H), dtype=torch.float32, device=dev)
+    ws_p = torch.empty(F.csa2_index_full_pool_workspace_size(Q, T, K), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(F.csa2_sparse_swa_decode_workspace_size(Q, H, K), dtype=torch.uint8, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+
+    def step(timed=False):
+        F.csa2_index_full_pool(wl.q_idx, wl.k_idx, None, K, K, idx, twin, row_seq=wl.row_seq, row_limit=wl.limit,
+                               workspace=ws_p)
+        if timed:
+            ev[0].record()
+        F.csa2_sparse_swa_decode(wl.q_lat, wl.codes, wl.scales, idx, wl.swa, wl.swa_start, wl.swa_len, SIGMA, o,
+                                 lse, row_seq=wl.row_seq, workspace=ws_a)
+        if timed:
+            ev[1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    attn_ms = 0.0
+    ev[2].record()
+    for _ in range(args.steps):
+        step(timed=True)
+        torch.cuda.synchronize()
+        attn_ms += ev[0].elapsed_time(ev[1])
+    ev[3].record()
+    torch.cuda.synchronize()
+    # the steps' time without the host synchronisations: a second run, untimed per call
+    ev[2].record()
+    for _ in range(args.steps):
+        step()
+    ev[3].record()
+    torch.cuda.synchronize()
+    ms = ev[2].elapsed_time(ev[3]) / args.steps
+    attn_ms /= args.steps
+    n_pos = K + cfg.window
+    attn_flops = Q * H * n_pos * 512 * 2 * 2                 # q.x and p.x per head and position
+    index_bytes = T * 64 + Q * 64 + 2 * Q * K * 4            # keys and queries read, two index arrays written
+    rec = {
+        "metric": METRIC,
+        "value": Q / (ms * 1e-3),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "launch": "eager",
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e2m1/e4m3 storage; e4m3xe4m3->f32 index; f16xf16->f32 attention",
+        "data": "synthetic (seeded torch normal draws; FP4 cache packed by the library)",
+        "config": {"workload": cfg.name, "queries": Q, "context": T, "heads": H, "topk": K, "window": cfg.window,
+                   "latent_channels": 512},
+        "index_algorithmic_bytes": index_bytes,
+        "roofline": {"kernel": "csa2_sparse_swa_decode (attn_chunk_kernel: one chunk per row, o and lse written "
+                               "directly)", "bound": "mfma",
+                     "achieved": attn_flops / (attn_ms * 1e-3) / 1e12, "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": attn_flops / (attn_ms * 1e-3) / 2.5e15, "traffic": None, "launch_ms": attn_ms,
+                     "flops_per_launch": attn_flops},
+    }
+    rec["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline_prefill(wl, cfg, args.cpu_sample or 16)
+    return rec
+
+
 def bench_pack(args, cfg):
     import torch
     import workloads as W
@@ -384,6 +527,8 @@ def main():
     print(f"# workload {cfg.name}: building inputs", file=sys.stderr, flush=True)
     if isinstance(cfg, W.PackStream):
         rec = bench_pack(args, cfg)
+    elif isinstance(cfg, W.ChunkedPrefill):
+        rec = bench_prefill(args, cfg)
     else:
         rec = bench_decode(args, cfg)
     print(json.dumps(rec), flush=True)

@@ -27,7 +27,9 @@
 //      transpose load), B = P from LDS; fp32 accumulators stay in VGPRs.
 // The chunk's unnormalised O, running max m and sum l go to the workspace; a
 // combine kernel merges the chunks (and, for a window merge, the sparse
-// result) into o and lse.
+// result) into o and lse.  When a row has one chunk and no prior result (enough
+// rows to fill the chip, e.g. chunked prefill), the chunk kernel normalises and
+// writes o and lse itself, with the combine's arithmetic for one chunk.
 #include <type_traits>
 
 #include "internal.hpp"
@@ -107,6 +109,8 @@ struct AttnArgs {
   float scale_log2;               // softmax scale * log2(e)
   float* o_part;                  // [L][R][n_chunks][H][512]
   float* ml_part;                 // [L][R][n_chunks][H][2]
+  float* o_out;                   // one chunk and no prior: the final o [L][R][H][512] (null: partials)
+  float* lse_out;                 // and lse [L][R][H] (may be null then)
   PageMap pm;                     // codes / scales as page pools (table null: [B][T] rows)
 };
 
@@ -124,6 +128,7 @@ attn_chunk_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float sp[4 * NT * 16 * kSStride];
   __shared__ __attribute__((aligned(16))) _Float16 pp[NT * 16 * kPStride];
   __shared__ float s_alpha[NT * 16];
+  __shared__ float s_inv_l[NT * 16];
   __shared__ int s_valid[kKT];
   __shared__ int s_pos[kMaxChunkKeys];        // this chunk's cache positions (-1: skip)
 
@@ -352,6 +357,23 @@ attn_chunk_kernel(const AttnArgs a) {
     if (j + 1 < n_sp) process(buf1, false, j + 1);
   }
 
+  if (a.o_out) {
+    // the row's only chunk and no prior: normalise here, as the combine would for one chunk
+    if (wave < NT && g == 0) s_inv_l[16 * wave + m] = l_run > 0.f ? 1.f / l_run : 0.f;
+    __syncthreads();
+    const int64_t orow = ((int64_t)layer * a.R + r) * H + hbase;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float inv = s_inv_l[16 * nt + m];
+      float* op = a.o_out + (orow + 16 * nt + m) * kLatent + cbase + 4 * g;
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        *reinterpret_cast<f32x4*>(op + 16 * t) = inv > 0.f ? oacc[t][nt] * inv : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (a.lse_out && wave < NT && g == 0)
+      a.lse_out[orow + 16 * wave + m] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : neg_inf;
+    return;
+  }
   // ---- this chunk's partial: unnormalised O, and (m, l) from the softmax owners
   const int64_t prow = (((int64_t)layer * a.R + r) * a.n_chunks + chunk) * H + hbase;
 #pragma unroll
@@ -542,10 +564,15 @@ static csa2_status attention_call(int32_t L, const uint16_t* q_lat, int32_t R, i
   if (!aligned(workspace, 256)) return CSA2_EALIGN;
   a.o_part = static_cast<float*>(workspace);
   a.ml_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + off_ml);
+  // one chunk per row and no prior result (many rows): the chunk kernel writes o and lse itself
+  const bool direct = a.n_chunks == 1 && o_prev == nullptr && lse_prev == nullptr;
+  a.o_out = direct ? o : nullptr;
+  a.lse_out = direct ? lse : nullptr;
   hipStream_t s = (hipStream_t)stream;
   launch_chunks(a, s);
-  attn_combine_kernel<<<dim3(H, R, L), kCombineThreads, 0, s>>>(a.o_part, a.ml_part, a.n_chunks, R, H, o_prev,
-                                                                lse_prev, o, lse);
+  if (!direct)
+    attn_combine_kernel<<<dim3(H, R, L), kCombineThreads, 0, s>>>(a.o_part, a.ml_part, a.n_chunks, R, H, o_prev,
+                                                                  lse_prev, o, lse);
   return launch_status();
 }
 

@@ -237,3 +237,49 @@ def test_layers_call_equals_single_layer_calls():
         ref_l = l1.cpu().numpy().astype(np.float64)
         for b in range(B):
             assert_attention_close(o[l, b].cpu().numpy(), lse[l, b].cpu().numpy(), ref_o[b], ref_l[b], f"layer {l} b {b}")
+
+
+def test_many_rows_single_chunk_writes_outputs_directly():
+    """With enough rows (here 300 over 2 sequences, 64 heads) each row is one chunk and the chunk
+    kernel writes the normalised o and lse itself: against the oracle on sampled rows, including
+    a row with no valid key and no window (o = 0, lse = -inf), a window-only row and a sparse-only
+    row; the same rows through csa2_sparse_decode (one chunk, direct) and csa2_swa_merge (with a
+    prior, through the combine) agree with the fused call within rounding."""
+    dev = device()
+    B, T, H, K, R = 2, 3000, 64, 256, 300
+    rng = np.random.default_rng(41)
+    lat, ref_rows = _cache(B, T, seed=43)
+    codes, scales = _gpu_cache(lat, dev)
+    row_seq = (np.arange(R) % B).astype(np.int32)
+    q = W.bf16_normal(44, (R, H, 512), std=0.5)
+    S = 400
+    swa = W.bf16_normal(45, (B, S, 512))
+    start = rng.integers(0, S - 128, R).astype(np.int32)
+    length = np.full(R, 128, dtype=np.int32)
+    idx = np.stack([np.sort(rng.choice(T, K, replace=False)) for _ in range(R)]).astype(np.int32)
+    idx[0] = -1
+    length[0] = 0                      # nothing at all
+    idx[1] = -1                        # window only
+    length[2] = 0                      # sparse only
+    idx[3, 100:] = -1                  # short sparse list
+    to = lambda a: torch.from_numpy(a).to(dev)
+    o = torch.empty((R, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((R, H), dtype=torch.float32, device=dev)
+    F.csa2_sparse_swa_decode(q.to(dev), codes, scales, to(idx), swa.to(dev), to(start), to(length), SIGMA, o, lse,
+                             row_seq=to(row_seq))
+    o2 = torch.empty_like(o)
+    lse2 = torch.empty_like(lse)
+    F.csa2_sparse_decode(q.to(dev), codes, scales, to(idx), SIGMA, o2, lse2, row_seq=to(row_seq))
+    F.csa2_swa_merge(q.to(dev), swa.to(dev), to(start), to(length), SIGMA, o2, lse2, o_sparse=o2, lse_sparse=lse2,
+                     row_seq=to(row_seq))
+    torch.cuda.synchronize()
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+    qf = q.to(torch.float64).numpy()
+    swf = swa.to(torch.float64).numpy()
+    for r in (0, 1, 2, 3, 150, R - 1):
+        b = int(row_seq[r])
+        o_s, l_s = OA.sparse_attend(qf[r], ref_rows[b], idx[r], SIGMA)
+        o_w, l_w = OA.attend(qf[r], OA.window_rows(swf[b], int(start[r]), int(length[r])), SIGMA)
+        o_ref, l_ref = OA.merge(o_s, l_s, o_w, l_w)
+        assert_attention_close(o[r].cpu().numpy(), lse[r].cpu().numpy(), o_ref, l_ref, f"row {r}")
+        assert_attention_close(o2[r].cpu().numpy(), lse2[r].cpu().numpy(), o_ref, l_ref, f"row {r} two calls")
