@@ -80,6 +80,7 @@ __device__ __forceinline__ f16x4 lds_tr16(const _Float16* p) {
 }
 
 constexpr int kMaxLayers = 8;
+constexpr int kPrefetch = 4;             // sparse tiles whose gathers are in flight ahead of the math (4 vs 2: -1.3 us on the 8 x 1M stack)
 
 // One launch covers L layers.  Layer l has its own queries, window rows and
 // outputs, and reads the index slice at idx + idx_off[l] (layers may share one).
@@ -114,7 +115,7 @@ struct AttnArgs {
   PageMap pm;                     // codes / scales as page pools (table null: [B][T] rows)
 };
 
-// raw FP4 data of the lane's two keys for one tile (prefetched two tiles ahead)
+// raw FP4 data of the lane's two keys for one tile (gathered kPrefetch tiles ahead)
 struct RawTile {
   uint4 v[2];         // 16 code bytes (32 channels) per key
   uint32_t sc[2];     // 2 scale bytes per key
@@ -267,7 +268,7 @@ attn_chunk_kernel(const AttnArgs a) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         *reinterpret_cast<f32x4*>(spmine + (16 * nt + m) * kSStride + 16 * mt + 4 * g) = sacc[nt];
-      if (!win && mt == 1 && j + 2 < n_sp) load_tile(raw, j + 2);   // buffer free: refill two tiles ahead
+      if (!win && mt == 1 && j + kPrefetch < n_sp) load_tile(raw, j + kPrefetch);   // buffer free: refill it
     }
     if (wave == 0 && g == 0) {
       s_valid[m] = valid_mt[0];
@@ -345,16 +346,18 @@ attn_chunk_kernel(const AttnArgs a) {
     }
   };
 
-  RawTile buf0, buf1;
-  if (n_sp > 0) load_tile(buf0, 0);
-  if (n_sp > 1) load_tile(buf1, 1);
+  RawTile buf[kPrefetch];
+#pragma unroll
+  for (int b = 0; b < kPrefetch; ++b)
+    if (b < n_sp) load_tile(buf[b], b);
   for (int i = 0; i < n_wt; ++i) {
     if (i > 0) load_window(w0 + i);
-    process(buf0, true, -1);
+    process(buf[0], true, -1);
   }
-  for (int j = 0; j < n_sp; j += 2) {
-    process(buf0, false, j);
-    if (j + 1 < n_sp) process(buf1, false, j + 1);
+  for (int j = 0; j < n_sp; j += kPrefetch) {
+#pragma unroll
+    for (int b = 0; b < kPrefetch; ++b)
+      if (j + b < n_sp) process(buf[b], false, j + b);
   }
 
   if (a.o_out) {
