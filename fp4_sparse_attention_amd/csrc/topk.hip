@@ -1909,7 +1909,8 @@ static csa2_status index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, i
   // Streaming selection.  Rows of one sequence in runs (chunked prefill) share
   // key tiles in the query-block scan, with candidate blocks of 1,024
   // positions; otherwise each row streams its keys, blocks of 128.
-  const bool qblocks = !index_scan_streams(R, row_seq);
+  // (positions within a block are 32-bit in the query-block scan: rows of up to 2^31 - 2^11 positions)
+  const bool qblocks = !index_scan_streams(R, row_seq) && T <= (int64_t(1) << 31) - 2048;
   const int bsz = qblocks ? kQueryBlockPositions : kBlockPositions;
   const int64_t nbk = qblocks ? (T + bsz - 1) / bsz : index_scan_blocks(T);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
