@@ -1924,7 +1924,7 @@ static csa2_status index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, i
   uint2* list = reinterpret_cast<uint2*>(ws + L.list);
   uint2* cand = reinterpret_cast<uint2*>(ws + L.cand);
   // gather / write workgroups per row: up to 64, fewer when many rows fill the chip anyway
-  const int groups = (int)std::min<int64_t>(std::min<int64_t>(kStreamGroups, nbk), std::max<int64_t>(1, 8192 / R));
+  const int groups = (int)std::min<int64_t>(std::min<int64_t>(kStreamGroups, nbk), std::max<int64_t>(1, 4096 / R));
   const int bpw = (int)((nbk + groups - 1) / groups);
   launch_index_sample_tau(q_idx, k_idx, R, T, row_seq, row_limit, k_pool, rows, hist, samp, s, pm);
   if (scan_start && hipEventRecord((hipEvent_t)scan_start, s) != hipSuccess) return CSA2_ELAUNCH;
