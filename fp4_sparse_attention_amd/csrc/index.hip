@@ -283,11 +283,14 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
 // Sample: S = 4096 keys per row in 512 runs of 8 adjacent positions; run u
 // starts at ((2u + 1) V) / 1024 - 4 (clamped to the visible range [0, V),
 // V = min(T, row_limit + 1)), so the runs cover the row evenly and each costs
-// one 512-byte read.  Each wave scores two 32-sample tiles with the scan's
-// tile arithmetic; the keys go to samp [R][S].  Grid (S / 256, R).
+// one 512-byte read.  Each wave scores kSampleTiles 32-sample tiles with the
+// scan's tile arithmetic (two for a few rows, four for many: fewer, longer
+// workgroups, -15 us at 4,096 rows); the keys go to samp [R][S].  Grid
+// (S / (128 kSampleTiles), R).
 constexpr int kSampleN = 4096;
 constexpr int kSampleRun = 8;
 
+template <int kSampleTiles>
 __global__ void __launch_bounds__(256)
 index_sample_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx, int64_t T,
                     const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit,
@@ -299,14 +302,14 @@ index_sample_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
   const int64_t V = limit < 0 ? 0 : (limit + 1 < T ? limit + 1 : T);
   const int seq = row_seq ? row_seq[r] : r;
   constexpr int kRuns = kSampleN / kSampleRun;
-  i32x8 kb[2];
-  bool ok[2][2];
+  i32x8 kb[kSampleTiles];
+  bool ok[kSampleTiles][2];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < kSampleTiles; ++u) {
     uint4 v[2];
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      const int64_t i = ((int64_t)(blockIdx.x * 4 + wave) * 2 + u) * kTile + 16 * hh + kn;
+      const int64_t i = ((int64_t)(blockIdx.x * 4 + wave) * kSampleTiles + u) * kTile + 16 * hh + kn;
       const int64_t run = i / kSampleRun;
       int64_t p0 = ((2 * run + 1) * V) / (2 * kRuns) - kSampleRun / 2;
       p0 = p0 < 0 ? 0 : (p0 > V - kSampleRun ? V - kSampleRun : p0);
@@ -321,9 +324,9 @@ index_sample_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
   f16x8 a[2];
   query_operands(q_idx + (int64_t)r * kIndexDim, lane, a);
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < kSampleTiles; ++u) {
     const float2 sc = mfma_score(a, kb[u]);
-    const int64_t i = ((int64_t)(blockIdx.x * 4 + wave) * 2 + u) * kTile + kn;
+    const int64_t i = ((int64_t)(blockIdx.x * 4 + wave) * kSampleTiles + u) * kTile + kn;
     if (lane < 16) {
       samp[(int64_t)r * kSampleN + i] = ok[u][0] ? score_key(sc.x) : 0u;
       samp[(int64_t)r * kSampleN + i + 16] = ok[u][1] ? score_key(sc.y) : 0u;
@@ -740,11 +743,12 @@ void launch_index_scan(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, in
 void launch_index_block_cand(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int64_t T,
                              const int32_t* row_seq, const int64_t* row_limit, float* scores, const CandOut& cand,
                              int bsz, hipStream_t s, const PageMap& pm) {
-  // about 2,048 workgroups, at least 4 blocks (one per wave) each; when grid.x
-  // is a multiple of 8, the workgroups of one key range (same x, every row
-  // group) land on one XCD and share its L2
+  // about 8,192 workgroups, at least 4 blocks (one per wave) each (8,192 beat
+  // 2,048 by 7% at 4,096 x 262,144: shorter workgroups balance better); when
+  // grid.x is a multiple of 8, the workgroups of one key range (same x, every
+  // row group) land on one XCD and share its L2
   const int64_t row_groups = ((int64_t)R + 31) / 32;
-  int64_t bpc = (cand.n_blocks * row_groups + 2047) / 2048;
+  int64_t bpc = (cand.n_blocks * row_groups + 8191) / 8192;
   bpc = (std::max<int64_t>(bpc, 4) + 3) / 4 * 4;
   const dim3 grid((unsigned)((cand.n_blocks + bpc - 1) / bpc), (unsigned)row_groups), blk(256);
   const bool paged = pm.table != nullptr;
@@ -760,7 +764,10 @@ void launch_index_block_cand(const uint8_t* q_idx, const uint8_t* k_idx, int32_t
 void launch_index_sample_tau(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int64_t T,
                              const int32_t* row_seq, const int64_t* row_limit, int32_t k, StreamRow* rows,
                              uint32_t* hist, uint32_t* samp, hipStream_t s, const PageMap& pm) {
-  index_sample_kernel<<<dim3(kSampleN / 256, R), 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, samp, pm);
+  if (R >= 64)
+    index_sample_kernel<4><<<dim3(kSampleN / (4 * 4 * kTile), R), 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, samp, pm);
+  else
+    index_sample_kernel<2><<<dim3(kSampleN / (4 * 2 * kTile), R), 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, samp, pm);
   index_tau_kernel<<<R, 1024, 0, s>>>(samp, T, row_limit, k, rows, hist);
 }
 
