@@ -995,7 +995,7 @@ topk_write_cand_kernel(int64_t N, const uint32_t* __restrict__ cand_key, const i
 // row, costs more than a launch here, and so does resolving the row again in
 // every write workgroup.)
 // ----------------------------------------------------------------------------
-constexpr int kStreamGroups = 64;        // gather / write workgroups per row
+constexpr int kStreamGroups = 32;        // gather / write workgroups per row (at most)
 constexpr int kListCap = 4096;           // boundary-bin list entries per row and selection
 constexpr int kSG = 256;                 // threads per gather / write workgroup
 
