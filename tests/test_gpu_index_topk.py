@@ -323,12 +323,13 @@ def test_index_full_pool_equals_separate_calls(R, T, k_pool, k_top):
 
 
 @pytest.mark.parametrize("R,B,T,k_pool,k_top", [(96, 3, 40000, 4000, 1000), (64, 1, 65536, 2048, 2048),
-                                                 (40, 2, 131072, 16384, 2048)])
+                                                 (40, 2, 131072, 16384, 2048), (40, 40, 33000, 1024, 128)])
 def test_index_full_pool_query_blocks_equal_separate_calls(R, B, T, k_pool, k_top):
     """Chunked-prefill rows (row_seq given, R >= 32): the query-block scan with 1,024-position
     candidate blocks gives the scores, pool (with scores) and Top-K of csa2_index_full +
     csa2_topk_pool bit for bit: interleaved sequences, a partial row group, a ragged last block,
-    causal limits, an empty row, rows shorter than either selection, a limit beyond T."""
+    causal limits, an empty row, rows shorter than either selection, a limit beyond T, and a
+    row group whose 32 rows all belong to different sequences (one pass per sequence)."""
     dev = device()
     k = torch.stack([W.fp8_normal(81, (T, 64), device=dev, chunk_index=b) for b in range(B)])
     q = W.fp8_normal(82, (R, 64), device=dev)
