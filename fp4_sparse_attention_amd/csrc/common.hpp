@@ -33,13 +33,14 @@ constexpr int kWindowMax = 128;     // sliding-window bound
 // ----------------------------------------------------------------------------
 // scalar conversions
 // ----------------------------------------------------------------------------
-// E4M3FN byte (non-NaN) -> fp32, exact.  Normal codes: exponent e (bias 7) and
-// mantissa m map to fp32 exponent e+120; subnormal codes are m * 2^-9.
+// E4M3FN byte -> fp32, exact.  Normal codes: exponent e (bias 7) and mantissa m
+// map to fp32 exponent e+120; subnormal codes are m * 2^-9; 0x7F / 0xFF are NaN.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
   uint32_t mag = b & 0x7Fu;
   float normal = __uint_as_float((mag << 20) + (120u << 23));
   float sub = (float)mag * 0.001953125f;
   float v = mag >= 8u ? normal : sub;
+  v = mag == 0x7Fu ? __builtin_nanf("") : v;
   return (b & 0x80u) ? -v : v;
 }
 

@@ -71,7 +71,10 @@ __device__ __forceinline__ void pack_block(const uint32_t* w, uint32_t& lo, uint
     amax_bits = max(amax_bits, max(a, b));    // |bf16| orders like its bit pattern
   }
   float amax = __uint_as_float(amax_bits << 16);
-  uint32_t code = e4m3_code_nonneg(__fdiv_rn(amax, 6.0f));
+  // a NaN anywhere in the block (|bits| above the infinity pattern) gives the
+  // NaN scale 0x7F; its NaN thresholds then leave every magnitude code at 0, so
+  // the whole block decodes to NaN.  Infinities saturate like large finite values.
+  uint32_t code = amax_bits > 0x7F80u ? 0x7Fu : e4m3_code_nonneg(__fdiv_rn(amax, 6.0f));
   float s = e4m3_to_f32(code);
   E2M1Thresholds t = make_thresholds(s);
   uint32_t out[2] = {0u, 0u};

@@ -24,7 +24,8 @@ Module map:
   formats    E2M1 / E4M3 codecs and the FP4 block pack/unpack     [MTP] ¶4
   indexer    exact indexer scores, Full and Reindex scoring          [MTP] ¶3, [HN]
   topk       Top-K / candidate-pool selection                         [HN], [MTP] ¶3
-  attention  sparse attention, sliding window, log-sum-exp merge      [HN], [MTP] ¶2, [FO]
+  attention  sparse attention, sliding window, log-sum-exp merge,     [HN], [MTP] ¶2, [FO]
+             query absorption / output unabsorption (per-head MLA maps)
   pipeline   one decode layer in Full / Reindex / Reuse role          [MTP] ¶3, [FO]
   paging     logical view of a paged global KV pool                    [HF] abstract
 

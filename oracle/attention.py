@@ -16,6 +16,13 @@ Readings where the pages are silent:
   * window and sparse parts form one softmax over the union of their keys
     (log-sum-exp merge), with no gate, sink or de-duplication.
 
+  * the per-head query and output live in a 128-d head space: a head's key
+    is W_UK,h x and its value W_UV,h x for a latent row x (W [128, 512] per
+    head), so the query is absorbed as q_lat = W_UK,h^T q and the latent
+    output is mapped back as o = W_UV,h o_lat (multi-head latent attention in
+    absorbed form; the pages name the 512-channel latent and the 128-d heads,
+    not the head mathematics).
+
 All arithmetic is float64; lse is a natural logarithm.
 """
 import numpy as np
@@ -77,3 +84,26 @@ def merge(o_a: np.ndarray, lse_a: np.ndarray, o_b: np.ndarray, lse_b: np.ndarray
         wb = np.where(np.isneginf(lse_b), 0.0, np.exp(lse_b - lse))
     o = wa[:, None] * o_a + wb[:, None] * o_b
     return o, lse
+
+
+def absorb(q: np.ndarray, w_uk: np.ndarray) -> np.ndarray:
+    """Absorbed queries: q_lat[..., h, c] = sum_d q[..., h, d] * w_uk[h, d, c].
+
+    q: [..., H, 128] per-head queries; w_uk: [H, 128, 512], the map from a
+    latent row to head h's key.  Returns float64 [..., H, 512].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    w = np.asarray(w_uk, dtype=np.float64)
+    return np.einsum("...hd,hdc->...hc", q, w)
+
+
+def unabsorb(o_lat: np.ndarray, w_uv: np.ndarray) -> np.ndarray:
+    """Head outputs: o[..., h, d] = sum_c w_uv[h, d, c] * o_lat[..., h, c].
+
+    o_lat: [..., H, 512] attention outputs in the latent space; w_uv:
+    [H, 128, 512], the map from a latent row to head h's value.  Returns
+    float64 [..., H, 128].
+    """
+    o = np.asarray(o_lat, dtype=np.float64)
+    w = np.asarray(w_uv, dtype=np.float64)
+    return np.einsum("...hc,hdc->...hd", o, w)

@@ -8,7 +8,7 @@ Tolerances (the design notes derive them):
   * Top-K sets from GPU scores vs exact scores: equal except swaps among
     scores within 1e-6 relative (checked on the exact scores);
   * attention: per (row, head) max_c |o - o_ref| / max_c |o_ref| <= 2e-3 and
-    |lse - lse_ref| <= 1e-4 * max(1, |lse_ref|).
+    |lse - lse_ref| <= 1e-4 (absolute).
 """
 import numpy as np
 import pytest
@@ -48,7 +48,7 @@ def assert_attention_close(o, lse, o_ref, lse_ref, what=""):
     assert np.array_equal(np.isneginf(lse), empty), f"{what}: empty-set pattern differs"
     ok = ~empty
     if ok.any():
-        lerr = np.abs(lse[ok] - lse_ref[ok]) / np.maximum(1.0, np.abs(lse_ref[ok]))
+        lerr = np.abs(lse[ok] - lse_ref[ok])
         assert float(lerr.max()) <= LSE_TOL, f"{what}: lse error {float(lerr.max()):.3e}"
     return worst
 

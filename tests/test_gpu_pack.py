@@ -32,6 +32,11 @@ def _special_rows():
     z = np.zeros(512); z[16:32] = -0.0; z[40] = 6 * 2.0 ** -10; z[64] = 4096.0; z[65] = -1e30
     z[80] = 3e-5; z[96:112] = -1e-3 * np.arange(16)
     rows.append(z)
+    # non-finite entries: a NaN block decodes to NaN, infinities saturate
+    nf = rng.standard_normal(512)
+    nf[3] = np.nan; nf[16 + 5] = -np.nan; nf[40] = np.inf; nf[41] = -np.inf; nf[64:80] = np.nan
+    nf[96] = np.inf; nf[97] = np.nan; nf[130] = -np.inf
+    rows.append(nf)
     x = np.stack(rows)
     return torch.from_numpy(x).to(torch.bfloat16)
 
@@ -57,6 +62,14 @@ def test_pack_special_values_bit_exact():
     rc, rs = OF.fp4_pack(x.to(torch.float64).numpy())
     assert np.array_equal(np_u8(scales), rs)
     assert np.array_equal(np_u8(codes), rc)
+    # the unpacked values, NaN blocks included (NaN compares by position; the
+    # sign bit is checked on every other value)
+    out = torch.empty_like(x.to(dev))
+    F.csa2_fp4_unpack(codes, scales, out)
+    got, ref = bf16_to_f64(out), OF.fp4_unpack(rc, rs)
+    assert np.array_equal(np.isnan(got), np.isnan(ref)) and int(np.isnan(ref).sum()) == 64
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin]) and np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
 
 
 def test_pack_strided_into_cache_rows():

@@ -149,3 +149,56 @@ def test_stack_roles_share_pool_and_indices():
     # a Reindex layer's scores are exactly the Full scores of its own query on the pool
     from oracle import indexer as I
     assert np.array_equal(res[1]["scores"], I.full_scores(layers[1]["q_idx"], k_idx)[pool])
+
+
+def _unabsorbed_heads(q_heads, rows, w_uk, w_uv, sigma):
+    """Multi-head attention written directly: head h's keys W_UK,h x and values
+    W_UV,h x for every latent row x, softmax over sigma q_h . k."""
+    H = q_heads.shape[0]
+    out = np.empty((H, w_uv.shape[1]))
+    lse = np.empty(H)
+    for h in range(H):
+        k = rows @ w_uk[h].T                 # [n, 128]
+        v = rows @ w_uv[h].T                 # [n, 128]
+        s = sigma * (k @ q_heads[h])         # [n]
+        out[h] = softmax(s) @ v
+        lse[h] = logsumexp(s)
+    return out, lse
+
+
+def test_absorbed_equals_unabsorbed_mla():
+    # associativity: (W_UK^T q) . x == q . (W_UK x) and W_UV (sum p x) == sum p (W_UV x)
+    rng = np.random.default_rng(9)
+    H, n = 6, 200
+    q = rng.standard_normal((H, 128))
+    w_uk = rng.standard_normal((H, 128, 512)) / np.sqrt(512)
+    w_uv = rng.standard_normal((H, 128, 512)) / np.sqrt(512)
+    rows = rng.standard_normal((n, 512))
+    sigma = 1 / np.sqrt(128)
+    o_lat, lse = A.attend(A.absorb(q, w_uk), rows, sigma)
+    o = A.unabsorb(o_lat, w_uv)
+    o2, lse2 = _unabsorbed_heads(q, rows, w_uk, w_uv, sigma)
+    assert np.allclose(o, o2, rtol=1e-12, atol=1e-12) and np.allclose(lse, lse2, rtol=1e-12, atol=1e-12)
+
+
+def test_absorb_orientation_one_hot_and_brute_force():
+    rng = np.random.default_rng(10)
+    H = 3
+    w_uk = rng.standard_normal((H, 128, 512))
+    w_uv = rng.standard_normal((H, 128, 512))
+    # a one-hot head query picks one row of W_UK,h; a one-hot latent output one column of W_UV,h
+    q = np.zeros((2, H, 128)); q[0, 1, 7] = 1.0; q[1, 2, 127] = -2.0
+    ql = A.absorb(q, w_uk)
+    assert ql.shape == (2, H, 512)
+    assert np.array_equal(ql[0, 1], w_uk[1, 7]) and np.array_equal(ql[1, 2], -2.0 * w_uk[2, 127])
+    assert np.all(ql[0, 0] == 0) and np.all(ql[1, 0] == 0)
+    ol = np.zeros((1, H, 512)); ol[0, 0, 300] = 1.0
+    o = A.unabsorb(ol, w_uv)
+    assert o.shape == (1, H, 128) and np.array_equal(o[0, 0], w_uv[0, :, 300]) and np.all(o[0, 1:] == 0)
+    # element-by-element sums on a small random case
+    qs = rng.standard_normal((2, H, 128)); os_ = rng.standard_normal((2, H, 512))
+    ql, oo = A.absorb(qs, w_uk), A.unabsorb(os_, w_uv)
+    for r, h, c in [(0, 0, 0), (1, 2, 511), (0, 1, 260)]:
+        assert np.isclose(ql[r, h, c], sum(qs[r, h, d] * w_uk[h, d, c] for d in range(128)), rtol=1e-13)
+    for r, h, d in [(0, 0, 0), (1, 2, 127), (1, 1, 64)]:
+        assert np.isclose(oo[r, h, d], sum(w_uv[h, d, c] * os_[r, h, c] for c in range(512)), rtol=1e-13)

@@ -251,3 +251,35 @@ def test_bf16_round_matches_torch():
     ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(F.bf16_round(x.astype(np.float32)), ref)
     assert np.array_equal(F.bf16_to_float(ref), torch.from_numpy(ref.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy())
+
+
+def test_non_finite_blocks():
+    # Reading for non-finite latent values: E4M3 has no infinity, and the scale
+    # rule already saturates finite values above 448, so an infinity behaves as
+    # the largest finite value (same scale and codes as a huge finite entry);
+    # a NaN makes the block's amax NaN, which encodes as the E4M3 NaN 0x7F, so
+    # the whole block decodes to NaN while the row's other blocks are untouched.
+    x = np.zeros((1, 48))
+    x[0, 1], x[0, 2], x[0, 3] = 1.0, -3.0, 1500.0
+    x[0, 16 + 1], x[0, 16 + 2] = 1.0, -3.0
+    x[0, 32 + 5] = 0.75
+    inf_row = x.copy(); inf_row[0, 3] = np.inf; inf_row[0, 4] = -np.inf
+    big_row = x.copy(); big_row[0, 3] = 1e30; big_row[0, 4] = -1e30
+    ci, si = F.fp4_pack(inf_row)
+    cb, sb = F.fp4_pack(big_row)
+    assert np.array_equal(ci, cb) and np.array_equal(si, sb)
+    assert si[0, 0] == 0x7E                                 # 448: saturated
+    assert (ci[0, 1] >> 4) == 0x7 and (ci[0, 2] & 0xF) == 0xF  # +6 / -6
+    back = F.fp4_unpack(ci, si)
+    assert back[0, 3] == 2688.0 and back[0, 4] == -2688.0
+    nan_row = x.copy(); nan_row[0, 16] = np.nan
+    cn, sn = F.fp4_pack(nan_row)
+    assert sn[0, 1] == 0x7F
+    assert np.all(cn[0, 8:16] & 0x77 == 0)                  # every magnitude code 0
+    assert (cn[0, 9] & 0xF) == 0x8                           # the sign of -3 is kept
+    back = F.fp4_unpack(cn, sn)
+    assert np.all(np.isnan(back[0, 16:32]))
+    ref_c, ref_s = F.fp4_pack(x)
+    keep = np.r_[0:8, 16:24]
+    assert np.array_equal(cn[0, keep], ref_c[0, keep]) and sn[0, 0] == ref_s[0, 0] and sn[0, 2] == ref_s[0, 2]
+    assert np.array_equal(back[0, np.r_[0:16, 32:48]], F.fp4_unpack(ref_c, ref_s)[0, np.r_[0:16, 32:48]])

@@ -16,10 +16,11 @@ positions.
 from .configs import (CONFIGS, TinyDecode, PackStream, FullDecode, DecodeStack,
                       ChunkedPrefill, by_name)
 from .generate import (outlier_channels, latent_rows, fp8_normal, bf16_normal,
-                       bf16_bits, fp8_bits, bits_to_bf16_float, decode_layer_inputs)
+                       bf16_bits, fp8_bits, bits_to_bf16_float, decode_layer_inputs,
+                       head_queries, absorb_weights)
 
 __all__ = [
     "CONFIGS", "TinyDecode", "PackStream", "FullDecode", "DecodeStack", "ChunkedPrefill",
     "by_name", "outlier_channels", "latent_rows", "fp8_normal", "bf16_normal", "bf16_bits",
-    "fp8_bits", "bits_to_bf16_float", "decode_layer_inputs",
+    "fp8_bits", "bits_to_bf16_float", "decode_layer_inputs", "head_queries", "absorb_weights",
 ]

@@ -12,13 +12,16 @@ Recipe (values are standard normal before the cast):
   * indexer keys and queries: 64-d OCP E4M3FN (torch cast, round-to-nearest-even);
   * latent queries: bf16 with std 0.5, the spread a unit-normal 128-d head query
     has after absorption into the 512-channel latent by N(0, 1/512) weights;
-  * sliding-window rows: bf16, same outlier channels as the latent KV.
+  * sliding-window rows: bf16, same outlier channels as the latent KV;
+  * per-head queries (128-d, before absorption): bf16 N(0, 1);
+  * absorption weights W_UK, W_UV [heads, 128, 512]: bf16 N(0, 1/512).
 """
 import numpy as np
 import torch
 
 # role ids for per-tensor generator seeds
 _ROLE_OUTLIER, _ROLE_LATENT, _ROLE_KIDX, _ROLE_QIDX, _ROLE_QLAT, _ROLE_SWA, _ROLE_MISC = range(7)
+_ROLE_QHEAD, _ROLE_WUK, _ROLE_WUV = 7, 8, 9
 
 
 def _gen(seed: int, role: int, device) -> torch.Generator:
@@ -98,3 +101,20 @@ def decode_layer_inputs(seed: int, layer: int, rows: int, heads: int, window_row
     if outliers.numel():
         swa[:, :, outliers.to(swa.device)] *= 8.0
     return {"q_lat": q_lat, "q_idx": q_idx, "swa": swa.to(torch.bfloat16)}
+
+
+def head_queries(seed: int, layer: int, rows: int, heads: int, head_dim: int = 128, device="cpu"):
+    """bf16 [rows, heads, head_dim] per-head queries, N(0, 1), before absorption."""
+    return bf16_normal(seed, (rows, heads, head_dim), std=1.0, device=device, role=_ROLE_QHEAD,
+                       chunk_index=layer)
+
+
+def absorb_weights(seed: int, layer: int, heads: int, head_dim: int = 128, channels: int = 512,
+                   device="cpu"):
+    """(W_UK, W_UV): bf16 [heads, head_dim, channels] each, N(0, 1/channels)."""
+    std = float(1.0 / np.sqrt(channels))
+    w_uk = bf16_normal(seed, (heads, head_dim, channels), std=std, device=device, role=_ROLE_WUK,
+                       chunk_index=layer)
+    w_uv = bf16_normal(seed, (heads, head_dim, channels), std=std, device=device, role=_ROLE_WUV,
+                       chunk_index=layer)
+    return w_uk, w_uv
