@@ -67,6 +67,8 @@ _SIGS = {
                                           _c_void_p, _size_t, _c_void_p]),
     "csa2_decode_append": (_i32, [_i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                                   _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "csa2_absorb_q": (_i32, [_c_void_p, _i32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p]),
+    "csa2_unabsorb_o": (_i32, [_c_void_p, _i32, _i32, _i32, _c_void_p, _c_void_p, _c_void_p]),
     "csa2_sparse_swa_decode_layers_paged": (_i32, [_i32, _c_void_p, _i32, _i32, _c_void_p, _c_void_p, _i32, _i64,
                                                    _c_void_p, _c_void_p, _i64, _i32, _c_void_p, _c_void_p, _i32,
                                                    _c_void_p, _i32, _c_void_p, _c_void_p, _f32, _c_void_p, _c_void_p,
@@ -656,3 +658,32 @@ def csa2_decode_append(new_latent, cache_rows, codes, scales, new_keys=None, k_i
                                   _p(k_idx), _p(new_window), _p(swa), S, _p(tok_pos), _p(swa_start), _p(swa_len),
                                   _stream(stream))
     _check("csa2_decode_append", st)
+
+
+def csa2_absorb_q(q, w_uk, q_lat, stream=None):
+    """Per-head queries into the latent space: q bf16 [R, H, 128], w_uk bf16 [H, 128, 512]
+    -> q_lat bf16 [R, H, 512] (written)."""
+    _need(q, torch.bfloat16, "q", 3)
+    _need(w_uk, torch.bfloat16, "w_uk", 3)
+    _need(q_lat, torch.bfloat16, "q_lat", 3)
+    for t, nm in ((q, "q"), (w_uk, "w_uk"), (q_lat, "q_lat")):
+        _dense(t, nm)
+    R, H, D = q.shape
+    if w_uk.shape != (H, D, 512) or q_lat.shape != (R, H, 512):
+        raise ValueError("absorb shapes")
+    _check("csa2_absorb_q", lib().csa2_absorb_q(_p(q), R, H, D, _p(w_uk), _p(q_lat), _stream(stream)))
+
+
+def csa2_unabsorb_o(o_lat, w_uv, out, stream=None):
+    """Latent attention outputs back to head space: o_lat fp32 [R, H, 512], w_uv bf16 [H, 128, 512]
+    -> out fp32 [R, H, 128] (written)."""
+    _need(o_lat, torch.float32, "o_lat", 3)
+    _need(w_uv, torch.bfloat16, "w_uv", 3)
+    _need(out, torch.float32, "out", 3)
+    for t, nm in ((o_lat, "o_lat"), (w_uv, "w_uv"), (out, "out")):
+        _dense(t, nm)
+    R, H, C = o_lat.shape
+    D = out.shape[2]
+    if C != 512 or w_uv.shape != (H, D, 512) or out.shape[:2] != (R, H):
+        raise ValueError("unabsorb shapes")
+    _check("csa2_unabsorb_o", lib().csa2_unabsorb_o(_p(o_lat), R, H, D, _p(w_uv), _p(out), _stream(stream)))

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa2.so")
-SOURCES = ["api.hip", "pack.hip", "index.hip", "topk.hip", "attention.hip"]
+SOURCES = ["api.hip", "pack.hip", "index.hip", "topk.hip", "attention.hip", "absorb.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

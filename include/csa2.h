@@ -92,12 +92,16 @@ const char* csa2_status_str(csa2_status status);
  * cache at position T-1 of every sequence (stride T * C/2 bytes).
  * Errors: EINVAL (null pointer, n_rows < 0, bad stride), ESHAPE (C), EALIGN.
  * n_rows == 0 is a no-op.
+ * Non-finite input: a block holding a NaN gets the NaN scale 0x7F and
+ * magnitude codes 0 (it unpacks to NaN); an infinity counts as a value above
+ * 448 * 6 (scale 448, element code +-6).
  * ------------------------------------------------------------------------- */
 csa2_status csa2_fp4_pack(const uint16_t* x, int64_t n_rows, int32_t C, int64_t x_row_stride,
                           uint8_t* codes, int64_t codes_row_stride,
                           uint8_t* scales, int64_t scales_row_stride, void* stream);
 
-/* FP4 unpack: x[r][c] = E2M1(code) * E4M3(scale) as bf16 (always exact).
+/* FP4 unpack: x[r][c] = E2M1(code) * E4M3(scale) as bf16 (always exact; a NaN
+ * scale byte 0x7F / 0xFF gives NaN).
  *   codes uint8 [n_rows][C/2], scales uint8 [n_rows][C/16] (dense), x bf16
  *   [n_rows][C] (dense).  Same errors as csa2_fp4_pack. */
 csa2_status csa2_fp4_unpack(const uint8_t* codes, const uint8_t* scales, int64_t n_rows, int32_t C,
@@ -222,6 +226,17 @@ csa2_status csa2_index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, int
                                  int32_t k_pool, int32_t k_top, int32_t* pool_idx, float* pool_scores,
                                  int32_t* top_idx, void* workspace, size_t workspace_bytes, void* scan_start,
                                  void* scan_end, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Arithmetic of every attention call below: the matrix cores form q . x with
+ * exact products (each head's query is scaled by a power of two into the f16
+ * range, and the score takes the power back; window rows, bf16 of any range,
+ * use bf16 products), add them in fp32, and run the softmax in fp32; P enters
+ * the value products as f16 for cache rows (2^-11 relative) and as a bf16 pair
+ * (high part + remainder, about 2^-17) for window rows.  Every finite bf16
+ * query and window value is supported; the scores softmax_scale * q . x must
+ * stay finite in fp32 (|score| < 2e38).
+ * ------------------------------------------------------------------------- */
 
 /* ---------------------------------------------------------------------------
  * Sparse attention over the FP4 cache (HN summary key points: global sparse
@@ -420,6 +435,36 @@ csa2_status csa2_decode_append(int32_t B, int32_t L, const uint16_t* new_latent,
                                uint8_t* codes, uint8_t* scales, const uint8_t* new_keys, uint8_t* k_idx,
                                const uint16_t* new_window, uint16_t* swa, int32_t S, const int64_t* tok_pos,
                                int32_t* swa_start, int32_t* swa_len, void* stream);
+
+/* -------------------------------------------------------------------------
+ * Query absorption and output unabsorption (helpers around the attention
+ * calls, which take absorbed queries and return latent outputs).  Every head
+ * attends over the one 512-channel latent row per position (HN summary key
+ * points: the layers share one main KV; MarkTechPost retelling, paragraph 3);
+ * head h's key of a latent row x is W_UK[h] x and its value W_UV[h] x, with
+ * 128-d head queries and outputs, so the attention of q over keys W_UK x
+ * equals the attention of q_lat = W_UK[h]^T q over the latent rows, and the
+ * head output is W_UV[h] applied to the latent output.
+ *
+ *   csa2_absorb_q:   q_lat[r][h][c] = sum_d q[r][h][d] * w_uk[h][d][c]
+ *     q      bf16 [R][H][D], D = 128
+ *     w_uk   bf16 [H][D][512]
+ *     q_lat  bf16 [R][H][512]: the fp32 sum of the exact bf16 products,
+ *            rounded once to bf16 (nearest, ties to even)
+ *   csa2_unabsorb_o: out[r][h][d] = sum_c w_uv[h][d][c] * o_lat[r][h][c]
+ *     o_lat  fp32 [R][H][512] (the attention calls' o)
+ *     w_uv   bf16 [H][D][512], D = 128
+ *     out    fp32 [R][H][D]: o_lat enters as two bf16 parts (nearest bf16 and
+ *            the nearest bf16 of the remainder, about 16 significant bits),
+ *            products exact, fp32 accumulation
+ * All tensors dense.  R == 0 is a no-op.
+ * Errors: EINVAL (R < 0, H <= 0, null pointer), ESHAPE (D != 128,
+ * H > 65535), EALIGN (16-byte pointers).
+ * ------------------------------------------------------------------------- */
+csa2_status csa2_absorb_q(const uint16_t* q, int32_t R, int32_t H, int32_t D, const uint16_t* w_uk,
+                          uint16_t* q_lat, void* stream);
+csa2_status csa2_unabsorb_o(const float* o_lat, int32_t R, int32_t H, int32_t D, const uint16_t* w_uv,
+                            float* out, void* stream);
 #ifdef __cplusplus
 }
 #endif

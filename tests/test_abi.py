@@ -208,3 +208,17 @@ def test_decode_append_argument_errors():
                                 NULL) == 2
     assert L.csa2_decode_append(2, 0, ctypes.c_void_p(264), DUMMY, DUMMY, DUMMY, NULL, NULL, NULL, NULL, 0, NULL, NULL,
                                 NULL, NULL) == 3
+
+
+def test_absorb_argument_errors():
+    L = F.lib()
+    assert L.csa2_absorb_q(NULL, 1, 4, 128, NULL, NULL, NULL) == 1                 # null pointers
+    assert L.csa2_absorb_q(DUMMY, -1, 4, 128, DUMMY, DUMMY, NULL) == 1             # R < 0
+    assert L.csa2_absorb_q(DUMMY, 1, 0, 128, DUMMY, DUMMY, NULL) == 1              # H <= 0
+    assert L.csa2_absorb_q(DUMMY, 1, 4, 64, DUMMY, DUMMY, NULL) == 2               # D != 128
+    assert L.csa2_absorb_q(ctypes.c_void_p(264), 1, 4, 128, DUMMY, DUMMY, NULL) == 3
+    assert L.csa2_absorb_q(DUMMY, 0, 4, 128, DUMMY, DUMMY, NULL) == 0              # empty: no-op
+    assert L.csa2_unabsorb_o(NULL, 1, 4, 128, DUMMY, DUMMY, NULL) == 1
+    assert L.csa2_unabsorb_o(DUMMY, 1, 4, 96, DUMMY, DUMMY, NULL) == 2
+    assert L.csa2_unabsorb_o(DUMMY, 1, 4, 128, DUMMY, ctypes.c_void_p(260), NULL) == 3
+    assert L.csa2_unabsorb_o(DUMMY, 0, 4, 128, DUMMY, DUMMY, NULL) == 0
