@@ -6,25 +6,38 @@
 // Absorbed multi-head latent attention: every head of a row attends over the
 // same 512-channel latent rows, used as key and as value.
 //
-// Work split (split-K): a workgroup of four waves owns one query row and one
-// chunk of keys (a run of 32-key tiles from idx, or one 32-row tile of the row's window), for
-// all H <= 64 heads.  Wave w owns latent channels [128w, 128w+128):
-//   1. gather: lane (m = l%16, g = l/16) loads 16 code bytes + 2 scale bytes
-//      (32 channels) of keys m and 16+m of the tile -- each FP4 element is
-//      fetched and dequantised by exactly one lane; the next tile's loads are
-//      in flight during the current tile's math;
-//   2. dequantise in registers (v_cvt_scalef32_pk_f16_fp4 with unit scale,
-//      times the E4M3 block scale in f16: exact, <= 6 significant bits in
-//      [2^-10, 2688]) straight into the A operands of
-//      v_mfma_f32_16x16x32_f16, and store the slice key-major in LDS;
-//   3. partial scores S^T[key][head] over the wave's 128 channels (B = the
-//      wave's slice of the queries, kept in registers);
-//   4. the four partials meet in LDS; wave w sums them for heads [16w, 16w+16)
-//      and runs the online softmax in the exp2 domain (one head per lane
-//      column, two cross-lane steps), publishing P (f16) and the rescale factors;
-//   5. O^T[channel][head] += X^T P^T for the wave's channels: the A operand is
-//      read from the key-major slice with ds_read_b64_tr_b16 (gfx950 LDS
-//      transpose load), B = P from LDS; fp32 accumulators stay in VGPRs.
+// Work split (split-K): a workgroup of four waves owns one query row of one
+// layer and one chunk of its keys (a run of 32-key tiles from idx, plus up to
+// one 32-row tile of the row's window), for all H <= 64 heads, so that every
+// gathered tile is dequantised once for all heads.  Wave w owns latent
+// channels [128 w, 128 w + 128):
+//   A. gather (eight tiles ahead, registers): lane (m = l % 16, g = l / 16)
+//      loads 16 code bytes and the 2 scale bytes (32 channels) of keys m and
+//      16 + m; dequantise in registers (v_cvt_scalef32_pk_f16_fp4 with unit
+//      scale -- the instruction's scale acts only as a power of two -- times the
+//      E4M3 block scale in f16; exact, <= 6 significant bits in [2^-10, 2688])
+//      into the A operands of v_mfma_f32_16x16x32_f16, store the slice key-major
+//      in LDS, and form the partial scores S^T[key][head] over the wave's 128
+//      channels;
+//   B. the four partials meet in LDS; wave w sums them for heads [16 w,
+//      16 w + 16) and runs the online softmax in the exp2 domain (one head per
+//      lane column, two cross-lane steps), publishing P and the rescale factor;
+//   C. O^T[channel][head] += X^T P^T for the wave's channels: the A operand is
+//      read from the key-major slice with ds_read_b64_tr_b16 (gfx950's
+//      transposing LDS read), B = P from LDS; fp32 accumulators in registers.
+// The loop is software-pipelined with two barriers per tile: the first region
+// holds A of tile i and the first half of C of tile i - 1, the second region B
+// of tile i and the rest of C of tile i - 1 (X and P are double-buffered), so
+// the matrix products of one tile overlap the dequantisation and softmax of
+// the next.
+//
+// Exactness for every finite bf16 input: each head's query is scaled by a
+// power of two that puts its largest magnitude at 2^15..2^16 before the f16
+// conversion (exact down to 2^-32 of that maximum), and the score picks the
+// power back up in its softmax scale; window rows, which are bf16 of any
+// range, go through v_mfma_f32_16x16x32_bf16 for Q K^T and, with P split into
+// a bf16 high part and a bf16 remainder, for P V.
+//
 // The chunk's unnormalised O, running max m and sum l go to the workspace; a
 // combine kernel merges the chunks (and, for a window merge, the sparse
 // result) into o and lse.  When a row has one chunk and no prior result (enough
@@ -37,20 +50,28 @@
 namespace csa2 {
 
 constexpr int kKT = 32;                  // keys per tile
-constexpr int kXwStride = 144;           // halfs per key row of a wave's slice (128 + 16 pad)
 constexpr int kSStride = 36;             // floats per head row of a partial-score tile
 constexpr int kPStride = 40;             // halfs per head row of P
-constexpr int kMaxChunkTiles = 64;       // tiles per chunk at most
+constexpr int kQwStride = 136;           // halfs per head row of a wave's bf16 query slice (128 + 8 pad)
+constexpr int kMaxChunkTiles = 64;       // sparse tiles per chunk at most
 constexpr int kMaxChunkKeys = kMaxChunkTiles * kKT;
 constexpr int kWindowChunks = kWindowMax / kKT;   // one-tile chunks covering the longest window
-constexpr float kRescaleSlack = 8.0f;    // keep the reference max until exceeded by 2^8
+constexpr float kMaxSlack = 15.0f;       // P = 2^(s - m_ref) stays below 2^15 (f16 holds it)
+constexpr float kRefLead = 8.0f;         // the reference starts this far above the first tile's max
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kPrefetch = 4;             // sparse tiles whose gathers are in flight ahead of the math (8 does not fit the registers)
+constexpr int kMaxLayers = 8;
+constexpr int kQTop = 15;                // a head's largest |q| is scaled to [2^15, 2^16)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ f32x4 mfma16(const f16x8& a, const f16x8& b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16bf(const bf16x8& a, const bf16x8& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // 8 E2M1 nibbles (one code dword; channel 2j in the low nibble of byte j) times
@@ -63,34 +84,51 @@ __device__ __forceinline__ f16x8 fp4x8_to_f16(uint32_t d, f16x2 s2) {
   return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], e[0], e[1]};
 }
 
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
-  float a = __uint_as_float(w << 16), b = __uint_as_float(w & 0xFFFF0000u);
-  f16x2 h = {(_Float16)a, (_Float16)b};
-  return __builtin_bit_cast(uint32_t, h);
+__device__ __forceinline__ s16x4 lds_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(p));
 }
 
-__device__ __forceinline__ f16x8 bf16x8_to_f16(uint4 v) {
-  uint32_t w[4] = {bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w)};
-  return __builtin_bit_cast(f16x8, w);
+// largest biased exponent field among 8 bf16 values (one uint4)
+__device__ __forceinline__ uint32_t bf16x8_max_exp(uint4 v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t e = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) e = max(e, max((w[i] >> 7) & 0xFFu, (w[i] >> 23) & 0xFFu));
+  return e;
 }
 
-__device__ __forceinline__ f16x4 lds_tr16(const _Float16* p) {
-  s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3)))*)(p));
-  return __builtin_bit_cast(f16x4, v);
+// 8 bf16 values times 2^-sh into f16 (exact for magnitudes >= 2^-17 after scaling)
+__device__ __forceinline__ f16x8 bf16x8_scaled(uint4 v, int sh) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  f16x8 h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[2 * i] = (_Float16)__builtin_ldexpf(__uint_as_float(w[i] << 16), -sh);
+    h[2 * i + 1] = (_Float16)__builtin_ldexpf(__uint_as_float(w[i] & 0xFFFF0000u), -sh);
+  }
+  return h;
 }
 
-constexpr int kMaxLayers = 8;
-constexpr int kPrefetch = 4;             // sparse tiles whose gathers are in flight ahead of the math (4 vs 2: -1.3 us on the 8 x 1M stack)
+// 8 bf16 values times 2^-sh, as bf16 (exact unless the result leaves the fp32 range)
+__device__ __forceinline__ bf16x8 bf16x8_scaled_bf16(uint4 v, int sh) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  bf16x8 b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    b[2 * i] = (__bf16)__builtin_ldexpf(__uint_as_float(w[i] << 16), -sh);
+    b[2 * i + 1] = (__bf16)__builtin_ldexpf(__uint_as_float(w[i] & 0xFFFF0000u), -sh);
+  }
+  return b;
+}
 
 // One launch covers L layers.  Layer l has its own queries, window rows and
 // outputs, and reads the index slice at idx + idx_off[l] (layers may share one).
 // Each (layer, row) splits its keys into n_chunks chunks: chunk c takes the
 // window tiles [c wpc, (c+1) wpc) (tile w: rows [32w, 32w+32) of the window)
-// and the sparse tiles [c spc, (c+1) spc).  Window tiles go first; the loads of
-// the first one are issued at the start of the workgroup.
+// and the sparse tiles [c spc, (c+1) spc).
 struct AttnArgs {
   const uint16_t* q_lat;          // bf16 [L][R][H][512]
-  int R, H, L, head_groups;
+  int R, H, L;
   const uint8_t* codes;           // [B][T][256]
   const uint8_t* scales;          // [B][T][32]
   int64_t T;
@@ -103,6 +141,7 @@ struct AttnArgs {
   int window_per_chunk;           // window tiles per chunk
   int sparse_per_chunk;           // sparse tiles per chunk
   int n_chunks;
+  int n_pairs;                    // R * n_chunks (row, chunk) pairs
   const uint16_t* swa;            // bf16 [L][B][S][512]
   int B, S;
   const int32_t* swa_start;       // [L][R]
@@ -115,48 +154,114 @@ struct AttnArgs {
   PageMap pm;                     // codes / scales as page pools (table null: [B][T] rows)
 };
 
-// raw FP4 data of the lane's two keys for one tile (gathered kPrefetch tiles ahead)
+// raw FP4 data of the lane's key for one tile (gathered kPrefetch tiles ahead):
+// lane (key n, half h) of wave w holds codes of channels 128 w + 64 h + [0, 64)
+// and the dword of their four block scales
 struct RawTile {
-  uint4 v[2];         // 16 code bytes (32 channels) per key
-  uint32_t sc[2];     // 2 scale bytes per key
-  int valid[2];
+  uint4 c0, c1;       // 32 code bytes
+  uint32_t sc;        // 4 scale bytes
 };
 
-template <int NT>
-__global__ void __launch_bounds__(256, 2)
-attn_chunk_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 xw[4 * kKT * kXwStride];
-  __shared__ __attribute__((aligned(16))) float sp[4 * NT * 16 * kSStride];
-  __shared__ __attribute__((aligned(16))) _Float16 pp[NT * 16 * kPStride];
-  __shared__ float s_alpha[NT * 16];
-  __shared__ float s_inv_l[NT * 16];
-  __shared__ int s_valid[kKT];
-  __shared__ int s_pos[kMaxChunkKeys];        // this chunk's cache positions (-1: skip)
+__device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32bf(const bf16x8& a, const bf16x8& b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
 
-  const int chunk = blockIdx.x;
-  const int r = blockIdx.y;
-  const int layer = blockIdx.z / a.head_groups;
+// Workgroup id -> (row, chunk, layer): the eight XCDs take workgroups in turn,
+// so ids b with the same b mod 8 share an XCD; all layers of one (row, chunk)
+// get consecutive ids of one XCD and gather their rows through the same L2.
+//
+// Matrix-core layouts (v_mfma_f32_32x32x16_*, the full-rate shape on gfx950;
+// the 16x16x32 shape issues at about half its rate), wave w, lane l with
+// n = l % 32, h = l / 32:
+//   operands: lane l holds row (or column) n, k = 8 h + j, j < 8; output:
+//   lane l holds column n, rows 8 q + 4 h + r in register 4 q + r.
+//   QK:  S^T[key][head] = X[key][ch] Q^T[ch][head]; k-step ks maps k = 8 h + j
+//        to channel 128 w + 64 h + 8 ks + j (for X, lane n is key n; for Q^T
+//        it is head 32 hb + n).  The output gives lane (n, h) keys 8 q + 4 h + r
+//        of head 32 hb + n.
+//   X^T: T_b = X_{2b} E_0 + X_{2b+1} E_1 with E_s[k][n] = (n == k + 16 s)
+//        puts channel k of k-step 2 b + s in column k + 16 s: lane (n, h) gets
+//        keys 8 q + 4 h + r of channel column n (exact: one product by 1.0).
+//        Column n is channel 128 w + 64 ((n % 16) / 8) + 16 b + 8 (n / 16) + n % 8.
+//   PV:  O^T[ch][head] += X^T P^T over key steps kk: lane (n, h) supplies keys
+//        {16 kk + 4 h + r, 16 kk + 8 + 4 h + r}, r < 4 -- registers 8 kk .. 8 kk
+//        + 7 of T_b for X^T, and for P^T the same keys of head 32 hb + n, which
+//        the softmax lane (head, g = 2 kk + h) writes as one 16-byte row.
+//        Output lane (n, h) register 4 q + r is head 32 hb + n, channel
+//        128 w + 64 (q & 1) + 16 b + 8 (q >> 1) + 4 h + r.
+template <int HB>
+__global__ void __launch_bounds__(256, 1)
+attn_chunk_kernel(const AttnArgs a) {
+  constexpr int NH = 32 * HB;                 // heads, padded to whole 32-head blocks
+  constexpr int NS = NH / 16;                 // softmax waves (16 heads each)
+  __shared__ __attribute__((aligned(16))) float sp[4][NH * kSStride];
+  __shared__ __attribute__((aligned(16))) uint16_t pp[2][NH * kPStride];
+  __shared__ float s_inv_l[NH];
+  __shared__ int s_restart;                   // a head's scores passed its reference by kMaxSlack
+  __shared__ __attribute__((aligned(16))) float s_mask[kKT];
+  __shared__ int s_qe[4][NH];
+  __shared__ int s_pos[kMaxChunkKeys];        // this chunk's cache rows (-1: skip)
+  __shared__ __attribute__((aligned(16))) uint16_t s_qw[4][NH * kQwStride];   // scaled queries, bf16
+
+  const int bid = blockIdx.x;
+  const int slot = bid >> 3;
+  const int layer = slot % a.L;
+  const int pair = (slot / a.L) * 8 + (bid & 7);
+  if (pair >= a.n_pairs) return;
+  const int r = pair / a.n_chunks;
+  const int chunk = pair - r * a.n_chunks;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int m = lane & 15;
-  const int g = lane >> 4;
+  const int n = lane & 31;                    // matrix-core row / column
+  const int hl = lane >> 5;                   // k half
+  const int m = lane & 15;                    // softmax: head within the wave's 16
+  const int g = lane >> 4;                    // softmax: key group 2 kk + h
   const int H = a.H;
-  const int hbase = (blockIdx.z % a.head_groups) * NT * 16;      // this workgroup's first head
   const int seq = a.row_seq ? a.row_seq[r] : r;
-  const int cbase = 128 * wave;                                   // this wave's channel slice
+  const int cbase = 128 * wave;               // this wave's channel slice
+  const float neg_inf = -__builtin_inff();
 
-  // this chunk's tiles: window tiles [w0, w0 + n_wt), then sparse tiles [sp0, sp0 + n_sp)
+  // this chunk's tiles: sparse tiles [sp0, sp0 + n_sp), then window tiles [w0, w0 + n_wt)
   const int w0 = chunk * a.window_per_chunk;
   const int n_wt = max(0, min(a.n_window_tiles, w0 + a.window_per_chunk) - w0);
   const int sp0 = chunk * a.sparse_per_chunk;
-  const int n_sp = max(0, min(a.n_sparse_tiles, sp0 + a.sparse_per_chunk) - sp0);
+  const int n_sp_real = max(0, min(a.n_sparse_tiles, sp0 + a.sparse_per_chunk) - sp0);
+  // sparse tiles run in groups of kPrefetch, the last group padded with key-less
+  // tiles, so that every step of the loop issues the same loads
+  const int n_sp = (n_sp_real + kPrefetch - 1) / kPrefetch * kPrefetch;
   const int k0 = sp0 * kKT;
-  const int k1 = min(a.K, (sp0 + n_sp) * kKT);
+  const int k1 = min(a.K, (sp0 + n_sp_real) * kKT);
 
-  // window rows of tile w: lane (m, g) takes channels cbase + 32g + [0, 32) of rows 32w + 16mt + m
-  uint4 wv[2][4];
-  int wvalid[2] = {0, 0};
+  // ---- queries (raw bf16), issued first: lane (n, h) holds channels cbase + 64 h
+  //      + [0, 64) of head 32 hb + n (zero past H)
+  const uint16_t* q_l = a.q_lat + (int64_t)layer * a.R * H * kLatent;
+  uint4 qraw[HB][8];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    const int head = 32 * hb + n;
+    const uint16_t* qrow = q_l + ((int64_t)r * H + min(head, H - 1)) * kLatent + cbase + 64 * hl;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint4 v = *reinterpret_cast<const uint4*>(qrow + 8 * ks);
+      qraw[hb][ks] = head < H ? v : make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  // ---- window rows of tile w: lane (n, h) takes channels cbase + 64 h + [0, 64)
+  //      of row 32 w + n; rows past the window's length read an in-bounds row
+  //      (the loads are unconditional) and are zeroed where they are used
+  uint4 wv[8];
+  bool wvalid = false;
   int w_st = 0, w_ln = 0;
   const uint16_t* swa_l = nullptr;
   if (n_wt > 0) {
@@ -167,227 +272,375 @@ attn_chunk_kernel(const AttnArgs a) {
     swa_l = a.swa + (int64_t)layer * a.B * a.S * kLatent;
   }
   auto load_window = [&](int w) {
+    const int kk = w * kKT + n;
+    wvalid = kk < w_ln;
+    const uint4* p = reinterpret_cast<const uint4*>(swa_l + ((int64_t)seq * a.S + (wvalid ? w_st + kk : 0)) * kLatent +
+                                                    cbase + 64 * hl);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int kk = w * kKT + 16 * mt + m;
-      wvalid[mt] = kk < w_ln;
-      const uint4* p = reinterpret_cast<const uint4*>(swa_l + ((int64_t)seq * a.S + (wvalid[mt] ? w_st + kk : 0)) *
-                                                      kLatent + cbase + 32 * g);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) wv[mt][ks] = wvalid[mt] ? p[ks] : make_uint4(0, 0, 0, 0);
-    }
+    for (int ks = 0; ks < 8; ++ks) wv[ks] = p[ks];
   };
-  if (n_wt > 0) load_window(w0);
 
-  // queries: B operand of S^T = X . Q^T; k-step ks holds channels cbase + 32g + 8ks + [0, 8)
-  const uint16_t* q_l = a.q_lat + (int64_t)layer * a.R * H * kLatent;
-  f16x8 qb[NT][4];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const uint16_t* qrow = q_l + ((int64_t)r * H + hbase + 16 * nt + m) * kLatent + cbase + 32 * g;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qb[nt][ks] = bf16x8_to_f16(*reinterpret_cast<const uint4*>(qrow + 8 * ks));
-  }
-
-  f32x4 oacc[8][NT];
-#pragma unroll
-  for (int t = 0; t < 8; ++t)
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) oacc[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
-
-  // positions of this chunk's sparse keys, staged once so that the gathers
-  // below do not wait on dependent index loads
+  // ---- cache rows of this chunk's sparse keys (page translation included),
+  //      staged once so that the gathers do not wait on dependent index or
+  //      page-table loads; a row of the codes array is below 2^31 (2^31 rows
+  //      would be 618 GB)
   if (n_sp > 0) {
     const int32_t* idx_row = a.idx + a.idx_off[layer] + (int64_t)r * a.K;
     for (int i = tid; i < n_sp * kKT; i += 256) {
       const int kk = k0 + i;
       const int pos = kk < k1 ? idx_row[kk] : -1;
-      s_pos[i] = (pos >= 0 && pos < a.T) ? pos : -1;
+      const int64_t row = (pos >= 0 && pos < a.T) ? phys_row(a.pm, seq, a.T, pos) : -1;
+      s_pos[i] = (int)row;
     }
-    __syncthreads();
   }
+  if (tid == 0) s_restart = 0;
+  // ---- per-head query exponent: the largest exponent field over the wave's
+  //      channels, then over the four waves (LDS)
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) {
+    uint32_t e = 0;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) e = max(e, bf16x8_max_exp(qraw[hb][ks]));
+    auto sw32 = __builtin_amdgcn_permlane32_swap(e, e, false, false);
+    e = max(sw32[0], sw32[1]);
+    if (hl == 0) s_qe[wave][32 * hb + n] = (int)e;
+  }
+  __syncthreads();
 
   // gather the FP4 codes + scales of sparse tile j's keys into a register buffer
+  // (every load is issued, an invalid key reading an in-bounds row, so the count
+  // of loads in flight is the same on every path)
   auto load_tile = [&](RawTile& raw, int j) {
+    const int row = s_pos[j * kKT + n];
+    const int64_t rr = row >= 0 ? row : 0;
+    const uint4* cp = reinterpret_cast<const uint4*>(a.codes + rr * kCodesRow + 64 * wave + 32 * hl);
+    raw.c0 = cp[0];
+    raw.c1 = cp[1];
+    raw.sc = *reinterpret_cast<const uint32_t*>(a.scales + rr * kScalesRow + 8 * wave + 4 * hl);
+  };
+  RawTile buf[kPrefetch];
+
+  // ---- queries scaled by 2^-sh (sh = largest exponent - kQTop) into f16
+  //      operands, and into bf16 in LDS for the window tiles
+  f16x8 qb[HB][8];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int pos = s_pos[j * kKT + 16 * mt + m];
-      const int64_t row = pos >= 0 ? phys_row(a.pm, seq, a.T, pos) : -1;
-      const bool ok = row >= 0;
-      raw.valid[mt] = ok;
-      if (ok) {
-        raw.v[mt] = *reinterpret_cast<const uint4*>(a.codes + row * kCodesRow + 64 * wave + 16 * g);
-        raw.sc[mt] = *reinterpret_cast<const uint16_t*>(a.scales + row * kScalesRow + 8 * wave + 2 * g);
+  for (int hb = 0; hb < HB; ++hb) {
+    int e = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) e = max(e, s_qe[w2][32 * hb + n]);
+    const int sh = (e == 0 ? -126 : e - 127) - kQTop;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      qb[hb][ks] = bf16x8_scaled(qraw[hb][ks], sh);
+      // exact: a bf16 value keeps its 8 significant bits
+      *reinterpret_cast<bf16x8*>(&s_qw[wave][(32 * hb + n) * kQwStride + 64 * hl + 8 * ks]) =
+          bf16x8_scaled_bf16(qraw[hb][ks], sh);
+    }
+  }
+  // softmax scale of the head this lane owns in the softmax step (2^sh folded in)
+  float ch = 0.f;
+  if (wave < NS) {
+    int e = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) e = max(e, s_qe[w2][16 * wave + m]);
+    const int sh = (e == 0 ? -126 : e - 127) - kQTop;
+    ch = __builtin_ldexpf(a.scale_log2, sh);
+  }
+  // the selection matrices E_0, E_1 as B operands: lane (n, h) holds E[8 h + j][n]
+  f16x8 esel[2];
+  bf16x8 eselb[2];
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool one = n == 8 * hl + j + 16 * s2;
+      esel[s2][j] = one ? (_Float16)1.0f : (_Float16)0.0f;
+      eselb[s2][j] = one ? (__bf16)1.0f : (__bf16)0.0f;
+    }
+
+  f32x16 oacc[4][HB];           // channel block b, head block hb
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) oacc[b][hb] = zero16();
+  // per softmax lane: the head's reference max (fixed by its first visible tile,
+  // or after a restart by every score seen), the largest score seen, and the sum
+  float m_ref = neg_inf, m_seen = neg_inf;
+  float l_run = 0.f;
+
+  // ---- A: partial scores of the tile into sp and its X^T operands into xt
+  //      (xt[2 b + kk]: f16 for cache tiles, bf16 for window tiles)
+  uint4 xt[8];
+  auto store_partials = [&](const f32x16 (&sacc)[HB]) {
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(&sp[wave][(32 * hb + n) * kSStride + 8 * q + 4 * hl]) =
+            f32x4{sacc[hb][4 * q], sacc[hb][4 * q + 1], sacc[hb][4 * q + 2], sacc[hb][4 * q + 3]};
+  };
+  auto pack_xt = [&](const f32x16& t, int b, bool bf) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      if (!bf) {
+        const f16x8 h = {(_Float16)t[8 * kk], (_Float16)t[8 * kk + 1], (_Float16)t[8 * kk + 2], (_Float16)t[8 * kk + 3],
+                         (_Float16)t[8 * kk + 4], (_Float16)t[8 * kk + 5], (_Float16)t[8 * kk + 6], (_Float16)t[8 * kk + 7]};
+        xt[2 * b + kk] = __builtin_bit_cast(uint4, h);
       } else {
-        raw.v[mt] = make_uint4(0, 0, 0, 0);
-        raw.sc[mt] = 0;
+        const bf16x8 h = {(__bf16)t[8 * kk], (__bf16)t[8 * kk + 1], (__bf16)t[8 * kk + 2], (__bf16)t[8 * kk + 3],
+                          (__bf16)t[8 * kk + 4], (__bf16)t[8 * kk + 5], (__bf16)t[8 * kk + 6], (__bf16)t[8 * kk + 7]};
+        xt[2 * b + kk] = __builtin_bit_cast(uint4, h);
       }
     }
   };
-
-  _Float16* xmine = xw + wave * kKT * kXwStride;
-  float* spmine = sp + wave * NT * 16 * kSStride;
-  const float neg_inf = -__builtin_inff();
-
-  // one tile: the window tile (win) or sparse tile j, whose buffer is refilled with j + 2
-  auto process = [&](RawTile& raw, bool win, int j) {
-    // ---- per 16-key half-tile: dequantise this wave's slice into A operands,
-    //      store it key-major in LDS, and form the partial scores
-    //      S^T[16mt + 4g + i][16nt + m] over the wave's 128 channels
-    int valid_mt[2];
+  auto stage_sparse = [&](RawTile& raw, int j, bool refill) {
+    const bool ok = s_pos[j * kKT + n] >= 0;
+    // an invalid key gets scale 0 (its codes then dequantise to +-0) and a
+    // masked score
+    const uint32_t sc = ok ? raw.sc : 0u;
+    const float sv[4] = {__builtin_amdgcn_cvt_f32_fp8((int)sc, 0), __builtin_amdgcn_cvt_f32_fp8((int)sc, 1),
+                         __builtin_amdgcn_cvt_f32_fp8((int)sc, 2), __builtin_amdgcn_cvt_f32_fp8((int)sc, 3)};
+    f16x2 hs[4];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      f16x8 xa[4];
-      if (!win) {
-        const uint32_t cw[4] = {raw.v[mt].x, raw.v[mt].y, raw.v[mt].z, raw.v[mt].w};
+    for (int bk = 0; bk < 4; ++bk) hs[bk] = f16x2{(_Float16)sv[bk], (_Float16)sv[bk]};
+    const uint32_t cw[8] = {raw.c0.x, raw.c0.y, raw.c0.z, raw.c0.w, raw.c1.x, raw.c1.y, raw.c1.z, raw.c1.w};
+    f32x16 sacc[HB];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const float sf = e4m3_to_f32((raw.sc[mt] >> (8 * (ks >> 1))) & 0xFFu);
-          const f16x2 s2 = {(_Float16)sf, (_Float16)sf};
-          xa[ks] = fp4x8_to_f16(cw[ks], s2);
-        }
-        valid_mt[mt] = raw.valid[mt];
-      } else {
-        // window rows: bf16 -> f16
+    for (int hb = 0; hb < HB; ++hb) sacc[hb] = zero16();
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) xa[ks] = bf16x8_to_f16(wv[mt][ks]);
-        valid_mt[mt] = wvalid[mt];
+    for (int b = 0; b < 4; ++b) {
+      const f16x8 xa0 = fp4x8_to_f16(cw[2 * b], hs[b]);
+      const f16x8 xa1 = fp4x8_to_f16(cw[2 * b + 1], hs[b]);
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        sacc[hb] = mfma32(xa0, qb[hb][2 * b], sacc[hb]);
+        sacc[hb] = mfma32(xa1, qb[hb][2 * b + 1], sacc[hb]);
       }
-      f16x8* dst = reinterpret_cast<f16x8*>(xmine + (16 * mt + m) * kXwStride + 32 * g);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) dst[ks] = xa[ks];
-      f32x4 sacc[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sacc[nt] = mfma16(xa[ks], qb[nt][ks], sacc[nt]);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        *reinterpret_cast<f32x4*>(spmine + (16 * nt + m) * kSStride + 16 * mt + 4 * g) = sacc[nt];
-      if (!win && mt == 1 && j + kPrefetch < n_sp) load_tile(raw, j + kPrefetch);   // buffer free: refill it
+      f32x16 t = mfma32(xa0, esel[0], zero16());
+      t = mfma32(xa1, esel[1], t);
+      pack_xt(t, b, false);
     }
-    if (wave == 0 && g == 0) {
-      s_valid[m] = valid_mt[0];
-      s_valid[16 + m] = valid_mt[1];
+    store_partials(sacc);
+    if (wave == 0 && hl == 0) s_mask[n] = ok ? 0.f : neg_inf;
+    // buffer free: refill it with the tile kPrefetch ahead (every group but the
+    // last has one)
+    if (refill) load_tile(raw, j + kPrefetch);
+  };
+  auto stage_window = [&]() {
+    const uint4 zero = make_uint4(0, 0, 0, 0);
+    f32x16 sacc[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) sacc[hb] = zero16();
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const bf16x8 xa0 = __builtin_bit_cast(bf16x8, wvalid ? wv[2 * b] : zero);
+      const bf16x8 xa1 = __builtin_bit_cast(bf16x8, wvalid ? wv[2 * b + 1] : zero);
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        const uint16_t* qw = &s_qw[wave][(32 * hb + n) * kQwStride + 64 * hl + 16 * b];
+        sacc[hb] = mfma32bf(xa0, *reinterpret_cast<const bf16x8*>(qw), sacc[hb]);
+        sacc[hb] = mfma32bf(xa1, *reinterpret_cast<const bf16x8*>(qw + 8), sacc[hb]);
+      }
+      f32x16 t = mfma32bf(xa0, eselb[0], zero16());
+      t = mfma32bf(xa1, eselb[1], t);
+      pack_xt(t, b, true);
     }
-    __syncthreads();
+    store_partials(sacc);
+    if (wave == 0 && hl == 0) s_mask[n] = wvalid ? 0.f : neg_inf;
+  };
 
-    // ---- softmax for heads [16w, 16w+16): lane (m, g) owns head 16w+m, keys 8g + [0, 8)
-    if (wave < NT) {
-      float s[8];
+  // ---- B: softmax of the tile for heads [16 w, 16 w + 16): lane (m, g) owns head
+  //      16 w + m and keys {16 kk + 4 h + i, 16 kk + 8 + 4 h + i}, (kk, h) =
+  //      (g / 2, g % 2), i < 4 (the P^T operand order); P goes to LDS (f16, or for
+  //      a window tile bf16 high parts and bf16 remainders)
+  auto softmax = [&](bool win) {
+    if (wave >= NS) return;
+    const int head = 16 * wave + m;
+    const int kb = 16 * (g >> 1) + 4 * (g & 1);
+    float s[8];
+    {
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(&sp[0][head * kSStride + kb]);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(&sp[0][head * kSStride + kb + 8]);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) s[q] = 0.f;
+      for (int q = 0; q < 4; ++q) { s[q] = v0[q]; s[4 + q] = v1[q]; }
+    }
 #pragma unroll
-      for (int w2 = 0; w2 < 4; ++w2) {
-        const float* src = sp + w2 * NT * 16 * kSStride + (16 * wave + m) * kSStride + 8 * g;
-        f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
-        f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 4);
+    for (int w2 = 1; w2 < 4; ++w2) {
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(&sp[w2][head * kSStride + kb]);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(&sp[w2][head * kSStride + kb + 8]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) { s[q] += v0[q]; s[4 + q] += v1[q]; }
-      }
-      float mx = neg_inf;
+      for (int q = 0; q < 4; ++q) { s[q] += v0[q]; s[4 + q] += v1[q]; }
+    }
+    const f32x4 mk0 = *reinterpret_cast<const f32x4*>(&s_mask[kb]);
+    const f32x4 mk1 = *reinterpret_cast<const f32x4*>(&s_mask[kb + 8]);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        s[q] = s_valid[8 * g + q] ? s[q] * a.scale_log2 : neg_inf;
-        mx = fmaxf(mx, s[q]);
-      }
-      mx = xor32_max(xor16_max(mx));
-      // P = 2^(s - m_ref) stays <= 2^8 in f16; m_ref moves only past that slack
-      const float m_new = (mx > m_run + kRescaleSlack) ? mx : m_run;
-      const bool live = m_new != neg_inf;
-      const float alpha = live ? exp2f(m_run - m_new) : 1.f;
-      float psum = 0.f;
+    for (int q = 0; q < 4; ++q) {
+      s[q] = __builtin_fmaf(s[q], ch, mk0[q]);
+      s[4 + q] = __builtin_fmaf(s[4 + q], ch, mk1[q]);
+    }
+    float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+    mx = xor32_max(xor16_max(mx));
+    // no rescaling of O inside the chunk: P = 2^(s - m_ref) with the reference
+    // set kRefLead above the head's first visible tile's max; a score more than
+    // kMaxSlack above the reference (P would pass 2^15) makes the workgroup redo
+    // the chunk with the largest score seen as the reference
+    if (m_ref == neg_inf && mx != neg_inf) m_ref = mx + kRefLead;
+    if (mx > m_ref + kMaxSlack) s_restart = 1;
+    m_seen = fmaxf(m_seen, mx);
+    const float m_use = m_ref == neg_inf ? 0.f : m_ref;     // nothing visible yet: every p is 0
+    float p[8], psum = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      p[q] = __builtin_amdgcn_exp2f(s[q] - m_use);
+      psum += p[q];
+    }
+    psum = xor32_sum(xor16_sum(psum));
+    l_run += psum;
+    if (!win) {
       f16x8 ph;
 #pragma unroll
+      for (int q = 0; q < 8; ++q) ph[q] = (_Float16)p[q];
+      *reinterpret_cast<f16x8*>(&pp[0][head * kPStride + 8 * g]) = ph;
+    } else {
+      bf16x8 hi, lo;
+#pragma unroll
       for (int q = 0; q < 8; ++q) {
-        float pj = live ? exp2f(s[q] - m_new) : 0.f;
-        psum += pj;
-        ph[q] = (_Float16)pj;
+        hi[q] = (__bf16)p[q];
+        lo[q] = (__bf16)(p[q] - (float)hi[q]);
       }
-      psum = xor32_sum(xor16_sum(psum));
-      l_run = l_run * alpha + psum;
-      m_run = m_new;
-      *reinterpret_cast<f16x8*>(pp + (16 * wave + m) * kPStride + 8 * g) = ph;
-      if (g == 0) s_alpha[16 * wave + m] = alpha;
-    }
-    __syncthreads();
-
-    // ---- rescale and accumulate O^T[cbase + 16t + 4g + i][16nt + m] += sum_k X[k][.] P[.][k]
-    float al[NT];
-    bool any_scale = false;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      al[nt] = s_alpha[16 * nt + m];
-      any_scale |= al[nt] != 1.f;
-    }
-    if (__any(any_scale)) {
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) oacc[t][nt] *= al[nt];
-    }
-    f16x8 pb[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) pb[nt] = *reinterpret_cast<const f16x8*>(pp + (16 * nt + m) * kPStride + 8 * g);
-    // transpose-read rows: source lane m supplies keys 8g + (m>>2) (+4) and channels 16t + 4(m&3) .. +3
-    const _Float16* tr0 = xmine + (8 * g + (m >> 2)) * kXwStride + 4 * (m & 3);
-    const _Float16* tr1 = tr0 + 4 * kXwStride;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      f16x4 lo = lds_tr16(tr0 + 16 * t);
-      f16x4 hi = lds_tr16(tr1 + 16 * t);
-      f16x8 xt = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) oacc[t][nt] = mfma16(xt, pb[nt], oacc[t][nt]);
+      *reinterpret_cast<bf16x8*>(&pp[0][head * kPStride + 8 * g]) = hi;
+      *reinterpret_cast<bf16x8*>(&pp[1][head * kPStride + 8 * g]) = lo;
     }
   };
 
-  RawTile buf[kPrefetch];
+  // ---- C: O^T[block b][head block hb] += X^T P^T for a tile whose X^T operands
+  //      are in xp (kind 0 f16 cache tile, 1 bf16 window tile) and whose P is in LDS
+  auto pv = [&](const uint4 (&xp)[8], int kind) {
 #pragma unroll
-  for (int b = 0; b < kPrefetch; ++b)
-    if (b < n_sp) load_tile(buf[b], b);
-  for (int i = 0; i < n_wt; ++i) {
-    if (i > 0) load_window(w0 + i);
-    process(buf[0], true, -1);
-  }
-  for (int j = 0; j < n_sp; j += kPrefetch) {
+    for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-    for (int b = 0; b < kPrefetch; ++b)
-      if (j + b < n_sp) process(buf[b], false, j + b);
+      for (int kk = 0; kk < 2; ++kk) {
+        const int prow = (32 * hb + n) * kPStride + 8 * (2 * kk + hl);
+        const uint4 ph = *reinterpret_cast<const uint4*>(&pp[0][prow]);
+        if (kind == 0) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            oacc[b][hb] = mfma32(__builtin_bit_cast(f16x8, xp[2 * b + kk]), __builtin_bit_cast(f16x8, ph), oacc[b][hb]);
+        } else {
+          const uint4 pl = *reinterpret_cast<const uint4*>(&pp[1][prow]);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const bf16x8 x = __builtin_bit_cast(bf16x8, xp[2 * b + kk]);
+            oacc[b][hb] = mfma32bf(x, __builtin_bit_cast(bf16x8, ph), oacc[b][hb]);
+            oacc[b][hb] = mfma32bf(x, __builtin_bit_cast(bf16x8, pl), oacc[b][hb]);
+          }
+        }
+      }
+  };
+
+  // ---- the pipelined loop over the sparse tiles: step j holds C of tile j - 1
+  //      (its X^T kept in registers, its P in LDS) and A of tile j, then B of
+  //      tile j; the last group is peeled so that it issues no refills and loads
+  //      the window rows half way through, once its first buffers are free.
+  //      (Scheduling barriers keep each step's instructions in place.)
+  uint4 xprev[8];
+  auto sparse_step = [&](RawTile& raw, int j, bool refill) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (j > 0) pv(xprev, 0);
+    stage_sparse(raw, j, refill);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    softmax(false);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) xprev[t] = xt[t];
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  for (;;) {
+    if (n_sp > 0) {
+#pragma unroll
+      for (int b = 0; b < kPrefetch; ++b) load_tile(buf[b], b);
+      for (int j = 0; j < n_sp - kPrefetch; j += kPrefetch) {
+#pragma unroll
+        for (int b = 0; b < kPrefetch; ++b) sparse_step(buf[b], j + b, true);
+      }
+      const int jl = n_sp - kPrefetch;
+#pragma unroll
+      for (int b = 0; b < kPrefetch; ++b) {
+        if (b == kPrefetch / 2 && n_wt > 0) load_window(w0);
+        sparse_step(buf[b], jl + b, false);
+      }
+      pv(xprev, 0);
+    } else if (n_wt > 0) {
+      load_window(w0);
+    }
+    // ---- window tiles, after the sparse ones (bf16 products; not pipelined)
+    for (int i = 0; i < n_wt; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i > 0) load_window(w0 + i);
+      __syncthreads();          // every wave is past the previous tile's P reads
+      stage_window();
+      __syncthreads();
+      softmax(true);
+      __syncthreads();
+      pv(xt, 1);
+    }
+    __syncthreads();
+    if (!s_restart) break;
+    // restart: every head's reference becomes its largest score (P <= 1 from now on)
+    __syncthreads();
+    if (tid == 0) s_restart = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) oacc[b][hb] = zero16();
+    m_ref = m_seen;
+    l_run = 0.f;
   }
 
+  // ---- outputs: lane (n, h) register 4 q + i of block (b, hb) is head 32 hb + n,
+  //      channel cbase + 64 (q & 1) + 16 b + 8 (q >> 1) + 4 h + i
+  const int64_t orow0 = ((int64_t)layer * a.R + r) * H;
   if (a.o_out) {
     // the row's only chunk and no prior: normalise here, as the combine would for one chunk
-    if (wave < NT && g == 0) s_inv_l[16 * wave + m] = l_run > 0.f ? 1.f / l_run : 0.f;
+    if (wave < NS && g == 0) s_inv_l[16 * wave + m] = l_run > 0.f ? 1.f / l_run : 0.f;
     __syncthreads();
-    const int64_t orow = ((int64_t)layer * a.R + r) * H + hbase;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const float inv = s_inv_l[16 * nt + m];
-      float* op = a.o_out + (orow + 16 * nt + m) * kLatent + cbase + 4 * g;
+    for (int hb = 0; hb < HB; ++hb) {
+      const int head = 32 * hb + n;
+      if (head >= H) continue;
+      const float inv = s_inv_l[head];
+      float* op = a.o_out + (orow0 + head) * kLatent + cbase + 4 * hl;
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        *reinterpret_cast<f32x4*>(op + 16 * t) = inv > 0.f ? oacc[t][nt] * inv : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = {oacc[b][hb][4 * q], oacc[b][hb][4 * q + 1], oacc[b][hb][4 * q + 2], oacc[b][hb][4 * q + 3]};
+          *reinterpret_cast<f32x4*>(op + 64 * (q & 1) + 16 * b + 8 * (q >> 1)) =
+              inv > 0.f ? v * inv : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     }
-    if (a.lse_out && wave < NT && g == 0)
-      a.lse_out[orow + 16 * wave + m] = l_run > 0.f ? (m_run + log2f(l_run)) * kLn2 : neg_inf;
+    if (a.lse_out && wave < NS && g == 0 && 16 * wave + m < H)
+      a.lse_out[orow0 + 16 * wave + m] = l_run > 0.f ? (m_ref + log2f(l_run)) * kLn2 : neg_inf;
     return;
   }
   // ---- this chunk's partial: unnormalised O, and (m, l) from the softmax owners
-  const int64_t prow = (((int64_t)layer * a.R + r) * a.n_chunks + chunk) * H + hbase;
+  const int64_t prow0 = (((int64_t)layer * a.R + r) * a.n_chunks + chunk) * H;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float* op = a.o_part + (prow + 16 * nt + m) * kLatent + cbase + 4 * g;
+  for (int hb = 0; hb < HB; ++hb) {
+    const int head = 32 * hb + n;
+    if (head >= H) continue;
+    float* op = a.o_part + (prow0 + head) * kLatent + cbase + 4 * hl;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4*>(op + 16 * t) = oacc[t][nt];
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4*>(op + 64 * (q & 1) + 16 * b + 8 * (q >> 1)) =
+            f32x4{oacc[b][hb][4 * q], oacc[b][hb][4 * q + 1], oacc[b][hb][4 * q + 2], oacc[b][hb][4 * q + 3]};
   }
-  if (wave < NT && g == 0) {
-    a.ml_part[(prow + 16 * wave + m) * 2 + 0] = m_run;
-    a.ml_part[(prow + 16 * wave + m) * 2 + 1] = l_run;
+  if (wave < NS && g == 0 && 16 * wave + m < H) {
+    a.ml_part[(prow0 + 16 * wave + m) * 2 + 0] = m_ref;
+    a.ml_part[(prow0 + 16 * wave + m) * 2 + 1] = l_run;
   }
 }
 
@@ -491,15 +744,12 @@ struct Plan {
   int sparse_per_chunk, window_per_chunk, n_chunks;
 };
 
-static int head_groups(int32_t H) { return H % 32 == 0 ? H / 32 : H / 16; }
+constexpr int kMinChunkTiles = kPrefetch;      // partial outputs stay small next to the gathered rows
 
-constexpr int kTargetWorkgroups = 512;         // two four-wave workgroups per CU
-constexpr int kMinChunkTiles = 4;              // partial outputs stay small next to the gathered rows
-
-// Chunks per (layer, row): about kTargetWorkgroups workgroups in total, at least
-// kMinChunkTiles sparse tiles per chunk; the window tiles are spread one per
-// chunk where there are enough chunks.
-static Plan chunk_plan(int32_t L, int32_t R, int32_t H, int32_t K, bool sparse, bool window) {
+// Chunks per (layer, row): about one workgroup per compute unit in total, whole
+// groups of kPrefetch sparse tiles per chunk; the window tiles are spread one
+// per chunk where there are enough chunks.
+static Plan chunk_plan(int32_t L, int32_t R, int32_t K, bool sparse, bool window) {
   Plan p;
   p.n_sparse_tiles = sparse ? (K + kKT - 1) / kKT : 0;
   p.n_window_tiles = window ? kWindowChunks : 0;
@@ -509,12 +759,13 @@ static Plan chunk_plan(int32_t L, int32_t R, int32_t H, int32_t K, bool sparse, 
     p.window_per_chunk = 1;
     return p;
   }
-  const int64_t per_chunk = (int64_t)L * R * head_groups(H);
-  const int64_t want = (kTargetWorkgroups + per_chunk - 1) / per_chunk;
+  const int64_t per_chunk = (int64_t)L * R;
+  const int64_t target = device_cu_count();
+  const int64_t want = (target + per_chunk - 1) / per_chunk;
   int64_t spc = (p.n_sparse_tiles + want - 1) / want;
   if (spc < kMinChunkTiles) spc = kMinChunkTiles;
+  spc = (spc + kPrefetch - 1) / kPrefetch * kPrefetch;     // whole groups of tiles
   if (spc > kMaxChunkTiles) spc = kMaxChunkTiles;
-  if (spc > p.n_sparse_tiles) spc = p.n_sparse_tiles;
   p.sparse_per_chunk = (int)spc;
   p.n_chunks = (int)((p.n_sparse_tiles + spc - 1) / spc);
   p.window_per_chunk = p.n_window_tiles ? (p.n_window_tiles + p.n_chunks - 1) / p.n_chunks : 0;
@@ -531,14 +782,12 @@ static size_t partial_bytes(int32_t L, int32_t R, int32_t H, int n_chunks, size_
 
 static bool heads_ok(int32_t H) { return H == 16 || H == 32 || H == 48 || H == 64; }
 
-// Heads are split into groups of 32 (or 16 when H is not a multiple of 32),
-// one workgroup per group: the 32-head kernel fits two waves per SIMD and two
-// workgroups per CU, which hides barrier and memory latency better than one
-// 64-head workgroup; the price is dequantising each tile once per group.
+// One workgroup per (row, chunk, layer) with every head: eight ids per XCD turn
 static void launch_chunks(const AttnArgs& a, hipStream_t s) {
-  const dim3 grid(a.n_chunks, a.R, a.head_groups * a.L);
-  if (a.H % 32 == 0) attn_chunk_kernel<2><<<grid, 256, 0, s>>>(a);
-  else attn_chunk_kernel<1><<<grid, 256, 0, s>>>(a);
+  const int64_t groups = ((int64_t)a.n_pairs + 7) / 8;
+  const dim3 grid((unsigned)(8 * a.L * groups));
+  if (a.H <= 32) attn_chunk_kernel<1><<<grid, 256, 0, s>>>(a);
+  else attn_chunk_kernel<2><<<grid, 256, 0, s>>>(a);
 }
 
 // shared launch of L layers of one attention form (sparse part, window part or both);
@@ -550,15 +799,16 @@ static csa2_status attention_call(int32_t L, const uint16_t* q_lat, int32_t R, i
                                   const float* o_prev, const float* lse_prev, float* o, float* lse,
                                   void* workspace, size_t workspace_bytes, void* stream,
                                   const PageMap& pm = PageMap{}) {
-  const Plan p = chunk_plan(L, R, H, K, idx != nullptr, swa != nullptr);
+  const Plan p = chunk_plan(L, R, K, idx != nullptr, swa != nullptr);
   AttnArgs a;
   a.pm = pm;
-  a.q_lat = q_lat; a.R = R; a.H = H; a.L = L; a.head_groups = head_groups(H);
+  a.q_lat = q_lat; a.R = R; a.H = H; a.L = L;
   a.codes = codes; a.scales = scales; a.T = T; a.row_seq = row_seq;
   a.idx = idx; a.K = K;
   for (int l = 0; l < kMaxLayers; ++l) a.idx_off[l] = (idx && l < L) ? idx_off[l] : 0;
   a.n_sparse_tiles = p.n_sparse_tiles; a.n_window_tiles = p.n_window_tiles;
   a.window_per_chunk = p.window_per_chunk; a.sparse_per_chunk = p.sparse_per_chunk; a.n_chunks = p.n_chunks;
+  a.n_pairs = R * p.n_chunks;
   a.swa = swa; a.B = B; a.S = S; a.swa_start = swa_start; a.swa_len = swa_len;
   a.scale_log2 = softmax_scale * kLog2e;
   size_t off_ml;
@@ -580,7 +830,7 @@ static csa2_status attention_call(int32_t L, const uint16_t* q_lat, int32_t R, i
 }
 
 static size_t attention_workspace(int32_t L, int32_t R, int32_t H, int32_t K, bool sparse, bool window) {
-  return partial_bytes(L, R, H, chunk_plan(L, R, H, K, sparse, window).n_chunks, nullptr);
+  return partial_bytes(L, R, H, chunk_plan(L, R, K, sparse, window).n_chunks, nullptr);
 }
 
 }  // namespace csa2

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <atomic>
+
 #include "csa2.h"
 
 namespace csa2 {
@@ -207,5 +209,23 @@ inline csa2_status launch_status() {
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// Compute units of the current device, queried once per device (each GPU the
+// library runs on keeps its own entry); 256, the MI355X count, if the query fails.
+constexpr int kMaxDevices = 64;
+inline int device_cu_count() {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+  if (dev >= 0) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (dev < 0 || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  if (dev >= 0) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
 
 }  // namespace csa2

@@ -692,18 +692,17 @@ index_block_cand_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __rest
 // per CU (3 beat 4 and 2 in a same-box sweep of the 8 x 1M candidate scan:
 // 95.6 vs 98.4 and 102 us; more concurrent key streams than that contend)
 static int64_t resident_blocks() {
-  static int64_t cached = 0;
-  if (cached == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-        hipSuccess)
-      cus = 256;
+  static std::atomic<int> per_cu_cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  int per_cu = per_cu_cache[dev].load(std::memory_order_relaxed);
+  if (per_cu <= 0) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(index_stream_kernel<true, false, false>), 256,
                                                       0) != hipSuccess || per_cu < 1)
       per_cu = 3;
-    cached = (int64_t)cus * std::min(per_cu, 3);
+    per_cu_cache[dev].store(per_cu, std::memory_order_relaxed);
   }
-  return cached;
+  return (int64_t)device_cu_count() * std::min(per_cu, 3);
 }
 
 static int tiles_per_block_for(int64_t n_tiles, int64_t rows) {

@@ -283,3 +283,49 @@ def test_many_rows_single_chunk_writes_outputs_directly():
         o_ref, l_ref = OA.merge(o_s, l_s, o_w, l_w)
         assert_attention_close(o[r].cpu().numpy(), lse[r].cpu().numpy(), o_ref, l_ref, f"row {r}")
         assert_attention_close(o2[r].cpu().numpy(), lse2[r].cpu().numpy(), o_ref, l_ref, f"row {r} two calls")
+
+
+def test_attention_exact_for_wide_range_bf16_inputs():
+    """Queries and window rows far outside the f16 range (bf16 magnitudes 2^-100 .. 2^80): each head's
+    query is scaled by a power of two before the f16 products and window rows go through bf16
+    products, so the result matches the oracle (fp64) as closely as for unit-scale inputs.  The lse of
+    a huge score carries fp32 relative error, so it is held to 1e-4 + 2^-16 * sigma * max_j sum_c
+    |q_c x_jc| (the fp32 rounding of the score sums) instead of the plain 1e-4."""
+    dev = device()
+    B, T, H, K = 3, 2000, 64, 256
+    rng = np.random.default_rng(91)
+    lat, ref_rows = _cache(B, T, seed=92)
+    codes, scales = _gpu_cache(lat, dev)
+    q = W.bf16_normal(93, (B, H, 512), std=0.5).to(torch.float32)
+    q[:, 0:16] *= 2.0 ** 40          # huge: products far above the f16 range
+    q[:, 16:32] *= 2.0 ** -60        # tiny: below the f16 subnormals
+    q[:, 48:64] *= 2.0 ** 20
+    q[1, 40, :7] = torch.tensor([1e30, -1e-38, 65504.0, 7e4, 2.0 ** -30, 0.0, -0.0])
+    q = q.to(torch.bfloat16)
+    S = 130
+    swa = W.bf16_normal(94, (B, S, 512)).to(torch.float32)
+    swa[0] *= 2.0 ** 80
+    swa[1] *= 2.0 ** -100
+    swa[2, 0::2] *= 2.0 ** 60
+    swa[2, 1::2] *= 2.0 ** -60
+    swa = swa.to(torch.bfloat16)
+    start = np.array([0, 2, 1], dtype=np.int32)
+    length = np.array([128, 128, 77], dtype=np.int32)
+    idx = np.stack([np.sort(rng.choice(T, K, replace=False)) for _ in range(B)]).astype(np.int32)
+    o = torch.empty((B, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    F.csa2_sparse_swa_decode(q.to(dev), codes, scales, torch.from_numpy(idx).to(dev), swa.to(dev),
+                             torch.from_numpy(start).to(dev), torch.from_numpy(length).to(dev), SIGMA, o, lse)
+    qf = q.to(torch.float64).numpy()
+    swf = swa.to(torch.float64).numpy()
+    for b in range(B):
+        win = OA.window_rows(swf[b], int(start[b]), int(length[b]))
+        o_s, l_s = OA.sparse_attend(qf[b], ref_rows[b], idx[b], SIGMA)
+        o_w, l_w = OA.attend(qf[b], win, SIGMA)
+        o_ref, l_ref = OA.merge(o_s, l_s, o_w, l_w)
+        got_o, got_l = o[b].cpu().numpy().astype(np.float64), lse[b].cpu().numpy().astype(np.float64)
+        err = np.abs(got_o - o_ref).max(axis=-1) / np.abs(o_ref).max(axis=-1)
+        assert float(err.max()) <= 2e-3, f"row {b}: normwise error {float(err.max()):.3e}"
+        rows = np.concatenate([ref_rows[b][idx[b]], win])
+        mag = SIGMA * (np.abs(qf[b]) @ np.abs(rows).T).max(axis=1)
+        assert np.all(np.abs(got_l - l_ref) <= 1e-4 + 2.0 ** -16 * mag), f"row {b}: lse"
