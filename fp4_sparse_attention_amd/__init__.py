@@ -52,6 +52,9 @@ _SIGS = {
     "csa2_sparse_swa_decode_layers": (_i32, [_i32, _c_void_p, _i32, _i32, _c_void_p, _c_void_p, _i32, _i64, _c_void_p,
                                              _c_void_p, _c_void_p, _i32, _c_void_p, _i32, _c_void_p, _c_void_p, _f32,
                                              _c_void_p, _c_void_p, _c_void_p, _size_t, _c_void_p]),
+    "csa2_sparse_swa_decode_layers_noalloc": (_i32, [_i32, _c_void_p, _i32, _i32, _c_void_p, _c_void_p, _i32, _i64,
+                                                     _c_void_p, _c_void_p, _c_void_p, _i32, _c_void_p, _i32,
+                                                     _c_void_p, _c_void_p, _f32, _c_void_p, _c_void_p, _c_void_p]),
     "csa2_swa_merge": (_i32, [_c_void_p, _i32, _i32, _c_void_p, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _f32,
                               _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t, _c_void_p]),
     # paged global KV
@@ -378,11 +381,8 @@ def csa2_sparse_swa_decode_layers_workspace_size(L, R, H, K):
     return int(lib().csa2_sparse_swa_decode_layers_workspace_size(L, R, H, K))
 
 
-def csa2_sparse_swa_decode_layers(q_lat, codes, scales, idx, layer_idx, swa, swa_start, swa_len, softmax_scale, o,
-                                  lse, row_seq=None, workspace=None, stream=None):
-    """L layers of csa2_sparse_swa_decode in one launch: q_lat bf16 [L, R, H, 512]; idx int32 [n, R, K];
-    layer_idx: L ints (host) selecting each layer's idx slice; swa bf16 [L, B, S, 512];
-    swa_start/swa_len int32 [L, R]; o fp32 [L, R, H, 512]; lse fp32 [L, R, H]."""
+def _layers_shapes(q_lat, codes, scales, idx, layer_idx, swa, swa_start, swa_len, o, lse, row_seq):
+    """Checks of the multi-layer attention arguments; returns L, R, H, B, T, K, S and the host layer_idx array."""
     _need(q_lat, torch.bfloat16, "q_lat", 4)
     _need(codes, torch.uint8, "codes", 3)
     _need(scales, torch.uint8, "scales", 3)
@@ -408,15 +408,40 @@ def csa2_sparse_swa_decode_layers(q_lat, codes, scales, idx, layer_idx, swa, swa
         raise ValueError("layer_idx entries must select one of the idx slices")
     if row_seq is not None:
         _need(row_seq, torch.int32, "row_seq", 1)
+    return L, R, H, B, T, K, S, (ctypes.c_int32 * L)(*layer_idx)
+
+
+def csa2_sparse_swa_decode_layers(q_lat, codes, scales, idx, layer_idx, swa, swa_start, swa_len, softmax_scale, o,
+                                  lse, row_seq=None, workspace=None, stream=None):
+    """L layers of csa2_sparse_swa_decode in one launch: q_lat bf16 [L, R, H, 512]; idx int32 [n, R, K];
+    layer_idx: L ints (host) selecting each layer's idx slice; swa bf16 [L, B, S, 512];
+    swa_start/swa_len int32 [L, R]; o fp32 [L, R, H, 512]; lse fp32 [L, R, H]."""
+    L, R, H, B, T, K, S, host_idx = _layers_shapes(q_lat, codes, scales, idx, layer_idx, swa, swa_start, swa_len, o,
+                                                   lse, row_seq)
     need = csa2_sparse_swa_decode_layers_workspace_size(L, R, H, K)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_lat.device)
-    host_idx = (ctypes.c_int32 * L)(*layer_idx)
     st = lib().csa2_sparse_swa_decode_layers(L, _p(q_lat), R, H, _p(codes), _p(scales), B, T, _p(row_seq), _p(idx),
                                              ctypes.cast(host_idx, ctypes.c_void_p), K, _p(swa), S, _p(swa_start),
                                              _p(swa_len), float(softmax_scale), _p(o), _p(lse), _p(workspace),
                                              workspace.numel(), _stream(stream))
     _check("csa2_sparse_swa_decode_layers", st)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def csa2_sparse_swa_decode_layers_noalloc(q_lat, codes, scales, idx, layer_idx, swa, swa_start, swa_len,
+                                          softmax_scale, o, lse, row_seq=None, stream=None):
+    """csa2_sparse_swa_decode_layers with no workspace: the chunk partials go to the library's fixed
+    64 MiB static device array (one per GPU, shared by every call on it).  Allocates no device memory."""
+    L, R, H, B, T, K, S, host_idx = _layers_shapes(q_lat, codes, scales, idx, layer_idx, swa, swa_start, swa_len, o,
+                                                   lse, row_seq)
+    st = lib().csa2_sparse_swa_decode_layers_noalloc(L, _p(q_lat), R, H, _p(codes), _p(scales), B, T, _p(row_seq),
+                                                     _p(idx), ctypes.cast(host_idx, ctypes.c_void_p), K, _p(swa), S,
+                                                     _p(swa_start), _p(swa_len), float(softmax_scale), _p(o), _p(lse),
+                                                     _stream(stream))
+    _check("csa2_sparse_swa_decode_layers_noalloc", st)
 
 
 def csa2_index_full_pool_workspace_size(R, T, k_pool):

@@ -11,6 +11,7 @@ extern "C" const char* csa2_status_str(csa2_status s) {
     case CSA2_EALIGN: return "pointer or stride not aligned as required";
     case CSA2_EWORKSPACE: return "workspace missing or too small";
     case CSA2_ELAUNCH: return "kernel launch failed";
+    case CSA2_ESCRATCH: return "shape needs more than the fixed scratch array of the allocation-free call";
     default: return "unknown status";
   }
 }

@@ -798,7 +798,7 @@ static csa2_status attention_call(int32_t L, const uint16_t* q_lat, int32_t R, i
                                   int32_t S, const int32_t* swa_start, const int32_t* swa_len, float softmax_scale,
                                   const float* o_prev, const float* lse_prev, float* o, float* lse,
                                   void* workspace, size_t workspace_bytes, void* stream,
-                                  const PageMap& pm = PageMap{}) {
+                                  const PageMap& pm = PageMap{}, bool scratch = false) {
   const Plan p = chunk_plan(L, R, K, idx != nullptr, swa != nullptr);
   AttnArgs a;
   a.pm = pm;
@@ -813,12 +813,17 @@ static csa2_status attention_call(int32_t L, const uint16_t* q_lat, int32_t R, i
   a.scale_log2 = softmax_scale * kLog2e;
   size_t off_ml;
   const size_t need = partial_bytes(L, R, H, a.n_chunks, &off_ml);
-  if (!workspace || workspace_bytes < need) return CSA2_EWORKSPACE;
+  // one chunk per row and no prior result (many rows): the chunk kernel writes o and lse itself
+  const bool direct = a.n_chunks == 1 && o_prev == nullptr && lse_prev == nullptr;
+  if (scratch) {
+    // the fixed static array: only partials use it
+    if (!direct && need > workspace_bytes) return CSA2_ESCRATCH;
+  } else if (!workspace || workspace_bytes < need) {
+    return CSA2_EWORKSPACE;
+  }
   if (!aligned(workspace, 256)) return CSA2_EALIGN;
   a.o_part = static_cast<float*>(workspace);
   a.ml_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + off_ml);
-  // one chunk per row and no prior result (many rows): the chunk kernel writes o and lse itself
-  const bool direct = a.n_chunks == 1 && o_prev == nullptr && lse_prev == nullptr;
   a.o_out = direct ? o : nullptr;
   a.lse_out = direct ? lse : nullptr;
   hipStream_t s = (hipStream_t)stream;
@@ -831,6 +836,25 @@ static csa2_status attention_call(int32_t L, const uint16_t* q_lat, int32_t R, i
 
 static size_t attention_workspace(int32_t L, int32_t R, int32_t H, int32_t K, bool sparse, bool window) {
   return partial_bytes(L, R, H, chunk_plan(L, R, K, sparse, window).n_chunks, nullptr);
+}
+
+// The allocation-free call's chunk partials live in this array, one copy per
+// GPU (the runtime places it when the code object loads on that GPU).  Host
+// code never passes the name itself to a kernel: its device address, resolved
+// once per device with that device current, is kept in scratch_dev[].
+constexpr size_t kScratchBytes = CSA2_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+static std::atomic<void*> scratch_dev[kMaxDevices];
+
+static void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = scratch_dev[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  // two threads that race here both store the same address
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return nullptr;
+  scratch_dev[dev].store(p, std::memory_order_release);
+  return p;
 }
 
 }  // namespace csa2
@@ -962,4 +986,27 @@ extern "C" csa2_status csa2_sparse_swa_decode_layers_paged(
   return attention_call(L, q_lat, R, H, code_pages, scale_pages, B, T, row_seq, idx, off, K, swa, S, swa_start,
                         swa_len, softmax_scale, nullptr, nullptr, o, lse, workspace, workspace_bytes, stream,
                         PageMap{block_table, max_blocks, page});
+}
+
+extern "C" csa2_status csa2_sparse_swa_decode_layers_noalloc(
+    int32_t L, const uint16_t* q_lat, int32_t R, int32_t H, const uint8_t* codes, const uint8_t* scales, int32_t B,
+    int64_t T, const int32_t* row_seq, const int32_t* idx, const int32_t* layer_idx, int32_t K, const uint16_t* swa,
+    int32_t S, const int32_t* swa_start, const int32_t* swa_len, float softmax_scale, float* o, float* lse,
+    void* stream) {
+  const csa2_status st = check_sparse_swa(L, q_lat, R, H, codes, scales, B, T, row_seq, idx, K, swa, S, swa_start,
+                                          swa_len, o, lse);
+  if (st != CSA2_OK) return st;
+  if (!layer_idx) return CSA2_EINVAL;
+  int64_t off[kMaxLayers];
+  for (int l = 0; l < L; ++l) {
+    if (layer_idx[l] < 0) return CSA2_EINVAL;
+    off[l] = (int64_t)layer_idx[l] * R * K;
+  }
+  // a shape beyond the array is refused before any HIP call
+  const Plan p = chunk_plan(L, R, K, true, true);
+  if (p.n_chunks > 1 && partial_bytes(L, R, H, p.n_chunks, nullptr) > kScratchBytes) return CSA2_ESCRATCH;
+  void* ws = scratch_ptr();
+  if (!ws) return CSA2_ELAUNCH;
+  return attention_call(L, q_lat, R, H, codes, scales, B, T, row_seq, idx, off, K, swa, S, swa_start, swa_len,
+                        softmax_scale, nullptr, nullptr, o, lse, ws, kScratchBytes, stream, PageMap{}, true);
 }

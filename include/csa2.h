@@ -26,7 +26,9 @@
  *   - Every tensor argument is a DEVICE pointer allocated and owned by the
  *     caller.  The library never allocates, frees or retains caller memory.
  *     Calls that need scratch memory take a caller-provided `workspace` whose
- *     size comes from the matching *_workspace_size() query.
+ *     size comes from the matching *_workspace_size() query (the one
+ *     allocation-free call near the end of this file uses a fixed static
+ *     array of the library's instead).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *     enqueues work on that stream and returns without synchronising.  The
  *     library launches no memset/memcpy nodes, so calls may be captured into a
@@ -60,7 +62,8 @@ enum {
   CSA2_ESHAPE = 2,     /* a dimension outside what the kernels support          */
   CSA2_EALIGN = 3,     /* a pointer or stride without the required alignment    */
   CSA2_EWORKSPACE = 4, /* workspace pointer NULL or smaller than required       */
-  CSA2_ELAUNCH = 5     /* hipGetLastError() reported a failure after a launch  */
+  CSA2_ELAUNCH = 5,    /* hipGetLastError() reported a failure after a launch  */
+  CSA2_ESCRATCH = 6    /* the shape needs more than the fixed scratch array     */
 };
 
 /* Version of this ABI (incremented on any incompatible change). */
@@ -465,6 +468,33 @@ csa2_status csa2_absorb_q(const uint16_t* q, int32_t R, int32_t H, int32_t D, co
                           uint16_t* q_lat, void* stream);
 csa2_status csa2_unabsorb_o(const float* o_lat, int32_t R, int32_t H, int32_t D, const uint16_t* w_uv,
                             float* out, void* stream);
+/* -------------------------------------------------------------------------
+ * Allocation-free multi-layer attention, for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.
+ *
+ * csa2_sparse_swa_decode_layers_noalloc computes exactly what
+ * csa2_sparse_swa_decode_layers computes (same arguments, same kernels), but
+ * its chunk partials go to a scratch array of CSA2_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) that the library holds as a static device variable, one per GPU,
+ * from the first call on that GPU until the process ends.  The call itself
+ * allocates nothing.  The array holds the partials of every shape with
+ * K <= 2048 on a 256-CU GPU; a shape whose partials need more returns
+ * CSA2_ESCRATCH before launching; a shape that runs each (layer, row)
+ * as one chunk needs none (csa2_sparse_swa_decode_layers_workspace_size tells
+ * the size the partials would take).  Every call on one GPU shares that GPU's
+ * array: calls that can overlap on one GPU (different streams, or threads
+ * without ordering) race and give wrong results; calls ordered on one stream
+ * are safe.  Nothing in the array needs to start cleared.  CSA2_ELAUNCH also
+ * reports a failure to resolve the array's device address.
+ * ------------------------------------------------------------------------- */
+#define CSA2_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+csa2_status csa2_sparse_swa_decode_layers_noalloc(int32_t L, const uint16_t* q_lat, int32_t R, int32_t H,
+                                                  const uint8_t* codes, const uint8_t* scales, int32_t B, int64_t T,
+                                                  const int32_t* row_seq, const int32_t* idx,
+                                                  const int32_t* layer_idx, int32_t K, const uint16_t* swa, int32_t S,
+                                                  const int32_t* swa_start, const int32_t* swa_len,
+                                                  float softmax_scale, float* o, float* lse, void* stream);
 #ifdef __cplusplus
 }
 #endif

@@ -29,7 +29,7 @@ def test_header_functions_all_exported_and_bound():
 def test_version_and_status_strings():
     assert F.csa2_abi_version() == 1
     L = F.lib()
-    for s in range(6):
+    for s in range(7):
         assert L.csa2_status_str(s)
     assert b"unknown" in L.csa2_status_str(99)
 
@@ -134,6 +134,24 @@ def test_layers_call_argument_errors():
     assert L.csa2_sparse_swa_decode_layers(*a) == 2          # H = 20
     a = list(args); a[20] = 100
     assert L.csa2_sparse_swa_decode_layers(*a) == 4          # workspace too small
+
+
+def test_noalloc_call_argument_errors():
+    # the allocation-free layers call refuses a shape whose partials exceed its static array before
+    # touching the GPU, and checks its other arguments like the workspace call
+    L = F.lib()
+    one = (ctypes.c_int32 * 1)(0)
+    args = [1, DUMMY, 128, 64, DUMMY, DUMMY, 1, 8192, DUMMY, DUMMY, ctypes.cast(one, ctypes.c_void_p), 8192, DUMMY,
+            128, DUMMY, DUMMY, 0.1, DUMMY, DUMMY, NULL]
+    assert F.csa2_sparse_swa_decode_layers_workspace_size(1, 128, 64, 8192) > F.NOALLOC_SCRATCH_BYTES
+    assert L.csa2_sparse_swa_decode_layers_noalloc(*args) == 6
+    a = list(args); a[10] = NULL
+    assert L.csa2_sparse_swa_decode_layers_noalloc(*a) == 1
+    a = list(args); a[3] = 20
+    assert L.csa2_sparse_swa_decode_layers_noalloc(*a) == 2
+    a = list(args); a[1] = NULL
+    assert L.csa2_sparse_swa_decode_layers_noalloc(*a) == 1
+    assert F.NOALLOC_SCRATCH_BYTES == 64 << 20
 
 
 def test_index_full_pool_argument_errors():
