@@ -48,7 +48,7 @@ def test_absorb_q_vs_oracle(R, H):
     assert np.mean(got != rne) <= 1e-3
 
 
-@pytest.mark.parametrize("R,H", [(8, 64), (64, 64), (1, 16), (77, 64)])
+@pytest.mark.parametrize("R,H", [(8, 64), (64, 64), (1, 16), (77, 64), (130, 48)])
 def test_unabsorb_o_vs_oracle(R, H):
     dev = device()
     g = torch.Generator(device=dev); g.manual_seed(12 + R)
