@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches only (no HIP graph replay)")
     ap.add_argument("--cpu-sample", type=int, default=0, help="sequences in the CPU-baseline sample (0 = auto)")
+    ap.add_argument("--input-sets", type=int, default=4,
+                    help="decode: query sets replayed in turn (different selections, different gathered rows)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
     return ap.parse_args()
@@ -66,8 +68,9 @@ def measured_traffic(name, digest, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def decode_step_bytes(B, T, H, K, P, modes, W=128):
-    """Compulsory bytes of one decode step (each call's inputs read once, outputs written once)."""
+def decode_step_bytes(B, T, H, K, P, modes, W=128, streams=True):
+    """Compulsory bytes of one decode step (each call's inputs read once, outputs written once).
+    streams: the Full layer's selection runs during its scan (csa2_index_full_pool_streams)."""
     C = 512
     total = B * (2 * C + 288)                          # pack the current token's row
     total += B * 2 * 64 + B * len(modes) * 3 * 2 * C  # its key copied; each layer's window row into both ring slots
@@ -77,7 +80,7 @@ def decode_step_bytes(B, T, H, K, P, modes, W=128):
                 # keys + query read; pool (positions + scores) and Top-K written: the streaming selection
                 # needs no score array
                 total += B * T * 64 + B * 64 + B * P * 8 + B * K * 4
-            elif T > 32768 and B * T * 16 <= (1 << 30):
+            elif streams:
                 # the streaming selection cuts the Top-K during the scan: keys + query read, Top-K written
                 total += B * T * 64 + B * 64 + B * K * 4
             else:
@@ -154,7 +157,7 @@ def cpu_baseline_decode(wl, cfg, n_seq):
 class Workload:
     """Seeded decode inputs on the GPU; the FP4 cache is packed by the library."""
 
-    def __init__(self, cfg, dev, chunk_rows=65536):
+    def __init__(self, cfg, dev, chunk_rows=65536, n_sets=1):
         import torch
         import workloads as W
         from fp4_sparse_attention_amd.decode import StackIO, pack_cache
@@ -182,6 +185,14 @@ class Workload:
         self.new_rows = self.latent_chunk_rows_at(T - 1)
         self.new_keys = self.k_idx[:, T - 1].clone()
         self.new_window = W.bf16_normal(cfg.seed, (L, B, 512), device=dev, chunk_index=7919)
+        # further query sets (latent and indexer queries of every layer), so that consecutive steps select
+        # different positions and gather different rows; they share the cache, keys and window rings
+        self.layer_sets = [self.layers]
+        for s in range(1, n_sets):
+            self.layer_sets.append(StackIO(
+                W.bf16_normal(cfg.seed, (L, B, cfg.heads, 512), std=0.5, device=dev, role=4, chunk_index=1000 + s),
+                W.fp8_normal(cfg.seed, (L, B, 64), device=dev, role=3, chunk_index=1000 + s),
+                self.layers.swa, self.layers.swa_start, self.layers.swa_len))
         torch.cuda.synchronize()
 
     def latent_chunk(self, b, c):
@@ -208,63 +219,130 @@ class Workload:
         return out
 
 
+def attention_layer_bytes(B, H, K, W=128, C=512):
+    """Compulsory bytes of one layer of the stacked attention launch: its index slice, the K gathered FP4 rows
+    (288 B each), the latent queries, the window rows, o and lse written."""
+    return B * K * (4 + 288) + B * H * C * 2 + B * W * C * 2 + B * H * (C + 1) * 4
+
+
+def time_absorb(cfg, dev, reps):
+    """Per-step time of the absorption helpers: one csa2_absorb_q and one csa2_unabsorb_o per layer, each
+    layer with its own W_UK / W_UV (bf16 [H, 128, 512])."""
+    import torch
+    import workloads as W
+    import fp4_sparse_attention_amd as F
+    L, B, H = len(cfg.modes), cfg.batch, cfg.heads
+    w = [W.absorb_weights(cfg.seed, l, H, device=dev) for l in range(L)]
+    q = [W.head_queries(cfg.seed, l, B, H, device=dev) for l in range(L)]
+    q_lat = torch.empty((L, B, H, 512), dtype=torch.bfloat16, device=dev)
+    o_lat = torch.randn((L, B, H, 512), device=dev)
+    out = torch.empty((L, B, H, 128), dtype=torch.float32, device=dev)
+
+    def absorb():
+        for l in range(L):
+            F.csa2_absorb_q(q[l], w[l][0], q_lat[l])
+
+    def unabsorb():
+        for l in range(L):
+            F.csa2_unabsorb_o(o_lat[l], w[l][1], out[l])
+
+    res = {}
+    for name, fn, per_layer in (("absorb_q", absorb, H * 128 * 512 * 2 + B * H * (128 + 512) * 2),
+                                ("unabsorb_o", unabsorb, H * 128 * 512 * 2 + B * H * (512 + 128) * 4)):
+        # the L calls captured into a graph and replayed, so that host launch overhead is not timed
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        res[name] = {"us_per_step": us, "calls_per_step": L, "bytes_per_step": L * per_layer,
+                     "gbps": L * per_layer / (us * 1e-6) / 1e9, "launch": "hip graph replay"}
+    return res
+
+
 def bench_decode(args, cfg):
     import torch
+    import fp4_sparse_attention_amd as F
     from fp4_sparse_attention_amd.decode import Csa2DecodeStack
     dev = torch.device("cuda:0")
-    wl = Workload(cfg, dev)
+    n_sets = max(1, args.input_sets)
+    wl = Workload(cfg, dev, n_sets=n_sets)
     stack = Csa2DecodeStack(cfg.batch, cfg.context, cfg.heads, cfg.topk, cfg.modes,
                             pool_size=cfg.pool if cfg.pool else 16384)
-    step = lambda: stack.step(wl.codes, wl.scales, wl.k_idx, wl.layers, SIGMA, new_rows=wl.new_rows,
-                              new_keys=wl.new_keys, new_window=wl.new_window)
-    for _ in range(args.warmup):
-        step()
+
+    def step(i, **kw):
+        stack.step(wl.codes, wl.scales, wl.k_idx, wl.layer_sets[i % n_sets], SIGMA, new_rows=wl.new_rows,
+                   new_keys=wl.new_keys, new_window=wl.new_window, **kw)
+
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
-    # eager steps, with events around the Full-layer scan for its roofline figure
+    # eager steps, with events around the Full-layer scan and the attention launch for their roofline figures
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    index_ev = []
+    index_ev, attn_ev = [], []
     t_start.record()
-    for _ in range(args.steps):
-        stack.step(wl.codes, wl.scales, wl.k_idx, wl.layers, SIGMA, new_rows=wl.new_rows, new_keys=wl.new_keys,
-                   new_window=wl.new_window, time_index=True)
+    for i in range(args.steps):
+        step(i, time_index=True, time_attention=True)
         index_ev.append(stack.index_events)
+        attn_ev.append(stack.attention_events)
     t_end.record()
     torch.cuda.synchronize()
     ms_eager = t_start.elapsed_time(t_end) / args.steps
     idx_ms = sum(a.elapsed_time(b) for a, b in index_ev) / len(index_ev)
+    attn_ms = sum(a.elapsed_time(b) for a, b in attn_ev) / len(attn_ev)
     ms = ms_eager
-    graph = None
+    graphs = None
     if not args.no_graph:
-        # the same step captured once into a HIP graph and replayed: every kernel of every step still
-        # runs; only the per-launch host overhead goes
+        # each query set's step captured once into a HIP graph and the graphs replayed in turn: every kernel
+        # of every step still runs; only the per-launch host overhead goes
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            step()
+            step(0)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        for _ in range(args.warmup):
-            graph.replay()
+        graphs = []
+        for i in range(n_sets):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % n_sets].replay()
         torch.cuda.synchronize()
         t_start.record()
-        for _ in range(args.steps):
-            graph.replay()
+        for i in range(args.steps):
+            graphs[i % n_sets].replay()
         t_end.record()
         torch.cuda.synchronize()
         ms = t_start.elapsed_time(t_end) / args.steps
     B, T, H, K = cfg.batch, cfg.context, cfg.heads, cfg.topk
+    L = len(cfg.modes)
     P = min(cfg.pool, T) if "reindex" in cfg.modes else 0
-    step_bytes = decode_step_bytes(B, T, H, K, P, cfg.modes, cfg.window)
-    # the Full-layer scan: 64-byte keys per position and the query; the streaming selection (rows longer than
-    # 32,768 positions) writes no scores, shorter rows write 4 bytes of score per position
-    streams = T > 32768 and B * T * 16 <= (1 << 30)
+    # the Full-layer scan: 64-byte keys per position and the query; when the library selects during the scan
+    # no score array is written, otherwise 4 bytes of score per position
+    streams = F.csa2_index_full_pool_streams(B, T)
+    step_bytes = decode_step_bytes(B, T, H, K, P, cfg.modes, cfg.window, streams)
     idx_bytes = B * T * (64 if streams else 64 + 4) + B * 64
     achieved = idx_bytes / (idx_ms * 1e-3) / 1e9
     digest = kernel_source_digest(["index.hip", "tile.hpp", "internal.hpp", "common.hpp"])
+    attn_bytes = L * attention_layer_bytes(B, H, K, cfg.window)
+    attn_achieved = attn_bytes / (attn_ms * 1e-3) / 1e9
+    attn_digest = kernel_source_digest(["attention.hip", "internal.hpp", "common.hpp"])
     rec = {
         "metric": METRIC,
         "value": B / (ms * 1e-3),
@@ -274,11 +352,12 @@ def bench_decode(args, cfg):
         "warmup": args.warmup,
         "ms_per_step": ms,
         "ms_per_step_eager": ms_eager,
-        "launch": "hip graph replay of the captured step" if graph is not None else "eager",
+        "launch": (f"hip graph replay of the captured step, {n_sets} query sets in turn" if graphs is not None
+                   else f"eager, {n_sets} query sets in turn"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e2m1/e4m3 storage; e4m3xe4m3->f32 index; f16xf16->f32 attention",
+        "dtype": "e2m1/e4m3 storage; e4m3xe4m3->f32 index; f16xf16->f32 sparse attention, bf16xbf16->f32 window",
         "data": "synthetic (seeded torch normal draws; FP4 cache packed by the library)",
         "config": {"workload": cfg.name, "batch": B, "context": T, "heads": H, "topk": K,
                    "layers": list(cfg.modes), "pool": P, "window": cfg.window, "latent_channels": 512},
@@ -289,6 +368,12 @@ def bench_decode(args, cfg):
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": measured_traffic("index_full", digest, cfg.name),
                      "launch_ms": idx_ms, "bytes_per_launch": idx_bytes},
+        "roofline_attention": {"kernel": f"csa2_sparse_swa_decode_layers ({L} layers: chunk + combine kernels)",
+                               "bound": "hbm", "achieved": attn_achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                               "frac": attn_achieved / HBM_PEAK_GBPS,
+                               "traffic": measured_traffic("attention", attn_digest, cfg.name),
+                               "launch_ms": attn_ms, "bytes_per_launch": attn_bytes},
+        "absorb_helpers": time_absorb(cfg, dev, max(args.steps, 5)),
     }
     if not args.no_cpu_baseline:
         n_seq = args.cpu_sample or (4 if T >= (1 << 20) else 8)
@@ -425,7 +510,7 @@ def bench_prefill(args, cfg):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e2m1/e4m3 storage; e4m3xe4m3->f32 index; f16xf16->f32 attention",
+        "dtype": "e2m1/e4m3 storage; e4m3xe4m3->f32 index; f16xf16->f32 sparse attention, bf16xbf16->f32 window",
         "data": "synthetic (seeded torch normal draws; FP4 cache packed by the library)",
         "config": {"workload": cfg.name, "queries": Q, "context": T, "heads": H, "topk": K, "window": cfg.window,
                    "latent_channels": 512},
@@ -511,7 +596,7 @@ def copy_calibration():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only (there is no multi-GPU path); use --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

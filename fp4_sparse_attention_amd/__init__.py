@@ -37,6 +37,7 @@ _SIGS = {
     "csa2_topk_pool": (_i32, [_c_void_p, _i32, _i64, _i64, _i32, _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                               _c_void_p, _size_t, _c_void_p]),
     "csa2_index_full_pool_workspace_size": (_size_t, [_i32, _i64, _i32]),
+    "csa2_index_full_pool_streams": (_i32, [_i32, _i64]),
     "csa2_index_full_pool": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i64, _c_void_p, _c_void_p, _c_void_p, _i32,
                                     _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t, _c_void_p, _c_void_p,
                                     _c_void_p]),
@@ -446,6 +447,11 @@ def csa2_sparse_swa_decode_layers_noalloc(q_lat, codes, scales, idx, layer_idx, 
 
 def csa2_index_full_pool_workspace_size(R, T, k_pool):
     return int(lib().csa2_index_full_pool_workspace_size(R, T, k_pool))
+
+
+def csa2_index_full_pool_streams(R, T):
+    """True when csa2_index_full_pool selects during the scoring pass at R rows of T positions."""
+    return bool(lib().csa2_index_full_pool_streams(R, T))
 
 
 def csa2_index_full_pool(q_idx, k_idx, scores, k_pool, k_top, pool_idx, top_idx, pool_scores=None, row_seq=None,

@@ -1873,6 +1873,10 @@ extern "C" size_t csa2_index_full_pool_workspace_size(int32_t R, int64_t T, int3
   return align_up(csa2_topk_workspace_size(R, T, k_pool), 256) + align_up((size_t)R * T * 4, 256);
 }
 
+extern "C" int32_t csa2_index_full_pool_streams(int32_t R, int64_t T) {
+  return (R > 0 && T > 0 && pool_may_stream(R, T)) ? 1 : 0;
+}
+
 static csa2_status index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int32_t B, int64_t T,
                                    const int32_t* row_seq, const int64_t* row_limit, float* scores, int32_t k_pool,
                                    int32_t k_top, int32_t* pool_idx, float* pool_scores, int32_t* top_idx,

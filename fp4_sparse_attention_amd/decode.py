@@ -111,13 +111,14 @@ class Csa2DecodeStack:
         self.ws_layers = torch.empty(csa2_sparse_swa_decode_layers_workspace_size(self.L, B, H, K), dtype=u8,
                                      device=dev)
         self.index_events = None
+        self.attention_events = None
         # the current token's cache row (position T - 1) and position, for the decode-time append
         self.tok_rows = torch.arange(B, dtype=torch.int64, device=dev) * T + (T - 1)
         self.tok_pos = torch.full((B,), T - 1, dtype=torch.int64, device=dev)
 
     def step(self, codes, scales, k_idx, layers, sigma: float, new_rows: Optional[torch.Tensor] = None,
              stream=None, time_index: bool = False, new_keys: Optional[torch.Tensor] = None,
-             new_window: Optional[torch.Tensor] = None):
+             new_window: Optional[torch.Tensor] = None, time_attention: bool = False):
         """Run every layer once.  layers: a StackIO (all layers' attention in one
         launch, after the selections) or a list of LayerIO (one attention call
         per layer).  new_rows (bf16 [B, 512]), if given, is the current token's
@@ -128,7 +129,8 @@ class Csa2DecodeStack:
         written into each layer's ring (the window bounds are updated).
 
         time_index: record HIP events around the Full-layer index call on the
-        stream (self.index_events holds the (start, end) pair)."""
+        stream (self.index_events holds the (start, end) pair).  time_attention:
+        the same around the stacked attention launch (self.attention_events)."""
         B, T, K = self.B, self.T, self.K
         stacked = layers if isinstance(layers, StackIO) else None
         ios = layers.layers if stacked is not None else list(layers)
@@ -195,9 +197,15 @@ class Csa2DecodeStack:
             else:
                 raise ValueError(mode)
         if stacked is not None and self.fused_attention:
+            ev = self._event_pair() if time_attention else None
+            if ev:
+                ev[0].record(stream)
             csa2_sparse_swa_decode_layers(stacked.q_lat, codes, scales, self.idx, src, stacked.swa, stacked.swa_start,
                                           stacked.swa_len, sigma, self.o, self.lse, workspace=self.ws_layers,
                                           stream=stream)
+            if ev:
+                ev[1].record(stream)
+                self.attention_events = ev
             return self.o, self.lse
         for li, io in enumerate(ios):
             idx = self.idx[src[li]]
@@ -210,6 +218,10 @@ class Csa2DecodeStack:
                 csa2_swa_merge(io.q_lat, io.swa, io.swa_start, io.swa_len, sigma, self.o[li], self.lse[li],
                                o_sparse=self.o[li], lse_sparse=self.lse[li], workspace=self.ws_swa, stream=stream)
         return self.o, self.lse
+
+    @staticmethod
+    def _event_pair():
+        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
     def _scan_events(self):
         # a fresh, already-created pair of timing events (the library records them)

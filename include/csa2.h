@@ -202,8 +202,9 @@ csa2_status csa2_topk_pool(const float* scores, int32_t R, int64_t N, int64_t ro
  *
  * Equivalent to csa2_index_full(q_idx, k_idx, R, B, T, row_seq, row_limit,
  * scores) followed by csa2_topk_pool(scores, R, T, T, k_pool, k_top, NULL,
- * pool_idx, pool_scores, top_idx): same scores, same selections.  Unless R x T
- * is too large for the candidate lists (R * T > 2^30), the selection streams:
+ * pool_idx, pool_scores, top_idx): same scores, same selections.  Unless the
+ * rows are short (T <= 32,768) or R x T is too large for the candidate lists
+ * (R * T > 2^30), the selection streams:
  * a strided sample of each row bounds its k_pool-th score from below, the
  * scoring pass keeps only the positions at or above that bound (in position
  * order, block by block) and the selection finishes on them; the result is
@@ -224,6 +225,11 @@ csa2_status csa2_topk_pool(const float* scores, int32_t R, int64_t N, int64_t ro
  * Errors: as those two calls; ELAUNCH also when an event cannot be recorded.
  * ------------------------------------------------------------------------- */
 size_t csa2_index_full_pool_workspace_size(int32_t R, int64_t T, int32_t k_pool);
+/* 1 when csa2_index_full_pool at R rows of T positions selects during the
+ * scoring pass (T > 32,768 and R * T <= 2^30: with scores NULL no score array
+ * is written or read), 0 when it scores first and then selects; 0 for
+ * non-positive sizes.  A host-side query, no GPU work. */
+int32_t csa2_index_full_pool_streams(int32_t R, int64_t T);
 csa2_status csa2_index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int32_t B, int64_t T,
                                  const int32_t* row_seq, const int64_t* row_limit, float* scores,
                                  int32_t k_pool, int32_t k_top, int32_t* pool_idx, float* pool_scores,
@@ -462,7 +468,7 @@ csa2_status csa2_decode_append(int32_t B, int32_t L, const uint16_t* new_latent,
  *            products exact, fp32 accumulation
  * All tensors dense.  R == 0 is a no-op.
  * Errors: EINVAL (R < 0, H <= 0, null pointer), ESHAPE (D != 128,
- * H > 65535), EALIGN (16-byte pointers).
+ * H > 65535, R > 4,194,240), EALIGN (16-byte pointers).
  * ------------------------------------------------------------------------- */
 csa2_status csa2_absorb_q(const uint16_t* q, int32_t R, int32_t H, int32_t D, const uint16_t* w_uk,
                           uint16_t* q_lat, void* stream);
