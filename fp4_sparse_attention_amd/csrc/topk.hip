@@ -373,11 +373,13 @@ constexpr int kSmallBins = 1 << kSmallBits;
 // key tau is found by three radix digits of 12, 10 and 10 bits (from bit 31;
 // the first histogram's total is the visible count); the ordered write then
 // needs one block scan of the threads' (above tau, equal to tau) counts, since
-// thread order is slot order.
+// thread order is slot order.  A second selection (k2 <= k, positions only)
+// reuses the keys in registers: when k2 == k it is written by the same pass.
 template <int J>
 __global__ void __launch_bounds__(kSmallThreads)
 topk_small_kernel(const float* __restrict__ scores, int N, int64_t stride, const int32_t* __restrict__ index_map,
-                  int32_t k, int32_t* __restrict__ idx_out, float* __restrict__ score_out) {
+                  int32_t k, int32_t* __restrict__ idx_out, float* __restrict__ score_out, int32_t k2,
+                  int32_t* __restrict__ idx2_out) {
   __shared__ uint32_t h[kSmallBins];
   __shared__ uint32_t wt[16];
   __shared__ uint32_t s_digit, s_above;
@@ -387,7 +389,6 @@ topk_small_kernel(const float* __restrict__ scores, int N, int64_t stride, const
   const int32_t* map_row = index_map ? index_map + (int64_t)r * N : nullptr;
   const int s0 = 4 * J * tid;
 
-  for (int i = tid; i < kSmallBins; i += kSmallThreads) h[i] = 0u;
   uint32_t key[J][4];
   int32_t pos[J][4];
   {
@@ -412,100 +413,116 @@ topk_small_kernel(const float* __restrict__ scores, int N, int64_t stride, const
       }
     }
   }
-  __syncthreads();
 
-  // radix select of tau, the k_eff-th largest visible key
-  uint32_t need = 0, prefix = 0u, k_eff = 0;
+  // radix select of tau, the k_eff-th largest visible key (k_eff = min(kk, visible))
+  auto select = [&](uint32_t kk, uint32_t& tau, uint32_t& need_eq, uint32_t& k_eff) {
+    uint32_t need = 0, prefix = 0u;
+    k_eff = 0;
 #pragma unroll 1
-  for (int d = 0; d < 3; ++d) {
-    const int shift = d == 0 ? 20 : (d == 1 ? 10 : 0);
-    const int hi = d == 0 ? 32 : (d == 1 ? 20 : 10);
-    const uint32_t bmask = d == 0 ? 4095u : 1023u;
-    if (d > 0) {
-      for (int i = tid; i < 1024; i += kSmallThreads) h[i] = 0u;
+    for (int d = 0; d < 3; ++d) {
+      const int shift = d == 0 ? 20 : (d == 1 ? 10 : 0);
+      const int hi = d == 0 ? 32 : (d == 1 ? 20 : 10);
+      const uint32_t bmask = d == 0 ? 4095u : 1023u;
+      const int nb = d == 0 ? 4096 : 1024;
+      for (int i = tid; i < nb; i += kSmallThreads) h[i] = 0u;
       __syncthreads();
-    }
 #pragma unroll
-    for (int it = 0; it < J; ++it)
+      for (int it = 0; it < J; ++it)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t kk = key[it][j];
-        if (kk != 0u && (hi == 32 || (kk >> hi) == (prefix >> hi))) atomicAdd(&h[(kk >> shift) & bmask], 1u);
-      }
-    __syncthreads();
-    // bins walked from the top: 4 per thread at the first digit, 1 after
-    const int per = d == 0 ? 4 : 1;
-    const int nb = d == 0 ? 4096 : 1024;
-    uint32_t c[4] = {0u, 0u, 0u, 0u}, local = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (j < per) {
-        c[j] = h[nb - 1 - per * tid - j];
-        local += c[j];
-      }
-    uint32_t total;
-    const uint32_t excl = block_scan_1024(local, wt, total);
-    if (d == 0) {
-      k_eff = total < (uint32_t)k ? total : (uint32_t)k;     // total = visible keys
-      need = k_eff;
-    }
-    if (need == 0u) break;
-    if (excl < need && need <= excl + local) {
-      uint32_t acc = excl;
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t x = key[it][j];
+          if (x != 0u && (hi == 32 || (x >> hi) == (prefix >> hi))) atomicAdd(&h[(x >> shift) & bmask], 1u);
+        }
+      __syncthreads();
+      // bins walked from the top: 4 per thread at the first digit, 1 after
+      const int per = d == 0 ? 4 : 1;
+      uint32_t c[4] = {0u, 0u, 0u, 0u}, local = 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (j < per) {
-          if (acc < need && need <= acc + c[j]) {
-            s_digit = (uint32_t)(nb - 1 - per * tid - j);
-            s_above = acc;
+          c[j] = h[nb - 1 - per * tid - j];
+          local += c[j];
+        }
+      uint32_t total;
+      const uint32_t excl = block_scan_1024(local, wt, total);
+      if (d == 0) {
+        k_eff = total < kk ? total : kk;     // total = visible keys
+        need = k_eff;
+      }
+      if (need == 0u) break;
+      if (excl < need && need <= excl + local) {
+        uint32_t acc = excl;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (j < per) {
+            if (acc < need && need <= acc + c[j]) {
+              s_digit = (uint32_t)(nb - 1 - per * tid - j);
+              s_above = acc;
+            }
+            acc += c[j];
           }
-          acc += c[j];
+      }
+      __syncthreads();
+      prefix |= s_digit << shift;
+      need -= s_above;
+      __syncthreads();
+    }
+    tau = prefix;
+    need_eq = need;
+  };
+
+  // ordered write: a slot's output index is (#keys > tau before it) + min(#keys == tau before it, need_eq);
+  // orow2 (or null) takes the same positions
+  auto write = [&](uint32_t tau, uint32_t need_eq, uint32_t k_eff, int32_t k_out, int32_t* orow, float* srow,
+                   int32_t* orow2) {
+    if (k_eff > 0) {
+      uint32_t cg = 0, ce = 0;
+#pragma unroll
+      for (int it = 0; it < J; ++it)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t x = key[it][j];
+          cg += x != 0u && x > tau;
+          ce += x != 0u && x == tau;
+        }
+      // both counts in one scan: each stays below 2^16 (N <= 32768)
+      uint32_t tot;
+      const uint32_t pre = block_scan_1024((cg << 16) | ce, wt, tot);
+      uint32_t g = pre >> 16, e = pre & 0xFFFFu;
+#pragma unroll
+      for (int it = 0; it < J; ++it)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t x = key[it][j];
+          const bool is_gt = x != 0u && x > tau;
+          const bool is_eq = x != 0u && x == tau;
+          const bool take = is_gt || (is_eq && e < need_eq);
+          const uint32_t o = g + (is_gt ? min(e, need_eq) : e);
+          g += is_gt ? 1u : 0u;
+          e += is_eq ? 1u : 0u;
+          if (take && o < k_eff) {
+            orow[o] = pos[it][j];
+            if (orow2) orow2[o] = pos[it][j];
+            if (srow) srow[o] = key_score(x);
+          }
         }
     }
-    __syncthreads();
-    prefix |= s_digit << shift;
-    need -= s_above;
-    __syncthreads();
-  }
-  const uint32_t tau = prefix, need_eq = need;
+    for (int i = (int)k_eff + tid; i < k_out; i += kSmallThreads) {
+      orow[i] = -1;
+      if (orow2) orow2[i] = -1;
+      if (srow) srow[i] = __builtin_nanf("");
+    }
+  };
 
-  // ordered write: a slot's output index is (#keys > tau before it) + min(#keys == tau before it, need_eq)
-  int32_t* orow = idx_out + (int64_t)r * k;
-  float* srow = score_out ? score_out + (int64_t)r * k : nullptr;
-  if (k_eff > 0) {
-    uint32_t cg = 0, ce = 0;
-#pragma unroll
-    for (int it = 0; it < J; ++it)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t kk = key[it][j];
-        cg += kk != 0u && kk > tau;
-        ce += kk != 0u && kk == tau;
-      }
-    // both counts in one scan: each stays below 2^16 (N <= 32768)
-    uint32_t tot;
-    const uint32_t pre = block_scan_1024((cg << 16) | ce, wt, tot);
-    uint32_t g = pre >> 16, e = pre & 0xFFFFu;
-#pragma unroll
-    for (int it = 0; it < J; ++it)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t kk = key[it][j];
-        const bool is_gt = kk != 0u && kk > tau;
-        const bool is_eq = kk != 0u && kk == tau;
-        const bool take = is_gt || (is_eq && e < need_eq);
-        const uint32_t o = g + (is_gt ? min(e, need_eq) : e);
-        g += is_gt ? 1u : 0u;
-        e += is_eq ? 1u : 0u;
-        if (take && o < k_eff) {
-          orow[o] = pos[it][j];
-          if (srow) srow[o] = key_score(kk);
-        }
-      }
-  }
-  for (int i = (int)k_eff + tid; i < k; i += kSmallThreads) {
-    orow[i] = -1;
-    if (srow) srow[i] = __builtin_nanf("");
+  uint32_t tau, need_eq, k_eff;
+  select((uint32_t)k, tau, need_eq, k_eff);
+  const bool same = idx2_out && k2 == k;
+  write(tau, need_eq, k_eff, k, idx_out + (int64_t)r * k, score_out ? score_out + (int64_t)r * k : nullptr,
+        same ? idx2_out + (int64_t)r * k2 : nullptr);
+  if (idx2_out && !same) {
+    __syncthreads();
+    select((uint32_t)k2, tau, need_eq, k_eff);
+    write(tau, need_eq, k_eff, k2, idx2_out + (int64_t)r * k2, nullptr, nullptr);
   }
 }
 
@@ -1719,17 +1736,23 @@ static size_t workspace_for(int32_t R, int64_t N) {
   }
 }
 
+// small path; a second selection (k2 <= k, positions only) when idx2_out is set
 static void launch_small(const float* scores, int32_t R, int64_t N, int64_t row_stride, int32_t k,
-                         const int32_t* index_map, int32_t* idx_out, float* score_out, hipStream_t s) {
+                         const int32_t* index_map, int32_t* idx_out, float* score_out, hipStream_t s,
+                         int32_t k2 = 0, int32_t* idx2_out = nullptr) {
   const int J = (int)((N + kSmallThreads * 4 - 1) / (kSmallThreads * 4));
   if (J <= 1)
-    topk_small_kernel<1><<<R, kSmallThreads, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out);
+    topk_small_kernel<1><<<R, kSmallThreads, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out,
+                                                     k2, idx2_out);
   else if (J <= 2)
-    topk_small_kernel<2><<<R, kSmallThreads, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out);
+    topk_small_kernel<2><<<R, kSmallThreads, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out,
+                                                     k2, idx2_out);
   else if (J <= 4)
-    topk_small_kernel<4><<<R, kSmallThreads, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out);
+    topk_small_kernel<4><<<R, kSmallThreads, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out,
+                                                     k2, idx2_out);
   else
-    topk_small_kernel<8><<<R, kSmallThreads, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out);
+    topk_small_kernel<8><<<R, kSmallThreads, 0, s>>>(scores, (int)N, row_stride, index_map, k, idx_out, score_out,
+                                                     k2, idx2_out);
 }
 
 // compact path; a second selection (k2 <= k, positions only) when idx2_out is set
@@ -1848,8 +1871,7 @@ extern "C" csa2_status csa2_topk_pool(const float* scores, int32_t R, int64_t N,
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   switch (choose_path(R, N)) {
     case kSmall:
-      launch_small(scores, R, N, row_stride, k_pool, index_map, pool_idx, pool_scores, s);
-      launch_small(scores, R, N, row_stride, k_top, index_map, top_idx, nullptr, s);
+      launch_small(scores, R, N, row_stride, k_pool, index_map, pool_idx, pool_scores, s, k_top, top_idx);
       break;
     case kCompact:
       launch_compact(scores, R, N, row_stride, k_pool, index_map, pool_idx, pool_scores, k_top, top_idx, ws, s);

@@ -238,7 +238,9 @@ def test_topk_multipass_path_sampled_rows():
 
 
 @pytest.mark.parametrize("R,N,k_pool,k_top,ties", [
-    (8, 16384, 4096, 512, False),          # one-workgroup path (two selections)
+    (8, 16384, 4096, 512, False),          # one-workgroup path (two selections in one launch)
+    (5, 3000, 700, 700, True),             # one-workgroup path, k_top == k_pool (one selection, two outputs)
+    (4, 20000, 2048, 100, True),           # one-workgroup path, heavy ties in both selections
     (4, 131072, 16384, 2048, False),       # candidate-list path, both selections from one list
     (3, 65536, 20000, 20000, True),        # k_top == k_pool, heavy ties
     (2, 1 << 20, 16384, 2048, False),      # the 1M-context pool shape
