@@ -56,16 +56,18 @@ def kernel_source_digest(files):
 
 
 def measured_traffic(name, digest, workload):
-    """HBM bytes per launch from committed counter runs, if taken on this kernel source and workload."""
+    """HBM bytes per launch from committed counter runs (FETCH_SIZE / WRITE_SIZE), if taken on this kernel
+    source and workload; profiles/<name>_traffic.json holds one record or a list of them."""
     path = os.path.join(HERE, "profiles", f"{name}_traffic.json")
     try:
         with open(path) as f:
-            rec = json.load(f)
+            recs = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != digest or rec.get("workload") != workload:
-        return None
-    return rec.get("hbm_bytes_per_launch")
+    for rec in recs if isinstance(recs, list) else [recs]:
+        if rec.get("kernel_source_sha256") == digest and rec.get("workload") == workload:
+            return rec.get("hbm_bytes_per_launch")
+    return None
 
 
 def decode_step_bytes(B, T, H, K, P, modes, W=128, streams=True):
