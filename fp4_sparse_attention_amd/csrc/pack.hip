@@ -6,8 +6,9 @@
 // blocks); the unpack gives a lane 8 channels, so that every wave store writes
 // a contiguous 1 KB of bf16 (with 32 channels per lane each store instruction
 // covered a 64-byte-strided quarter of 4 KB, and with nontemporal stores the
-// unpack ran at 1.4 TB/s).  The kernels are HBM-bound; the arithmetic is kept
-// to integer/compare work (about a dozen lane-ops per element).
+// unpack ran at 1.4 TB/s).  The kernels are HBM-bound: the pack rounds with
+// gfx950's FP4 conversion instruction (about five lane-ops per element, see
+// pack_block), the unpack with integer bit work.
 #include "common.hpp"
 
 namespace csa2 {
@@ -32,69 +33,73 @@ __device__ __forceinline__ uint32_t e4m3_code_nonneg(float v) {
   return code > 0x7Eu ? 0x7Eu : code;
 }
 
-// E2M1 nibble of x given the block's decoded scale thresholds.  t[i] = mid_i *
-// scale for the midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 (exact in fp32);
-// at an exact midpoint the even neighbour wins, which is the upper one for
-// 0.75, 1.75, 3.5 (>=) and the lower one for the others (>).
-struct E2M1Thresholds {
-  float t0, t1, t2, t3, t4, t5, t6;
-};
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ E2M1Thresholds make_thresholds(float s) {
-  E2M1Thresholds t;
-  const float inf = __builtin_inff();
-  bool z = (s == 0.0f);
-  t.t0 = z ? inf : 0.25f * s;
-  t.t1 = z ? inf : 0.75f * s;
-  t.t2 = z ? inf : 1.25f * s;
-  t.t3 = z ? inf : 1.75f * s;
-  t.t4 = z ? inf : 2.5f * s;
-  t.t5 = z ? inf : 3.5f * s;
-  t.t6 = z ? inf : 5.0f * s;
-  return t;
-}
-
-__device__ __forceinline__ uint32_t e2m1_nibble(uint32_t xbits16, const E2M1Thresholds& t) {
-  float ax = __uint_as_float((xbits16 & 0x7FFFu) << 16);
-  uint32_t m = (uint32_t)(ax > t.t0) + (uint32_t)(ax >= t.t1) + (uint32_t)(ax > t.t2) +
-               (uint32_t)(ax >= t.t3) + (uint32_t)(ax > t.t4) + (uint32_t)(ax >= t.t5) +
-               (uint32_t)(ax > t.t6);
-  return m | ((xbits16 >> 12) & 8u);
+// E2M1 code of x / s, nearest with ties to even, saturating at 6, from y =
+// x * r with r = v_rcp_f32(s) (within 1 ulp of 1/s):
+//   * y is within 2^-22 of x / s (relative).  A midpoint m of the E2M1 grid
+//     (0.25, 0.75, ..., 5) has at most 3 significant bits, so m s has at most 7
+//     and x (bf16, 8 bits) either equals m s or differs from it by at least
+//     2^-8 relative;
+//   * rounding y to 10 significant bits therefore returns exactly m when x / s
+//     is the midpoint m, and keeps every other value on its side of every
+//     midpoint (it moves y by at most 2^-10 relative);
+//   * v_cvt_scalef32_pk_fp4_f32 with unit scale then rounds to nearest even on
+//     the E2M1 grid, saturates magnitudes above 6 (infinities included) to 6,
+//     and keeps the sign of zero.
+// So the code equals the nearest-even E2M1 value of the exact quotient.
+__device__ __forceinline__ float snap10(float y) {
+  return __uint_as_float((__float_as_uint(y) + 0x2000u) & 0xFFFFC000u);
 }
 
 // one 16-channel block: 8 dwords of packed bf16 pairs -> 2 dwords of nibbles + scale byte
 __device__ __forceinline__ void pack_block(const uint32_t* w, uint32_t& lo, uint32_t& hi, uint32_t& sc) {
-  uint32_t amax_bits = 0;
+  // |bf16| orders like its bit pattern: the largest magnitude from packed 16-bit maxima
+  u16x2 m2 = {0, 0};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t a = w[i] & 0x7FFFu, b = (w[i] >> 16) & 0x7FFFu;
-    amax_bits = max(amax_bits, max(a, b));    // |bf16| orders like its bit pattern
-  }
-  float amax = __uint_as_float(amax_bits << 16);
+  for (int i = 0; i < 8; ++i) m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+  const uint32_t amax_bits = max((uint32_t)m2[0], (uint32_t)m2[1]);
+  const float amax = __uint_as_float(amax_bits << 16);
   // a NaN anywhere in the block (|bits| above the infinity pattern) gives the
-  // NaN scale 0x7F; its NaN thresholds then leave every magnitude code at 0, so
-  // the whole block decodes to NaN.  Infinities saturate like large finite values.
-  uint32_t code = amax_bits > 0x7F80u ? 0x7Fu : e4m3_code_nonneg(__fdiv_rn(amax, 6.0f));
-  float s = e4m3_to_f32(code);
-  E2M1Thresholds t = make_thresholds(s);
+  // NaN scale 0x7F and every magnitude code 0 (the whole block decodes to NaN);
+  // infinities saturate like large finite values
+  const uint32_t code = amax_bits > 0x7F80u ? 0x7Fu : e4m3_code_nonneg(__fdiv_rn(amax, 6.0f));
   uint32_t out[2] = {0u, 0u};
+  if (code == 0x7Fu) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t n0 = e2m1_nibble(w[i] & 0xFFFFu, t);
-    uint32_t n1 = e2m1_nibble(w[i] >> 16, t);
-    out[i >> 2] |= (n0 | (n1 << 4)) << (8 * (i & 3));
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t n0 = (w[i] >> 12) & 8u, n1 = (w[i] >> 28) & 8u;
+      out[i >> 2] |= (n0 | (n1 << 4)) << (8 * (i & 3));
+    }
+  } else {
+    // a zero scale (amax / 6 below half the smallest E4M3 step) takes every magnitude to 0
+    const float s = e4m3_to_f32(code);
+    const float r = code == 0u ? 0.0f : __builtin_amdgcn_rcpf(s);
+    // channels 2i (low nibble) and 2i + 1 of pair i into byte i % 4 of out[i / 4]
+    auto lo_f = [&](int i) { return snap10(__uint_as_float(w[i] << 16) * r); };
+    auto hi_f = [&](int i) { return snap10(__uint_as_float(w[i] & 0xFFFF0000u) * r); };
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      uint32_t d = 0u;
+      d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, lo_f(4 * q + 0), hi_f(4 * q + 0), 1.0f, 0);
+      d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, lo_f(4 * q + 1), hi_f(4 * q + 1), 1.0f, 1);
+      d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, lo_f(4 * q + 2), hi_f(4 * q + 2), 1.0f, 2);
+      d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, lo_f(4 * q + 3), hi_f(4 * q + 3), 1.0f, 3);
+      out[q] = d;
+    }
   }
   lo = out[0];
   hi = out[1];
   sc = code;
 }
 
-// Pack: one thread owns 32 consecutive channels of one row (two scale
-// blocks): 64 bytes of bf16 in (plain loads: nontemporal ones were 8% slower),
-// 16 bytes of codes and 2 scale bytes out.  (8 channels per lane, with fully
+// Pack: one thread owns NB scale blocks (16 NB consecutive channels) of one
+// row: 32 NB bytes of bf16 in (plain loads: nontemporal ones were 8% slower),
+// 8 NB bytes of codes and NB scale bytes out.  (8 channels per lane, with fully
 // contiguous wave accesses and the block amax shared across a lane pair, ran
-// slower: the per-block scale and threshold work then repeats every 8
-// channels, and the pack is issue-bound at this rate.)
+// slower with threshold-compare rounding: the per-block scale work then
+// repeats every 8 channels.)
+template <int NB>
 __global__ void __launch_bounds__(256)
 fp4_pack_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int parts_per_row, int64_t x_stride,
                 uint8_t* __restrict__ codes, int64_t codes_stride, uint8_t* __restrict__ scales,
@@ -115,15 +120,24 @@ fp4_pack_kernel(const uint16_t* __restrict__ x, int64_t n_rows, int parts_per_ro
     // output row: the input row's own, or (scatter) out_rows[row]; a negative entry skips the row
     const int64_t orow = out_rows ? out_rows[row] : row;
     if (orow < 0) continue;
-    const uint4* src = reinterpret_cast<const uint4*>(x + row * x_stride + part * 32);
-    const uint4 v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
-    const uint32_t w0[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-    const uint32_t w1[8] = {v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
-    uint32_t c0, c1, c2, c3, s0, s1;
-    pack_block(w0, c0, c1, s0);
-    pack_block(w1, c2, c3, s1);
-    *reinterpret_cast<uint4*>(codes + orow * codes_stride + part * 16) = make_uint4(c0, c1, c2, c3);
-    *reinterpret_cast<uint16_t*>(scales + orow * scales_stride + part * 2) = (uint16_t)(s0 | (s1 << 8));
+    const uint4* src = reinterpret_cast<const uint4*>(x + row * x_stride + part * 16 * NB);
+    uint4 v[2 * NB];
+#pragma unroll
+    for (int i = 0; i < 2 * NB; ++i) v[i] = src[i];
+    uint32_t c[2 * NB], sc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const uint32_t w[8] = {v[2 * b].x, v[2 * b].y, v[2 * b].z, v[2 * b].w,
+                             v[2 * b + 1].x, v[2 * b + 1].y, v[2 * b + 1].z, v[2 * b + 1].w};
+      pack_block(w, c[2 * b], c[2 * b + 1], sc[b]);
+    }
+    if constexpr (NB == 2) {
+      *reinterpret_cast<uint4*>(codes + orow * codes_stride + part * 16) = make_uint4(c[0], c[1], c[2], c[3]);
+      *reinterpret_cast<uint16_t*>(scales + orow * scales_stride + part * 2) = (uint16_t)(sc[0] | (sc[1] << 8));
+    } else {
+      *reinterpret_cast<uint2*>(codes + orow * codes_stride + part * 8) = make_uint2(c[0], c[1]);
+      scales[orow * scales_stride + part] = (uint8_t)sc[0];
+    }
   }
 }
 
@@ -217,9 +231,17 @@ decode_append_kernel(int B, int L, const uint16_t* __restrict__ new_latent, cons
   }
 }
 
+// Two scale blocks per pack thread (one block per thread measured 317 vs 306 us
+// at 2^20 rows).  The grids give every item its own thread up to 256
+// workgroups per compute unit (2^20 rows: 65,536 workgroups); a grid-stride
+// loop with 16 workgroups per CU ran the pack at 306 us, 32 at 295, 128 at 288,
+// one item per thread at 280.
+constexpr int kPackNB = 2;
+constexpr int64_t kStreamWgPerCu = 256;
+
 static int stream_grid(int64_t total_threads) {
   int64_t blocks = (total_threads + 255) / 256;
-  const int64_t cap = 256 * 16;               // 16 workgroups per CU, grid-stride beyond
+  const int64_t cap = 256 * kStreamWgPerCu;   // workgroups, grid-stride beyond
   return (int)(blocks < cap ? (blocks > 0 ? blocks : 1) : cap);
 }
 
@@ -238,8 +260,8 @@ extern "C" csa2_status csa2_fp4_pack(const uint16_t* x, int64_t n_rows, int32_t 
   if (n_rows == 0) return CSA2_OK;
   if (!x || !codes || !scales) return CSA2_EINVAL;
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2)) return CSA2_EALIGN;
-  const int parts = C / 32;
-  fp4_pack_kernel<<<stream_grid(n_rows * parts), 256, 0, (hipStream_t)stream>>>(
+  const int parts = C / (16 * kPackNB);
+  fp4_pack_kernel<kPackNB><<<stream_grid(n_rows * parts), 256, 0, (hipStream_t)stream>>>(
       x, n_rows, parts, x_row_stride, codes, codes_row_stride, scales, scales_row_stride, nullptr);
   return launch_status();
 }
@@ -255,8 +277,8 @@ extern "C" csa2_status csa2_fp4_pack_rows(const uint16_t* x, int64_t n_rows, int
   if (n_rows == 0) return CSA2_OK;
   if (!x || !out_rows || !codes || !scales) return CSA2_EINVAL;
   if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 2) || !aligned(out_rows, 8)) return CSA2_EALIGN;
-  const int parts = C / 32;
-  fp4_pack_kernel<<<stream_grid(n_rows * parts), 256, 0, (hipStream_t)stream>>>(
+  const int parts = C / (16 * kPackNB);
+  fp4_pack_kernel<kPackNB><<<stream_grid(n_rows * parts), 256, 0, (hipStream_t)stream>>>(
       x, n_rows, parts, x_row_stride, codes, codes_row_stride, scales, scales_row_stride, out_rows);
   return launch_status();
 }

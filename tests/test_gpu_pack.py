@@ -106,3 +106,53 @@ def test_pack_stream_1m_rows_sampled_and_round_trip():
     rc, rs = OF.fp4_pack(xs)
     assert np.array_equal(np_u8(codes[rt]), rc) and np.array_equal(np_u8(scales[rt]), rs)
     assert np.array_equal(bf16_to_f64(xb[rt]), OF.fp4_unpack(rc, rs))
+
+
+def _every_scale_rows():
+    """Blocks for every finite E4M3 scale code c: the first element fixes the block maximum (6 s_c, or
+    the largest bf16 value whose sixth still rounds to s_c, so that elements up to 6.4 s_c saturate),
+    the others run through every bf16 magnitude from 2^-14 s_c up to that maximum, with alternating
+    signs, plus zeros of both signs; every E2M1 midpoint times s_c (a bf16 value) is among them."""
+    blocks = []
+    all_bf16 = OF.bf16_to_float(np.arange(0, 0x7F80, dtype=np.uint16))        # every finite magnitude
+    for c in range(1, 0x7F):
+        s = float(OF.e4m3_decode(np.array([c]))[0])
+        above = all_bf16[(all_bf16 > 6 * s) & (all_bf16 <= 6.5 * s)]
+        codes = OF.block_scales(np.repeat(above[:, None], 16, axis=1))[:, 0] if above.size else np.array([])
+        tops = [6 * s] + ([float(above[codes == c].max())] if np.any(codes == c) else [])
+        for top in tops:
+            vals = all_bf16[(all_bf16 >= s * 2.0 ** -14) & (all_bf16 <= top)]
+            vals = np.concatenate([vals, [0.0, -0.0]])
+            sign = np.where(np.arange(vals.size) % 2 == 0, 1.0, -1.0)
+            vals = vals * sign
+            n_blk = -(-vals.size // 15)
+            pad = np.zeros(n_blk * 15)
+            pad[:vals.size] = vals
+            b = np.empty((n_blk, 16))
+            b[:, 0] = top
+            b[:, 1:] = pad.reshape(n_blk, 15)
+            blocks.append(b)
+    # scale code 0: every magnitude below half the smallest E4M3 step times 6
+    tiny = all_bf16[all_bf16 < 6 * 2.0 ** -10][-15:]
+    blocks.append(np.concatenate([[6 * 2.0 ** -11], tiny * np.where(np.arange(15) % 2, -1, 1)])[None, :])
+    b = np.concatenate(blocks)
+    n_rows = -(-b.shape[0] // 32)
+    rows = np.zeros((n_rows * 32, 16))
+    rows[:b.shape[0]] = b
+    return rows.reshape(n_rows, 512)
+
+
+def test_pack_every_scale_and_magnitude_bit_exact():
+    """The pack's E2M1 rounding (hardware FP4 conversion of the snapped quotient) against the oracle's
+    threshold rule on every finite scale code and every bf16 magnitude up to the block maximum:
+    ties to even, saturation above 6, signed zeros, zero scale."""
+    dev = device()
+    x64 = _every_scale_rows()
+    x = torch.from_numpy(x64).to(torch.bfloat16)
+    assert np.array_equal(x.to(torch.float64).numpy(), x64)          # every value is a bf16 value
+    codes, scales = _gpu_pack(x.to(dev))
+    rc, rs = OF.fp4_pack(x64)
+    assert np.array_equal(np_u8(scales), rs)
+    gc = np_u8(codes)
+    bad = np.argwhere(gc != rc)
+    assert bad.size == 0, f"{bad.shape[0]} code bytes differ, first at {bad[:4].tolist()}"
