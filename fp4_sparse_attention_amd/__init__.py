@@ -38,6 +38,7 @@ _SIGS = {
                               _c_void_p, _size_t, _c_void_p]),
     "csa2_index_full_pool_workspace_size": (_size_t, [_i32, _i64, _i32]),
     "csa2_index_full_pool_streams": (_i32, [_i32, _i64]),
+    "csa2_index_full_pool_batch_workspace_size": (_size_t, [_i32, _i64, _i32]),
     "csa2_index_full_pool": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i64, _c_void_p, _c_void_p, _c_void_p, _i32,
                                     _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _size_t, _c_void_p, _c_void_p,
                                     _c_void_p]),
@@ -447,6 +448,11 @@ def csa2_sparse_swa_decode_layers_noalloc(q_lat, codes, scales, idx, layer_idx, 
 
 def csa2_index_full_pool_workspace_size(R, T, k_pool):
     return int(lib().csa2_index_full_pool_workspace_size(R, T, k_pool))
+
+
+def csa2_index_full_pool_batch_workspace_size(rows_per_batch, T, k_pool):
+    """Workspace bytes for streaming batches of rows_per_batch rows (a larger workspace: fewer batches)."""
+    return int(lib().csa2_index_full_pool_batch_workspace_size(rows_per_batch, T, k_pool))
 
 
 def csa2_index_full_pool_streams(R, T):

@@ -1884,19 +1884,93 @@ extern "C" csa2_status csa2_topk_pool(const float* scores, int32_t R, int64_t N,
   return launch_status();
 }
 
-// Whether csa2_index_full_pool takes its streaming path for this shape (every
-// row layout does when the compact selection fits; otherwise scores go to
-// the caller's array or the workspace first, and csa2_topk_pool selects).
-static bool pool_may_stream(int32_t R, int64_t T) { return choose_path(R, T) == kCompact; }
+// Whether csa2_index_full_pool takes its streaming path: rows longer than the
+// one-workgroup selection's limit.  Short rows are scored first (into the
+// caller's array or the workspace) and csa2_topk_pool selects.
+static bool pool_may_stream(int32_t R, int64_t T) { return R > 0 && T > kSmallMax; }
+
+// The streaming selection runs over batches of rows whose candidate storage
+// (sized for the worst case, every visible position a candidate: 8 bytes per
+// position) fits the workspace.  The size query asks for batches that fit
+// kPoolBatchBytes, below 1 GB for any R (4,096 rows x 2^20 positions: 96-row
+// batches, 43 of them); a larger workspace runs fewer, larger batches (every
+// batch costs about seven launches' fixed time: at 4,096 x 262,144, ten
+// batches of 416 rows took 1.79 ms against 1.05 ms for one).  Batches of 32 or
+// more rows are whole multiples of 32 (the query-block scan's row block).
+constexpr size_t kPoolBatchBytes = size_t(896) << 20;
+
+static size_t stream_bytes(int32_t R, int64_t T) {
+  const size_t a = stream_layout(R, T, index_scan_blocks(T)).total;
+  const size_t b = stream_layout(R, T, (T + kQueryBlockPositions - 1) / kQueryBlockPositions).total;
+  return a > b ? a : b;
+}
+
+// the most rows per batch (up to R) whose storage fits `bytes`, at least one
+static int32_t stream_batch_rows(int32_t R, int64_t T, size_t bytes) {
+  int64_t rb = (int64_t)(bytes / stream_bytes(1, T));
+  if (rb >= R) rb = R;
+  if (rb > 32 && rb < R) rb -= rb % 32;
+  while (rb > 1 && stream_bytes((int32_t)rb, T) > bytes) rb -= rb > 32 ? 32 : 1;
+  return (int32_t)(rb < 1 ? 1 : rb);
+}
 
 extern "C" size_t csa2_index_full_pool_workspace_size(int32_t R, int64_t T, int32_t k_pool) {
   if (R <= 0 || T <= 0) return 0;
-  if (pool_may_stream(R, T)) return stream_layout(R, T, index_scan_blocks(T)).total;
+  if (pool_may_stream(R, T)) return stream_bytes(stream_batch_rows(R, T, kPoolBatchBytes), T);
   return align_up(csa2_topk_workspace_size(R, T, k_pool), 256) + align_up((size_t)R * T * 4, 256);
+}
+
+extern "C" size_t csa2_index_full_pool_batch_workspace_size(int32_t rows_per_batch, int64_t T, int32_t k_pool) {
+  if (rows_per_batch <= 0 || T <= 0) return 0;
+  if (pool_may_stream(rows_per_batch, T)) return stream_bytes(rows_per_batch, T);
+  return csa2_index_full_pool_workspace_size(rows_per_batch, T, k_pool);
 }
 
 extern "C" int32_t csa2_index_full_pool_streams(int32_t R, int64_t T) {
   return (R > 0 && T > 0 && pool_may_stream(R, T)) ? 1 : 0;
+}
+
+// Streaming selection of R rows (one batch).  Rows of one sequence in runs
+// (chunked prefill) share key tiles in the query-block scan, with candidate
+// blocks of 1,024 positions; otherwise each row streams its keys, blocks of 128.
+// (positions within a block are 32-bit in the query-block scan: rows of up to
+// 2^31 - 2^11 positions)
+static csa2_status stream_pool_batch(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int64_t T,
+                              const int32_t* row_seq, const int64_t* row_limit, float* scores, int32_t k_pool,
+                              int32_t k_top, int32_t* pool_idx, float* pool_scores, int32_t* top_idx, uint8_t* ws,
+                              void* scan_start, void* scan_end, hipStream_t s, const PageMap& pm) {
+  const bool qblocks = !index_scan_streams(R, row_seq) && T <= (int64_t(1) << 31) - 2048;
+  const int bsz = qblocks ? kQueryBlockPositions : kBlockPositions;
+  const int64_t nbk = qblocks ? (T + bsz - 1) / bsz : index_scan_blocks(T);
+  const StreamLayout L = stream_layout(R, T, nbk);
+  StreamRow* rows = reinterpret_cast<StreamRow*>(ws + L.rows);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
+  uint32_t* samp = reinterpret_cast<uint32_t*>(ws + L.samp);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + L.cnt);
+  uint32_t* above = reinterpret_cast<uint32_t*>(ws + L.above);
+  StreamBase* base = reinterpret_cast<StreamBase*>(ws + L.base);
+  uint2* list = reinterpret_cast<uint2*>(ws + L.list);
+  uint2* cand = reinterpret_cast<uint2*>(ws + L.cand);
+  // gather / write workgroups per row: up to 64, fewer when many rows fill the chip anyway
+  const int groups = (int)std::min<int64_t>(std::min<int64_t>(kStreamGroups, nbk), std::max<int64_t>(1, 4096 / R));
+  const int bpw = (int)((nbk + groups - 1) / groups);
+  launch_index_sample_tau(q_idx, k_idx, R, T, row_seq, row_limit, k_pool, rows, hist, samp, s, pm);
+  if (scan_start && hipEventRecord((hipEvent_t)scan_start, s) != hipSuccess) return CSA2_ELAUNCH;
+  const CandOut co{rows, hist, cand, cnt, nbk};
+  if (qblocks) {
+    launch_index_block_cand(q_idx, k_idx, R, T, row_seq, row_limit, scores, co, bsz, s, pm);
+    stream_hist_kernel<<<R, kSG, 0, s>>>(T, nbk, bsz, rows, hist, cand, cnt);
+  } else {
+    launch_index_scan(q_idx, k_idx, R, T, row_seq, row_limit, scores, &co, s, pm);
+  }
+  if (scan_end && hipEventRecord((hipEvent_t)scan_end, s) != hipSuccess) return CSA2_ELAUNCH;
+  stream_gather_kernel<<<dim3(groups, R), kSG, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, nbk, bpw, bsz, rows,
+                                                       hist, cand, cnt, above, list, k_pool, k_top, pm);
+  stream_finish_kernel<<<R, kSG, 0, s>>>(T, nbk, bpw, bsz, groups, rows, hist, above, list, cand, cnt, base, k_pool,
+                                          k_top);
+  stream_write_kernel<<<dim3(groups, R), kSG, 0, s>>>(T, nbk, bpw, bsz, rows, base, cand, cnt, k_pool, k_top,
+                                                      pool_idx, pool_scores, top_idx);
+  return launch_status();
 }
 
 static csa2_status index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int32_t B, int64_t T,
@@ -1932,43 +2006,27 @@ static csa2_status index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, i
     return csa2_topk_pool(sc, R, T, T, k_pool, k_top, nullptr, pool_idx, pool_scores, top_idx, workspace, tk,
                           stream);
   }
-  // Streaming selection.  Rows of one sequence in runs (chunked prefill) share
-  // key tiles in the query-block scan, with candidate blocks of 1,024
-  // positions; otherwise each row streams its keys, blocks of 128.
-  // (positions within a block are 32-bit in the query-block scan: rows of up to 2^31 - 2^11 positions)
-  const bool qblocks = !index_scan_streams(R, row_seq) && T <= (int64_t(1) << 31) - 2048;
-  const int bsz = qblocks ? kQueryBlockPositions : kBlockPositions;
-  const int64_t nbk = qblocks ? (T + bsz - 1) / bsz : index_scan_blocks(T);
+  // Streaming selection in batches of rows.  A batch without row_seq starts at
+  // sequence r0: its keys (dense) or its block-table rows (paged) are offset.
+  // The scan events bracket the first batch's scan start and the last one's end.
+  const int32_t rb = stream_batch_rows(R, T, workspace_bytes);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const StreamLayout L = stream_layout(R, T, nbk);
-  StreamRow* rows = reinterpret_cast<StreamRow*>(ws + L.rows);
-  uint32_t* hist = reinterpret_cast<uint32_t*>(ws + L.hist);
-  uint32_t* samp = reinterpret_cast<uint32_t*>(ws + L.samp);
-  uint32_t* cnt = reinterpret_cast<uint32_t*>(ws + L.cnt);
-  uint32_t* above = reinterpret_cast<uint32_t*>(ws + L.above);
-  StreamBase* base = reinterpret_cast<StreamBase*>(ws + L.base);
-  uint2* list = reinterpret_cast<uint2*>(ws + L.list);
-  uint2* cand = reinterpret_cast<uint2*>(ws + L.cand);
-  // gather / write workgroups per row: up to 64, fewer when many rows fill the chip anyway
-  const int groups = (int)std::min<int64_t>(std::min<int64_t>(kStreamGroups, nbk), std::max<int64_t>(1, 4096 / R));
-  const int bpw = (int)((nbk + groups - 1) / groups);
-  launch_index_sample_tau(q_idx, k_idx, R, T, row_seq, row_limit, k_pool, rows, hist, samp, s, pm);
-  if (scan_start && hipEventRecord((hipEvent_t)scan_start, s) != hipSuccess) return CSA2_ELAUNCH;
-  const CandOut co{rows, hist, cand, cnt, nbk};
-  if (qblocks) {
-    launch_index_block_cand(q_idx, k_idx, R, T, row_seq, row_limit, scores, co, bsz, s, pm);
-    stream_hist_kernel<<<R, kSG, 0, s>>>(T, nbk, bsz, rows, hist, cand, cnt);
-  } else {
-    launch_index_scan(q_idx, k_idx, R, T, row_seq, row_limit, scores, &co, s, pm);
+  for (int32_t r0 = 0; r0 < R; r0 += rb) {
+    const int32_t n = std::min(rb, R - r0);
+    const uint8_t* kb = k_idx;
+    PageMap pb = pm;
+    if (!row_seq) {
+      if (pm.table) pb.table = pm.table + (int64_t)r0 * pm.max_blocks;
+      else kb = k_idx + (int64_t)r0 * T * kIndexDim;
+    }
+    const csa2_status st = stream_pool_batch(
+        q_idx + (int64_t)r0 * kIndexDim, kb, n, T, row_seq ? row_seq + r0 : nullptr,
+        row_limit ? row_limit + r0 : nullptr, scores ? scores + (int64_t)r0 * T : nullptr, k_pool, k_top,
+        pool_idx + (int64_t)r0 * k_pool, pool_scores ? pool_scores + (int64_t)r0 * k_pool : nullptr,
+        top_idx + (int64_t)r0 * k_top, ws, r0 == 0 ? scan_start : nullptr, r0 + n >= R ? scan_end : nullptr, s, pb);
+    if (st != CSA2_OK) return st;
   }
-  if (scan_end && hipEventRecord((hipEvent_t)scan_end, s) != hipSuccess) return CSA2_ELAUNCH;
-  stream_gather_kernel<<<dim3(groups, R), kSG, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, nbk, bpw, bsz, rows,
-                                                       hist, cand, cnt, above, list, k_pool, k_top, pm);
-  stream_finish_kernel<<<R, kSG, 0, s>>>(T, nbk, bpw, bsz, groups, rows, hist, above, list, cand, cnt, base, k_pool,
-                                          k_top);
-  stream_write_kernel<<<dim3(groups, R), kSG, 0, s>>>(T, nbk, bpw, bsz, rows, base, cand, cnt, k_pool, k_top,
-                                                      pool_idx, pool_scores, top_idx);
-  return launch_status();
+  return CSA2_OK;
 }
 
 extern "C" csa2_status csa2_index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int32_t B,

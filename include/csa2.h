@@ -203,8 +203,7 @@ csa2_status csa2_topk_pool(const float* scores, int32_t R, int64_t N, int64_t ro
  * Equivalent to csa2_index_full(q_idx, k_idx, R, B, T, row_seq, row_limit,
  * scores) followed by csa2_topk_pool(scores, R, T, T, k_pool, k_top, NULL,
  * pool_idx, pool_scores, top_idx): same scores, same selections.  Unless the
- * rows are short (T <= 32,768) or R x T is too large for the candidate lists
- * (R * T > 2^30), the selection streams:
+ * rows are short (T <= 32,768), the selection streams:
  * a strided sample of each row bounds its k_pool-th score from below, the
  * scoring pass keeps only the positions at or above that bound (in position
  * order, block by block) and the selection finishes on them; the result is
@@ -215,20 +214,31 @@ csa2_status csa2_topk_pool(const float* scores, int32_t R, int64_t N, int64_t ro
  *   scores     fp32 [R][T], written (masked positions -inf), or NULL: no
  *              scores are written (the selection does not need them)
  *   workspace  >= csa2_index_full_pool_workspace_size(R, T, k_pool) bytes
- *              (when the selection streams: about R * T * 8 bytes for the
- *              candidate blocks; otherwise the Top-K workspace and room for
- *              the scores when the caller passes none)
+ *              (when the selection streams: about T * 8 bytes of candidate
+ *              blocks per row for one batch of rows; the call runs as many row
+ *              batches as needed, in order, on the stream.  The size query
+ *              asks for batches that keep the workspace below 1 GB for any R;
+ *              a larger workspace, e.g. from
+ *              csa2_index_full_pool_batch_workspace_size(R, T, k_pool) for a
+ *              single batch, runs fewer batches (each costs a few launches).
+ *              For short rows: the Top-K workspace and room for the scores
+ *              when the caller passes none)
  *   scan_start, scan_end  hipEvent_t handles or NULL: when given, recorded on
  *              the stream right before and right after the scoring kernel
- *              (to time it apart from the selection)
+ *              (to time it apart from the selection; with several row batches,
+ *              before the first batch's scan and after the last one's)
  * Other arguments as for csa2_index_full and csa2_topk_pool.
  * Errors: as those two calls; ELAUNCH also when an event cannot be recorded.
  * ------------------------------------------------------------------------- */
 size_t csa2_index_full_pool_workspace_size(int32_t R, int64_t T, int32_t k_pool);
+/* Workspace bytes for streaming batches of rows_per_batch rows of T positions
+ * (for T <= 32,768 the call does not stream: as
+ * csa2_index_full_pool_workspace_size(rows_per_batch, T, k_pool)). */
+size_t csa2_index_full_pool_batch_workspace_size(int32_t rows_per_batch, int64_t T, int32_t k_pool);
 /* 1 when csa2_index_full_pool at R rows of T positions selects during the
- * scoring pass (T > 32,768 and R * T <= 2^30: with scores NULL no score array
- * is written or read), 0 when it scores first and then selects; 0 for
- * non-positive sizes.  A host-side query, no GPU work. */
+ * scoring pass (T > 32,768: with scores NULL no score array is written or
+ * read), 0 when it scores first and then selects; 0 for non-positive sizes.
+ * A host-side query, no GPU work. */
 int32_t csa2_index_full_pool_streams(int32_t R, int64_t T);
 csa2_status csa2_index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int32_t B, int64_t T,
                                  const int32_t* row_seq, const int64_t* row_limit, float* scores,

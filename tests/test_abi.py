@@ -168,13 +168,17 @@ def test_index_full_pool_argument_errors():
     assert L.csa2_index_full_pool(*a) == 1        # R != B without row_seq
     a = list(base); a[14] = 16
     assert L.csa2_index_full_pool(*a) == 4        # workspace
-    # streaming shapes (rows longer than 32,768, R x T <= 2^30): room for the candidate blocks
+    # streaming shapes (rows longer than 32,768): room for the candidate blocks of one batch of rows; the
+    # size query keeps every shape below 1 GB (row batches), a single batch takes R x T x 8 bytes and more
     assert F.csa2_index_full_pool_workspace_size(8, 1 << 20, 16384) >= 8 * (1 << 20) * 8
-    assert F.csa2_index_full_pool_workspace_size(4096, 1 << 18, 2048) >= 4096 * (1 << 18) * 8
+    for R, T in ((4096, 1 << 18), (4096, 1 << 20), (5000, 1 << 18), (65536, 1 << 21)):
+        assert F.csa2_index_full_pool_streams(R, T)
+        assert F.csa2_index_full_pool_workspace_size(R, T, 2048) < 10 ** 9
+        assert F.csa2_index_full_pool_batch_workspace_size(R, T, 2048) >= R * T * 8
+    assert not F.csa2_index_full_pool_streams(64, 1 << 15)
     # shapes that select from scores get room for the scores the caller may not take
-    for R, T in ((64, 1 << 15), (5000, 1 << 18)):
-        assert (F.csa2_index_full_pool_workspace_size(R, T, 2048)
-                >= F.csa2_topk_workspace_size(R, T, 2048) + R * T * 4)
+    assert (F.csa2_index_full_pool_workspace_size(64, 1 << 15, 2048)
+            >= F.csa2_topk_workspace_size(64, 1 << 15, 2048) + 64 * (1 << 15) * 4)
     # scores may be null: the argument checks still run (and fail here on the workspace, before any launch)
     a = list(base); a[7] = NULL; a[14] = 16
     assert L.csa2_index_full_pool(*a) == 4
