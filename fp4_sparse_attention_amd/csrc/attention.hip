@@ -827,6 +827,14 @@ static csa2_status attention_call(int32_t L, const uint16_t* q_lat, int32_t R, i
   a.o_out = direct ? o : nullptr;
   a.lse_out = direct ? lse : nullptr;
   hipStream_t s = (hipStream_t)stream;
+  {
+    // the index slices the layers read: [0, (largest offset) + R K)
+    int64_t n_idx = 0;
+    for (int l = 0; idx && l < L; ++l) n_idx = std::max<int64_t>(n_idx, idx_off[l] + (int64_t)R * K);
+    const csa2_status dc = debug_check(row_seq, R, B, swa ? swa_start : nullptr, swa ? swa_len : nullptr,
+                                       (int64_t)L * R, S, idx, n_idx, T, s);
+    if (dc != CSA2_OK) return dc;
+  }
   launch_chunks(a, s);
   if (!direct)
     attn_combine_kernel<<<dim3(H, R, L), kCombineThreads, 0, s>>>(a.o_part, a.ml_part, a.n_chunks, R, H, o_prev,

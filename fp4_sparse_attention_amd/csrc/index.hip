@@ -792,6 +792,10 @@ extern "C" csa2_status csa2_index_full(const uint8_t* q_idx, const uint8_t* k_id
   if (!row_seq && R != B) return CSA2_EINVAL;
   if (T % 4 != 0 || T >= (int64_t(1) << 31)) return CSA2_ESHAPE;
   if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(scores, 16)) return CSA2_EALIGN;
+  {
+    const csa2_status dc = debug_check(row_seq, R, B, nullptr, nullptr, 0, 0, nullptr, 0, T, (hipStream_t)stream);
+    if (dc != CSA2_OK) return dc;
+  }
   const int64_t n_tiles = (T + kTile - 1) / kTile;
   hipStream_t s = (hipStream_t)stream;
   if (!index_scan_streams(R, row_seq)) {
@@ -812,6 +816,10 @@ extern "C" csa2_status csa2_index_reindex(const uint8_t* q_idx, const uint8_t* k
   if (!row_seq && R != B) return CSA2_EINVAL;
   if (P % 4 != 0 || T >= (int64_t(1) << 31)) return CSA2_ESHAPE;
   if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(scores, 16) || !aligned(pool, 16)) return CSA2_EALIGN;
+  {
+    const csa2_status dc = debug_check(row_seq, R, B, nullptr, nullptr, 0, 0, nullptr, 0, T, (hipStream_t)stream);
+    if (dc != CSA2_OK) return dc;
+  }
   const int64_t n_tiles = (P + kTile - 1) / kTile;
   int tpb = tiles_per_block_for(n_tiles, R);
   dim3 grid(ceil_div(n_tiles, tpb), R);
@@ -837,6 +845,10 @@ extern "C" csa2_status csa2_index_full_paged(const uint8_t* q_idx, const uint8_t
   csa2_status st = check_pages(block_table, max_blocks, page, T);
   if (st != CSA2_OK) return st;
   if (!aligned(q_idx, 16) || !aligned(k_pages, 16) || !aligned(scores, 16)) return CSA2_EALIGN;
+  {
+    const csa2_status dc = debug_check(row_seq, R, B, nullptr, nullptr, 0, 0, nullptr, 0, T, (hipStream_t)stream);
+    if (dc != CSA2_OK) return dc;
+  }
   launch_index_scan(q_idx, k_pages, R, T, row_seq, row_limit, scores, nullptr, (hipStream_t)stream,
                     PageMap{block_table, max_blocks, page});
   return launch_status();
@@ -853,6 +865,10 @@ extern "C" csa2_status csa2_index_reindex_paged(const uint8_t* q_idx, const uint
   csa2_status st = check_pages(block_table, max_blocks, page, T);
   if (st != CSA2_OK) return st;
   if (!aligned(q_idx, 16) || !aligned(k_pages, 16) || !aligned(scores, 16) || !aligned(pool, 16)) return CSA2_EALIGN;
+  {
+    const csa2_status dc = debug_check(row_seq, R, B, nullptr, nullptr, 0, 0, nullptr, 0, T, (hipStream_t)stream);
+    if (dc != CSA2_OK) return dc;
+  }
   const int64_t n_tiles = (P + kTile - 1) / kTile;
   int tpb = tiles_per_block_for(n_tiles, R);
   dim3 grid(ceil_div(n_tiles, tpb), R);

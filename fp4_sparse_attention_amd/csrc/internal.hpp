@@ -74,4 +74,17 @@ csa2_status check_pages(const int32_t* block_table, int64_t max_blocks, int32_t 
 // query-block kernel (chunked prefill) for this row layout
 bool index_scan_streams(int32_t R, const int32_t* row_seq);
 
+// Opt-in validation (the environment variable CSA2_DEBUG set to anything but
+// "0", read at every call): before its own launches a call checks its
+// device-side row_seq entries against [0, B) (an entry outside reads another
+// sequence's memory or past the arrays) and, strictly, the entries the kernels
+// would otherwise skip: window bounds outside 0 <= start, 0 <= len <= 128,
+// start + len <= S, and attention indices outside [-1, T).  It waits for the
+// check on the stream and returns CSA2_EINVAL on a bad entry, launching nothing
+// else.  Off: returns CSA2_OK at once.  (With it on, a call synchronises: not
+// for graph capture.)
+csa2_status debug_check(const int32_t* row_seq, int32_t R, int32_t B, const int32_t* swa_start,
+                        const int32_t* swa_len, int64_t n_win, int32_t S, const int32_t* idx, int64_t n_idx,
+                        int64_t T, hipStream_t s);
+
 }  // namespace csa2

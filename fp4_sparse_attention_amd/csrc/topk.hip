@@ -1988,6 +1988,10 @@ static csa2_status index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, i
   if (!workspace || workspace_bytes < csa2_index_full_pool_workspace_size(R, T, k_pool)) return CSA2_EWORKSPACE;
   if (!aligned(workspace, 256)) return CSA2_EALIGN;
   hipStream_t s = (hipStream_t)stream;
+  {
+    const csa2_status dc = debug_check(row_seq, R, B, nullptr, nullptr, 0, 0, nullptr, 0, T, s);
+    if (dc != CSA2_OK) return dc;
+  }
   if (!pool_may_stream(R, T)) {
     // short rows or very long R x T: scores first (into the workspace when the
     // caller takes none), then the selection

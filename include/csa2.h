@@ -37,6 +37,15 @@
  *     it returns a non-zero status before launching anything and leaves the
  *     outputs untouched.  CSA2_ELAUNCH reports a failed launch; device faults
  *     surface at the caller's next synchronisation.
+ *   - Debug validation: with the environment variable CSA2_DEBUG set to
+ *     anything but "0" (read at every call), the index, selection and
+ *     attention calls first check their device-side row_seq entries against
+ *     [0, B) and, strictly, window bounds and attention indices (entries the
+ *     kernels would otherwise skip: start < 0, len outside [0, 128],
+ *     start + len > S, an index outside [-1, T)); they wait for the check and
+ *     return CSA2_EINVAL on a bad entry without launching anything else.
+ *     Such calls synchronise their stream (not for graph capture).  Page ids
+ *     are not checked (the pool size is not an argument).
  *   - Indices are int32 (positions < 2^31); lse values are natural logarithms.
  *   - bf16 tensors are passed as uint16_t bit patterns, E4M3 as uint8_t.
  *   - Unless stated otherwise, every pointer must be 16-byte aligned and every
