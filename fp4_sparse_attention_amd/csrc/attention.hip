@@ -10,33 +10,32 @@
 // layer and one chunk of its keys (a run of 32-key tiles from idx, plus up to
 // one 32-row tile of the row's window), for all H <= 64 heads, so that every
 // gathered tile is dequantised once for all heads.  Wave w owns latent
-// channels [128 w, 128 w + 128):
-//   A. gather (eight tiles ahead, registers): lane (m = l % 16, g = l / 16)
-//      loads 16 code bytes and the 2 scale bytes (32 channels) of keys m and
-//      16 + m; dequantise in registers (v_cvt_scalef32_pk_f16_fp4 with unit
-//      scale -- the instruction's scale acts only as a power of two -- times the
-//      E4M3 block scale in f16; exact, <= 6 significant bits in [2^-10, 2688])
-//      into the A operands of v_mfma_f32_16x16x32_f16, store the slice key-major
-//      in LDS, and form the partial scores S^T[key][head] over the wave's 128
-//      channels;
-//   B. the four partials meet in LDS; wave w sums them for heads [16 w,
-//      16 w + 16) and runs the online softmax in the exp2 domain (one head per
-//      lane column, two cross-lane steps), publishing P and the rescale factor;
-//   C. O^T[channel][head] += X^T P^T for the wave's channels: the A operand is
-//      read from the key-major slice with ds_read_b64_tr_b16 (gfx950's
-//      transposing LDS read), B = P from LDS; fp32 accumulators in registers.
-// The loop is software-pipelined with two barriers per tile: the first region
-// holds A of tile i and the first half of C of tile i - 1, the second region B
-// of tile i and the rest of C of tile i - 1 (X and P are double-buffered), so
-// the matrix products of one tile overlap the dequantisation and softmax of
-// the next.
+// channels [128 w, 128 w + 128).  Per tile:
+//   A. the FP4 codes + scales of the tile's keys, gathered four tiles ahead into
+//      registers, are dequantised in registers (v_cvt_scalef32_pk_f16_fp4 with
+//      unit scale -- the instruction's scale acts only as a power of two --
+//      times the E4M3 block scale in f16; exact, <= 6 significant bits in
+//      [2^-10, 2688]) into the A operands of v_mfma_f32_32x32x16_f16; the wave
+//      forms the partial scores S^T[key][head] over its 128 channels, and X^T in
+//      registers with two more products against 0/1 selection matrices;
+//   B. the four partials meet in LDS; waves 0..H/16-1 sum them for 16 heads each
+//      and run the softmax in the exp2 domain (one head per lane column,
+//      cross-lane max and sum), publishing P (f16) in LDS;
+//   C. O^T[channel][head] += X^T P^T for the wave's channels, fp32 accumulators
+//      in registers.
+// Two barriers per tile: the first region holds C of tile i - 1 and A of tile i,
+// the second B of tile i, so the products of one tile overlap the
+// dequantisation of the next.
 //
 // Exactness for every finite bf16 input: each head's query is scaled by a
 // power of two that puts its largest magnitude at 2^15..2^16 before the f16
 // conversion (exact down to 2^-32 of that maximum), and the score picks the
 // power back up in its softmax scale; window rows, which are bf16 of any
-// range, go through v_mfma_f32_16x16x32_bf16 for Q K^T and, with P split into
-// a bf16 high part and a bf16 remainder, for P V.
+// range, go through v_mfma_f32_32x32x16_bf16 for Q K^T and, with P split into
+// a bf16 high part and a bf16 remainder, for P V.  Within a chunk there is no
+// rescaling: P = 2^(s - m_ref) with m_ref set 8 above the first visible tile's
+// maximum; a chunk whose scores pass m_ref + 15 (P would leave f16's range)
+// restarts with m_ref = the largest score seen.
 //
 // The chunk's unnormalised O, running max m and sum l go to the workspace; a
 // combine kernel merges the chunks (and, for a window merge, the sparse
@@ -540,8 +539,7 @@ attn_chunk_kernel(const AttnArgs a) {
 
   // ---- the pipelined loop over the sparse tiles: step j holds C of tile j - 1
   //      (its X^T kept in registers, its P in LDS) and A of tile j, then B of
-  //      tile j; the last group is peeled so that it issues no refills and loads
-  //      the window rows half way through, once its first buffers are free.
+  //      tile j; the last group is peeled so that it issues no refills.
   //      (Scheduling barriers keep each step's instructions in place.)
   uint4 xprev[8];
   auto sparse_step = [&](RawTile& raw, int j, bool refill) {
@@ -567,7 +565,6 @@ attn_chunk_kernel(const AttnArgs a) {
       const int jl = n_sp - kPrefetch;
 #pragma unroll
       for (int b = 0; b < kPrefetch; ++b) {
-        if (b == kPrefetch / 2 && n_wt > 0) load_window(w0);
         sparse_step(buf[b], jl + b, false);
       }
       pv(xprev, 0);
@@ -577,7 +574,10 @@ attn_chunk_kernel(const AttnArgs a) {
     // ---- window tiles, after the sparse ones (bf16 products; not pipelined)
     for (int i = 0; i < n_wt; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      if (i > 0) load_window(w0 + i);
+      // (the first window tile's rows are loaded here too: held through the last
+      // sparse group they pushed 25 more registers to scratch, and the chunk ran
+      // 1-5% slower)
+      if (i > 0 || n_sp > 0) load_window(w0 + i);
       __syncthreads();          // every wave is past the previous tile's P reads
       stage_window();
       __syncthreads();
