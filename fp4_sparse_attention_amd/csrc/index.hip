@@ -518,12 +518,14 @@ index_block_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict_
 // of index_stream_kernel in place of the scores.  Workgroup x covers the
 // candidate blocks [x bpc, (x + 1) bpc) (bsz positions each), wave w the
 // blocks x bpc + w, + 4, ..., each block's tiles in order.  The products take
-// the keys as the A operand and the queries as B, so lane 16 g + n holds
-// keys 4 g .. 4 g + 3 of a 16-key half tile for query row n (16 per
-// matrix-core pass): a lane tests four scores of one row, the row's four
-// lanes (n, n + 16, n + 32, n + 48) order their candidates with two lane-pair
-// exchanges, and the row's running count for the block stays in a register.
-// The dot products are the same as with the operands the other way round.
+// the keys as the A operand and the queries as B; the two 16-key halves of a
+// 32-key tile interleave by fours (half hh holds positions 8 i + 4 hh + 0..3,
+// i = 0..3), so lane 16 g + n ends up with the eight consecutive positions
+// 8 g .. 8 g + 7 of the tile for query row n: a lane tests eight scores of one
+// row, the row's four lanes (n, n + 16, n + 32, n + 48) order their candidates
+// with two lane-pair exchanges per tile, and the row's running count for the
+// block stays in a register.  The dot products are the same as with the
+// operands the other way round.
 constexpr int kCandUnroll = 2;     // tiles in flight per wave
 
 // v of lane l ^ 16 and of lane l ^ 32 (the swaps leave the lane's own value
@@ -582,9 +584,12 @@ index_block_cand_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __rest
     for (int m = 0; m < 32; ++m)
       if (!(done >> m & 1u) && s_seq[m] == seq) active |= 1u << m;
     done |= active;
-    int max_lim = -1;
+    int max_lim = -1, min_lim = Ti;
     for (int m = 0; m < 32; ++m)
-      if (active >> m & 1u) max_lim = max(max_lim, s_lim[m]);
+      if (active >> m & 1u) {
+        max_lim = max(max_lim, s_lim[m]);
+        min_lim = min(min_lim, s_lim[m]);
+      }
 
     // B operands: lane 16 g + n holds bytes 16 g .. 16 g + 15 of query row 16 mt + n
     f16x8 a[2][2];
@@ -624,10 +629,12 @@ index_block_cand_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __rest
             mapped[u] = row0 >= 0;
             uint4 v[2];
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-              v[hh] = (row0 >= 0 && p0 + 16 * hh + kn < Ti)
-                          ? load_key_part<false>(k_idx + (row0 + 16 * hh + kn) * kIndexDim + 16 * g)
+            for (int hh = 0; hh < 2; ++hh) {
+              const int off = 8 * (kn >> 2) + 4 * hh + (kn & 3);
+              v[hh] = (row0 >= 0 && p0 + off < Ti)
+                          ? load_key_part<false>(k_idx + (row0 + off) * kIndexDim + 16 * g)
                           : make_uint4(0, 0, 0, 0);
+            }
             b[u] = tile_pair(v[0], v[1]);
           }
 #pragma unroll
@@ -645,35 +652,54 @@ index_block_cand_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __rest
                 acc[hh][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[hh][0], a[mt][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
                 acc[hh][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kb[hh][1], a[mt][1], acc[hh][mt], 0, 0, 0);
               }
+            // lane 16 g + n holds positions pl .. pl + 7 of query row n: slot 4 hh + j is
+            // acc[hh][.][j]; a tile fully mapped, inside T and visible to every active row (all
+            // but the tiles at the causal edge) needs only the threshold test per score
+            const int pl = p0 + 8 * g;
+            const bool full = mapped[u] && p0 + kTile <= Ti && p0 + kTile - 1 <= min_lim;
+            const int n_t = min(8, max(0, Ti - pl));
+            const int n_in = mapped[u] ? n_t : 0;
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const int pl = p0 + 16 * hh + 4 * g;
-              const int n_t = min(4, max(0, Ti - pl));
-              const int n_in = mapped[u] ? n_t : 0;
+            for (int mt = 0; mt < 2; ++mt) {
+              const int n_vis = full ? (live[mt] ? 8 : 0) : min(n_in, max(0, lim[mt] - pl + 1));
+              uint32_t m8 = 0;
+              if (full) {
+                if (live[mt]) {
 #pragma unroll
-              for (int mt = 0; mt < 2; ++mt) {
-                const int n_vis = min(n_in, max(0, lim[mt] - pl + 1));
-                uint32_t m4 = 0;
+                  for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) m4 |= (uint32_t)((j < n_vis) & (acc[hh][mt][j] >= tf[mt])) << j;
-                const uint32_t cnt = (uint32_t)__popc(m4);
-                const uint32_t x16 = lane_xor16(cnt);
-                const uint32_t pair = cnt + x16;
-                const uint32_t x32 = lane_xor32(pair);
-                uint32_t o = at[mt] + ((g & 1) ? x16 : 0u) + ((g & 2) ? x32 : 0u);
-                at[mt] += pair + x32;
-                while (m4) {
-                  const int j = __builtin_ctz(m4);
-                  m4 &= m4 - 1u;
-                  const float sv = j == 0 ? acc[hh][mt][0] : (j == 1 ? acc[hh][mt][1] : (j == 2 ? acc[hh][mt][2] : acc[hh][mt][3]));
-                  kp_row[mt][pb + o] = make_uint2(score_key(sv), (uint32_t)(pl + j));
-                  ++o;
+                    for (int j = 0; j < 4; ++j) m8 |= (uint32_t)(acc[hh][mt][j] >= tf[mt]) << (4 * hh + j);
                 }
-                if (kOut && live[mt]) {
+              } else {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
                   for (int j = 0; j < 4; ++j)
-                    if (j < n_t) scores[(int64_t)(r0 + 16 * mt + kn) * T + pl + j] = j < n_vis ? acc[hh][mt][j] : neg_inf;
-                }
+                    m8 |= (uint32_t)((4 * hh + j < n_vis) & (acc[hh][mt][j] >= tf[mt])) << (4 * hh + j);
+              }
+              // the row's four lanes in position order: g = 0, 1, 2, 3
+              const uint32_t cnt = (uint32_t)__popc(m8);
+              const uint32_t x16 = lane_xor16(cnt);
+              const uint32_t pair = cnt + x16;
+              const uint32_t x32 = lane_xor32(pair);
+              uint32_t o = at[mt] + ((g & 1) ? x16 : 0u) + ((g & 2) ? x32 : 0u);
+              at[mt] += pair + x32;
+              while (m8) {
+                const int sl = __builtin_ctz(m8);
+                m8 &= m8 - 1u;
+                const f32x4 h = sl < 4 ? acc[0][mt] : acc[1][mt];
+                const int j = sl & 3;
+                const float sv = j == 0 ? h[0] : (j == 1 ? h[1] : (j == 2 ? h[2] : h[3]));
+                kp_row[mt][pb + o] = make_uint2(score_key(sv), (uint32_t)(pl + sl));
+                ++o;
+              }
+              if (kOut && live[mt]) {
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                  for (int j = 0; j < 4; ++j)
+                    if (4 * hh + j < n_t)
+                      scores[(int64_t)(r0 + 16 * mt + kn) * T + pl + 4 * hh + j] = 4 * hh + j < n_vis ? acc[hh][mt][j] : neg_inf;
               }
             }
           }

@@ -1907,6 +1907,9 @@ static size_t stream_bytes(int32_t R, int64_t T) {
 
 // the most rows per batch (up to R) whose storage fits `bytes`, at least one
 static int32_t stream_batch_rows(int32_t R, int64_t T, size_t bytes) {
+  // all rows at once when they fit (the per-row estimate below carries each
+  // batch's fixed part once per row, so it alone would split such a workspace)
+  if (stream_bytes(R, T) <= bytes) return R;
   int64_t rb = (int64_t)(bytes / stream_bytes(1, T));
   if (rb >= R) rb = R;
   if (rb > 32 && rb < R) rb -= rb % 32;
