@@ -25,14 +25,17 @@
 //      in registers.
 // Two barriers per tile: the first region holds C of tile i - 1 and A of tile i,
 // the second B of tile i, so the products of one tile overlap the
-// dequantisation of the next.
+// dequantisation of the next.  The first four sparse tiles' rows are gathered
+// with the query loads, with no barrier before the first tile, so that the
+// gathers' latency overlaps the query loads; the window tile comes last.
 //
-// Exactness for every finite bf16 input: each head's query is scaled by a
-// power of two that puts its largest magnitude at 2^15..2^16 before the f16
-// conversion (exact down to 2^-32 of that maximum), and the score picks the
-// power back up in its softmax scale; window rows, which are bf16 of any
-// range, go through v_mfma_f32_32x32x16_bf16 for Q K^T and, with P split into
-// a bf16 high part and a bf16 remainder, for P V.  Within a chunk there is no
+// Exactness for every finite bf16 input: each wave's slice of each head's
+// query is scaled by a power of two that puts the slice's largest magnitude at
+// 2^15..2^16 before the f16 conversion (exact down to 2^-32 of that maximum),
+// and the softmax multiplies the wave's partial score by the same power of two
+// (exact) before the four are added; window rows, which are bf16 of any range,
+// go through v_mfma_f32_32x32x16_bf16 for Q K^T and, with P split into a bf16
+// high part and a bf16 remainder, for P V.  Within a chunk there is no
 // rescaling: P = 2^(s - m_ref) with m_ref set 8 above the first visible tile's
 // maximum; a chunk whose scores pass m_ref + 15 (P would leave f16's range)
 // restarts with m_ref = the largest score seen.
@@ -56,7 +59,7 @@ constexpr int kMaxChunkTiles = 64;       // sparse tiles per chunk at most
 constexpr int kMaxChunkKeys = kMaxChunkTiles * kKT;
 constexpr int kWindowChunks = kWindowMax / kKT;   // one-tile chunks covering the longest window
 constexpr float kMaxSlack = 15.0f;       // P = 2^(s - m_ref) stays below 2^15 (f16 holds it)
-constexpr float kRefLead = 8.0f;         // the reference starts this far above the first tile's max
+constexpr float kRefLead = 8.0f;         // the reference starts this far above the first visible tile's max
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr int kPrefetch = 4;             // sparse tiles whose gathers are in flight ahead of the math (8 does not fit the registers)
@@ -140,7 +143,8 @@ struct AttnArgs {
   int window_per_chunk;           // window tiles per chunk
   int sparse_per_chunk;           // sparse tiles per chunk
   int n_chunks;
-  int n_pairs;                    // R * n_chunks (row, chunk) pairs
+  int n_wg;                       // L * R * n_chunks workgroups with work
+  int per_xcd;                    // ceil(n_wg / 8): the slice of the (row, layer, chunk) list each XCD takes
   const uint16_t* swa;            // bf16 [L][B][S][512]
   int B, S;
   const int32_t* swa_start;       // [L][R]
@@ -174,9 +178,11 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 
-// Workgroup id -> (row, chunk, layer): the eight XCDs take workgroups in turn,
-// so ids b with the same b mod 8 share an XCD; all layers of one (row, chunk)
-// get consecutive ids of one XCD and gather their rows through the same L2.
+// Workgroup id -> (row, layer, chunk): the eight XCDs take workgroup ids in
+// turn (id b runs on XCD b mod 8), and XCD x takes the x-th contiguous slice of
+// the list of (row, layer, chunk) triples, row-major, so that the chunks of one
+// row -- which read the same queries, and for layers that share an index slice
+// the same cache rows -- meet in one L2.
 //
 // Matrix-core layouts (v_mfma_f32_32x32x16_*, the full-rate shape on gfx950;
 // the 16x16x32 shape issues at about half its rate), wave w, lane l with
@@ -207,17 +213,15 @@ attn_chunk_kernel(const AttnArgs a) {
   __shared__ float s_inv_l[NH];
   __shared__ int s_restart;                   // a head's scores passed its reference by kMaxSlack
   __shared__ __attribute__((aligned(16))) float s_mask[kKT];
-  __shared__ int s_qe[4][NH];
+  __shared__ __attribute__((aligned(16))) int s_qsh[NH][4];      // query shift of (head, wave)
   __shared__ int s_pos[kMaxChunkKeys];        // this chunk's cache rows (-1: skip)
   __shared__ __attribute__((aligned(16))) uint16_t s_qw[4][NH * kQwStride];   // scaled queries, bf16
 
-  const int bid = blockIdx.x;
-  const int slot = bid >> 3;
-  const int layer = slot % a.L;
-  const int pair = (slot / a.L) * 8 + (bid & 7);
-  if (pair >= a.n_pairs) return;
-  const int r = pair / a.n_chunks;
-  const int chunk = pair - r * a.n_chunks;
+  const int wg = (int)(blockIdx.x & 7) * a.per_xcd + (int)(blockIdx.x >> 3);
+  if (wg >= a.n_wg) return;
+  const int chunk = wg % a.n_chunks;
+  const int layer = (wg / a.n_chunks) % a.L;
+  const int r = wg / (a.n_chunks * a.L);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -241,8 +245,27 @@ attn_chunk_kernel(const AttnArgs a) {
   const int k0 = sp0 * kKT;
   const int k1 = min(a.K, (sp0 + n_sp_real) * kKT);
 
-  // ---- queries (raw bf16), issued first: lane (n, h) holds channels cbase + 64 h
-  //      + [0, 64) of head 32 hb + n (zero past H)
+  // ---- loads, in the order they are issued: the index entries (this lane's key
+  //      of each tile of the first group, and the chunk's entries for s_pos),
+  //      the queries, the first window tile's rows, then -- once the first
+  //      group's entries are in -- that group's cache rows, so that the gathers'
+  //      latency overlaps the query loads (no barrier before the first tile)
+  const int32_t* idx_row = n_sp > 0 ? a.idx + a.idx_off[layer] + (int64_t)r * a.K : nullptr;
+  constexpr int kPosPerThread = kMaxChunkKeys / 256;
+  int first_pos[kPrefetch];
+  int chunk_pos[kPosPerThread];
+  // (loads are unconditional, at clamped in-bounds addresses, and masked after
+  // they return, so that no branch or wait sits between them)
+  if (n_sp > 0) {
+#pragma unroll
+    for (int j = 0; j < kPrefetch; ++j) first_pos[j] = idx_row[min(k0 + j * kKT + n, k1 - 1)];
+#pragma unroll
+    for (int u = 0; u < kPosPerThread; ++u)
+      if (256 * u < n_sp * kKT) chunk_pos[u] = idx_row[min(k0 + tid + 256 * u, k1 - 1)];
+  }
+
+  // queries (raw bf16): lane (n, h) holds channels cbase + 64 h + [0, 64) of head
+  // 32 hb + n (zero past H)
   const uint16_t* q_l = a.q_lat + (int64_t)layer * a.R * H * kLatent;
   uint4 qraw[HB][8];
 #pragma unroll
@@ -250,15 +273,12 @@ attn_chunk_kernel(const AttnArgs a) {
     const int head = 32 * hb + n;
     const uint16_t* qrow = q_l + ((int64_t)r * H + min(head, H - 1)) * kLatent + cbase + 64 * hl;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const uint4 v = *reinterpret_cast<const uint4*>(qrow + 8 * ks);
-      qraw[hb][ks] = head < H ? v : make_uint4(0, 0, 0, 0);
-    }
+    for (int ks = 0; ks < 8; ++ks) qraw[hb][ks] = *reinterpret_cast<const uint4*>(qrow + 8 * ks);
   }
 
-  // ---- window rows of tile w: lane (n, h) takes channels cbase + 64 h + [0, 64)
-  //      of row 32 w + n; rows past the window's length read an in-bounds row
-  //      (the loads are unconditional) and are zeroed where they are used
+  // window rows of tile w: lane (n, h) takes channels cbase + 64 h + [0, 64) of
+  // row 32 w + n; rows past the window's length read an in-bounds row (the loads
+  // are unconditional) and are zeroed where they are used
   uint4 wv[8];
   bool wvalid = false;
   int w_st = 0, w_ln = 0;
@@ -278,72 +298,70 @@ attn_chunk_kernel(const AttnArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) wv[ks] = p[ks];
   };
+  if (n_wt > 0 && n_sp == 0) load_window(w0);
 
-  // ---- cache rows of this chunk's sparse keys (page translation included),
-  //      staged once so that the gathers do not wait on dependent index or
-  //      page-table loads; a row of the codes array is below 2^31 (2^31 rows
-  //      would be 618 GB)
-  if (n_sp > 0) {
-    const int32_t* idx_row = a.idx + a.idx_off[layer] + (int64_t)r * a.K;
-    for (int i = tid; i < n_sp * kKT; i += 256) {
-      const int kk = k0 + i;
-      const int pos = kk < k1 ? idx_row[kk] : -1;
-      const int64_t row = (pos >= 0 && pos < a.T) ? phys_row(a.pm, seq, a.T, pos) : -1;
-      s_pos[i] = (int)row;
-    }
-  }
-  if (tid == 0) s_restart = 0;
-  // ---- per-head query exponent: the largest exponent field over the wave's
-  //      channels, then over the four waves (LDS)
-#pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    uint32_t e = 0;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) e = max(e, bf16x8_max_exp(qraw[hb][ks]));
-    auto sw32 = __builtin_amdgcn_permlane32_swap(e, e, false, false);
-    e = max(sw32[0], sw32[1]);
-    if (hl == 0) s_qe[wave][32 * hb + n] = (int)e;
-  }
-  __syncthreads();
-
-  // gather the FP4 codes + scales of sparse tile j's keys into a register buffer
-  // (every load is issued, an invalid key reading an in-bounds row, so the count
-  // of loads in flight is the same on every path)
-  auto load_tile = [&](RawTile& raw, int j) {
-    const int row = s_pos[j * kKT + n];
+  // cache row of an index entry (page translation included; -1: skip); a row
+  // of the codes array is below 2^31 (2^31 rows would be 618 GB)
+  auto cache_row = [&](int pos) -> int {
+    return (pos >= 0 && pos < a.T) ? (int)phys_row(a.pm, seq, a.T, pos) : -1;
+  };
+  // gather the FP4 codes + scales of one key into a register buffer (every load
+  // is issued, an invalid key reading an in-bounds row, so the count of loads in
+  // flight is the same on every path)
+  auto load_row = [&](RawTile& raw, int row) {
     const int64_t rr = row >= 0 ? row : 0;
     const uint4* cp = reinterpret_cast<const uint4*>(a.codes + rr * kCodesRow + 64 * wave + 32 * hl);
     raw.c0 = cp[0];
     raw.c1 = cp[1];
     raw.sc = *reinterpret_cast<const uint32_t*>(a.scales + rr * kScalesRow + 8 * wave + 4 * hl);
   };
+  // sparse tile j's key for this lane, from the staged rows
+  auto load_tile = [&](RawTile& raw, int j) { load_row(raw, s_pos[j * kKT + n]); };
   RawTile buf[kPrefetch];
+  if (n_sp > 0) {
+#pragma unroll
+    for (int j = 0; j < kPrefetch; ++j) load_row(buf[j], cache_row(k0 + j * kKT + n < k1 ? first_pos[j] : -1));
+    // the chunk's cache rows, staged once so that the later gathers do not wait
+    // on dependent index or page-table loads (visible after the barrier before
+    // the sparse tiles)
+#pragma unroll
+    for (int u = 0; u < kPosPerThread; ++u) {
+      const int i = tid + 256 * u;
+      if (i < n_sp * kKT) s_pos[i] = cache_row(k0 + i < k1 ? chunk_pos[u] : -1);
+    }
+  }
+  if (tid == 0) s_restart = 0;
 
-  // ---- queries scaled by 2^-sh (sh = largest exponent - kQTop) into f16
-  //      operands, and into bf16 in LDS for the window tiles
+  // ---- query shift of (head, wave): the largest exponent field over the wave's
+  //      128 channels of the head puts that slice's largest magnitude at
+  //      2^kQTop..2^(kQTop+1) in f16 (exact down to 2^-32 of it); the softmax
+  //      multiplies each wave's partial score by 2^shift before adding them.
+  //      Queries into f16 operands, and for window tiles into bf16 in LDS (read
+  //      only by this wave).
   f16x8 qb[HB][8];
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
-    int e = 0;
+    // a padding head (32 hb + n >= H) read head H - 1's row: zero it
+    if (32 * hb + n >= H) {
 #pragma unroll
-    for (int w2 = 0; w2 < 4; ++w2) e = max(e, s_qe[w2][32 * hb + n]);
-    const int sh = (e == 0 ? -126 : e - 127) - kQTop;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      qb[hb][ks] = bf16x8_scaled(qraw[hb][ks], sh);
-      // exact: a bf16 value keeps its 8 significant bits
-      *reinterpret_cast<bf16x8*>(&s_qw[wave][(32 * hb + n) * kQwStride + 64 * hl + 8 * ks]) =
-          bf16x8_scaled_bf16(qraw[hb][ks], sh);
+      for (int ks = 0; ks < 8; ++ks) qraw[hb][ks] = make_uint4(0, 0, 0, 0);
     }
-  }
-  // softmax scale of the head this lane owns in the softmax step (2^sh folded in)
-  float ch = 0.f;
-  if (wave < NS) {
-    int e = 0;
+    uint32_t e = 0;
 #pragma unroll
-    for (int w2 = 0; w2 < 4; ++w2) e = max(e, s_qe[w2][16 * wave + m]);
-    const int sh = (e == 0 ? -126 : e - 127) - kQTop;
-    ch = __builtin_ldexpf(a.scale_log2, sh);
+    for (int ks = 0; ks < 8; ++ks) e = max(e, bf16x8_max_exp(qraw[hb][ks]));
+    auto sw32 = __builtin_amdgcn_permlane32_swap(e, e, false, false);
+    e = max(sw32[0], sw32[1]);
+    const int sh = (e == 0 ? -126 : (int)e - 127) - kQTop;
+    if (hl == 0) s_qsh[32 * hb + n][wave] = sh;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qb[hb][ks] = bf16x8_scaled(qraw[hb][ks], sh);
+    if (n_wt > 0) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        // exact: a bf16 value keeps its 8 significant bits
+        *reinterpret_cast<bf16x8*>(&s_qw[wave][(32 * hb + n) * kQwStride + 64 * hl + 8 * ks]) =
+            bf16x8_scaled_bf16(qraw[hb][ks], sh);
+    }
   }
   // the selection matrices E_0, E_1 as B operands: lane (n, h) holds E[8 h + j][n]
   f16x8 esel[2];
@@ -456,26 +474,33 @@ attn_chunk_kernel(const AttnArgs a) {
     if (wave >= NS) return;
     const int head = 16 * wave + m;
     const int kb = 16 * (g >> 1) + 4 * (g & 1);
+    // each wave's partial score times 2^(its query shift) (exact), summed in fp32
+    const int4 shv = *reinterpret_cast<const int4*>(&s_qsh[head][0]);
+    const float fw[4] = {__builtin_ldexpf(1.f, shv.x), __builtin_ldexpf(1.f, shv.y), __builtin_ldexpf(1.f, shv.z),
+                         __builtin_ldexpf(1.f, shv.w)};
     float s[8];
     {
       const f32x4 v0 = *reinterpret_cast<const f32x4*>(&sp[0][head * kSStride + kb]);
       const f32x4 v1 = *reinterpret_cast<const f32x4*>(&sp[0][head * kSStride + kb + 8]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) { s[q] = v0[q]; s[4 + q] = v1[q]; }
+      for (int q = 0; q < 4; ++q) { s[q] = v0[q] * fw[0]; s[4 + q] = v1[q] * fw[0]; }
     }
 #pragma unroll
     for (int w2 = 1; w2 < 4; ++w2) {
       const f32x4 v0 = *reinterpret_cast<const f32x4*>(&sp[w2][head * kSStride + kb]);
       const f32x4 v1 = *reinterpret_cast<const f32x4*>(&sp[w2][head * kSStride + kb + 8]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) { s[q] += v0[q]; s[4 + q] += v1[q]; }
+      for (int q = 0; q < 4; ++q) {
+        s[q] = __builtin_fmaf(v0[q], fw[w2], s[q]);
+        s[4 + q] = __builtin_fmaf(v1[q], fw[w2], s[4 + q]);
+      }
     }
     const f32x4 mk0 = *reinterpret_cast<const f32x4*>(&s_mask[kb]);
     const f32x4 mk1 = *reinterpret_cast<const f32x4*>(&s_mask[kb + 8]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      s[q] = __builtin_fmaf(s[q], ch, mk0[q]);
-      s[4 + q] = __builtin_fmaf(s[4 + q], ch, mk1[q]);
+      s[q] = __builtin_fmaf(s[q], a.scale_log2, mk0[q]);
+      s[4 + q] = __builtin_fmaf(s[4 + q], a.scale_log2, mk1[q]);
     }
     float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
     mx = xor32_max(xor16_max(mx));
@@ -554,30 +579,29 @@ attn_chunk_kernel(const AttnArgs a) {
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
+  bool first_pass = true;
   for (;;) {
     if (n_sp > 0) {
+      // (the first pass's first group was gathered in the prologue)
+      if (!first_pass) {
 #pragma unroll
-      for (int b = 0; b < kPrefetch; ++b) load_tile(buf[b], b);
+        for (int b = 0; b < kPrefetch; ++b) load_tile(buf[b], b);
+      }
+      __syncthreads();          // the staged rows and the query shifts are visible
       for (int j = 0; j < n_sp - kPrefetch; j += kPrefetch) {
 #pragma unroll
         for (int b = 0; b < kPrefetch; ++b) sparse_step(buf[b], j + b, true);
       }
       const int jl = n_sp - kPrefetch;
 #pragma unroll
-      for (int b = 0; b < kPrefetch; ++b) {
-        sparse_step(buf[b], jl + b, false);
-      }
+      for (int b = 0; b < kPrefetch; ++b) sparse_step(buf[b], jl + b, false);
       pv(xprev, 0);
-    } else if (n_wt > 0) {
-      load_window(w0);
     }
-    // ---- window tiles, after the sparse ones (bf16 products; not pipelined)
+    // ---- window tiles, after the sparse ones (bf16 products; not pipelined);
+    //      a window-only chunk's first rows were loaded with the queries
     for (int i = 0; i < n_wt; ++i) {
       __builtin_amdgcn_sched_barrier(0);
-      // (the first window tile's rows are loaded here too: held through the last
-      // sparse group they pushed 25 more registers to scratch, and the chunk ran
-      // 1-5% slower)
-      if (i > 0 || n_sp > 0) load_window(w0 + i);
+      if (i > 0 || n_sp > 0 || !first_pass) load_window(w0 + i);
       __syncthreads();          // every wave is past the previous tile's P reads
       stage_window();
       __syncthreads();
@@ -596,6 +620,7 @@ attn_chunk_kernel(const AttnArgs a) {
       for (int hb = 0; hb < HB; ++hb) oacc[b][hb] = zero16();
     m_ref = m_seen;
     l_run = 0.f;
+    first_pass = false;
   }
 
   // ---- outputs: lane (n, h) register 4 q + i of block (b, hb) is head 32 hb + n,
@@ -782,10 +807,10 @@ static size_t partial_bytes(int32_t L, int32_t R, int32_t H, int n_chunks, size_
 
 static bool heads_ok(int32_t H) { return H == 16 || H == 32 || H == 48 || H == 64; }
 
-// One workgroup per (row, chunk, layer) with every head: eight ids per XCD turn
+// One workgroup per (row, layer, chunk) with every head; XCD x takes the x-th
+// slice of per_xcd of them
 static void launch_chunks(const AttnArgs& a, hipStream_t s) {
-  const int64_t groups = ((int64_t)a.n_pairs + 7) / 8;
-  const dim3 grid((unsigned)(8 * a.L * groups));
+  const dim3 grid((unsigned)(8 * a.per_xcd));
   if (a.H <= 32) attn_chunk_kernel<1><<<grid, 256, 0, s>>>(a);
   else attn_chunk_kernel<2><<<grid, 256, 0, s>>>(a);
 }
@@ -808,7 +833,8 @@ static csa2_status attention_call(int32_t L, const uint16_t* q_lat, int32_t R, i
   for (int l = 0; l < kMaxLayers; ++l) a.idx_off[l] = (idx && l < L) ? idx_off[l] : 0;
   a.n_sparse_tiles = p.n_sparse_tiles; a.n_window_tiles = p.n_window_tiles;
   a.window_per_chunk = p.window_per_chunk; a.sparse_per_chunk = p.sparse_per_chunk; a.n_chunks = p.n_chunks;
-  a.n_pairs = R * p.n_chunks;
+  a.n_wg = L * R * p.n_chunks;
+  a.per_xcd = (a.n_wg + 7) / 8;
   a.swa = swa; a.B = B; a.S = S; a.swa_start = swa_start; a.swa_len = swa_len;
   a.scale_log2 = softmax_scale * kLog2e;
   size_t off_ml;

@@ -257,8 +257,9 @@ csa2_status csa2_index_full_pool(const uint8_t* q_idx, const uint8_t* k_idx, int
 
 /* ---------------------------------------------------------------------------
  * Arithmetic of every attention call below: the matrix cores form q . x with
- * exact products (each head's query is scaled by a power of two into the f16
- * range, and the score takes the power back; window rows, bf16 of any range,
+ * exact products (each 128-channel slice of each head's query is scaled by a
+ * power of two into the f16 range, and its partial score takes the power back;
+ * window rows, bf16 of any range,
  * use bf16 products), add them in fp32, and run the softmax in fp32; P enters
  * the value products as f16 for cache rows (2^-11 relative) and as a bf16 pair
  * (high part + remainder, about 2^-17) for window rows.  Every finite bf16
