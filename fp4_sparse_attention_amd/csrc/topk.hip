@@ -370,19 +370,25 @@ constexpr int kSmallBins = 1 << kSmallBits;
 
 // Thread t owns the 4J consecutive slots [4J t, 4J t + 4J) of the row (4096 J
 // >= N), with their index_map entries, in registers.  The k-th largest visible
-// key tau is found by three radix digits of 12, 10 and 10 bits (from bit 31;
-// the first histogram's total is the visible count); the ordered write then
-// needs one block scan of the threads' (above tau, equal to tau) counts, since
-// thread order is slot order.  A second selection (k2 <= k, positions only)
-// reuses the keys in registers: when k2 == k it is written by the same pass.
+// key tau is found by up to three radix digits of 12, 10 and 10 bits (from bit
+// 31; the first histogram's total is the visible count), each in a histogram of
+// its own (all three cleared up front): when the boundary bin of a digit holds
+// exactly the keys still needed, the whole bin is taken and the later digits
+// are skipped (tau = one below the bin, no ties to resolve) -- after the second
+// digit this is the usual case.  The ordered write then needs one block scan of
+// the threads' (above tau, equal to tau) counts, since thread order is slot
+// order.  A second selection (k2 <= k, positions only) reuses the keys in
+// registers: when k2 == k it is written by the same pass.
 template <int J>
 __global__ void __launch_bounds__(kSmallThreads)
 topk_small_kernel(const float* __restrict__ scores, int N, int64_t stride, const int32_t* __restrict__ index_map,
                   int32_t k, int32_t* __restrict__ idx_out, float* __restrict__ score_out, int32_t k2,
                   int32_t* __restrict__ idx2_out) {
-  __shared__ uint32_t h[kSmallBins];
+  constexpr int kHistWords = kSmallBins + 2 * 1024;     // digit 0 (12 bits), digits 1 and 2 (10 bits)
+  __shared__ uint32_t hh[kHistWords];
   __shared__ uint32_t wt[16];
-  __shared__ uint32_t s_digit, s_above;
+  __shared__ uint32_t wt2[2][16];
+  __shared__ uint32_t s_res[3][3];                      // per digit: bin, keys above it, keys in it
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const float* row = scores + (int64_t)r * stride;
@@ -414,18 +420,38 @@ topk_small_kernel(const float* __restrict__ scores, int N, int64_t stride, const
     }
   }
 
+  // block scan whose wave totals go to one of two buffers, so that it needs a
+  // single barrier (a buffer is reused only two digits later, past other barriers)
+  auto scan1 = [&](uint32_t v, uint32_t* w, uint32_t& total) -> uint32_t {
+    const int lane = tid & 63, wave = tid >> 6;
+    const uint32_t inc = wave_inclusive_scan(v);
+    if (lane == 63) w[wave] = inc;
+    __syncthreads();
+    uint32_t base = 0, tot = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < 16; ++w2) {
+      const uint32_t t = w[w2];
+      base += w2 < wave ? t : 0u;
+      tot += t;
+    }
+    total = tot;
+    return base + inc - v;
+  };
+
   // radix select of tau, the k_eff-th largest visible key (k_eff = min(kk, visible))
   auto select = [&](uint32_t kk, uint32_t& tau, uint32_t& need_eq, uint32_t& k_eff) {
+    for (int i = tid; i < kHistWords; i += kSmallThreads) hh[i] = 0u;
+    __syncthreads();
     uint32_t need = 0, prefix = 0u;
     k_eff = 0;
+    bool whole_bin = false;
 #pragma unroll 1
     for (int d = 0; d < 3; ++d) {
       const int shift = d == 0 ? 20 : (d == 1 ? 10 : 0);
       const int hi = d == 0 ? 32 : (d == 1 ? 20 : 10);
       const uint32_t bmask = d == 0 ? 4095u : 1023u;
       const int nb = d == 0 ? 4096 : 1024;
-      for (int i = tid; i < nb; i += kSmallThreads) h[i] = 0u;
-      __syncthreads();
+      uint32_t* h = hh + (d == 0 ? 0 : kSmallBins + 1024 * (d - 1));
 #pragma unroll
       for (int it = 0; it < J; ++it)
 #pragma unroll
@@ -444,7 +470,7 @@ topk_small_kernel(const float* __restrict__ scores, int N, int64_t stride, const
           local += c[j];
         }
       uint32_t total;
-      const uint32_t excl = block_scan_1024(local, wt, total);
+      const uint32_t excl = scan1(local, wt2[d & 1], total);
       if (d == 0) {
         k_eff = total < kk ? total : kk;     // total = visible keys
         need = k_eff;
@@ -456,19 +482,25 @@ topk_small_kernel(const float* __restrict__ scores, int N, int64_t stride, const
         for (int j = 0; j < 4; ++j)
           if (j < per) {
             if (acc < need && need <= acc + c[j]) {
-              s_digit = (uint32_t)(nb - 1 - per * tid - j);
-              s_above = acc;
+              s_res[d][0] = (uint32_t)(nb - 1 - per * tid - j);
+              s_res[d][1] = acc;
+              s_res[d][2] = c[j];
             }
             acc += c[j];
           }
       }
       __syncthreads();
-      prefix |= s_digit << shift;
-      need -= s_above;
-      __syncthreads();
+      prefix |= s_res[d][0] << shift;
+      need -= s_res[d][1];
+      // every key of the boundary bin [prefix, prefix + 2^shift) is taken: tau
+      // one below the bin selects exactly the keys above it and the bin
+      if (need == s_res[d][2] && prefix != 0u) {
+        whole_bin = true;
+        break;
+      }
     }
-    tau = prefix;
-    need_eq = need;
+    tau = whole_bin ? prefix - 1u : prefix;
+    need_eq = whole_bin ? 0u : need;
   };
 
   // ordered write: a slot's output index is (#keys > tau before it) + min(#keys == tau before it, need_eq);
