@@ -11,21 +11,23 @@
 // one 32-row tile of the row's window), for all H <= 64 heads, so that every
 // gathered tile is dequantised once for all heads.  Wave w owns latent
 // channels [128 w, 128 w + 128).  Per tile:
-//   A. the FP4 codes + scales of the tile's keys, gathered four tiles ahead into
+//   A. the FP4 codes + scales of the tile's keys, gathered two tiles ahead into
 //      registers, are dequantised in registers (v_cvt_scalef32_pk_f16_fp4 with
 //      unit scale -- the instruction's scale acts only as a power of two --
 //      times the E4M3 block scale in f16; exact, <= 6 significant bits in
 //      [2^-10, 2688]) into the A operands of v_mfma_f32_32x32x16_f16; the wave
-//      forms the partial scores S^T[key][head] over its 128 channels, and X^T in
-//      registers with two more products against 0/1 selection matrices;
+//      forms the partial scores S^T[key][head] over its 128 channels and leaves
+//      its slice X[key][channel] in LDS;
 //   B. the four partials meet in LDS; waves 0..H/16-1 sum them for 16 heads each
-//      and run the softmax in the exp2 domain (one head per lane column,
-//      cross-lane max and sum), publishing P (f16) in LDS;
-//   C. O^T[channel][head] += X^T P^T for the wave's channels, fp32 accumulators
-//      in registers.
+//      and run the softmax in the exp2 domain (one head per lane column),
+//      publishing P (f16) in LDS; the head's running sum stays split over its
+//      four lanes until the chunk ends;
+//   C. O^T[channel][head] += X^T P^T for the wave's channels, X^T read from its
+//      LDS slice with gfx950's transposing read (ds_read_b64_tr_b16), fp32
+//      accumulators in registers.
 // Two barriers per tile: the first region holds C of tile i - 1 and A of tile i,
 // the second B of tile i, so the products of one tile overlap the
-// dequantisation of the next.  The first four sparse tiles' rows are gathered
+// dequantisation of the next.  The first two sparse tiles' rows are gathered
 // with the query loads, with no barrier before the first tile, so that the
 // gathers' latency overlaps the query loads; the window tile comes last.
 //
@@ -34,8 +36,9 @@
 // 2^15..2^16 before the f16 conversion (exact down to 2^-32 of that maximum),
 // and the softmax multiplies the wave's partial score by the same power of two
 // (exact) before the four are added; window rows, which are bf16 of any range,
-// go through v_mfma_f32_32x32x16_bf16 for Q K^T and, with P split into a bf16
-// high part and a bf16 remainder, for P V.  Within a chunk there is no
+// go through v_mfma_f32_32x32x16_bf16 for Q K^T (the same f16 query operands
+// widened to bf16, exact) and, with P split into a bf16 high part and a bf16
+// remainder, for P V.  Within a chunk there is no
 // rescaling: P = 2^(s - m_ref) with m_ref set 8 above the first visible tile's
 // maximum; a chunk whose scores pass m_ref + 15 (P would leave f16's range)
 // restarts with m_ref = the largest score seen.
@@ -54,7 +57,7 @@ namespace csa2 {
 constexpr int kKT = 32;                  // keys per tile
 constexpr int kSStride = 36;             // floats per head row of a partial-score tile
 constexpr int kPStride = 40;             // halfs per head row of P
-constexpr int kQwStride = 136;           // halfs per head row of a wave's bf16 query slice (128 + 8 pad)
+constexpr int kXStride = 144;            // halfs per key row of a wave's dequantised tile slice (128 + 16 pad)
 constexpr int kMaxChunkTiles = 64;       // sparse tiles per chunk at most
 constexpr int kMaxChunkKeys = kMaxChunkTiles * kKT;
 constexpr int kWindowChunks = kWindowMax / kKT;   // one-tile chunks covering the longest window
@@ -62,7 +65,8 @@ constexpr float kMaxSlack = 15.0f;       // P = 2^(s - m_ref) stays below 2^15 (
 constexpr float kRefLead = 8.0f;         // the reference starts this far above the first visible tile's max
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kPrefetch = 4;             // sparse tiles whose gathers are in flight ahead of the math (8 does not fit the registers)
+constexpr int kPrefetch = 2;             // sparse tiles whose gathers are in flight ahead of the math (4 ran 1.5-2 us
+                                         // slower per 4-layer call: its registers cost the tile loop more than the cover gained)
 constexpr int kMaxLayers = 8;
 constexpr int kQTop = 15;                // a head's largest |q| is scaled to [2^15, 2^16)
 
@@ -192,17 +196,14 @@ __device__ __forceinline__ f32x16 zero16() {
 //   QK:  S^T[key][head] = X[key][ch] Q^T[ch][head]; k-step ks maps k = 8 h + j
 //        to channel 128 w + 64 h + 8 ks + j (for X, lane n is key n; for Q^T
 //        it is head 32 hb + n).  The output gives lane (n, h) keys 8 q + 4 h + r
-//        of head 32 hb + n.
-//   X^T: T_b = X_{2b} E_0 + X_{2b+1} E_1 with E_s[k][n] = (n == k + 16 s)
-//        puts channel k of k-step 2 b + s in column k + 16 s: lane (n, h) gets
-//        keys 8 q + 4 h + r of channel column n (exact: one product by 1.0).
-//        Column n is channel 128 w + 64 ((n % 16) / 8) + 16 b + 8 (n / 16) + n % 8.
-//   PV:  O^T[ch][head] += X^T P^T over key steps kk: lane (n, h) supplies keys
-//        {16 kk + 4 h + r, 16 kk + 8 + 4 h + r}, r < 4 -- registers 8 kk .. 8 kk
-//        + 7 of T_b for X^T, and for P^T the same keys of head 32 hb + n, which
-//        the softmax lane (head, g = 2 kk + h) writes as one 16-byte row.
-//        Output lane (n, h) register 4 q + r is head 32 hb + n, channel
-//        128 w + 64 (q & 1) + 16 b + 8 (q >> 1) + 4 h + r.
+//        of head 32 hb + n.  The lane also writes its 64 channels of key n to
+//        the wave's slice X[key][channel] in LDS.
+//   PV:  O^T[ch][head] += X^T P^T over channel blocks b (32 channels) and key
+//        steps kk (16 keys): lane (n, h) supplies channel 32 b + n and keys
+//        16 kk + 8 h + j of X^T (two transposing LDS reads), and for P^T the
+//        same keys of head 32 hb + n, which the softmax lane (head, g = 2 kk +
+//        h) writes as one 16-byte row.  Output lane (n, h) register 4 q + r is
+//        head 32 hb + n, channel 128 w + 32 b + 8 q + 4 h + r.
 template <int HB>
 __global__ void __launch_bounds__(256, 1)
 attn_chunk_kernel(const AttnArgs a) {
@@ -215,7 +216,7 @@ attn_chunk_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float s_mask[kKT];
   __shared__ __attribute__((aligned(16))) int s_qsh[NH][4];      // query shift of (head, wave)
   __shared__ int s_pos[kMaxChunkKeys];        // this chunk's cache rows (-1: skip)
-  __shared__ __attribute__((aligned(16))) uint16_t s_qw[4][NH * kQwStride];   // scaled queries, bf16
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[4][kKT * kXStride];   // each wave's tile slice X[key][ch]
 
   const int wg = (int)(blockIdx.x & 7) * a.per_xcd + (int)(blockIdx.x >> 3);
   if (wg >= a.n_wg) return;
@@ -336,8 +337,7 @@ attn_chunk_kernel(const AttnArgs a) {
   //      128 channels of the head puts that slice's largest magnitude at
   //      2^kQTop..2^(kQTop+1) in f16 (exact down to 2^-32 of it); the softmax
   //      multiplies each wave's partial score by 2^shift before adding them.
-  //      Queries into f16 operands, and for window tiles into bf16 in LDS (read
-  //      only by this wave).
+  //      Queries into f16 operands (window tiles widen them to bf16, exact).
   f16x8 qb[HB][8];
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
@@ -355,25 +355,7 @@ attn_chunk_kernel(const AttnArgs a) {
     if (hl == 0) s_qsh[32 * hb + n][wave] = sh;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qb[hb][ks] = bf16x8_scaled(qraw[hb][ks], sh);
-    if (n_wt > 0) {
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        // exact: a bf16 value keeps its 8 significant bits
-        *reinterpret_cast<bf16x8*>(&s_qw[wave][(32 * hb + n) * kQwStride + 64 * hl + 8 * ks]) =
-            bf16x8_scaled_bf16(qraw[hb][ks], sh);
-    }
   }
-  // the selection matrices E_0, E_1 as B operands: lane (n, h) holds E[8 h + j][n]
-  f16x8 esel[2];
-  bf16x8 eselb[2];
-#pragma unroll
-  for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool one = n == 8 * hl + j + 16 * s2;
-      esel[s2][j] = one ? (_Float16)1.0f : (_Float16)0.0f;
-      eselb[s2][j] = one ? (__bf16)1.0f : (__bf16)0.0f;
-    }
 
   f32x16 oacc[4][HB];           // channel block b, head block hb
 #pragma unroll
@@ -381,13 +363,16 @@ attn_chunk_kernel(const AttnArgs a) {
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) oacc[b][hb] = zero16();
   // per softmax lane: the head's reference max (fixed by its first visible tile,
-  // or after a restart by every score seen), the largest score seen, and the sum
+  // or after a restart by every score seen), the largest score this lane saw, and
+  // this lane's part of the sum
   float m_ref = neg_inf, m_seen = neg_inf;
   float l_run = 0.f;
+  float fw[4] = {0.f, 0.f, 0.f, 0.f};
+  bool fw_ready = false;
 
-  // ---- A: partial scores of the tile into sp and its X^T operands into xt
-  //      (xt[2 b + kk]: f16 for cache tiles, bf16 for window tiles)
-  uint4 xt[8];
+  // ---- A: partial scores of the tile into sp, and the wave's slice of the tile
+  //      X[key][channel] (f16 for cache tiles, bf16 bits for window tiles) into
+  //      s_x[wave] for the PV products, which read it transposed
   auto store_partials = [&](const f32x16 (&sacc)[HB]) {
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
@@ -396,20 +381,7 @@ attn_chunk_kernel(const AttnArgs a) {
         *reinterpret_cast<f32x4*>(&sp[wave][(32 * hb + n) * kSStride + 8 * q + 4 * hl]) =
             f32x4{sacc[hb][4 * q], sacc[hb][4 * q + 1], sacc[hb][4 * q + 2], sacc[hb][4 * q + 3]};
   };
-  auto pack_xt = [&](const f32x16& t, int b, bool bf) {
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      if (!bf) {
-        const f16x8 h = {(_Float16)t[8 * kk], (_Float16)t[8 * kk + 1], (_Float16)t[8 * kk + 2], (_Float16)t[8 * kk + 3],
-                         (_Float16)t[8 * kk + 4], (_Float16)t[8 * kk + 5], (_Float16)t[8 * kk + 6], (_Float16)t[8 * kk + 7]};
-        xt[2 * b + kk] = __builtin_bit_cast(uint4, h);
-      } else {
-        const bf16x8 h = {(__bf16)t[8 * kk], (__bf16)t[8 * kk + 1], (__bf16)t[8 * kk + 2], (__bf16)t[8 * kk + 3],
-                          (__bf16)t[8 * kk + 4], (__bf16)t[8 * kk + 5], (__bf16)t[8 * kk + 6], (__bf16)t[8 * kk + 7]};
-        xt[2 * b + kk] = __builtin_bit_cast(uint4, h);
-      }
-    }
-  };
+  uint16_t* xrow = &s_x[wave][n * kXStride + 64 * hl];     // key n, this lane's 64 channels
   auto stage_sparse = [&](RawTile& raw, int j, bool refill) {
     const bool ok = s_pos[j * kKT + n] >= 0;
     // an invalid key gets scale 0 (its codes then dequantise to +-0) and a
@@ -433,15 +405,22 @@ attn_chunk_kernel(const AttnArgs a) {
         sacc[hb] = mfma32(xa0, qb[hb][2 * b], sacc[hb]);
         sacc[hb] = mfma32(xa1, qb[hb][2 * b + 1], sacc[hb]);
       }
-      f32x16 t = mfma32(xa0, esel[0], zero16());
-      t = mfma32(xa1, esel[1], t);
-      pack_xt(t, b, false);
+      *reinterpret_cast<f16x8*>(xrow + 16 * b) = xa0;
+      *reinterpret_cast<f16x8*>(xrow + 16 * b + 8) = xa1;
     }
     store_partials(sacc);
     if (wave == 0 && hl == 0) s_mask[n] = ok ? 0.f : neg_inf;
     // buffer free: refill it with the tile kPrefetch ahead (every group but the
     // last has one)
     if (refill) load_tile(raw, j + kPrefetch);
+  };
+  // f16 query operand widened to bf16 (exact: a scaled bf16 value in f16 keeps
+  // its 8 significant bits)
+  auto q_bf16 = [&](const f16x8& h) {
+    bf16x8 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (__bf16)(float)h[i];
+    return o;
   };
   auto stage_window = [&]() {
     const uint4 zero = make_uint4(0, 0, 0, 0);
@@ -450,45 +429,49 @@ attn_chunk_kernel(const AttnArgs a) {
     for (int hb = 0; hb < HB; ++hb) sacc[hb] = zero16();
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const bf16x8 xa0 = __builtin_bit_cast(bf16x8, wvalid ? wv[2 * b] : zero);
-      const bf16x8 xa1 = __builtin_bit_cast(bf16x8, wvalid ? wv[2 * b + 1] : zero);
+      const uint4 w0 = wvalid ? wv[2 * b] : zero, w1 = wvalid ? wv[2 * b + 1] : zero;
+      const bf16x8 xa0 = __builtin_bit_cast(bf16x8, w0);
+      const bf16x8 xa1 = __builtin_bit_cast(bf16x8, w1);
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
-        const uint16_t* qw = &s_qw[wave][(32 * hb + n) * kQwStride + 64 * hl + 16 * b];
-        sacc[hb] = mfma32bf(xa0, *reinterpret_cast<const bf16x8*>(qw), sacc[hb]);
-        sacc[hb] = mfma32bf(xa1, *reinterpret_cast<const bf16x8*>(qw + 8), sacc[hb]);
+        sacc[hb] = mfma32bf(xa0, q_bf16(qb[hb][2 * b]), sacc[hb]);
+        sacc[hb] = mfma32bf(xa1, q_bf16(qb[hb][2 * b + 1]), sacc[hb]);
       }
-      f32x16 t = mfma32bf(xa0, eselb[0], zero16());
-      t = mfma32bf(xa1, eselb[1], t);
-      pack_xt(t, b, true);
+      *reinterpret_cast<uint4*>(xrow + 16 * b) = w0;
+      *reinterpret_cast<uint4*>(xrow + 16 * b + 8) = w1;
     }
     store_partials(sacc);
     if (wave == 0 && hl == 0) s_mask[n] = wvalid ? 0.f : neg_inf;
   };
 
   // ---- B: softmax of the tile for heads [16 w, 16 w + 16): lane (m, g) owns head
-  //      16 w + m and keys {16 kk + 4 h + i, 16 kk + 8 + 4 h + i}, (kk, h) =
-  //      (g / 2, g % 2), i < 4 (the P^T operand order); P goes to LDS (f16, or for
-  //      a window tile bf16 high parts and bf16 remainders)
+  //      16 w + m and keys 8 g .. 8 g + 7; P goes to LDS (f16, or for a window
+  //      tile bf16 high parts and bf16 remainders)
   auto softmax = [&](bool win) {
     if (wave >= NS) return;
     const int head = 16 * wave + m;
-    const int kb = 16 * (g >> 1) + 4 * (g & 1);
-    // each wave's partial score times 2^(its query shift) (exact), summed in fp32
-    const int4 shv = *reinterpret_cast<const int4*>(&s_qsh[head][0]);
-    const float fw[4] = {__builtin_ldexpf(1.f, shv.x), __builtin_ldexpf(1.f, shv.y), __builtin_ldexpf(1.f, shv.z),
-                         __builtin_ldexpf(1.f, shv.w)};
+    const int kb = 8 * g;
+    // each wave's partial score times 2^(its query shift) (exact), summed in fp32;
+    // the four factors are read once, at the first tile (past a barrier)
+    if (!fw_ready) {
+      const int4 shv = *reinterpret_cast<const int4*>(&s_qsh[head][0]);
+      fw[0] = __builtin_ldexpf(1.f, shv.x);
+      fw[1] = __builtin_ldexpf(1.f, shv.y);
+      fw[2] = __builtin_ldexpf(1.f, shv.z);
+      fw[3] = __builtin_ldexpf(1.f, shv.w);
+      fw_ready = true;
+    }
     float s[8];
     {
       const f32x4 v0 = *reinterpret_cast<const f32x4*>(&sp[0][head * kSStride + kb]);
-      const f32x4 v1 = *reinterpret_cast<const f32x4*>(&sp[0][head * kSStride + kb + 8]);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(&sp[0][head * kSStride + kb + 4]);
 #pragma unroll
       for (int q = 0; q < 4; ++q) { s[q] = v0[q] * fw[0]; s[4 + q] = v1[q] * fw[0]; }
     }
 #pragma unroll
     for (int w2 = 1; w2 < 4; ++w2) {
       const f32x4 v0 = *reinterpret_cast<const f32x4*>(&sp[w2][head * kSStride + kb]);
-      const f32x4 v1 = *reinterpret_cast<const f32x4*>(&sp[w2][head * kSStride + kb + 8]);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(&sp[w2][head * kSStride + kb + 4]);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         s[q] = __builtin_fmaf(v0[q], fw[w2], s[q]);
@@ -496,30 +479,32 @@ attn_chunk_kernel(const AttnArgs a) {
       }
     }
     const f32x4 mk0 = *reinterpret_cast<const f32x4*>(&s_mask[kb]);
-    const f32x4 mk1 = *reinterpret_cast<const f32x4*>(&s_mask[kb + 8]);
+    const f32x4 mk1 = *reinterpret_cast<const f32x4*>(&s_mask[kb + 4]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       s[q] = __builtin_fmaf(s[q], a.scale_log2, mk0[q]);
       s[4 + q] = __builtin_fmaf(s[4 + q], a.scale_log2, mk1[q]);
     }
-    float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-    mx = xor32_max(xor16_max(mx));
-    // no rescaling of O inside the chunk: P = 2^(s - m_ref) with the reference
-    // set kRefLead above the head's first visible tile's max; a score more than
-    // kMaxSlack above the reference (P would pass 2^15) makes the workgroup redo
-    // the chunk with the largest score seen as the reference
-    if (m_ref == neg_inf && mx != neg_inf) m_ref = mx + kRefLead;
-    if (mx > m_ref + kMaxSlack) s_restart = 1;
+    // this lane's max; the head's four lanes (g) meet only where they must
+    const float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
     m_seen = fmaxf(m_seen, mx);
+    // no rescaling of O inside the chunk: P = 2^(s - m_ref) with the reference
+    // set kRefLead above the head's first visible tile's max (a cross-lane max,
+    // taken only while some head of the wave has no reference yet); a score more
+    // than kMaxSlack above the reference (P would pass 2^15) makes the workgroup
+    // redo the chunk with the largest score seen as the reference
+    if (__any(m_ref == neg_inf)) {
+      const float hm = xor32_max(xor16_max(mx));
+      if (m_ref == neg_inf && hm != neg_inf) m_ref = hm + kRefLead;
+    }
+    if (mx > m_ref + kMaxSlack) s_restart = 1;
     const float m_use = m_ref == neg_inf ? 0.f : m_ref;     // nothing visible yet: every p is 0
-    float p[8], psum = 0.f;
+    float p[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       p[q] = __builtin_amdgcn_exp2f(s[q] - m_use);
-      psum += p[q];
+      l_run += p[q];            // this lane's share of the sum (the head's lanes are added at the end)
     }
-    psum = xor32_sum(xor16_sum(psum));
-    l_run += psum;
     if (!win) {
       f16x8 ph;
 #pragma unroll
@@ -537,45 +522,53 @@ attn_chunk_kernel(const AttnArgs a) {
     }
   };
 
-  // ---- C: O^T[block b][head block hb] += X^T P^T for a tile whose X^T operands
-  //      are in xp (kind 0 f16 cache tile, 1 bf16 window tile) and whose P is in LDS
-  auto pv = [&](const uint4 (&xp)[8], int kind) {
+  // ---- C: O^T[block b][head block hb] += X^T P^T for the tile in s_x[wave]
+  //      (kind 0 f16 cache tile, 1 bf16 window tile) whose P is in LDS.  Lane
+  //      (m, G) = (l % 16, l / 16) reads with ds_read_b64_tr_b16 the keys
+  //      16 kk + 8 (G / 2) + j, j < 8, of channel 32 b + 16 (G % 2) + m: the A
+  //      operand rows are the block's channels in order, k its keys in order
+  const uint16_t* xtr = &s_x[wave][(8 * ((lane >> 4) >> 1) + ((lane & 15) >> 2)) * kXStride + 16 * ((lane >> 4) & 1) +
+                                   4 * (lane & 3)];
+  auto pv = [&](int kind) {
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
+    for (int kk = 0; kk < 2; ++kk) {
+      uint4 ph[HB], pl[HB];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      for (int hb = 0; hb < HB; ++hb) {
         const int prow = (32 * hb + n) * kPStride + 8 * (2 * kk + hl);
-        const uint4 ph = *reinterpret_cast<const uint4*>(&pp[0][prow]);
-        if (kind == 0) {
+        ph[hb] = *reinterpret_cast<const uint4*>(&pp[0][prow]);
+        if (kind == 1) pl[hb] = *reinterpret_cast<const uint4*>(&pp[1][prow]);
+      }
 #pragma unroll
-          for (int b = 0; b < 4; ++b)
-            oacc[b][hb] = mfma32(__builtin_bit_cast(f16x8, xp[2 * b + kk]), __builtin_bit_cast(f16x8, ph), oacc[b][hb]);
-        } else {
-          const uint4 pl = *reinterpret_cast<const uint4*>(&pp[1][prow]);
+      for (int b = 0; b < 4; ++b) {
+        const uint16_t* p = xtr + 16 * kk * kXStride + 32 * b;
+        const s16x4 lo = lds_tr16(p), hi = lds_tr16(p + 4 * kXStride);
+        const short x8[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const bf16x8 x = __builtin_bit_cast(bf16x8, xp[2 * b + kk]);
-            oacc[b][hb] = mfma32bf(x, __builtin_bit_cast(bf16x8, ph), oacc[b][hb]);
-            oacc[b][hb] = mfma32bf(x, __builtin_bit_cast(bf16x8, pl), oacc[b][hb]);
+        for (int hb = 0; hb < HB; ++hb) {
+          if (kind == 0) {
+            oacc[b][hb] = mfma32(__builtin_bit_cast(f16x8, x8), __builtin_bit_cast(f16x8, ph[hb]), oacc[b][hb]);
+          } else {
+            const bf16x8 x = __builtin_bit_cast(bf16x8, x8);
+            oacc[b][hb] = mfma32bf(x, __builtin_bit_cast(bf16x8, ph[hb]), oacc[b][hb]);
+            oacc[b][hb] = mfma32bf(x, __builtin_bit_cast(bf16x8, pl[hb]), oacc[b][hb]);
           }
         }
       }
+    }
   };
 
   // ---- the pipelined loop over the sparse tiles: step j holds C of tile j - 1
-  //      (its X^T kept in registers, its P in LDS) and A of tile j, then B of
+  //      (its slice still in LDS, its P in LDS) and A of tile j, then B of
   //      tile j; the last group is peeled so that it issues no refills.
   //      (Scheduling barriers keep each step's instructions in place.)
-  uint4 xprev[8];
   auto sparse_step = [&](RawTile& raw, int j, bool refill) {
     __builtin_amdgcn_sched_barrier(0);
-    if (j > 0) pv(xprev, 0);
+    if (j > 0) pv(0);           // the previous tile, whose slice s_x[wave] still holds
     stage_sparse(raw, j, refill);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
     softmax(false);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) xprev[t] = xt[t];
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -595,7 +588,7 @@ attn_chunk_kernel(const AttnArgs a) {
       const int jl = n_sp - kPrefetch;
 #pragma unroll
       for (int b = 0; b < kPrefetch; ++b) sparse_step(buf[b], jl + b, false);
-      pv(xprev, 0);
+      pv(0);
     }
     // ---- window tiles, after the sparse ones (bf16 products; not pipelined);
     //      a window-only chunk's first rows were loaded with the queries
@@ -607,7 +600,7 @@ attn_chunk_kernel(const AttnArgs a) {
       __syncthreads();
       softmax(true);
       __syncthreads();
-      pv(xt, 1);
+      pv(1);
     }
     __syncthreads();
     if (!s_restart) break;
@@ -618,13 +611,16 @@ attn_chunk_kernel(const AttnArgs a) {
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) oacc[b][hb] = zero16();
-    m_ref = m_seen;
+    m_ref = xor32_max(xor16_max(m_seen));
     l_run = 0.f;
     first_pass = false;
   }
 
+  // the head's sum over its four softmax lanes
+  l_run = xor32_sum(xor16_sum(l_run));
+
   // ---- outputs: lane (n, h) register 4 q + i of block (b, hb) is head 32 hb + n,
-  //      channel cbase + 64 (q & 1) + 16 b + 8 (q >> 1) + 4 h + i
+  //      channel cbase + 32 b + 8 q + 4 h + i
   const int64_t orow0 = ((int64_t)layer * a.R + r) * H;
   if (a.o_out) {
     // the row's only chunk and no prior: normalise here, as the combine would for one chunk
@@ -641,7 +637,7 @@ attn_chunk_kernel(const AttnArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const f32x4 v = {oacc[b][hb][4 * q], oacc[b][hb][4 * q + 1], oacc[b][hb][4 * q + 2], oacc[b][hb][4 * q + 3]};
-          *reinterpret_cast<f32x4*>(op + 64 * (q & 1) + 16 * b + 8 * (q >> 1)) =
+          *reinterpret_cast<f32x4*>(op + 32 * b + 8 * q) =
               inv > 0.f ? v * inv : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
@@ -660,7 +656,7 @@ attn_chunk_kernel(const AttnArgs a) {
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<f32x4*>(op + 64 * (q & 1) + 16 * b + 8 * (q >> 1)) =
+        *reinterpret_cast<f32x4*>(op + 32 * b + 8 * q) =
             f32x4{oacc[b][hb][4 * q], oacc[b][hb][4 * q + 1], oacc[b][hb][4 * q + 2], oacc[b][hb][4 * q + 3]};
   }
   if (wave < NS && g == 0 && 16 * wave + m < H) {
