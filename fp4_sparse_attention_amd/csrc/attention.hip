@@ -757,6 +757,61 @@ attn_combine_kernel(const float* __restrict__ o_part, const float* __restrict__ 
   if (lse_out && tid == 0) lse_out[orow] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : neg_inf;
 }
 
+// The same merge for rows of at most kCombineFew chunks (the decode shapes):
+// every thread loads every chunk's (m, l) and its four channels of every
+// partial at once, so the kernel waits for one round of loads, with no LDS or
+// barriers; the arithmetic is the general kernel's, chunk by chunk in order.
+constexpr int kCombineFew = 16;
+
+__global__ void __launch_bounds__(kCombineThreads)
+attn_combine_few_kernel(const float* __restrict__ o_part, const float* __restrict__ ml_part, int n_chunks, int R,
+                        int H, const float* __restrict__ o_prev, const float* __restrict__ lse_prev,
+                        float* __restrict__ o_out, float* __restrict__ lse_out) {
+  const int h = blockIdx.x, r = blockIdx.y, layer = blockIdx.z;
+  const int c4 = threadIdx.x * 4;
+  const int64_t base = (((int64_t)layer * R + r) * n_chunks) * H + h;       // + chunk * H
+  const int64_t orow = ((int64_t)layer * R + r) * H + h;
+  const float neg_inf = -__builtin_inff();
+  float2 ml[kCombineFew];
+  f32x4 v[kCombineFew];
+#pragma unroll
+  for (int c = 0; c < kCombineFew; ++c) {
+    if (c < n_chunks) {
+      ml[c] = *reinterpret_cast<const float2*>(ml_part + (base + (int64_t)c * H) * 2);
+      v[c] = *reinterpret_cast<const f32x4*>(o_part + (base + (int64_t)c * H) * kLatent + c4);
+    }
+  }
+  float M = neg_inf;
+#pragma unroll
+  for (int c = 0; c < kCombineFew; ++c)
+    if (c < n_chunks && ml[c].y > 0.f) M = fmaxf(M, ml[c].x);
+  float mp = neg_inf;
+  if (lse_prev) {
+    mp = lse_prev[orow] * kLog2e;
+    M = fmaxf(M, mp);
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float Lsum = 0.f;
+  if (M != neg_inf) {
+#pragma unroll
+    for (int c = 0; c < kCombineFew; ++c)
+      if (c < n_chunks && ml[c].y > 0.f) {
+        const float w = exp2f(ml[c].x - M);
+        Lsum += ml[c].y * w;
+        acc += v[c] * w;
+      }
+  }
+  if (lse_prev && mp != neg_inf) {
+    const float w = exp2f(mp - M);
+    Lsum += w;
+    acc += *reinterpret_cast<const f32x4*>(o_prev + orow * kLatent + c4) * w;
+  }
+  const f32x4 res = Lsum > 0.f ? acc * (1.f / Lsum) : f32x4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();                 // o_out / lse_out may alias o_prev / lse_prev
+  *reinterpret_cast<f32x4*>(o_out + orow * kLatent + c4) = res;
+  if (lse_out && threadIdx.x == 0) lse_out[orow] = Lsum > 0.f ? (M + log2f(Lsum)) * kLn2 : neg_inf;
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -858,7 +913,10 @@ static csa2_status attention_call(int32_t L, const uint16_t* q_lat, int32_t R, i
     if (dc != CSA2_OK) return dc;
   }
   launch_chunks(a, s);
-  if (!direct)
+  if (!direct && a.n_chunks <= kCombineFew)
+    attn_combine_few_kernel<<<dim3(H, R, L), kCombineThreads, 0, s>>>(a.o_part, a.ml_part, a.n_chunks, R, H, o_prev,
+                                                                      lse_prev, o, lse);
+  else if (!direct)
     attn_combine_kernel<<<dim3(H, R, L), kCombineThreads, 0, s>>>(a.o_part, a.ml_part, a.n_chunks, R, H, o_prev,
                                                                   lse_prev, o, lse);
   return launch_status();
