@@ -820,7 +820,7 @@ struct Plan {
   int sparse_per_chunk, window_per_chunk, n_chunks;
 };
 
-constexpr int kMinChunkTiles = kPrefetch;      // partial outputs stay small next to the gathered rows
+constexpr int kMinChunkTiles = 4;              // partial outputs stay small next to the gathered rows
 
 // Chunks per (layer, row): about one workgroup per compute unit in total, whole
 // groups of kPrefetch sparse tiles per chunk; the window tiles are spread one
