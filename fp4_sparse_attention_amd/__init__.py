@@ -28,6 +28,8 @@ _SIGS = {
     "csa2_fp4_pack": (_i32, [_c_void_p, _i64, _i32, _i64, _c_void_p, _i64, _c_void_p, _i64, _c_void_p]),
     "csa2_fp4_unpack": (_i32, [_c_void_p, _c_void_p, _i64, _i32, _c_void_p, _c_void_p]),
     "csa2_index_full": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "csa2_index_full_fp8": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i64, _c_void_p, _c_void_p, _c_void_p,
+                                   _c_void_p]),
     "csa2_index_reindex": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i64, _c_void_p, _c_void_p, _i32, _c_void_p,
                                   _c_void_p]),
     "csa2_topk_workspace_size": (_size_t, [_i32, _i64, _i32]),
@@ -171,8 +173,7 @@ def csa2_fp4_unpack(codes, scales, x, stream=None):
     _check("csa2_fp4_unpack", lib().csa2_fp4_unpack(_p(codes), _p(scales), n, C, _p(x), _stream(stream)))
 
 
-def csa2_index_full(q_idx, k_idx, scores, row_seq=None, row_limit=None, stream=None):
-    """q_idx uint8 [R, 64]; k_idx uint8 [B, T, 64]; scores fp32 [R, T] (written)."""
+def _index_full_args(q_idx, k_idx, scores, row_seq, row_limit):
     _need(q_idx, torch.uint8, "q_idx", 2)
     _need(k_idx, torch.uint8, "k_idx", 3)
     _need(scores, torch.float32, "scores", 2)
@@ -186,8 +187,22 @@ def csa2_index_full(q_idx, k_idx, scores, row_seq=None, row_limit=None, stream=N
         _need(row_seq, torch.int32, "row_seq", 1)
     if row_limit is not None:
         _need(row_limit, torch.int64, "row_limit", 1)
+    return R, B, T
+
+
+def csa2_index_full(q_idx, k_idx, scores, row_seq=None, row_limit=None, stream=None):
+    """q_idx uint8 [R, 64]; k_idx uint8 [B, T, 64]; scores fp32 [R, T] (written)."""
+    R, B, T = _index_full_args(q_idx, k_idx, scores, row_seq, row_limit)
     st = lib().csa2_index_full(_p(q_idx), _p(k_idx), R, B, T, _p(row_seq), _p(row_limit), _p(scores), _stream(stream))
     _check("csa2_index_full", st)
+
+
+def csa2_index_full_fp8(q_idx, k_idx, scores, row_seq=None, row_limit=None, stream=None):
+    """csa2_index_full's scores through the FP8 matrix instruction (approximate; see the header)."""
+    R, B, T = _index_full_args(q_idx, k_idx, scores, row_seq, row_limit)
+    st = lib().csa2_index_full_fp8(_p(q_idx), _p(k_idx), R, B, T, _p(row_seq), _p(row_limit), _p(scores),
+                                   _stream(stream))
+    _check("csa2_index_full_fp8", st)
 
 
 def csa2_index_reindex(q_idx, k_idx, pool, scores, row_seq=None, stream=None):

@@ -28,8 +28,9 @@
 namespace csa2 {
 
 // One query row per workgroup row (grid.y = R).  Used for decode (Full and
-// Reindex).  kGather: column c of row r scores position pool[r][c].
-template <bool kGather>
+// Reindex).  kGather: column c of row r scores position pool[r][c].  kFp8:
+// scores through the FP8 matrix instruction (csa2_index_full_fp8).
+template <bool kGather, bool kFp8 = false>
 __global__ void __launch_bounds__(256)
 index_rows_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx, int64_t T,
                   const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit,
@@ -46,7 +47,9 @@ index_rows_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__
   const int32_t* prow = kGather ? pool + (int64_t)r * n_cols : nullptr;
 
   f16x8 a[2];
-  query_operands(q_idx + (int64_t)r * kIndexDim, lane, a);
+  long a8[2];
+  if constexpr (kFp8) query_operands_fp8(q_idx + (int64_t)r * kIndexDim, lane, a8);
+  else query_operands(q_idx + (int64_t)r * kIndexDim, lane, a);
 
   const int64_t n_tiles = (n_cols + kTile - 1) / kTile;
   const int64_t t_begin = (int64_t)blockIdx.x * tiles_per_block;
@@ -74,7 +77,7 @@ index_rows_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t t = t0 + 4 * u;
-      const float2 sc = mfma_score(a, b[u]);
+      const float2 sc = kFp8 ? mfma_score_fp8(a8, b[u]) : mfma_score(a, b[u]);
       const int64_t c = t * kTile + kn;
       if (t < t_end && lane < 16) {
         if (c < n_cols) out[c] = ok[u][0] ? sc.x : neg_inf;
@@ -831,6 +834,26 @@ extern "C" csa2_status csa2_index_full(const uint8_t* q_idx, const uint8_t* k_id
   } else {
     launch_index_scan(q_idx, k_idx, R, T, row_seq, row_limit, scores, nullptr, s, PageMap{});
   }
+  return launch_status();
+}
+
+extern "C" csa2_status csa2_index_full_fp8(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int32_t B,
+                                           int64_t T, const int32_t* row_seq, const int64_t* row_limit,
+                                           float* scores, void* stream) {
+  if (!q_idx || !k_idx || !scores) return CSA2_EINVAL;
+  if (R <= 0 || B <= 0 || T <= 0) return CSA2_EINVAL;
+  if (!row_seq && R != B) return CSA2_EINVAL;
+  if (T % 4 != 0 || T >= (int64_t(1) << 31)) return CSA2_ESHAPE;
+  if (!aligned(q_idx, 16) || !aligned(k_idx, 16) || !aligned(scores, 16)) return CSA2_EALIGN;
+  {
+    const csa2_status dc = debug_check(row_seq, R, B, nullptr, nullptr, 0, 0, nullptr, 0, T, (hipStream_t)stream);
+    if (dc != CSA2_OK) return dc;
+  }
+  const int64_t n_tiles = (T + kTile - 1) / kTile;
+  const int tpb = tiles_per_block_for(n_tiles, R);
+  const dim3 grid(ceil_div(n_tiles, tpb), R);
+  index_rows_kernel<false, true><<<grid, 256, 0, (hipStream_t)stream>>>(q_idx, k_idx, T, row_seq, row_limit, nullptr,
+                                                                        T, scores, tpb, PageMap{});
   return launch_status();
 }
 

@@ -69,4 +69,27 @@ __device__ __forceinline__ void query_operands(const uint8_t* q_row, int lane, f
   fp8x16_to_f16(x.x, x.y, x.z, x.w, a);
 }
 
+// The FP8 matrix instruction on the same layout, for csa2_index_full_fp8 only:
+// the raw E4M3 bytes go in as operands, with no widening.  This is not the
+// arithmetic above -- the instruction does not form the exact sum of its 32
+// products (on unit-normal E4M3 data about half the scores differ from the
+// exactly rounded value, by up to about 2^-15 sum |q k|) -- so no selection in
+// this library uses it.
+__device__ __forceinline__ void query_operands_fp8(const uint8_t* q_row, int lane, long* a8) {
+  uint4 x = make_uint4(0, 0, 0, 0);
+  if ((lane & 15) == 0) x = *reinterpret_cast<const uint4*>(q_row + 16 * (lane >> 4));
+  a8[0] = (long)(((uint64_t)x.y << 32) | x.x);
+  a8[1] = (long)(((uint64_t)x.w << 32) | x.z);
+}
+
+__device__ __forceinline__ float2 mfma_score_fp8(const long* a8, const i32x8& kb) {
+  auto pair = [](int lo, int hi) { return (long)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo); };
+  f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+  c0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a8[0], pair(kb[0], kb[1]), c0, 0, 0, 0);
+  c0 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a8[1], pair(kb[2], kb[3]), c0, 0, 0, 0);
+  c1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a8[0], pair(kb[4], kb[5]), c1, 0, 0, 0);
+  c1 = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a8[1], pair(kb[6], kb[7]), c1, 0, 0, 0);
+  return make_float2(c0[0], c1[0]);
+}
+
 }  // namespace csa2

@@ -146,6 +146,20 @@ csa2_status csa2_index_full(const uint8_t* q_idx, const uint8_t* k_idx, int32_t 
                             const int32_t* row_seq, const int64_t* row_limit, float* scores,
                             void* stream);
 
+/* The same Full-mode scores through the FP8 matrix instruction
+ * (v_mfma_f32_16x16x32_fp8_fp8): the E4M3 bytes go in unconverted, for callers
+ * that accept approximate scores (MarkTechPost retelling, paragraph 3: a Full
+ * layer scores the whole context; the indexer keys are E4M3).  Arguments,
+ * layout and errors as csa2_index_full.  The instruction does not
+ * form the exact sum of its 32 products: on unit-normal E4M3 data about half
+ * the scores differ from the exactly rounded value, by up to about 2^-15 *
+ * sum_d |q_d k_d|; over arbitrary finite E4M3 bytes nearly all do, by up to
+ * about 2^-12 * sum_d |q_d k_d| (the stated bound is 2^-10 * sum_d |q_d k_d|).  The selections of this library
+ * (csa2_index_full_pool, csa2_topk on csa2_index_full scores) take exact scores
+ * and do not use it. */
+csa2_status csa2_index_full_fp8(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int32_t B, int64_t T,
+                                const int32_t* row_seq, const int64_t* row_limit, float* scores, void* stream);
+
 /* Reindex-mode scores (MarkTechPost retelling, paragraph 3: a Reindex layer
  * rescores the shared candidate set; HN summary key points: the deeper layers'
  * cost is bounded by the pool, not the context).
