@@ -111,22 +111,39 @@ topk_hist_kernel(const float* __restrict__ scores, int64_t N, int64_t stride, co
   }
 }
 
-// block-wide exclusive prefix sum of one value per thread (256 threads)
+// block-wide exclusive prefix sum of one value per thread (256 threads); the
+// wave scans run on DPP row shifts and broadcasts, not LDS lane exchanges
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* tmp /* >= 4 */, uint32_t& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_inclusive_scan(v);
   if (lane == 63) tmp[wave] = x;
   __syncthreads();
-  uint32_t base = 0;
-  for (int w = 0; w < wave; ++w) base += tmp[w];
-  total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+  const uint32_t t0 = tmp[0], t1 = tmp[1], t2 = tmp[2], t3 = tmp[3];
+  const uint32_t base = (wave > 0 ? t0 : 0u) + (wave > 1 ? t1 : 0u) + (wave > 2 ? t2 : 0u);
+  total = t0 + t1 + t2 + t3;
   __syncthreads();
   return base + x - v;
+}
+
+// the same for N values per thread at once (one pair of barriers); tmp >= 4 N
+template <int N>
+__device__ __forceinline__ void block_exclusive_scan_n(const uint32_t (&v)[N], uint32_t (&excl)[N], uint32_t* tmp,
+                                                       uint32_t (&total)[N]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t x[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    x[i] = wave_inclusive_scan(v[i]);
+    if (lane == 63) tmp[4 * i + wave] = x[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const uint32_t t0 = tmp[4 * i], t1 = tmp[4 * i + 1], t2 = tmp[4 * i + 2], t3 = tmp[4 * i + 3];
+    excl[i] = (wave > 0 ? t0 : 0u) + (wave > 1 ? t1 : 0u) + (wave > 2 ? t2 : 0u) + x[i] - v[i];
+    total[i] = t0 + t1 + t2 + t3;
+  }
+  __syncthreads();
 }
 
 // Find the digit value holding the need-th largest remaining key.
@@ -1053,6 +1070,27 @@ struct StreamBase {
   uint32_t eq[2];                        // keys == tau in the workgroups before this one
 };
 
+// What a gather workgroup hands to its row's finishing workgroup inside the
+// same launch (boundary-bin list entries, its counts above the boundary bins)
+// goes through agent-scope atomic stores and loads: they reach and read the
+// device's coherence point directly, so the hand-off needs no release fence,
+// which on this multi-XCD part writes back the writer's whole L2.
+__device__ __forceinline__ void put_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void put_agent(uint2* p, uint2 v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), ((uint64_t)v.y << 32) | v.x, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t get_agent(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint2 get_agent(const uint2* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<uint2*>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_uint2((uint32_t)v, (uint32_t)(v >> 32));
+}
+
 // the need-th largest of n keys (need in [1, n]); returns it and sets rank_gt
 // to the number of keys above it.  256 threads; keys in LDS or global memory.
 __device__ uint32_t kth_largest_256(const uint32_t* keys, uint32_t n, uint32_t need, uint32_t* h /* 4096 */,
@@ -1185,12 +1223,15 @@ __device__ __forceinline__ void bins_from_top(const uint32_t* hr, const uint32_t
                                               uint32_t& total) {
   const int tid = threadIdx.x;
   constexpr int kPer = kStreamBins / kSG;
-  uint32_t c[kPer], local = 0;
+  static_assert(kPer == 16, "four 16-byte loads per thread");
+  // thread tid's bins 4095 - 16 tid - j (j < 16): one contiguous 64-byte run, loaded as four vectors
+  const uint4* h4 = reinterpret_cast<const uint4*>(hr + (kStreamBins - kPer * (tid + 1)));
+  const uint4 v0 = h4[0], v1 = h4[1], v2 = h4[2], v3 = h4[3];
+  const uint32_t c[kPer] = {v3.w, v3.z, v3.y, v3.x, v2.w, v2.z, v2.y, v2.x,
+                            v1.w, v1.z, v1.y, v1.x, v0.w, v0.z, v0.y, v0.x};
+  uint32_t local = 0;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    c[j] = hr[kStreamBins - 1 - kPer * tid - j];
-    local += c[j];
-  }
+  for (int j = 0; j < kPer; ++j) local += c[j];
   const uint32_t excl = block_exclusive_scan(local, tmp, total);
   if (tid == 0)
     for (int i = 0; i < 6; ++i) s_b[i] = 0u;
@@ -1314,57 +1355,6 @@ stream_hist_kernel(int64_t T, int64_t nbk, int bsz, const StreamRow* __restrict_
   for (int i = tid; i < kStreamBins; i += kSG) hr[i] = h[i];
 }
 
-// gather: per workgroup, the candidates above each boundary bin in its blocks,
-// and the candidates inside the boundary bin appended to the row's short list;
-// in a row to rebuild, the rebuild of its blocks instead
-__global__ void __launch_bounds__(kSG)
-stream_gather_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx, int64_t T,
-                     const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit, int64_t nbk, int bpw,
-                     int bsz, StreamRow* __restrict__ rows, uint32_t* __restrict__ hist, uint2* __restrict__ cand,
-                     uint32_t* __restrict__ cand_cnt, uint32_t* __restrict__ above_out, uint2* __restrict__ list,
-                     int32_t k, int32_t k2, PageMap pm) {
-  __shared__ uint32_t tmp[8];
-  __shared__ uint32_t s_b[6];
-  __shared__ uint32_t h[kStreamBins];
-  const int r = blockIdx.y, g = blockIdx.x, G = gridDim.x, tid = threadIdx.x;
-  const int R = gridDim.y;
-  const uint32_t tau_s = rows[r].tau_s, sh = rows[r].sh;
-  uint2* kp = cand + (int64_t)r * T;
-  uint32_t* cn = cand_cnt + (int64_t)r * nbk;
-  uint32_t* hr = hist + (int64_t)r * kStreamHistWords;
-  // the first block's head is loaded with the histogram
-  const int64_t blk0 = (int64_t)g * bpw, blk1 = min(nbk, blk0 + bpw);
-  BlockHead hd0 = {};
-  if (blk0 + tid < blk1) hd0 = load_head(kp, cn, blk0 + tid, bsz);
-  const RowBins rb = row_bins(hr, tau_s, k, k2, tmp, s_b);
-  if (rb.rebuild) {
-    rebuild_blocks(q_idx, k_idx, T, r, row_seq, row_limit, blk0, blk1, bsz, kp, cn, hr + kStreamBins, h, pm);
-    return;
-  }
-  if (rb.overflow || rb.k_eff[0] == 0u) return;
-  uint32_t ab[2] = {0u, 0u};
-  for (int64_t blk = blk0 + tid; blk < blk1; blk += kSG) {
-    const BlockHead hd = blk == blk0 + tid ? hd0 : load_head(kp, cn, blk, bsz);
-    for_block(hd, kp, blk, bsz, [&](uint32_t kx, int32_t p) {
-      const uint32_t d = min((kx - tau_s) >> sh, (uint32_t)(kStreamBins - 1));
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        if (d > rb.b0[s]) ++ab[s];
-        if (d == rb.b0[s]) {
-          const uint32_t i = atomicAdd(&rows[r].n_list[s], 1u);
-          list[((int64_t)s * R + r) * kListCap + i] = make_uint2(kx, (uint32_t)p);
-        }
-      }
-    });
-  }
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    uint32_t tot;
-    block_exclusive_scan(ab[s], tmp, tot);
-    if (tid == 0) above_out[((int64_t)r * G + g) * 2 + s] = tot;
-  }
-}
-
 // the need-th largest key among a row's candidate blocks that pass `keep`,
 // starting from a known prefix: radix digits of the bits below bit `hi`
 // (11 bits and then 10 at a time), prefix bits at and above `hi` must match.
@@ -1419,39 +1409,54 @@ __device__ uint32_t select_in_blocks(const uint2* kp, const uint32_t* cn, int64_
   return prefix;
 }
 
-// finish: one workgroup per row.  From the short lists: each selection's k-th
-// key tau (kth_largest_256), the ties at tau it takes, and for every gather
+// finish of row r, by the row's last gather workgroup.  From the short lists:
+// each selection's k-th key tau, the ties at tau it takes, and for every gather
 // workgroup the keys above tau and equal to tau in the blocks before it.  In a
 // rebuilt or overflowing row, the k-th keys by radix passes over the blocks and
 // the per-workgroup counts by a pass over them.
-__global__ void __launch_bounds__(kSG)
-stream_finish_kernel(int64_t T, int64_t nbk, int bpw, int bsz, int G, StreamRow* __restrict__ rows,
-                     const uint32_t* __restrict__ hist, const uint32_t* __restrict__ above_out,
-                     const uint2* __restrict__ list, const uint2* __restrict__ cand,
-                     const uint32_t* __restrict__ cand_cnt, StreamBase* __restrict__ base_out, int32_t k,
-                     int32_t k2) {
-  __shared__ uint32_t tmp[8];
-  __shared__ uint32_t s_b[6];
-  __shared__ uint32_t res[2];
-  __shared__ uint32_t h[kStreamBins];
-  __shared__ uint32_t s_lk[kListCap];
-  __shared__ uint32_t s_gt[kStreamGroups], s_eq[kStreamGroups];
-  __shared__ uint32_t res2[4];
-  const int r = blockIdx.x, tid = threadIdx.x;
-  const int R = gridDim.x;
-  const StreamRow st = rows[r];
+struct FinishLds {
+  uint32_t* tmp;     // 8
+  uint32_t* s_b;     // 6
+  uint32_t* res;     // 2
+  uint32_t* h;       // kStreamBins
+  uint32_t* s_lk;    // kListCap, 16-byte aligned
+  uint32_t* s_gt;    // kStreamGroups
+  uint32_t* s_eq;    // kStreamGroups
+  uint32_t* res2;    // 4
+};
+
+__device__ void finish_row(int r, int R, int64_t T, int64_t nbk, int bpw, int bsz, int G, StreamRow* __restrict__ rows,
+                           const uint32_t* __restrict__ hist, const uint32_t* __restrict__ above_out,
+                           const uint2* __restrict__ list, const uint2* __restrict__ cand,
+                           const uint32_t* __restrict__ cand_cnt, StreamBase* __restrict__ base_out, int32_t k,
+                           int32_t k2, const RowBins& rb, const FinishLds& lds) {
+  uint32_t* tmp = lds.tmp;
+  uint32_t* s_b = lds.s_b;
+  uint32_t* res = lds.res;
+  uint32_t* h = lds.h;
+  uint32_t* s_lk = lds.s_lk;
+  uint32_t* s_gt = lds.s_gt;
+  uint32_t* s_eq = lds.s_eq;
+  uint32_t* res2 = lds.res2;
+  const int tid = threadIdx.x;
+  struct {
+    uint32_t tau_s, sh, n_list[2];
+  } st;
+  st.tau_s = rows[r].tau_s;
+  st.sh = rows[r].sh;
+  st.n_list[0] = get_agent(&rows[r].n_list[0]);
+  st.n_list[1] = get_agent(&rows[r].n_list[1]);
   const uint32_t* hr = hist + (int64_t)r * kStreamHistWords;
   const uint2* kp = cand + (int64_t)r * T;
   const uint32_t* cn = cand_cnt + (int64_t)r * nbk;
-  // entry tid of each list and workgroup tid's gather counts, loaded with the histogram
+  // entry tid of each list and workgroup tid's gather counts
   uint2 le0[2];
   uint32_t ab0[2];
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    le0[s] = list[((int64_t)s * R + r) * kListCap + tid];
-    ab0[s] = tid < G ? above_out[((int64_t)r * G + tid) * 2 + s] : 0u;
+    le0[s] = get_agent(&list[((int64_t)s * R + r) * kListCap + tid]);
+    ab0[s] = tid < G ? get_agent(&above_out[((int64_t)r * G + tid) * 2 + s]) : 0u;
   }
-  const RowBins rb = row_bins(hr, st.tau_s, k, k2, tmp, s_b);
   StreamBase* bo = base_out + (int64_t)r * G;
   const uint32_t kk[2] = {(uint32_t)k, (uint32_t)k2};
   uint32_t tau[2] = {0u, 0u}, need_eq[2] = {0u, 0u}, k_eff[2] = {rb.k_eff[0], rb.k_eff[1]};
@@ -1463,25 +1468,34 @@ stream_finish_kernel(int64_t T, int64_t nbk, int bpw, int bsz, int G, StreamRow*
     // ranks it by counting, and the workgroup counts follow in the same pass
     uint32_t* lk1 = s_lk + kSG;
     uint32_t* gts = s_gt;                         // [2][kStreamGroups] in s_gt / s_eq pairs below
-    if (tid < (int)st.n_list[0]) s_lk[tid] = le0[0].x;
-    if (tid < (int)st.n_list[1]) lk1[tid] = le0[1].x;
+    // entries past a list's end are 0, which no visible key equals or falls below
+    s_lk[tid] = tid < (int)st.n_list[0] ? le0[0].x : 0u;
+    lk1[tid] = tid < (int)st.n_list[1] ? le0[1].x : 0u;
     for (int i = tid; i < kStreamGroups; i += kSG) { s_gt[i] = 0u; s_eq[i] = 0u; h[i] = 0u; h[kStreamGroups + i] = 0u; }
     if (tid < 4) res2[tid] = 0u;
     __syncthreads();
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const uint32_t n = st.n_list[s], need = rb.k_eff[s] - rb.above[s];
-      const uint32_t* lk = s == 0 ? s_lk : lk1;
-      const uint32_t mine = le0[s].x;
-      uint32_t gt = 0u, eq = 0u;
-      for (uint32_t j = 0; j < n; ++j) {
-        const uint32_t o = lk[j];
-        gt += o > mine;
-        eq += o == mine;
+    {
+      // both lists in one pass, four entries per LDS read and several reads in flight
+      const uint4* l0 = reinterpret_cast<const uint4*>(s_lk);
+      const uint4* l1 = reinterpret_cast<const uint4*>(lk1);
+      const uint32_t n4 = (max(st.n_list[0], st.n_list[1]) + 3u) >> 2;
+      const uint32_t m0 = le0[0].x, m1 = le0[1].x;
+      uint32_t gt[2] = {0u, 0u}, eq[2] = {0u, 0u};
+#pragma unroll 4
+      for (uint32_t j = 0; j < n4; ++j) {
+        const uint4 a = l0[j], b = l1[j];
+        gt[0] += (uint32_t)(a.x > m0) + (uint32_t)(a.y > m0) + (uint32_t)(a.z > m0) + (uint32_t)(a.w > m0);
+        eq[0] += (uint32_t)(a.x == m0) + (uint32_t)(a.y == m0) + (uint32_t)(a.z == m0) + (uint32_t)(a.w == m0);
+        gt[1] += (uint32_t)(b.x > m1) + (uint32_t)(b.y > m1) + (uint32_t)(b.z > m1) + (uint32_t)(b.w > m1);
+        eq[1] += (uint32_t)(b.x == m1) + (uint32_t)(b.y == m1) + (uint32_t)(b.z == m1) + (uint32_t)(b.w == m1);
       }
-      if (tid < (int)n && gt < need && need <= gt + eq) {
-        res2[2 * s] = mine;
-        res2[2 * s + 1] = gt;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const uint32_t n = st.n_list[s], need = rb.k_eff[s] - rb.above[s];
+        if (tid < (int)n && gt[s] < need && need <= gt[s] + eq[s]) {
+          res2[2 * s] = le0[s].x;
+          res2[2 * s + 1] = gt[s];
+        }
       }
     }
     __syncthreads();
@@ -1519,7 +1533,7 @@ stream_finish_kernel(int64_t T, int64_t nbk, int bpw, int bsz, int G, StreamRow*
     for (int s = 0; s < 2; ++s) {
       const uint32_t n = st.n_list[s];
       const uint2* ls = list + ((int64_t)s * R + r) * kListCap;
-      for (uint32_t i = tid; i < n; i += kSG) s_lk[i] = i == (uint32_t)tid ? le0[s].x : ls[i].x;
+      for (uint32_t i = tid; i < n; i += kSG) s_lk[i] = i == (uint32_t)tid ? le0[s].x : get_agent(&ls[i]).x;
       for (int i = tid; i < G; i += kSG) { s_gt[i] = 0u; s_eq[i] = 0u; }
       __syncthreads();
       const uint32_t need = rb.k_eff[s] - rb.above[s];
@@ -1527,7 +1541,7 @@ stream_finish_kernel(int64_t T, int64_t nbk, int bpw, int bsz, int G, StreamRow*
       tau[s] = kth_largest_256(s_lk, n, need, h, tmp, res, gt_in_list);
       need_eq[s] = need - gt_in_list;
       for (uint32_t i = tid; i < n; i += kSG) {
-        const int32_t p = (int32_t)(i == (uint32_t)tid ? le0[s].y : ls[i].y);
+        const int32_t p = (int32_t)(i == (uint32_t)tid ? le0[s].y : get_agent(&ls[i]).y);
         const uint32_t wg = (uint32_t)(((int64_t)p / bsz) / bpw);
         if (s_lk[i] > tau[s]) atomicAdd(&s_gt[wg], 1u);
         else if (s_lk[i] == tau[s]) atomicAdd(&s_eq[wg], 1u);
@@ -1621,13 +1635,95 @@ stream_finish_kernel(int64_t T, int64_t nbk, int bpw, int bsz, int G, StreamRow*
   }
 }
 
+// the gather pass over blocks [blk0, blk1) of row r: each boundary bin's
+// entries appended to its list, and the workgroup's counts above the boundary
+// bins, both handed to the finishing workgroup with agent-scope stores
+__device__ __forceinline__ void gather_blocks(StreamRow* rows, int r, int R, int G, int g, int64_t blk0, int64_t blk1,
+                                              int bsz, const uint2* kp, const uint32_t* cn, const BlockHead& hd0,
+                                              uint32_t tau_s, uint32_t sh, const RowBins& rb, uint2* list,
+                                              uint32_t* above_out, uint32_t* tmp) {
+  const int tid = threadIdx.x;
+  uint32_t ab[2] = {0u, 0u};
+  for (int64_t blk = blk0 + tid; blk < blk1; blk += kSG) {
+    const BlockHead hd = blk == blk0 + tid ? hd0 : load_head(kp, cn, blk, bsz);
+    for_block(hd, kp, blk, bsz, [&](uint32_t kx, int32_t p) {
+      const uint32_t d = min((kx - tau_s) >> sh, (uint32_t)(kStreamBins - 1));
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        if (d > rb.b0[s]) ++ab[s];
+        if (d == rb.b0[s]) {
+          const uint32_t i = atomicAdd(&rows[r].n_list[s], 1u);
+          put_agent(&list[((int64_t)s * R + r) * kListCap + i], make_uint2(kx, (uint32_t)p));
+        }
+      }
+    });
+  }
+  {
+    uint32_t ex[2], tot[2];
+    block_exclusive_scan_n<2>(ab, ex, tmp, tot);
+    if (tid == 0) {
+      put_agent(&above_out[((int64_t)r * G + g) * 2], tot[0]);
+      put_agent(&above_out[((int64_t)r * G + g) * 2 + 1], tot[1]);
+    }
+  }
+}
+
+// gather: per workgroup, the candidates above each boundary bin in its blocks,
+// and the candidates inside the boundary bin appended to the row's short list;
+// in a row to rebuild, the rebuild of its blocks instead.  The row's last
+// workgroup to arrive (a ticket in the row's state, cleared by the threshold
+// kernel) then finishes the row.
+__global__ void __launch_bounds__(kSG)
+stream_gather_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx, int64_t T,
+                     const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit, int64_t nbk, int bpw,
+                     int bsz, StreamRow* __restrict__ rows, uint32_t* __restrict__ hist, uint2* __restrict__ cand,
+                     uint32_t* __restrict__ cand_cnt, uint32_t* __restrict__ above_out, uint2* __restrict__ list,
+                     StreamBase* __restrict__ base_out, int32_t k, int32_t k2, PageMap pm) {
+  __shared__ uint32_t tmp[8];
+  __shared__ uint32_t s_b[6];
+  __shared__ uint32_t h[kStreamBins];
+  __shared__ uint32_t res[2];
+  __shared__ __align__(16) uint32_t s_lk[kListCap];
+  __shared__ uint32_t s_gt[kStreamGroups], s_eq[kStreamGroups];
+  __shared__ uint32_t res2[4];
+  __shared__ uint32_t s_last;
+  const int r = blockIdx.y, g = blockIdx.x, G = gridDim.x, tid = threadIdx.x;
+  const int R = gridDim.y;
+  const uint32_t tau_s = rows[r].tau_s, sh = rows[r].sh;
+  uint2* kp = cand + (int64_t)r * T;
+  uint32_t* cn = cand_cnt + (int64_t)r * nbk;
+  uint32_t* hr = hist + (int64_t)r * kStreamHistWords;
+  // the first block's head is loaded with the histogram
+  const int64_t blk0 = (int64_t)g * bpw, blk1 = min(nbk, blk0 + bpw);
+  BlockHead hd0 = {};
+  if (blk0 + tid < blk1) hd0 = load_head(kp, cn, blk0 + tid, bsz);
+  const RowBins rb = row_bins(hr, tau_s, k, k2, tmp, s_b);
+  if (rb.rebuild) {
+    rebuild_blocks(q_idx, k_idx, T, r, row_seq, row_limit, blk0, blk1, bsz, kp, cn, hr + kStreamBins, h, pm);
+    // the rebuilt blocks and counts are plain stores: publish them (rare path)
+    __threadfence();
+  } else if (!rb.overflow && rb.k_eff[0] != 0u) {
+    gather_blocks(rows, r, R, G, g, blk0, blk1, bsz, kp, cn, hd0, tau_s, sh, rb, list, above_out, tmp);
+  }
+  // every thread's hand-off stores have completed before the ticket is taken
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(&rows[r].ticket, 1u) == (uint32_t)(G - 1) ? 1u : 0u;
+  __syncthreads();
+  if (s_last == 0u) return;
+  if (rb.rebuild) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const FinishLds lds{tmp, s_b, res, h, s_lk, s_gt, s_eq, res2};
+  finish_row(r, R, T, nbk, bpw, bsz, G, rows, hist, above_out, list, cand, cand_cnt, base_out, k, k2, rb, lds);
+}
+
+
 // ordered write: each workgroup's blocks, thread t taking a contiguous run of them
 __global__ void __launch_bounds__(kSG)
 stream_write_kernel(int64_t T, int64_t nbk, int bpw, int bsz, const StreamRow* __restrict__ rows,
                     const StreamBase* __restrict__ base, const uint2* __restrict__ cand,
                     const uint32_t* __restrict__ cand_cnt, int32_t k, int32_t k2, int32_t* __restrict__ idx_out,
                     float* __restrict__ score_out, int32_t* __restrict__ idx2_out) {
-  __shared__ uint32_t tmp[8];
+  __shared__ uint32_t tmp[16];
   const int r = blockIdx.y, g = blockIdx.x, G = gridDim.x, tid = threadIdx.x;
   const uint2* kp = cand + (int64_t)r * T;
   const uint32_t* cn = cand_cnt + (int64_t)r * nbk;
@@ -1660,11 +1756,15 @@ stream_write_kernel(int64_t T, int64_t nbk, int bpw, int bsz, const StreamRow* _
       }
     });
   uint32_t gs[2], es[2];
+  {
+    const uint32_t v[4] = {gt[0], eq[0], gt[1], eq[1]};
+    uint32_t ex[4], tot[4];
+    block_exclusive_scan_n<4>(v, ex, tmp, tot);
 #pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    uint32_t tot;
-    gs[s] = bs.gt[s] + block_exclusive_scan(gt[s], tmp, tot);
-    es[s] = bs.eq[s] + block_exclusive_scan(eq[s], tmp, tot);
+    for (int s = 0; s < 2; ++s) {
+      gs[s] = bs.gt[s] + ex[2 * s];
+      es[s] = bs.eq[s] + ex[2 * s + 1];
+    }
   }
   for (int64_t blk = my0; blk < my1; ++blk)
     for_block(blk == my0 ? hd0 : load_head(kp, cn, blk, bsz), kp, blk, bsz, [&](uint32_t kx, int32_t p) {
@@ -2000,9 +2100,7 @@ static csa2_status stream_pool_batch(const uint8_t* q_idx, const uint8_t* k_idx,
   }
   if (scan_end && hipEventRecord((hipEvent_t)scan_end, s) != hipSuccess) return CSA2_ELAUNCH;
   stream_gather_kernel<<<dim3(groups, R), kSG, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, nbk, bpw, bsz, rows,
-                                                       hist, cand, cnt, above, list, k_pool, k_top, pm);
-  stream_finish_kernel<<<R, kSG, 0, s>>>(T, nbk, bpw, bsz, groups, rows, hist, above, list, cand, cnt, base, k_pool,
-                                          k_top);
+                                                       hist, cand, cnt, above, list, base, k_pool, k_top, pm);
   stream_write_kernel<<<dim3(groups, R), kSG, 0, s>>>(T, nbk, bpw, bsz, rows, base, cand, cnt, k_pool, k_top,
                                                       pool_idx, pool_scores, top_idx);
   return launch_status();
