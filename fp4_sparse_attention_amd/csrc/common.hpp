@@ -133,6 +133,44 @@ __device__ __forceinline__ uint32_t block_scan_1024(uint32_t v, uint32_t* wt, ui
   return base + inc - v;
 }
 
+// block-wide exclusive prefix sum, 256 threads (4 waves); wt holds >= 4 words
+__device__ __forceinline__ uint32_t block_scan_256(uint32_t v, uint32_t* wt, uint32_t& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t inc = wave_inclusive_scan(v);
+  if (lane == 63) wt[wave] = inc;
+  __syncthreads();
+  const uint32_t t0 = wt[0], t1 = wt[1], t2 = wt[2], t3 = wt[3];
+  total = t0 + t1 + t2 + t3;
+  const uint32_t base = (wave > 0 ? t0 : 0u) + (wave > 1 ? t1 : 0u) + (wave > 2 ? t2 : 0u);
+  __syncthreads();
+  return base + inc - v;
+}
+
+// the same digit search by 256 threads (kNB / 256 bins per thread)
+template <int kNB>
+__device__ __forceinline__ void find_bin_256(const uint32_t* hh, uint32_t need, uint32_t* wt, uint32_t* out2) {
+  constexpr int kPer = kNB / 256;
+  uint32_t c[kPer], local = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    c[j] = hh[kNB - 1 - kPer * threadIdx.x - j];
+    local += c[j];
+  }
+  uint32_t total;
+  const uint32_t excl = block_scan_256(local, wt, total);
+  if (excl < need && need <= excl + local) {
+    uint32_t acc = excl;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (acc < need && need <= acc + c[j]) {
+        out2[0] = (uint32_t)(kNB - 1 - kPer * threadIdx.x - j);
+        out2[1] = acc;
+      }
+      acc += c[j];
+    }
+  }
+}
+
 // digit search over a histogram in LDS by 1024 threads: bins are walked from the
 // top, thread t owns bins nb-1-(nb/1024)t-j; returns the bin holding the need-th
 // largest entry and the count above it (need >= 1 and <= the histogram total)

@@ -107,6 +107,74 @@ index_rows_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__
 //    order every workgroup would flush at each row boundary, measured slower).
 constexpr int kUnitTiles = 16;
 
+// Sampling for the candidate threshold (the sample and threshold kernels below)
+constexpr int kSampleN = 4096;
+constexpr int kSampleRun = 8;
+
+// rank m of the sample key that bounds a selection of k among V visible positions (0: take every position)
+__device__ __forceinline__ uint32_t sample_rank(int32_t k, int64_t V) {
+  if (V <= 0) return 0u;
+  const double mu = (double)k * (double)kSampleN / (double)V;
+  const double m = ceil(mu + 4.0 * sqrt(mu) + 8.0);
+  return m > (double)kSampleN ? 0u : (uint32_t)m;
+}
+
+// The threshold kernel's steps by the 256 threads of a scan workgroup, for
+// row r's 4,096 sample keys (16 per thread): tau_s, the lower edge of the
+// 22-bit key prefix holding the m-th largest sample (digits of 12 and 10
+// bits), and sh from the sample maximum.  h: 4,096 LDS words, zero on entry
+// and on return; wt: 8 words; res: 2 words.
+__device__ void sample_threshold_256(const uint32_t* __restrict__ samp_row, int64_t V, int32_t k, uint32_t* h,
+                                     uint32_t* wt, uint32_t* res, uint32_t& tau_s, uint32_t& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t m = sample_rank(k, V);
+  if (m == 0u) {
+    tau_s = 0u;
+    sh = 21u;             // (key >> 21) < 2048 for every key
+    return;
+  }
+  constexpr int kPer = kSampleN / 256;
+  const uint4* s4 = reinterpret_cast<const uint4*>(samp_row) + (kPer / 4) * tid;
+  uint32_t key[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer / 4; ++q) {
+    const uint4 v = s4[q];
+    key[4 * q] = v.x; key[4 * q + 1] = v.y; key[4 * q + 2] = v.z; key[4 * q + 3] = v.w;
+  }
+  uint32_t kmax = 0u;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    kmax = max(kmax, key[j]);
+    atomicAdd(&h[key[j] >> 20], 1u);
+  }
+  __syncthreads();
+  uint32_t need = m;
+  find_bin_256<4096>(h, need, wt, res);
+  __syncthreads();
+  uint32_t prefix = res[0] << 20;
+  need -= res[1];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) h[16 * tid + j] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if ((key[j] >> 20) == (prefix >> 20)) atomicAdd(&h[(key[j] >> 10) & 1023u], 1u);
+  __syncthreads();
+  find_bin_256<1024>(h, need, wt, res);
+  kmax = wave_max_u32(kmax);
+  if (lane == 0) wt[4 + wave] = kmax;
+  __syncthreads();
+  prefix |= res[0] << 10;
+  const uint32_t mx = max(max(wt[4], wt[5]), max(wt[6], wt[7]));
+#pragma unroll
+  for (int j = 0; j < 4; ++j) h[4 * tid + j] = 0u;
+  __syncthreads();
+  const uint32_t span = mx - prefix;      // mx >= prefix: prefix is at most a sample key
+  const int bits = span ? 32 - __builtin_clz(span) : 0;
+  tau_s = prefix;
+  sh = (uint32_t)(bits > 11 ? bits - 11 : 0);
+}
+
 // kPaged: keys in a page pool (pm.table set); kOut: scores written (always
 // for the scores-only scan).  Both are template switches so that the common
 // decode scan carries no page translation and no score stores.
@@ -116,6 +184,7 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
                     const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit,
                     float* __restrict__ scores, int R, int64_t units_per_row, CandOut cand, PageMap pm) {
   __shared__ uint32_t h[kCand ? kStreamBins : 1];
+  __shared__ uint32_t s_wt[kCand ? 8 : 1], s_res[kCand ? 2 : 1];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int kn = lane & 15;          // the lane's keys kn and kn + 16 of each tile
@@ -228,9 +297,27 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
     __syncthreads();
   }
   Unit cur, nxt;
-  fetch(r, j, cur);
   f16x8 a[2];
-  query(r, a);
+  if (kCand && cand.samp) {
+    // every workgroup serves one row (R <= G): the row's threshold from its sample, derived alike by each of
+    // the row's workgroups; the one holding the row's first unit records it for the selection passes
+    fetch(r, j, cur);
+    query_operands(q_idx + (int64_t)r * kIndexDim, lane, a);
+    const int64_t limit = row_limit ? row_limit[r] : T - 1;
+    const int64_t V = limit < 0 ? 0 : (limit + 1 < T ? limit + 1 : T);
+    uint32_t t_s, s_h;
+    sample_threshold_256(cand.samp + (int64_t)r * kSampleN, V, cand.k, h, s_wt, s_res, t_s, s_h);
+    tau = uniform_u32(t_s);
+    sh = uniform_u32(s_h);
+    tf = tau ? key_score(tau) : -3.402823466e38f;
+    if (j == 0 && threadIdx.x == 0) {
+      cand.row[r].tau_s = tau;
+      cand.row[r].sh = sh;
+    }
+  } else {
+    fetch(r, j, cur);
+    query(r, a);
+  }
   while (r < R) {
     int rn = r;
     int64_t jn = j;
@@ -289,16 +376,22 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
 // one 512-byte read.  Each wave scores kSampleTiles 32-sample tiles with the
 // scan's tile arithmetic (two for a few rows, four for many: fewer, longer
 // workgroups, -15 us at 4,096 rows); the keys go to samp [R][S].  Grid
-// (S / (128 kSampleTiles), R).
-constexpr int kSampleN = 4096;
-constexpr int kSampleRun = 8;
+// (S / (128 kSampleTiles), R).  Given hist (when no threshold kernel runs),
+// the row's workgroups also clear its histogram and selection state for the
+// scan.
 
 template <int kSampleTiles>
 __global__ void __launch_bounds__(256)
 index_sample_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx, int64_t T,
                     const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit,
-                    uint32_t* __restrict__ samp, PageMap pm) {
+                    uint32_t* __restrict__ samp, StreamRow* __restrict__ rows, uint32_t* __restrict__ hist,
+                    PageMap pm) {
   const int r = blockIdx.y, tid = threadIdx.x;
+  if (hist) {
+    uint4* hr = reinterpret_cast<uint4*>(hist + (int64_t)r * kStreamHistWords);
+    for (int i = blockIdx.x * 256 + tid; i < kStreamHistWords / 4; i += gridDim.x * 256) hr[i] = make_uint4(0u, 0u, 0u, 0u);
+    if (blockIdx.x == 0 && tid == 0) rows[r] = StreamRow{};
+  }
   const int lane = tid & 63, wave = tid >> 6;
   const int kn = lane & 15, part = 16 * (lane >> 4);
   const int64_t limit = row_limit ? row_limit[r] : T - 1;
@@ -345,12 +438,6 @@ index_sample_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
 // position) when m > S.  The candidate histogram's digit shift sh puts the
 // sample's largest key at digit < 2048.  Also clears the row's histogram and
 // selection state before the scan.
-__device__ __forceinline__ uint32_t sample_rank(int32_t k, int64_t V) {
-  if (V <= 0) return 0u;
-  const double mu = (double)k * (double)kSampleN / (double)V;
-  const double m = ceil(mu + 4.0 * sqrt(mu) + 8.0);
-  return m > (double)kSampleN ? 0u : (uint32_t)m;
-}
 
 __global__ void __launch_bounds__(1024)
 index_tau_kernel(const uint32_t* __restrict__ samp, int64_t T, const int64_t* __restrict__ row_limit, int32_t k,
@@ -792,12 +879,16 @@ void launch_index_block_cand(const uint8_t* q_idx, const uint8_t* k_idx, int32_t
 
 void launch_index_sample_tau(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int64_t T,
                              const int32_t* row_seq, const int64_t* row_limit, int32_t k, StreamRow* rows,
-                             uint32_t* hist, uint32_t* samp, hipStream_t s, const PageMap& pm) {
+                             uint32_t* hist, uint32_t* samp, bool tau, hipStream_t s, const PageMap& pm) {
+  // the threshold kernel clears the rows' state when it runs, the sample kernel otherwise
+  uint32_t* clear = tau ? nullptr : hist;
   if (R >= 64)
-    index_sample_kernel<4><<<dim3(kSampleN / (4 * 4 * kTile), R), 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, samp, pm);
+    index_sample_kernel<4><<<dim3(kSampleN / (4 * 4 * kTile), R), 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit,
+                                                                                samp, rows, clear, pm);
   else
-    index_sample_kernel<2><<<dim3(kSampleN / (4 * 2 * kTile), R), 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, samp, pm);
-  index_tau_kernel<<<R, 1024, 0, s>>>(samp, T, row_limit, k, rows, hist);
+    index_sample_kernel<2><<<dim3(kSampleN / (4 * 2 * kTile), R), 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit,
+                                                                                samp, rows, clear, pm);
+  if (tau) index_tau_kernel<<<R, 1024, 0, s>>>(samp, T, row_limit, k, rows, hist);
 }
 
 int64_t index_sample_words() { return kSampleN; }
@@ -808,6 +899,8 @@ int64_t index_scan_blocks(int64_t T) {
 }
 
 bool index_scan_streams(int32_t R, const int32_t* row_seq) { return !(row_seq && R >= 32); }
+
+bool index_scan_derives_tau(int32_t R) { return (int64_t)R <= resident_blocks(); }
 
 }  // namespace csa2
 

@@ -36,6 +36,9 @@ struct CandOut {
   uint2* kp;            // [R][T] (key, position)
   uint32_t* cnt;        // [R][n_blocks]
   int64_t n_blocks;     // blocks per row the scan writes counts for (4 per 512-position unit)
+  const uint32_t* samp; // [R][index_sample_words()] sample keys: the scan derives each row's tau_s and sh
+                        // from them (and stores them in the row state); null: already in the row state
+  int32_t k;            // the selection size the threshold is taken for (with samp)
 };
 
 // Full-mode index scan on `s`; with cand, also emits the candidates (and then
@@ -54,12 +57,17 @@ void launch_index_block_cand(const uint8_t* q_idx, const uint8_t* k_idx, int32_t
                              const int32_t* row_seq, const int64_t* row_limit, float* scores, const CandOut& cand,
                              int bsz, hipStream_t s, const PageMap& pm);
 
-// per-row threshold tau_s and digit shift for a selection of k from a
-// strided sample of the row's scores (samp: [R][index_sample_words()]
-// scratch); clears the row's histogram and state
+// a strided sample of each row's scores (samp: [R][index_sample_words()]
+// scratch), with the rows' histogram and state cleared; with tau, also the
+// threshold kernel that derives tau_s and the digit shift for a selection of
+// k from the sample (without it the candidate scan derives them itself)
 void launch_index_sample_tau(const uint8_t* q_idx, const uint8_t* k_idx, int32_t R, int64_t T,
                              const int32_t* row_seq, const int64_t* row_limit, int32_t k, StreamRow* rows,
-                             uint32_t* hist, uint32_t* samp, hipStream_t s, const PageMap& pm);
+                             uint32_t* hist, uint32_t* samp, bool tau, hipStream_t s, const PageMap& pm);
+
+// whether the candidate scan of R rows gives every workgroup a single row, so
+// that it can take the row's threshold from the sample itself (CandOut::samp)
+bool index_scan_derives_tau(int32_t R);
 int64_t index_sample_words();
 
 // blocks per row whose counts the candidate scan writes

@@ -2089,9 +2089,12 @@ static csa2_status stream_pool_batch(const uint8_t* q_idx, const uint8_t* k_idx,
   // gather / write workgroups per row: up to 64, fewer when many rows fill the chip anyway
   const int groups = (int)std::min<int64_t>(std::min<int64_t>(kStreamGroups, nbk), std::max<int64_t>(1, 4096 / R));
   const int bpw = (int)((nbk + groups - 1) / groups);
-  launch_index_sample_tau(q_idx, k_idx, R, T, row_seq, row_limit, k_pool, rows, hist, samp, s, pm);
+  // the per-row scan derives each row's threshold from the sample itself when each of its workgroups
+  // serves one row; otherwise (and for the query-block scan) the threshold kernel does
+  const bool scan_tau = !qblocks && index_scan_derives_tau(R);
+  launch_index_sample_tau(q_idx, k_idx, R, T, row_seq, row_limit, k_pool, rows, hist, samp, !scan_tau, s, pm);
   if (scan_start && hipEventRecord((hipEvent_t)scan_start, s) != hipSuccess) return CSA2_ELAUNCH;
-  const CandOut co{rows, hist, cand, cnt, nbk};
+  const CandOut co{rows, hist, cand, cnt, nbk, scan_tau ? samp : nullptr, k_pool};
   if (qblocks) {
     launch_index_block_cand(q_idx, k_idx, R, T, row_seq, row_limit, scores, co, bsz, s, pm);
     stream_hist_kernel<<<R, kSG, 0, s>>>(T, nbk, bsz, rows, hist, cand, cnt);
