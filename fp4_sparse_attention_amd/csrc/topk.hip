@@ -417,22 +417,37 @@ topk_small_kernel(const float* __restrict__ scores, int N, int64_t stride, const
   {
     float4 v[J];
     int4 mp[J];
+    // every load unconditional (slots past N re-read the row's first four, N >= 4, and are masked after):
+    // a load under a branch made the compiler wait for each before issuing the next
+    if (map_row) {
 #pragma unroll
-    for (int it = 0; it < J; ++it) {
-      const int s = s0 + 4 * it;
-      const bool in = s < N;
-      v[it] = in ? *reinterpret_cast<const float4*>(row + s) : make_float4(0.f, 0.f, 0.f, 0.f);
-      mp[it] = in ? (map_row ? *reinterpret_cast<const int4*>(map_row + s) : make_int4(s, s + 1, s + 2, s + 3))
-                  : make_int4(-1, -1, -1, -1);
+      for (int it = 0; it < J; ++it) {
+        const int sc = s0 + 4 * it < N ? s0 + 4 * it : 0;
+        v[it] = *reinterpret_cast<const float4*>(row + sc);
+        mp[it] = *reinterpret_cast<const int4*>(map_row + sc);
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < J; ++it) {
+        const int sc = s0 + 4 * it < N ? s0 + 4 * it : 0;
+        v[it] = *reinterpret_cast<const float4*>(row + sc);
+        mp[it] = make_int4(sc, sc + 1, sc + 2, sc + 3);
+      }
     }
+    // the histograms are cleared while the loads are in flight
+    for (int i = tid; i < kHistWords; i += kSmallThreads) hh[i] = 0u;
+    __syncthreads();
 #pragma unroll
     for (int it = 0; it < J; ++it) {
+      const bool in = s0 + 4 * it < N;
       const float f[4] = {v[it].x, v[it].y, v[it].z, v[it].w};
       const int32_t m4[4] = {mp[it].x, mp[it].y, mp[it].z, mp[it].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        key[it][j] = m4[j] < 0 ? 0u : score_key(f[j]);
-        pos[it][j] = m4[j];
+        key[it][j] = (!in || m4[j] < 0) ? 0u : score_key(f[j]);
+        pos[it][j] = in ? m4[j] : -1;
+        // the first selection's top digit, counted as each load lands
+        if (key[it][j] != 0u) atomicAdd(&hh[key[it][j] >> 20], 1u);
       }
     }
   }
@@ -456,9 +471,12 @@ topk_small_kernel(const float* __restrict__ scores, int N, int64_t stride, const
   };
 
   // radix select of tau, the k_eff-th largest visible key (k_eff = min(kk, visible))
-  auto select = [&](uint32_t kk, uint32_t& tau, uint32_t& need_eq, uint32_t& k_eff) {
-    for (int i = tid; i < kHistWords; i += kSmallThreads) hh[i] = 0u;
-    __syncthreads();
+  auto select = [&](uint32_t kk, uint32_t& tau, uint32_t& need_eq, uint32_t& k_eff, bool first) {
+    // the first selection finds its histograms cleared and the top digit's counted
+    if (!first) {
+      for (int i = tid; i < kHistWords; i += kSmallThreads) hh[i] = 0u;
+      __syncthreads();
+    }
     uint32_t need = 0, prefix = 0u;
     k_eff = 0;
     bool whole_bin = false;
@@ -469,13 +487,15 @@ topk_small_kernel(const float* __restrict__ scores, int N, int64_t stride, const
       const uint32_t bmask = d == 0 ? 4095u : 1023u;
       const int nb = d == 0 ? 4096 : 1024;
       uint32_t* h = hh + (d == 0 ? 0 : kSmallBins + 1024 * (d - 1));
+      if (d > 0 || !first) {
 #pragma unroll
-      for (int it = 0; it < J; ++it)
+        for (int it = 0; it < J; ++it)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t x = key[it][j];
-          if (x != 0u && (hi == 32 || (x >> hi) == (prefix >> hi))) atomicAdd(&h[(x >> shift) & bmask], 1u);
-        }
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t x = key[it][j];
+            if (x != 0u && (hi == 32 || (x >> hi) == (prefix >> hi))) atomicAdd(&h[(x >> shift) & bmask], 1u);
+          }
+      }
       __syncthreads();
       // bins walked from the top: 4 per thread at the first digit, 1 after
       const int per = d == 0 ? 4 : 1;
@@ -564,13 +584,13 @@ topk_small_kernel(const float* __restrict__ scores, int N, int64_t stride, const
   };
 
   uint32_t tau, need_eq, k_eff;
-  select((uint32_t)k, tau, need_eq, k_eff);
+  select((uint32_t)k, tau, need_eq, k_eff, true);
   const bool same = idx2_out && k2 == k;
   write(tau, need_eq, k_eff, k, idx_out + (int64_t)r * k, score_out ? score_out + (int64_t)r * k : nullptr,
         same ? idx2_out + (int64_t)r * k2 : nullptr);
   if (idx2_out && !same) {
     __syncthreads();
-    select((uint32_t)k2, tau, need_eq, k_eff);
+    select((uint32_t)k2, tau, need_eq, k_eff, false);
     write(tau, need_eq, k_eff, k2, idx2_out + (int64_t)r * k2, nullptr, nullptr);
   }
 }
