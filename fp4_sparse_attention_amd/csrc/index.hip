@@ -30,7 +30,7 @@ namespace csa2 {
 // One query row per workgroup row (grid.y = R).  Used for decode (Full and
 // Reindex).  kGather: column c of row r scores position pool[r][c].  kFp8:
 // scores through the FP8 matrix instruction (csa2_index_full_fp8).
-template <bool kGather, bool kFp8 = false>
+template <bool kGather, bool kFp8 = false, bool kPaged = false>
 __global__ void __launch_bounds__(256)
 index_rows_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx, int64_t T,
                   const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit,
@@ -59,20 +59,40 @@ index_rows_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__
   for (int64_t t0 = t_begin + wave; t0 < t_end; t0 += 4 * kUnroll) {
     i32x8 b[kUnroll];
     bool ok[kUnroll][2];
+    // every load unconditional, at a clamped index (column 0, key row 0) and masked after: a load under a
+    // branch made the compiler wait for each pool id before issuing the next
+    int64_t p[kUnroll][2];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t t = t0 + 4 * u;
-      uint4 v[2];
+    for (int u = 0; u < kUnroll; ++u)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int64_t c = t * kTile + 16 * h + kn;
-        int64_t p = -1;
-        if (t < t_end && c < n_cols) p = kGather ? (int64_t)prow[c] : c;
-        const int64_t row = (p >= 0 && p < T && p <= limit) ? phys_row(pm, seq, T, p) : -1;
-        ok[u][h] = row >= 0;
-        v[h] = ok[u][h] ? load_key_part(k_idx + row * kIndexDim + part) : make_uint4(0, 0, 0, 0);
+        const int64_t c = (t0 + 4 * u) * kTile + 16 * h + kn;
+        const bool in = t0 + 4 * u < t_end && c < n_cols;
+        if (kGather) {
+          const int64_t pv = (int64_t)prow[in ? c : 0];
+          p[u][h] = in ? pv : -1;
+        } else {
+          p[u][h] = in ? c : -1;
+        }
       }
-      b[u] = tile_pair(v[0], v[1]);
+    uint4 v[kUnroll][2];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t q = p[u][h];
+        const bool vis = q >= 0 && q < T && q <= limit;
+        // the dense layout as plain arithmetic (a page-table branch here made every key load wait)
+        const int64_t row = !vis ? -1 : (kPaged ? phys_row(pm, seq, T, q) : (int64_t)seq * T + q);
+        ok[u][h] = row >= 0;
+        v[u][h] = load_key_part(k_idx + (ok[u][h] ? row : 0) * kIndexDim + part);
+      }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        if (!ok[u][h]) v[u][h] = make_uint4(0, 0, 0, 0);
+      b[u] = tile_pair(v[u][0], v[u][1]);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -380,7 +400,7 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
 // the row's workgroups also clear its histogram and selection state for the
 // scan.
 
-template <int kSampleTiles>
+template <int kSampleTiles, bool kPaged>
 __global__ void __launch_bounds__(256)
 index_sample_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ k_idx, int64_t T,
                     const int32_t* __restrict__ row_seq, const int64_t* __restrict__ row_limit,
@@ -400,9 +420,11 @@ index_sample_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
   constexpr int kRuns = kSampleN / kSampleRun;
   i32x8 kb[kSampleTiles];
   bool ok[kSampleTiles][2];
+  // rows first, then every load unconditional (key row 0 where masked): a load under a branch, or after a
+  // page-table branch, made the compiler wait for each before issuing the next
+  int64_t rw[kSampleTiles][2];
 #pragma unroll
-  for (int u = 0; u < kSampleTiles; ++u) {
-    uint4 v[2];
+  for (int u = 0; u < kSampleTiles; ++u)
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
       const int64_t i = ((int64_t)(blockIdx.x * 4 + wave) * kSampleTiles + u) * kTile + 16 * hh + kn;
@@ -411,14 +433,24 @@ index_sample_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
       p0 = p0 < 0 ? 0 : (p0 > V - kSampleRun ? V - kSampleRun : p0);
       int64_t p = p0 + i % kSampleRun;
       p = p < 0 ? 0 : (p >= V ? V - 1 : p);
-      const int64_t row = V > 0 ? phys_row(pm, seq, T, p) : -1;
-      ok[u][hh] = row >= 0;
-      v[hh] = ok[u][hh] ? load_key_part(k_idx + row * kIndexDim + part) : make_uint4(0, 0, 0, 0);
+      rw[u][hh] = V <= 0 ? -1 : (kPaged ? phys_row(pm, seq, T, p) : (int64_t)seq * T + p);
+      ok[u][hh] = rw[u][hh] >= 0;
     }
-    kb[u] = tile_pair(v[0], v[1]);
-  }
+  // the query with the keys, in the same round trip
   f16x8 a[2];
   query_operands(q_idx + (int64_t)r * kIndexDim, lane, a);
+  uint4 v[kSampleTiles][2];
+#pragma unroll
+  for (int u = 0; u < kSampleTiles; ++u)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) v[u][hh] = load_key_part(k_idx + (ok[u][hh] ? rw[u][hh] : 0) * kIndexDim + part);
+#pragma unroll
+  for (int u = 0; u < kSampleTiles; ++u) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      if (!ok[u][hh]) v[u][hh] = make_uint4(0, 0, 0, 0);
+    kb[u] = tile_pair(v[u][0], v[u][1]);
+  }
 #pragma unroll
   for (int u = 0; u < kSampleTiles; ++u) {
     const float2 sc = mfma_score(a, kb[u]);
@@ -882,12 +914,14 @@ void launch_index_sample_tau(const uint8_t* q_idx, const uint8_t* k_idx, int32_t
                              uint32_t* hist, uint32_t* samp, bool tau, hipStream_t s, const PageMap& pm) {
   // the threshold kernel clears the rows' state when it runs, the sample kernel otherwise
   uint32_t* clear = tau ? nullptr : hist;
-  if (R >= 64)
-    index_sample_kernel<4><<<dim3(kSampleN / (4 * 4 * kTile), R), 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit,
-                                                                                samp, rows, clear, pm);
-  else
-    index_sample_kernel<2><<<dim3(kSampleN / (4 * 2 * kTile), R), 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit,
-                                                                                samp, rows, clear, pm);
+  const dim3 g4(kSampleN / (4 * 4 * kTile), R), g2(kSampleN / (4 * 2 * kTile), R);
+  if (pm.table) {
+    if (R >= 64) index_sample_kernel<4, true><<<g4, 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, samp, rows, clear, pm);
+    else index_sample_kernel<2, true><<<g2, 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, samp, rows, clear, pm);
+  } else {
+    if (R >= 64) index_sample_kernel<4, false><<<g4, 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, samp, rows, clear, pm);
+    else index_sample_kernel<2, false><<<g2, 256, 0, s>>>(q_idx, k_idx, T, row_seq, row_limit, samp, rows, clear, pm);
+  }
   if (tau) index_tau_kernel<<<R, 1024, 0, s>>>(samp, T, row_limit, k, rows, hist);
 }
 
@@ -1014,7 +1048,8 @@ extern "C" csa2_status csa2_index_reindex_paged(const uint8_t* q_idx, const uint
   const int64_t n_tiles = (P + kTile - 1) / kTile;
   int tpb = tiles_per_block_for(n_tiles, R);
   dim3 grid(ceil_div(n_tiles, tpb), R);
-  index_rows_kernel<true><<<grid, 256, 0, (hipStream_t)stream>>>(q_idx, k_pages, T, row_seq, nullptr, pool, P,
-                                                                 scores, tpb, PageMap{block_table, max_blocks, page});
+  index_rows_kernel<true, false, true><<<grid, 256, 0, (hipStream_t)stream>>>(q_idx, k_pages, T, row_seq, nullptr,
+                                                                               pool, P, scores, tpb,
+                                                                               PageMap{block_table, max_blocks, page});
   return launch_status();
 }
