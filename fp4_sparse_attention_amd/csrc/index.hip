@@ -205,6 +205,13 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
                     float* __restrict__ scores, int R, int64_t units_per_row, CandOut cand, PageMap pm) {
   __shared__ uint32_t h[kCand ? kStreamBins : 1];
   __shared__ uint32_t s_wt[kCand ? 8 : 1], s_res[kCand ? 2 : 1];
+  // each wave's candidates (with their slots in the row's block area) held back in LDS and written out in
+  // bursts when the stage fills and when the workgroup leaves the row: stores mixed into the key stream, one
+  // per ballot, had cost ~4.5 us of the 8 x 1M scan (a per-block burst did not help; a per-row one does)
+  constexpr int kStage = 512;
+  __shared__ uint2 s_ent[kCand ? 4 : 1][kCand ? kStage : 1];
+  __shared__ uint32_t s_dst[kCand ? 4 : 1][kCand ? kStage : 1];
+  uint32_t n_st = 0;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int kn = lane & 15;          // the lane's keys kn and kn + 16 of each tile
@@ -299,7 +306,13 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
       tf = tau ? key_score(tau) : -3.402823466e38f;
     }
   };
+  auto wave_flush = [&](int rr) {
+    uint2* base = cand.kp + (int64_t)rr * T;
+    for (uint32_t e = lane; e < n_st; e += 64) base[s_dst[wave][e]] = s_ent[wave][e];
+    n_st = 0;
+  };
   auto flush = [&](int rr) {
+    wave_flush(rr);
     __syncthreads();
     uint32_t* g = cand.hist + (int64_t)rr * kStreamHistWords;
     for (int i = threadIdx.x; i < kStreamBins; i += 256) {
@@ -360,7 +373,7 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
     if (kCand) {
       // this wave's block: 4 j + wave, positions [128 (4 j + wave), + 128)
       const int64_t blk = 4 * j + wave;
-      uint2* oc = cand.kp + (int64_t)r * T + blk * kBlockPositions;
+      if (n_st + kBlockPositions > (uint32_t)kStage) wave_flush(r);
       uint32_t at = 0;
 #pragma unroll
       for (int i = 0; i < kUnroll; ++i) {
@@ -370,12 +383,15 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
           const uint64_t m = __ballot(c);
           if (c) {
             const uint32_t kk = score_key(key[i][hh]);
-            oc[at + lanes_below(m)] = make_uint2(kk, (uint32_t)((t0 + i) * kTile + 16 * hh + kn));
+            const uint32_t o = at + lanes_below(m);
+            s_ent[wave][n_st + o] = make_uint2(kk, (uint32_t)((t0 + i) * kTile + 16 * hh + kn));
+            s_dst[wave][n_st + o] = (uint32_t)(blk * kBlockPositions) + o;
             atomicAdd(&h[min((kk - tau) >> sh, (uint32_t)(kStreamBins - 1))], 1u);
           }
           at += (uint32_t)__popcll(m);
         }
       }
+      n_st += at;
       if (lane == 0) cand.cnt[(int64_t)r * cand.n_blocks + blk] = at;
     }
     if (rn != r) {
