@@ -197,10 +197,19 @@ decode_append_kernel(int B, int L, const uint16_t* __restrict__ new_latent, cons
                      int32_t* __restrict__ swa_len) {
   constexpr int W = kWindowMax;
   const int b = blockIdx.x, tid = threadIdx.x;
+  // every load issued first, at addresses valid for every thread (the branches come after): the row and the
+  // token position, this thread's part of the latent row (pack threads) or of the key, and its first window
+  // element; behind branches they had made the compiler wait for each in turn
   const int64_t row = cache_rows[b];
+  const int64_t t = new_window ? tok_pos[b] : -1;
+  const uint4* src = reinterpret_cast<const uint4*>(new_latent + (int64_t)b * kLatent + (tid & 15) * 32);
+  const uint4 v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
+  const uint4 kv = new_keys ? *reinterpret_cast<const uint4*>(new_keys + (int64_t)b * kIndexDim + 16 * (tid & 3))
+                            : make_uint4(0u, 0u, 0u, 0u);
+  const int e0 = tid < L * 64 ? tid : 0;
+  const uint4 wv0 = new_window ? reinterpret_cast<const uint4*>(new_window + ((int64_t)(e0 >> 6) * B + b) * kLatent)[e0 & 63]
+                               : make_uint4(0u, 0u, 0u, 0u);
   if (row >= 0 && tid < 16) {
-    const uint4* src = reinterpret_cast<const uint4*>(new_latent + (int64_t)b * kLatent + tid * 32);
-    const uint4 v0 = src[0], v1 = src[1], v2 = src[2], v3 = src[3];
     const uint32_t w0[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
     const uint32_t w1[8] = {v2.x, v2.y, v2.z, v2.w, v3.x, v3.y, v3.z, v3.w};
     uint32_t c0, c1, c2, c3, s0, s1;
@@ -210,17 +219,15 @@ decode_append_kernel(int B, int L, const uint16_t* __restrict__ new_latent, cons
     *reinterpret_cast<uint16_t*>(scales + row * kScalesRow + tid * 2) = (uint16_t)(s0 | (s1 << 8));
   } else if (row >= 0 && tid < 20 && new_keys) {
     const int q = tid - 16;
-    *reinterpret_cast<uint4*>(k_idx + row * kIndexDim + 16 * q) =
-        *reinterpret_cast<const uint4*>(new_keys + (int64_t)b * kIndexDim + 16 * q);
+    *reinterpret_cast<uint4*>(k_idx + row * kIndexDim + 16 * q) = kv;
   }
   if (!new_window) return;
-  const int64_t t = tok_pos[b];
   if (t < 0) return;
   const int slot = (int)(t % W);
   for (int e = tid; e < L * 64; e += 256) {
     const int l = e >> 6, c = e & 63;
     const int64_t lb = (int64_t)l * B + b;
-    const uint4 v = reinterpret_cast<const uint4*>(new_window + lb * kLatent)[c];
+    const uint4 v = e == tid ? wv0 : reinterpret_cast<const uint4*>(new_window + lb * kLatent)[c];
     uint16_t* ring = swa + lb * S * kLatent;
     reinterpret_cast<uint4*>(ring + (int64_t)slot * kLatent)[c] = v;
     reinterpret_cast<uint4*>(ring + (int64_t)(slot + W) * kLatent)[c] = v;
