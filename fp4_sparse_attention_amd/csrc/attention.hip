@@ -665,6 +665,34 @@ attn_chunk_kernel(const AttnArgs a) {
   }
 }
 
+// The combine's workgroup -> (layer, row, head): XCD x (workgroup ids b with
+// b mod 8 = x) takes the (layer, row) pairs whose first chunk the chunk kernel
+// ran on XCD x, so the partials are read back through the L2 that took their
+// writes.  Pair p = row * L + layer owns chunk workgroups [p nc, p nc + nc) of
+// the chunk kernel's list, of which XCD x took [x per_xcd, x per_xcd + per_xcd).
+struct CombineMap {
+  int L, R, H, n_chunks, per_xcd;
+};
+
+__device__ __forceinline__ int combine_pair_begin(const CombineMap& cm, int x) {
+  const int64_t p = ((int64_t)x * cm.per_xcd + cm.n_chunks - 1) / cm.n_chunks;
+  const int64_t P = (int64_t)cm.L * cm.R;
+  return (int)(p < P ? p : P);
+}
+
+// false: a padding workgroup with no (layer, row, head)
+__device__ __forceinline__ bool combine_item(const CombineMap& cm, int& h, int& r, int& layer) {
+  const int x = (int)(blockIdx.x & 7), s = (int)(blockIdx.x >> 3);
+  const int p0 = combine_pair_begin(cm, x);
+  const int p1 = x == 7 ? cm.L * cm.R : combine_pair_begin(cm, x + 1);
+  if (s >= (p1 - p0) * cm.H) return false;
+  const int p = p0 + s / cm.H;
+  h = s % cm.H;
+  r = p / cm.L;
+  layer = p % cm.L;
+  return true;
+}
+
 // Merge the chunk partials of each (row, head), optionally with a finished
 // prior result (o_prev normalised, lse_prev natural log), into o and lse.
 // Thread t owns channels [4t, 4t+4).  The chunk weights 2^(m_c - M) go through
@@ -693,12 +721,14 @@ __device__ __forceinline__ float block_sum_128(float v, float* red) {
 }
 
 __global__ void __launch_bounds__(kCombineThreads)
-attn_combine_kernel(const float* __restrict__ o_part, const float* __restrict__ ml_part, int n_chunks, int R, int H,
+attn_combine_kernel(const float* __restrict__ o_part, const float* __restrict__ ml_part, const CombineMap cm,
                     const float* __restrict__ o_prev, const float* __restrict__ lse_prev,
                     float* __restrict__ o_out, float* __restrict__ lse_out) {
   __shared__ float s_w[kCombineThreads];
   __shared__ float red[2];
-  const int h = blockIdx.x, r = blockIdx.y, layer = blockIdx.z;
+  int h, r, layer;
+  if (!combine_item(cm, h, r, layer)) return;
+  const int n_chunks = cm.n_chunks, R = cm.R, H = cm.H;
   const int tid = threadIdx.x;
   const int c4 = tid * 4;
   const int64_t base = (((int64_t)layer * R + r) * n_chunks) * H + h;       // + chunk * H
@@ -764,10 +794,12 @@ attn_combine_kernel(const float* __restrict__ o_part, const float* __restrict__ 
 constexpr int kCombineFew = 16;
 
 __global__ void __launch_bounds__(kCombineThreads)
-attn_combine_few_kernel(const float* __restrict__ o_part, const float* __restrict__ ml_part, int n_chunks, int R,
-                        int H, const float* __restrict__ o_prev, const float* __restrict__ lse_prev,
+attn_combine_few_kernel(const float* __restrict__ o_part, const float* __restrict__ ml_part, const CombineMap cm,
+                        const float* __restrict__ o_prev, const float* __restrict__ lse_prev,
                         float* __restrict__ o_out, float* __restrict__ lse_out) {
-  const int h = blockIdx.x, r = blockIdx.y, layer = blockIdx.z;
+  int h, r, layer;
+  if (!combine_item(cm, h, r, layer)) return;
+  const int n_chunks = cm.n_chunks, R = cm.R, H = cm.H;
   const int c4 = threadIdx.x * 4;
   const int64_t base = (((int64_t)layer * R + r) * n_chunks) * H + h;       // + chunk * H
   const int64_t orow = ((int64_t)layer * R + r) * H + h;
@@ -913,12 +945,22 @@ static csa2_status attention_call(int32_t L, const uint16_t* q_lat, int32_t R, i
     if (dc != CSA2_OK) return dc;
   }
   launch_chunks(a, s);
-  if (!direct && a.n_chunks <= kCombineFew)
-    attn_combine_few_kernel<<<dim3(H, R, L), kCombineThreads, 0, s>>>(a.o_part, a.ml_part, a.n_chunks, R, H, o_prev,
-                                                                      lse_prev, o, lse);
-  else if (!direct)
-    attn_combine_kernel<<<dim3(H, R, L), kCombineThreads, 0, s>>>(a.o_part, a.ml_part, a.n_chunks, R, H, o_prev,
-                                                                  lse_prev, o, lse);
+  if (!direct) {
+    const CombineMap cm{L, R, H, a.n_chunks, a.per_xcd};
+    // the largest number of (layer, row) pairs one XCD combines (the same split as combine_pair_begin)
+    const int64_t P = (int64_t)L * R;
+    auto pair_begin = [&](int x) {
+      const int64_t p = ((int64_t)x * a.per_xcd + a.n_chunks - 1) / a.n_chunks;
+      return p < P ? p : P;
+    };
+    int64_t most = 0;
+    for (int x = 0; x < 8; ++x) most = std::max<int64_t>(most, (x == 7 ? P : pair_begin(x + 1)) - pair_begin(x));
+    const dim3 grid((unsigned)(8 * most * H));
+    if (a.n_chunks <= kCombineFew)
+      attn_combine_few_kernel<<<grid, kCombineThreads, 0, s>>>(a.o_part, a.ml_part, cm, o_prev, lse_prev, o, lse);
+    else
+      attn_combine_kernel<<<grid, kCombineThreads, 0, s>>>(a.o_part, a.ml_part, cm, o_prev, lse_prev, o, lse);
+  }
   return launch_status();
 }
 

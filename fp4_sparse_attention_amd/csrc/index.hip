@@ -140,11 +140,24 @@ __device__ __forceinline__ uint32_t sample_rank(int32_t k, int64_t V) {
 }
 
 // The threshold kernel's steps by the 256 threads of a scan workgroup, for
-// row r's 4,096 sample keys (16 per thread): tau_s, the lower edge of the
-// 22-bit key prefix holding the m-th largest sample (digits of 12 and 10
-// bits), and sh from the sample maximum.  h: 4,096 LDS words, zero on entry
-// and on return; wt: 8 words; res: 2 words.
-__device__ void sample_threshold_256(const uint32_t* __restrict__ samp_row, int64_t V, int32_t k, uint32_t* h,
+// row r's 4,096 sample keys (16 per thread, loaded by sample_load_256): tau_s,
+// the lower edge of the 22-bit key prefix holding the m-th largest sample
+// (digits of 12 and 10 bits), and sh from the sample maximum.  h: 4,096 LDS
+// words, zero on entry and on return; wt: 8 words; res: 2 words.
+constexpr int kSamplePer = kSampleN / 256;
+
+// Issued before the workgroup's first key loads: loads complete in issue
+// order, so sample keys loaded after them would wait for the whole unit.
+__device__ __forceinline__ void sample_load_256(const uint32_t* __restrict__ samp_row, uint32_t (&key)[kSamplePer]) {
+  const uint4* s4 = reinterpret_cast<const uint4*>(samp_row) + (kSamplePer / 4) * threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < kSamplePer / 4; ++q) {
+    const uint4 v = s4[q];
+    key[4 * q] = v.x; key[4 * q + 1] = v.y; key[4 * q + 2] = v.z; key[4 * q + 3] = v.w;
+  }
+}
+
+__device__ void sample_threshold_256(const uint32_t (&key)[kSamplePer], int64_t V, int32_t k, uint32_t* h,
                                      uint32_t* wt, uint32_t* res, uint32_t& tau_s, uint32_t& sh) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint32_t m = sample_rank(k, V);
@@ -153,14 +166,7 @@ __device__ void sample_threshold_256(const uint32_t* __restrict__ samp_row, int6
     sh = 21u;             // (key >> 21) < 2048 for every key
     return;
   }
-  constexpr int kPer = kSampleN / 256;
-  const uint4* s4 = reinterpret_cast<const uint4*>(samp_row) + (kPer / 4) * tid;
-  uint32_t key[kPer];
-#pragma unroll
-  for (int q = 0; q < kPer / 4; ++q) {
-    const uint4 v = s4[q];
-    key[4 * q] = v.x; key[4 * q + 1] = v.y; key[4 * q + 2] = v.z; key[4 * q + 3] = v.w;
-  }
+  constexpr int kPer = kSamplePer;
   uint32_t kmax = 0u;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
@@ -294,6 +300,28 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
       x.b[i] = tile_pair(v[0], v[1]);
     }
   };
+  // the same loads with no branch: a masked half reads key row 0 of the array and is left as loaded (its
+  // score only lands in its own output column, which the ok flag discards; zeroing the loaded registers would
+  // wait for the load).  The prologue's sample keys, issued first, can then be waited for alone while the
+  // unit's keys are in flight.
+  auto fetch_flat = [&](int rr, int64_t jj, Unit& x) {
+    const int64_t t0 = tile_of(jj);
+    const int seq = row_seq ? row_seq[rr] : rr;
+    const int64_t limit = row_limit ? row_limit[rr] : T - 1;
+#pragma unroll
+    for (int i = 0; i < kUnroll; ++i) {
+      const int64_t p0 = (t0 + i) * kTile;
+      const int64_t row0 = p0 >= T ? -1 : (kPaged ? phys_row(pm, seq, T, p0) : (int64_t)seq * T + p0);
+      uint4 v[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int64_t p = p0 + 16 * hh + kn;
+        x.ok[i][hh] = row0 >= 0 && p < T && p <= limit;
+        v[hh] = load_key_part<kCand>(k_idx + (x.ok[i][hh] ? row0 + 16 * hh + kn : 0) * kIndexDim + part);
+      }
+      x.b[i] = tile_pair(v[0], v[1]);
+    }
+  };
   uint32_t tau = 0, sh = 0;
   float tf = 0.f;
   auto query = [&](int rr, f16x8* a) {
@@ -334,12 +362,14 @@ index_stream_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict
   if (kCand && cand.samp) {
     // every workgroup serves one row (R <= G): the row's threshold from its sample, derived alike by each of
     // the row's workgroups; the one holding the row's first unit records it for the selection passes
-    fetch(r, j, cur);
+    uint32_t skey[kSamplePer];
+    sample_load_256(cand.samp + (int64_t)r * kSampleN, skey);
+    fetch_flat(r, j, cur);
     query_operands(q_idx + (int64_t)r * kIndexDim, lane, a);
     const int64_t limit = row_limit ? row_limit[r] : T - 1;
     const int64_t V = limit < 0 ? 0 : (limit + 1 < T ? limit + 1 : T);
     uint32_t t_s, s_h;
-    sample_threshold_256(cand.samp + (int64_t)r * kSampleN, V, cand.k, h, s_wt, s_res, t_s, s_h);
+    sample_threshold_256(skey, V, cand.k, h, s_wt, s_res, t_s, s_h);
     tau = uniform_u32(t_s);
     sh = uniform_u32(s_h);
     tf = tau ? key_score(tau) : -3.402823466e38f;
