@@ -858,7 +858,7 @@ constexpr int kMinChunkTiles = 4;              // partial outputs stay small nex
 // Chunks per (layer, row): about one workgroup per compute unit in total, whole
 // groups of kPrefetch sparse tiles per chunk; the window tiles are spread one
 // per chunk where there are enough chunks.
-static Plan chunk_plan(int32_t L, int32_t R, int32_t K, bool sparse, bool window) {
+static Plan chunk_plan(int32_t L, int32_t R, int32_t H, int32_t K, bool sparse, bool window) {
   Plan p;
   p.n_sparse_tiles = sparse ? (K + kKT - 1) / kKT : 0;
   p.n_window_tiles = window ? kWindowChunks : 0;
@@ -872,7 +872,12 @@ static Plan chunk_plan(int32_t L, int32_t R, int32_t K, bool sparse, bool window
   const int64_t target = device_cu_count();
   const int64_t want = (target + per_chunk - 1) / per_chunk;
   int64_t spc = (p.n_sparse_tiles + want - 1) / want;
-  if (spc < kMinChunkTiles) spc = kMinChunkTiles;
+  // a latency-bound call whose chunk partials stay small even at one prefetch group per chunk (within 256 KB
+  // in all: a single row of a few heads) may use such chunks (one row of 16 heads, K = 256: 16.3 -> 12.5 us
+  // per call; two rows of 64 heads at K = 2,048, 8 MB of partials that way, ran 0.4 us slower)
+  const int64_t small_parts = (int64_t)((p.n_sparse_tiles + kPrefetch - 1) / kPrefetch) * L * R * H * kLatent * 4;
+  const int64_t min_tiles = small_parts <= (256 << 10) ? kPrefetch : kMinChunkTiles;
+  if (spc < min_tiles) spc = min_tiles;
   spc = (spc + kPrefetch - 1) / kPrefetch * kPrefetch;     // whole groups of tiles
   if (spc > kMaxChunkTiles) spc = kMaxChunkTiles;
   p.sparse_per_chunk = (int)spc;
@@ -908,7 +913,7 @@ static csa2_status attention_call(int32_t L, const uint16_t* q_lat, int32_t R, i
                                   const float* o_prev, const float* lse_prev, float* o, float* lse,
                                   void* workspace, size_t workspace_bytes, void* stream,
                                   const PageMap& pm = PageMap{}, bool scratch = false) {
-  const Plan p = chunk_plan(L, R, K, idx != nullptr, swa != nullptr);
+  const Plan p = chunk_plan(L, R, H, K, idx != nullptr, swa != nullptr);
   AttnArgs a;
   a.pm = pm;
   a.q_lat = q_lat; a.R = R; a.H = H; a.L = L;
@@ -966,7 +971,7 @@ static csa2_status attention_call(int32_t L, const uint16_t* q_lat, int32_t R, i
 }
 
 static size_t attention_workspace(int32_t L, int32_t R, int32_t H, int32_t K, bool sparse, bool window) {
-  return partial_bytes(L, R, H, chunk_plan(L, R, K, sparse, window).n_chunks, nullptr);
+  return partial_bytes(L, R, H, chunk_plan(L, R, H, K, sparse, window).n_chunks, nullptr);
 }
 
 // The allocation-free call's chunk partials live in this array, one copy per
@@ -1134,7 +1139,7 @@ extern "C" csa2_status csa2_sparse_swa_decode_layers_noalloc(
     off[l] = (int64_t)layer_idx[l] * R * K;
   }
   // a shape beyond the array is refused before any HIP call
-  const Plan p = chunk_plan(L, R, K, true, true);
+  const Plan p = chunk_plan(L, R, H, K, true, true);
   if (p.n_chunks > 1 && partial_bytes(L, R, H, p.n_chunks, nullptr) > kScratchBytes) return CSA2_ESCRATCH;
   void* ws = scratch_ptr();
   if (!ws) return CSA2_ELAUNCH;
